@@ -1,0 +1,477 @@
+"""Plain CPU oracle for the KV-cache scoring / selection / compaction / re-RoPE path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library imports this module.  Only the
+test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may import or call it.  It shares no code with the HIP path: it is written from the
+four pages on agent-session KV eviction and from plain mathematics, in NumPy float64,
+slowly and without blocking, fusion or reordering beyond what each definition states.
+
+Pages and the parts used (cited by title and section):
+  * "PACE: Keeping the Right Tokens in the KV Cache Is Not Enough for Long-Horizon
+    LLM Agents" -- Sec. 2 (budgeted eviction, H2O / SnapKV / StreamingLLM),
+    Sec. 3.1 (blueprint, foresight bonus), Sec. 3.2 (bounded positions, renumbering,
+    Proposition 1, choosing the limit), Sec. 3.5 (split-half RoPE), Table 1 (budget
+    2,048 incl. 4 sinks and 128 recent), Sec. 5.7 / 7 (foresight floor of 50K).
+  * "MemDecay: Region-Aware KV Cache Eviction for Efficient LLM Agent Inference" --
+    Method (region labels, EWMA, decay clock, composite score, pinned regions,
+    page-mean eviction, half-life).
+  * "Rethinking KV Cache Eviction for Agentic LLM Serving" (Penelope) -- the
+    illustrative cost example, the single-request measurement, and Part one (free
+    only the needed leading blocks of the private history).
+  * "ActKV: Efficient LLM Agents through Action-Guided KV Cache Management" --
+    Sec. 2.3 (attention score), Sec. 2.5 (paged KV layout and slot-map example),
+    Sec. 3.3 (the three primitives), Sec. 7.1 (score recovery from the LSE).
+
+Readings of points the pages leave open are listed next to each function.
+Parity status: every function here is pinned by a ``-m "not gpu"`` test except the
+exact numerical values of ``foresight_bonus`` (see its docstring: parity unpinned,
+only its ordering properties are pinned).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------------------
+# bf16 rounding (storage type of cached keys and values)
+# --------------------------------------------------------------------------------------
+
+BF16_MAX = float.fromhex("0x1.fep127")  # largest finite bf16
+
+
+def bf16_round(x):
+    """Round float64 values to the nearest bf16 value, ties to even (RNE).
+
+    bf16 keeps 8 significant bits, the float32 exponent range, and subnormals down to
+    2**-133.  For |x| in [2**(e-1), 2**e) the spacing is 2**(e-8); below the smallest
+    normal 2**-126 the spacing stays 2**-133.  Scaling by a power of two is exact, so
+    ``rint`` (round half to even) on the scaled value is exact RNE.
+    Returns float64 arrays holding exactly representable bf16 values.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e, -125) - 8
+    r = np.ldexp(np.rint(np.ldexp(x, -q)), q)
+    r = np.where(np.abs(r) > BF16_MAX, np.copysign(np.inf, r), r)
+    return np.where(np.isfinite(x), r, x)
+
+
+def bf16_bits(x):
+    """uint16 bit patterns of float64 values that are exactly bf16."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_from_bits(b):
+    """float64 values of uint16 bf16 bit patterns."""
+    u = np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------------------
+# Paged KV layout (ActKV Sec. 2.5)
+# --------------------------------------------------------------------------------------
+
+def slot_map(block_table, page_size, n_tokens):
+    """Physical slot of each logical token: block_table[j // BS] * BS + j % BS.
+
+    ActKV Sec. 2.5: a block table maps logical token positions to physical blocks of
+    BS slots; with BS=2, block_table=[17, 9] and 3 used tokens the slots are
+    [34, 35, 18].
+    """
+    bt = np.asarray(block_table, dtype=np.int64)
+    return [int(bt[j // page_size]) * page_size + j % page_size for j in range(n_tokens)]
+
+
+def gather_logical(paged, block_table, page_size, n_tokens):
+    """Logical-order view of one paged cache tensor.
+
+    ``paged`` is [layers][physical_pages][page_size][kv_heads][head_dim] (ActKV's
+    PagedKVCache[.., B, BS, H, D] per layer); returns [layers][n_tokens][kv_heads][D].
+    ``block_table=None`` means physical page == logical page.
+    """
+    paged = np.asarray(paged)
+    nl, npg, ps, hk, d = paged.shape
+    assert ps == page_size
+    flat = paged.reshape(nl, npg * ps, hk, d)
+    if block_table is None:
+        slots = np.arange(n_tokens)
+    else:
+        slots = np.asarray(slot_map(block_table, page_size, n_tokens), dtype=np.int64)
+    return flat[:, slots]
+
+
+# --------------------------------------------------------------------------------------
+# O1: windowed attention mass  (MemDecay Method; ActKV Sec. 2.3 and 7.1; PACE Sec. 2)
+# --------------------------------------------------------------------------------------
+
+def attention_mass(q, k, scale=None):
+    """Windowed softmax attention mass received by every cached token.
+
+    q: [L][W][Hq][D] window queries (already rotated at their own positions),
+    k: [L][N][Hkv][D] cached keys in logical order.  Returns (mass[N], lse[L][Hq][W]).
+
+    For layer l, query head h (KV head g = h // (Hq/Hkv), contiguous GQA groups) and
+    window query w, which sits at logical position N - W + w and sees keys j <= N-W+w:
+        s_j  = scale * <q[l,w,h], k[l,j,g]>
+        LSE  = log sum_j exp(s_j)                 (ActKV Sec. 7.1's log-sum-exp)
+        A_j  = exp(s_j - LSE)                     (softmax, ActKV Sec. 2.3)
+        mass_j = sum over (l, h, w) of A_j        (masked keys contribute 0)
+    Readings: scale defaults to 1/sqrt(D) (ActKV prints softmax(q K^T) without a scale;
+    the standard attention scale is used); the window's own keys are scored causally.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    nl, w_len, hq, d = q.shape
+    nl2, n, hkv, d2 = k.shape
+    assert nl == nl2 and d == d2 and hq % hkv == 0 and 1 <= w_len <= n
+    g_size = hq // hkv
+    if scale is None or scale == 0:
+        scale = 1.0 / math.sqrt(d)
+    qpos = n - w_len + np.arange(w_len)
+    visible = np.arange(n)[None, :] <= qpos[:, None]          # [W][N]
+    mass = np.zeros(n, dtype=np.float64)
+    lse = np.zeros((nl, hq, w_len), dtype=np.float64)
+    for layer in range(nl):
+        for h in range(hq):
+            g = h // g_size
+            s = scale * (q[layer, :, h, :] @ k[layer, :, g, :].T)   # [W][N]
+            s = np.where(visible, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            row_lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+            a = np.exp(s - row_lse[:, None])                       # 0 where masked
+            mass += a.sum(axis=0)
+            lse[layer, h] = row_lse
+    return mass, lse
+
+
+# --------------------------------------------------------------------------------------
+# O3: foresight bonus  (PACE Sec. 3.1, Sec. 5.7 and Sec. 7)
+# --------------------------------------------------------------------------------------
+
+def foresight_bonus(next_use, floor=50000.0):
+    """Per-span bonus from the forward-reference table.
+
+    PACE turns the planner's dependency graph into a per-span bonus that dominates
+    attention scores, keeps soonest-needed context first, is added to H2O's score, and
+    has a constant floor (50K).  The formula itself is not printed.  Reading: with d >= 1
+    the number of steps until the soonest future step that reads the span,
+        bonus = floor * (1 + 1/d),   and 0 when no future step reads it (d <= 0).
+    PARITY UNPINNED for the exact values; pinned only for dominance over unprotected
+    scores below the floor and for soonest-first ordering.
+    """
+    d = np.asarray(next_use, dtype=np.float64)
+    out = np.zeros_like(d)
+    sel = d >= 1
+    out[sel] = floor * (1.0 + 1.0 / d[sel])
+    return out
+
+
+def token_bonus(span_id, span_bonus):
+    """Bonus of each token: the bonus of the span it belongs to (span id -1: none)."""
+    sid = np.asarray(span_id, dtype=np.int64)
+    sb = np.asarray(span_bonus, dtype=np.float64)
+    out = np.zeros(sid.shape, dtype=np.float64)
+    has = sid >= 0
+    out[has] = sb[sid[has]]
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# O2: MemDecay and H2O epilogues
+# --------------------------------------------------------------------------------------
+
+def memdecay_update(abar, region, base_prio, decay_rate, rho, alpha, tau, dt_steps,
+                    ewma, clock, bonus=None):
+    """One MemDecay scoring step (MemDecay, Method).
+
+        a_i  <- rho * a_i + (1 - rho) * Abar_i
+        dt_i <- 0 if Abar_i > tau else dt_i + dt_steps        (clock resets on use)
+        s_i   = b_r(i) * exp(-lambda_r(i) * dt_i) + alpha * a_i  (+ foresight bonus)
+    Readings: updates in the order EWMA, clock, score; "attention above tau" is a
+    strict comparison of the windowed Abar_i; dt counts decode steps, dt_steps per
+    observation (k > 1 for sampled intervals).  Returns (ewma', clock', score).
+    """
+    abar = np.asarray(abar, dtype=np.float64)
+    r = np.asarray(region, dtype=np.int64)
+    b = np.asarray(base_prio, dtype=np.float64)[r]
+    lam = np.asarray(decay_rate, dtype=np.float64)[r]
+    a_new = rho * np.asarray(ewma, dtype=np.float64) + (1.0 - rho) * abar
+    clock = np.asarray(clock, dtype=np.int64)
+    c_new = np.where(abar > tau, 0, clock + dt_steps)
+    s = b * np.exp(-lam * c_new) + alpha * a_new
+    if bonus is not None:
+        s = s + np.asarray(bonus, dtype=np.float64)
+    return a_new, c_new, s
+
+
+def h2o_update(mass, accum, bonus=None):
+    """H2O accumulated attention (PACE Sec. 2): acc <- acc + mass; s = acc (+ bonus)."""
+    acc = np.asarray(accum, dtype=np.float64) + np.asarray(mass, dtype=np.float64)
+    s = acc.copy()
+    if bonus is not None:
+        s = s + np.asarray(bonus, dtype=np.float64)
+    return acc, s
+
+
+def pinned_tokens(n_tokens, region=None, pinned_regions=0, n_sink=0, n_recent=0,
+                  token_pinned=None):
+    """Tokens kept unconditionally.
+
+    MemDecay pins whole regions (system by default); PACE's budget always includes 4
+    sink and 128 recent tokens (Table 1).  A token is pinned if any rule pins it.
+    ``pinned_regions`` is a bit mask over region labels.
+    """
+    p = np.zeros(n_tokens, dtype=bool)
+    if region is not None and pinned_regions:
+        r = np.asarray(region, dtype=np.int64)
+        p |= ((pinned_regions >> r) & 1).astype(bool)
+    p[: min(n_sink, n_tokens)] = True
+    if n_recent > 0:
+        p[max(0, n_tokens - n_recent):] = True
+    if token_pinned is not None:
+        p |= np.asarray(token_pinned).astype(bool)
+    return p
+
+
+def page_mean(score, page_size):
+    """MemDecay's page score S_p = (1/|p|) sum_{i in p} s_i over the tokens present."""
+    s = np.asarray(score, dtype=np.float64)
+    n = s.shape[0]
+    n_pages = -(-n // page_size)
+    return np.array([s[p * page_size:min(n, (p + 1) * page_size)].mean()
+                     for p in range(n_pages)])
+
+
+def page_any(flags, page_size):
+    """A page is pinned when any of its tokens is pinned (keeps pinned tokens alive)."""
+    f = np.asarray(flags).astype(bool)
+    n = f.shape[0]
+    n_pages = -(-n // page_size)
+    return np.array([f[p * page_size:min(n, (p + 1) * page_size)].any()
+                     for p in range(n_pages)])
+
+
+# --------------------------------------------------------------------------------------
+# O4: budget selection (MemDecay Method; PACE Table 1; ActKV Sec. 3.3 "Eviction")
+# --------------------------------------------------------------------------------------
+
+STATUS_PINNED_OVER_BUDGET = 1
+STATUS_NAN_SCORE = 2
+
+
+def select_items(score, pinned, budget):
+    """Keep all pinned items, then the best (budget - #pinned) others.
+
+    Total order on items: higher score first; on an exact tie the lower index first;
+    -0.0 counts as +0.0; NaN scores order after every number.  Returns
+    (kept item indices ascending, status bits).  When the pinned items alone exceed
+    the budget they are all kept (MemDecay keeps pinned tokens unconditionally) and
+    STATUS_PINNED_OVER_BUDGET is set.
+    """
+    s = np.asarray(score, dtype=np.float64)
+    n = s.shape[0]
+    pin = np.zeros(n, dtype=bool) if pinned is None else np.asarray(pinned).astype(bool)
+    status = 0
+    if np.isnan(s).any():
+        status |= STATUS_NAN_SCORE
+    pinned_idx = [i for i in range(n) if pin[i]]
+    others = [i for i in range(n) if not pin[i]]
+
+    def order_key(i):
+        v = s[i]
+        if math.isnan(v):
+            return (1, 0.0, i)
+        return (0, -(v + 0.0), i)
+
+    others.sort(key=order_key)
+    room = budget - len(pinned_idx)
+    if room < 0:
+        status |= STATUS_PINNED_OVER_BUDGET
+        room = 0
+    kept = sorted(pinned_idx + others[:room])
+    return np.array(kept, dtype=np.int64), status
+
+
+def expand_items(items, item_tokens, n_tokens):
+    """Token indices of kept items, ascending; a partial last page keeps what it has."""
+    out = []
+    for it in items:
+        for t in range(int(it) * item_tokens, min(n_tokens, (int(it) + 1) * item_tokens)):
+            out.append(t)
+    return np.array(out, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------------------
+# O5: Penelope segment eviction and recompute cost
+# --------------------------------------------------------------------------------------
+
+def segment_evict_len(n_tokens, prefix_len, evict_tokens, block):
+    """Tokens actually freed: the needed count rounded up to whole blocks, capped at
+    the private history (Penelope, Part one: split at block boundaries and free only
+    the leading blocks needed)."""
+    e = -(-evict_tokens // block) * block
+    return max(0, min(e, n_tokens - prefix_len))
+
+
+def select_segment(n_tokens, prefix_len, evict_tokens, block):
+    """Keep [0, P) and [P + E', N): delete from the front of the private history."""
+    e = segment_evict_len(n_tokens, prefix_len, evict_tokens, block)
+    keep = list(range(prefix_len)) + list(range(prefix_len + e, n_tokens))
+    return np.array(keep, dtype=np.int64)
+
+
+QWEN3_8B_LINEAR_UNITS = 23552
+
+
+def recompute_cost(a, b, linear_units=QWEN3_8B_LINEAR_UNITS):
+    """Cost of recomputing tokens at positions [a, b).
+
+    Penelope's model: one unit is one query-key pair; a token at position p attends to
+    the p tokens before it and its linear/FFN work is a position-independent constant
+    (23,552 units for Qwen3-8B).  Summed one token at a time.
+    """
+    return float(sum(linear_units + p for p in range(a, b)))
+
+
+# --------------------------------------------------------------------------------------
+# O6: exact re-rotation and compaction  (PACE Sec. 3.2 Proposition 1, Sec. 3.5)
+# --------------------------------------------------------------------------------------
+
+def rope_inv_freq(theta, head_dim):
+    """theta_i = base ** (-2 i / D), i < D/2 (standard RoPE frequencies), float64."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(theta), -2.0 * i / head_dim)
+
+
+def rope_rotate(k, delta, theta):
+    """Rotate split-half RoPE pairs (i, i + D/2) of k[..., D] by angle delta * theta_i.
+
+        x' = x cos(phi) - y sin(phi),   y' = x sin(phi) + y cos(phi)
+    ``delta`` broadcasts against k's leading dims.  float64 throughout.
+    """
+    k = np.asarray(k, dtype=np.float64)
+    d = k.shape[-1]
+    half = d // 2
+    phi = np.asarray(delta, dtype=np.float64)[..., None] * rope_inv_freq(theta, d)
+    c, s = np.cos(phi), np.sin(phi)
+    x, y = k[..., :half], k[..., half:]
+    return np.concatenate([x * c - y * s, x * s + y * c], axis=-1)
+
+
+def renumbered_positions(n_keep, renumber_base, old_pos_kept):
+    """New physical positions: base + rank when renumbering (order-preserving and
+    gap-collapsing, PACE Sec. 3.2), otherwise unchanged."""
+    if renumber_base is None or renumber_base < 0:
+        return np.asarray(old_pos_kept, dtype=np.int64).copy()
+    return renumber_base + np.arange(n_keep, dtype=np.int64)
+
+
+def compact_rerope(k, v, keep, old_pos, renumber_base, theta):
+    """Stable in-order gather of kept tokens plus exact re-rotation of their keys.
+
+    k, v: [L][N][Hkv][D] logical arrays holding bf16 values; keep: ascending kept token
+    indices.  Rank r takes source j = keep[r].  V is copied verbatim.  K is copied
+    verbatim when delta = new_pos - old_pos is 0, otherwise rotated by delta in float64
+    (Proposition 1: re-rotating the cached key by the position difference gives the key
+    at the new position) and rounded once to bf16 (RNE).  Returns (k', v', new_pos).
+    Reading: the "fp32" derivation of the pages is evaluated here in float64 from the
+    exact bf16 inputs, so the oracle holds the correctly rounded result.
+    """
+    keep = np.asarray(keep, dtype=np.int64)
+    old_kept = np.asarray(old_pos, dtype=np.int64)[keep]
+    new_pos = renumbered_positions(len(keep), renumber_base, old_kept)
+    delta = new_pos - old_kept
+    kk = np.asarray(k, dtype=np.float64)[:, keep]
+    vv = np.asarray(v, dtype=np.float64)[:, keep].copy()
+    out_k = kk.copy()
+    moved = np.nonzero(delta != 0)[0]
+    if moved.size:
+        rot = rope_rotate(kk[:, moved], delta[moved][None, :, None], theta)
+        out_k[:, moved] = bf16_round(rot)
+    return out_k, vv, new_pos
+
+
+def gather_meta(arr, keep):
+    """Per-token metadata follows its token through compaction."""
+    return np.asarray(arr)[np.asarray(keep, dtype=np.int64)]
+
+
+# --------------------------------------------------------------------------------------
+# Renumber trigger and limit rule (PACE Sec. 3.2)
+# --------------------------------------------------------------------------------------
+
+def renumber_needed(next_pos, headroom, limit):
+    """Renumber when the next physical position comes within the headroom of the limit.
+    Reading: 'within h of L' means next_pos >= L - h."""
+    return next_pos >= limit - headroom
+
+
+def smallest_limit(budget, interval, chunk):
+    """Smallest power-of-two limit with L >= R_max + C, R_max = budget + interval."""
+    need = budget + interval + chunk
+    limit = 1
+    while limit < need:
+        limit *= 2
+    return limit
+
+
+def simulate_renumbers(session_tokens, budget, limit, headroom):
+    """Count renumbers in a session where eviction runs after every appended token.
+
+    Tokens arrive one at a time; the resident row is evicted back to the budget; the
+    trigger is checked after each eviction; a renumber moves the row to positions
+    0..n-1 and the next token continues right after it (PACE Sec. 3.2).
+    """
+    next_pos = 0
+    resident = 0
+    count = 0
+    for _ in range(session_tokens):
+        next_pos += 1
+        resident = min(resident + 1, budget)
+        if renumber_needed(next_pos, headroom, limit):
+            next_pos = resident
+            count += 1
+    return count
+
+
+# --------------------------------------------------------------------------------------
+# Whole pipeline on small inputs
+# --------------------------------------------------------------------------------------
+
+def score_step(q, k, *, policy, scale=None, region=None, base_prio=None, decay_rate=None,
+               rho=0.9, alpha=1.0, tau=0.01, dt_steps=1, ewma=None, clock=None,
+               accum=None, span_id=None, span_next_use=None, bonus_floor=50000.0,
+               pinned_regions=0, n_sink=0, n_recent=0, token_pinned=None, item_tokens=1):
+    """Score one eviction step: mass -> policy epilogue -> per-item score and pin flag.
+
+    policy 'memdecay' divides the mass by L*Hq*W ("averaged over heads and layers");
+    policy 'h2o' accumulates the summed mass.  Returns a dict of float64 arrays.
+    """
+    mass, lse = attention_mass(q, k, scale)
+    nl, w_len, hq, _ = np.asarray(q).shape
+    n = mass.shape[0]
+    bonus = None
+    if span_id is not None and span_next_use is not None:
+        bonus = token_bonus(span_id, foresight_bonus(span_next_use, bonus_floor))
+    out = {"mass": mass, "lse": lse}
+    if policy == "memdecay":
+        abar = mass / (nl * hq * w_len)
+        a, c, s = memdecay_update(abar, region, base_prio, decay_rate, rho, alpha, tau,
+                                  dt_steps, ewma, clock, bonus)
+        out.update(abar=abar, ewma=a, clock=c, token_score=s)
+    elif policy == "h2o":
+        acc, s = h2o_update(mass, accum if accum is not None else np.zeros(n), bonus)
+        out.update(accum=acc, token_score=s)
+    else:
+        raise ValueError(policy)
+    pin = pinned_tokens(n, region, pinned_regions, n_sink, n_recent, token_pinned)
+    out["token_pinned"] = pin
+    if item_tokens == 1:
+        out["item_score"] = out["token_score"]
+        out["item_pinned"] = pin
+    else:
+        out["item_score"] = page_mean(out["token_score"], item_tokens)
+        out["item_pinned"] = page_any(pin, item_tokens)
+    return out

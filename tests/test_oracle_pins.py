@@ -1,0 +1,520 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix (CPU only).
+
+Each test ties one oracle function to something other than itself: a value printed on
+a page (fixtures under tests/golden/), a closed form, an invariant, an independent
+library routine (torch's bf16 conversion, torch's scaled-dot-product attention, a
+Hugging-Face-style rotate-half RoPE, complex multiplication), or brute force.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from conftest import read_golden
+
+
+# ---------------------------------------------------------------------------------------
+# bf16 rounding
+# ---------------------------------------------------------------------------------------
+
+def test_bf16_round_matches_torch_rne():
+    g = torch.Generator().manual_seed(1)
+    x = torch.randn(200_000, generator=g) * torch.exp(torch.randn(200_000, generator=g) * 20)
+    # include subnormal-range and huge values, exact ties and their neighbours
+    ties = torch.tensor([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 2 ** -130 * 1.5,
+                         2 ** -133 * 0.5, 2 ** -133 * 1.5, 3.3895e38, -0.0, 0.0, 1e-45],
+                        dtype=torch.float32)
+    x = torch.cat([x.float(), ties])
+    ref = x.to(torch.bfloat16).float().double().numpy()
+    got = O.bf16_round(x.double().numpy())
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), (x.numpy()[~same][:5], got[~same][:5], ref[~same][:5])
+    # signed zero preserved
+    assert np.signbit(O.bf16_round(np.array([-0.0])))[0]
+
+
+def test_bf16_round_ties_to_even_by_hand():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: even mantissa is 1.0
+    assert O.bf16_round(np.array([1.0 + 2 ** -8]))[0] == 1.0
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6: even is 1 + 2^-6
+    assert O.bf16_round(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
+    # just above the tie rounds up
+    assert O.bf16_round(np.array([1.0 + 2 ** -8 + 2 ** -30]))[0] == 1.0 + 2 ** -7
+    # bit pattern round trip
+    v = O.bf16_round(np.array([1.5, -2.25, 3.0e-3]))
+    assert (O.bf16_from_bits(O.bf16_bits(v)) == v).all()
+
+
+# ---------------------------------------------------------------------------------------
+# Paged layout (ActKV Sec. 2.5)
+# ---------------------------------------------------------------------------------------
+
+def test_slot_map_actkv_example():
+    gd = read_golden("actkv_slot_map.txt")
+    slots = O.slot_map(list(gd["block_table"]), gd["page_size"], gd["n_tokens"])
+    assert tuple(slots) == gd["slots"]
+
+
+def test_gather_logical_follows_block_table():
+    rng = np.random.default_rng(3)
+    nl, pg, hk, d, n = 2, 4, 2, 3, 13
+    n_pages = -(-n // pg)
+    bt = rng.permutation(n_pages + 3)[:n_pages]
+    paged = rng.standard_normal((nl, n_pages + 3, pg, hk, d))
+    logical = O.gather_logical(paged, bt, pg, n)
+    for layer in range(nl):
+        for j in range(n):
+            assert (logical[layer, j] == paged[layer, bt[j // pg], j % pg]).all()
+    ident = O.gather_logical(paged, None, pg, n)
+    assert (ident[:, 5] == paged[:, 1, 1]).all()
+
+
+# ---------------------------------------------------------------------------------------
+# O1 attention mass
+# ---------------------------------------------------------------------------------------
+
+def _rand_qk(rng, nl, w, hq, hkv, d, n):
+    q = O.bf16_round(rng.standard_normal((nl, w, hq, d)))
+    k = O.bf16_round(rng.standard_normal((nl, n, hkv, d)))
+    return q, k
+
+
+@pytest.mark.parametrize("nl,w,hq,hkv,d,n", [(1, 4, 4, 2, 8, 37), (2, 3, 6, 2, 16, 20),
+                                              (1, 1, 2, 1, 4, 5), (2, 5, 8, 8, 8, 5)])
+def test_attention_mass_matches_torch_sdpa(nl, w, hq, hkv, d, n):
+    """Attention weights recovered from torch's SDPA with identity values (V = I gives
+    o = A), GQA via enable_gqa (query head h reads KV head h // G), causal window."""
+    rng = np.random.default_rng(nl * 100 + n)
+    q, k = _rand_qk(rng, nl, w, hq, hkv, d, n)
+    mass, lse = O.attention_mass(q, k)
+    qpos = n - w + np.arange(w)
+    mask = torch.from_numpy(np.arange(n)[None, :] <= qpos[:, None])
+    ref = np.zeros(n)
+    for layer in range(nl):
+        qt = torch.from_numpy(q[layer]).permute(1, 0, 2)[None]          # [1,Hq,W,D]
+        kt = torch.from_numpy(k[layer]).permute(1, 0, 2)[None]          # [1,Hkv,N,D]
+        vt = torch.eye(n, dtype=torch.float64)[None, None].expand(1, hkv, n, n).contiguous()
+        a = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, vt, attn_mask=mask, enable_gqa=True)                 # [1,Hq,W,N]
+        ref += a.sum(dim=(0, 1, 2)).numpy()
+    np.testing.assert_allclose(mass, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_mass_sums_to_row_count():
+    rng = np.random.default_rng(5)
+    q, k = _rand_qk(rng, 3, 7, 6, 3, 16, 50)
+    mass, _ = O.attention_mass(q, k)
+    assert abs(mass.sum() - 3 * 6 * 7) < 1e-11
+
+
+def test_attention_mass_equal_keys_closed_form():
+    """All keys equal: each query spreads 1/(visible count) over its visible keys."""
+    rng = np.random.default_rng(6)
+    nl, w, hq, hkv, d, n = 2, 4, 4, 2, 8, 11
+    q = rng.standard_normal((nl, w, hq, d))
+    k = np.broadcast_to(rng.standard_normal((1, 1, hkv, d)), (nl, n, hkv, d)).copy()
+    mass, _ = O.attention_mass(q, k)
+    expect = np.zeros(n)
+    for wi in range(w):
+        qi = n - w + wi
+        expect[: qi + 1] += nl * hq / (qi + 1)
+    np.testing.assert_allclose(mass, expect, rtol=1e-13)
+
+
+def test_attention_mass_planted_key_dominates():
+    rng = np.random.default_rng(7)
+    nl, w, hq, hkv, d, n = 1, 4, 4, 2, 16, 40
+    q, k = _rand_qk(rng, nl, w, hq, hkv, d, n)
+    for g in range(hkv):
+        k[0, 9, g] = 40.0 * q[0, :, 2 * g:2 * g + 2].sum(axis=(0, 1))
+    mass, _ = O.attention_mass(q, k)
+    assert mass.argmax() == 9 and mass[9] > 0.5 * nl * hq * w
+
+
+def test_attention_mass_kv_head_permutation_invariant():
+    rng = np.random.default_rng(8)
+    nl, w, hq, hkv, d, n = 2, 3, 6, 3, 8, 17
+    q, k = _rand_qk(rng, nl, w, hq, hkv, d, n)
+    perm = np.array([2, 0, 1])
+    g = hq // hkv
+    qperm = np.concatenate([q[:, :, p * g:(p + 1) * g] for p in perm], axis=2)
+    m1, _ = O.attention_mass(q, k)
+    m2, _ = O.attention_mass(qperm, k[:, :, perm])
+    np.testing.assert_allclose(m1, m2, rtol=1e-13)
+
+
+def test_lse_matches_logsumexp_scipy():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(9)
+    q, k = _rand_qk(rng, 1, 3, 2, 1, 8, 12)
+    _, lse = O.attention_mass(q, k)
+    for wi in range(3):
+        qi = 12 - 3 + wi
+        s = (q[0, wi, 1] @ k[0, : qi + 1, 0].T) / math.sqrt(8)
+        assert abs(lse[0, 1, wi] - logsumexp(s)) < 1e-12
+
+
+# ---------------------------------------------------------------------------------------
+# O2 MemDecay / H2O closed forms
+# ---------------------------------------------------------------------------------------
+
+def test_memdecay_idle_steps_closed_form():
+    rng = np.random.default_rng(10)
+    n = 50
+    region = rng.integers(0, 7, n)
+    b = rng.uniform(0, 2, 7)
+    lam = rng.uniform(0.004, 0.05, 7)
+    a0 = rng.uniform(0, 0.1, n)
+    c0 = rng.integers(0, 100, n)
+    rho, alpha, dt = 0.9, 1.3, 3
+    a, c = a0.copy(), c0.copy()
+    for _ in range(7):
+        a, c, s = O.memdecay_update(np.zeros(n), region, b, lam, rho, alpha, 0.01, dt, a, c)
+    np.testing.assert_allclose(a, rho ** 7 * a0, rtol=1e-13)
+    assert (c == c0 + 7 * dt).all()
+    np.testing.assert_allclose(s, b[region] * np.exp(-lam[region] * (c0 + 7 * dt))
+                               + alpha * rho ** 7 * a0, rtol=1e-13)
+
+
+def test_memdecay_constant_attention_fixed_point():
+    n = 5
+    region = np.arange(n)
+    b = np.linspace(0.2, 1.8, 7)
+    lam = np.full(7, 0.02)
+    cval = 0.3
+    a0 = np.array([0.0, 0.1, 0.5, 1.0, 2.0])
+    a, c = a0.copy(), np.full(n, 40)
+    rho = 0.8
+    for step in range(1, 30):
+        a, c, s = O.memdecay_update(np.full(n, cval), region, b, lam, rho, 2.0, 0.01, 1, a, c)
+        np.testing.assert_allclose(a, cval + rho ** step * (a0 - cval), rtol=1e-12)
+        assert (c == 0).all()
+    np.testing.assert_allclose(s, b[region] + 2.0 * (cval + rho ** 29 * (a0 - cval)), rtol=1e-12)
+
+
+def test_memdecay_half_life():
+    """t_1/2 = ln 2 / lambda: after one half-life the decay term is b/2 (MemDecay)."""
+    lam = math.log(2) / 64
+    _, _, s = O.memdecay_update(np.zeros(1), [0], [1.7] + [0] * 6, [lam] + [0] * 6,
+                                0.9, 0.0, 0.01, 64, np.zeros(1), np.zeros(1, dtype=np.int64))
+    assert abs(s[0] - 0.85) < 1e-15
+    gd = read_golden("memdecay_halflife.txt")
+    # the generator's lambda range spans the measured half-lives (system .. scratchpad)
+    lo, hi = 0.004, 0.05
+    assert math.log(2) / hi <= gd["scratchpad_halflife"][0]
+    assert math.log(2) / lo >= gd["system_halflife"][0]
+
+
+def test_memdecay_reset_is_strict_and_zero_clock():
+    tau = 0.01
+    abar = np.array([tau, np.nextafter(tau, 1), 0.0])
+    a, c, s = O.memdecay_update(abar, [1, 1, 1], [0, 0.5] + [0] * 5, [0, 0.1] + [0] * 5,
+                                0.5, 1.0, tau, 2, np.zeros(3), np.array([10, 10, 10]))
+    assert list(c) == [12, 0, 12]
+    # dt = 0 gives s = b + alpha * a
+    assert abs(s[1] - (0.5 + a[1])) < 1e-15
+
+
+def test_h2o_accumulates():
+    rng = np.random.default_rng(11)
+    masses = [rng.uniform(0, 3, 9) for _ in range(4)]
+    acc = np.zeros(9)
+    for m in masses:
+        acc, s = O.h2o_update(m, acc)
+    np.testing.assert_allclose(acc, np.sum(masses, axis=0), rtol=1e-14)
+    _, s2 = O.h2o_update(np.zeros(9), acc, bonus=np.full(9, 2.0))
+    np.testing.assert_allclose(s2, acc + 2.0)
+
+
+# ---------------------------------------------------------------------------------------
+# O3 foresight (ordering properties only; exact values are parity unpinned)
+# ---------------------------------------------------------------------------------------
+
+def test_foresight_dominance_and_soonest_first():
+    gd = read_golden("pace_numbers.txt")
+    floor = gd["foresight_floor"]
+    bon = O.foresight_bonus(np.array([0, 1, 2, 16, 1000]), floor)
+    assert bon[0] == 0
+    assert bon[1] > bon[2] > bon[3] > bon[4] >= floor
+    # every protected token outranks every unprotected one while unprotected attention
+    # stays below the floor (the pages' maxima were 14.6K and 25.1K)
+    unprot = np.array([0.0, gd["max_unprotected_1m"], gd["max_unprotected_2m"]])
+    assert (bon[1:].min() + 0.0) > unprot.max()
+
+
+# ---------------------------------------------------------------------------------------
+# pins / page aggregation
+# ---------------------------------------------------------------------------------------
+
+def test_pinned_rules_and_pages():
+    n = 37
+    region = np.array([0] * 5 + [3] * 20 + [5] * 12)
+    pin = O.pinned_tokens(n, region, pinned_regions=(1 << 0) | (1 << 5), n_sink=2, n_recent=3)
+    assert pin[:5].all() and not pin[5:25].any() and pin[25:].all()
+    pin2 = O.pinned_tokens(n, region, 0, n_sink=4, n_recent=2)
+    assert list(np.nonzero(pin2)[0]) == [0, 1, 2, 3, 35, 36]
+    s = np.arange(n, dtype=np.float64)
+    pm = O.page_mean(s, 16)
+    full = s[:32].reshape(2, 16).mean(axis=1)
+    np.testing.assert_allclose(pm[:2], full)
+    assert pm[2] == np.mean([32, 33, 34, 35, 36])
+    assert list(O.page_any(pin2, 16)) == [True, False, True]
+
+
+# ---------------------------------------------------------------------------------------
+# O4 selection
+# ---------------------------------------------------------------------------------------
+
+def _valid_by_definition(score, pinned, budget, kept):
+    """Characterisation: kept contains every pinned item, has size min(max(B,#pin), n),
+    and every kept unpinned item precedes every evicted unpinned item in the order
+    (score desc, index asc)."""
+    n = len(score)
+    kept = set(kept)
+    npin = int(sum(pinned))
+    if not all(i in kept for i in range(n) if pinned[i]):
+        return False
+    if len(kept) != min(n, max(budget, npin)):
+        return False
+    for i in kept:
+        if pinned[i]:
+            continue
+        for e in range(n):
+            if e in kept or pinned[e]:
+                continue
+            if not (score[i] > score[e] or (score[i] == score[e] and i < e)):
+                return False
+    return True
+
+
+def test_select_exhaustive_brute_force():
+    alphabet = [0.0, 0.5, 1.0]
+    count = 0
+    for n in range(1, 6):
+        for scores in itertools.product(alphabet, repeat=n):
+            for pmask in range(0, 1 << n, 3):
+                pinned = [(pmask >> i) & 1 for i in range(n)]
+                for budget in range(0, n + 1):
+                    kept, status = O.select_items(np.array(scores), np.array(pinned), budget)
+                    # exactly one subset satisfies the characterisation
+                    valid = [c for size in range(n + 1)
+                             for c in itertools.combinations(range(n), size)
+                             if _valid_by_definition(scores, pinned, budget, c)]
+                    assert len(valid) == 1
+                    assert list(kept) == list(valid[0])
+                    assert bool(status & O.STATUS_PINNED_OVER_BUDGET) == (sum(pinned) > budget)
+                    count += 1
+    assert count > 1000
+
+
+def test_select_properties_random():
+    for seed in range(5):
+        s = synth.scores(3000, seed=seed, alphabet=[0.1, 0.2, 0.3, 0.4] if seed % 2 else None)
+        pin = synth.pinned_mask(3000, seed=seed, frac=0.02).numpy().astype(bool)
+        budget = 500
+        kept, _ = O.select_items(s.double().numpy(), pin, budget)
+        assert len(kept) == budget
+        assert (np.diff(kept) > 0).all()
+        assert set(np.nonzero(pin)[0]) <= set(kept)
+        sv = s.double().numpy()
+        ev = np.setdiff1d(np.arange(3000), kept)
+        ev = ev[~pin[ev]]
+        kn = kept[~pin[kept]]
+        assert sv[kn].min() >= sv[ev].max()
+
+
+def test_select_nan_last_and_signed_zero():
+    s = np.array([np.nan, -0.0, 0.0, -1.0, np.nan, 2.0])
+    kept, status = O.select_items(s, None, 3)
+    assert list(kept) == [1, 2, 5] and status & O.STATUS_NAN_SCORE
+    kept, _ = O.select_items(s, None, 5)
+    assert list(kept) == [0, 1, 2, 3, 5]
+
+
+def test_expand_pages_partial_tail():
+    assert list(O.expand_items([0, 2], 4, 10)) == [0, 1, 2, 3, 8, 9]
+
+
+# ---------------------------------------------------------------------------------------
+# O5 Penelope
+# ---------------------------------------------------------------------------------------
+
+def test_penelope_illustrative_example():
+    gd = read_golden("penelope_cost.txt")
+    u = gd["linear_units"]
+    p, priv, free = gd["example_prefix"], gd["example_private"], gd["example_free"]
+    end = O.recompute_cost(p + priv - free, p + priv, u)
+    front = O.recompute_cost(p, p + free, u)
+    ratio = end / front
+    assert abs(ratio - gd["example_ratio_about"]) < 0.05
+    assert abs(ratio - 124551.5 / 54551.5) < 1e-12
+    # mean tokens-before of each choice, as the page states
+    assert abs((end / free - u) - gd["example_end_mean_before"]) < 1000
+    assert abs((front / free - u) - gd["example_front_mean_before"]) < 1000
+
+
+@pytest.mark.parametrize("ctx_k,key", [(8, "measure_8k_speedup"), (128, "measure_128k_speedup")])
+@pytest.mark.parametrize("with_append", [False, True])
+def test_penelope_measurement_within_4pct(ctx_k, key, with_append):
+    gd = read_golden("penelope_cost.txt")
+    u = gd["linear_units"]
+    n = ctx_k * 1024
+    e = int(round(gd["measure_frac"] * n))
+    start = gd["measure_start"]
+    add = O.recompute_cost(n, n + gd["measure_append"], u) if with_append else 0.0
+    end = O.recompute_cost(n - e, n, u) + add
+    front = O.recompute_cost(start, start + e, u) + add
+    assert abs(end / front / gd[key] - 1) < gd["measure_tolerance"]
+
+
+def test_penelope_segment_blocks():
+    assert O.segment_evict_len(131072, 16384, 39322, 16) == 39328
+    keep = O.select_segment(100, 10, 7, 4)
+    assert list(keep) == list(range(10)) + list(range(18, 100))
+    assert O.segment_evict_len(40, 30, 50, 16) == 10
+
+
+# ---------------------------------------------------------------------------------------
+# O6 re-rotation (PACE Sec. 3.2, Proposition 1)
+# ---------------------------------------------------------------------------------------
+
+def _rope_hf(x, pos, theta):
+    """Model-side rotary embedding written the Hugging Face way (rotate_half)."""
+    x = torch.from_numpy(np.asarray(x, dtype=np.float64))
+    d = x.shape[-1]
+    inv = 1.0 / (theta ** (torch.arange(0, d, 2, dtype=torch.float64) / d))
+    freqs = torch.as_tensor(pos, dtype=torch.float64)[..., None] * inv
+    emb = torch.cat([freqs, freqs], dim=-1)
+    rot = torch.cat([-x[..., d // 2:], x[..., : d // 2]], dim=-1)
+    return (x * emb.cos() + rot * emb.sin()).numpy()
+
+
+@pytest.mark.parametrize("theta", [1e4, 1e6])
+def test_proposition1_exact_rerotation(theta):
+    rng = np.random.default_rng(12)
+    k0 = rng.standard_normal((20, 128))
+    p = rng.integers(0, 1_000_000, 20)
+    qn = rng.integers(0, 8192, 20)
+    cached = _rope_hf(k0, p, theta)
+    re = O.rope_rotate(cached, qn - p, theta)
+    want = _rope_hf(k0, qn, theta)
+    np.testing.assert_allclose(re, want, atol=1e-9)
+
+
+def test_rotation_is_complex_multiplication():
+    rng = np.random.default_rng(13)
+    k = rng.standard_normal((5, 128))
+    delta = np.array([1, -3, 1000, -39328, 77777])
+    out = O.rope_rotate(k, delta, 1e6)
+    z = k[:, :64] + 1j * k[:, 64:]
+    inv = np.power(1e6, -np.arange(64) * 2.0 / 128)
+    zr = z * np.exp(1j * delta[:, None] * inv)
+    np.testing.assert_allclose(out[:, :64], zr.real, atol=1e-12)
+    np.testing.assert_allclose(out[:, 64:], zr.imag, atol=1e-12)
+
+
+def test_rotation_composition_shift_invariance_norms():
+    rng = np.random.default_rng(14)
+    x, y = rng.standard_normal((2, 128))
+    a, b, s = 1234, 99, 50_000
+    r1 = O.rope_rotate(O.rope_rotate(x, a, 1e6), b - a, 1e6)
+    np.testing.assert_allclose(r1, O.rope_rotate(x, b, 1e6), atol=1e-11)
+    d1 = O.rope_rotate(x, a, 1e6) @ O.rope_rotate(y, b, 1e6)
+    d2 = O.rope_rotate(x, a + s, 1e6) @ O.rope_rotate(y, b + s, 1e6)
+    assert abs(d1 - d2) < 1e-10
+    rx = O.rope_rotate(x, 777, 1e6)
+    np.testing.assert_allclose(rx[:64] ** 2 + rx[64:] ** 2, x[:64] ** 2 + x[64:] ** 2, rtol=1e-12)
+
+
+def test_compact_rerope_definition():
+    rng = np.random.default_rng(15)
+    nl, n, hk, d = 2, 30, 2, 128
+    k = O.bf16_round(rng.standard_normal((nl, n, hk, d)))
+    v = O.bf16_round(rng.standard_normal((nl, n, hk, d)))
+    keep = np.array([0, 1, 2, 7, 8, 20, 29])
+    old_pos = np.arange(n) + 100
+    old_pos[:3] = [0, 1, 2]                       # first three keep their place: delta 0
+    k2, v2, newp = O.compact_rerope(k, v, keep, old_pos, 0, 1e6)
+    assert list(newp) == list(range(len(keep)))
+    assert (v2 == v[:, keep]).all()
+    assert (k2[:, :3] == k[:, :3]).all()          # delta 0: verbatim
+    for r, j in enumerate(keep):
+        want = O.bf16_round(O.rope_rotate(k[:, j], r - old_pos[j], 1e6))
+        assert (k2[:, r] == want).all()
+    # two roundings at most through bf16 storage: round-trip to a far position and back
+    k_far = O.bf16_round(O.rope_rotate(k[:, 5], 100_000, 1e6))
+    back = O.bf16_round(O.rope_rotate(k_far, -100_000, 1e6))
+    # each bf16 rounding moves a pair by at most 2^-9 * sqrt(2) of its norm; rotation
+    # preserves that norm, so two roundings stay within 2^-8 * sqrt(2) of it
+    x, y = k[:, 5, :, :64], k[:, 5, :, 64:]
+    norm = np.sqrt(x ** 2 + y ** 2)
+    err = np.sqrt((back[..., :64] - x) ** 2 + (back[..., 64:] - y) ** 2)
+    assert (err <= 2 ** -8 * math.sqrt(2) * norm + 1e-30).all()
+    # no renumbering keeps positions and every key
+    k3, _, p3 = O.compact_rerope(k, v, keep, old_pos, -1, 1e6)
+    assert (p3 == old_pos[keep]).all() and (k3 == k[:, keep]).all()
+
+
+def test_renumbered_rotary_distance_bounded():
+    gd = read_golden("pace_numbers.txt")
+    keep = np.sort(np.random.default_rng(16).choice(100_000, gd["budget"], replace=False))
+    newp = O.renumbered_positions(len(keep), 0, keep)
+    # a query continuing right after the row sees every kept token within the limit
+    assert (len(keep) - newp).max() <= gd["limit"]
+    assert (np.diff(newp) == 1).all()
+
+
+# ---------------------------------------------------------------------------------------
+# Limit rule and renumber trigger (PACE Sec. 3.2)
+# ---------------------------------------------------------------------------------------
+
+def test_limit_rule():
+    gd = read_golden("pace_numbers.txt")
+    for interval in (1, 512, 2048):
+        assert O.smallest_limit(gd["budget"], interval, gd["prefill_chunk"]) == gd["limit"]
+    assert O.smallest_limit(gd["budget"], 2049, gd["prefill_chunk"]) == 16384
+
+
+def test_renumber_counts_match_pages():
+    """With headroom 2,048 (reading) the per-token trigger gives the pages' counts."""
+    gd = read_golden("pace_numbers.txt")
+    for tokens, key in [(100_000, "renumbers_100k"), (1_000_000, "renumbers_1m"),
+                        (2_000_000, "renumbers_2m")]:
+        got = O.simulate_renumbers(tokens, gd["budget"], gd["limit"], 2048)
+        assert abs(got / gd[key] - 1) < 0.035, (tokens, got)
+
+
+def test_kv_footprint_arithmetic():
+    gd = read_golden("pace_numbers.txt")
+    w = synth.workload(3)
+    assert w.kv_bytes_per_token == gd["kv_bytes_per_token"] == 144 * 1024
+    assert abs(w.kv_bytes_per_token * 100_000 / 1e9 - gd["kv_gb_100k"]) < 0.05
+    assert abs(w.kv_bytes_per_token * 1_000_000 / 1e9 - gd["kv_gb_1m"]) < 0.6
+
+
+# ---------------------------------------------------------------------------------------
+# PACE inactive equivalence (Sec. 5.7): no renumbering, no bonus == plain H2O
+# ---------------------------------------------------------------------------------------
+
+def test_inactive_equivalence_is_plain_h2o():
+    w = synth.workload(3, n_layers=2, n_tokens=200, n_q_heads=4, n_kv_heads=2, window=8,
+                       n_spans=0, budget_tokens=40)
+    k, v, _ = synth.kv_cache(w, seed=2)
+    q = synth.window_queries(w, seed=2)
+    kl = O.gather_logical(k.float().double().numpy(), None, 16, w.n_tokens)
+    vl = O.gather_logical(v.float().double().numpy(), None, 16, w.n_tokens)
+    out = O.score_step(q.float().double().numpy(), kl, policy="h2o", n_sink=4, n_recent=8)
+    kept, _ = O.select_items(out["item_score"], out["item_pinned"], w.budget_items)
+    k2, v2, p2 = O.compact_rerope(kl, vl, kept, np.arange(w.n_tokens), -1, w.rope_theta)
+    mass, _ = O.attention_mass(q.float().double().numpy(), kl)
+    pin = np.zeros(w.n_tokens, bool)
+    pin[:4] = pin[-8:] = True
+    order = sorted([i for i in range(w.n_tokens) if not pin[i]], key=lambda i: (-mass[i], i))
+    plain = sorted(list(np.nonzero(pin)[0]) + order[: w.budget_items - pin.sum()])
+    assert list(kept) == plain
+    assert (k2 == kl[:, plain]).all() and (v2 == vl[:, plain]).all()
+    assert list(p2) == plain
