@@ -1,0 +1,274 @@
+"""Python binding of libkvscore (MI355X / gfx950 KV-cache scoring, selection,
+compaction and exact re-rotation).
+
+This module only marshals arguments: it turns torch tensors into device pointers and
+sizes, passes the current HIP stream, and raises on error codes.  Every step of the
+path runs in the HIP kernels of libkvscore.so; there is no fallback.  The functions
+carry the names of the C entry points declared in include/kvscore.h, whose comments
+document arguments, layouts, ownership and errors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvscore.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvscore.h")
+
+KV_OK = 0
+KV_EINVAL = -1
+KV_EUNSUPPORTED = -2
+KV_EWORKSPACE = -3
+KV_EHIP = -4
+KV_ELIMIT = -5
+KV_STATUS_PINNED_OVER_BUDGET = 1
+KV_STATUS_NAN_SCORE = 2
+KV_STATUS_KEEP_OVERFLOW = 4
+KV_POLICY_MEMDECAY = 0
+KV_POLICY_H2O = 1
+KV_MAX_META = 8
+
+
+class KvError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {kv_strerror(code)} (code {code})")
+
+
+class KvCacheDesc(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("n_layers", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("n_tokens", ctypes.c_int64), ("layer_stride", ctypes.c_int64),
+                ("page_stride", ctypes.c_int64), ("block_table", ctypes.c_void_p)]
+
+
+class KvMetaDesc(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p),
+                ("elem_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class KvScoreParams(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("n_q_heads", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("policy", ctypes.c_int32), ("item_tokens", ctypes.c_int32),
+                ("dt_steps", ctypes.c_int32), ("lse_in", ctypes.c_void_p),
+                ("region", ctypes.c_void_p), ("base_prio", ctypes.c_void_p),
+                ("decay_rate", ctypes.c_void_p), ("n_regions", ctypes.c_int32),
+                ("rho", ctypes.c_float), ("alpha", ctypes.c_float), ("tau", ctypes.c_float),
+                ("ewma", ctypes.c_void_p), ("clock", ctypes.c_void_p),
+                ("accum", ctypes.c_void_p), ("span_id", ctypes.c_void_p),
+                ("span_next_use", ctypes.c_void_p), ("n_spans", ctypes.c_int32),
+                ("bonus_floor", ctypes.c_float), ("pinned_regions", ctypes.c_uint32),
+                ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
+                ("token_pinned", ctypes.c_void_p), ("mass", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("token_score", ctypes.c_void_p),
+                ("item_score", ctypes.c_void_p), ("item_pinned", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkvscore.so (built in place by compaction_kv_score_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m compaction_kv_score_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        P = ctypes.POINTER
+        sigs = {
+            "kv_abi_version": (i32, []),
+            "kv_strerror": (ctypes.c_char_p, [i32]),
+            "kv_renumber_needed": (i32, [i64, i32, i32]),
+            "kv_score_workspace_size": (i32, [P(KvCacheDesc), P(KvScoreParams), P(sz)]),
+            "kv_score": (i32, [P(KvCacheDesc), P(KvScoreParams), vp, sz, vp]),
+            "kv_select_workspace_size": (i32, [i64, P(sz)]),
+            "kv_select": (i32, [vp, vp, i64, i32, i64, i64, vp, i64, vp, vp, vp, sz, vp]),
+            "kv_select_segment": (i32, [i64, i64, i64, i32, vp, i64, vp, P(i64), P(i64), vp]),
+            "kv_compact_rerope": (i32, [P(KvCacheDesc), P(KvCacheDesc), vp, vp, i64, vp, vp, i32,
+                                        ctypes.c_double, i32, P(KvMetaDesc), i32, vp]),
+            "kv_compact_segment_inplace": (i32, [P(KvCacheDesc), i64, i64, vp, i32, ctypes.c_double,
+                                                 i32, P(KvMetaDesc), i32, vp]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/kvscore.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"^\s*(?:int32_t|const char \*)\s*(kv_\w+)\s*\(", text, re.M)))
+
+
+# ------------------------------------------------------------------------- marshalling
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor or None")
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libkvscore must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libkvscore must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(code: int, where: str):
+    if code < 0:
+        raise KvError(code, where)
+    return code
+
+
+def kv_abi_version() -> int:
+    return lib().kv_abi_version()
+
+
+def kv_strerror(code: int) -> str:
+    return lib().kv_strerror(code).decode()
+
+
+def kv_renumber_needed(next_pos: int, headroom: int, limit: int) -> bool:
+    return bool(lib().kv_renumber_needed(next_pos, headroom, limit))
+
+
+class PagedCache:
+    """A paged KV cache row held in two torch tensors of shape
+    [layers][physical pages][page_size][kv_heads][head_dim] (bf16, contiguous) plus an
+    optional int32 block table; n_tokens logical tokens are in use."""
+
+    def __init__(self, k, v, n_tokens, block_table=None):
+        if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16 or k.shape != v.shape:
+            raise ValueError("k and v must be bf16 tensors of the same shape")
+        if k.dim() != 5:
+            raise ValueError("k and v must be [layers][pages][page_size][kv_heads][head_dim]")
+        self.k, self.v, self.block_table = k, v, block_table
+        self.n_tokens = int(n_tokens)
+        nl, npg, ps, hk, d = k.shape
+        self.n_layers, self.n_phys_pages, self.page_size, self.n_kv_heads, self.head_dim = nl, npg, ps, hk, d
+        if block_table is not None and block_table.dtype != torch.int32:
+            raise ValueError("block_table must be int32")
+
+    def desc(self) -> KvCacheDesc:
+        nl, npg, ps, hk, d = self.k.shape
+        return KvCacheDesc(_ptr(self.k), _ptr(self.v), nl, hk, d, ps, self.n_tokens,
+                           npg * ps * hk * d, ps * hk * d, _ptr(self.block_table))
+
+
+def _meta_array(meta):
+    meta = list(meta or [])
+    if len(meta) > KV_MAX_META:
+        raise ValueError("too many metadata arrays")
+    arr = (KvMetaDesc * max(1, len(meta)))()
+    for i, (src, dst) in enumerate(meta):
+        arr[i] = KvMetaDesc(_ptr(src), _ptr(dst), src.element_size(), 0)
+    return arr, len(meta)
+
+
+def _score_params(q, *, policy, window, item_tokens, scale=0.0, dt_steps=1, lse_in=None,
+                  region=None, base_prio=None, decay_rate=None, rho=0.9, alpha=1.0, tau=0.01,
+                  ewma=None, clock=None, accum=None, span_id=None, span_next_use=None,
+                  bonus_floor=50000.0, pinned_regions=0, n_sink=0, n_recent=0,
+                  token_pinned=None, mass=None, lse=None, token_score=None, item_score=None,
+                  item_pinned=None):
+    pol = {"memdecay": KV_POLICY_MEMDECAY, "h2o": KV_POLICY_H2O}.get(policy, policy)
+    n_regions = int(base_prio.numel()) if base_prio is not None else 0
+    n_spans = int(span_next_use.numel()) if span_next_use is not None else 0
+    return KvScoreParams(
+        _ptr(q), int(q.shape[2]), int(window), float(scale), int(pol), int(item_tokens),
+        int(dt_steps), _ptr(lse_in), _ptr(region), _ptr(base_prio), _ptr(decay_rate), n_regions,
+        float(rho), float(alpha), float(tau), _ptr(ewma), _ptr(clock), _ptr(accum),
+        _ptr(span_id), _ptr(span_next_use), n_spans, float(bonus_floor), int(pinned_regions),
+        int(n_sink), int(n_recent), _ptr(token_pinned), _ptr(mass), _ptr(lse),
+        _ptr(token_score), _ptr(item_score), _ptr(item_pinned))
+
+
+def kv_score_workspace_size(cache: PagedCache, q, **kw) -> int:
+    p = _score_params(q, **kw)
+    n = ctypes.c_size_t(0)
+    _check(lib().kv_score_workspace_size(ctypes.byref(cache.desc()), ctypes.byref(p), ctypes.byref(n)),
+           "kv_score_workspace_size")
+    return n.value
+
+
+def kv_score(cache: PagedCache, q, workspace=None, **kw):
+    """Score the cache row (see kv_score in include/kvscore.h); keyword arguments are the
+    fields of kv_score_params (tensors on the device, scalars as Python numbers)."""
+    p = _score_params(q, **kw)
+    d = cache.desc()
+    if workspace is None:
+        workspace = torch.empty(kv_score_workspace_size(cache, q, **kw), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().kv_score(ctypes.byref(d), ctypes.byref(p), _ptr(workspace), workspace.numel(),
+                          _stream(q.device)), "kv_score")
+    return workspace
+
+
+def kv_select_workspace_size(n_items: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().kv_select_workspace_size(int(n_items), ctypes.byref(n)), "kv_select_workspace_size")
+    return n.value
+
+
+def kv_select(item_score, item_pinned, item_tokens, n_tokens, budget_items, keep_tokens, n_keep,
+              status=None, workspace=None):
+    """Budget selection (see kv_select in include/kvscore.h)."""
+    n_items = int(item_score.numel())
+    if workspace is None:
+        workspace = torch.empty(kv_select_workspace_size(n_items), dtype=torch.uint8,
+                                device=item_score.device)
+    _check(lib().kv_select(_ptr(item_score), _ptr(item_pinned), n_items, int(item_tokens),
+                           int(n_tokens), int(budget_items), _ptr(keep_tokens), keep_tokens.numel(),
+                           _ptr(n_keep), _ptr(status), _ptr(workspace), workspace.numel(),
+                           _stream(item_score.device)), "kv_select")
+    return workspace
+
+
+def kv_select_segment(n_tokens, prefix_len, evict_tokens, block, keep_tokens=None, n_keep_dev=None):
+    """Penelope segment (see kv_select_segment); returns (n_keep, evict_len)."""
+    nk, el = ctypes.c_int64(0), ctypes.c_int64(0)
+    dev = keep_tokens.device if keep_tokens is not None else (
+        n_keep_dev.device if n_keep_dev is not None else None)
+    stream = _stream(dev) if dev is not None else None
+    _check(lib().kv_select_segment(int(n_tokens), int(prefix_len), int(evict_tokens), int(block),
+                                   _ptr(keep_tokens),
+                                   keep_tokens.numel() if keep_tokens is not None else 0,
+                                   _ptr(n_keep_dev), ctypes.byref(nk), ctypes.byref(el), stream),
+           "kv_select_segment")
+    return nk.value, el.value
+
+
+def kv_compact_rerope(src: PagedCache, dst: PagedCache, keep_tokens, n_keep, max_keep, old_pos,
+                      new_pos=None, renumber_base=-1, rope_theta=1e6, limit=0, meta=None):
+    """Gather + exact re-rotation (see kv_compact_rerope); meta is a list of (src, dst)
+    tensor pairs gathered with the keep list."""
+    arr, n_meta = _meta_array(meta)
+    _check(lib().kv_compact_rerope(ctypes.byref(src.desc()), ctypes.byref(dst.desc()),
+                                   _ptr(keep_tokens), _ptr(n_keep), int(max_keep), _ptr(old_pos),
+                                   _ptr(new_pos), int(renumber_base), float(rope_theta), int(limit),
+                                   arr, n_meta, _stream(src.k.device)), "kv_compact_rerope")
+
+
+def kv_compact_segment_inplace(cache: PagedCache, prefix_len, evict_len, pos, renumber_base=-1,
+                               rope_theta=1e6, limit=0, meta=None):
+    """In-place segment eviction (see kv_compact_segment_inplace); meta is a list of
+    tensors moved in place."""
+    arr, n_meta = _meta_array([(m, m) for m in (meta or [])])
+    _check(lib().kv_compact_segment_inplace(ctypes.byref(cache.desc()), int(prefix_len), int(evict_len),
+                                            _ptr(pos), int(renumber_base), float(rope_theta), int(limit),
+                                            arr, n_meta, _stream(cache.k.device)),
+           "kv_compact_segment_inplace")

@@ -1,0 +1,419 @@
+// C ABI of libkvscore: argument validation, workspace layout and launch order.
+// The entry points and their contracts are documented in include/kvscore.h.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "kv_internal.h"
+
+using namespace kvs;
+
+namespace {
+
+thread_local char g_err_text[512];
+
+int32_t hip_fail(hipError_t e) {
+  snprintf(g_err_text, sizeof(g_err_text), "HIP call failed: %s", hipGetErrorString(e));
+  return KV_EHIP;
+}
+
+// gfx950 check, cached per device ordinal (immutable facts, safe to share).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int32_t check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return KV_EUNSUPPORTED;
+  int v = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    v = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_ok[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? KV_OK : KV_EUNSUPPORTED;
+}
+
+int log2_exact(int64_t v) {
+  if (v <= 0 || (v & (v - 1)) != 0) return -1;
+  int s = 0;
+  while ((1LL << s) < v) ++s;
+  return s;
+}
+
+int32_t check_cache(const kv_cache_desc* c) {
+  if (!c || !c->k || !c->v) return KV_EINVAL;
+  if (c->n_layers <= 0 || c->n_kv_heads <= 0 || c->n_tokens <= 0) return KV_EINVAL;
+  if (c->n_tokens > 0x7FFFFFFFLL) return KV_EINVAL;
+  if (c->head_dim != kHeadDim) return KV_EUNSUPPORTED;
+  const int ps = log2_exact(c->page_size);
+  if (ps < 0 || ps > 10) return KV_EUNSUPPORTED;
+  const int64_t slot = (int64_t)c->n_kv_heads * c->head_dim;
+  if (c->page_stride < slot * c->page_size) return KV_EINVAL;
+  if (c->n_layers > 1 && c->layer_stride < c->page_stride) return KV_EINVAL;
+  if (((uintptr_t)c->k | (uintptr_t)c->v) & 15) return KV_EINVAL;
+  if ((c->page_stride | c->layer_stride) & 7) return KV_EINVAL;  // keep 16-byte alignment
+  return KV_OK;
+}
+
+struct ScoreLayout {
+  int rows, group, n_chunks, chunk;
+  size_t off_lse_part, off_lse2, off_mass, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int32_t score_layout(const kv_cache_desc* c, const kv_score_params* p, ScoreLayout* L) {
+  int32_t rc = check_cache(c);
+  if (rc) return rc;
+  if (!p) return KV_EINVAL;
+  if (p->n_q_heads <= 0 || p->n_q_heads % c->n_kv_heads) return KV_EINVAL;
+  if (p->window <= 0 || p->window > c->n_tokens) return KV_EINVAL;
+  const int group = p->n_q_heads / c->n_kv_heads;
+  const int64_t rows = (int64_t)group * p->window;
+  if (rows > kMaxRows) return KV_EUNSUPPORTED;
+  // chunk: a multiple of the 64-key tile, large enough to amortise the query load and
+  // small enough that the grid has thousands of workgroups
+  const int64_t units = (int64_t)c->n_layers * c->n_kv_heads;
+  int64_t chunk = 4096;
+  while (chunk > 256 && units * ((c->n_tokens + chunk - 1) / chunk) < 2048) chunk >>= 1;
+  L->rows = (int)rows;
+  L->group = group;
+  L->chunk = (int)chunk;
+  L->n_chunks = (int)((c->n_tokens + chunk - 1) / chunk);
+  size_t off = 0;
+  L->off_lse_part = off;
+  off = align256(off + (size_t)units * L->n_chunks * rows * sizeof(float2));
+  L->off_lse2 = off;
+  off = align256(off + (size_t)units * rows * sizeof(float));
+  L->off_mass = off;
+  off = align256(off + (size_t)units * c->n_tokens * sizeof(float));
+  L->total = off;
+  return KV_OK;
+}
+
+int32_t check_meta(const kv_meta_desc* meta, int32_t n_meta, MetaSet* out) {
+  memset(out, 0, sizeof(*out));
+  if (n_meta < 0 || n_meta > KV_MAX_META) return KV_EINVAL;
+  if (n_meta > 0 && !meta) return KV_EINVAL;
+  for (int i = 0; i < n_meta; ++i) {
+    const int b = meta[i].elem_bytes;
+    if (!meta[i].src || !meta[i].dst || (b != 1 && b != 2 && b != 4 && b != 8)) return KV_EINVAL;
+    out->src[i] = meta[i].src;
+    out->dst[i] = meta[i].dst;
+    out->elem_bytes[i] = b;
+  }
+  out->n = n_meta;
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kv_abi_version(void) { return KV_ABI_VERSION; }
+
+const char* kv_strerror(int32_t code) {
+  switch (code) {
+    case KV_OK:
+      return "ok";
+    case KV_EINVAL:
+      return "invalid argument (null pointer, size, stride or shape)";
+    case KV_EUNSUPPORTED:
+      return "unsupported (head_dim != 128, page size not a power of two <= 1024, "
+             "more than 512 rows per KV head, page items above 256 tokens, or not a gfx950 device)";
+    case KV_EWORKSPACE:
+      return "workspace too small";
+    case KV_EHIP:
+      return g_err_text[0] ? g_err_text : "HIP call failed";
+    case KV_ELIMIT:
+      return "renumbered row does not fit under the position limit";
+    default:
+      return "unknown kvscore status";
+  }
+}
+
+int32_t kv_renumber_needed(int64_t next_pos, int32_t headroom, int32_t limit) {
+  return next_pos >= (int64_t)limit - headroom ? 1 : 0;
+}
+
+int32_t kv_score_workspace_size(const kv_cache_desc* cache, const kv_score_params* p,
+                                size_t* bytes) {
+  if (!bytes) return KV_EINVAL;
+  ScoreLayout L;
+  const int32_t rc = score_layout(cache, p, &L);
+  if (rc) return rc;
+  *bytes = L.total;
+  return KV_OK;
+}
+
+int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  ScoreLayout L;
+  int32_t rc = score_layout(c, p, &L);
+  if (rc) return rc;
+  if (!p->q || !p->item_score || !p->item_pinned) return KV_EINVAL;
+  if (p->item_tokens != 1 && p->item_tokens != c->page_size) return KV_EINVAL;
+  const int item_shift = log2_exact(p->item_tokens);
+  if (item_shift > 8) return KV_EUNSUPPORTED;
+  if (p->policy == KV_POLICY_MEMDECAY) {
+    if (!p->ewma || !p->clock || !p->region || !p->base_prio || !p->decay_rate) return KV_EINVAL;
+    if (p->n_regions <= 0 || p->n_regions > 32) return KV_EINVAL;
+  } else if (p->policy == KV_POLICY_H2O) {
+    if (!p->accum) return KV_EINVAL;
+  } else {
+    return KV_EINVAL;
+  }
+  if (p->region && (p->n_regions <= 0 || p->n_regions > 32)) return KV_EINVAL;
+  if (p->span_id && (!p->span_next_use || p->n_spans <= 0)) return KV_EINVAL;
+  if (p->n_sink < 0 || p->n_recent < 0 || p->dt_steps < 0) return KV_EINVAL;
+  if (!ws || ws_bytes < L.total) return KV_EWORKSPACE;
+  if ((rc = check_device())) return rc;
+
+  char* w = (char*)ws;
+  const float scale = p->scale != 0.f ? p->scale : 1.0f / sqrtf((float)kHeadDim);
+  const float c2 = (float)((double)scale * 1.4426950408889634);
+  const int n_lg = c->n_layers * c->n_kv_heads;
+  hipError_t e;
+
+  ScoreArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.k = (const uint16_t*)c->k;
+  sa.layer_stride = c->layer_stride;
+  sa.page_stride = c->page_stride;
+  sa.block_table = c->block_table;
+  sa.n_layers = c->n_layers;
+  sa.n_kv_heads = c->n_kv_heads;
+  sa.page_shift = log2_exact(c->page_size);
+  sa.n_tokens = c->n_tokens;
+  sa.q = (const uint16_t*)p->q;
+  sa.n_q_heads = p->n_q_heads;
+  sa.window = p->window;
+  sa.group = L.group;
+  sa.rows = L.rows;
+  sa.c = c2;
+  sa.chunk = L.chunk;
+  sa.n_chunks = L.n_chunks;
+  sa.lse_part = (float2*)(w + L.off_lse_part);
+  sa.lse2 = (const float*)(w + L.off_lse2);
+  sa.mass_part = (float*)(w + L.off_mass);
+
+  if (!p->lse_in) {
+    if ((e = launch_score_pass(sa, false, stream)) != hipSuccess) return hip_fail(e);
+  }
+  CombineArgs ca;
+  ca.lse_part = sa.lse_part;
+  ca.n_chunks = L.n_chunks;
+  ca.rows = L.rows;
+  ca.n_kv_heads = c->n_kv_heads;
+  ca.n_q_heads = p->n_q_heads;
+  ca.group = L.group;
+  ca.window = p->window;
+  ca.n_lg = n_lg;
+  ca.c = c2;
+  ca.lse_in = p->lse_in;
+  ca.lse2 = (float*)(w + L.off_lse2);
+  ca.lse_out = p->lse;
+  if ((e = launch_lse_combine(ca, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = launch_score_pass(sa, true, stream)) != hipSuccess) return hip_fail(e);
+
+  EpilogueArgs ea;
+  memset(&ea, 0, sizeof(ea));
+  ea.mass_part = sa.mass_part;
+  ea.n_parts = n_lg;
+  ea.n_tokens = c->n_tokens;
+  ea.mass_norm = 1.0 / ((double)c->n_layers * p->n_q_heads * p->window);
+  ea.policy = p->policy;
+  ea.item_shift = item_shift;
+  ea.dt_steps = p->dt_steps;
+  ea.region = p->region;
+  ea.base_prio = p->base_prio;
+  ea.decay_rate = p->decay_rate;
+  ea.n_regions = p->n_regions;
+  ea.rho = p->rho;
+  ea.alpha = p->alpha;
+  ea.tau = p->tau;
+  ea.ewma = p->ewma;
+  ea.clock = p->clock;
+  ea.accum = p->accum;
+  ea.span_id = p->span_id;
+  ea.span_next_use = p->span_next_use;
+  ea.n_spans = p->n_spans;
+  ea.bonus_floor = p->bonus_floor;
+  ea.pinned_regions = p->pinned_regions;
+  ea.n_sink = p->n_sink;
+  ea.n_recent = p->n_recent;
+  ea.token_pinned = p->token_pinned;
+  ea.mass = p->mass;
+  ea.token_score = p->token_score;
+  ea.item_score = p->item_score;
+  ea.item_pinned = p->item_pinned;
+  if ((e = launch_epilogue(ea, stream)) != hipSuccess) return hip_fail(e);
+  return KV_OK;
+}
+
+int32_t kv_select_workspace_size(int64_t n_items, size_t* bytes) {
+  if (!bytes || n_items <= 0) return KV_EINVAL;
+  *bytes = select_workspace_bytes(n_items);
+  return KV_OK;
+}
+
+int32_t kv_select(const float* item_score, const uint8_t* item_pinned, int64_t n_items,
+                  int32_t item_tokens, int64_t n_tokens, int64_t budget_items, int32_t* keep_tokens,
+                  int64_t keep_capacity, int64_t* n_keep, uint32_t* status, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  if (!item_score || !keep_tokens || !n_keep || n_items <= 0 || item_tokens <= 0) return KV_EINVAL;
+  if (n_tokens <= 0 || n_tokens > 0x7FFFFFFFLL || budget_items < 0 || keep_capacity < 0)
+    return KV_EINVAL;
+  if ((n_tokens + item_tokens - 1) / item_tokens != n_items) return KV_EINVAL;
+  if (!ws || ws_bytes < select_workspace_bytes(n_items)) return KV_EWORKSPACE;
+  int32_t rc = check_device();
+  if (rc) return rc;
+  SelectArgs a;
+  memset(&a, 0, sizeof(a));
+  a.score = item_score;
+  a.pinned = item_pinned;
+  a.n_items = n_items;
+  a.item_tokens = item_tokens;
+  a.n_tokens = n_tokens;
+  a.budget = budget_items;
+  a.keep = keep_tokens;
+  a.keep_capacity = keep_capacity;
+  a.n_keep = n_keep;
+  a.status = status;
+  a.n_blocks = select_blocks(n_items);
+  a.per_block = (n_items + a.n_blocks - 1) / a.n_blocks;
+  char* w = (char*)ws;
+  a.st = (SelectState*)w;
+  a.hist = (uint32_t*)(w + 256);
+  a.counts = (int64_t*)(w + 256 + (size_t)a.n_blocks * 256 * sizeof(uint32_t));
+  const hipError_t e = launch_select(a, stream);
+  return e == hipSuccess ? KV_OK : hip_fail(e);
+}
+
+int32_t kv_select_segment(int64_t n_tokens, int64_t prefix_len, int64_t evict_tokens, int32_t block,
+                          int32_t* keep_tokens, int64_t keep_capacity, int64_t* n_keep_dev,
+                          int64_t* n_keep_host, int64_t* evict_len_host, hipStream_t stream) {
+  if (n_tokens <= 0 || n_tokens > 0x7FFFFFFFLL || prefix_len < 0 || prefix_len > n_tokens ||
+      evict_tokens < 0 || block <= 0)
+    return KV_EINVAL;
+  int64_t e = (evict_tokens + block - 1) / block * block;
+  if (e > n_tokens - prefix_len) e = n_tokens - prefix_len;
+  const int64_t n_keep = n_tokens - e;
+  if (n_keep_host) *n_keep_host = n_keep;
+  if (evict_len_host) *evict_len_host = e;
+  if (!keep_tokens && !n_keep_dev) return KV_OK;
+  if (keep_tokens && keep_capacity < n_keep) return KV_EINVAL;
+  int32_t rc = check_device();
+  if (rc) return rc;
+  const hipError_t he = launch_segment_keep(n_tokens, prefix_len, e, keep_tokens, keep_capacity,
+                                            n_keep_dev, n_keep, stream);
+  return he == hipSuccess ? KV_OK : hip_fail(he);
+}
+
+static void fill_compact_common(CompactArgs* a, const kv_cache_desc* src, const kv_cache_desc* dst,
+                                int32_t renumber_base, double rope_theta) {
+  a->src_k = (const uint16_t*)src->k;
+  a->src_v = (const uint16_t*)src->v;
+  a->src_layer_stride = src->layer_stride;
+  a->src_page_stride = src->page_stride;
+  a->src_bt = src->block_table;
+  a->dst_k = (uint16_t*)dst->k;
+  a->dst_v = (uint16_t*)dst->v;
+  a->dst_layer_stride = dst->layer_stride;
+  a->dst_page_stride = dst->page_stride;
+  a->dst_bt = dst->block_table;
+  a->n_layers = src->n_layers;
+  a->n_kv_heads = src->n_kv_heads;
+  a->src_page_shift = log2_exact(src->page_size);
+  a->dst_page_shift = log2_exact(dst->page_size);
+  a->renumber_base = renumber_base;
+  a->log_theta = log(rope_theta);
+}
+
+int32_t kv_compact_rerope(const kv_cache_desc* src, const kv_cache_desc* dst,
+                          const int32_t* keep_tokens, const int64_t* n_keep, int64_t max_keep,
+                          const int32_t* old_pos, int32_t* new_pos, int32_t renumber_base,
+                          double rope_theta, int32_t limit, const kv_meta_desc* meta,
+                          int32_t n_meta, hipStream_t stream) {
+  int32_t rc = check_cache(src);
+  if (rc) return rc;
+  if ((rc = check_cache(dst))) return rc;
+  if (!keep_tokens || !old_pos || max_keep < 0) return KV_EINVAL;
+  if (dst->n_layers != src->n_layers || dst->n_kv_heads != src->n_kv_heads) return KV_EINVAL;
+  if (max_keep > dst->n_tokens || max_keep > src->n_tokens) return KV_EINVAL;
+  if (src->k == dst->k || src->v == dst->v) return KV_EINVAL;
+  if (!(rope_theta > 1.0)) return KV_EINVAL;
+  if (renumber_base >= 0 && limit > 0 && (int64_t)renumber_base + max_keep > limit) return KV_ELIMIT;
+  MetaSet ms;
+  if ((rc = check_meta(meta, n_meta, &ms))) return rc;
+  if (max_keep == 0) return KV_OK;
+  if ((rc = check_device())) return rc;
+  CompactArgs a;
+  memset(&a, 0, sizeof(a));
+  fill_compact_common(&a, src, dst, renumber_base, rope_theta);
+  a.keep = keep_tokens;
+  a.rank0 = 0;
+  a.rank1 = max_keep;
+  a.n_keep = n_keep;
+  a.old_pos = old_pos;
+  a.new_pos = new_pos;
+  a.meta = ms;
+  hipError_t e = launch_compact(a, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if (new_pos || ms.n) {
+    if ((e = launch_gather_meta(a, stream)) != hipSuccess) return hip_fail(e);
+  }
+  return KV_OK;
+}
+
+int32_t kv_compact_segment_inplace(const kv_cache_desc* cache, int64_t prefix_len, int64_t evict_len,
+                                   int32_t* pos, int32_t renumber_base, double rope_theta,
+                                   int32_t limit, const kv_meta_desc* meta, int32_t n_meta,
+                                   hipStream_t stream) {
+  int32_t rc = check_cache(cache);
+  if (rc) return rc;
+  const int64_t N = cache->n_tokens;
+  if (!pos || prefix_len < 0 || evict_len < 0 || prefix_len + evict_len > N) return KV_EINVAL;
+  if (!(rope_theta > 1.0)) return KV_EINVAL;
+  const int64_t n_keep = N - evict_len;
+  if (renumber_base >= 0 && limit > 0 && (int64_t)renumber_base + n_keep > limit) return KV_ELIMIT;
+  MetaSet ms;
+  if ((rc = check_meta(meta, n_meta, &ms))) return rc;
+  for (int i = 0; i < ms.n; ++i)
+    if (ms.src[i] != ms.dst[i]) return KV_EINVAL;
+  if ((rc = check_device())) return rc;
+  CompactArgs a;
+  memset(&a, 0, sizeof(a));
+  fill_compact_common(&a, cache, cache, renumber_base, rope_theta);
+  a.keep = nullptr;
+  a.split = prefix_len;
+  a.shift = evict_len;
+  a.n_keep = nullptr;
+  a.old_pos = pos;
+  a.new_pos = pos;
+  a.meta = ms;
+  hipError_t e;
+  // prefix: stays in place (re-rotated only if its positions change)
+  a.rank0 = 0;
+  a.rank1 = prefix_len;
+  if ((e = launch_compact(a, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = launch_gather_meta(a, stream)) != hipSuccess) return hip_fail(e);
+  if (evict_len == 0) return KV_OK;
+  // suffix: rounds of at most evict_len ranks; round k reads [r0+E, r1+E) and writes
+  // [r0, r1), disjoint because r1 - r0 <= E; later rounds read only beyond r1 + E.
+  for (int64_t r0 = prefix_len; r0 < n_keep; r0 += evict_len) {
+    a.rank0 = r0;
+    a.rank1 = r0 + evict_len < n_keep ? r0 + evict_len : n_keep;
+    if ((e = launch_compact(a, stream)) != hipSuccess) return hip_fail(e);
+    if ((e = launch_gather_meta(a, stream)) != hipSuccess) return hip_fail(e);
+  }
+  return KV_OK;
+}
+
+}  // extern "C"

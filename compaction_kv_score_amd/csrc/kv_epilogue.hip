@@ -1,0 +1,108 @@
+// Per-token policy epilogue of kv_score.
+//
+// Reduces the per-(layer, KV head) attention-mass partials of one token in a fixed
+// order (float64 accumulation), then applies the retention policy:
+//   MemDecay (MemDecay, Method): Abar = mass / (L*Hq*W) ("averaged over heads and
+//     layers"); a <- rho*a + (1-rho)*Abar; the decay clock resets when Abar > tau and
+//     otherwise advances by dt_steps; s = b_r * exp(-lambda_r * clock) + alpha * a.
+//   H2O (PACE Sec. 2, heavy hitters): acc <- acc + mass; s = acc.
+// plus PACE's foresight bonus (Sec. 3.1; floor as in Sec. 5.7 and 7) for tokens whose
+// span a future step reads, and the pinning rules (MemDecay pinned regions, PACE
+// Table 1 sinks and recent window).  In page mode a page's score is the mean over the
+// tokens it holds (MemDecay's S_p) and a page is pinned when any token is.
+#include "kv_internal.h"
+
+namespace kvs {
+
+namespace {
+
+constexpr int kEpiThreads = 256;
+
+__global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
+  __shared__ float s_sum[kEpiThreads];
+  __shared__ int s_cnt[kEpiThreads];
+  __shared__ int s_pin[kEpiThreads];
+  const int tid = threadIdx.x;
+  const int64_t N = a.n_tokens;
+  const int64_t i = (int64_t)blockIdx.x * kEpiThreads + tid;
+  const bool valid = i < N;
+
+  float score = 0.f;
+  int pinned = 0;
+  if (valid) {
+    double msum = 0.0;
+    const float* mp = a.mass_part + i;
+    for (int p = 0; p < a.n_parts; ++p) msum += (double)mp[(int64_t)p * N];
+    const float mass = (float)msum;
+    if (a.mass) a.mass[i] = mass;
+
+    float bonus = 0.f;
+    if (a.span_id) {
+      const int sid = a.span_id[i];
+      if (sid >= 0 && sid < a.n_spans) {
+        const int d = a.span_next_use[sid];
+        if (d >= 1) bonus = a.bonus_floor * (1.0f + 1.0f / (float)d);
+      }
+    }
+    int r = 0;
+    if (a.region) {
+      r = a.region[i];
+      if (r >= a.n_regions) r = a.n_regions - 1;
+    }
+    if (a.policy == KV_POLICY_MEMDECAY) {
+      const float abar = (float)(msum * a.mass_norm);
+      const float ew = a.rho * a.ewma[i] + (1.0f - a.rho) * abar;
+      const int32_t clk = abar > a.tau ? 0 : a.clock[i] + a.dt_steps;
+      a.ewma[i] = ew;
+      a.clock[i] = clk;
+      const float b = a.base_prio ? a.base_prio[r] : 0.f;
+      const float lam = a.decay_rate ? a.decay_rate[r] : 0.f;
+      score = b * expf(-lam * (float)clk) + a.alpha * ew + bonus;
+    } else {
+      const float acc = a.accum[i] + mass;
+      a.accum[i] = acc;
+      score = acc + bonus;
+    }
+    if (a.token_score) a.token_score[i] = score;
+    pinned = (i < a.n_sink) || (i >= N - a.n_recent) ||
+             (a.region && ((a.pinned_regions >> r) & 1u)) ||
+             (a.token_pinned && a.token_pinned[i] != 0);
+  }
+
+  if (a.item_shift == 0) {
+    if (valid) {
+      a.item_score[i] = score;
+      a.item_pinned[i] = (uint8_t)pinned;
+    }
+    return;
+  }
+  // page mode: pairwise reduction inside each aligned segment of item_tokens threads
+  s_sum[tid] = valid ? score : 0.f;
+  s_cnt[tid] = valid ? 1 : 0;
+  s_pin[tid] = pinned;
+  __syncthreads();
+  const int it = 1 << a.item_shift;
+  for (int stride = 1; stride < it; stride <<= 1) {
+    if ((tid & (2 * stride - 1)) == 0) {
+      s_sum[tid] += s_sum[tid + stride];
+      s_cnt[tid] += s_cnt[tid + stride];
+      s_pin[tid] |= s_pin[tid + stride];
+    }
+    __syncthreads();
+  }
+  if ((tid & (it - 1)) == 0 && s_cnt[tid] > 0) {
+    const int64_t page = i >> a.item_shift;
+    a.item_score[page] = s_sum[tid] / (float)s_cnt[tid];
+    a.item_pinned[page] = (uint8_t)(s_pin[tid] != 0);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_epilogue(const EpilogueArgs& a, hipStream_t s) {
+  const int64_t blocks = (a.n_tokens + kEpiThreads - 1) / kEpiThreads;
+  hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)blocks), dim3(kEpiThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

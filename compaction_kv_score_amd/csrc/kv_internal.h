@@ -1,0 +1,153 @@
+// Internal declarations shared by the HIP translation units of libkvscore.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvscore.h"
+
+namespace kvs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 128;
+constexpr int kTile = 64;          // keys per scoring tile
+constexpr int kLdsStride = 136;    // bf16 elements per key row in LDS (128 + 8 padding)
+constexpr int kMaxRows = 512;      // G*W rows per (layer, KV head): 8 waves x 64 rows
+
+// Physical element offset of token j's row start (head 0, dim 0) inside one layer.
+__device__ __forceinline__ int64_t token_offset(int64_t j, int page_shift, int64_t page_stride,
+                                                const int32_t* __restrict__ block_table,
+                                                int slot_stride) {
+  const int64_t page = j >> page_shift;
+  const int64_t slot = j & ((1LL << page_shift) - 1);
+  const int64_t phys = block_table ? (int64_t)block_table[page] : page;
+  return phys * page_stride + slot * slot_stride;
+}
+
+// ---------------------------------------------------------------- scoring kernels
+struct ScoreArgs {
+  const uint16_t* k;            // bf16 bits
+  int64_t layer_stride, page_stride;
+  const int32_t* block_table;
+  int n_layers, n_kv_heads, page_shift;
+  int64_t n_tokens;
+  const uint16_t* q;            // bf16 bits [L][W][Hq][128]
+  int n_q_heads, window, group, rows;
+  float c;                      // scale * log2(e)
+  int chunk, n_chunks;
+  float2* lse_part;             // [L*Hkv][n_chunks][rows] (max, sum) in log2 units
+  const float* lse2;            // [L*Hkv][rows] log2-unit LSE (pass 2 input)
+  float* mass_part;             // [L*Hkv][N]
+};
+
+hipError_t launch_score_pass(const ScoreArgs& a, bool pass2, hipStream_t s);
+
+struct CombineArgs {
+  const float2* lse_part;
+  int n_chunks, rows, n_kv_heads, n_q_heads, group, window, n_lg;
+  float c;
+  const float* lse_in;          // optional natural-log LSE input [L][Hq][W]
+  float* lse2;                  // [L*Hkv][rows]
+  float* lse_out;               // optional [L][Hq][W]
+};
+hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t s);
+
+struct EpilogueArgs {
+  const float* mass_part;       // [n_parts][N]
+  int n_parts;
+  int64_t n_tokens;
+  double mass_norm;             // 1 / (L*Hq*W)
+  int policy, item_shift;       // item_tokens = 1 << item_shift
+  int dt_steps;
+  const uint8_t* region;
+  const float* base_prio;
+  const float* decay_rate;
+  int n_regions;
+  float rho, alpha, tau;
+  float* ewma;
+  int32_t* clock;
+  float* accum;
+  const int32_t* span_id;
+  const int32_t* span_next_use;
+  int n_spans;
+  float bonus_floor;
+  uint32_t pinned_regions;
+  int64_t n_sink, n_recent;
+  const uint8_t* token_pinned;
+  float* mass;
+  float* token_score;
+  float* item_score;
+  uint8_t* item_pinned;
+};
+hipError_t launch_epilogue(const EpilogueArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- selection kernels
+struct SelectState {               // lives in the select workspace
+  uint32_t prefix;               // key bits fixed so far
+  uint32_t mask;
+  int64_t k_rem;                 // items still to take among candidates
+  int64_t n_pinned;
+  int64_t n_cand;
+  uint32_t mode;                 // 0 radix, 1 keep all unpinned, 2 keep none
+  uint32_t nan_seen;
+  uint32_t ticket;
+  uint32_t pad;
+};
+struct SelectArgs {
+  const float* score;
+  const uint8_t* pinned;
+  int64_t n_items;
+  int item_tokens;
+  int64_t n_tokens;
+  int64_t budget;
+  int32_t* keep;
+  int64_t keep_capacity;
+  int64_t* n_keep;
+  uint32_t* status;
+  SelectState* st;
+  uint32_t* hist;                // [n_blocks][256]
+  int64_t* counts;               // [n_blocks][2]
+  int n_blocks;
+  int64_t per_block;             // items per block
+};
+int select_blocks(int64_t n_items);
+size_t select_workspace_bytes(int64_t n_items);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_segment_keep(int64_t n_tokens, int64_t prefix, int64_t evict, int32_t* keep,
+                               int64_t capacity, int64_t* n_keep_dev, int64_t n_keep,
+                               hipStream_t s);
+
+// ---------------------------------------------------------------- compaction kernels
+struct MetaSet {
+  const void* src[KV_MAX_META];
+  void* dst[KV_MAX_META];
+  int elem_bytes[KV_MAX_META];
+  int n;
+};
+struct CompactArgs {
+  const uint16_t* src_k;
+  const uint16_t* src_v;
+  int64_t src_layer_stride, src_page_stride;
+  const int32_t* src_bt;
+  uint16_t* dst_k;
+  uint16_t* dst_v;
+  int64_t dst_layer_stride, dst_page_stride;
+  const int32_t* dst_bt;
+  int n_layers, n_kv_heads, src_page_shift, dst_page_shift;
+  // rank -> source token: keep[r] when keep != nullptr, else r (+ shift when r >= split)
+  const int32_t* keep;
+  int64_t split, shift;
+  int64_t rank0, rank1;          // ranks handled by this launch
+  const int64_t* n_keep;         // device count (nullable); ranks >= it are skipped
+  const int32_t* old_pos;        // [N] indexed by source token
+  int32_t* new_pos;              // [ranks] (nullable)
+  int32_t renumber_base;
+  double log_theta;              // ln(rope_theta)
+  MetaSet meta;
+};
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+hipError_t launch_gather_meta(const CompactArgs& a, hipStream_t s);
+
+}  // namespace kvs

@@ -1,0 +1,313 @@
+// Budget selection on gfx950: deterministic radix select with an index tie-break.
+//
+// MemDecay (Method) keeps pinned tokens unconditionally and fills the rest of a fixed
+// budget by score; PACE (Table 1) always keeps 4 sinks and 128 recent tokens; ActKV
+// (Sec. 3.3) turns scores and a budget into a keep mask.  Here the kept set is
+//   pinned  U  the best (budget - #pinned) unpinned items
+// in the total order (score descending, index ascending; -0 == +0; NaN last), and it is
+// emitted as an ascending list of token indices so that compaction preserves order.
+//
+// Steps, all on the device (no host synchronisation; n_keep stays in device memory):
+//   1. four histogram passes over 8-bit digits of an order-preserving uint32 key, most
+//      significant first.  Each block builds a private LDS histogram of the candidates
+//      that still match the digits fixed so far; the last block to finish (atomic
+//      ticket) sums the block histograms in block order and fixes the next digit.
+//      Afterwards T is the key of the K-th best unpinned item and k_rem is how many
+//      items with key == T are still to be taken (the lowest indices win).
+//   2. a count pass: per block, items kept for sure and items equal to T.
+//   3. an emit pass: every block derives its output offset from the counts of the
+//      blocks before it, then walks its items in index order with wavefront ballots and
+//      an LDS scan across waves, and writes the kept token indices.
+#include "kv_internal.h"
+
+namespace kvs {
+
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelMaxBlocks = 64;
+constexpr int kWaves = kSelThreads / 64;
+
+__device__ __forceinline__ uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (s != s) return 0u;                 // NaN orders after every number
+  if (u == 0x80000000u) u = 0u;          // -0.0 counts as +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ bool item_pinned(const SelectArgs& a, int64_t i) {
+  return a.pinned != nullptr && a.pinned[i] != 0;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, int pass) {
+  __shared__ uint32_t h[256];
+  __shared__ uint32_t s_npin, s_nan;
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  for (int b = tid; b < 256; b += kSelThreads) h[b] = 0;
+  if (tid == 0) {
+    s_npin = 0;
+    s_nan = 0;
+  }
+  __syncthreads();
+
+  const uint32_t mode = pass == 0 ? 0u : a.st->mode;
+  if (mode != 0) return;  // decided without a radix pass (uniform across the grid)
+  const uint32_t prefix = pass == 0 ? 0u : a.st->prefix;
+  const uint32_t mask = pass == 0 ? 0u : a.st->mask;
+  const int shift = 24 - 8 * pass;
+
+  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
+  const int64_t end = begin + a.per_block < a.n_items ? begin + a.per_block : a.n_items;
+  uint32_t npin = 0, nan_seen = 0;
+  for (int64_t i = begin + tid; i < end; i += kSelThreads) {
+    if (item_pinned(a, i)) {
+      ++npin;
+      continue;
+    }
+    const float s = a.score[i];
+    nan_seen |= (s != s) ? 1u : 0u;
+    const uint32_t key = order_key(s);
+    if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+  }
+  if (pass == 0) {
+    if (npin) atomicAdd(&s_npin, npin);
+    if (nan_seen) atomicOr(&s_nan, 1u);
+  }
+  __syncthreads();
+  for (int b = tid; b < 256; b += kSelThreads) a.hist[(int64_t)blockIdx.x * 256 + b] = h[b];
+  if (pass == 0 && tid == 0) {
+    a.counts[2 * blockIdx.x] = s_npin;
+    a.counts[2 * blockIdx.x + 1] = s_nan;
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.st->ticket, 1u) == (uint32_t)gridDim.x - 1u;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  // ---- last block: global histogram in block order, then fix this pass's digit
+  for (int b = tid; b < 256; b += kSelThreads) {
+    uint32_t tot = 0;
+    for (int blk = 0; blk < (int)gridDim.x; ++blk)
+      tot += __atomic_load_n(&a.hist[(int64_t)blk * 256 + b], __ATOMIC_RELAXED);
+    h[b] = tot;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    SelectState st = *a.st;
+    if (pass == 0) {
+      int64_t n_pin = 0;
+      uint32_t nan_any = 0;
+      for (int blk = 0; blk < (int)gridDim.x; ++blk) {
+        n_pin += __atomic_load_n(&a.counts[2 * blk], __ATOMIC_RELAXED);
+        nan_any |= (uint32_t)__atomic_load_n(&a.counts[2 * blk + 1], __ATOMIC_RELAXED);
+      }
+      st.n_pinned = n_pin;
+      st.n_cand = a.n_items - n_pin;
+      st.nan_seen = nan_any;
+      st.prefix = 0;
+      st.mask = 0;
+      const int64_t k = a.budget - n_pin;
+      st.k_rem = k;
+      st.mode = k >= st.n_cand ? 1u : (k <= 0 ? 2u : 0u);
+    }
+    if (st.mode == 0) {
+      int64_t above = 0;
+      int digit = 0;
+      for (int b = 255; b >= 0; --b) {
+        const int64_t cnt = h[b];
+        if (above + cnt >= st.k_rem) {
+          digit = b;
+          break;
+        }
+        above += cnt;
+      }
+      st.k_rem -= above;
+      st.prefix |= (uint32_t)digit << shift;
+      st.mask |= 255u << shift;
+    }
+    st.ticket = 0;
+    *a.st = st;
+    __threadfence();
+  }
+}
+
+// Per block: items kept for sure (pinned, or key above T, or everything in mode 1) and
+// unpinned items whose key equals T (ties, resolved by index in the emit pass).
+__global__ __launch_bounds__(kSelThreads) void select_count_kernel(SelectArgs a) {
+  __shared__ uint32_t s_def, s_eq;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s_def = 0;
+    s_eq = 0;
+  }
+  __syncthreads();
+  const uint32_t mode = a.st->mode;
+  const uint32_t T = a.st->prefix;
+  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
+  const int64_t end = begin + a.per_block < a.n_items ? begin + a.per_block : a.n_items;
+  uint32_t def = 0, eq = 0;
+  for (int64_t i = begin + tid; i < end; i += kSelThreads) {
+    if (item_pinned(a, i) || mode == 1u) {
+      ++def;
+      continue;
+    }
+    if (mode == 2u) continue;
+    const uint32_t key = order_key(a.score[i]);
+    def += key > T;
+    eq += key == T;
+  }
+  if (def) atomicAdd(&s_def, def);
+  if (eq) atomicAdd(&s_eq, eq);
+  __syncthreads();
+  if (tid == 0) {
+    a.counts[2 * blockIdx.x] = s_def;
+    a.counts[2 * blockIdx.x + 1] = s_eq;
+  }
+}
+
+// Exclusive prefix of a per-thread flag over the block, in thread order; returns the
+// prefix and writes the block total.  Wavefront ballots inside waves, LDS across them.
+__device__ __forceinline__ uint32_t block_scan(bool flag, uint32_t* s_wave, uint32_t& total) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(flag);
+  const uint64_t below = lane == 0 ? 0ull : (bal & (~0ull >> (64 - lane)));
+  const uint32_t in_wave = (uint32_t)__popcll(below);
+  if (lane == 0) s_wave[wv] = (uint32_t)__popcll(bal);
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t c = s_wave[w];
+    before += w < wv ? c : 0u;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return before + in_wave;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) {
+  __shared__ uint32_t s_wave[kWaves];
+  __shared__ int64_t s_kept_before, s_eq_before;
+  __shared__ int s_last_kept;
+  const int tid = threadIdx.x;
+  const uint32_t mode = a.st->mode;
+  const uint32_t T = a.st->prefix;
+  const int64_t k_rem = mode == 0u ? a.st->k_rem : 0;
+  if (tid == 0) {
+    int64_t kept = 0, eqb = 0;
+    for (int b = 0; b < (int)blockIdx.x; ++b) {
+      const int64_t def = a.counts[2 * b];
+      const int64_t eq = a.counts[2 * b + 1];
+      int64_t take = k_rem - eqb;
+      take = take < 0 ? 0 : (take > eq ? eq : take);
+      kept += def + take;
+      eqb += eq;
+    }
+    s_kept_before = kept;
+    s_eq_before = eqb;
+    s_last_kept = 0;
+  }
+  __syncthreads();
+  int64_t kept_before = s_kept_before;
+  int64_t eq_before = s_eq_before;
+  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
+  const int64_t end = begin + a.per_block < a.n_items ? begin + a.per_block : a.n_items;
+  const int it = a.item_tokens;
+  for (int64_t base = begin; base < end; base += kSelThreads) {
+    const int64_t i = base + tid;
+    const bool valid = i < end;
+    bool def = false, eq = false;
+    if (valid) {
+      if (item_pinned(a, i) || mode == 1u) {
+        def = true;
+      } else if (mode == 0u) {
+        const uint32_t key = order_key(a.score[i]);
+        def = key > T;
+        eq = key == T;
+      }
+    }
+    uint32_t eq_total;
+    const uint32_t eq_rank = block_scan(eq, s_wave, eq_total);
+    const bool kept = def || (eq && eq_before + (int64_t)eq_rank < k_rem);
+    uint32_t kept_total;
+    const uint32_t out_rank = block_scan(kept, s_wave, kept_total);
+    if (kept) {
+      const int64_t out = (kept_before + out_rank) * it;
+      const int64_t t0 = i * it;
+      const int64_t t1 = t0 + it < a.n_tokens ? t0 + it : a.n_tokens;
+      for (int64_t t = t0; t < t1; ++t) {
+        const int64_t o = out + (t - t0);
+        if (o < a.keep_capacity) a.keep[o] = (int32_t)t;
+      }
+      if (i == a.n_items - 1) s_last_kept = 1;
+    }
+    kept_before += kept_total;
+    eq_before += eq_total;
+  }
+  __syncthreads();
+  if (blockIdx.x == gridDim.x - 1 && tid == 0) {
+    // the last item may be a partial page holding n_tokens - (n_items-1)*it tokens
+    int64_t n_tok = kept_before * it;
+    if (s_last_kept) n_tok -= (int64_t)a.n_items * it - a.n_tokens;
+    *a.n_keep = n_tok;
+    uint32_t status = 0;
+    if (a.st->nan_seen) status |= KV_STATUS_NAN_SCORE;
+    if (a.st->n_pinned > a.budget) status |= KV_STATUS_PINNED_OVER_BUDGET;
+    if (n_tok > a.keep_capacity) status |= KV_STATUS_KEEP_OVERFLOW;
+    if (a.status) *a.status = status;
+  }
+}
+
+__global__ __launch_bounds__(256) void segment_keep_kernel(int64_t prefix, int64_t evict,
+                                                           int32_t* keep, int64_t n_write,
+                                                           int64_t* n_keep_dev, int64_t n_keep) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r == 0 && n_keep_dev) *n_keep_dev = n_keep;
+  if (keep && r < n_write) keep[r] = (int32_t)(r < prefix ? r : r + evict);
+}
+
+}  // namespace
+
+int select_blocks(int64_t n_items) {
+  int64_t b = (n_items + 4095) / 4096;
+  if (b < 1) b = 1;
+  if (b > kSelMaxBlocks) b = kSelMaxBlocks;
+  return (int)b;
+}
+
+size_t select_workspace_bytes(int64_t n_items) {
+  const int nb = select_blocks(n_items);
+  return 256 + (size_t)nb * 256 * sizeof(uint32_t) + (size_t)nb * 2 * sizeof(int64_t);
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+  hipError_t e = hipMemsetAsync(a.st, 0, sizeof(SelectState), s);
+  if (e != hipSuccess) return e;
+  const dim3 grid(a.n_blocks), block(kSelThreads);
+  for (int pass = 0; pass < 4; ++pass) {
+    hipLaunchKernelGGL(select_hist_kernel, grid, block, 0, s, a, pass);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(select_count_kernel, grid, block, 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(select_emit_kernel, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_keep(int64_t n_tokens, int64_t prefix, int64_t evict, int32_t* keep,
+                               int64_t capacity, int64_t* n_keep_dev, int64_t n_keep,
+                               hipStream_t s) {
+  (void)n_tokens;
+  const int64_t n_write = keep ? (n_keep < capacity ? n_keep : capacity) : 0;
+  const int64_t n = n_write > 1 ? n_write : 1;
+  hipLaunchKernelGGL(segment_keep_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     prefix, evict, keep, n_write, n_keep_dev, n_keep);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

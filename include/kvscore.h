@@ -1,0 +1,246 @@
+/*
+ * kvscore.h -- C ABI of the MI355X (gfx950) KV-cache scoring / selection / compaction
+ * library.
+ *
+ * The library implements, for one sequence row of a paged bf16 KV cache, the three
+ * primitives that ActKV ("ActKV: Efficient LLM Agents through Action-Guided KV Cache
+ * Management", Sec. 3.3) names for every score-based compression method,
+ *     AttnScore <- CalAttn(q, K),  KeepMask <- Eviction(AttnScore, Budget),
+ *     KV <- Compaction(KV, KeepMask),
+ * plus PACE's bounded-position renumbering ("PACE: Keeping the Right Tokens in the KV
+ * Cache Is Not Enough for Long-Horizon LLM Agents", Sec. 3.2, Proposition 1).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers owned by the caller unless marked "host".
+ *   - The library never allocates device memory and keeps no mutable global state;
+ *     scratch space is a caller-provided workspace sized by the *_workspace_size call.
+ *   - Work is enqueued asynchronously on the caller's stream; outputs are valid once the
+ *     stream has reached that point.  Calls on different streams are independent as
+ *     long as their buffers (workspaces included) do not overlap.
+ *   - Errors are returned as int32 codes (KV_OK = 0, negative = error, positive =
+ *     warning); nothing is enqueued when an error is returned for bad arguments.
+ *     kv_strerror() describes a code.  Conditions that only the device can see (NaN
+ *     scores, more pinned items than the budget) are reported in a device status word.
+ */
+#ifndef KVSCORE_H
+#define KVSCORE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KV_ABI_VERSION 1
+
+/* return codes */
+#define KV_OK 0
+#define KV_EINVAL (-1)        /* null pointer, bad size or stride, W > N, Hq % Hkv != 0 */
+#define KV_EUNSUPPORTED (-2)  /* head_dim != 128, page size not a power of two <= 1024,
+                                 G*W > 512 rows, or the current device is not gfx950 */
+#define KV_EWORKSPACE (-3)    /* workspace smaller than *_workspace_size reported */
+#define KV_EHIP (-4)          /* a HIP call failed; kv_strerror appends its message */
+#define KV_ELIMIT (-5)        /* renumbered row does not fit under the position limit */
+
+/* bits of the device status word written by kv_select */
+#define KV_STATUS_PINNED_OVER_BUDGET 1u /* pinned items alone exceed the budget: all of
+                                           them are kept (MemDecay keeps pinned tokens
+                                           unconditionally) and n_keep > budget */
+#define KV_STATUS_NAN_SCORE 2u          /* some score was NaN; NaN orders after numbers */
+#define KV_STATUS_KEEP_OVERFLOW 4u      /* keep list larger than keep_capacity; only the
+                                           first keep_capacity entries were written */
+
+/*
+ * One sequence row of a paged KV cache, all layers (ActKV Sec. 2.5: PagedKVCache
+ * [2, B, BS, H, D] with a block table mapping logical token positions to blocks).
+ * Element d of KV head h of logical token j in layer l lives at
+ *     base + l*layer_stride + phys(j/page_size)*page_stride
+ *          + (j%page_size)*n_kv_heads*head_dim + h*head_dim + d        (bf16 elements)
+ * with phys(p) = block_table[p], or p when block_table is NULL.  k and v may share
+ * one allocation (set v = k + offset).  All strides are in elements.
+ */
+typedef struct kv_cache_desc {
+  void *k;                    /* bf16 keys (post-RoPE, as the model cached them) */
+  void *v;                    /* bf16 values */
+  int32_t n_layers;
+  int32_t n_kv_heads;
+  int32_t head_dim;           /* must be 128 */
+  int32_t page_size;          /* power of two, 1..1024 */
+  int64_t n_tokens;           /* N: logical tokens in the row */
+  int64_t layer_stride;       /* elements between layers */
+  int64_t page_stride;        /* elements between physical pages; >= page_size*Hkv*D */
+  const int32_t *block_table; /* device [ceil(N/page_size)] or NULL (identity) */
+} kv_cache_desc;
+
+/* Metadata array that travels with its token through compaction:
+ * dst[r] = src[keep[r]] for element size elem_bytes (1, 2, 4 or 8). */
+typedef struct kv_meta_desc {
+  const void *src;
+  void *dst;
+  int32_t elem_bytes;
+  int32_t reserved;
+} kv_meta_desc;
+
+#define KV_MAX_META 8
+
+#define KV_POLICY_MEMDECAY 0 /* MemDecay region-decay score */
+#define KV_POLICY_H2O 1      /* H2O accumulated attention (PACE's base policy) */
+
+/*
+ * kv_score parameters.
+ *
+ * Attention mass (MemDecay, Method: windowed mean attention mass averaged over heads
+ * and layers; ActKV Sec. 2.3 / 7.1: A = exp(q.k - LSE); PACE Sec. 2: SnapKV window):
+ * the W window queries are the last W tokens of the row.  For layer l, query head h
+ * (KV head h / (Hq/Hkv)) and window query w at position N-W+w,
+ *     s_j = scale * <q[l][w][h], k[l][j][h/G]>  for j <= N-W+w,
+ *     LSE = log sum_j exp(s_j),  mass_j = sum_{l,h,w} exp(s_j - LSE).
+ *
+ * Policy epilogue, per token i:
+ *   MEMDECAY (MemDecay, Method):  Abar = mass / (L*Hq*W);
+ *       ewma <- rho*ewma + (1-rho)*Abar;  clock <- (Abar > tau) ? 0 : clock + dt_steps;
+ *       s = base_prio[r]*exp(-decay_rate[r]*clock) + alpha*ewma + bonus
+ *   H2O (PACE Sec. 2):  accum <- accum + mass;  s = accum + bonus
+ * Foresight bonus (PACE Sec. 3.1 and 7): bonus = bonus_floor*(1 + 1/d) for the token's
+ * span when d = span_next_use[span_id[i]] >= 1, else 0 (d = steps until the soonest
+ * future step that reads the span).
+ * Pinned tokens (MemDecay pinned regions; PACE Table 1 sinks and recent window): a token
+ * is pinned if its region bit is set in pinned_regions, or i < n_sink, or
+ * i >= N - n_recent, or token_pinned[i] != 0.
+ * Items: item_tokens == 1 scores tokens; item_tokens == page_size scores pages by the
+ * mean of their tokens' scores (MemDecay S_p, over the tokens present) and pins a page
+ * when any of its tokens is pinned.
+ */
+typedef struct kv_score_params {
+  const void *q;              /* bf16 [L][W][Hq][128], rotated at their own positions */
+  int32_t n_q_heads;          /* Hq, multiple of Hkv; G*W <= 512 with G = Hq/Hkv */
+  int32_t window;             /* W, 1..N */
+  float scale;                /* softmax scale; 0 => 1/sqrt(128) */
+  int32_t policy;             /* KV_POLICY_* */
+  int32_t item_tokens;        /* 1 or page_size */
+  int32_t dt_steps;           /* decode steps per observation (MemDecay's k) */
+  const float *lse_in;        /* [L][Hq][W] natural-log LSE from the attention
+                                 backend, or NULL to compute it (extra pass over K) */
+  /* MemDecay */
+  const uint8_t *region;      /* [N] region label per token (NULL: no regions) */
+  const float *base_prio;     /* [n_regions] b_r >= 0 */
+  const float *decay_rate;    /* [n_regions] lambda_r >= 0 */
+  int32_t n_regions;          /* 1..32; labels must be < n_regions */
+  float rho, alpha, tau;
+  float *ewma;                /* [N] in/out (MEMDECAY) */
+  int32_t *clock;             /* [N] in/out (MEMDECAY) */
+  /* H2O */
+  float *accum;               /* [N] in/out (H2O) */
+  /* foresight */
+  const int32_t *span_id;     /* [N] span of each token, -1 = none (NULL: no bonus) */
+  const int32_t *span_next_use; /* [n_spans] */
+  int32_t n_spans;
+  float bonus_floor;
+  /* pinning */
+  uint32_t pinned_regions;    /* bit r pins region r */
+  int32_t n_sink;
+  int32_t n_recent;
+  const uint8_t *token_pinned; /* [N] or NULL */
+  /* outputs */
+  float *mass;                /* [N] summed attention mass, or NULL */
+  float *lse;                 /* [L][Hq][W] natural-log LSE, or NULL */
+  float *token_score;         /* [N] or NULL */
+  float *item_score;          /* [ceil(N/item_tokens)] */
+  uint8_t *item_pinned;       /* [ceil(N/item_tokens)] */
+} kv_score_params;
+
+int32_t kv_abi_version(void);
+
+/* Text for a return code (static storage; KV_EHIP text includes the last HIP error
+ * seen by the calling thread). */
+const char *kv_strerror(int32_t code);
+
+/* Host-only.  Workspace bytes kv_score needs for this cache and these parameters. */
+int32_t kv_score_workspace_size(const kv_cache_desc *cache, const kv_score_params *p,
+                                size_t *bytes /* host */);
+
+/* Score every cached token (CalAttn + policy epilogue).  cache and p are host
+ * structs; the arrays they point to are device memory.  Updates ewma/clock or accum in
+ * place and writes item_score / item_pinned (and mass, lse when given). */
+int32_t kv_score(const kv_cache_desc *cache, const kv_score_params *p, void *workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/* Host-only.  Workspace bytes kv_select needs for n_items items. */
+int32_t kv_select_workspace_size(int64_t n_items, size_t *bytes /* host */);
+
+/*
+ * Budget selection (MemDecay, Method; PACE Table 1; ActKV Sec. 3.3 "Eviction").
+ * Keeps every pinned item, then the best (budget_items - #pinned) other items in the
+ * total order: higher score first, exact ties by lower index, -0.0 == +0.0, NaN last.
+ * Writes the kept TOKEN indices in ascending order to keep_tokens (pages expand to
+ * their tokens; a partial last page contributes the tokens it has), the number of
+ * kept tokens to *n_keep (device int64) and KV_STATUS_* bits to *status (device).
+ * item_pinned may be NULL.  keep_capacity is the length of keep_tokens in tokens.
+ */
+int32_t kv_select(const float *item_score, const uint8_t *item_pinned, int64_t n_items,
+                  int32_t item_tokens, int64_t n_tokens, int64_t budget_items,
+                  int32_t *keep_tokens, int64_t keep_capacity, int64_t *n_keep,
+                  uint32_t *status, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/*
+ * Segment eviction from the front of the private history ("Rethinking KV Cache
+ * Eviction for Agentic LLM Serving", Part one): keep [0, P) and [P + E', N) where
+ * E' = min(ceil(E / block) * block, N - P) frees only whole blocks.  Writes the keep
+ * list (ascending) when keep_tokens is not NULL, n_keep to *n_keep_dev when not NULL,
+ * and returns n_keep and E' through the host pointers.
+ */
+int32_t kv_select_segment(int64_t n_tokens, int64_t prefix_len, int64_t evict_tokens,
+                          int32_t block, int32_t *keep_tokens, int64_t keep_capacity,
+                          int64_t *n_keep_dev, int64_t *n_keep_host /* host */,
+                          int64_t *evict_len_host /* host */, hipStream_t stream);
+
+/*
+ * Stable in-order gather of the kept tokens into dst, with exact re-rotation of the
+ * kept keys (PACE Sec. 3.2, Proposition 1; split-half RoPE, Sec. 3.5).
+ * Rank r < n_keep takes source token j = keep_tokens[r]:
+ *   new_pos[r] = renumber_base + r     when renumber_base >= 0 (order-preserving,
+ *                                      gap-collapsing renumbering),
+ *              = old_pos[j]            otherwise;
+ *   V: copied verbatim;  K: copied verbatim when new_pos[r] == old_pos[j], otherwise
+ *   each pair (x_i, x_{i+64}) is rotated by (new_pos[r]-old_pos[j]) * theta_i with
+ *   theta_i = rope_theta^(-2i/128), computed in float64 and rounded once to bf16 (RNE).
+ *   Every meta[m] array is gathered the same way.
+ * n_keep (device, may be NULL = max_keep) is clamped to max_keep (host bound that
+ * sizes the launch).  dst must not overlap src.  dst.n_tokens >= max_keep; its layer
+ * and head shapes must equal src's.  limit > 0 with renumbering requires
+ * renumber_base + max_keep <= limit (PACE's L), else KV_ELIMIT.  new_pos may be NULL.
+ */
+int32_t kv_compact_rerope(const kv_cache_desc *src, const kv_cache_desc *dst,
+                          const int32_t *keep_tokens, const int64_t *n_keep,
+                          int64_t max_keep, const int32_t *old_pos, int32_t *new_pos,
+                          int32_t renumber_base, double rope_theta, int32_t limit,
+                          const kv_meta_desc *meta /* host array */, int32_t n_meta,
+                          hipStream_t stream);
+
+/*
+ * In-place form of segment eviction + compaction + re-rotation: removes tokens
+ * [P, P + E') of the row and shifts the suffix [P + E', N) left by E' inside the same
+ * cache, re-rotating each moved key by its position change.  pos[N] holds the physical
+ * positions on entry; on return pos[0 .. N-E') holds the new ones (renumber_base >= 0:
+ * base + r; otherwise unchanged, i.e. Penelope keeps original positions).  The move runs
+ * in rounds of at most E' tokens so that no round reads a slot another round of it
+ * writes.  Metadata arrays (meta[m].src == meta[m].dst) move the same way.
+ */
+int32_t kv_compact_segment_inplace(const kv_cache_desc *cache, int64_t prefix_len,
+                                   int64_t evict_len, int32_t *pos, int32_t renumber_base,
+                                   double rope_theta, int32_t limit,
+                                   const kv_meta_desc *meta /* host array */,
+                                   int32_t n_meta, hipStream_t stream);
+
+/* Host-only.  PACE's renumber trigger (Sec. 3.2): 1 when the next physical position
+ * comes within headroom of the limit (next_pos >= limit - headroom), else 0. */
+int32_t kv_renumber_needed(int64_t next_pos, int32_t headroom, int32_t limit);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSCORE_H */

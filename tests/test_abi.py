@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header declares,
+and its host-only logic and argument validation follow the header's contract.
+
+Only validation paths that return before any device call are exercised here (dummy,
+never dereferenced pointers); compute parity lives in the gpu-marked tests.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import compaction_kv_score_amd as kv
+import oracle as O
+
+FAKE = 0x10000  # 16-byte aligned dummy device address, never dereferenced here
+
+
+def _cache(**over):
+    d = dict(k=FAKE, v=FAKE * 2, n_layers=2, n_kv_heads=2, head_dim=128, page_size=16,
+             n_tokens=100, layer_stride=7 * 16 * 2 * 128, page_stride=16 * 2 * 128,
+             block_table=None)
+    d.update(over)
+    return kv.KvCacheDesc(**d)
+
+
+def test_library_exports_every_declared_function():
+    names = kv.declared_functions()
+    assert len(names) >= 10
+    lib = kv.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert kv.kv_abi_version() == 1
+
+
+def test_strerror_texts():
+    for code in (kv.KV_OK, kv.KV_EINVAL, kv.KV_EUNSUPPORTED, kv.KV_EWORKSPACE, kv.KV_EHIP, kv.KV_ELIMIT):
+        assert len(kv.kv_strerror(code)) >= 2
+    assert "unknown" in kv.kv_strerror(12345)
+
+
+@pytest.mark.parametrize("next_pos", [0, 4095, 6143, 6144, 6145, 8191, 100000])
+def test_renumber_trigger_matches_oracle(next_pos):
+    assert kv.kv_renumber_needed(next_pos, 2048, 8192) == O.renumber_needed(next_pos, 2048, 8192)
+
+
+@pytest.mark.parametrize("n,p,e,blk", [(131072, 16384, 39322, 16), (100, 10, 7, 4), (40, 30, 50, 16),
+                                       (64, 0, 0, 16), (64, 64, 5, 16), (1000, 3, 999, 64)])
+def test_select_segment_host_result_matches_oracle(n, p, e, blk):
+    n_keep, evict = kv.kv_select_segment(n, p, e, blk)
+    assert evict == O.segment_evict_len(n, p, e, blk)
+    assert n_keep == len(O.select_segment(n, p, e, blk))
+
+
+def test_select_segment_rejects_bad_arguments():
+    L = kv.lib()
+    nk, el = ctypes.c_int64(), ctypes.c_int64()
+    assert L.kv_select_segment(10, 11, 1, 16, None, 0, None, ctypes.byref(nk), ctypes.byref(el), None) == kv.KV_EINVAL
+    assert L.kv_select_segment(10, 2, 1, 0, None, 0, None, ctypes.byref(nk), ctypes.byref(el), None) == kv.KV_EINVAL
+    assert L.kv_select_segment(0, 0, 1, 16, None, 0, None, ctypes.byref(nk), ctypes.byref(el), None) == kv.KV_EINVAL
+
+
+def _score_params(**over):
+    d = dict(q=FAKE, n_q_heads=4, window=8, scale=0.0, policy=kv.KV_POLICY_H2O, item_tokens=1,
+             dt_steps=1, accum=FAKE, item_score=FAKE, item_pinned=FAKE)
+    d.update(over)
+    return kv.KvScoreParams(**d)
+
+
+def test_score_workspace_size_and_validation():
+    L = kv.lib()
+    n = ctypes.c_size_t()
+    c, p = _cache(), _score_params()
+    assert L.kv_score_workspace_size(ctypes.byref(c), ctypes.byref(p), ctypes.byref(n)) == kv.KV_OK
+    rows, n_lg = 2 * 8, 2 * 2
+    assert n.value >= n_lg * 100 * 4 + n_lg * rows * 4  # mass partials + LSE at least
+    bad = [
+        (_cache(head_dim=64), p, kv.KV_EUNSUPPORTED),
+        (_cache(page_size=12), p, kv.KV_EUNSUPPORTED),
+        (_cache(k=None), p, kv.KV_EINVAL),
+        (_cache(page_stride=100), p, kv.KV_EINVAL),
+        (c, _score_params(n_q_heads=3), kv.KV_EINVAL),
+        (c, _score_params(window=101), kv.KV_EINVAL),
+        (c, _score_params(window=0), kv.KV_EINVAL),
+    ]
+    for cc, pp, want in bad:
+        assert L.kv_score_workspace_size(ctypes.byref(cc), ctypes.byref(pp), ctypes.byref(n)) == want
+    # 40 query heads per KV head x 16 window rows = 640 rows > 512
+    pp = _score_params(n_q_heads=80, window=16)
+    assert L.kv_score_workspace_size(ctypes.byref(c), ctypes.byref(pp), ctypes.byref(n)) == kv.KV_EUNSUPPORTED
+
+
+def test_score_rejects_missing_state_and_small_workspace():
+    L = kv.lib()
+    c = _cache()
+    p = _score_params(policy=kv.KV_POLICY_MEMDECAY)  # no ewma / clock / region
+    assert L.kv_score(ctypes.byref(c), ctypes.byref(p), FAKE, 1 << 30, None) == kv.KV_EINVAL
+    p = _score_params()
+    assert L.kv_score(ctypes.byref(c), ctypes.byref(p), FAKE, 16, None) == kv.KV_EWORKSPACE
+    p = _score_params(item_tokens=8)
+    assert L.kv_score(ctypes.byref(c), ctypes.byref(p), FAKE, 1 << 30, None) == kv.KV_EINVAL
+
+
+def test_select_validation():
+    L = kv.lib()
+    n = ctypes.c_size_t()
+    assert L.kv_select_workspace_size(1000, ctypes.byref(n)) == kv.KV_OK and n.value > 0
+    assert L.kv_select_workspace_size(0, ctypes.byref(n)) == kv.KV_EINVAL
+    # n_items inconsistent with n_tokens / item_tokens
+    assert L.kv_select(FAKE, None, 10, 16, 100, 3, FAKE, 100, FAKE, None, FAKE, 1 << 20, None) == kv.KV_EINVAL
+    assert L.kv_select(FAKE, None, 7, 16, 100, 3, FAKE, 100, FAKE, None, FAKE, 8, None) == kv.KV_EWORKSPACE
+    assert L.kv_select(None, None, 7, 16, 100, 3, FAKE, 100, FAKE, None, FAKE, 1 << 20, None) == kv.KV_EINVAL
+
+
+def test_compact_limit_rule_and_validation():
+    """PACE Sec. 3.2: a renumbered row base + n must fit under the limit L."""
+    L = kv.lib()
+    src = _cache(n_tokens=10000, layer_stride=700 * 16 * 256, page_stride=16 * 256)
+    dst = _cache(k=FAKE * 8, v=FAKE * 16, n_tokens=4096, layer_stride=300 * 16 * 256,
+                 page_stride=16 * 256)
+    meta = (kv.KvMetaDesc * 1)()
+    args = lambda base, maxk, limit: (ctypes.byref(src), ctypes.byref(dst), FAKE, None, maxk, FAKE,
+                                      None, base, 1e6, limit, meta, 0, None)
+    assert L.kv_compact_rerope(*args(0, 4096, 4095)) == kv.KV_ELIMIT
+    assert L.kv_compact_rerope(*args(100, 4000, 4096)) == kv.KV_ELIMIT
+    assert L.kv_compact_rerope(*args(0, 4097, 8192)) == kv.KV_EINVAL       # dst too small
+    same = _cache(n_tokens=10000, layer_stride=700 * 16 * 256, page_stride=16 * 256)
+    assert L.kv_compact_rerope(ctypes.byref(src), ctypes.byref(same), FAKE, None, 10, FAKE, None,
+                               -1, 1e6, 0, meta, 0, None) == kv.KV_EINVAL  # src == dst
+    assert L.kv_compact_rerope(*args(0, 10, 0)[:8], 0.5, 0, meta, 0, None) == kv.KV_EINVAL  # theta
+    bad_meta = (kv.KvMetaDesc * 1)(kv.KvMetaDesc(FAKE, FAKE, 3, 0))
+    assert L.kv_compact_rerope(*args(0, 10, 0)[:10], bad_meta, 1, None) == kv.KV_EINVAL
+    assert L.kv_compact_segment_inplace(ctypes.byref(src), 100, 20, FAKE, 0, 1e4, 9000, meta, 0,
+                                        None) == kv.KV_ELIMIT
+    assert L.kv_compact_segment_inplace(ctypes.byref(src), 9990, 20, FAKE, 0, 1e4, 0, meta, 0,
+                                        None) == kv.KV_EINVAL
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        kv._ptr(torch.zeros(4))

@@ -1,0 +1,474 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Bars (stated once here and used below):
+  * kept indices, compacted V, unrotated K, positions, metadata: bit-exact;
+  * re-rotated bf16 keys: within 1 bf16 ulp of the oracle's correctly rounded value;
+  * attention mass, token/page scores, EWMA: within 1e-5 relative (fp32 vs fp64);
+    LSE within 1e-5 absolute (it is a logarithm);
+  * decay clocks: exact, except tokens whose windowed mass lies within 1e-5 relative of
+    tau, where an fp32-vs-fp64 difference may legitimately flip the reset;
+  * end to end (each side scores for itself): kept sets may differ only in items whose
+    oracle score is within 1e-5 relative of the selection threshold.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compaction_kv_score_amd as kv
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+RTOL = 1e-5
+
+
+def np64(t):
+    return t.detach().cpu().double().numpy() if t.dtype != torch.bfloat16 else \
+        t.detach().float().cpu().double().numpy()
+
+
+def f32(x):
+    """Round a Python/NumPy value to float32 (what the device receives)."""
+    return np.float32(x).astype(np.float64)
+
+
+def assert_rel(got, ref, rtol=RTOL, what=""):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    bad = np.abs(got - ref) > rtol * np.abs(ref) + 1e-35
+    assert not bad.any(), (what, int(bad.sum()), got[bad][:5], ref[bad][:5])
+
+
+def ulp_bf16(x):
+    x = np.abs(np.asarray(x, np.float64))
+    _, e = np.frexp(x)
+    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+
+
+def assert_bf16_within_1ulp(got, ref, what=""):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    bad = np.abs(got - ref) > ulp_bf16(ref)
+    assert not bad.any(), (what, int(bad.sum()), got[bad][:5], ref[bad][:5])
+
+
+# ------------------------------------------------------------------------------ compaction
+
+def _paged_to_logical(t, bt, pg, n):
+    return O.gather_logical(np64(t), None if bt is None else bt.cpu().numpy(), pg, n)
+
+
+@pytest.mark.parametrize("nl,hkv,n,n_keep,shuffle,base,theta", [
+    (1, 2, 512, 128, False, 0, 1e6),
+    (3, 2, 1000, 333, True, 0, 1e6),
+    (2, 8, 777, 100, True, -1, 1e4),
+    (2, 8, 4096, 1, False, 5, 1e4),
+    (28, 2, 2048, 512, True, 0, 1e6),
+])
+def test_compact_rerope_parity(nl, hkv, n, n_keep, shuffle, base, theta):
+    w = synth.workload(2, n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n)
+    k, v, bt = synth.kv_cache(w, seed=n, device=DEV, paged_shuffle=shuffle, extra_pages=3)
+    g = torch.Generator().manual_seed(n + 1)
+    keep = torch.sort(torch.randperm(n, generator=g)[:n_keep])[0].to(torch.int32)
+    # old positions: some tokens were renumbered before (delta 0 for some, up to ~1e6)
+    old_pos = torch.arange(n, dtype=torch.int32) + torch.randint(0, 1_000_000, (n,), generator=g,
+                                                                   dtype=torch.int32)
+    old_pos[keep[: max(1, n_keep // 4)]] = torch.arange(max(1, n_keep // 4), dtype=torch.int32) + max(base, 0)
+    region = torch.randint(0, 7, (n,), generator=g, dtype=torch.int32).to(torch.uint8)
+    ewma = torch.rand(n, generator=g)
+    span = torch.randint(-1, 200, (n,), generator=g, dtype=torch.int32)
+    big = torch.randint(-2 ** 62, 2 ** 62, (n,), generator=g, dtype=torch.int64)
+    n_dst_pages = -(-n_keep // 16) + 2
+    dk = torch.zeros((nl, n_dst_pages, 16, hkv, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    dbt = torch.randperm(n_dst_pages, generator=g)[: -(-n_keep // 16)].to(torch.int32).to(DEV) if shuffle else None
+    src = kv.PagedCache(k, v, n, bt)
+    dst = kv.PagedCache(dk, dv, n_keep, dbt)
+    outs = [torch.zeros(n_keep, dtype=x.dtype, device=DEV) for x in (region, ewma, span, big)]
+    new_pos = torch.full((n_keep,), -7, dtype=torch.int32, device=DEV)
+    kv.kv_compact_rerope(src, dst, keep.to(DEV), None, n_keep, old_pos.to(DEV), new_pos,
+                         renumber_base=base, rope_theta=theta, limit=0,
+                         meta=[(x.to(DEV), o) for x, o in zip((region, ewma, span, big), outs)])
+    torch.cuda.synchronize()
+    kl = _paged_to_logical(k, bt, 16, n)
+    vl = _paged_to_logical(v, bt, 16, n)
+    rk, rv, rpos = O.compact_rerope(kl, vl, keep.numpy(), old_pos.numpy(), base, theta)
+    gk = _paged_to_logical(dk, dbt, 16, n_keep)
+    gv = _paged_to_logical(dv, dbt, 16, n_keep)
+    assert (new_pos.cpu().numpy() == rpos).all()
+    assert (gv == rv).all(), "V must be bit-exact"
+    delta = rpos - old_pos.numpy()[keep.numpy()]
+    still = delta == 0
+    assert (gk[:, still] == rk[:, still]).all(), "unrotated K must be bit-exact"
+    assert_bf16_within_1ulp(gk[:, ~still], rk[:, ~still], "rotated K")
+    exact = (gk[:, ~still] == rk[:, ~still]).mean() if (~still).any() else 1.0
+    assert exact > 0.999
+    for x, o in zip((region, ewma, span, big), outs):
+        assert (o.cpu() == x[keep.long()]).all()
+
+
+def test_compact_respects_device_count():
+    w = synth.workload(1)
+    k, v, _ = synth.kv_cache(w, seed=1, device=DEV)
+    keep = torch.arange(0, 512, 4, dtype=torch.int32, device=DEV)
+    n_keep = torch.tensor([50], dtype=torch.int64, device=DEV)
+    dk = torch.zeros((1, 8, 16, 2, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    pos = torch.arange(512, dtype=torch.int32, device=DEV)
+    newp = torch.full((128,), -1, dtype=torch.int32, device=DEV)
+    kv.kv_compact_rerope(kv.PagedCache(k, v, 512), kv.PagedCache(dk, dv, 128), keep, n_keep, 128, pos,
+                         newp, renumber_base=0, rope_theta=1e6)
+    torch.cuda.synchronize()
+    flat = dk.reshape(1, 128, 2, 128)
+    assert (flat[:, 50:] == 0).all() and (newp[50:] == -1).all() and (newp[:50] == torch.arange(50, device=DEV)).all()
+    assert (flat[:, 1:50] != 0).any()
+
+
+@pytest.mark.parametrize("nl,n,prefix,frac,base,theta,shuffle", [
+    (2, 1000, 100, 0.3, 0, 1e4, False),
+    (3, 4096, 512, 0.3, 0, 1e4, True),
+    (2, 600, 0, 0.9, -1, 1e4, False),
+    (2, 300, 200, 0.05, 7, 1e6, False),
+])
+def test_segment_inplace_parity(nl, n, prefix, frac, base, theta, shuffle):
+    w = synth.workload(4, n_layers=nl, n_tokens=n)
+    k, v, bt = synth.kv_cache(w, seed=n, device=DEV, paged_shuffle=shuffle, extra_pages=2)
+    n_keep, e = kv.kv_select_segment(n, prefix, int(frac * n), 16)
+    keep = O.select_segment(n, prefix, int(frac * n), 16)
+    assert n_keep == len(keep)
+    kl = _paged_to_logical(k, bt, 16, n)
+    vl = _paged_to_logical(v, bt, 16, n)
+    pos = torch.arange(n, dtype=torch.int32, device=DEV)
+    region = torch.randint(0, 7, (n,), dtype=torch.int32).to(torch.uint8)
+    reg_dev = region.to(DEV)
+    kv.kv_compact_segment_inplace(kv.PagedCache(k, v, n, bt), prefix, e, pos, renumber_base=base,
+                                  rope_theta=theta, meta=[reg_dev])
+    torch.cuda.synchronize()
+    rk, rv, rpos = O.compact_rerope(kl, vl, keep, np.arange(n), base, theta)
+    gk = _paged_to_logical(k, bt, 16, n)[:, :n_keep]
+    gv = _paged_to_logical(v, bt, 16, n)[:, :n_keep]
+    assert (pos[:n_keep].cpu().numpy() == rpos).all()
+    assert (gv == rv).all()
+    delta = rpos - keep
+    assert (gk[:, delta == 0] == rk[:, delta == 0]).all()
+    assert_bf16_within_1ulp(gk, rk, "segment K")
+    assert (reg_dev[:n_keep].cpu().numpy() == region.numpy()[keep]).all()
+
+
+# ------------------------------------------------------------------------------ selection
+
+def _select_case(n_items, item_tokens, n_tokens, budget, score, pinned, cap=None):
+    cap = cap if cap is not None else n_tokens
+    keep = torch.full((max(cap, 1),), -1, dtype=torch.int32, device=DEV)
+    n_keep = torch.zeros(1, dtype=torch.int64, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kv.kv_select(score.to(DEV), None if pinned is None else pinned.to(DEV), item_tokens, n_tokens, budget,
+                 keep[:cap] if cap else keep[:1], n_keep, status)
+    torch.cuda.synchronize()
+    items, st = O.select_items(score.double().numpy(), None if pinned is None else pinned.numpy(), budget)
+    toks = O.expand_items(items, item_tokens, n_tokens)
+    nk = int(n_keep.item())
+    assert nk == len(toks), (nk, len(toks))
+    assert (keep[: min(nk, cap)].cpu().numpy() == toks[:cap]).all()
+    want = st | (kv.KV_STATUS_KEEP_OVERFLOW if len(toks) > cap else 0)
+    assert int(status.item()) == want
+
+
+@pytest.mark.parametrize("n,alphabet,pin_frac,budget_frac,nan,negz", [
+    (1, None, 0.0, 1.0, 0, False),
+    (5, [0.0, 0.5, 1.0], 0.2, 0.6, 0, True),
+    (100, [0.1, 0.2], 0.1, 0.3, 0, False),
+    (4097, None, 0.02, 0.1, 0.01, True),
+    (100_000, None, 0.0013, 0.02048, 0, False),
+    (100_000, [1.0, 2.0, 3.0], 0.05, 0.5, 0, False),
+    (300_000, None, 0.3, 0.2, 0.001, True),        # pinned exceed the budget
+    (62_500, None, 0.0, 0.002048, 0, False),
+])
+def test_select_token_mode(n, alphabet, pin_frac, budget_frac, nan, negz):
+    s = synth.scores(n, seed=n, alphabet=alphabet, nan_frac=nan, neg_zero=negz)
+    pin = synth.pinned_mask(n, seed=n, frac=pin_frac) if pin_frac else None
+    _select_case(n, 1, n, int(round(budget_frac * n)), s, pin)
+
+
+@pytest.mark.parametrize("n_tokens,budget_pages", [(512, 8), (2048, 32), (1000, 20), (1_000_000, 128),
+                                                   (17, 2), (16, 0)])
+def test_select_page_mode(n_tokens, budget_pages):
+    n_items = -(-n_tokens // 16)
+    s = synth.scores(n_items, seed=n_tokens, alphabet=[0.25, 0.5, 0.75] if n_tokens < 5000 else None)
+    pin = synth.pinned_mask(n_items, seed=n_tokens, frac=0.05)
+    _select_case(n_items, 16, n_tokens, budget_pages, s, pin)
+
+
+def test_select_overflow_and_budget_extremes():
+    s = synth.scores(1000, seed=3)
+    _select_case(1000, 1, 1000, 1000, s, None)
+    _select_case(1000, 1, 1000, 5000, s, None)
+    _select_case(1000, 1, 1000, 0, s, synth.pinned_mask(1000, seed=3, frac=0.01))
+    _select_case(1000, 1, 1000, 600, s, None, cap=100)
+
+
+def test_select_segment_device_list():
+    keep = torch.full((131072,), -1, dtype=torch.int32, device=DEV)
+    nk_dev = torch.zeros(1, dtype=torch.int64, device=DEV)
+    n_keep, e = kv.kv_select_segment(131072, 16384, int(0.3 * 131072), 16, keep, nk_dev)
+    torch.cuda.synchronize()
+    ref = O.select_segment(131072, 16384, int(0.3 * 131072), 16)
+    assert e == 39328 and n_keep == len(ref) == int(nk_dev.item())
+    assert (keep[:n_keep].cpu().numpy() == ref).all()
+
+
+# ------------------------------------------------------------------------------ scoring
+
+def _make_score_inputs(w, seed, shuffle, plant=True):
+    k, v, bt = synth.kv_cache(w, seed=seed, device="cpu", paged_shuffle=shuffle, extra_pages=2)
+    q = synth.window_queries(w, seed=seed)
+    if plant:
+        synth.plant_heavy_keys(w, k, q, bt, seed=seed)
+    return k.to(DEV), v.to(DEV), (bt.to(DEV) if bt is not None else None), q
+
+
+def _run_score(w, k, v, bt, q, *, policy, item_tokens, state, lse_in=None, **kw):
+    n = w.n_tokens
+    n_items = -(-n // item_tokens)
+    out = dict(mass=torch.zeros(n, device=DEV), lse=torch.zeros((w.n_layers, w.n_q_heads, w.window), device=DEV),
+               token_score=torch.zeros(n, device=DEV), item_score=torch.zeros(n_items, device=DEV),
+               item_pinned=torch.zeros(n_items, dtype=torch.uint8, device=DEV))
+    kv.kv_score(kv.PagedCache(k, v, n, bt), q.to(DEV), policy=policy, window=w.window, item_tokens=item_tokens,
+                lse_in=lse_in, **state, **kw, **out)
+    torch.cuda.synchronize()
+    return {key: t.cpu() for key, t in out.items()}
+
+
+def _memdecay_state(w, seed):
+    ewma, clock = synth.memdecay_state(w, seed)
+    b, lam = synth.region_params(seed)
+    return dict(region=synth.regions(w, seed), base_prio=b, decay_rate=lam, ewma=ewma, clock=clock)
+
+
+def _compare_memdecay(w, q, k_logical, st0, dev_state, got, rho, alpha, tau, dt_steps, item_tokens,
+                      pinned_regions, n_sink=0, n_recent=0, span_id=None, next_use=None, floor=50000.0):
+    ref = O.score_step(np64(q), k_logical, policy="memdecay", region=st0["region"].numpy(),
+                       base_prio=np64(st0["base_prio"]), decay_rate=np64(st0["decay_rate"]),
+                       rho=f32(rho), alpha=f32(alpha), tau=f32(tau), dt_steps=dt_steps,
+                       ewma=np64(st0["ewma"]), clock=st0["clock"].numpy(),
+                       span_id=None if span_id is None else span_id.numpy(),
+                       span_next_use=None if next_use is None else next_use.numpy(), bonus_floor=floor,
+                       pinned_regions=pinned_regions, n_sink=n_sink, n_recent=n_recent,
+                       item_tokens=item_tokens)
+    assert_rel(np64(got["mass"]), ref["mass"], what="mass")
+    assert np.abs(np64(got["lse"]) - ref["lse"]).max() < 1e-5
+    boundary = np.abs(ref["abar"] - f32(tau)) <= 1e-5 * f32(tau)
+    ok = ~boundary
+    assert_rel(np64(dev_state["ewma"])[ok], ref["ewma"][ok], what="ewma")
+    assert (dev_state["clock"].numpy()[ok] == ref["clock"][ok]).all()
+    assert_rel(np64(got["token_score"])[ok], ref["token_score"][ok], what="token score")
+    item_ok = ok if item_tokens == 1 else ~O.page_any(boundary, item_tokens)
+    assert_rel(np64(got["item_score"])[item_ok], ref["item_score"][item_ok], what="item score")
+    assert (got["item_pinned"].numpy().astype(bool) == ref["item_pinned"]).all()
+    return ref, boundary
+
+
+@pytest.mark.parametrize("cfg,over,shuffle", [
+    (1, {}, False),
+    (1, {}, True),
+    (2, {}, True),
+    (1, dict(n_tokens=1000, window=37, n_q_heads=6, n_kv_heads=2, n_layers=2), True),
+    (1, dict(n_tokens=77, window=77, n_q_heads=4, n_kv_heads=4, n_layers=1, system_prefix=5), False),
+    (1, dict(n_tokens=5000, window=64, n_q_heads=32, n_kv_heads=8, n_layers=2, system_prefix=64), True),
+    (1, dict(n_tokens=9000, window=16, n_q_heads=64, n_kv_heads=2, n_layers=1), False),
+])
+def test_score_memdecay_parity(cfg, over, shuffle):
+    w = synth.workload(cfg, **over)
+    k, v, bt, q = _make_score_inputs(w, seed=11 + w.n_tokens, shuffle=shuffle)
+    st0 = _memdecay_state(w, seed=w.n_tokens)
+    dev_state = {key: t.clone() for key, t in st0.items()}
+    dev = {key: t.to(DEV) for key, t in dev_state.items()}
+    got = _run_score(w, k, v, bt, q, policy="memdecay", item_tokens=w.item_tokens, state=dev,
+                     rho=w.rho, alpha=w.alpha, tau=w.tau, dt_steps=3, pinned_regions=1)
+    dev_state = {key: t.cpu() for key, t in dev.items()}
+    kl = _paged_to_logical(k, bt, 16, w.n_tokens)
+    _compare_memdecay(w, q, kl, st0, dev_state, got, w.rho, w.alpha, w.tau, 3, w.item_tokens, 1)
+
+
+def test_score_memdecay_sixteen_steps():
+    """State carried across 16 scoring steps with fresh window queries (config 1)."""
+    w = synth.workload(1)
+    k, v, bt, _ = _make_score_inputs(w, seed=5, shuffle=True)
+    st = _memdecay_state(w, seed=5)
+    dev = {key: t.to(DEV) for key, t in st.items()}
+    ref_ewma, ref_clock = np64(st["ewma"]), st["clock"].numpy().astype(np.int64)
+    kl = _paged_to_logical(k, bt, 16, w.n_tokens)
+    excluded = np.zeros(w.n_tokens, bool)
+    for step in range(16):
+        q = synth.window_queries(w, seed=100 + step)
+        got = _run_score(w, k, v, bt, q, policy="memdecay", item_tokens=16, state=dev, rho=w.rho,
+                         alpha=w.alpha, tau=w.tau, dt_steps=1, pinned_regions=1)
+        ref = O.score_step(np64(q), kl, policy="memdecay", region=st["region"].numpy(),
+                           base_prio=np64(st["base_prio"]), decay_rate=np64(st["decay_rate"]),
+                           rho=f32(w.rho), alpha=f32(w.alpha), tau=f32(w.tau), dt_steps=1,
+                           ewma=ref_ewma, clock=ref_clock, pinned_regions=1, item_tokens=16)
+        excluded |= np.abs(ref["abar"] - f32(w.tau)) <= 1e-5 * f32(w.tau)
+        ok = ~excluded
+        assert_rel(np64(dev["ewma"].cpu())[ok], ref["ewma"][ok], rtol=2e-5, what=f"ewma step {step}")
+        assert (dev["clock"].cpu().numpy()[ok] == ref["clock"][ok]).all(), step
+        assert_rel(np64(got["token_score"])[ok], ref["token_score"][ok], rtol=2e-5, what=f"score step {step}")
+        ref_ewma, ref_clock = ref["ewma"], ref["clock"]
+    assert excluded.mean() < 0.01
+
+
+@pytest.mark.parametrize("over,shuffle", [
+    (dict(n_tokens=3000, n_layers=2, n_spans=40), True),
+    (dict(n_tokens=10_000, n_layers=1, n_spans=200), False),
+])
+def test_score_h2o_foresight_parity(over, shuffle):
+    w = synth.workload(3, **over)
+    k, v, bt, q = _make_score_inputs(w, seed=w.n_tokens, shuffle=shuffle)
+    span_id, next_use = synth.spans(w, seed=3, p_needed=0.2)
+    accum = synth.h2o_state(w, seed=3)
+    dev_acc = accum.to(DEV)
+    got = _run_score(w, k, v, bt, q, policy="h2o", item_tokens=1, state=dict(accum=dev_acc),
+                     span_id=span_id.to(DEV), span_next_use=next_use.to(DEV), bonus_floor=50000.0,
+                     n_sink=w.n_sink, n_recent=w.n_recent)
+    kl = _paged_to_logical(k, bt, 16, w.n_tokens)
+    ref = O.score_step(np64(q), kl, policy="h2o", accum=np64(accum), span_id=span_id.numpy(),
+                       span_next_use=next_use.numpy(), bonus_floor=50000.0, n_sink=w.n_sink,
+                       n_recent=w.n_recent)
+    assert_rel(np64(got["mass"]), ref["mass"], what="mass")
+    assert_rel(np64(dev_acc.cpu()), ref["accum"], what="accum")
+    assert_rel(np64(got["item_score"]), ref["item_score"], what="score")
+    assert (got["item_pinned"].numpy().astype(bool) == ref["item_pinned"]).all()
+    assert (next_use > 0).any()
+
+
+def test_score_with_supplied_lse():
+    """Single-pass mode: LSE given by the attention backend (ActKV Sec. 7.1)."""
+    w = synth.workload(1, n_tokens=3000, n_layers=2, window=48)
+    k, v, bt, q = _make_score_inputs(w, seed=9, shuffle=True)
+    kl = _paged_to_logical(k, bt, 16, w.n_tokens)
+    mass, lse = O.attention_mass(np64(q), kl)
+    acc = torch.zeros(w.n_tokens, device=DEV)
+    got = _run_score(w, k, v, bt, q, policy="h2o", item_tokens=1, state=dict(accum=acc),
+                     lse_in=torch.from_numpy(lse).float().to(DEV))
+    assert_rel(np64(got["mass"]), mass, rtol=2e-5, what="mass with supplied LSE")
+
+
+def test_pipeline_end_to_end_config2():
+    """score -> select -> compact on the GPU against the oracle pipeline (config 2)."""
+    w = synth.workload(2)
+    k, v, bt, q = _make_score_inputs(w, seed=21, shuffle=True)
+    st0 = _memdecay_state(w, seed=21)
+    dev = {key: t.to(DEV) for key, t in st0.items()}
+    got = _run_score(w, k, v, bt, q, policy="memdecay", item_tokens=16, state=dev, rho=w.rho,
+                     alpha=w.alpha, tau=w.tau, dt_steps=1, pinned_regions=1)
+    keep = torch.zeros(w.budget_tokens + 64, dtype=torch.int32, device=DEV)
+    n_keep = torch.zeros(1, dtype=torch.int64, device=DEV)
+    kv.kv_select(got["item_score"].to(DEV), got["item_pinned"].to(DEV), 16, w.n_tokens, w.budget_items,
+                 keep, n_keep)
+    kl = _paged_to_logical(k, bt, 16, w.n_tokens)
+    ref = O.score_step(np64(q), kl, policy="memdecay", region=st0["region"].numpy(),
+                       base_prio=np64(st0["base_prio"]), decay_rate=np64(st0["decay_rate"]),
+                       rho=f32(w.rho), alpha=f32(w.alpha), tau=f32(w.tau), dt_steps=1,
+                       ewma=np64(st0["ewma"]), clock=st0["clock"].numpy(), pinned_regions=1, item_tokens=16)
+    items, _ = O.select_items(ref["item_score"], ref["item_pinned"], w.budget_items)
+    torch.cuda.synchronize()
+    nk = int(n_keep.item())
+    got_items = np.unique(keep[:nk].cpu().numpy() // 16)
+    diff = set(items.tolist()) ^ set(got_items.tolist())
+    if diff:
+        unp = ~ref["item_pinned"]
+        thr = np.sort(ref["item_score"][unp])[::-1][w.budget_items - ref["item_pinned"].sum() - 1]
+        for d in diff:
+            assert abs(ref["item_score"][d] - thr) <= 1e-5 * abs(thr), d
+    # compaction of the GPU keep list, renumbered to 0..n-1
+    dk = torch.zeros((w.n_layers, w.budget_tokens // 16 + 4, 16, 2, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    pos = torch.arange(w.n_tokens, dtype=torch.int32, device=DEV)
+    newp = torch.zeros(w.budget_tokens + 64, dtype=torch.int32, device=DEV)
+    kv.kv_compact_rerope(kv.PagedCache(k, v, w.n_tokens, bt), kv.PagedCache(dk, dv, w.budget_tokens + 64),
+                         keep, n_keep, w.budget_tokens + 64, pos, newp, renumber_base=0,
+                         rope_theta=w.rope_theta, limit=8192)
+    torch.cuda.synchronize()
+    keep_np = keep[:nk].cpu().numpy()
+    rk, rv, _ = O.compact_rerope(kl, _paged_to_logical(v, bt, 16, w.n_tokens), keep_np, np.arange(w.n_tokens),
+                                 0, w.rope_theta)
+    gk = np64(dk).reshape(w.n_layers, -1, 2, 128)[:, :nk]
+    gv = np64(dv).reshape(w.n_layers, -1, 2, 128)[:, :nk]
+    assert (gv == rv).all()
+    assert_bf16_within_1ulp(gk, rk, "pipeline K")
+
+
+# ------------------------------------------------------------------------------ full sizes
+
+@pytest.fixture(scope="module")
+def qwen3_100k():
+    w = synth.workload(3)
+    k, v, _ = synth.kv_cache(w, seed=0, device=DEV)
+    q = synth.window_queries(w, seed=0, device=DEV)
+    yield w, k, v, q
+    del k, v
+    torch.cuda.empty_cache()
+
+
+def test_full_size_qwen3_100k_score_properties(qwen3_100k):
+    """Launch configuration of the benchmark: 36 layers, 32/8 heads, N = 100,000."""
+    w, k, v, q = qwen3_100k
+    span_id, next_use = synth.spans(w, seed=0)
+    acc = torch.zeros(w.n_tokens, device=DEV)
+    got = _run_score(w, k, v, None, q, policy="h2o", item_tokens=1, state=dict(accum=acc),
+                     span_id=span_id.to(DEV), span_next_use=next_use.to(DEV), n_sink=4, n_recent=128)
+    mass = np64(got["mass"])
+    total = w.n_layers * w.n_q_heads * w.window
+    assert abs(mass.sum() / total - 1) < 1e-5          # each query's softmax row sums to 1
+    assert (mass > 0).all()
+    # sampled LSE rows against the oracle's definition over all 100K keys
+    g = torch.Generator().manual_seed(0)
+    for _ in range(6):
+        layer = int(torch.randint(0, w.n_layers, (1,), generator=g))
+        h = int(torch.randint(0, w.n_q_heads, (1,), generator=g))
+        wi = int(torch.randint(0, w.window, (1,), generator=g))
+        kk = np64(k[layer, :, :, h // 4, :].reshape(-1, 128)[: w.n_tokens])
+        qq = np64(q[layer, wi, h])
+        qpos = w.n_tokens - w.window + wi
+        s = (kk[: qpos + 1] @ qq) / math.sqrt(128)
+        m = s.max()
+        ref = m + math.log(np.exp(s - m).sum())
+        assert abs(float(got["lse"][layer, h, wi]) - ref) < 1e-5
+
+
+def test_full_size_qwen3_100k_two_layer_mass(qwen3_100k):
+    """Full N with a 2-layer slice of the cache: every token's mass against the oracle."""
+    w, k, v, q = qwen3_100k
+    w2 = synth.workload(3, n_layers=2)
+    k2, v2, q2 = k[:2].contiguous(), v[:2].contiguous(), q[:2].contiguous()
+    acc = torch.zeros(w.n_tokens, device=DEV)
+    got = _run_score(w2, k2, v2, None, q2, policy="h2o", item_tokens=1, state=dict(accum=acc))
+    kl = np64(k2).reshape(2, -1, 8, 128)[:, : w.n_tokens]
+    mass, lse = O.attention_mass(np64(q2), kl)
+    assert_rel(np64(got["mass"]), mass, what="mass at N=100K")
+    assert np.abs(np64(got["lse"]) - lse).max() < 1e-5
+
+
+def test_full_size_qwen3_100k_compaction_sampled(qwen3_100k):
+    w, k, v, q = qwen3_100k
+    g = torch.Generator().manual_seed(1)
+    keep = torch.sort(torch.randperm(w.n_tokens, generator=g)[: w.budget_tokens])[0].to(torch.int32)
+    dk = torch.zeros((w.n_layers, w.budget_tokens // 16, 16, 8, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    pos = torch.arange(w.n_tokens, dtype=torch.int32, device=DEV)
+    newp = torch.zeros(w.budget_tokens, dtype=torch.int32, device=DEV)
+    kv.kv_compact_rerope(kv.PagedCache(k, v, w.n_tokens), kv.PagedCache(dk, dv, w.budget_tokens),
+                         keep.to(DEV), None, w.budget_tokens, pos, newp, renumber_base=0,
+                         rope_theta=w.rope_theta, limit=w.limit)
+    torch.cuda.synchronize()
+    ranks = sorted(set([0, 1, w.budget_tokens - 1] + torch.randint(0, w.budget_tokens, (40,), generator=g).tolist()))
+    src = keep[ranks].long()
+    kf = k.reshape(w.n_layers, -1, 8, 128)
+    vf = v.reshape(w.n_layers, -1, 8, 128)
+    ks, vs = np64(kf[:, src.to(DEV)]), np64(vf[:, src.to(DEV)])
+    rk = O.bf16_round(O.rope_rotate(ks, (np.array(ranks) - src.numpy())[None, :, None], w.rope_theta))
+    gk = np64(dk.reshape(w.n_layers, -1, 8, 128)[:, ranks])
+    gv = np64(dv.reshape(w.n_layers, -1, 8, 128)[:, ranks])
+    assert (gv == vs).all()
+    assert_bf16_within_1ulp(gk, rk, "K at N=100K")
+    assert (newp.cpu().numpy() == np.arange(w.budget_tokens)).all()
