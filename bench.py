@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Throughput of the KV-cache eviction hot path on one MI355X.
+
+One step = one pass of the whole path over one row of synthetic cache already resident
+in HBM:
+    kv_score  (LSE pass -> LSE combine -> mass pass -> policy epilogue)
+    kv_select (radix select of the budget)
+    kv_compact_rerope (in-order gather of the kept tokens, all layers, exact re-RoPE)
+Default workload: Qwen3-8B-shaped session, 36 layers, 32 Q / 8 KV heads, head_dim 128,
+bf16 (144 KiB/token), N = 100,000 tokens, W = 64 window queries, budget 2,048 tokens
+with 4 sinks + 128 recent pinned, H2O score plus a foresight bonus from 200 spans, PACE
+renumbering under L = 8,192.
+
+Prints one JSON line: metric/value (KV tokens scored+evicted+compacted per second), a
+roofline entry for the dominant kernel (timed with HIP events on its launch stream) and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (timing on the library's own stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            arr[i] = h
+        return arr
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ev, stream) == 0
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return out.value
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "compaction_kv_score_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when the
+    kernel's source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or rec.get("source_hash") != source_hash(*rec.get("sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, layers):
+    """The CPU oracle, untuned, on a bounded sample of the workload: attention mass and
+    epilogue for `layers` of the 36 layers at full N, selection at full N, compaction of
+    the full budget for the same layers; scaled to all layers."""
+    import numpy as np
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    ws = synth.workload(3, n_layers=layers)
+    k, v, _ = synth.kv_cache(ws, seed=0)
+    q = synth.window_queries(ws, seed=0)
+    span_id, next_use = synth.spans(ws, seed=0)
+    kl = k.float().double().numpy().reshape(layers, -1, ws.n_kv_heads, ws.head_dim)[:, : ws.n_tokens]
+    vl = v.float().double().numpy().reshape(layers, -1, ws.n_kv_heads, ws.head_dim)[:, : ws.n_tokens]
+    t0 = time.perf_counter()
+    out = O.score_step(q.float().double().numpy(), kl, policy="h2o", accum=np.zeros(ws.n_tokens),
+                       span_id=span_id.numpy(), span_next_use=next_use.numpy(), n_sink=ws.n_sink,
+                       n_recent=ws.n_recent)
+    t1 = time.perf_counter()
+    kept, _ = O.select_items(out["item_score"], out["item_pinned"], ws.budget_items)
+    t2 = time.perf_counter()
+    O.compact_rerope(kl, vl, kept, np.arange(ws.n_tokens), 0, ws.rope_theta)
+    t3 = time.perf_counter()
+    scale = w.n_layers / layers
+    total = (t1 - t0) * scale + (t2 - t1) + (t3 - t2) * scale
+    return {
+        "value": w.n_tokens / total,
+        "unit": "KV tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{layers} of {w.n_layers} layers at N={w.n_tokens} (score + compaction "
+                   f"scaled x{scale:g}), selection at full N; measured {t3 - t0:.1f} s "
+                   f"on {os.cpu_count()} host CPUs ({platform.processor() or platform.machine()})"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload number (3: Qwen3-8B, N=100K)")
+    ap.add_argument("--cpu-layers", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) three "
+                         "times, to calibrate the FETCH_SIZE / WRITE_SIZE counters")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        a = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": a.numel() * 2, "launches": 3}))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the per-token mass would be all-reduced across ranks; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    if args.config != 3:
+        print("only workload 3 (Qwen3-8B, N=100K) is a bench line", file=sys.stderr)
+        sys.exit(2)
+
+    import compaction_kv_score_amd as kv
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.workload(args.config)
+    N, NL, HKV, HQ, D, W = w.n_tokens, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.window
+    B = w.budget_tokens
+    print(f"[bench] generating {w.name}: {N} tokens x {w.kv_bytes_per_token} B", file=sys.stderr, flush=True)
+    k, v, _ = synth.kv_cache(w, seed=0, device=dev)
+    q = synth.window_queries(w, seed=0, device=dev)
+    span_id, next_use = synth.spans(w, seed=0)
+    span_id, next_use = span_id.to(dev), next_use.to(dev)
+    accum = torch.zeros(N, device=dev)
+    item_score = torch.zeros(N, device=dev)
+    item_pinned = torch.zeros(N, dtype=torch.uint8, device=dev)
+    keep = torch.zeros(B, dtype=torch.int32, device=dev)
+    n_keep = torch.zeros(1, dtype=torch.int64, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    old_pos = torch.arange(N, dtype=torch.int32, device=dev)
+    new_pos = torch.zeros(B, dtype=torch.int32, device=dev)
+    dst_k = torch.zeros((NL, B // w.page_size, w.page_size, HKV, D), dtype=torch.bfloat16, device=dev)
+    dst_v = torch.zeros_like(dst_k)
+    dst_accum = torch.zeros(B, device=dev)
+    dst_span = torch.zeros(B, dtype=torch.int32, device=dev)
+    src = kv.PagedCache(k, v, N)
+    dst = kv.PagedCache(dst_k, dst_v, B)
+    score_kw = dict(policy="h2o", window=W, item_tokens=1, accum=accum, span_id=span_id,
+                    span_next_use=next_use, bonus_floor=50000.0, n_sink=w.n_sink, n_recent=w.n_recent,
+                    item_score=item_score, item_pinned=item_pinned)
+    ws_score = torch.empty(kv.kv_score_workspace_size(src, q, **score_kw), dtype=torch.uint8, device=dev)
+    ws_sel = torch.empty(kv.kv_select_workspace_size(N), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    hip = HipEvents()
+    n_ev = 8
+
+    def step(ev):
+        kv.kv_score(src, q, workspace=ws_score, stage_events=ctypes.cast(ev, ctypes.c_void_p), **score_kw)
+        kv.kv_select(item_score, item_pinned, 1, N, B, keep, n_keep, status, workspace=ws_sel)
+        hip.record(ev[5], sh)
+        kv.kv_compact_rerope(src, dst, keep, n_keep, B, old_pos, new_pos, renumber_base=0,
+                             rope_theta=w.rope_theta, limit=w.limit,
+                             meta=[(accum, dst_accum), (span_id, dst_span)])
+        hip.record(ev[6], sh)
+
+    warm = hip.create(n_ev)
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    events = [hip.create(n_ev) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    assert int(status.item()) == 0 and int(n_keep.item()) == B
+
+    def avg(a, b):
+        return sum(hip.ms(e[a], e[b]) for e in events) / len(events)
+
+    t_lse, t_comb, t_mass, t_epi = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    t_sel, t_cmp = avg(4, 5), avg(5, 6)
+    k_bytes = NL * N * HKV * D * 2
+    q_bytes = NL * W * HQ * D * 2
+    flops = 2.0 * NL * HQ * W * N * D
+    cmp_bytes = 2 * B * w.kv_bytes_per_token
+    kern = {
+        "lse_pass": {"ms": t_lse, "bytes": k_bytes + q_bytes, "flops": flops},
+        "mass_pass": {"ms": t_mass, "bytes": k_bytes + q_bytes, "flops": flops},
+        "compact_rerope": {"ms": t_cmp, "bytes": cmp_bytes, "flops": 0.0},
+    }
+    for name, r in kern.items():
+        r["gbs"] = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+        r["hbm_frac"] = r["gbs"] / HBM_PEAK_GBS
+        r["mfma_frac"] = r["flops"] / (r["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    dom = max(("lse_pass", "mass_pass"), key=lambda n: kern[n]["ms"])
+    traffic = measured_traffic(dom)
+    result = {
+        "metric": "KV tokens scored+evicted+compacted/sec (all layers)",
+        "value": N / (ms_step * 1e-3),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_layers": NL, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
+                   "n_tokens": N, "window": W, "budget_tokens": B, "page_size": w.page_size,
+                   "policy": "h2o+foresight", "renumber_limit": w.limit},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(kern[dom]["gbs"], 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern[dom]["hbm_frac"], 4),
+                     "traffic": traffic,
+                     "mfma_tflops": round(kern[dom]["flops"] / (kern[dom]["ms"] * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(kern[dom]["mfma_frac"], 4)},
+        "stages_ms": {"lse_pass": round(t_lse, 4), "lse_combine": round(t_comb, 4),
+                      "mass_pass": round(t_mass, 4), "epilogue": round(t_epi, 4),
+                      "select": round(t_sel, 4), "compact_rerope": round(t_cmp, 4)},
+        "compact_rerope": {"achieved": round(kern["compact_rerope"]["gbs"], 1), "unit": "GB/s",
+                           "frac": round(kern["compact_rerope"]["hbm_frac"], 4)},
+    }
+    print(f"[bench] {ms_step:.3f} ms/step; stages {result['stages_ms']}", file=sys.stderr, flush=True)
+    del k, v, dst_k, dst_v, ws_score
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_layers)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,7 +67,8 @@ class KvScoreParams(ctypes.Structure):
                 ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
                 ("token_pinned", ctypes.c_void_p), ("mass", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p), ("token_score", ctypes.c_void_p),
-                ("item_score", ctypes.c_void_p), ("item_pinned", ctypes.c_void_p)]
+                ("item_score", ctypes.c_void_p), ("item_pinned", ctypes.c_void_p),
+                ("stage_events", ctypes.c_void_p)]
 
 
 _lib = None
@@ -184,7 +185,7 @@ def _score_params(q, *, policy, window, item_tokens, scale=0.0, dt_steps=1, lse_
                   ewma=None, clock=None, accum=None, span_id=None, span_next_use=None,
                   bonus_floor=50000.0, pinned_regions=0, n_sink=0, n_recent=0,
                   token_pinned=None, mass=None, lse=None, token_score=None, item_score=None,
-                  item_pinned=None):
+                  item_pinned=None, stage_events=None):
     pol = {"memdecay": KV_POLICY_MEMDECAY, "h2o": KV_POLICY_H2O}.get(policy, policy)
     n_regions = int(base_prio.numel()) if base_prio is not None else 0
     n_spans = int(span_next_use.numel()) if span_next_use is not None else 0
@@ -194,7 +195,7 @@ def _score_params(q, *, policy, window, item_tokens, scale=0.0, dt_steps=1, lse_
         float(rho), float(alpha), float(tau), _ptr(ewma), _ptr(clock), _ptr(accum),
         _ptr(span_id), _ptr(span_next_use), n_spans, float(bonus_floor), int(pinned_regions),
         int(n_sink), int(n_recent), _ptr(token_pinned), _ptr(mass), _ptr(lse),
-        _ptr(token_score), _ptr(item_score), _ptr(item_pinned))
+        _ptr(token_score), _ptr(item_score), _ptr(item_pinned), stage_events)
 
 
 def kv_score_workspace_size(cache: PagedCache, q, **kw) -> int:

@@ -203,9 +203,13 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   sa.lse2 = (const float*)(w + L.off_lse2);
   sa.mass_part = (float*)(w + L.off_mass);
 
+  hipEvent_t* ev = p->stage_events;
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  if ((e = mark(0)) != hipSuccess) return hip_fail(e);
   if (!p->lse_in) {
     if ((e = launch_score_pass(sa, false, stream)) != hipSuccess) return hip_fail(e);
   }
+  if ((e = mark(1)) != hipSuccess) return hip_fail(e);
   CombineArgs ca;
   ca.lse_part = sa.lse_part;
   ca.n_chunks = L.n_chunks;
@@ -220,7 +224,9 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   ca.lse2 = (float*)(w + L.off_lse2);
   ca.lse_out = p->lse;
   if ((e = launch_lse_combine(ca, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = mark(2)) != hipSuccess) return hip_fail(e);
   if ((e = launch_score_pass(sa, true, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = mark(3)) != hipSuccess) return hip_fail(e);
 
   EpilogueArgs ea;
   memset(&ea, 0, sizeof(ea));
@@ -254,6 +260,7 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   ea.item_score = p->item_score;
   ea.item_pinned = p->item_pinned;
   if ((e = launch_epilogue(ea, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = mark(4)) != hipSuccess) return hip_fail(e);
   return KV_OK;
 }
 

@@ -149,6 +149,9 @@ typedef struct kv_score_params {
   float *token_score;         /* [N] or NULL */
   float *item_score;          /* [ceil(N/item_tokens)] */
   uint8_t *item_pinned;       /* [ceil(N/item_tokens)] */
+  /* profiling (optional): host array of 5 events, recorded on the stream before the LSE
+     pass, after it, after the LSE combine, after the mass pass and after the epilogue */
+  hipEvent_t *stage_events;
 } kv_score_params;
 
 int32_t kv_abi_version(void);
