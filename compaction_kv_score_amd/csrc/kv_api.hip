@@ -62,7 +62,7 @@ int32_t check_cache(const kv_cache_desc* c) {
 }
 
 struct ScoreLayout {
-  int rows, group, n_chunks, chunk;
+  int rows, group, n_chunks, chunk, n_rsplit;
   size_t off_lse_part, off_lse2, off_mass, total;
 };
 
@@ -79,10 +79,12 @@ int32_t score_layout(const kv_cache_desc* c, const kv_score_params* p, ScoreLayo
   if (rows > kMaxRows) return KV_EUNSUPPORTED;
   // chunk: a multiple of the 64-key tile, large enough to amortise the query load and
   // small enough that the grid has thousands of workgroups
+  const int n_rsplit = (int)((rows + kRowsPerGroup - 1) / kRowsPerGroup);
   const int64_t units = (int64_t)c->n_layers * c->n_kv_heads;
   int64_t chunk = 4096;
-  while (chunk > 256 && units * ((c->n_tokens + chunk - 1) / chunk) < 2048) chunk >>= 1;
+  while (chunk > 256 && units * n_rsplit * ((c->n_tokens + chunk - 1) / chunk) < 2048) chunk >>= 1;
   L->rows = (int)rows;
+  L->n_rsplit = n_rsplit;
   L->group = group;
   L->chunk = (int)chunk;
   L->n_chunks = (int)((c->n_tokens + chunk - 1) / chunk);
@@ -92,7 +94,7 @@ int32_t score_layout(const kv_cache_desc* c, const kv_score_params* p, ScoreLayo
   L->off_lse2 = off;
   off = align256(off + (size_t)units * rows * sizeof(float));
   L->off_mass = off;
-  off = align256(off + (size_t)units * c->n_tokens * sizeof(float));
+  off = align256(off + (size_t)units * n_rsplit * c->n_tokens * sizeof(float));
   L->total = off;
   return KV_OK;
 }
@@ -196,6 +198,7 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   sa.window = p->window;
   sa.group = L.group;
   sa.rows = L.rows;
+  sa.n_rsplit = L.n_rsplit;
   sa.c = c2;
   sa.chunk = L.chunk;
   sa.n_chunks = L.n_chunks;
@@ -231,7 +234,7 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   EpilogueArgs ea;
   memset(&ea, 0, sizeof(ea));
   ea.mass_part = sa.mass_part;
-  ea.n_parts = n_lg;
+  ea.n_parts = n_lg * L.n_rsplit;
   ea.n_tokens = c->n_tokens;
   ea.mass_norm = 1.0 / ((double)c->n_layers * p->n_q_heads * p->window);
   ea.policy = p->policy;

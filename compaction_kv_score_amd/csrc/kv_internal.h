@@ -10,11 +10,12 @@ namespace kvs {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kHeadDim = 128;
 constexpr int kTile = 64;          // keys per scoring tile
-constexpr int kLdsStride = 136;    // bf16 elements per key row in LDS (128 + 8 padding)
-constexpr int kMaxRows = 512;      // G*W rows per (layer, KV head): 8 waves x 64 rows
+constexpr int kMaxRows = 512;      // G*W rows per (layer, KV head)
+constexpr int kRowsPerGroup = 256; // rows one scoring workgroup covers: 8 waves x 32 rows
 
 // Physical element offset of token j's row start (head 0, dim 0) inside one layer.
 __device__ __forceinline__ int64_t token_offset(int64_t j, int page_shift, int64_t page_stride,
@@ -35,11 +36,12 @@ struct ScoreArgs {
   int64_t n_tokens;
   const uint16_t* q;            // bf16 bits [L][W][Hq][128]
   int n_q_heads, window, group, rows;
+  int n_rsplit;                 // workgroups sharing the rows of one (layer, KV head)
   float c;                      // scale * log2(e)
   int chunk, n_chunks;
   float2* lse_part;             // [L*Hkv][n_chunks][rows] (max, sum) in log2 units
   const float* lse2;            // [L*Hkv][rows] log2-unit LSE (pass 2 input)
-  float* mass_part;             // [L*Hkv][N]
+  float* mass_part;             // [L*Hkv][n_rsplit][N]
 };
 
 hipError_t launch_score_pass(const ScoreArgs& a, bool pass2, hipStream_t s);

@@ -9,15 +9,23 @@
 //   pass 2: mass_part[l,g][j] = sum_r exp(s_rj - LSE_r)
 //
 // Work decomposition: one workgroup per (layer, KV head, chunk of keys).  Its waves
-// each own 64 of the G*W rows and keep those rows' queries in registers as MFMA A
-// operands for the whole chunk; 64-key tiles of K are staged through LDS (double
-// buffered, 16-byte global loads, padded rows against bank conflicts) and shared by
-// all waves as B operands of v_mfma_f32_16x16x32_bf16.  Logits stay in the fp32
-// accumulators and are consumed in registers: nothing of size rows x N is stored.
+// each own 64 of the G*W rows and keep those rows' queries in registers as MFMA
+// operands for the whole chunk.  64-key tiles of K (16 KiB) stream into a ring of LDS
+// buffers by direct global->LDS 16-byte loads issued several tiles ahead, so HBM
+// latency hides behind tiles of work and no VGPRs stage the data.  Rows are stored
+// with an XOR swizzle of their 16-byte pieces, which keeps the loads coalesced (every
+// 16 lanes read one 256-byte key row) and the fragment reads free of bank conflicts.
+// Page addresses are wave-uniform: a wave-wide load covers 4 keys of one page.
+//
+// Inside a tile each wave works on 32-key halves with two accumulator sets: it computes
+// the logits of one half (v_mfma_f32_32x32x16_bf16) while turning the previous half into
+// exponentials, and the two waves sharing a SIMD order these parts oppositely, so that
+// the matrix core and the vector ALU overlap instead of taking turns.  Logits stay in fp32 accumulators and are consumed in registers: nothing
+// of size rows x N is stored.
 //
 // Exponentials use exp2 with the scale folded into c = scale * log2(e).  Pass 1 keeps
-// a running reference per lane and row and rescales only when a tile's sum would leave
-// the safe range (the first tile always does), so the steady state costs one fma, one
+// a running reference per lane and row and rescales only when a half's sum would leave
+// the safe range (the first half always does), so the steady state costs one fma, one
 // exp and one add per logit.  All reductions have a fixed order: results do not depend
 // on scheduling.
 #include "kv_internal.h"
@@ -26,27 +34,70 @@ namespace kvs {
 
 namespace {
 
+constexpr int kStages = 4;                          // K tiles resident in LDS
+constexpr int kAhead = kStages - 1;                 // prefetch distance in tiles
+static_assert(kStages >= 3, "a stage is refilled one barrier after its last read");
+constexpr int kRowBytes = kHeadDim * 2;             // 256 B per key row
+constexpr int kTileBytes = kTile * kRowBytes;       // 16 KiB
+constexpr int kLoadsPerTile = kTileBytes / 1024;    // wave-wide 16-byte loads per tile
+
+// s_waitcnt immediate for gfx9: vmcnt <= vm, lgkmcnt <= lgkm, expcnt unconstrained.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
+}
+
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Shared pieces of both passes: query fragments in registers, K tiles through LDS.
+// Compiler-only fence: keeps LDS accesses on their side of a hand-placed barrier.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte global -> LDS load of every lane: lane L's 16 bytes land at lds + 16*L.  It is
+// issued from inline assembly so that the compiler does not track it: otherwise it
+// would conservatively wait for these loads before every LDS read, which would undo the
+// prefetch.  Completion is awaited explicitly with vmcnt before the barrier that
+// publishes a tile (all waits in this file are hand-placed for that reason).
+__device__ __forceinline__ void dma16(const void* src, const uint8_t* lds) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)lds);
+  uint32_t saved;
+  // M0 carries the LDS destination; the previous M0 is restored so that the compiler's
+  // own view of M0 stays valid.  The wait state separates the M0 write from its use.
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(dst)
+      : "memory");
+}
+
+// Everything a workgroup needs to locate its keys and queries.  The G*W rows of one
+// (layer, KV head) are split into groups of at most 256 rows, one workgroup each; wave
+// wv owns rows row0 + 32*wv .. row0 + 32*wv + 31 of its group.
 template <int NW>
-struct TileCtx {
-  static constexpr int NT = NW * 64;
-  static constexpr int kPieces = kTile * 16;           // 16-byte pieces per K tile
-  static constexpr int PPT = (kPieces + NT - 1) / NT;  // pieces per thread
+struct Ctx {
+  static constexpr int LPW = (kLoadsPerTile + NW - 1) / NW;  // loads per wave per tile
+  static constexpr bool kJunk = (kLoadsPerTile % NW) != 0;
 
   const ScoreArgs& a;
-  int tid, lane, wv, chunk_id, g, layer, lg, n_tiles, slot_stride;
+  int lane, wv, chunk_id, rs, row0, g, layer, lg, n_tiles, slot_stride;
   int64_t j0, j1;
   const uint16_t* kbase;
+  int fo[8];                      // per-lane LDS byte offsets of the K fragments (per ks)
+  int voff[LPW];                  // per-lane element offsets of this wave's loads in a page
 
-  __device__ TileCtx(const ScoreArgs& args) : a(args) {
-    tid = threadIdx.x;
-    lane = tid & 63;
-    wv = tid >> 6;
+  __device__ Ctx(const ScoreArgs& args) : a(args) {
+    lane = threadIdx.x & 63;
+    wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int bid = blockIdx.x;
     chunk_id = bid % a.n_chunks;
     bid /= a.n_chunks;
+    rs = bid % a.n_rsplit;
+    bid /= a.n_rsplit;
+    row0 = rs * kRowsPerGroup;
     g = bid % a.n_kv_heads;
     layer = bid / a.n_kv_heads;
     lg = layer * a.n_kv_heads + g;
@@ -55,294 +106,427 @@ struct TileCtx {
     n_tiles = (int)((j1 - j0 + kTile - 1) / kTile);
     slot_stride = a.n_kv_heads * kHeadDim;
     kbase = a.k + (int64_t)layer * a.layer_stride + g * kHeadDim;
+    // key row kk = 32*kb + lane%32 holds dims 16*ks + 8*(lane/32) in piece
+    // c16 = 2*ks + lane/32, stored at piece slot c16 ^ (kk % 16)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      fo[ks] = (lane & 31) * kRowBytes + (((2 * ks + (lane >> 5)) ^ (lane & 15)) << 4);
+#pragma unroll
+    for (int m = 0; m < LPW; ++m) {
+      const int row = 4 * load_slot(m) + (lane >> 4);
+      voff[m] = (lane >> 4) * slot_stride + (((lane & 15) ^ (row & 15)) << 3);
+    }
   }
 
-  // Query rows 64*wv + 16*blk + lane%16 as 16x16x32 fragments (dims 32*ks + 8*(lane/16)).
-  __device__ void load_queries(bf16x8 (&qf)[4][4]) const {
+  // Query row row0 + 32*wv + lane%32 as 32x32x16 fragments: dims 16*ks + 8*(lane/32).
+  __device__ void load_queries(bf16x8 (&qf)[8]) const {
     const int W = a.window;
+    const int row = row0 + wv * 32 + (lane & 31);
+    if (row < a.rows) {
+      const int hl = row / W;
+      const int w = row - hl * W;
+      const int h = g * a.group + hl;
+      const uint16_t* qp =
+          a.q + (((int64_t)layer * W + w) * a.n_q_heads + h) * kHeadDim + 8 * (lane >> 5);
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const int row = wv * 64 + blk * 16 + (lane & 15);
-      if (row < a.rows) {
-        const int hl = row / W;
-        const int w = row - hl * W;
-        const int h = g * a.group + hl;
-        const uint16_t* qp =
-            a.q + (((int64_t)layer * W + w) * a.n_q_heads + h) * kHeadDim + 8 * (lane >> 4);
+      for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
+    } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qf[blk][ks] = *(const bf16x8*)(qp + 32 * ks);
-      } else {
+      for (int ks = 0; ks < 8; ++ks) qf[ks] = bf16x8{};
+    }
+  }
+
+  // Load slots of this wave: wave wv fills rows 4*LPW*wv .. 4*LPW*(wv+1)-1 of a tile,
+  // 4 rows per wave-wide load.  When 16 is not a multiple of NW the surplus loads of
+  // the last waves go to a junk buffer, so every wave has the same number in flight.
+  __device__ __forceinline__ int load_slot(int m) const {
+    const int i = wv * LPW + m;
+    return kJunk && i >= kLoadsPerTile ? kLoadsPerTile - 1 : i;
+  }
+
+  __device__ __forceinline__ bool uniform_tile(int t) const {
+    return a.page_shift >= 2 && j0 + (int64_t)(t + 1) * kTile <= j1;
+  }
+
+  // Physical pages of this wave's loads of tile t (scalar loads, issued one iteration
+  // before they are needed so that their latency hides behind a tile of work).
+  __device__ __forceinline__ void fetch_pages(int t, const int32_t* __restrict__ bt,
+                                              int32_t (&ph)[LPW]) const {
+    if (!uniform_tile(t)) return;
+    const int64_t tile_j0 = j0 + (int64_t)t * kTile;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qf[blk][ks] = bf16x8{};
+    for (int m = 0; m < LPW; ++m) {
+      const int64_t page = (tile_j0 + 4 * load_slot(m)) >> a.page_shift;
+      ph[m] = bt ? bt[page] : (int32_t)page;
+    }
+  }
+
+  // Loads of a full tile whose pages are wave-uniform (page size >= 4): the per-lane part
+  // of every address is precomputed.
+  __device__ __forceinline__ void issue_fast(int t, uint8_t* stage, uint8_t* junk,
+                                             const int32_t (&ph)[LPW]) const {
+    const int64_t tile_j0 = j0 + (int64_t)t * kTile;
+    const int64_t pmask = (1LL << a.page_shift) - 1;
+#pragma unroll
+    for (int m = 0; m < LPW; ++m) {
+      const int i = load_slot(m);
+      uint8_t* dst = kJunk && wv * LPW + m >= kLoadsPerTile ? junk : stage + i * 1024;
+      const uint16_t* base =
+          kbase + (int64_t)ph[m] * a.page_stride + ((tile_j0 + 4 * i) & pmask) * slot_stride;
+      dma16(base + voff[m], dst);
+    }
+  }
+
+  // Issue this wave's direct-to-LDS loads of tile t into `stage`.  Load slot i fills
+  // rows 4i..4i+3; lane L carries piece (L%16) ^ (row%16) of row 4i + L/16, so it lands
+  // in swizzled position.  Keys past the chunk end are clamped to the last valid key
+  // (their logits are masked later).
+  __device__ void issue_tile(int t, uint8_t* stage, uint8_t* junk, const int32_t* __restrict__ bt,
+                             const int32_t (&ph)[LPW]) const {
+    const int64_t tile_j0 = j0 + (int64_t)t * kTile;
+    if (uniform_tile(t)) {
+      // a wave-wide load reads 4 keys of one page: the page address is wave-uniform
+      const int64_t pmask = (1LL << a.page_shift) - 1;
+#pragma unroll
+      for (int m = 0; m < LPW; ++m) {
+        const int i = load_slot(m);
+        uint8_t* dst = kJunk && wv * LPW + m >= kLoadsPerTile ? junk : stage + i * 1024;
+        const int row = 4 * i + (lane >> 4);
+        const int c16 = (lane & 15) ^ (row & 15);
+        const uint16_t* base =
+            kbase + (int64_t)ph[m] * a.page_stride + ((tile_j0 + 4 * i) & pmask) * slot_stride;
+        dma16(base + (lane >> 4) * slot_stride + c16 * 8, dst);
+      }
+    } else {
+      // small pages or the chunk's ragged last tile: per-lane addresses
+#pragma unroll
+      for (int m = 0; m < LPW; ++m) {
+        const int i = load_slot(m);
+        uint8_t* dst = kJunk && wv * LPW + m >= kLoadsPerTile ? junk : stage + i * 1024;
+        const int row = 4 * i + (lane >> 4);
+        const int c16 = (lane & 15) ^ (row & 15);
+        int64_t j = tile_j0 + row;
+        if (j >= j1) j = j1 - 1;
+        const uint16_t* src =
+            kbase + token_offset(j, a.page_shift, a.page_stride, bt, slot_stride) + c16 * 8;
+        dma16(src, dst);
       }
     }
   }
 
-  __device__ void load_tile(int t, uint4 (&r)[PPT]) const {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + i * NT;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (p < kPieces) {
-        const int key = p >> 4;
-        const int c16 = p & 15;
-        const int64_t j = j0 + (int64_t)t * kTile + key;
-        if (j < j1) {
-          const int64_t off = token_offset(j, a.page_shift, a.page_stride, a.block_table, slot_stride);
-          v = *(const uint4*)(kbase + off + c16 * 8);
-        }
-      }
-      r[i] = v;
+  // Wait until at most `pending` tiles of this wave's loads are still in flight (the
+  // newest ones), make this wave's LDS writes visible, then synchronise the workgroup.
+  __device__ __forceinline__ void wait_and_barrier(int pending) const {
+    compiler_fence();
+    static_assert(kAhead <= 5, "wait cases below cover up to 4 pending tiles");
+    switch (pending) {
+      case 0: __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(waitcnt_imm(LPW, 0)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * LPW, 0)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * LPW, 0)); break;
+      default: __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * LPW, 0)); break;
     }
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
   }
 
-  __device__ void store_tile(uint16_t* buf, const uint4 (&r)[PPT]) const {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + i * NT;
-      if (p < kPieces) *(uint4*)&buf[(p >> 4) * kLdsStride + (p & 15) * 8] = r[i];
-    }
-  }
-
-  // K fragment of keys 16*kb + lane%16, dims 32*ks + 8*(lane/16), from an LDS tile.
-  __device__ bf16x8 key_frag(const uint16_t* buf, int kb, int ks) const {
-    return *(const bf16x8*)&buf[(16 * kb + (lane & 15)) * kLdsStride + 32 * ks + 8 * (lane >> 4)];
+  // K fragment of half `half` (keys 32*half + lane%32), dims 16*ks + 8*(lane/32).
+  __device__ __forceinline__ bf16x8 key_frag(const uint8_t* tile, int half, int ks) const {
+    return *(const bf16x8*)(tile + half * 32 * kRowBytes + fo[ks]);
   }
 };
 
-// Pass 1: per-chunk (max, sum) of 2^(c*s) for every row, computed as S^T = K Q^T so that
-// each lane holds 4 query rows x 16 keys of a tile and the running softmax state is
-// lane-local (4 maxima, 4 sums).
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 2) void lse_pass_kernel(ScoreArgs a) {
-  using Ctx = TileCtx<NW>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kTile * kLdsStride];
-  const Ctx x(a);
-  const int lane = x.lane;
-  const float c = a.c;
-  const int W = a.window;
-  const int64_t first_partial_key = a.n_tokens - W;  // keys above it are hidden from some rows
+// --------------------------------------------------------------------------- pipeline
+// The tile loop shared by both passes.  Pass P provides mma(tile, half, acc) (the
+// logits of one 32-key half), consume<kMask>(acc, half_j0, half, cb) (the VALU work on
+// them), between(t, cb) (after the barrier that ends tile t's reads) and finish().
+// Each iteration computes the logits of the next half while the previous half goes
+// through exp, so the matrix core and the vector ALU have independent work in flight.
+// The steady-state loop covers tiles that are full, visible to every row and loaded
+// through the fast page path; the remaining tiles take the general loop with every
+// check in place.
+template <int NW, class P>
+__device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[kTileBytes],
+                                          uint8_t* junk, const int32_t* __restrict__ bt) {
+  const int nt = x.n_tiles;
+  // full tiles (all 64 keys before the chunk end) with wave-uniform pages
+  const int nf = x.a.page_shift >= 2 ? (int)((x.j1 - x.j0) / kTile) : 0;
+  // clean tiles: full and every key visible to every window row
+  const int64_t last_clean_key = x.a.n_tokens - x.a.window;
+  const int64_t clean_end = x.j1 < last_clean_key + 1 ? x.j1 : last_clean_key + 1;
+  const int nc = clean_end > x.j0 ? (int)((clean_end - x.j0) / kTile) : 0;
 
-  bf16x8 qf[4][4];
-  x.load_queries(qf);
-  // this lane's query rows: 64*wv + 16*qb + lane%16
-  int wq[4];
-#pragma unroll
-  for (int qb = 0; qb < 4; ++qb) wq[qb] = (x.wv * 64 + 16 * qb + (lane & 15)) % W;
-
-  float m[4], l[4];
-#pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    m[qb] = -1e30f;
-    l[qb] = 0.f;
+  int32_t ph[Ctx<NW>::LPW] = {};
+  for (int t = 0; t < kAhead && t < nt; ++t) {
+    x.fetch_pages(t, bt, ph);
+    x.issue_tile(t, kt[t], junk, bt, ph);
   }
+  if (kAhead < nt) x.fetch_pages(kAhead, bt, ph);
+  x.wait_and_barrier((nt < kAhead ? nt : kAhead) - 1);
 
-  uint4 pre[Ctx::PPT];
-  x.load_tile(0, pre);
-  x.store_tile(lds[0], pre);
-  __syncthreads();
-
-  for (int t = 0; t < x.n_tiles; ++t) {
-    const uint16_t* cur = lds[t & 1];
-    if (t + 1 < x.n_tiles) x.load_tile(t + 1, pre);
-
-    // acc[kb][qb]: C[key][query], lane holds query 16*qb + lane%16, keys 16*kb + 4*(lane/16) + i
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) acc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 kf = x.key_frag(cur, kb, ks);
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
-          acc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], acc[kb][qb], 0, 0, 0);
-      }
-    }
-
-    const int64_t tile_j0 = x.j0 + (int64_t)t * kTile;
-    if (tile_j0 + kTile - 1 > first_partial_key) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t j = tile_j0 + 16 * kb + 4 * (lane >> 4) + i;
-#pragma unroll
-          for (int qb = 0; qb < 4; ++qb)
-            if (j >= x.j1 || j > first_partial_key + wq[qb]) acc[kb][qb][i] = -INFINITY;
-        }
-    }
-
-    float ts[4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      float s = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s += exp2f_fast(__builtin_fmaf(acc[kb][qb][i], c, -m[qb]));
-      ts[qb] = s;
-    }
-    const float mx = fmaxf(fmaxf(ts[0], ts[1]), fmaxf(ts[2], ts[3]));
-    // rescale when a tile sum left [0, 2^64]; always on the first tile (m = -1e30)
-    if (__builtin_amdgcn_ballot_w64(!(mx <= 0x1p64f)) != 0) {
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, acc[kb][qb][i] * c);
-        const float mn = fmaxf(m[qb], tmax);
-        l[qb] *= exp2f_fast(m[qb] - mn);
-        m[qb] = mn;
-        float s = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s += exp2f_fast(__builtin_fmaf(acc[kb][qb][i], c, -mn));
-        ts[qb] = s;
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) l[qb] += ts[qb];
-
-    if (t + 1 < x.n_tiles) x.store_tile(lds[(t + 1) & 1], pre);
-    __syncthreads();
+  f32x16 acc0, acc1;
+  p.mma(kt[0], 0, acc0);
+  int t = 0, st = 0, cb = 0;  // tile, its LDS stage, its column buffer (t % 3)
+  for (; t + kAhead < nf && t < nc; ++t) {
+    const int64_t tj = x.j0 + (int64_t)t * kTile;
+    const int st1 = st == kStages - 1 ? 0 : st + 1;
+    const int sta = st == 0 ? kStages - 1 : st - 1;   // stage of tile t + kAhead
+    const int cb1 = cb == 2 ? 0 : cb + 1;
+    const int cbp = cb == 0 ? 2 : cb - 1;
+    x.issue_fast(t + kAhead, kt[sta], junk, ph);
+    if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
+    p.mma(kt[st], 1, acc1);
+    p.template consume<false>(acc0, tj, 0, cb);
+    x.wait_and_barrier(kAhead - 1);
+    if (t >= 1) p.between(t - 1, cbp);
+    p.mma(kt[st1], 0, acc0);
+    p.template consume<false>(acc1, tj + 32, 1, cb);
+    st = st1;
+    cb = cb1;
   }
-
-  // combine the 4 lanes holding the same query (lane, lane^16, lane^32, lane^48)
-#pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-#pragma unroll
-    for (int off = 16; off < 64; off <<= 1) {
-      const float mo = __shfl_xor(m[qb], off);
-      const float lo = __shfl_xor(l[qb], off);
-      const float mn = fmaxf(m[qb], mo);
-      l[qb] = l[qb] * exp2f_fast(m[qb] - mn) + lo * exp2f_fast(mo - mn);
-      m[qb] = mn;
-    }
+  for (; t < nt; ++t) {
+    const int64_t tj = x.j0 + (int64_t)t * kTile;
+    const int st1 = st == kStages - 1 ? 0 : st + 1;
+    const int sta = st == 0 ? kStages - 1 : st - 1;
+    const int cb1 = cb == 2 ? 0 : cb + 1;
+    const int cbp = cb == 0 ? 2 : cb - 1;
+    if (t + kAhead < nt) x.issue_tile(t + kAhead, kt[sta], junk, bt, ph);
+    if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
+    p.mma(kt[st], 1, acc1);
+    if (tj + 31 > last_clean_key || tj + 32 > x.j1)
+      p.template consume<true>(acc0, tj, 0, cb);
+    else
+      p.template consume<false>(acc0, tj, 0, cb);
+    // tile t+1 must be resident; tiles t+2 .. t+kAhead may still be loading
+    const int issued = t + kAhead < nt ? t + kAhead : nt - 1;
+    x.wait_and_barrier(issued - (t + 1) > 0 ? issued - (t + 1) : 0);
+    if (t >= 1) p.between(t - 1, cbp);
+    if (t + 1 < nt) p.mma(kt[st1], 0, acc0);
+    if (tj + 63 > last_clean_key || tj + 64 > x.j1)
+      p.template consume<true>(acc1, tj + 32, 1, cb);
+    else
+      p.template consume<false>(acc1, tj + 32, 1, cb);
+    st = st1;
+    cb = cb1;
   }
-  if (lane < 16) {
-    float2* out = a.lse_part + ((int64_t)x.lg * a.n_chunks + x.chunk_id) * a.rows;
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const int row = x.wv * 64 + 16 * qb + lane;
-      if (row < a.rows) out[row] = make_float2(m[qb], l[qb]);
-    }
-  }
+  x.wait_and_barrier(0);
+  p.finish(nt - 1, cb == 0 ? 2 : cb - 1);
 }
 
-// Pass 2: mass_part[l,g][j] = sum over rows of 2^(c*s - lse2), computed as S = Q K^T so
-// that each lane holds 16 rows x 4 keys of a tile and the per-key sums are lane-local.
+// --------------------------------------------------------------------------- pass 1
+// S^T = K Q^T: each lane holds one query row (row0 + 32*wv + lane%32) against 16 keys of
+// a half (8*(i/4) + 4*(lane/32) + i%4), so the running softmax state is lane-local.
 template <int NW>
-__global__ __launch_bounds__(NW * 64, 2) void mass_pass_kernel(ScoreArgs a) {
-  using Ctx = TileCtx<NW>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kTile * kLdsStride];
-  __shared__ float colp[2][NW][kTile];
-  const Ctx x(a);
-  const int lane = x.lane;
-  const float c = a.c;
-  const int W = a.window;
-  const int64_t N = a.n_tokens;
-  const int64_t first_partial_key = N - W;
+struct LsePass {
+  using C = Ctx<NW>;
+  const C& x;
+  const bf16x8 (&qf)[8];
+  float c;
+  int64_t last_key;               // last key this lane's row may see
+  float m, l;
 
-  bf16x8 qf[4][4];
+  __device__ LsePass(const C& ctx, const bf16x8 (&q)[8]) : x(ctx), qf(q) {
+    c = x.a.c;
+    const int w = (x.row0 + x.wv * 32 + (x.lane & 31)) % x.a.window;
+    last_key = x.a.n_tokens - x.a.window + w;
+    m = -1e30f;
+    l = 0.f;
+  }
+
+  __device__ __forceinline__ void mma(const uint8_t* tile, int half, f32x16& acc) const {
+    bf16x8 kf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = x.key_frag(tile, half, ks);
+    acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], acc, 0, 0, 0);
+  }
+
+  // Bit i set when element i is a key this lane's row must not see (past the chunk
+  // end, or after the row's own position).
+  __device__ uint32_t hidden(int64_t half_j0) const {
+    uint32_t h = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t j = half_j0 + 8 * (i >> 2) + 4 * (x.lane >> 5) + (i & 3);
+      if (j >= x.j1 || j > last_key) h |= 1u << i;
+    }
+    return h;
+  }
+
+  // Sum of 2^(c*s - ref) over the half; hidden keys are excluded through their exponent
+  // argument (the accumulators are only read, never rewritten).
+  template <bool kMask>
+  __device__ __forceinline__ float sums(const f32x16& acc, uint32_t h, float ref) const {
+    float e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float arg = __builtin_fmaf(acc[i], c, -ref);
+      if (kMask && ((h >> i) & 1u)) arg = -INFINITY;
+      e[i] = exp2f_fast(arg);
+    }
+#pragma unroll
+    for (int st = 1; st < 16; st <<= 1)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2 * st) e[i] += e[i + st];
+    return e[0];
+  }
+
+  // Fold a half into the running state, rescaling when its sum left [0, 2^64].
+  template <bool kMask>
+  __device__ __forceinline__ void consume(const f32x16& acc, int64_t half_j0, int, int) {
+    const uint32_t h = kMask ? hidden(half_j0) : 0u;
+    float ts = sums<kMask>(acc, h, m);
+    if (__builtin_amdgcn_ballot_w64(!(ts <= 0x1p64f)) != 0) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (!kMask || !((h >> i) & 1u)) tmax = fmaxf(tmax, acc[i] * c);
+      const float mn = fmaxf(m, tmax);
+      l *= exp2f_fast(m - mn);
+      m = mn;
+      ts = sums<kMask>(acc, h, m);
+    }
+    l += ts;
+  }
+
+  __device__ __forceinline__ void between(int, int) {}
+
+  // combine the two lanes holding the same query (lane, lane^32) and store the chunk's
+  // (max, sum) of the row
+  __device__ void finish(int, int) {
+    const float mo = __shfl_xor(m, 32);
+    const float lo = __shfl_xor(l, 32);
+    const float mn = fmaxf(m, mo);
+    const float ln = l * exp2f_fast(m - mn) + lo * exp2f_fast(mo - mn);
+    const int row = x.row0 + x.wv * 32 + x.lane;
+    if (x.lane < 32 && row < x.a.rows)
+      x.a.lse_part[((int64_t)x.lg * x.a.n_chunks + x.chunk_id) * x.a.rows + row] = make_float2(mn, ln);
+  }
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void lse_pass_kernel(ScoreArgs a,
+                                                             const int32_t* __restrict__ bt) {
+  using C = Ctx<NW>;
+  __shared__ __attribute__((aligned(1024))) uint8_t kt[kStages][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t junk[C::kJunk ? 1024 : 16];
+  const C x(a);
+  bf16x8 qf[8];
   x.load_queries(qf);
-  // C-row cr = 4*rb + i is row 64*wv + 16*rb + 4*(lane/16) + i
-  float nl[16];
+  LsePass<NW> p(x, qf);
+  run_tiles(x, p, kt, junk, bt);
+}
+
+// --------------------------------------------------------------------------- pass 2
+// S = Q K^T: each lane holds one key of a half (32*half + lane%32) against 16 rows
+// (row0 + 32*wv + 8*(i/4) + 4*(lane/32) + i%4), so the per-key row sums are lane-local.
+// Each lane leaves its partial in LDS; after the next barrier 64 threads add the 2*NW
+// partials of each key in a fixed order and store the tile's column sums.
+template <int NW>
+struct MassPass {
+  using C = Ctx<NW>;
+  static constexpr int kColStride = 2 * NW + 1;     // floats per key (partials + pad)
+  const C& x;
+  const bf16x8 (&qf)[8];
+  float (*colp)[kTile * kColStride];
+  float c;
+  float nl[16];                                      // -LSE2 of this lane's rows
+
+  __device__ MassPass(const C& ctx, const bf16x8 (&q)[8], float (*cp)[kTile * kColStride])
+      : x(ctx), qf(q), colp(cp) {
+    c = x.a.c;
 #pragma unroll
-  for (int cr = 0; cr < 16; ++cr) {
-    const int row = x.wv * 64 + (cr >> 2) * 16 + 4 * (lane >> 4) + (cr & 3);
-    nl[cr] = row < a.rows ? -a.lse2[(int64_t)x.lg * a.rows + row] : -INFINITY;
+    for (int i = 0; i < 16; ++i) {
+      const int row = x.row0 + x.wv * 32 + 8 * (i >> 2) + 4 * (x.lane >> 5) + (i & 3);
+      nl[i] = row < x.a.rows ? -x.a.lse2[(int64_t)x.lg * x.a.rows + row] : -INFINITY;
+    }
   }
 
-  uint4 pre[Ctx::PPT];
-  x.load_tile(0, pre);
-  x.store_tile(lds[0], pre);
-  __syncthreads();
+  __device__ __forceinline__ void mma(const uint8_t* tile, int half, f32x16& acc) const {
+    bf16x8 kf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = x.key_frag(tile, half, ks);
+    acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], acc, 0, 0, 0);
+  }
 
-  for (int t = 0; t < x.n_tiles; ++t) {
-    const int buf = t & 1;
-    const uint16_t* cur = lds[buf];
-    if (t + 1 < x.n_tiles) x.load_tile(t + 1, pre);
-
-    // Two halves of 32 keys keep only half of the accumulators live.
-    // acc[rb][kh]: C[row][key], lane holds key 16*(2*half+kh) + lane%16,
-    // rows 16*rb + 4*(lane/16) + i
-    const int64_t tile_j0 = x.j0 + (int64_t)t * kTile;
-    const bool masked = tile_j0 + kTile - 1 > first_partial_key;
+  // Bit i set when row i of this lane must not see its key (past the chunk end, or
+  // after the row's own position).
+  __device__ uint32_t hidden(int64_t half_j0) const {
+    const int64_t j = half_j0 + (x.lane & 31);
+    const int64_t first_partial_key = x.a.n_tokens - x.a.window;
+    uint32_t h = 0;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x4 acc[4][2];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) acc[rb][kh] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const bf16x8 kf = x.key_frag(cur, 2 * half + kh, ks);
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb)
-            acc[rb][kh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[rb][ks], kf, acc[rb][kh], 0, 0, 0);
-        }
-      }
-      if (masked) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int w = (x.wv * 64 + rb * 16 + 4 * (lane >> 4) + i) % W;
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-              const int64_t j = tile_j0 + 16 * (2 * half + kh) + (lane & 15);
-              if (j >= x.j1 || j > first_partial_key + w) acc[rb][kh][i] = -INFINITY;
-            }
-          }
-      }
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        float s = 0.f;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s += exp2f_fast(__builtin_fmaf(acc[rb][kh][i], c, nl[rb * 4 + i]));
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
-        if (lane < 16) colp[buf][x.wv][16 * (2 * half + kh) + lane] = s;
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int w = (x.row0 + x.wv * 32 + 8 * (i >> 2) + 4 * (x.lane >> 5) + (i & 3)) % x.a.window;
+      if (j >= x.j1 || j > first_partial_key + w) h |= 1u << i;
     }
+    return h;
+  }
 
-    if (t + 1 < x.n_tiles) x.store_tile(lds[buf ^ 1], pre);
-    __syncthreads();
+  // Column sum of one half: hidden entries are excluded by their exponent argument (the
+  // accumulators are only read, never rewritten).
+  template <bool kMask>
+  __device__ __forceinline__ void consume(const f32x16& acc, int64_t half_j0, int half, int cb) const {
+    const uint32_t h = kMask ? hidden(half_j0) : 0u;
+    float e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float arg = __builtin_fmaf(acc[i], c, nl[i]);
+      if (kMask && ((h >> i) & 1u)) arg = -INFINITY;
+      e[i] = exp2f_fast(arg);
+    }
+#pragma unroll
+    for (int st = 1; st < 16; st <<= 1)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2 * st) e[i] += e[i + st];
+    colp[cb][(32 * half + (x.lane & 31)) * kColStride + 2 * x.wv + (x.lane >> 5)] = e[0];
+  }
 
-    if (x.tid < kTile) {
-      const int64_t j = tile_j0 + x.tid;
+  // 64 threads: column sums of finished tile t, partials added in a fixed order.
+  __device__ __forceinline__ void between(int t, int cb) const {
+    if (threadIdx.x < kTile) {
+      const int64_t j = x.j0 + (int64_t)t * kTile + threadIdx.x;
       if (j < x.j1) {
-        float s = colp[buf][0][x.tid];
+        const float* q = colp[cb] + threadIdx.x * kColStride;
+        float s = q[0];
 #pragma unroll
-        for (int w2 = 1; w2 < NW; ++w2) s += colp[buf][w2][x.tid];
-        a.mass_part[(int64_t)x.lg * N + j] = s;
+        for (int k = 1; k < 2 * NW; ++k) s += q[k];
+        x.a.mass_part[((int64_t)x.lg * x.a.n_rsplit + x.rs) * x.a.n_tokens + j] = s;
       }
     }
   }
+
+  __device__ void finish(int t, int cb) const { between(t, cb); }
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void mass_pass_kernel(ScoreArgs a,
+                                                              const int32_t* __restrict__ bt) {
+  using C = Ctx<NW>;
+  using P = MassPass<NW>;
+  __shared__ __attribute__((aligned(1024))) uint8_t kt[kStages][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t junk[C::kJunk ? 1024 : 16];
+  __shared__ float colp[3][kTile * P::kColStride];
+  const C x(a);
+  bf16x8 qf[8];
+  x.load_queries(qf);
+  P p(x, qf, colp);
+  run_tiles(x, p, kt, junk, bt);
 }
 
 template <bool PASS2>
 hipError_t launch_nw(const ScoreArgs& a, int nw, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.n_chunks * a.n_kv_heads * a.n_layers));
+  const dim3 grid((unsigned)((int64_t)a.n_chunks * a.n_rsplit * a.n_kv_heads * a.n_layers));
   switch (nw) {
-#define KVS_CASE(NWV)                                                              \
-  case NWV:                                                                        \
-    if (PASS2)                                                                     \
-      hipLaunchKernelGGL((mass_pass_kernel<NWV>), grid, dim3(NWV * 64), 0, s, a);  \
-    else                                                                           \
-      hipLaunchKernelGGL((lse_pass_kernel<NWV>), grid, dim3(NWV * 64), 0, s, a);   \
+#define KVS_CASE(NWV)                                                                          \
+  case NWV:                                                                                    \
+    if (PASS2)                                                                                 \
+      hipLaunchKernelGGL((mass_pass_kernel<NWV>), grid, dim3(NWV * 64), 0, s, a, a.block_table); \
+    else                                                                                       \
+      hipLaunchKernelGGL((lse_pass_kernel<NWV>), grid, dim3(NWV * 64), 0, s, a, a.block_table);  \
     break;
     KVS_CASE(1)
     KVS_CASE(2)
@@ -392,7 +576,8 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
 }  // namespace
 
 hipError_t launch_score_pass(const ScoreArgs& a, bool pass2, hipStream_t s) {
-  const int nw = (a.rows + 63) / 64;
+  const int group_rows = a.rows < kRowsPerGroup ? a.rows : kRowsPerGroup;
+  const int nw = (group_rows + 31) / 32;
   return pass2 ? launch_nw<true>(a, nw, s) : launch_nw<false>(a, nw, s);
 }
 
