@@ -86,7 +86,8 @@ struct Ctx {
   int lane, wv, chunk_id, rs, row0, g, layer, lg, n_tiles, slot_stride;
   int64_t j0, j1;
   const uint16_t* kbase;
-  int fo[8];                      // per-lane LDS byte offsets of the K fragments (per ks)
+  int fo0;                        // per-lane LDS byte offset of K fragment ks = 0; the
+                                  // fragment of k-step ks sits at fo0 ^ (ks << 5)
   int voff[LPW];                  // per-lane element offsets of this wave's loads in a page
 
   __device__ Ctx(const ScoreArgs& args) : a(args) {
@@ -108,9 +109,9 @@ struct Ctx {
     kbase = a.k + (int64_t)layer * a.layer_stride + g * kHeadDim;
     // key row kk = 32*kb + lane%32 holds dims 16*ks + 8*(lane/32) in piece
     // c16 = 2*ks + lane/32, stored at piece slot c16 ^ (kk % 16)
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      fo[ks] = (lane & 31) * kRowBytes + (((2 * ks + (lane >> 5)) ^ (lane & 15)) << 4);
+    // piece slot (2*ks + lane/32) ^ (lane%16) = ((lane/32) ^ (lane%16)) ^ 2*ks, so the
+    // k-step only flips bits 5..7 of the byte offset
+    fo0 = (lane & 31) * kRowBytes + (((lane >> 5) ^ (lane & 15)) << 4);
 #pragma unroll
     for (int m = 0; m < LPW; ++m) {
       const int row = 4 * load_slot(m) + (lane >> 4);
@@ -232,20 +233,23 @@ struct Ctx {
 
   // K fragment of half `half` (keys 32*half + lane%32), dims 16*ks + 8*(lane/32).
   __device__ __forceinline__ bf16x8 key_frag(const uint8_t* tile, int half, int ks) const {
-    return *(const bf16x8*)(tile + half * 32 * kRowBytes + fo[ks]);
+    return *(const bf16x8*)(tile + half * 32 * kRowBytes + (fo0 ^ (ks << 5)));
   }
 };
 
 // --------------------------------------------------------------------------- pipeline
 // The tile loop shared by both passes.  Pass P provides mma(tile, half, acc) (the
 // logits of one 32-key half), consume<kMask>(acc, half_j0, half, cb) (the VALU work on
-// them), between(t, cb) (after the barrier that ends tile t's reads) and finish().
-// Each iteration computes the logits of the next half while the previous half goes
-// through exp, so the matrix core and the vector ALU have independent work in flight.
-// The steady-state loop covers tiles that are full, visible to every row and loaded
-// through the fast page path; the remaining tiles take the general loop with every
-// check in place.
-template <int NW, class P>
+// them), between(t, cb) (after the barrier that closes tile t's partials) and finish().
+// The steady-state loops cover tiles that are full, visible to every row and loaded
+// through the fast page path; the remaining tiles take a general loop with every check
+// in place.  Column buffer cb of tile t is t % 3.
+//
+// kOverlap: each wave computes the logits of the next half while the previous half
+// goes through exp (two accumulator sets), so one wave keeps both the matrix core and
+// the vector ALU busy.  Otherwise each half runs MFMA then exp with one accumulator
+// set and the overlap comes from the other waves resident on the SIMD.
+template <bool kOverlap, int NW, class P>
 __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[kTileBytes],
                                           uint8_t* junk, const int32_t* __restrict__ bt) {
   const int nt = x.n_tiles;
@@ -264,53 +268,86 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
   if (kAhead < nt) x.fetch_pages(kAhead, bt, ph);
   x.wait_and_barrier((nt < kAhead ? nt : kAhead) - 1);
 
-  f32x16 acc0, acc1;
-  p.mma(kt[0], 0, acc0);
-  int t = 0, st = 0, cb = 0;  // tile, its LDS stage, its column buffer (t % 3)
-  for (; t + kAhead < nf && t < nc; ++t) {
-    const int64_t tj = x.j0 + (int64_t)t * kTile;
-    const int st1 = st == kStages - 1 ? 0 : st + 1;
-    const int sta = st == 0 ? kStages - 1 : st - 1;   // stage of tile t + kAhead
-    const int cb1 = cb == 2 ? 0 : cb + 1;
-    const int cbp = cb == 0 ? 2 : cb - 1;
-    x.issue_fast(t + kAhead, kt[sta], junk, ph);
-    if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
-    p.mma(kt[st], 1, acc1);
-    p.template consume<false>(acc0, tj, 0, cb);
-    x.wait_and_barrier(kAhead - 1);
-    if (t >= 1) p.between(t - 1, cbp);
-    p.mma(kt[st1], 0, acc0);
-    p.template consume<false>(acc1, tj + 32, 1, cb);
-    st = st1;
-    cb = cb1;
-  }
-  for (; t < nt; ++t) {
-    const int64_t tj = x.j0 + (int64_t)t * kTile;
-    const int st1 = st == kStages - 1 ? 0 : st + 1;
-    const int sta = st == 0 ? kStages - 1 : st - 1;
-    const int cb1 = cb == 2 ? 0 : cb + 1;
-    const int cbp = cb == 0 ? 2 : cb - 1;
-    if (t + kAhead < nt) x.issue_tile(t + kAhead, kt[sta], junk, bt, ph);
-    if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
-    p.mma(kt[st], 1, acc1);
-    if (tj + 31 > last_clean_key || tj + 32 > x.j1)
-      p.template consume<true>(acc0, tj, 0, cb);
-    else
+  // hidden keys exist only in halves that reach past the last clean key or the chunk end
+  auto masked = [&](int64_t hj) { return hj + 31 > last_clean_key || hj + 32 > x.j1; };
+  int t = 0, st = 0, cb = 0;  // tile, its LDS stage, its column buffer
+  if (kOverlap) {
+    f32x16 acc0, acc1;
+    p.mma(kt[0], 0, acc0);
+    for (; t + kAhead < nf && t < nc; ++t) {
+      const int64_t tj = x.j0 + (int64_t)t * kTile;
+      const int st1 = st == kStages - 1 ? 0 : st + 1;
+      const int sta = st == 0 ? kStages - 1 : st - 1;   // stage of tile t + kAhead
+      const int cbp = cb == 0 ? 2 : cb - 1;
+      x.issue_fast(t + kAhead, kt[sta], junk, ph);
+      if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
+      p.mma(kt[st], 1, acc1);
       p.template consume<false>(acc0, tj, 0, cb);
-    // tile t+1 must be resident; tiles t+2 .. t+kAhead may still be loading
-    const int issued = t + kAhead < nt ? t + kAhead : nt - 1;
-    x.wait_and_barrier(issued - (t + 1) > 0 ? issued - (t + 1) : 0);
-    if (t >= 1) p.between(t - 1, cbp);
-    if (t + 1 < nt) p.mma(kt[st1], 0, acc0);
-    if (tj + 63 > last_clean_key || tj + 64 > x.j1)
-      p.template consume<true>(acc1, tj + 32, 1, cb);
-    else
+      x.wait_and_barrier(kAhead - 1);
+      if (t >= 1) p.between(t - 1, cbp);
+      p.mma(kt[st1], 0, acc0);
       p.template consume<false>(acc1, tj + 32, 1, cb);
-    st = st1;
-    cb = cb1;
+      st = st1;
+      cb = cb == 2 ? 0 : cb + 1;
+    }
+    for (; t < nt; ++t) {
+      const int64_t tj = x.j0 + (int64_t)t * kTile;
+      const int st1 = st == kStages - 1 ? 0 : st + 1;
+      const int sta = st == 0 ? kStages - 1 : st - 1;
+      const int cbp = cb == 0 ? 2 : cb - 1;
+      if (t + kAhead < nt) x.issue_tile(t + kAhead, kt[sta], junk, bt, ph);
+      if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
+      p.mma(kt[st], 1, acc1);
+      if (masked(tj)) p.template consume<true>(acc0, tj, 0, cb);
+      else p.template consume<false>(acc0, tj, 0, cb);
+      // tile t+1 must be resident; tiles t+2 .. t+kAhead may still be loading
+      const int issued = t + kAhead < nt ? t + kAhead : nt - 1;
+      x.wait_and_barrier(issued - (t + 1) > 0 ? issued - (t + 1) : 0);
+      if (t >= 1) p.between(t - 1, cbp);
+      if (t + 1 < nt) p.mma(kt[st1], 0, acc0);
+      if (masked(tj + 32)) p.template consume<true>(acc1, tj + 32, 1, cb);
+      else p.template consume<false>(acc1, tj + 32, 1, cb);
+      st = st1;
+      cb = cb == 2 ? 0 : cb + 1;
+    }
+    x.wait_and_barrier(0);
+    p.between(nt - 1, cb == 0 ? 2 : cb - 1);
+  } else {
+    f32x16 acc;
+    for (; t + kAhead < nf && t < nc; ++t) {
+      const int64_t tj = x.j0 + (int64_t)t * kTile;
+      const int sta = st == 0 ? kStages - 1 : st - 1;
+      x.issue_fast(t + kAhead, kt[sta], junk, ph);
+      if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
+      p.mma(kt[st], 0, acc);
+      p.template consume<false>(acc, tj, 0, cb);
+      p.mma(kt[st], 1, acc);
+      p.template consume<false>(acc, tj + 32, 1, cb);
+      x.wait_and_barrier(kAhead - 1);
+      p.between(t, cb);
+      st = st == kStages - 1 ? 0 : st + 1;
+      cb = cb == 2 ? 0 : cb + 1;
+    }
+    for (; t < nt; ++t) {
+      const int64_t tj = x.j0 + (int64_t)t * kTile;
+      const int sta = st == 0 ? kStages - 1 : st - 1;
+      if (t + kAhead < nt) x.issue_tile(t + kAhead, kt[sta], junk, bt, ph);
+      if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int64_t hj = tj + 32 * half;
+        p.mma(kt[st], half, acc);
+        if (masked(hj)) p.template consume<true>(acc, hj, half, cb);
+        else p.template consume<false>(acc, hj, half, cb);
+      }
+      const int issued = t + kAhead < nt ? t + kAhead : nt - 1;
+      x.wait_and_barrier(issued - (t + 1) > 0 ? issued - (t + 1) : 0);
+      p.between(t, cb);
+      st = st == kStages - 1 ? 0 : st + 1;
+      cb = cb == 2 ? 0 : cb + 1;
+    }
   }
-  x.wait_and_barrier(0);
-  p.finish(nt - 1, cb == 0 ? 2 : cb - 1);
+  p.finish();
 }
 
 // --------------------------------------------------------------------------- pass 1
@@ -334,12 +371,16 @@ struct LsePass {
   }
 
   __device__ __forceinline__ void mma(const uint8_t* tile, int half, f32x16& acc) const {
-    bf16x8 kf[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kf[ks] = x.key_frag(tile, half, ks);
     acc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], acc, 0, 0, 0);
+    for (int k0 = 0; k0 < 8; k0 += 4) {
+      bf16x8 kf[8];
+#pragma unroll
+      for (int ks = k0; ks < k0 + 4; ++ks) kf[ks] = x.key_frag(tile, half, ks);
+#pragma unroll
+      for (int ks = k0; ks < k0 + 4; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], acc, 0, 0, 0);
+    }
   }
 
   // Bit i set when element i is a key this lane's row must not see (past the chunk
@@ -358,18 +399,15 @@ struct LsePass {
   // argument (the accumulators are only read, never rewritten).
   template <bool kMask>
   __device__ __forceinline__ float sums(const f32x16& acc, uint32_t h, float ref) const {
-    float e[16];
+    float r[4];                                      // four running partial sums
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float arg = __builtin_fmaf(acc[i], c, -ref);
       if (kMask && ((h >> i) & 1u)) arg = -INFINITY;
-      e[i] = exp2f_fast(arg);
+      const float e = exp2f_fast(arg);
+      r[i & 3] = i < 4 ? e : r[i & 3] + e;
     }
-#pragma unroll
-    for (int st = 1; st < 16; st <<= 1)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2 * st) e[i] += e[i + st];
-    return e[0];
+    return (r[0] + r[1]) + (r[2] + r[3]);
   }
 
   // Fold a half into the running state, rescaling when its sum left [0, 2^64].
@@ -394,7 +432,7 @@ struct LsePass {
 
   // combine the two lanes holding the same query (lane, lane^32) and store the chunk's
   // (max, sum) of the row
-  __device__ void finish(int, int) {
+  __device__ void finish() {
     const float mo = __shfl_xor(m, 32);
     const float lo = __shfl_xor(l, 32);
     const float mn = fmaxf(m, mo);
@@ -405,9 +443,18 @@ struct LsePass {
   }
 };
 
+// Two workgroups per CU need ceil(2*NW/4) waves per SIMD: 3 for five or six waves (at
+// most 168 VGPRs per lane), 4 for eight (at most 128).  amdgpu_waves_per_eu makes the
+// register allocator honour that; smaller workgroups are bound by LDS instead.
+#ifndef KVS_LSE_OVERLAP
+#define KVS_LSE_OVERLAP true
+#endif
+#ifndef KVS_MASS_OVERLAP
+#define KVS_MASS_OVERLAP false
+#endif
+
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void lse_pass_kernel(ScoreArgs a,
-                                                             const int32_t* __restrict__ bt) {
+__device__ __forceinline__ void lse_pass_body(const ScoreArgs& a, const int32_t* __restrict__ bt) {
   using C = Ctx<NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t kt[kStages][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t junk[C::kJunk ? 1024 : 16];
@@ -415,14 +462,30 @@ __global__ __launch_bounds__(NW * 64) void lse_pass_kernel(ScoreArgs a,
   bf16x8 qf[8];
   x.load_queries(qf);
   LsePass<NW> p(x, qf);
-  run_tiles(x, p, kt, junk, bt);
+  run_tiles<KVS_LSE_OVERLAP>(x, p, kt, junk, bt);
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void lse_pass_kernel(ScoreArgs a, const int32_t* __restrict__ bt) {
+  lse_pass_body<NW>(a, bt);
+}
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void lse_pass_kernel_3w(
+    ScoreArgs a, const int32_t* __restrict__ bt) {
+  lse_pass_body<NW>(a, bt);
+}
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void lse_pass_kernel_4w(
+    ScoreArgs a, const int32_t* __restrict__ bt) {
+  lse_pass_body<NW>(a, bt);
 }
 
 // --------------------------------------------------------------------------- pass 2
 // S = Q K^T: each lane holds one key of a half (32*half + lane%32) against 16 rows
 // (row0 + 32*wv + 8*(i/4) + 4*(lane/32) + i%4), so the per-key row sums are lane-local.
-// Each lane leaves its partial in LDS; after the next barrier 64 threads add the 2*NW
-// partials of each key in a fixed order and store the tile's column sums.
+// Each lane leaves its partial in LDS; after the barrier that closes the tile 64
+// threads add the 2*NW partials of each key in a fixed order and store the tile's
+// column sums (two column buffers alternate between tiles).
 template <int NW>
 struct MassPass {
   using C = Ctx<NW>;
@@ -430,26 +493,46 @@ struct MassPass {
   const C& x;
   const bf16x8 (&qf)[8];
   float (*colp)[kTile * kColStride];
+  const float* nlw;                                  // -LSE2 of this wave's 32 rows (LDS)
   float c;
-  float nl[16];                                      // -LSE2 of this lane's rows
 
-  __device__ MassPass(const C& ctx, const bf16x8 (&q)[8], float (*cp)[kTile * kColStride])
+  // nls: LDS block of NW*32 floats; each wave stores -LSE2 of its rows (-inf past the
+  // last row).  Only the owning wave reads them, so no barrier is needed.
+  __device__ MassPass(const C& ctx, const bf16x8 (&q)[8], float (*cp)[kTile * kColStride],
+                      float* nls)
       : x(ctx), qf(q), colp(cp) {
     c = x.a.c;
+    float* own = nls + x.wv * 32;
+    if (x.lane < 32) {
+      const int row = x.row0 + x.wv * 32 + x.lane;
+      own[x.lane] = row < x.a.rows ? -x.a.lse2[(int64_t)x.lg * x.a.rows + row] : -INFINITY;
+    }
+    nlw = own;
+  }
+
+  // -LSE2 of this lane's 16 rows 8*(i/4) + 4*(lane/32) + i%4, as four float4 reads
+  __device__ __forceinline__ void load_nl(float (&nl)[16]) const {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = x.row0 + x.wv * 32 + 8 * (i >> 2) + 4 * (x.lane >> 5) + (i & 3);
-      nl[i] = row < x.a.rows ? -x.a.lse2[(int64_t)x.lg * x.a.rows + row] : -INFINITY;
+    for (int g = 0; g < 4; ++g) {
+      const float4 v = *(const float4*)(nlw + 8 * g + 4 * (x.lane >> 5));
+      nl[4 * g] = v.x;
+      nl[4 * g + 1] = v.y;
+      nl[4 * g + 2] = v.z;
+      nl[4 * g + 3] = v.w;
     }
   }
 
   __device__ __forceinline__ void mma(const uint8_t* tile, int half, f32x16& acc) const {
-    bf16x8 kf[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kf[ks] = x.key_frag(tile, half, ks);
     acc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], acc, 0, 0, 0);
+    for (int k0 = 0; k0 < 8; k0 += 4) {
+      bf16x8 kf[8];
+#pragma unroll
+      for (int ks = k0; ks < k0 + 4; ++ks) kf[ks] = x.key_frag(tile, half, ks);
+#pragma unroll
+      for (int ks = k0; ks < k0 + 4; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], acc, 0, 0, 0);
+    }
   }
 
   // Bit i set when row i of this lane must not see its key (past the chunk end, or
@@ -471,18 +554,18 @@ struct MassPass {
   template <bool kMask>
   __device__ __forceinline__ void consume(const f32x16& acc, int64_t half_j0, int half, int cb) const {
     const uint32_t h = kMask ? hidden(half_j0) : 0u;
-    float e[16];
+    float nl[16];
+    load_nl(nl);
+    float r[4];                                      // four running partial sums
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float arg = __builtin_fmaf(acc[i], c, nl[i]);
       if (kMask && ((h >> i) & 1u)) arg = -INFINITY;
-      e[i] = exp2f_fast(arg);
+      const float e = exp2f_fast(arg);
+      r[i & 3] = i < 4 ? e : r[i & 3] + e;
     }
-#pragma unroll
-    for (int st = 1; st < 16; st <<= 1)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2 * st) e[i] += e[i + st];
-    colp[cb][(32 * half + (x.lane & 31)) * kColStride + 2 * x.wv + (x.lane >> 5)] = e[0];
+    colp[cb][(32 * half + (x.lane & 31)) * kColStride + 2 * x.wv + (x.lane >> 5)] =
+        (r[0] + r[1]) + (r[2] + r[3]);
   }
 
   // 64 threads: column sums of finished tile t, partials added in a fixed order.
@@ -499,43 +582,58 @@ struct MassPass {
     }
   }
 
-  __device__ void finish(int t, int cb) const { between(t, cb); }
+  __device__ __forceinline__ void finish() const {}
 };
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void mass_pass_kernel(ScoreArgs a,
-                                                              const int32_t* __restrict__ bt) {
+__device__ __forceinline__ void mass_pass_body(const ScoreArgs& a, const int32_t* __restrict__ bt) {
   using C = Ctx<NW>;
   using P = MassPass<NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t kt[kStages][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t junk[C::kJunk ? 1024 : 16];
   __shared__ float colp[3][kTile * P::kColStride];
+  __shared__ __attribute__((aligned(16))) float nls[NW * 32];
   const C x(a);
   bf16x8 qf[8];
   x.load_queries(qf);
-  P p(x, qf, colp);
-  run_tiles(x, p, kt, junk, bt);
+  P p(x, qf, colp, nls);
+  run_tiles<KVS_MASS_OVERLAP>(x, p, kt, junk, bt);
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void mass_pass_kernel(ScoreArgs a, const int32_t* __restrict__ bt) {
+  mass_pass_body<NW>(a, bt);
+}
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void mass_pass_kernel_3w(
+    ScoreArgs a, const int32_t* __restrict__ bt) {
+  mass_pass_body<NW>(a, bt);
+}
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void mass_pass_kernel_4w(
+    ScoreArgs a, const int32_t* __restrict__ bt) {
+  mass_pass_body<NW>(a, bt);
 }
 
 template <bool PASS2>
 hipError_t launch_nw(const ScoreArgs& a, int nw, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)a.n_chunks * a.n_rsplit * a.n_kv_heads * a.n_layers));
   switch (nw) {
-#define KVS_CASE(NWV)                                                                          \
-  case NWV:                                                                                    \
-    if (PASS2)                                                                                 \
-      hipLaunchKernelGGL((mass_pass_kernel<NWV>), grid, dim3(NWV * 64), 0, s, a, a.block_table); \
-    else                                                                                       \
-      hipLaunchKernelGGL((lse_pass_kernel<NWV>), grid, dim3(NWV * 64), 0, s, a, a.block_table);  \
+#define KVS_CASE(NWV, SUFFIX)                                                                        \
+  case NWV:                                                                                           \
+    if (PASS2)                                                                                        \
+      hipLaunchKernelGGL((mass_pass_kernel##SUFFIX<NWV>), grid, dim3(NWV * 64), 0, s, a, a.block_table); \
+    else                                                                                              \
+      hipLaunchKernelGGL((lse_pass_kernel##SUFFIX<NWV>), grid, dim3(NWV * 64), 0, s, a, a.block_table);  \
     break;
-    KVS_CASE(1)
-    KVS_CASE(2)
-    KVS_CASE(3)
-    KVS_CASE(4)
-    KVS_CASE(5)
-    KVS_CASE(6)
-    KVS_CASE(7)
-    KVS_CASE(8)
+    KVS_CASE(1, )
+    KVS_CASE(2, )
+    KVS_CASE(3, )
+    KVS_CASE(4, )
+    KVS_CASE(5, _3w)
+    KVS_CASE(6, _3w)
+    KVS_CASE(7, )
+    KVS_CASE(8, _4w)
 #undef KVS_CASE
     default:
       return hipErrorInvalidValue;
