@@ -30,9 +30,19 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
   float score = 0.f;
   int pinned = 0;
   if (valid) {
+    // fixed-order float64 sum of the partials; loads are issued 8 at a time so that
+    // enough of them are in flight
     double msum = 0.0;
     const float* mp = a.mass_part + i;
-    for (int p = 0; p < a.n_parts; ++p) msum += (double)mp[(int64_t)p * N];
+    int p = 0;
+    for (; p + 8 <= a.n_parts; p += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = mp[(int64_t)(p + k) * N];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) msum += (double)v[k];
+    }
+    for (; p < a.n_parts; ++p) msum += (double)mp[(int64_t)p * N];
     const float mass = (float)msum;
     if (a.mass) a.mass[i] = mass;
 

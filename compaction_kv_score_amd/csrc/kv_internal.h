@@ -109,11 +109,12 @@ struct SelectArgs {
   int64_t* n_keep;
   uint32_t* status;
   SelectState* st;
-  uint32_t* hist;                // [n_blocks][256]
+  uint32_t* hist;                // [n_blocks][kSelBins]
   int64_t* counts;               // [n_blocks][2]
   int n_blocks;
   int64_t per_block;             // items per block
 };
+constexpr int kSelBins = 2048;     // radix-select histogram bins (11-bit digits)
 int select_blocks(int64_t n_items);
 size_t select_workspace_bytes(int64_t n_items);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);

@@ -8,8 +8,8 @@
 // emitted as an ascending list of token indices so that compaction preserves order.
 //
 // Steps, all on the device (no host synchronisation; n_keep stays in device memory):
-//   1. four histogram passes over 8-bit digits of an order-preserving uint32 key, most
-//      significant first.  Each block builds a private LDS histogram of the candidates
+//   1. three histogram passes over 11-, 11- and 10-bit digits of an order-preserving
+//      uint32 key, most significant first.  Each block builds a private LDS histogram of the candidates
 //      that still match the digits fixed so far; the last block to finish (atomic
 //      ticket) sums the block histograms in block order and fixes the next digit.
 //      Afterwards T is the key of the K-th best unpinned item and k_rem is how many
@@ -18,6 +18,7 @@
 //   3. an emit pass: every block derives its output offset from the counts of the
 //      blocks before it, then walks its items in index order with wavefront ballots and
 //      an LDS scan across waves, and writes the kept token indices.
+
 #include "kv_internal.h"
 
 namespace kvs {
@@ -27,6 +28,7 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kSelMaxBlocks = 64;
 constexpr int kWaves = kSelThreads / 64;
+constexpr int kBins = kSelBins;
 
 __device__ __forceinline__ uint32_t order_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -39,12 +41,35 @@ __device__ __forceinline__ bool item_pinned(const SelectArgs& a, int64_t i) {
   return a.pinned != nullptr && a.pinned[i] != 0;
 }
 
+// Add 1 to bin[d] for every lane with `want`.  Scores of a long row are concentrated in
+// a few bins, so the lanes sharing the most common digits are merged into one atomic
+// each first and only the rest are added one by one.
+__device__ __forceinline__ void hist_add(uint32_t* bin, bool want, uint32_t d) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    const uint64_t act = __builtin_amdgcn_ballot_w64(want);
+    if (act == 0) return;
+    const int leader = __builtin_ctzll(act);
+    const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
+    const uint64_t same = __builtin_amdgcn_ballot_w64(want && d == dl);
+    if (lane == leader) atomicAdd(&bin[dl], (uint32_t)__popcll(same));
+    if (d == dl) want = false;
+  }
+  if (want) atomicAdd(&bin[d], 1u);
+}
+
+// Digit widths of the three MSB-first passes: 11, 11 and 10 bits.
+__device__ __forceinline__ int pass_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__device__ __forceinline__ uint32_t pass_dmask(int pass) { return pass == 2 ? 1023u : 2047u; }
+
 __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, int pass) {
-  __shared__ uint32_t h[256];
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t s_wsum[kWaves];
   __shared__ uint32_t s_npin, s_nan;
   __shared__ int s_last;
-  const int tid = threadIdx.x;
-  for (int b = tid; b < 256; b += kSelThreads) h[b] = 0;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int b = tid; b < kBins; b += kSelThreads) h[b] = 0;
   if (tid == 0) {
     s_npin = 0;
     s_nan = 0;
@@ -55,27 +80,28 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
   if (mode != 0) return;  // decided without a radix pass (uniform across the grid)
   const uint32_t prefix = pass == 0 ? 0u : a.st->prefix;
   const uint32_t mask = pass == 0 ? 0u : a.st->mask;
-  const int shift = 24 - 8 * pass;
+  const int shift = pass_shift(pass);
+  const uint32_t dmask = pass_dmask(pass);
 
   const int64_t begin = (int64_t)blockIdx.x * a.per_block;
   const int64_t end = begin + a.per_block < a.n_items ? begin + a.per_block : a.n_items;
   uint32_t npin = 0, nan_seen = 0;
-  for (int64_t i = begin + tid; i < end; i += kSelThreads) {
-    if (item_pinned(a, i)) {
-      ++npin;
-      continue;
-    }
-    const float s = a.score[i];
-    nan_seen |= (s != s) ? 1u : 0u;
-    const uint32_t key = order_key(s);
-    if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+  for (int64_t i0 = begin; i0 < end; i0 += kSelThreads) {
+    const int64_t i = i0 + tid;
+    const bool in = i < end;
+    const bool pin = in && item_pinned(a, i);
+    const float sc = in ? a.score[i] : 0.f;
+    const uint32_t key = order_key(sc);
+    npin += pin ? 1u : 0u;
+    nan_seen |= (in && !pin && sc != sc) ? 1u : 0u;
+    hist_add(h, in && !pin && (key & mask) == prefix, (key >> shift) & dmask);
   }
   if (pass == 0) {
     if (npin) atomicAdd(&s_npin, npin);
     if (nan_seen) atomicOr(&s_nan, 1u);
   }
   __syncthreads();
-  for (int b = tid; b < 256; b += kSelThreads) a.hist[(int64_t)blockIdx.x * 256 + b] = h[b];
+  for (int b = tid; b < kBins; b += kSelThreads) a.hist[(int64_t)blockIdx.x * kBins + b] = h[b];
   if (pass == 0 && tid == 0) {
     a.counts[2 * blockIdx.x] = s_npin;
     a.counts[2 * blockIdx.x + 1] = s_nan;
@@ -87,20 +113,29 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
   if (!s_last) return;
   __threadfence();
 
-  // ---- last block: global histogram in block order, then fix this pass's digit
-  for (int b = tid; b < 256; b += kSelThreads) {
+  // ---- last block: global histogram (blocks summed in order), then the digit
+  const int nb = (int)gridDim.x;
+  for (int b = tid; b < kBins; b += kSelThreads) {
     uint32_t tot = 0;
-    for (int blk = 0; blk < (int)gridDim.x; ++blk)
-      tot += __atomic_load_n(&a.hist[(int64_t)blk * 256 + b], __ATOMIC_RELAXED);
+    int blk = 0;
+    for (; blk + 8 <= nb; blk += 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[k] = __atomic_load_n(&a.hist[(int64_t)(blk + k) * kBins + b], __ATOMIC_RELAXED);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) tot += v[k];
+    }
+    for (; blk < nb; ++blk) tot += __atomic_load_n(&a.hist[(int64_t)blk * kBins + b], __ATOMIC_RELAXED);
     h[b] = tot;
   }
-  __syncthreads();
+  __shared__ SelectState st;
   if (tid == 0) {
-    SelectState st = *a.st;
+    st = *a.st;
     if (pass == 0) {
       int64_t n_pin = 0;
       uint32_t nan_any = 0;
-      for (int blk = 0; blk < (int)gridDim.x; ++blk) {
+      for (int blk = 0; blk < nb; ++blk) {
         n_pin += __atomic_load_n(&a.counts[2 * blk], __ATOMIC_RELAXED);
         nan_any |= (uint32_t)__atomic_load_n(&a.counts[2 * blk + 1], __ATOMIC_RELAXED);
       }
@@ -113,21 +148,41 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
       st.k_rem = k;
       st.mode = k >= st.n_cand ? 1u : (k <= 0 ? 2u : 0u);
     }
-    if (st.mode == 0) {
-      int64_t above = 0;
-      int digit = 0;
-      for (int b = 255; b >= 0; --b) {
-        const int64_t cnt = h[b];
-        if (above + cnt >= st.k_rem) {
-          digit = b;
-          break;
-        }
-        above += cnt;
-      }
-      st.k_rem -= above;
-      st.prefix |= (uint32_t)digit << shift;
-      st.mask |= 255u << shift;
+  }
+  __syncthreads();
+  if (st.mode == 0) {
+    // thread t owns bins 2047-2t and 2046-2t (descending); an exclusive scan of the
+    // pair sums locates the bin where the count from the top reaches k_rem
+    const int64_t k_rem = st.k_rem;
+    const uint32_t c0 = h[kBins - 1 - 2 * tid], c1 = h[kBins - 2 - 2 * tid];
+    uint32_t incl = c0 + c1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
     }
+    if (lane == 63) s_wsum[wv] = incl;
+    __syncthreads();
+    int64_t before = 0;
+    for (int w = 0; w < wv; ++w) before += s_wsum[w];
+    const int64_t excl = before + incl - (c0 + c1);
+    int digit = -1;
+    int64_t above = 0;
+    if (excl < k_rem && excl + c0 >= k_rem) {
+      digit = kBins - 1 - 2 * tid;
+      above = excl;
+    } else if (excl + c0 < k_rem && excl + c0 + c1 >= k_rem) {
+      digit = kBins - 2 - 2 * tid;
+      above = excl + c0;
+    }
+    if (digit >= 0) {
+      st.k_rem = k_rem - above;
+      st.prefix |= (uint32_t)digit << shift;
+      st.mask |= dmask << shift;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
     st.ticket = 0;
     *a.st = st;
     __threadfence();
@@ -282,14 +337,14 @@ int select_blocks(int64_t n_items) {
 
 size_t select_workspace_bytes(int64_t n_items) {
   const int nb = select_blocks(n_items);
-  return 256 + (size_t)nb * 256 * sizeof(uint32_t) + (size_t)nb * 2 * sizeof(int64_t);
+  return 256 + (size_t)nb * kBins * sizeof(uint32_t) + (size_t)nb * 2 * sizeof(int64_t);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   hipError_t e = hipMemsetAsync(a.st, 0, sizeof(SelectState), s);
   if (e != hipSuccess) return e;
   const dim3 grid(a.n_blocks), block(kSelThreads);
-  for (int pass = 0; pass < 4; ++pass) {
+  for (int pass = 0; pass < 3; ++pass) {
     hipLaunchKernelGGL(select_hist_kernel, grid, block, 0, s, a, pass);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
