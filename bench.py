@@ -84,6 +84,73 @@ def measured_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
+# rocprofv3 kernel names -> the names used for the roofline, and their sources
+TRAFFIC_KERNELS = {
+    "lse_pass": ("lse_pass_kernel", ["kv_score.hip", "kv_internal.h"]),
+    "mass_pass": ("mass_pass_kernel", ["kv_score.hip", "kv_internal.h"]),
+    "compact_rerope": ("compact_kernel", ["kv_compact.hip", "kv_internal.h"]),
+}
+
+
+def pmc_summary(fetch_dir, write_dir, out_json):
+    """HBM traffic per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE),
+    each holding the bench run (bench_counter_collection.csv) and the 1 GiB copy
+    calibration run (copy_counter_collection.csv).  The counters are in KiB per
+    dispatch; each is scaled by the factor that makes the copy read (write) exactly
+    1 GiB.  Writes out_json and returns a markdown table."""
+    import csv
+    import glob
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return acc
+
+    def find(d, stem):
+        hits = glob.glob(os.path.join(d, "**", f"{stem}_counter_collection.csv"), recursive=True)
+        if not hits:
+            raise SystemExit(f"no {stem}_counter_collection.csv under {d}")
+        return hits[0]
+
+    res = {}
+    calib = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        copy = per_kernel(find(d, "copy"), counter)
+        cvals = [v for k, vs in copy.items() if "copyBuffer" in k for v in vs]
+        if not cvals:
+            raise SystemExit(f"{counter}: no copy kernel in the calibration run")
+        scale = float(1 << 30) / (sum(cvals) / len(cvals))
+        calib[counter] = scale
+        bench = per_kernel(find(d, "bench"), counter)
+        for name, (needle, _) in TRAFFIC_KERNELS.items():
+            vals = [v for k, vs in bench.items() if needle in k for v in vs]
+            if vals:
+                res.setdefault(name, {})[counter] = sum(vals) / len(vals) * scale
+    w = __import__("synth").workload(3)
+    alg = {"lse_pass": w.n_layers * w.n_tokens * w.n_kv_heads * w.head_dim * 2
+                       + w.n_layers * w.window * w.n_q_heads * w.head_dim * 2}
+    alg["mass_pass"] = alg["lse_pass"]
+    alg["compact_rerope"] = 2 * w.budget_tokens * w.kv_bytes_per_token
+    out = {"_calibration": {"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30,
+                            "fetch_scale": calib["FETCH_SIZE"], "write_scale": calib["WRITE_SIZE"]}}
+    rows = ["| Kernel | FETCH (scaled, GB) | WRITE (scaled, GB) | Traffic (GB) | Algorithmic (GB) "
+            "| Traffic / algorithmic |", "|---|---|---|---|---|---|"]
+    for name, v in res.items():
+        f, wr = v.get("FETCH_SIZE", 0.0), v.get("WRITE_SIZE", 0.0)
+        srcs = TRAFFIC_KERNELS[name][1]
+        out[name] = {"bytes_per_launch": f + wr, "fetch_bytes": f, "write_bytes": wr,
+                     "algorithmic_bytes": alg[name], "sources": srcs, "source_hash": source_hash(*srcs)}
+        rows.append(f"| {name} | {f / 1e9:.4f} | {wr / 1e9:.4f} | {(f + wr) / 1e9:.4f} | "
+                    f"{alg[name] / 1e9:.4f} | {(f + wr) / alg[name]:.3f} |")
+    with open(out_json, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return "\n".join(rows) + (f"\n\nscales: FETCH_SIZE x{calib['FETCH_SIZE']:.4f}, "
+                              f"WRITE_SIZE x{calib['WRITE_SIZE']:.4f}")
+
+
 def cpu_baseline(w, layers):
     """The CPU oracle, untuned, on a bounded sample of the workload: attention mass and
     epilogue for `layers` of the 36 layers at full N, selection at full N, compaction of
@@ -132,10 +199,17 @@ def main():
     ap.add_argument("--config", type=int, default=3, help="workload number (3: Qwen3-8B, N=100K)")
     ap.add_argument("--cpu-layers", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn the rocprofv3 FETCH_SIZE / WRITE_SIZE runs (bench + copy calibration "
+                         "in each directory) into profiles/traffic.json and print a table")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) three "
                          "times, to calibrate the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary[0], args.pmc_summary[1],
+                          os.path.join(ROOT, "profiles", "traffic.json")))
+        return
     if args.copy_calibration:
         a = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")
         b = torch.empty_like(a)
