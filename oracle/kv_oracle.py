@@ -106,11 +106,13 @@ def gather_logical(paged, block_table, page_size, n_tokens):
 # O1: windowed attention mass  (MemDecay Method; ActKV Sec. 2.3 and 7.1; PACE Sec. 2)
 # --------------------------------------------------------------------------------------
 
-def attention_mass(q, k, scale=None):
+def attention_mass(q, k, scale=None, lse=None):
     """Windowed softmax attention mass received by every cached token.
 
     q: [L][W][Hq][D] window queries (already rotated at their own positions),
     k: [L][N][Hkv][D] cached keys in logical order.  Returns (mass[N], lse[L][Hq][W]).
+    lse: optional [L][Hq][W] natural-log LSE supplied by the attention backend (ActKV
+    Sec. 7.1 recovers A from it); computed from the keys when None.
 
     For layer l, query head h (KV head g = h // (Hq/Hkv), contiguous GQA groups) and
     window query w, which sits at logical position N - W + w and sees keys j <= N-W+w:
@@ -132,18 +134,65 @@ def attention_mass(q, k, scale=None):
     qpos = n - w_len + np.arange(w_len)
     visible = np.arange(n)[None, :] <= qpos[:, None]          # [W][N]
     mass = np.zeros(n, dtype=np.float64)
-    lse = np.zeros((nl, hq, w_len), dtype=np.float64)
+    lse_out = np.zeros((nl, hq, w_len), dtype=np.float64)
     for layer in range(nl):
         for h in range(hq):
             g = h // g_size
             s = scale * (q[layer, :, h, :] @ k[layer, :, g, :].T)   # [W][N]
             s = np.where(visible, s, -np.inf)
-            m = s.max(axis=1, keepdims=True)
-            row_lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+            if lse is None:
+                m = s.max(axis=1, keepdims=True)
+                row_lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+            else:
+                row_lse = np.asarray(lse, dtype=np.float64)[layer, h]
             a = np.exp(s - row_lse[:, None])                       # 0 where masked
             mass += a.sum(axis=0)
-            lse[layer, h] = row_lse
-    return mass, lse
+            lse_out[layer, h] = row_lse
+    return mass, lse_out
+
+
+def attention_score_max_group(q, k, scale=None, lse=None):
+    """Attention score with the maximum over each GQA group (ActKV Sec. 7.1, Algorithm 3).
+
+    q: [L][W][Hq][D], k: [L][N][Hkv][D] as in attention_mass.  For layer l, KV head g and
+    window (action) query w, a key's attention is the maximum over the query heads h of
+    g's group of A_j = exp(s_j - LSE) (same s, LSE and causal visibility as
+    attention_mass).  ActKV keeps a running mean of it over the action queries; the score
+    here sums it over window queries, KV heads and layers (one keep list serves every
+    layer and head), so that score / (L*Hkv*W) is the mean.
+    lse: optional [L][Hq][W] natural-log LSE supplied by the attention backend (ActKV
+    recovers scores from it); computed from the keys when None.
+    Returns (score[N], lse[L][Hq][W]).
+    Reading: ActKV does not say how the per-(layer, KV head) scores combine into one keep
+    mask; summing them follows MemDecay's averaging over heads and layers.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    nl, w_len, hq, d = q.shape
+    nl2, n, hkv, d2 = k.shape
+    assert nl == nl2 and d == d2 and hq % hkv == 0 and 1 <= w_len <= n
+    g_size = hq // hkv
+    if scale is None or scale == 0:
+        scale = 1.0 / math.sqrt(d)
+    qpos = n - w_len + np.arange(w_len)
+    visible = np.arange(n)[None, :] <= qpos[:, None]          # [W][N]
+    score = np.zeros(n, dtype=np.float64)
+    lse_out = np.zeros((nl, hq, w_len), dtype=np.float64)
+    for layer in range(nl):
+        for g in range(hkv):
+            best = np.zeros((w_len, n), dtype=np.float64)       # max over the group
+            for h in range(g * g_size, (g + 1) * g_size):
+                s = scale * (q[layer, :, h, :] @ k[layer, :, g, :].T)
+                s = np.where(visible, s, -np.inf)
+                if lse is None:
+                    m = s.max(axis=1, keepdims=True)
+                    row_lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+                else:
+                    row_lse = np.asarray(lse, dtype=np.float64)[layer, h]
+                lse_out[layer, h] = row_lse
+                best = np.maximum(best, np.exp(s - row_lse[:, None]))
+            score += best.sum(axis=0)
+    return score, lse_out
 
 
 # --------------------------------------------------------------------------------------
@@ -443,21 +492,33 @@ def simulate_renumbers(session_tokens, budget, limit, headroom):
 def score_step(q, k, *, policy, scale=None, region=None, base_prio=None, decay_rate=None,
                rho=0.9, alpha=1.0, tau=0.01, dt_steps=1, ewma=None, clock=None,
                accum=None, span_id=None, span_next_use=None, bonus_floor=50000.0,
-               pinned_regions=0, n_sink=0, n_recent=0, token_pinned=None, item_tokens=1):
+               pinned_regions=0, n_sink=0, n_recent=0, token_pinned=None, item_tokens=1,
+               aggregate="sum", lse_in=None):
     """Score one eviction step: mass -> policy epilogue -> per-item score and pin flag.
 
-    policy 'memdecay' divides the mass by L*Hq*W ("averaged over heads and layers");
-    policy 'h2o' accumulates the summed mass.  Returns a dict of float64 arrays.
+    aggregate 'sum' sums the attention over every query head (attention_mass);
+    'max_group' takes the maximum over each GQA group first (attention_score_max_group,
+    ActKV).  policy 'memdecay' divides by the number of summed terms, L*Hq*W or L*Hkv*W
+    ("averaged over heads and layers"); policy 'h2o' accumulates the sum.  lse_in is an
+    optional supplied LSE.  Returns a dict of float64 arrays.
     """
-    mass, lse = attention_mass(q, k, scale)
     nl, w_len, hq, _ = np.asarray(q).shape
+    hkv = np.asarray(k).shape[2]
+    if aggregate == "sum":
+        mass, lse = attention_mass(q, k, scale, lse_in)
+        terms = nl * hq * w_len
+    elif aggregate == "max_group":
+        mass, lse = attention_score_max_group(q, k, scale, lse_in)
+        terms = nl * hkv * w_len
+    else:
+        raise ValueError(aggregate)
     n = mass.shape[0]
     bonus = None
     if span_id is not None and span_next_use is not None:
         bonus = token_bonus(span_id, foresight_bonus(span_next_use, bonus_floor))
     out = {"mass": mass, "lse": lse}
     if policy == "memdecay":
-        abar = mass / (nl * hq * w_len)
+        abar = mass / terms
         a, c, s = memdecay_update(abar, region, base_prio, decay_rate, rho, alpha, tau,
                                   dt_steps, ewma, clock, bonus)
         out.update(abar=abar, ewma=a, clock=c, token_score=s)

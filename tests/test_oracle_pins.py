@@ -159,6 +159,75 @@ def test_lse_matches_logsumexp_scipy():
 
 
 # ---------------------------------------------------------------------------------------
+# O1b ActKV aggregation: maximum over each GQA group (Sec. 7.1, Algorithm 3)
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nl,w,hq,hkv,d,n", [(1, 4, 8, 2, 8, 30), (2, 3, 4, 1, 16, 21),
+                                              (1, 2, 8, 1, 8, 9)])
+def test_max_group_matches_torch_sdpa(nl, w, hq, hkv, d, n):
+    """Per (layer, KV head, window query): the maximum over the group's query heads of
+    torch's SDPA attention weights (identity values give o = A), summed."""
+    rng = np.random.default_rng(nl * 1000 + n)
+    q, k = _rand_qk(rng, nl, w, hq, hkv, d, n)
+    score, _ = O.attention_score_max_group(q, k)
+    qpos = n - w + np.arange(w)
+    mask = torch.from_numpy(np.arange(n)[None, :] <= qpos[:, None])
+    g = hq // hkv
+    ref = np.zeros(n)
+    for layer in range(nl):
+        qt = torch.from_numpy(q[layer]).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(k[layer]).permute(1, 0, 2)[None]
+        vt = torch.eye(n, dtype=torch.float64)[None, None].expand(1, hkv, n, n).contiguous()
+        a = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, vt, attn_mask=mask, enable_gqa=True)[0]               # [Hq,W,N]
+        ref += a.reshape(hkv, g, w, n).max(dim=1).values.sum(dim=(0, 1)).numpy()
+    np.testing.assert_allclose(score, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_max_group_one_head_per_group_is_the_sum():
+    rng = np.random.default_rng(11)
+    q, k = _rand_qk(rng, 2, 5, 3, 3, 8, 23)
+    np.testing.assert_allclose(O.attention_score_max_group(q, k)[0], O.attention_mass(q, k)[0],
+                               rtol=1e-13)
+
+
+def test_max_group_identical_heads_closed_form():
+    """Heads of a group that share their queries see the same weights: max = sum / G."""
+    rng = np.random.default_rng(12)
+    nl, w, hkv, g, d, n = 2, 4, 2, 4, 8, 19
+    base = O.bf16_round(rng.standard_normal((nl, w, hkv, d)))
+    q = np.repeat(base, g, axis=2)                                       # [L][W][Hq][D]
+    k = O.bf16_round(rng.standard_normal((nl, n, hkv, d)))
+    np.testing.assert_allclose(O.attention_score_max_group(q, k)[0], O.attention_mass(q, k)[0] / g,
+                               rtol=1e-13)
+
+
+def test_max_group_bounds_and_totals():
+    """max <= sum <= G * max per key; every softmax row sums to 1, so the total score
+    lies between L*Hkv*W and L*Hq*W."""
+    rng = np.random.default_rng(13)
+    nl, w, hq, hkv, d, n = 2, 6, 8, 2, 16, 40
+    q, k = _rand_qk(rng, nl, w, hq, hkv, d, n)
+    smax, _ = O.attention_score_max_group(q, k)
+    ssum, _ = O.attention_mass(q, k)
+    assert (smax <= ssum * (1 + 1e-12)).all() and (ssum <= 4 * smax * (1 + 1e-12)).all()
+    assert nl * hkv * w - 1e-9 <= smax.sum() <= nl * hq * w + 1e-9
+
+
+def test_supplied_lse_closed_forms():
+    """A supplied LSE equal to the true one changes nothing; shifting it by delta scales
+    every recovered weight by exp(-delta) (ActKV Sec. 7.1: A = exp(s - LSE))."""
+    rng = np.random.default_rng(14)
+    q, k = _rand_qk(rng, 2, 3, 8, 2, 8, 15)
+    for fn in (O.attention_mass, O.attention_score_max_group):
+        s0, lse = fn(q, k)
+        s1, _ = fn(q, k, lse=lse)
+        np.testing.assert_allclose(s1, s0, rtol=1e-14)
+        s2, _ = fn(q, k, lse=lse + 0.75)
+        np.testing.assert_allclose(s2, s0 * math.exp(-0.75), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------
 # O2 MemDecay / H2O closed forms
 # ---------------------------------------------------------------------------------------
 
