@@ -30,7 +30,10 @@ KV_STATUS_NAN_SCORE = 2
 KV_STATUS_KEEP_OVERFLOW = 4
 KV_POLICY_MEMDECAY = 0
 KV_POLICY_H2O = 1
+KV_AGG_SUM = 0
+KV_AGG_MAX_GROUP = 1
 KV_MAX_META = 8
+KV_ABI_VERSION = 2  # layout of the structs below
 
 
 class KvError(RuntimeError):
@@ -68,7 +71,7 @@ class KvScoreParams(ctypes.Structure):
                 ("token_pinned", ctypes.c_void_p), ("mass", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p), ("token_score", ctypes.c_void_p),
                 ("item_score", ctypes.c_void_p), ("item_pinned", ctypes.c_void_p),
-                ("stage_events", ctypes.c_void_p)]
+                ("stage_events", ctypes.c_void_p), ("aggregate", ctypes.c_int32)]
 
 
 _lib = None
@@ -102,6 +105,9 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
+        if L.kv_abi_version() != KV_ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.kv_abi_version()}, this binding "
+                               f"expects {KV_ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 
@@ -185,8 +191,9 @@ def _score_params(q, *, policy, window, item_tokens, scale=0.0, dt_steps=1, lse_
                   ewma=None, clock=None, accum=None, span_id=None, span_next_use=None,
                   bonus_floor=50000.0, pinned_regions=0, n_sink=0, n_recent=0,
                   token_pinned=None, mass=None, lse=None, token_score=None, item_score=None,
-                  item_pinned=None, stage_events=None):
+                  item_pinned=None, stage_events=None, aggregate="sum"):
     pol = {"memdecay": KV_POLICY_MEMDECAY, "h2o": KV_POLICY_H2O}.get(policy, policy)
+    agg = {"sum": KV_AGG_SUM, "max_group": KV_AGG_MAX_GROUP}.get(aggregate, aggregate)
     n_regions = int(base_prio.numel()) if base_prio is not None else 0
     n_spans = int(span_next_use.numel()) if span_next_use is not None else 0
     return KvScoreParams(
@@ -195,7 +202,7 @@ def _score_params(q, *, policy, window, item_tokens, scale=0.0, dt_steps=1, lse_
         float(rho), float(alpha), float(tau), _ptr(ewma), _ptr(clock), _ptr(accum),
         _ptr(span_id), _ptr(span_next_use), n_spans, float(bonus_floor), int(pinned_regions),
         int(n_sink), int(n_recent), _ptr(token_pinned), _ptr(mass), _ptr(lse),
-        _ptr(token_score), _ptr(item_score), _ptr(item_pinned), stage_events)
+        _ptr(token_score), _ptr(item_score), _ptr(item_pinned), stage_events, int(agg))
 
 
 def kv_score_workspace_size(cache: PagedCache, q, **kw) -> int:

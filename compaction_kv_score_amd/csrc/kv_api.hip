@@ -62,7 +62,7 @@ int32_t check_cache(const kv_cache_desc* c) {
 }
 
 struct ScoreLayout {
-  int rows, group, n_chunks, chunk, n_rsplit;
+  int rows, group, row_stride, max_log, n_chunks, chunk, n_rsplit;
   size_t off_lse_part, off_lse2, off_mass, total;
 };
 
@@ -75,7 +75,16 @@ int32_t score_layout(const kv_cache_desc* c, const kv_score_params* p, ScoreLayo
   if (p->n_q_heads <= 0 || p->n_q_heads % c->n_kv_heads) return KV_EINVAL;
   if (p->window <= 0 || p->window > c->n_tokens) return KV_EINVAL;
   const int group = p->n_q_heads / c->n_kv_heads;
-  const int64_t rows = (int64_t)group * p->window;
+  // rows per window query: G, or G rounded up to a power of two for the group maximum
+  int row_stride = group, max_log = 0;
+  if (p->aggregate == KV_AGG_MAX_GROUP) {
+    while ((1 << max_log) < group) ++max_log;
+    if (max_log > 5) return KV_EUNSUPPORTED;
+    row_stride = 1 << max_log;
+  } else if (p->aggregate != KV_AGG_SUM) {
+    return KV_EINVAL;
+  }
+  const int64_t rows = (int64_t)row_stride * p->window;
   if (rows > kMaxRows) return KV_EUNSUPPORTED;
   // chunk: a multiple of the 64-key tile, large enough to amortise the query load and
   // small enough that the grid has thousands of workgroups
@@ -86,6 +95,8 @@ int32_t score_layout(const kv_cache_desc* c, const kv_score_params* p, ScoreLayo
   L->rows = (int)rows;
   L->n_rsplit = n_rsplit;
   L->group = group;
+  L->row_stride = row_stride;
+  L->max_log = max_log;
   L->chunk = (int)chunk;
   L->n_chunks = (int)((c->n_tokens + chunk - 1) / chunk);
   size_t off = 0;
@@ -128,7 +139,8 @@ const char* kv_strerror(int32_t code) {
       return "invalid argument (null pointer, size, stride or shape)";
     case KV_EUNSUPPORTED:
       return "unsupported (head_dim != 128, page size not a power of two <= 1024, "
-             "more than 512 rows per KV head, page items above 256 tokens, or not a gfx950 device)";
+             "more than 512 rows per KV head, a GQA group above 32 heads with the group "
+             "maximum, page items above 256 tokens, or not a gfx950 device)";
     case KV_EWORKSPACE:
       return "workspace too small";
     case KV_EHIP:
@@ -198,6 +210,8 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   sa.window = p->window;
   sa.group = L.group;
   sa.rows = L.rows;
+  sa.row_stride = L.row_stride;
+  sa.max_log = L.max_log;
   sa.n_rsplit = L.n_rsplit;
   sa.c = c2;
   sa.chunk = L.chunk;
@@ -221,6 +235,7 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   ca.n_q_heads = p->n_q_heads;
   ca.group = L.group;
   ca.window = p->window;
+  ca.row_stride = L.row_stride;
   ca.n_lg = n_lg;
   ca.c = c2;
   ca.lse_in = p->lse_in;
@@ -236,7 +251,10 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   ea.mass_part = sa.mass_part;
   ea.n_parts = n_lg * L.n_rsplit;
   ea.n_tokens = c->n_tokens;
-  ea.mass_norm = 1.0 / ((double)c->n_layers * p->n_q_heads * p->window);
+  // MemDecay's average over heads and layers: Hq terms per (layer, window query) when
+  // summing, one per KV head when each group contributes its maximum
+  const int terms_per_query = p->aggregate == KV_AGG_MAX_GROUP ? c->n_kv_heads : p->n_q_heads;
+  ea.mass_norm = 1.0 / ((double)c->n_layers * terms_per_query * p->window);
   ea.policy = p->policy;
   ea.item_shift = item_shift;
   ea.dt_steps = p->dt_steps;

@@ -36,6 +36,8 @@ struct ScoreArgs {
   int64_t n_tokens;
   const uint16_t* q;            // bf16 bits [L][W][Hq][128]
   int n_q_heads, window, group, rows;
+  int row_stride;               // rows per window query: row = w * row_stride + h_local
+  int max_log;                  // 0: sum over query heads; m > 0: max over groups of 2^m rows
   int n_rsplit;                 // workgroups sharing the rows of one (layer, KV head)
   float c;                      // scale * log2(e)
   int chunk, n_chunks;
@@ -48,7 +50,7 @@ hipError_t launch_score_pass(const ScoreArgs& a, bool pass2, hipStream_t s);
 
 struct CombineArgs {
   const float2* lse_part;
-  int n_chunks, rows, n_kv_heads, n_q_heads, group, window, n_lg;
+  int n_chunks, rows, n_kv_heads, n_q_heads, group, window, n_lg, row_stride;
   float c;
   const float* lse_in;          // optional natural-log LSE input [L][Hq][W]
   float* lse2;                  // [L*Hkv][rows]
@@ -60,7 +62,7 @@ struct EpilogueArgs {
   const float* mass_part;       // [n_parts][N]
   int n_parts;
   int64_t n_tokens;
-  double mass_norm;             // 1 / (L*Hq*W)
+  double mass_norm;             // 1 / (L*Hq*W), or 1 / (L*Hkv*W) for the group maximum
   int policy, item_shift;       // item_tokens = 1 << item_shift
   int dt_steps;
   const uint8_t* region;

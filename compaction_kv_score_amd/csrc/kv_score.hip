@@ -3,10 +3,19 @@
 // What is computed (MemDecay, Method: windowed attention mass averaged over heads and
 // layers; ActKV Sec. 2.3 and 7.1: A = exp(q.k - LSE) recovered from the log-sum-exp;
 // PACE Sec. 2: SnapKV's observation window):
-//   for every layer l, KV head g and window row r = (query head h in g's GQA group,
-//   window query w), s_rj = scale * <q_r, k_j> over keys j <= N - W + w;
+//   for every layer l, KV head g and window row r = (window query w, query head h of
+//   g's GQA group), s_rj = scale * <q_r, k_j> over keys j <= N - W + w;
 //   pass 1: LSE_r = log sum_j exp(s_rj)   (per key chunk, combined afterwards)
-//   pass 2: mass_part[l,g][j] = sum_r exp(s_rj - LSE_r)
+//   pass 2, sum mode:  mass_part[l,g][j] = sum_r exp(s_rj - LSE_r)
+//   pass 2, max mode (ActKV Sec. 7.1, Algorithm 3):
+//          mass_part[l,g][j] = sum_w max_h exp(s_(w,h)j - LSE_(w,h))
+//                            = sum_w exp(max_h (s_(w,h)j - LSE_(w,h)))
+// Rows are ordered window-query major: r = w * RS + h_local, with RS = G in sum mode and
+// RS = G rounded up to a power of two in max mode (rows with h_local >= G are padding:
+// zero queries and an infinite LSE, so they contribute nothing).  A group then occupies
+// RS consecutive, aligned rows, which the MFMA output layout keeps inside one lane or
+// one lane pair, so the max costs a few v_max and at most one cross-half shuffle, and
+// only one exponential per group is taken.
 //
 // Work decomposition: one workgroup per (layer, KV head, chunk of keys).  Its waves
 // each own 64 of the G*W rows and keep those rows' queries in registers as MFMA
@@ -120,12 +129,13 @@ struct Ctx {
   }
 
   // Query row row0 + 32*wv + lane%32 as 32x32x16 fragments: dims 16*ks + 8*(lane/32).
+  // Padding rows (past the last row, or h_local >= G) get zero queries.
   __device__ void load_queries(bf16x8 (&qf)[8]) const {
     const int W = a.window;
     const int row = row0 + wv * 32 + (lane & 31);
-    if (row < a.rows) {
-      const int hl = row / W;
-      const int w = row - hl * W;
+    const int w = row / a.row_stride;
+    const int hl = row - w * a.row_stride;
+    if (row < a.rows && hl < a.group) {
       const int h = g * a.group + hl;
       const uint16_t* qp =
           a.q + (((int64_t)layer * W + w) * a.n_q_heads + h) * kHeadDim + 8 * (lane >> 5);
@@ -364,7 +374,7 @@ struct LsePass {
 
   __device__ LsePass(const C& ctx, const bf16x8 (&q)[8]) : x(ctx), qf(q) {
     c = x.a.c;
-    const int w = (x.row0 + x.wv * 32 + (x.lane & 31)) % x.a.window;
+    const int w = (x.row0 + x.wv * 32 + (x.lane & 31)) / x.a.row_stride;
     last_key = x.a.n_tokens - x.a.window + w;
     m = -1e30f;
     l = 0.f;
@@ -485,8 +495,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 // (row0 + 32*wv + 8*(i/4) + 4*(lane/32) + i%4), so the per-key row sums are lane-local.
 // Each lane leaves its partial in LDS; after the barrier that closes the tile 64
 // threads add the 2*NW partials of each key in a fixed order and store the tile's
-// column sums (two column buffers alternate between tiles).
-template <int NW>
+// column sums (three column buffers rotate between tiles).
+// kMaxLog = 0: sum over rows.  kMaxLog = m > 0: max over aligned groups of 2^m rows
+// first (RS = 2^m), one exponential per group.
+template <int NW, int kMaxLog>
 struct MassPass {
   using C = Ctx<NW>;
   static constexpr int kColStride = 2 * NW + 1;     // floats per key (partials + pad)
@@ -543,29 +555,85 @@ struct MassPass {
     uint32_t h = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int w = (x.row0 + x.wv * 32 + 8 * (i >> 2) + 4 * (x.lane >> 5) + (i & 3)) % x.a.window;
+      const int w = (x.row0 + x.wv * 32 + 8 * (i >> 2) + 4 * (x.lane >> 5) + (i & 3)) / x.a.row_stride;
       if (j >= x.j1 || j > first_partial_key + w) h |= 1u << i;
     }
     return h;
   }
 
-  // Column sum of one half: hidden entries are excluded by their exponent argument (the
-  // accumulators are only read, never rewritten).
+  // This lane's share of the column sum of one half: hidden entries are excluded by
+  // their exponent argument (the accumulators are only read, never rewritten).
   template <bool kMask>
   __device__ __forceinline__ void consume(const f32x16& acc, int64_t half_j0, int half, int cb) const {
     const uint32_t h = kMask ? hidden(half_j0) : 0u;
     float nl[16];
     load_nl(nl);
-    float r[4];                                      // four running partial sums
+    float part;
+    if constexpr (kMaxLog == 0) {
+      float r[4];                                    // four running partial sums
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float arg = __builtin_fmaf(acc[i], c, nl[i]);
-      if (kMask && ((h >> i) & 1u)) arg = -INFINITY;
-      const float e = exp2f_fast(arg);
-      r[i & 3] = i < 4 ? e : r[i & 3] + e;
+      for (int i = 0; i < 16; ++i) {
+        float arg = __builtin_fmaf(acc[i], c, nl[i]);
+        if (kMask && ((h >> i) & 1u)) arg = -INFINITY;
+        const float e = exp2f_fast(arg);
+        r[i & 3] = i < 4 ? e : r[i & 3] + e;
+      }
+      part = (r[0] + r[1]) + (r[2] + r[3]);
+    } else {
+      float arg[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        arg[i] = __builtin_fmaf(acc[i], c, nl[i]);
+        if (kMask && ((h >> i) & 1u)) arg[i] = -INFINITY;
+      }
+      part = group_max_sum(arg);
     }
-    colp[cb][(32 * half + (x.lane & 31)) * kColStride + 2 * x.wv + (x.lane >> 5)] =
-        (r[0] + r[1]) + (r[2] + r[3]);
+    colp[cb][(32 * half + (x.lane & 31)) * kColStride + 2 * x.wv + (x.lane >> 5)] = part;
+  }
+
+  // Sum over this lane's groups of exp2(max of the group's arguments).  Element i holds
+  // row 8*(i/4) + 4*(lane/32) + i%4 of the wave's 32: groups of 2 and 4 rows lie inside
+  // the lane; a group of 8, 16 or 32 rows spans both halves of the lane pair
+  // (lane, lane ^ 32), which exchange their partial maxima once and split the groups
+  // between them (for 32 rows the upper lane contributes 0).
+  __device__ __forceinline__ float group_max_sum(const float (&arg)[16]) const {
+    if constexpr (kMaxLog == 1) {
+      float r[4];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const float e = exp2f_fast(fmaxf(arg[2 * p], arg[2 * p + 1]));
+        r[p & 3] = p < 4 ? e : r[p & 3] + e;
+      }
+      return (r[0] + r[1]) + (r[2] + r[3]);
+    } else {
+      float v[4];                                    // max over rows 8m + 4*(lane/32) + 0..3
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        v[m] = fmaxf(fmaxf(arg[4 * m], arg[4 * m + 1]), fmaxf(arg[4 * m + 2], arg[4 * m + 3]));
+      if constexpr (kMaxLog == 2) {
+        return (exp2f_fast(v[0]) + exp2f_fast(v[1])) + (exp2f_fast(v[2]) + exp2f_fast(v[3]));
+      } else {
+        const bool upper = x.lane >= 32;
+        if constexpr (kMaxLog == 3) {
+          // lower lane finishes groups 0 and 1, upper lane groups 2 and 3
+          const float r0 = __shfl_xor(upper ? v[0] : v[2], 32);
+          const float r1 = __shfl_xor(upper ? v[1] : v[3], 32);
+          const float g0 = fmaxf(upper ? v[2] : v[0], r0);
+          const float g1 = fmaxf(upper ? v[3] : v[1], r1);
+          return exp2f_fast(g0) + exp2f_fast(g1);
+        } else if constexpr (kMaxLog == 4) {
+          const float u0 = fmaxf(v[0], v[1]);        // rows 0..15
+          const float u1 = fmaxf(v[2], v[3]);        // rows 16..31
+          const float r = __shfl_xor(upper ? u0 : u1, 32);
+          return exp2f_fast(fmaxf(upper ? u1 : u0, r));
+        } else {
+          static_assert(kMaxLog == 5, "groups of at most 32 rows");
+          const float u = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+          const float r = __shfl_xor(u, 32);
+          return upper ? 0.f : exp2f_fast(fmaxf(u, r));
+        }
+      }
+    }
   }
 
   // 64 threads: column sums of finished tile t, partials added in a fixed order.
@@ -585,10 +653,10 @@ struct MassPass {
   __device__ __forceinline__ void finish() const {}
 };
 
-template <int NW>
+template <int NW, int kMaxLog>
 __device__ __forceinline__ void mass_pass_body(const ScoreArgs& a, const int32_t* __restrict__ bt) {
   using C = Ctx<NW>;
-  using P = MassPass<NW>;
+  using P = MassPass<NW, kMaxLog>;
   __shared__ __attribute__((aligned(1024))) uint8_t kt[kStages][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t junk[C::kJunk ? 1024 : 16];
   __shared__ float colp[3][kTile * P::kColStride];
@@ -600,29 +668,31 @@ __device__ __forceinline__ void mass_pass_body(const ScoreArgs& a, const int32_t
   run_tiles<KVS_MASS_OVERLAP>(x, p, kt, junk, bt);
 }
 
-template <int NW>
+template <int NW, int kMaxLog>
 __global__ __launch_bounds__(NW * 64) void mass_pass_kernel(ScoreArgs a, const int32_t* __restrict__ bt) {
-  mass_pass_body<NW>(a, bt);
+  mass_pass_body<NW, kMaxLog>(a, bt);
 }
-template <int NW>
+template <int NW, int kMaxLog>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void mass_pass_kernel_3w(
     ScoreArgs a, const int32_t* __restrict__ bt) {
-  mass_pass_body<NW>(a, bt);
+  mass_pass_body<NW, kMaxLog>(a, bt);
 }
-template <int NW>
+template <int NW, int kMaxLog>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void mass_pass_kernel_4w(
     ScoreArgs a, const int32_t* __restrict__ bt) {
-  mass_pass_body<NW>(a, bt);
+  mass_pass_body<NW, kMaxLog>(a, bt);
 }
 
-template <bool PASS2>
+// MODE < 0: LSE pass; MODE >= 0: mass pass with kMaxLog = MODE.
+template <int MODE>
 hipError_t launch_nw(const ScoreArgs& a, int nw, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)a.n_chunks * a.n_rsplit * a.n_kv_heads * a.n_layers));
   switch (nw) {
 #define KVS_CASE(NWV, SUFFIX)                                                                        \
   case NWV:                                                                                           \
-    if (PASS2)                                                                                        \
-      hipLaunchKernelGGL((mass_pass_kernel##SUFFIX<NWV>), grid, dim3(NWV * 64), 0, s, a, a.block_table); \
+    if constexpr (MODE >= 0)                                                                          \
+      hipLaunchKernelGGL((mass_pass_kernel##SUFFIX<NWV, (MODE < 0 ? 0 : MODE)>), grid, dim3(NWV * 64), \
+                         0, s, a, a.block_table);                                                     \
     else                                                                                              \
       hipLaunchKernelGGL((lse_pass_kernel##SUFFIX<NWV>), grid, dim3(NWV * 64), 0, s, a, a.block_table);  \
     break;
@@ -649,8 +719,12 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
   const int row = (int)(idx - (int64_t)lg * a.rows);
   const int layer = lg / a.n_kv_heads;
   const int g = lg - layer * a.n_kv_heads;
-  const int hl = row / a.window;
-  const int w = row - hl * a.window;
+  const int w = row / a.row_stride;
+  const int hl = row - w * a.row_stride;
+  if (hl >= a.group) {                 // padding row of max mode: weight exp(-inf) = 0
+    a.lse2[idx] = INFINITY;
+    return;
+  }
   const int h = g * a.group + hl;
   const int64_t nat = ((int64_t)layer * a.n_q_heads + h) * a.window + w;
   float lse2;
@@ -676,7 +750,16 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
 hipError_t launch_score_pass(const ScoreArgs& a, bool pass2, hipStream_t s) {
   const int group_rows = a.rows < kRowsPerGroup ? a.rows : kRowsPerGroup;
   const int nw = (group_rows + 31) / 32;
-  return pass2 ? launch_nw<true>(a, nw, s) : launch_nw<false>(a, nw, s);
+  if (!pass2) return launch_nw<-1>(a, nw, s);
+  switch (a.max_log) {
+    case 0: return launch_nw<0>(a, nw, s);
+    case 1: return launch_nw<1>(a, nw, s);
+    case 2: return launch_nw<2>(a, nw, s);
+    case 3: return launch_nw<3>(a, nw, s);
+    case 4: return launch_nw<4>(a, nw, s);
+    case 5: return launch_nw<5>(a, nw, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t s) {

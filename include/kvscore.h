@@ -33,13 +33,15 @@
 extern "C" {
 #endif
 
-#define KV_ABI_VERSION 1
+#define KV_ABI_VERSION 2
 
 /* return codes */
 #define KV_OK 0
 #define KV_EINVAL (-1)        /* null pointer, bad size or stride, W > N, Hq % Hkv != 0 */
 #define KV_EUNSUPPORTED (-2)  /* head_dim != 128, page size not a power of two <= 1024,
-                                 G*W > 512 rows, or the current device is not gfx950 */
+                                 more than 512 window rows per KV head (G*W, or
+                                 pow2ceil(G)*W with KV_AGG_MAX_GROUP), G > 32 with
+                                 KV_AGG_MAX_GROUP, or the device is not gfx950 */
 #define KV_EWORKSPACE (-3)    /* workspace smaller than *_workspace_size reported */
 #define KV_EHIP (-4)          /* a HIP call failed; kv_strerror appends its message */
 #define KV_ELIMIT (-5)        /* renumbered row does not fit under the position limit */
@@ -88,6 +90,9 @@ typedef struct kv_meta_desc {
 #define KV_POLICY_MEMDECAY 0 /* MemDecay region-decay score */
 #define KV_POLICY_H2O 1      /* H2O accumulated attention (PACE's base policy) */
 
+#define KV_AGG_SUM 0         /* sum the weights of every query head */
+#define KV_AGG_MAX_GROUP 1   /* per KV head, the maximum over its GQA group (ActKV) */
+
 /*
  * kv_score parameters.
  *
@@ -96,10 +101,16 @@ typedef struct kv_meta_desc {
  * the W window queries are the last W tokens of the row.  For layer l, query head h
  * (KV head h / (Hq/Hkv)) and window query w at position N-W+w,
  *     s_j = scale * <q[l][w][h], k[l][j][h/G]>  for j <= N-W+w,
- *     LSE = log sum_j exp(s_j),  mass_j = sum_{l,h,w} exp(s_j - LSE).
+ *     LSE = log sum_j exp(s_j),  A_j = exp(s_j - LSE),
+ *     KV_AGG_SUM:        mass_j = sum_{l,h,w} A_j;
+ *     KV_AGG_MAX_GROUP:  mass_j = sum_{l,g,w} max_{h in group g} A_j   (ActKV Sec. 7.1,
+ *                        Algorithm 3: the attention of a KV head is the maximum over
+ *                        the query heads that share it).
+ * When lse_in is given its values are used as LSE (no pass computes it).
  *
  * Policy epilogue, per token i:
- *   MEMDECAY (MemDecay, Method):  Abar = mass / (L*Hq*W);
+ *   MEMDECAY (MemDecay, Method):  Abar = mass / T with T = L*Hq*W terms (KV_AGG_SUM)
+ *       or T = L*Hkv*W (KV_AGG_MAX_GROUP);
  *       ewma <- rho*ewma + (1-rho)*Abar;  clock <- (Abar > tau) ? 0 : clock + dt_steps;
  *       s = base_prio[r]*exp(-decay_rate[r]*clock) + alpha*ewma + bonus
  *   H2O (PACE Sec. 2):  accum <- accum + mass;  s = accum + bonus
@@ -115,7 +126,7 @@ typedef struct kv_meta_desc {
  */
 typedef struct kv_score_params {
   const void *q;              /* bf16 [L][W][Hq][128], rotated at their own positions */
-  int32_t n_q_heads;          /* Hq, multiple of Hkv; G*W <= 512 with G = Hq/Hkv */
+  int32_t n_q_heads;          /* Hq, multiple of Hkv; G = Hq/Hkv (see KV_EUNSUPPORTED) */
   int32_t window;             /* W, 1..N */
   float scale;                /* softmax scale; 0 => 1/sqrt(128) */
   int32_t policy;             /* KV_POLICY_* */
@@ -144,7 +155,7 @@ typedef struct kv_score_params {
   int32_t n_recent;
   const uint8_t *token_pinned; /* [N] or NULL */
   /* outputs */
-  float *mass;                /* [N] summed attention mass, or NULL */
+  float *mass;                /* [N] mass_j as defined above, or NULL */
   float *lse;                 /* [L][Hq][W] natural-log LSE, or NULL */
   float *token_score;         /* [N] or NULL */
   float *item_score;          /* [ceil(N/item_tokens)] */
@@ -152,6 +163,7 @@ typedef struct kv_score_params {
   /* profiling (optional): host array of 5 events, recorded on the stream before the LSE
      pass, after it, after the LSE combine, after the mass pass and after the epilogue */
   hipEvent_t *stage_events;
+  int32_t aggregate;          /* KV_AGG_*; memset-zeroed params select KV_AGG_SUM */
 } kv_score_params;
 
 int32_t kv_abi_version(void);

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     lib = kv.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert kv.kv_abi_version() == 1
+    assert kv.kv_abi_version() == kv.KV_ABI_VERSION == 2
 
 
 def test_strerror_texts():
@@ -87,6 +87,28 @@ def test_score_workspace_size_and_validation():
     # 40 query heads per KV head x 16 window rows = 640 rows > 512
     pp = _score_params(n_q_heads=80, window=16)
     assert L.kv_score_workspace_size(ctypes.byref(c), ctypes.byref(pp), ctypes.byref(n)) == kv.KV_EUNSUPPORTED
+
+
+def test_score_group_maximum_validation():
+    """The group maximum pads each group to a power of two: G = 3 with W = 150 fits as
+    a sum (450 rows) but not as a maximum (4 * 150 = 600 rows); groups above 32 heads
+    and unknown aggregation codes are rejected."""
+    L = kv.lib()
+    n = ctypes.c_size_t()
+    c = _cache(n_tokens=1000, layer_stride=70 * 16 * 2 * 128)
+    size = {}
+    for agg in (kv.KV_AGG_SUM, kv.KV_AGG_MAX_GROUP):
+        p = _score_params(n_q_heads=6, window=100, aggregate=agg)
+        assert L.kv_score_workspace_size(ctypes.byref(c), ctypes.byref(p), ctypes.byref(n)) == kv.KV_OK
+        size[agg] = n.value
+    assert size[kv.KV_AGG_MAX_GROUP] > size[kv.KV_AGG_SUM]  # 400 padded rows vs 300
+    cases = [(_score_params(n_q_heads=6, window=150), kv.KV_OK),
+             (_score_params(n_q_heads=6, window=150, aggregate=kv.KV_AGG_MAX_GROUP), kv.KV_EUNSUPPORTED),
+             (_score_params(n_q_heads=64, window=8, aggregate=kv.KV_AGG_MAX_GROUP), kv.KV_OK),
+             (_score_params(n_q_heads=66, window=4, aggregate=kv.KV_AGG_MAX_GROUP), kv.KV_EUNSUPPORTED),
+             (_score_params(n_q_heads=4, window=8, aggregate=7), kv.KV_EINVAL)]
+    for p, want in cases:
+        assert L.kv_score_workspace_size(ctypes.byref(c), ctypes.byref(p), ctypes.byref(n)) == want
 
 
 def test_score_rejects_missing_state_and_small_workspace():

@@ -353,6 +353,62 @@ def test_score_with_supplied_lse():
     assert_rel(np64(got["mass"]), mass, rtol=2e-5, what="mass with supplied LSE")
 
 
+@pytest.mark.parametrize("hq,hkv,window,n_tokens,n_layers", [
+    (4, 4, 24, 700, 2),      # G = 1: equals the sum
+    (4, 2, 40, 1500, 1),     # G = 2
+    (6, 2, 33, 2000, 2),     # G = 3, padded to 4
+    (32, 8, 64, 5000, 2),    # G = 4: Qwen3-8B / Mistral-7B heads, 256 rows
+    (28, 4, 32, 3000, 1),    # G = 7, padded to 8 (Qwen2.5-7B heads)
+    (40, 8, 50, 2500, 1),    # G = 5, padded to 8: 400 rows, two row groups
+    (32, 2, 20, 1800, 1),    # G = 16: 320 rows
+    (32, 1, 16, 1300, 1),    # G = 32: 512 rows
+])
+def test_score_max_group_parity(hq, hkv, window, n_tokens, n_layers):
+    """ActKV's aggregation (Sec. 7.1, Algorithm 3): per KV head the maximum over its
+    query heads of exp(s - LSE), against the oracle; MemDecay divides by L*Hkv*W."""
+    w = synth.workload(1, n_tokens=n_tokens, window=window, n_q_heads=hq, n_kv_heads=hkv,
+                       n_layers=n_layers)
+    k, v, bt, q = _make_score_inputs(w, seed=31 + n_tokens, shuffle=True)
+    st0 = _memdecay_state(w, seed=n_tokens)
+    dev = {key: t.clone().to(DEV) for key, t in st0.items()}
+    got = _run_score(w, k, v, bt, q, policy="memdecay", item_tokens=w.item_tokens, state=dev,
+                     rho=w.rho, alpha=w.alpha, tau=w.tau, dt_steps=2, pinned_regions=1,
+                     aggregate="max_group")
+    kl = _paged_to_logical(k, bt, 16, w.n_tokens)
+    ref = O.score_step(np64(q), kl, policy="memdecay", region=st0["region"].numpy(),
+                       base_prio=np64(st0["base_prio"]), decay_rate=np64(st0["decay_rate"]),
+                       rho=f32(w.rho), alpha=f32(w.alpha), tau=f32(w.tau), dt_steps=2,
+                       ewma=np64(st0["ewma"]), clock=st0["clock"].numpy(), pinned_regions=1,
+                       item_tokens=w.item_tokens, aggregate="max_group")
+    assert_rel(np64(got["mass"]), ref["mass"], what="group-max score")
+    assert np.abs(np64(got["lse"]) - ref["lse"]).max() < 1e-5
+    ok = np.abs(ref["abar"] - f32(w.tau)) > 1e-5 * f32(w.tau)
+    assert_rel(np64(dev["ewma"].cpu())[ok], ref["ewma"][ok], what="ewma")
+    assert (dev["clock"].cpu().numpy()[ok] == ref["clock"][ok]).all()
+    assert_rel(np64(got["token_score"])[ok], ref["token_score"][ok], what="token score")
+    if hq == hkv:   # one head per group: the same numbers as the sum
+        s = _run_score(w, k, v, bt, q, policy="h2o", item_tokens=1,
+                       state=dict(accum=torch.zeros(w.n_tokens, device=DEV)))
+        assert torch.equal(s["mass"], got["mass"])
+
+
+@pytest.mark.parametrize("aggregate,shift", [("sum", 0.0), ("max_group", 0.0), ("max_group", 0.3)])
+def test_score_supplied_lse_both_modes(aggregate, shift):
+    """A supplied LSE is used as given (ActKV Sec. 7.1): also when it is not the keys' own."""
+    w = synth.workload(1, n_tokens=2600, n_layers=2, window=40, n_q_heads=12, n_kv_heads=4)
+    k, v, bt, q = _make_score_inputs(w, seed=17, shuffle=True)
+    kl = _paged_to_logical(k, bt, 16, w.n_tokens)
+    _, lse = O.attention_mass(np64(q), kl)
+    lse_in = (lse + shift).astype(np.float32)
+    fn = O.attention_mass if aggregate == "sum" else O.attention_score_max_group
+    mass, _ = fn(np64(q), kl, lse=lse_in.astype(np.float64))
+    got = _run_score(w, k, v, bt, q, policy="h2o", item_tokens=1,
+                     state=dict(accum=torch.zeros(w.n_tokens, device=DEV)),
+                     lse_in=torch.from_numpy(lse_in).to(DEV), aggregate=aggregate)
+    assert_rel(np64(got["mass"]), mass, rtol=2e-5, what=f"{aggregate} with supplied LSE")
+    assert np.abs(np64(got["lse"]) - lse_in).max() < 1e-5
+
+
 def test_pipeline_end_to_end_config2():
     """score -> select -> compact on the GPU against the oracle pipeline (config 2)."""
     w = synth.workload(2)
