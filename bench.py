@@ -151,6 +151,36 @@ def pmc_summary(fetch_dir, write_dir, out_json):
                               f"WRITE_SIZE x{calib['WRITE_SIZE']:.4f}")
 
 
+def clock_summary(pmc_dir):
+    """Effective core clock and MFMA busy share per kernel from a rocprofv3 --pmc run with
+    GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES.  rocprofv3 sums GRBM_GUI_ACTIVE over the
+    8 XCDs of the MI355X (a memory-only kernel reads 2.4 GHz with this factor); the MFMA
+    busy share divides by the cycles of all 1,024 SIMDs.  Returns a markdown table."""
+    import csv
+    import glob
+    hits = glob.glob(os.path.join(pmc_dir, "**", "*_counter_collection.csv"), recursive=True)
+    if not hits:
+        raise SystemExit(f"no *_counter_collection.csv under {pmc_dir}")
+    per = {}
+    for r in csv.DictReader(open(hits[0])):
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        d = per.setdefault(key, {"dur_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    rows = ["| Kernel | Dispatches | Average (us) | Effective clock (GHz) | MFMA busy |",
+            "|---|---|---|---|---|"]
+    for needle in ("lse_pass_kernel", "mass_pass_kernel", "compact_kernel", "select_hist_kernel",
+                   "epilogue_kernel", "lse_combine_kernel"):
+        ds = [d for (k, _), d in per.items() if needle in k and "GRBM_GUI_ACTIVE" in d]
+        if not ds:
+            continue
+        dur = sum(d["dur_ns"] for d in ds) / len(ds)
+        cyc = sum(d["GRBM_GUI_ACTIVE"] for d in ds) / len(ds) / 8.0
+        mfma = sum(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds) / len(ds)
+        rows.append(f"| {needle} | {len(ds)} | {dur / 1e3:.1f} | {cyc / dur:.2f} | "
+                    f"{mfma / (1024.0 * cyc):.1%} |")
+    return "\n".join(rows)
+
+
 def cpu_baseline(w, layers):
     """The CPU oracle, untuned, on a bounded sample of the workload: attention mass and
     epilogue for `layers` of the 36 layers at full N, selection at full N, compaction of
@@ -202,6 +232,9 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn the rocprofv3 FETCH_SIZE / WRITE_SIZE runs (bench + copy calibration "
                          "in each directory) into profiles/traffic.json and print a table")
+    ap.add_argument("--clock-summary", metavar="PMC_DIR",
+                    help="print effective clock and MFMA busy share per kernel from a "
+                         "rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES run and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) three "
                          "times, to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -209,6 +242,9 @@ def main():
     if args.pmc_summary:
         print(pmc_summary(args.pmc_summary[0], args.pmc_summary[1],
                           os.path.join(ROOT, "profiles", "traffic.json")))
+        return
+    if args.clock_summary:
+        print(clock_summary(args.clock_summary))
         return
     if args.copy_calibration:
         a = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")
