@@ -394,19 +394,64 @@ def rope_inv_freq(theta, head_dim):
     return np.power(float(theta), -2.0 * i / head_dim)
 
 
-def rope_rotate(k, delta, theta):
+def rope_rotate(k, delta, theta=None, inv_freq=None):
     """Rotate split-half RoPE pairs (i, i + D/2) of k[..., D] by angle delta * theta_i.
 
         x' = x cos(phi) - y sin(phi),   y' = x sin(phi) + y cos(phi)
-    ``delta`` broadcasts against k's leading dims.  float64 throughout.
+    ``delta`` broadcasts against k's leading dims.  The frequencies are base ** (-2i/D)
+    for a scalar ``theta``, or the given ``inv_freq`` table.  float64 throughout.
     """
     k = np.asarray(k, dtype=np.float64)
     d = k.shape[-1]
     half = d // 2
-    phi = np.asarray(delta, dtype=np.float64)[..., None] * rope_inv_freq(theta, d)
+    freq = rope_inv_freq(theta, d) if inv_freq is None else np.asarray(inv_freq, dtype=np.float64)
+    assert freq.shape == (half,)
+    phi = np.asarray(delta, dtype=np.float64)[..., None] * freq
     c, s = np.cos(phi), np.sin(phi)
     x, y = k[..., :half], k[..., half:]
     return np.concatenate([x * c - y * s, x * s + y * c], axis=-1)
+
+
+def scaled_inv_freq(kind, base, head_dim=128, factor=1.0, original_max_position=8192,
+                    low_freq_factor=1.0, high_freq_factor=4.0, beta_fast=32.0, beta_slow=1.0):
+    """RoPE frequencies under static scaling (PACE Sec. 3.5 names default, linear, YaRN
+    and Llama-3 style scaling; the definitions are the published methods):
+      default: theta_i = base ** (-2i/D);
+      linear:  theta_i / factor (position interpolation);
+      llama3:  wavelength w_i = 2 pi / theta_i.  Dims with w_i < L / high_freq_factor keep
+               theta_i, dims with w_i > L / low_freq_factor get theta_i / factor, the rest
+               blend (1 - t) theta_i / factor + t theta_i with
+               t = (L / w_i - low_freq_factor) / (high_freq_factor - low_freq_factor);
+      yarn:    "NTK-by-parts": r_i = L / w_i rotations over the original context L,
+               g = clip((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1),
+               theta'_i = (1 - g) theta_i / factor + g theta_i.
+    L = original_max_position.  Only the rotation is defined here: YaRN's attention
+    temperature scales q and k when they are cached, and re-rotating a cached key by a
+    position difference leaves that factor in place.
+    """
+    theta = rope_inv_freq(base, head_dim)
+    if kind == "default":
+        return theta
+    if kind == "linear":
+        return theta / factor
+    wavelen = 2.0 * math.pi / theta
+    L = float(original_max_position)
+    if kind == "llama3":
+        out = np.empty_like(theta)
+        for i in range(theta.size):
+            if wavelen[i] < L / high_freq_factor:
+                out[i] = theta[i]
+            elif wavelen[i] > L / low_freq_factor:
+                out[i] = theta[i] / factor
+            else:
+                t = (L / wavelen[i] - low_freq_factor) / (high_freq_factor - low_freq_factor)
+                out[i] = (1.0 - t) * theta[i] / factor + t * theta[i]
+        return out
+    if kind == "yarn":
+        r = L / wavelen
+        g = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
+        return (1.0 - g) * theta / factor + g * theta
+    raise ValueError(kind)
 
 
 def renumbered_positions(n_keep, renumber_base, old_pos_kept):
@@ -440,6 +485,62 @@ def compact_rerope(k, v, keep, old_pos, renumber_base, theta):
         rot = rope_rotate(kk[:, moved], delta[moved][None, :, None], theta)
         out_k[:, moved] = bf16_round(rot)
     return out_k, vv, new_pos
+
+
+REF_NONE = -(2 ** 31)   # position of an empty reference-store entry
+
+
+def compact_rerope_store(k, v, keep, old_pos, renumber_base, inv_freq, ref_k, ref_pos):
+    """compact_rerope with PACE's reference store (Sec. 3.2, non-compounding re-rotation).
+
+    ref_k: [L][N][Hkv][D] reference keys and ref_pos: [N] the position each is valid at
+    (REF_NONE = empty), indexed by source token like k.  For rank r with source j, old
+    position op and new position np:
+      * the entry is used when it is not empty and the stored key, re-rotated from
+        ref_pos[j] to op and rounded, equals the cached key bit for bit (the check
+        against the stored key); the new key is then the stored key rotated by
+        np - ref_pos[j] and rounded once, and the entry moves to slot r;
+      * otherwise, when the position changes, this is the key's first re-rotation: the
+        cached key and op are copied into the store at slot r and the new key is the
+        cached key rotated by np - op, rounded once;
+      * otherwise the key is copied and slot r of the store stays empty.
+    Every key therefore carries at most two roundings: the engine's own when it cached
+    the key, and one from the stored copy.  Returns (k', v', new_pos, ref_k', ref_pos',
+    used) where ref_k' is defined where ref_pos' is not REF_NONE and used[r] says
+    whether the store entry served rank r.
+    Reading: entries are created at the first position change (a key that never moves
+    has no rounding to protect against); PACE does not say more.
+    """
+    keep = np.asarray(keep, dtype=np.int64)
+    k = np.asarray(k, dtype=np.float64)
+    ref_k = np.asarray(ref_k, dtype=np.float64)
+    ref_pos = np.asarray(ref_pos, dtype=np.int64)
+    old_kept = np.asarray(old_pos, dtype=np.int64)[keep]
+    new_pos = renumbered_positions(len(keep), renumber_base, old_kept)
+    nl, _, hkv, d = k.shape
+    out_k = np.zeros((nl, len(keep), hkv, d))
+    out_ref = np.zeros((nl, len(keep), hkv, d))
+    out_ref_pos = np.full(len(keep), REF_NONE, dtype=np.int64)
+    used = np.zeros(len(keep), dtype=bool)
+    for r, j in enumerate(keep):
+        op, np_ = old_kept[r], new_pos[r]
+        valid = False
+        if ref_pos[j] != REF_NONE:
+            back = bf16_round(rope_rotate(ref_k[:, j], op - ref_pos[j], inv_freq=inv_freq))
+            valid = bool((back == k[:, j]).all())
+        if valid:
+            out_k[:, r] = bf16_round(rope_rotate(ref_k[:, j], np_ - ref_pos[j], inv_freq=inv_freq))
+            out_ref[:, r] = ref_k[:, j]
+            out_ref_pos[r] = ref_pos[j]
+            used[r] = True
+        elif np_ != op:
+            out_k[:, r] = bf16_round(rope_rotate(k[:, j], np_ - op, inv_freq=inv_freq))
+            out_ref[:, r] = k[:, j]
+            out_ref_pos[r] = op
+        else:
+            out_k[:, r] = k[:, j]
+    vv = np.asarray(v, dtype=np.float64)[:, keep].copy()
+    return out_k, vv, new_pos, out_ref, out_ref_pos, used
 
 
 def gather_meta(arr, keep):

@@ -517,15 +517,142 @@ def test_compact_rerope_definition():
     # two roundings at most through bf16 storage: round-trip to a far position and back
     k_far = O.bf16_round(O.rope_rotate(k[:, 5], 100_000, 1e6))
     back = O.bf16_round(O.rope_rotate(k_far, -100_000, 1e6))
-    # each bf16 rounding moves a pair by at most 2^-9 * sqrt(2) of its norm; rotation
-    # preserves that norm, so two roundings stay within 2^-8 * sqrt(2) of it
+    # bf16 keeps 8 significant bits: each RNE rounding moves a component by at most
+    # 2^-8 of its magnitude, hence a pair by at most 2^-8 of its norm; rotation preserves
+    # the norm, so two roundings stay within 2^-8 * (2 + 2^-8) of it
     x, y = k[:, 5, :, :64], k[:, 5, :, 64:]
     norm = np.sqrt(x ** 2 + y ** 2)
     err = np.sqrt((back[..., :64] - x) ** 2 + (back[..., 64:] - y) ** 2)
-    assert (err <= 2 ** -8 * math.sqrt(2) * norm + 1e-30).all()
+    assert (err <= 2 ** -8 * (2 + 2 ** -8) * norm + 1e-30).all()
     # no renumbering keeps positions and every key
     k3, _, p3 = O.compact_rerope(k, v, keep, old_pos, -1, 1e6)
     assert (p3 == old_pos[keep]).all() and (k3 == k[:, keep]).all()
+
+
+def test_scaled_inv_freq_special_cases():
+    """PACE Sec. 3.5's static scalings against their defining cases: linear divides every
+    frequency; with factor 1 Llama-3 and YaRN reduce to plain RoPE; Llama-3 keeps the
+    high-frequency dims, divides the low-frequency ones and blends in between; YaRN keeps
+    dims turning more than beta_fast times over the original context and divides those
+    turning less than beta_slow times."""
+    base = 5e5
+    d = O.scaled_inv_freq("default", base)
+    np.testing.assert_array_equal(d, np.power(base, -np.arange(64) / 64.0))
+    np.testing.assert_allclose(O.scaled_inv_freq("linear", base, factor=4.0), d / 4.0, rtol=1e-15)
+    np.testing.assert_allclose(O.scaled_inv_freq("llama3", base, factor=1.0), d, rtol=1e-15)
+    np.testing.assert_allclose(O.scaled_inv_freq("yarn", base, factor=1.0), d, rtol=1e-15)
+    wl = 2 * math.pi / d
+    ll = O.scaled_inv_freq("llama3", base, factor=8.0, original_max_position=8192,
+                           low_freq_factor=1.0, high_freq_factor=4.0)
+    hi, lo = wl < 8192 / 4.0, wl > 8192 / 1.0
+    assert hi.any() and lo.any() and (~hi & ~lo).any()
+    np.testing.assert_array_equal(ll[hi], d[hi])
+    np.testing.assert_allclose(ll[lo], d[lo] / 8.0, rtol=1e-15)
+    mid = ~hi & ~lo
+    assert ((ll[mid] > d[mid] / 8.0) & (ll[mid] < d[mid])).all()
+    assert (np.diff(ll) < 0).all()
+    ya = O.scaled_inv_freq("yarn", base, factor=16.0, original_max_position=4096)
+    r = 4096 / wl
+    fast, slow = r > 32.0, r < 1.0
+    assert fast.any() and slow.any()
+    np.testing.assert_allclose(ya[fast], d[fast], rtol=1e-15)
+    np.testing.assert_allclose(ya[slow], d[slow] / 16.0, rtol=1e-15)
+    m = ~fast & ~slow
+    assert ((ya[m] > d[m] / 16.0) & (ya[m] < d[m])).all()
+
+
+@pytest.mark.parametrize("kind", ["linear", "llama3", "yarn"])
+def test_proposition1_holds_for_scaled_tables(kind):
+    """Re-rotating a key cached at p by q - p gives the key cached at q for any fixed
+    frequency table (the model-side rotation written the rotate_half way)."""
+    inv = O.scaled_inv_freq(kind, 5e5, factor=8.0, original_max_position=8192)
+    rng = np.random.default_rng(18)
+    k0 = rng.standard_normal((10, 128))
+    p, qn = rng.integers(0, 500_000, 10), rng.integers(0, 8192, 10)
+
+    def hf(x, pos):
+        f = torch.as_tensor(pos, dtype=torch.float64)[:, None] * torch.from_numpy(inv)
+        emb = torch.cat([f, f], dim=-1)
+        xt = torch.from_numpy(x)
+        rot = torch.cat([-xt[:, 64:], xt[:, :64]], dim=-1)
+        return (xt * emb.cos() + rot * emb.sin()).numpy()
+
+    np.testing.assert_allclose(O.rope_rotate(hf(k0, p), qn - p, inv_freq=inv), hf(k0, qn), atol=1e-9)
+
+
+def _pair_error(k, true):
+    """Largest error of a rotation pair relative to the pair's norm."""
+    e = np.sqrt((k[..., :64] - true[..., :64]) ** 2 + (k[..., 64:] - true[..., 64:]) ** 2)
+    n = np.sqrt(true[..., :64] ** 2 + true[..., 64:] ** 2)
+    return float((e / n).max())
+
+
+def test_reference_store_error_stays_two_roundings():
+    """PACE Sec. 3.2: deriving every position from the stored copy keeps the error at
+    about two bf16 roundings however many renumbers a key survives, while re-rotating the
+    stored key adds one rounding per position change."""
+    rng = np.random.default_rng(19)
+    nl, n, hk = 1, 48, 2
+    inv = O.scaled_inv_freq("default", 1e6)
+    x = rng.standard_normal((nl, n, hk, 128))                    # keys before rotation
+    pos0 = rng.integers(0, 8192, n)
+    k_store = O.bf16_round(O.rope_rotate(x, pos0[None, :, None], inv_freq=inv))
+    k_plain = k_store.copy()
+    v = np.zeros_like(k_store)
+    ref_k, ref_pos = np.zeros_like(k_store), np.full(n, O.REF_NONE)
+    keep = np.arange(n)
+    pos_s, pos_p, prev = pos0, pos0, -1
+    for step in range(60):
+        base = int(rng.integers(0, 4096))
+        base = base + 1 if base == prev else base
+        prev = base
+        k_store, _, pos_s, ref_k, ref_pos, used = O.compact_rerope_store(
+            k_store, v, keep, pos_s, base, inv, ref_k, ref_pos)
+        k_plain, _, pos_p = O.compact_rerope(k_plain, v, keep, pos_p, base, 1e6)
+        assert used.all() == (step > 0)
+        assert (ref_pos == pos0).all()                # the store keeps the cached copy
+    assert (pos_s == pos_p).all()
+    true = O.rope_rotate(x, pos_s[None, :, None], inv_freq=inv)
+    bound = 2.0 ** -8 * (2 + 2.0 ** -8)                      # two roundings (see above)
+    assert _pair_error(k_store, true) <= bound
+    assert _pair_error(k_plain, true) > bound                # compounding without the store
+
+
+def test_reference_store_first_use_and_foreign_entry():
+    """With an empty store the keys equal plain compaction and moved keys are stored at
+    their old positions; an entry that fails the check against the cached key (its slot
+    was reused) is ignored and replaced."""
+    rng = np.random.default_rng(20)
+    nl, n, hk = 2, 24, 2
+    k = O.bf16_round(rng.standard_normal((nl, n, hk, 128)))
+    v = O.bf16_round(rng.standard_normal((nl, n, hk, 128)))
+    old = np.arange(n) + 50
+    old[:4] = np.arange(4)                                   # ranks 0..3 keep their place
+    keep = np.array([0, 1, 2, 3, 9, 10, 17, 23])
+    inv = O.scaled_inv_freq("default", 1e6)
+    empty_k, empty_p = np.zeros_like(k), np.full(n, O.REF_NONE)
+    k1, v1, p1, rk, rp, used = O.compact_rerope_store(k, v, keep, old, 0, inv, empty_k, empty_p)
+    k0, v0, p0 = O.compact_rerope(k, v, keep, old, 0, 1e6)
+    assert (k1 == k0).all() and (v1 == v0).all() and (p1 == p0).all() and not used.any()
+    assert (rp[:4] == O.REF_NONE).all() and (rp[4:] == old[keep[4:]]).all()
+    assert (rk[:, 4:] == k[:, keep[4:]]).all()
+    # slot 9 holds a stale entry of another key: the check fails, the slot is re-seeded
+    bad_k, bad_p = empty_k.copy(), empty_p.copy()
+    bad_k[:, 9] = O.bf16_round(rng.standard_normal((nl, hk, 128)))
+    bad_p[9] = 40
+    k2, _, _, rk2, rp2, used2 = O.compact_rerope_store(k, v, keep, old, 0, inv, bad_k, bad_p)
+    assert not used2.any() and (k2 == k0).all()
+    assert rp2[4] == old[9] and (rk2[:, 4] == k[:, 9]).all()
+    # a valid entry is used even when the cached key is not where it was stored
+    good_k, good_p = empty_k.copy(), empty_p.copy()
+    good_k[:, 17] = O.bf16_round(rng.standard_normal((nl, hk, 128)))
+    good_p[17] = 5
+    kc = k.copy()
+    kc[:, 17] = O.bf16_round(O.rope_rotate(good_k[:, 17], old[17] - 5, inv_freq=inv))
+    k3, _, _, rk3, rp3, used3 = O.compact_rerope_store(kc, v, keep, old, 0, inv, good_k, good_p)
+    assert used3[6] and used3.sum() == 1 and rp3[6] == 5
+    want = O.bf16_round(O.rope_rotate(good_k[:, 17], 6 - 5, inv_freq=inv))
+    assert (k3[:, 6] == want).all()
 
 
 def test_renumbered_rotary_distance_bounded():
