@@ -32,6 +32,12 @@ KV_POLICY_MEMDECAY = 0
 KV_POLICY_H2O = 1
 KV_AGG_SUM = 0
 KV_AGG_MAX_GROUP = 1
+KV_ROPE_DEFAULT = 0
+KV_ROPE_LINEAR = 1
+KV_ROPE_LLAMA3 = 2
+KV_ROPE_YARN = 3
+KV_ROPE_TABLE = 4
+KV_REF_NONE = -(2 ** 31)
 KV_MAX_META = 8
 KV_ABI_VERSION = 2  # layout of the structs below
 
@@ -74,6 +80,19 @@ class KvScoreParams(ctypes.Structure):
                 ("stage_events", ctypes.c_void_p), ("aggregate", ctypes.c_int32)]
 
 
+class KvRope(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("original_max_position", ctypes.c_int32),
+                ("base", ctypes.c_double), ("factor", ctypes.c_double),
+                ("low_freq_factor", ctypes.c_double), ("high_freq_factor", ctypes.c_double),
+                ("beta_fast", ctypes.c_double), ("beta_slow", ctypes.c_double),
+                ("inv_freq", ctypes.POINTER(ctypes.c_double))]
+
+
+class KvRefStore(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("n_slots", ctypes.c_int64),
+                ("layer_stride", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -100,6 +119,13 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_double, i32, P(KvMetaDesc), i32, vp]),
             "kv_compact_segment_inplace": (i32, [P(KvCacheDesc), i64, i64, vp, i32, ctypes.c_double,
                                                  i32, P(KvMetaDesc), i32, vp]),
+            "kv_rope_inv_freq": (i32, [P(KvRope), P(ctypes.c_double)]),
+            "kv_ref_invalidate": (i32, [P(KvRefStore), i64, i64, vp]),
+            "kv_compact_rerope_ex": (i32, [P(KvCacheDesc), P(KvCacheDesc), vp, vp, i64, vp, vp, i32,
+                                           P(KvRope), i32, P(KvMetaDesc), i32, P(KvRefStore),
+                                           P(KvRefStore), vp]),
+            "kv_compact_segment_inplace_ex": (i32, [P(KvCacheDesc), i64, i64, vp, i32, P(KvRope), i32,
+                                                    P(KvMetaDesc), i32, P(KvRefStore), vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -260,23 +286,86 @@ def kv_select_segment(n_tokens, prefix_len, evict_tokens, block, keep_tokens=Non
     return nk.value, el.value
 
 
+def kv_rope(kind="default", base=1e6, factor=1.0, original_max_position=8192, low_freq_factor=1.0,
+            high_freq_factor=4.0, beta_fast=32.0, beta_slow=1.0, table=None) -> KvRope:
+    """A kv_rope descriptor (see include/kvscore.h); kind is a name or a KV_ROPE_* code."""
+    code = {"default": KV_ROPE_DEFAULT, "linear": KV_ROPE_LINEAR, "llama3": KV_ROPE_LLAMA3,
+            "yarn": KV_ROPE_YARN, "table": KV_ROPE_TABLE}.get(kind, kind)
+    r = KvRope(int(code), int(original_max_position), float(base), float(factor), float(low_freq_factor),
+               float(high_freq_factor), float(beta_fast), float(beta_slow), None)
+    if table is not None:
+        arr = (ctypes.c_double * 64)(*[float(x) for x in table])
+        r._table = arr                      # keep the host array alive with the struct
+        r.inv_freq = ctypes.cast(arr, ctypes.POINTER(ctypes.c_double))
+    return r
+
+
+def kv_rope_inv_freq(rope: KvRope) -> list:
+    out = (ctypes.c_double * 64)()
+    _check(lib().kv_rope_inv_freq(ctypes.byref(rope), out), "kv_rope_inv_freq")
+    return list(out)
+
+
+class RefStore:
+    """Reference store of a row (see kv_ref_store): keys [L][slots][Hkv][128] bf16 and
+    positions [slots] int32 (KV_REF_NONE = empty), both device tensors."""
+
+    def __init__(self, k, pos):
+        assert k.dim() == 4 and k.shape[3] == 128 and k.dtype == torch.bfloat16 and k.is_contiguous()
+        assert pos.dtype == torch.int32 and pos.numel() == k.shape[1]
+        self.k, self.pos = k, pos
+
+    @classmethod
+    def empty(cls, n_layers, n_slots, n_kv_heads, device):
+        return cls(torch.zeros((n_layers, n_slots, n_kv_heads, 128), dtype=torch.bfloat16, device=device),
+                   torch.full((n_slots,), KV_REF_NONE, dtype=torch.int32, device=device))
+
+    def desc(self) -> KvRefStore:
+        return KvRefStore(_ptr(self.k), _ptr(self.pos), int(self.k.shape[1]),
+                          int(self.k.shape[1] * self.k.shape[2] * 128))
+
+
+def kv_ref_invalidate(ref: RefStore, first, count):
+    _check(lib().kv_ref_invalidate(ctypes.byref(ref.desc()), int(first), int(count),
+                                   _stream(ref.pos.device)), "kv_ref_invalidate")
+
+
 def kv_compact_rerope(src: PagedCache, dst: PagedCache, keep_tokens, n_keep, max_keep, old_pos,
-                      new_pos=None, renumber_base=-1, rope_theta=1e6, limit=0, meta=None):
-    """Gather + exact re-rotation (see kv_compact_rerope); meta is a list of (src, dst)
-    tensor pairs gathered with the keep list."""
+                      new_pos=None, renumber_base=-1, rope_theta=1e6, limit=0, meta=None, rope=None,
+                      ref_src=None, ref_dst=None):
+    """Gather + exact re-rotation (see kv_compact_rerope / kv_compact_rerope_ex); meta is a
+    list of (src, dst) tensor pairs gathered with the keep list.  rope (a KvRope) replaces
+    rope_theta; ref_src / ref_dst are RefStore objects."""
     arr, n_meta = _meta_array(meta)
-    _check(lib().kv_compact_rerope(ctypes.byref(src.desc()), ctypes.byref(dst.desc()),
-                                   _ptr(keep_tokens), _ptr(n_keep), int(max_keep), _ptr(old_pos),
-                                   _ptr(new_pos), int(renumber_base), float(rope_theta), int(limit),
-                                   arr, n_meta, _stream(src.k.device)), "kv_compact_rerope")
+    if rope is None and ref_src is None and ref_dst is None:
+        _check(lib().kv_compact_rerope(ctypes.byref(src.desc()), ctypes.byref(dst.desc()),
+                                       _ptr(keep_tokens), _ptr(n_keep), int(max_keep), _ptr(old_pos),
+                                       _ptr(new_pos), int(renumber_base), float(rope_theta), int(limit),
+                                       arr, n_meta, _stream(src.k.device)), "kv_compact_rerope")
+        return
+    rope = rope if rope is not None else kv_rope("default", base=rope_theta)
+    rs = ctypes.byref(ref_src.desc()) if ref_src is not None else None
+    rd = ctypes.byref(ref_dst.desc()) if ref_dst is not None else None
+    _check(lib().kv_compact_rerope_ex(ctypes.byref(src.desc()), ctypes.byref(dst.desc()),
+                                      _ptr(keep_tokens), _ptr(n_keep), int(max_keep), _ptr(old_pos),
+                                      _ptr(new_pos), int(renumber_base), ctypes.byref(rope), int(limit),
+                                      arr, n_meta, rs, rd, _stream(src.k.device)), "kv_compact_rerope_ex")
 
 
 def kv_compact_segment_inplace(cache: PagedCache, prefix_len, evict_len, pos, renumber_base=-1,
-                               rope_theta=1e6, limit=0, meta=None):
-    """In-place segment eviction (see kv_compact_segment_inplace); meta is a list of
-    tensors moved in place."""
+                               rope_theta=1e6, limit=0, meta=None, rope=None, ref=None):
+    """In-place segment eviction (see kv_compact_segment_inplace / _ex); meta is a list of
+    tensors moved in place; ref is a RefStore moved in place."""
     arr, n_meta = _meta_array([(m, m) for m in (meta or [])])
-    _check(lib().kv_compact_segment_inplace(ctypes.byref(cache.desc()), int(prefix_len), int(evict_len),
-                                            _ptr(pos), int(renumber_base), float(rope_theta), int(limit),
-                                            arr, n_meta, _stream(cache.k.device)),
-           "kv_compact_segment_inplace")
+    if rope is None and ref is None:
+        _check(lib().kv_compact_segment_inplace(ctypes.byref(cache.desc()), int(prefix_len), int(evict_len),
+                                                _ptr(pos), int(renumber_base), float(rope_theta), int(limit),
+                                                arr, n_meta, _stream(cache.k.device)),
+               "kv_compact_segment_inplace")
+        return
+    rope = rope if rope is not None else kv_rope("default", base=rope_theta)
+    rf = ctypes.byref(ref.desc()) if ref is not None else None
+    _check(lib().kv_compact_segment_inplace_ex(ctypes.byref(cache.desc()), int(prefix_len), int(evict_len),
+                                               _ptr(pos), int(renumber_base), ctypes.byref(rope), int(limit),
+                                               arr, n_meta, rf, _stream(cache.k.device)),
+           "kv_compact_segment_inplace_ex")

@@ -344,8 +344,64 @@ int32_t kv_select_segment(int64_t n_tokens, int64_t prefix_len, int64_t evict_to
   return he == hipSuccess ? KV_OK : hip_fail(he);
 }
 
+int32_t kv_rope_inv_freq(const kv_rope* rope, double* inv_freq) {
+  if (!rope || !inv_freq) return KV_EINVAL;
+  const int half = kHeadDim / 2;
+  if (rope->kind == KV_ROPE_TABLE) {
+    if (!rope->inv_freq) return KV_EINVAL;
+    for (int i = 0; i < half; ++i) {
+      if (!isfinite(rope->inv_freq[i])) return KV_EINVAL;
+      inv_freq[i] = rope->inv_freq[i];
+    }
+    return KV_OK;
+  }
+  if (!(rope->base > 1.0) || !isfinite(rope->base)) return KV_EINVAL;
+  const bool scaled = rope->kind != KV_ROPE_DEFAULT;
+  if (scaled && !(rope->factor > 0.0 && isfinite(rope->factor))) return KV_EINVAL;
+  const double L = (double)rope->original_max_position;
+  if ((rope->kind == KV_ROPE_LLAMA3 || rope->kind == KV_ROPE_YARN) && !(L > 0.0)) return KV_EINVAL;
+  if (rope->kind == KV_ROPE_LLAMA3 &&
+      !(rope->low_freq_factor > 0.0 && rope->high_freq_factor > rope->low_freq_factor))
+    return KV_EINVAL;
+  if (rope->kind == KV_ROPE_YARN && !(rope->beta_fast > rope->beta_slow)) return KV_EINVAL;
+  if (rope->kind < KV_ROPE_DEFAULT || rope->kind > KV_ROPE_YARN) return KV_EINVAL;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < half; ++i) {
+    const double f = pow(rope->base, -(2.0 * i) / kHeadDim);
+    double out = f;
+    if (rope->kind == KV_ROPE_LINEAR) {
+      out = f / rope->factor;
+    } else if (rope->kind == KV_ROPE_LLAMA3) {
+      const double w = two_pi / f;
+      if (w < L / rope->high_freq_factor) {
+        out = f;
+      } else if (w > L / rope->low_freq_factor) {
+        out = f / rope->factor;
+      } else {
+        const double t = (L / w - rope->low_freq_factor) / (rope->high_freq_factor - rope->low_freq_factor);
+        out = (1.0 - t) * f / rope->factor + t * f;
+      }
+    } else if (rope->kind == KV_ROPE_YARN) {
+      const double rot = L / (two_pi / f);
+      double g = (rot - rope->beta_slow) / (rope->beta_fast - rope->beta_slow);
+      g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+      out = (1.0 - g) * f / rope->factor + g * f;
+    }
+    inv_freq[i] = out;
+  }
+  return KV_OK;
+}
+
+static int32_t check_ref(const kv_ref_store* r, const kv_cache_desc* c, int64_t min_slots) {
+  if (!r->k || !r->pos || r->n_slots < min_slots || r->n_slots <= 0) return KV_EINVAL;
+  const int64_t slot = (int64_t)c->n_kv_heads * kHeadDim;
+  if (c->n_layers > 1 && r->layer_stride < r->n_slots * slot) return KV_EINVAL;
+  if (((uintptr_t)r->k & 15) || (r->layer_stride & 7)) return KV_EINVAL;
+  return KV_OK;
+}
+
 static void fill_compact_common(CompactArgs* a, const kv_cache_desc* src, const kv_cache_desc* dst,
-                                int32_t renumber_base, double rope_theta) {
+                                int32_t renumber_base, const double* inv_freq) {
   a->src_k = (const uint16_t*)src->k;
   a->src_v = (const uint16_t*)src->v;
   a->src_layer_stride = src->layer_stride;
@@ -361,14 +417,42 @@ static void fill_compact_common(CompactArgs* a, const kv_cache_desc* src, const 
   a->src_page_shift = log2_exact(src->page_size);
   a->dst_page_shift = log2_exact(dst->page_size);
   a->renumber_base = renumber_base;
-  a->log_theta = log(rope_theta);
+  for (int i = 0; i < kHeadDim / 2; ++i) a->inv_freq[i] = inv_freq[i];
 }
 
-int32_t kv_compact_rerope(const kv_cache_desc* src, const kv_cache_desc* dst,
-                          const int32_t* keep_tokens, const int64_t* n_keep, int64_t max_keep,
-                          const int32_t* old_pos, int32_t* new_pos, int32_t renumber_base,
-                          double rope_theta, int32_t limit, const kv_meta_desc* meta,
-                          int32_t n_meta, hipStream_t stream) {
+static void fill_ref(CompactArgs* a, const kv_ref_store* src, const kv_ref_store* dst) {
+  if (!src) return;
+  a->ref_src_k = (const uint16_t*)src->k;
+  a->ref_src_pos = src->pos;
+  a->ref_src_layer_stride = src->layer_stride;
+  a->ref_dst_k = (uint16_t*)dst->k;
+  a->ref_dst_pos = dst->pos;
+  a->ref_dst_layer_stride = dst->layer_stride;
+}
+
+static int32_t rope_table(const kv_rope* rope, double* inv_freq) {
+  kv_rope def;
+  memset(&def, 0, sizeof(def));
+  def.kind = KV_ROPE_DEFAULT;
+  def.base = 1e6;
+  return kv_rope_inv_freq(rope ? rope : &def, inv_freq);
+}
+
+int32_t kv_ref_invalidate(const kv_ref_store* ref, int64_t first, int64_t count, hipStream_t stream) {
+  if (!ref || !ref->pos || first < 0 || count < 0 || first + count > ref->n_slots) return KV_EINVAL;
+  if (count == 0) return KV_OK;
+  int32_t rc = check_device();
+  if (rc) return rc;
+  const hipError_t e = launch_ref_invalidate(ref->pos + first, count, stream);
+  return e == hipSuccess ? KV_OK : hip_fail(e);
+}
+
+int32_t kv_compact_rerope_ex(const kv_cache_desc* src, const kv_cache_desc* dst,
+                             const int32_t* keep_tokens, const int64_t* n_keep, int64_t max_keep,
+                             const int32_t* old_pos, int32_t* new_pos, int32_t renumber_base,
+                             const kv_rope* rope, int32_t limit, const kv_meta_desc* meta,
+                             int32_t n_meta, const kv_ref_store* ref_src, const kv_ref_store* ref_dst,
+                             hipStream_t stream) {
   int32_t rc = check_cache(src);
   if (rc) return rc;
   if ((rc = check_cache(dst))) return rc;
@@ -376,7 +460,13 @@ int32_t kv_compact_rerope(const kv_cache_desc* src, const kv_cache_desc* dst,
   if (dst->n_layers != src->n_layers || dst->n_kv_heads != src->n_kv_heads) return KV_EINVAL;
   if (max_keep > dst->n_tokens || max_keep > src->n_tokens) return KV_EINVAL;
   if (src->k == dst->k || src->v == dst->v) return KV_EINVAL;
-  if (!(rope_theta > 1.0)) return KV_EINVAL;
+  double inv_freq[kHeadDim / 2];
+  if ((rc = rope_table(rope, inv_freq))) return rc;
+  if ((ref_src == nullptr) != (ref_dst == nullptr)) return KV_EINVAL;
+  if (ref_src) {
+    if ((rc = check_ref(ref_src, src, src->n_tokens)) || (rc = check_ref(ref_dst, src, max_keep))) return rc;
+    if (ref_src->k == ref_dst->k || ref_src->pos == ref_dst->pos) return KV_EINVAL;
+  }
   if (renumber_base >= 0 && limit > 0 && (int64_t)renumber_base + max_keep > limit) return KV_ELIMIT;
   MetaSet ms;
   if ((rc = check_meta(meta, n_meta, &ms))) return rc;
@@ -384,7 +474,8 @@ int32_t kv_compact_rerope(const kv_cache_desc* src, const kv_cache_desc* dst,
   if ((rc = check_device())) return rc;
   CompactArgs a;
   memset(&a, 0, sizeof(a));
-  fill_compact_common(&a, src, dst, renumber_base, rope_theta);
+  fill_compact_common(&a, src, dst, renumber_base, inv_freq);
+  fill_ref(&a, ref_src, ref_dst);
   a.keep = keep_tokens;
   a.rank0 = 0;
   a.rank1 = max_keep;
@@ -400,15 +491,30 @@ int32_t kv_compact_rerope(const kv_cache_desc* src, const kv_cache_desc* dst,
   return KV_OK;
 }
 
-int32_t kv_compact_segment_inplace(const kv_cache_desc* cache, int64_t prefix_len, int64_t evict_len,
-                                   int32_t* pos, int32_t renumber_base, double rope_theta,
-                                   int32_t limit, const kv_meta_desc* meta, int32_t n_meta,
-                                   hipStream_t stream) {
+int32_t kv_compact_rerope(const kv_cache_desc* src, const kv_cache_desc* dst,
+                          const int32_t* keep_tokens, const int64_t* n_keep, int64_t max_keep,
+                          const int32_t* old_pos, int32_t* new_pos, int32_t renumber_base,
+                          double rope_theta, int32_t limit, const kv_meta_desc* meta,
+                          int32_t n_meta, hipStream_t stream) {
+  kv_rope rope;
+  memset(&rope, 0, sizeof(rope));
+  rope.kind = KV_ROPE_DEFAULT;
+  rope.base = rope_theta;
+  return kv_compact_rerope_ex(src, dst, keep_tokens, n_keep, max_keep, old_pos, new_pos, renumber_base,
+                              &rope, limit, meta, n_meta, nullptr, nullptr, stream);
+}
+
+int32_t kv_compact_segment_inplace_ex(const kv_cache_desc* cache, int64_t prefix_len, int64_t evict_len,
+                                      int32_t* pos, int32_t renumber_base, const kv_rope* rope,
+                                      int32_t limit, const kv_meta_desc* meta, int32_t n_meta,
+                                      const kv_ref_store* ref, hipStream_t stream) {
   int32_t rc = check_cache(cache);
   if (rc) return rc;
   const int64_t N = cache->n_tokens;
   if (!pos || prefix_len < 0 || evict_len < 0 || prefix_len + evict_len > N) return KV_EINVAL;
-  if (!(rope_theta > 1.0)) return KV_EINVAL;
+  double inv_freq[kHeadDim / 2];
+  if ((rc = rope_table(rope, inv_freq))) return rc;
+  if (ref && (rc = check_ref(ref, cache, N))) return rc;
   const int64_t n_keep = N - evict_len;
   if (renumber_base >= 0 && limit > 0 && (int64_t)renumber_base + n_keep > limit) return KV_ELIMIT;
   MetaSet ms;
@@ -418,7 +524,8 @@ int32_t kv_compact_segment_inplace(const kv_cache_desc* cache, int64_t prefix_le
   if ((rc = check_device())) return rc;
   CompactArgs a;
   memset(&a, 0, sizeof(a));
-  fill_compact_common(&a, cache, cache, renumber_base, rope_theta);
+  fill_compact_common(&a, cache, cache, renumber_base, inv_freq);
+  fill_ref(&a, ref, ref);
   a.keep = nullptr;
   a.split = prefix_len;
   a.shift = evict_len;
@@ -442,6 +549,18 @@ int32_t kv_compact_segment_inplace(const kv_cache_desc* cache, int64_t prefix_le
     if ((e = launch_gather_meta(a, stream)) != hipSuccess) return hip_fail(e);
   }
   return KV_OK;
+}
+
+int32_t kv_compact_segment_inplace(const kv_cache_desc* cache, int64_t prefix_len, int64_t evict_len,
+                                   int32_t* pos, int32_t renumber_base, double rope_theta,
+                                   int32_t limit, const kv_meta_desc* meta, int32_t n_meta,
+                                   hipStream_t stream) {
+  kv_rope rope;
+  memset(&rope, 0, sizeof(rope));
+  rope.kind = KV_ROPE_DEFAULT;
+  rope.base = rope_theta;
+  return kv_compact_segment_inplace_ex(cache, prefix_len, evict_len, pos, renumber_base, &rope, limit,
+                                       meta, n_meta, nullptr, stream);
 }
 
 }  // extern "C"

@@ -11,9 +11,16 @@
 // c + 64 of one head, i.e. dims 8c..8c+7 and 64+8c..64+8c+7) and writes them to the
 // destination slot of its rank.  V is copied bit for bit.  K is copied bit for bit when
 // the position does not change; otherwise each split-half pair (x_i, x_{i+64}) is
-// rotated by delta * theta_i, theta_i = base^(-2i/128), with the 64 cos/sin values of
-// the token computed once in float64 into LDS, the rotation done in float64 from the
-// exact bf16 inputs, and one round-to-nearest-even to bf16.
+// rotated by delta * theta_i, with theta_i from the caller's frequency table (plain
+// base^(-2i/128) or a static scaling, PACE Sec. 3.5), the 64 cos/sin values of the
+// token computed once in float64 into LDS, the rotation done in float64 from the exact
+// bf16 inputs, and one round-to-nearest-even to bf16.
+//
+// With a reference store (PACE Sec. 3.2, non-compounding re-rotation) the workgroup
+// first checks the source slot's entry: the stored key re-rotated to the token's current
+// position and rounded must equal the cached key.  A valid entry is the rotation source
+// (and moves to the destination slot); otherwise a key whose position changes is stored
+// with its current position before it is rotated.
 #include "kv_internal.h"
 
 namespace kvs {
@@ -74,8 +81,37 @@ __device__ __forceinline__ void rotate_chunk(uint4& lo, uint4& hi, const double2
   hi = make_uint4(yl[0], yl[1], yl[2], yl[3]);
 }
 
+// Value equality of two bf16 patterns: +0 equals -0 and NaN equals nothing.
+__device__ __forceinline__ bool bf16_same(uint32_t x, uint32_t y) {
+  const uint32_t mx = x & 0x7FFFu, my = y & 0x7FFFu;
+  if (mx > 0x7F80u || my > 0x7F80u) return false;
+  return x == y || (mx == 0 && my == 0);
+}
+
+__device__ __forceinline__ bool chunk_same(const uint4& p, const uint4& q) {
+  const uint32_t pv[4] = {p.x, p.y, p.z, p.w};
+  const uint32_t qv[4] = {q.x, q.y, q.z, q.w};
+  bool same = true;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    same = same && bf16_same(pv[w] & 0xFFFFu, qv[w] & 0xFFFFu) && bf16_same(pv[w] >> 16, qv[w] >> 16);
+  return same;
+}
+
+// cos/sin of delta * theta_i for the 64 pairs, in float64.
+__device__ __forceinline__ void fill_rotation(double2* cs, const CompactArgs& a, int64_t delta, int tid) {
+  if (tid < kHeadDim / 2) {
+    double s, c;
+    sincos((double)delta * a.inv_freq[tid], &s, &c);
+    cs[tid] = make_double2(c, s);
+  }
+}
+
+template <bool kStore>
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a) {
   __shared__ double2 cs[64];
+  __shared__ double2 cs_chk[kStore ? 64 : 1];
+  __shared__ int s_bad;
   const int tid = threadIdx.x;
   const int64_t r = a.rank0 + blockIdx.x;
   if (r >= a.rank1) return;
@@ -83,41 +119,78 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
   const int64_t j = source_token(a, r);
   const int32_t op = a.old_pos[j];
   const int32_t np = a.renumber_base >= 0 ? a.renumber_base + (int32_t)r : op;
-  const int64_t delta = (int64_t)np - (int64_t)op;
   const bool in_place = a.keep == nullptr && j == r && a.src_k == a.dst_k;
-  if (in_place && delta == 0) return;  // already where it belongs
-
-  if (delta != 0) {
-    if (tid < 64) {
-      const double inv = exp(-(2.0 * tid / kHeadDim) * a.log_theta);
-      double s, c;
-      sincos((double)delta * inv, &s, &c);
-      cs[tid] = make_double2(c, s);
-    }
-    __syncthreads();
-  }
+  if (in_place && np == op) return;  // already where it belongs, store entry included
 
   const int slot_stride = a.n_kv_heads * kHeadDim;
   const int64_t src_off = token_offset(j, a.src_page_shift, a.src_page_stride, a.src_bt, slot_stride);
   const int64_t dst_off = token_offset(r, a.dst_page_shift, a.dst_page_stride, a.dst_bt, slot_stride);
   const int per_layer = a.n_kv_heads * 8;
   const int items = a.n_layers * per_layer;
+
+  int32_t rp = KV_REF_NONE;
+  bool use_ref = false;
+  if (kStore) {
+    rp = a.ref_src_pos[j];
+    if (rp != KV_REF_NONE) {
+      // check the entry against the cached key at its current position
+      fill_rotation(cs_chk, a, (int64_t)op - rp, tid);
+      if (tid == 0) s_bad = 0;
+      __syncthreads();
+      bool bad = false;
+      for (int e = tid; e < items; e += kCompactThreads) {
+        const int layer = e / per_layer;
+        const int rem = e - layer * per_layer;
+        const int64_t col = (rem >> 3) * kHeadDim + (rem & 7) * 8;
+        const int64_t so = (int64_t)layer * a.src_layer_stride + src_off + col;
+        const int64_t ro = (int64_t)layer * a.ref_src_layer_stride + j * slot_stride + col;
+        const uint4 klo = *(const uint4*)(a.src_k + so);
+        const uint4 khi = *(const uint4*)(a.src_k + so + 64);
+        uint4 rlo = *(const uint4*)(a.ref_src_k + ro);
+        uint4 rhi = *(const uint4*)(a.ref_src_k + ro + 64);
+        rotate_chunk(rlo, rhi, &cs_chk[(rem & 7) * 8]);
+        bad = bad || !chunk_same(rlo, klo) || !chunk_same(rhi, khi);
+      }
+      if (bad) s_bad = 1;
+      __syncthreads();
+      use_ref = s_bad == 0;
+    }
+  }
+  const int64_t delta = use_ref ? (int64_t)np - rp : (int64_t)np - op;
+  const bool seed = kStore && !use_ref && np != op;
+  const bool move_entry = kStore && use_ref && !(a.ref_dst_k == a.ref_src_k && j == r);
+  if (delta != 0) {
+    fill_rotation(cs, a, delta, tid);
+    __syncthreads();
+  }
+
 #pragma unroll 2
   for (int e = tid; e < items; e += kCompactThreads) {
     const int layer = e / per_layer;
     const int rem = e - layer * per_layer;
-    const int h = rem >> 3;
-    const int cidx = rem & 7;
-    const int64_t so = (int64_t)layer * a.src_layer_stride + src_off + h * kHeadDim + cidx * 8;
-    const int64_t d_o = (int64_t)layer * a.dst_layer_stride + dst_off + h * kHeadDim + cidx * 8;
-    uint4 klo = *(const uint4*)(a.src_k + so);
-    uint4 khi = *(const uint4*)(a.src_k + so + 64);
+    const int64_t col = (rem >> 3) * kHeadDim + (rem & 7) * 8;
+    const int64_t so = (int64_t)layer * a.src_layer_stride + src_off + col;
+    const int64_t d_o = (int64_t)layer * a.dst_layer_stride + dst_off + col;
+    uint4 klo, khi;
+    if (kStore && use_ref) {
+      const int64_t ro = (int64_t)layer * a.ref_src_layer_stride + j * slot_stride + col;
+      klo = *(const uint4*)(a.ref_src_k + ro);
+      khi = *(const uint4*)(a.ref_src_k + ro + 64);
+    } else {
+      klo = *(const uint4*)(a.src_k + so);
+      khi = *(const uint4*)(a.src_k + so + 64);
+    }
+    if (kStore && (seed || move_entry)) {
+      const int64_t rd = (int64_t)layer * a.ref_dst_layer_stride + r * slot_stride + col;
+      *(uint4*)(a.ref_dst_k + rd) = klo;
+      *(uint4*)(a.ref_dst_k + rd + 64) = khi;
+    }
     uint4 vlo, vhi;
     if (!in_place) {
       vlo = *(const uint4*)(a.src_v + so);
       vhi = *(const uint4*)(a.src_v + so + 64);
     }
-    if (delta != 0) rotate_chunk(klo, khi, &cs[cidx * 8]);
+    if (delta != 0) rotate_chunk(klo, khi, &cs[(rem & 7) * 8]);
     *(uint4*)(a.dst_k + d_o) = klo;
     *(uint4*)(a.dst_k + d_o + 64) = khi;
     if (!in_place) {
@@ -125,6 +198,12 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
       *(uint4*)(a.dst_v + d_o + 64) = vhi;
     }
   }
+  if (kStore && tid == 0) a.ref_dst_pos[r] = use_ref ? rp : (seed ? op : KV_REF_NONE);
+}
+
+__global__ __launch_bounds__(256) void ref_invalidate_kernel(int32_t* pos, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) pos[i] = KV_REF_NONE;
 }
 
 // New positions and per-token metadata, one thread per rank (coalesced over ranks).
@@ -157,7 +236,16 @@ __global__ __launch_bounds__(256) void gather_meta_kernel(CompactArgs a) {
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const int64_t n = a.rank1 - a.rank0;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)n), dim3(kCompactThreads), 0, s, a);
+  if (a.ref_src_k)
+    hipLaunchKernelGGL(compact_kernel<true>, dim3((unsigned)n), dim3(kCompactThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(compact_kernel<false>, dim3((unsigned)n), dim3(kCompactThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ref_invalidate(int32_t* pos, int64_t count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ref_invalidate_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, pos, count);
   return hipGetLastError();
 }
 

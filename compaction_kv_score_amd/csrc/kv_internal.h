@@ -149,10 +149,18 @@ struct CompactArgs {
   const int32_t* old_pos;        // [N] indexed by source token
   int32_t* new_pos;              // [ranks] (nullable)
   int32_t renumber_base;
-  double log_theta;              // ln(rope_theta)
+  double inv_freq[kHeadDim / 2]; // RoPE frequency of pair (i, i + 64)
+  // reference store (nullable): keys [L][slot][Hkv][128] bf16 and valid positions [slot]
+  const uint16_t* ref_src_k;
+  const int32_t* ref_src_pos;
+  int64_t ref_src_layer_stride;
+  uint16_t* ref_dst_k;
+  int32_t* ref_dst_pos;
+  int64_t ref_dst_layer_stride;
   MetaSet meta;
 };
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+hipError_t launch_ref_invalidate(int32_t* pos, int64_t count, hipStream_t s);
 hipError_t launch_gather_meta(const CompactArgs& a, hipStream_t s);
 
 }  // namespace kvs

@@ -236,6 +236,84 @@ int32_t kv_compact_rerope(const kv_cache_desc *src, const kv_cache_desc *dst,
                           hipStream_t stream);
 
 /*
+ * RoPE frequency tables (PACE Sec. 3.5: split-half RoPE with static frequency scaling,
+ * default, linear, YaRN and Llama-3 style).  theta_i (i < 64) rotates pair (i, i + 64).
+ *   KV_ROPE_DEFAULT: theta_i = base^(-2i/128)
+ *   KV_ROPE_LINEAR:  theta_i = base^(-2i/128) / factor
+ *   KV_ROPE_LLAMA3:  with w_i = 2 pi / base^(-2i/128) and L = original_max_position:
+ *                    w_i < L/high_freq_factor keeps the frequency, w_i > L/low_freq_factor
+ *                    divides it by factor, in between (1-t)/factor + t times it with
+ *                    t = (L/w_i - low_freq_factor) / (high_freq_factor - low_freq_factor)
+ *   KV_ROPE_YARN:    r_i = L / w_i, g = clamp((r_i - beta_slow)/(beta_fast - beta_slow), 0, 1),
+ *                    (1-g)/factor + g times the frequency (only the rotation: a magnitude
+ *                    factor applied when the key was cached stays in it)
+ *   KV_ROPE_TABLE:   the caller's 64 frequencies (host array)
+ */
+#define KV_ROPE_DEFAULT 0
+#define KV_ROPE_LINEAR 1
+#define KV_ROPE_LLAMA3 2
+#define KV_ROPE_YARN 3
+#define KV_ROPE_TABLE 4
+
+typedef struct kv_rope {
+  int32_t kind;                 /* KV_ROPE_* */
+  int32_t original_max_position;/* L for LLAMA3 and YARN */
+  double base;                  /* rope_theta, > 1 */
+  double factor;                /* LINEAR, LLAMA3, YARN: > 0 */
+  double low_freq_factor;       /* LLAMA3 */
+  double high_freq_factor;      /* LLAMA3, > low_freq_factor */
+  double beta_fast, beta_slow;  /* YARN ramp ends in rotations over L (32 and 1 typical) */
+  const double *inv_freq;       /* host [64], KV_ROPE_TABLE */
+} kv_rope;
+
+/* Host-only.  The 64 frequencies of *rope; KV_EINVAL for an unknown kind or a bad
+ * parameter (non-positive factor, base <= 1, non-finite table entry). */
+int32_t kv_rope_inv_freq(const kv_rope *rope, double inv_freq[64] /* host */);
+
+/*
+ * Reference store of PACE (Sec. 3.2, non-compounding re-rotation): for every slot of a
+ * row, a bf16 copy of the key and the position it is valid at.  Element d of KV head h
+ * of slot s in layer l sits at k + l*layer_stride + (s*n_kv_heads + h)*128 + d.
+ * pos[s] == KV_REF_NONE marks an empty entry.  A compaction given a store:
+ *   - uses slot j's entry when it is not empty and the stored key, re-rotated from
+ *     pos[j] to the token's current position and rounded to bf16, equals the cached key
+ *     (value equality per element); the new key is then the stored key rotated to the
+ *     new position (one rounding), and the entry moves with the token;
+ *   - otherwise, when the token's position changes, stores the cached key with its
+ *     current position before rotating it (the key's first re-rotation);
+ *   - otherwise leaves the destination entry empty.
+ * Callers empty the entries of slots they reuse (kv_ref_invalidate); a stale entry that
+ * was missed fails the check and is replaced.  Device pointers, caller-owned.
+ */
+#define KV_REF_NONE INT32_MIN
+
+typedef struct kv_ref_store {
+  void *k;                      /* bf16 */
+  int32_t *pos;                 /* [n_slots] */
+  int64_t n_slots;
+  int64_t layer_stride;         /* elements, >= n_slots*n_kv_heads*128 when n_layers > 1 */
+} kv_ref_store;
+
+/* Empties entries [first, first + count) of the store (pos = KV_REF_NONE). */
+int32_t kv_ref_invalidate(const kv_ref_store *ref, int64_t first, int64_t count,
+                          hipStream_t stream);
+
+/*
+ * kv_compact_rerope with a frequency table and an optional reference store.  rope NULL
+ * means KV_ROPE_DEFAULT with base 1e6.  ref_src (indexed by source token, n_slots >=
+ * src.n_tokens) and ref_dst (indexed by rank, n_slots >= max_keep) are both given or
+ * both NULL, and must not overlap each other or the caches.  ref_dst entries of ranks
+ * >= n_keep are not written.
+ */
+int32_t kv_compact_rerope_ex(const kv_cache_desc *src, const kv_cache_desc *dst,
+                             const int32_t *keep_tokens, const int64_t *n_keep,
+                             int64_t max_keep, const int32_t *old_pos, int32_t *new_pos,
+                             int32_t renumber_base, const kv_rope *rope /* host */,
+                             int32_t limit, const kv_meta_desc *meta /* host array */,
+                             int32_t n_meta, const kv_ref_store *ref_src /* host */,
+                             const kv_ref_store *ref_dst /* host */, hipStream_t stream);
+
+/*
  * In-place form of segment eviction + compaction + re-rotation: removes tokens
  * [P, P + E') of the row and shifts the suffix [P + E', N) left by E' inside the same
  * cache, re-rotating each moved key by its position change.  pos[N] holds the physical
@@ -249,6 +327,15 @@ int32_t kv_compact_segment_inplace(const kv_cache_desc *cache, int64_t prefix_le
                                    double rope_theta, int32_t limit,
                                    const kv_meta_desc *meta /* host array */,
                                    int32_t n_meta, hipStream_t stream);
+
+/* kv_compact_segment_inplace with a frequency table (NULL: default, base 1e6) and an
+ * optional reference store (n_slots >= N) that moves in place with its tokens.  A token
+ * that keeps both its slot and its position is not touched, and neither is its entry. */
+int32_t kv_compact_segment_inplace_ex(const kv_cache_desc *cache, int64_t prefix_len,
+                                      int64_t evict_len, int32_t *pos, int32_t renumber_base,
+                                      const kv_rope *rope /* host */, int32_t limit,
+                                      const kv_meta_desc *meta /* host array */, int32_t n_meta,
+                                      const kv_ref_store *ref /* host */, hipStream_t stream);
 
 /* Host-only.  PACE's renumber trigger (Sec. 3.2): 1 when the next physical position
  * comes within headroom of the limit (next_pos >= limit - headroom), else 0. */

@@ -462,14 +462,16 @@ def renumbered_positions(n_keep, renumber_base, old_pos_kept):
     return renumber_base + np.arange(n_keep, dtype=np.int64)
 
 
-def compact_rerope(k, v, keep, old_pos, renumber_base, theta):
+def compact_rerope(k, v, keep, old_pos, renumber_base, theta, inv_freq=None):
     """Stable in-order gather of kept tokens plus exact re-rotation of their keys.
 
     k, v: [L][N][Hkv][D] logical arrays holding bf16 values; keep: ascending kept token
     indices.  Rank r takes source j = keep[r].  V is copied verbatim.  K is copied
     verbatim when delta = new_pos - old_pos is 0, otherwise rotated by delta in float64
     (Proposition 1: re-rotating the cached key by the position difference gives the key
-    at the new position) and rounded once to bf16 (RNE).  Returns (k', v', new_pos).
+    at the new position) and rounded once to bf16 (RNE).  The frequencies are
+    theta ** (-2i/D), or the inv_freq table when given (scaled RoPE).
+    Returns (k', v', new_pos).
     Reading: the "fp32" derivation of the pages is evaluated here in float64 from the
     exact bf16 inputs, so the oracle holds the correctly rounded result.
     """
@@ -482,7 +484,7 @@ def compact_rerope(k, v, keep, old_pos, renumber_base, theta):
     out_k = kk.copy()
     moved = np.nonzero(delta != 0)[0]
     if moved.size:
-        rot = rope_rotate(kk[:, moved], delta[moved][None, :, None], theta)
+        rot = rope_rotate(kk[:, moved], delta[moved][None, :, None], theta, inv_freq)
         out_k[:, moved] = bf16_round(rot)
     return out_k, vv, new_pos
 

@@ -161,3 +161,46 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         kv._ptr(torch.zeros(4))
+
+
+@pytest.mark.parametrize("kind,kw", [
+    ("default", {}), ("linear", dict(factor=4.0)),
+    ("llama3", dict(factor=8.0, original_max_position=8192, low_freq_factor=1.0, high_freq_factor=4.0)),
+    ("yarn", dict(factor=16.0, original_max_position=4096, beta_fast=32.0, beta_slow=1.0))])
+@pytest.mark.parametrize("base", [1e4, 5e5, 1e6])
+def test_rope_tables_match_oracle(kind, kw, base):
+    """kv_rope_inv_freq (host-only) against the oracle's scaled tables."""
+    got = np.array(kv.kv_rope_inv_freq(kv.kv_rope(kind, base=base, **kw)))
+    np.testing.assert_allclose(got, O.scaled_inv_freq(kind, base, **kw), rtol=1e-14, atol=0)
+
+
+def test_rope_table_validation_and_explicit_table():
+    L = kv.lib()
+    out = (ctypes.c_double * 64)()
+    for bad in (kv.kv_rope("default", base=1.0), kv.kv_rope("linear", factor=0.0),
+                kv.kv_rope("llama3", factor=8.0, low_freq_factor=4.0, high_freq_factor=1.0),
+                kv.kv_rope("yarn", factor=2.0, beta_fast=1.0, beta_slow=32.0),
+                kv.kv_rope(7), kv.kv_rope("table"),
+                kv.kv_rope("table", table=[1.0] * 63 + [float("nan")])):
+        assert L.kv_rope_inv_freq(ctypes.byref(bad), out) == kv.KV_EINVAL
+    tab = [0.5 ** i for i in range(64)]
+    assert kv.kv_rope_inv_freq(kv.kv_rope("table", table=tab)) == tab
+
+
+def test_compact_ex_store_validation():
+    L = kv.lib()
+    src, dst = _cache(), _cache(k=FAKE * 3, v=FAKE * 4)
+    rope = kv.kv_rope("default")
+    store = lambda k, pos, n=100: kv.KvRefStore(k, pos, n, n * 2 * 128)  # noqa: E731
+    a, b = store(FAKE * 5, FAKE * 6), store(FAKE * 7, FAKE * 8)
+    call = lambda rs, rd, mk=10: L.kv_compact_rerope_ex(  # noqa: E731
+        ctypes.byref(src), ctypes.byref(dst), FAKE, None, mk, FAKE, None, 0, ctypes.byref(rope), 0,
+        None, 0, rs, rd, None)
+    assert call(ctypes.byref(a), None) == kv.KV_EINVAL                        # one store only
+    assert call(ctypes.byref(a), ctypes.byref(a)) == kv.KV_EINVAL             # same store twice
+    small = store(FAKE * 5, FAKE * 6, n=50)
+    assert call(ctypes.byref(small), ctypes.byref(b)) == kv.KV_EINVAL         # fewer slots than N
+    assert call(ctypes.byref(a), ctypes.byref(store(FAKE * 7, FAKE * 8, n=5))) == kv.KV_EINVAL
+    r = kv.KvRefStore(FAKE, FAKE, 100, 100 * 2 * 128)
+    assert L.kv_ref_invalidate(ctypes.byref(r), 90, 20, None) == kv.KV_EINVAL
+    assert L.kv_ref_invalidate(ctypes.byref(r), 0, 0, None) == kv.KV_OK
