@@ -353,6 +353,103 @@ def expand_items(items, item_tokens, n_tokens):
 
 
 # --------------------------------------------------------------------------------------
+# O4b: ActKV LRFU keep scores with the top-p hit mask (ActKV Sec. 5.1, Algorithm 1)
+# --------------------------------------------------------------------------------------
+
+def topp_weights(score):
+    """Fixed-point weights of the top-p rule: w_j = floor(s_j * 2**shift) for finite
+    s_j > 0, else 0, with shift = 52 - ceil(log2 n) - e where max s < 2**e, so that the
+    total stays below 2**52 and every sum below is exact in integers and in float64.
+    Reading: ActKV gives the rule (an entry is a hit when its score is in the top-p set,
+    p = 90%) but not the arithmetic; fixing it in integers makes the set reproducible.
+    Returns (w as Python ints, shift)."""
+    sc = np.asarray(score, dtype=np.float32).astype(np.float64)
+    good = np.isfinite(sc) & (sc > 0)
+    n = len(sc)
+    if not good.any():
+        return [0] * n, 0
+    e = int(np.frexp(sc[good].max())[1])            # max < 2**e
+    bits = 52 - (int(math.ceil(math.log2(n))) if n > 1 else 0)
+    shift = bits - e
+    w = [int(math.floor(math.ldexp(float(x), shift))) if g else 0 for x, g in zip(sc, good)]
+    return w, shift
+
+
+def topp_hit_mask(score, p):
+    """Hit mask of ActKV's LRFU (Sec. 5.1): the smallest prefix of the entries in the
+    total order (score descending, index ascending; -0 == +0; NaN and non-positive
+    scores carry no weight) whose weight reaches ceil(p * W), W the total weight (see
+    topp_weights), p as float32.  No entry is a hit when that target is 0."""
+    sc = np.asarray(score, dtype=np.float32)
+    w, _ = topp_weights(sc)
+    total = sum(w)
+    target = math.ceil(float(np.float32(p)) * float(total))
+    hit = np.zeros(len(sc), dtype=bool)
+    if target <= 0:
+        return hit
+    key = np.where(np.isnan(sc), -np.inf, sc.astype(np.float64))
+    key = np.where(key == 0, 0.0, key)
+    order = sorted(range(len(sc)), key=lambda j: (-key[j], j))
+    acc = 0
+    for j in order:
+        if w[j] == 0:
+            break
+        hit[j] = True
+        acc += w[j]
+        if acc >= target:
+            break
+    return hit
+
+
+def lrfu_update(keep_score, attn_score, p=0.9, decay=0.5):
+    """One keep-score step of ActKV's attention-aware LRFU (Sec. 5.1, Algorithm 1):
+    KS <- decay * KS + AttnScore on hits, KS <- decay * KS on misses.  New entries
+    enter with KS = 0 (the caller appends zeros).  float64; returns (KS', hit)."""
+    a = np.asarray(attn_score, dtype=np.float32)
+    hit = topp_hit_mask(a, p)
+    ks = float(np.float32(decay)) * np.asarray(keep_score, dtype=np.float64)
+    ks = ks + np.where(hit, a.astype(np.float64), 0.0)
+    return ks, hit
+
+
+# --------------------------------------------------------------------------------------
+# O4c: ActKV in-place tail compaction (ActKV Sec. 7.2, Algorithm 4)
+# --------------------------------------------------------------------------------------
+
+def tail_window(n_tokens, budget, block):
+    """Target region of the compaction: the last X = ceil(budget/block) of the
+    Y = ceil(n_tokens/block) logical blocks, from start = (Y - X)*block for budget
+    slots.  Returns (start, end)."""
+    y = -(-n_tokens // block)
+    x = -(-budget // block)
+    start = (y - x) * block
+    return start, start + budget
+
+
+def tail_compaction_pairs(n_tokens, keep, budget, block):
+    """Copy plan of Algorithm 4: destinations are the slots of the target region whose
+    entries are not kept, sources the kept entries outside it, both ascending, paired in
+    order.  Sources and destinations are disjoint, so all copies can run at once.
+    Returns (start, end, src, dst, overflow) with overflow when more kept entries lie
+    outside the region than it has free slots (only the first ones are paired)."""
+    start, end = tail_window(n_tokens, budget, block)
+    keep = np.asarray(keep, dtype=np.int64)
+    inside = set(int(j) for j in keep if start <= j < end)
+    dst = [p for p in range(start, end) if p not in inside]
+    src = [int(j) for j in keep if not (start <= j < end)]
+    n = min(len(src), len(dst))
+    return start, end, np.array(src[:n], dtype=np.int64), np.array(dst[:n], dtype=np.int64), len(src) > len(dst)
+
+
+def tail_compact(arr, src, dst):
+    """Apply the plan to a logical array [..., slots, ...] along axis 1 (slot axis):
+    arr[:, dst] = arr[:, src].  Metadata arrays [slots] use axis 0 (pass arr[None])."""
+    out = np.array(arr, copy=True)
+    out[:, dst] = np.asarray(arr)[:, src]
+    return out
+
+
+# --------------------------------------------------------------------------------------
 # O5: Penelope segment eviction and recompute cost
 # --------------------------------------------------------------------------------------
 

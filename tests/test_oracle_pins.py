@@ -448,6 +448,132 @@ def test_penelope_segment_blocks():
 
 
 # ---------------------------------------------------------------------------------------
+# O4b ActKV LRFU and top-p hit mask (Sec. 5.1, Algorithm 1)
+# ---------------------------------------------------------------------------------------
+
+def _rank_order(sc):
+    key = np.where(np.isnan(sc), -np.inf, sc.astype(np.float64))
+    key = np.where(key == 0, 0.0, key)
+    return sorted(range(len(sc)), key=lambda j: (-key[j], j))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_topp_hit_mask_is_the_minimal_prefix(seed):
+    """The hits reach the target weight, dropping the lowest-ranked hit falls short of
+    it, and every hit ranks above every positive-weight miss (total order: score
+    descending, index ascending)."""
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(1, 40))
+    sc = rng.choice([0.0, -0.0, 0.25, 0.5, 1e-3, 3.0, float(rng.random())], n).astype(np.float32)
+    if seed % 3 == 0:
+        sc[rng.integers(0, n)] = np.nan
+    p = float(rng.choice([0.5, 0.9, 0.999, 1.0]))
+    hit = O.topp_hit_mask(sc, p)
+    w, _ = O.topp_weights(sc)
+    total = sum(w)
+    target = math.ceil(float(np.float32(p)) * total)
+    hw = [w[j] for j in range(n) if hit[j]]
+    if target == 0:
+        assert not hit.any()
+        return
+    assert sum(hw) >= target
+    order = [j for j in _rank_order(sc)]
+    ranks = {j: r for r, j in enumerate(order)}
+    last = max((j for j in range(n) if hit[j]), key=lambda j: ranks[j])
+    assert sum(hw) - w[last] < target
+    for j in range(n):
+        if not hit[j] and w[j] > 0:
+            assert all(ranks[h] < ranks[j] for h in range(n) if hit[h])
+    assert all(w[j] > 0 for j in range(n) if hit[j])
+
+
+def test_topp_weights_exact_and_bounded():
+    rng = np.random.default_rng(310)
+    sc = (rng.random(100_000) ** 4).astype(np.float32)
+    w, shift = O.topp_weights(sc)
+    assert sum(w) < 2 ** 52
+    order = np.argsort(sc, kind="stable")
+    ws = np.array(w, dtype=np.float64)[order]
+    assert (np.diff(ws) >= 0).all()                   # monotone in the score
+    j = int(np.argmax(sc))
+    assert w[j] == math.floor(float(sc[j]) * 2.0 ** shift)
+
+
+def test_topp_special_cases():
+    # one entry holding 95% of the weight is the only hit at p = 90%
+    sc = np.array([0.01] * 5 + [0.95] + [0.01] * 0, dtype=np.float32)
+    assert O.topp_hit_mask(sc, 0.9).tolist() == [False] * 5 + [True]
+    # p = 1 takes every entry with weight; equal scores are taken by index
+    sc = np.array([0.2, 0.2, 0.2, 0.0, 0.2, 0.2], dtype=np.float32)
+    assert O.topp_hit_mask(sc, 1.0).tolist() == [True, True, True, False, True, True]
+    assert O.topp_hit_mask(sc, 0.5).tolist() == [True, True, True, False, False, False]
+    assert not O.topp_hit_mask(np.zeros(7, np.float32), 0.9).any()
+    assert not O.topp_hit_mask(sc, 0.0).any()
+
+
+def test_lrfu_update_rule():
+    """KS <- lambda KS + AttnScore on hits, lambda KS on misses (Algorithm 1, steps 4-7):
+    lambda = 0 keeps only the current hits, lambda = 1 accumulates, and a missed entry
+    decays geometrically instead of dropping out."""
+    a = np.array([0.5, 0.25, 0.125, 0.125], dtype=np.float32)  # 0.75 < 0.85 <= 0.875
+    ks0 = np.array([1.0, 2.0, 3.0, 4.0])
+    ks, hit = O.lrfu_update(ks0, a, p=0.85, decay=0.0)
+    assert hit.tolist() == [True, True, True, False]
+    np.testing.assert_allclose(ks, np.where(hit, a.astype(np.float64), 0.0))
+    ks, _ = O.lrfu_update(ks0, a, p=1.0, decay=1.0)
+    np.testing.assert_allclose(ks, ks0 + a.astype(np.float64))
+    ks = np.array([1.0, 0.0])
+    for _ in range(5):
+        ks, hit = O.lrfu_update(ks, np.array([0.0, 1.0], np.float32), p=0.9, decay=0.5)
+        assert hit.tolist() == [False, True]
+    assert ks[0] == 0.5 ** 5 and ks[1] == 1.0 + 0.5 + 0.25 + 0.125 + 0.0625
+
+
+# ---------------------------------------------------------------------------------------
+# O4c ActKV in-place tail compaction (Sec. 7.2, Algorithm 4)
+# ---------------------------------------------------------------------------------------
+
+def test_tail_compaction_worked_example():
+    """40 used slots in blocks of 8 and a budget of 12: Y = 5, X = 2, region [24, 36).
+    Kept 33 and 35 stay; 1, 5, 20 and 38 move into the first free slots 24..27."""
+    start, end, src, dst, over = O.tail_compaction_pairs(40, [1, 5, 20, 33, 35, 38], 12, 8)
+    assert (start, end, over) == (24, 36, False)
+    assert src.tolist() == [1, 5, 20, 38] and dst.tolist() == [24, 25, 26, 27]
+    arr = np.arange(48)[None, :] * 10
+    out = O.tail_compact(arr, src, dst)
+    assert out[0, 24:28].tolist() == [10, 50, 200, 380] and out[0, 33] == 330 and out[0, 35] == 350
+    assert (out[0, :24] == arr[0, :24]).all()
+    # more kept entries than the region holds: only the first ones are paired
+    *_, src2, dst2, over2 = O.tail_compaction_pairs(40, list(range(0, 40, 3)), 12, 8)
+    assert over2 and len(src2) == len(dst2)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tail_compaction_invariants(seed):
+    rng = np.random.default_rng(320 + seed)
+    bs = int(rng.choice([4, 16, 64]))
+    n = int(rng.integers(bs + 1, 600))
+    budget = int(rng.integers(1, n))
+    n_keep = int(rng.integers(0, budget + 1))
+    keep = np.sort(rng.choice(n, n_keep, replace=False))
+    start, end, src, dst, over = O.tail_compaction_pairs(n, keep, budget, bs)
+    y, x = -(-n // bs), -(-budget // bs)
+    assert start == (y - x) * bs and end - start == budget and end <= y * bs
+    assert not over
+    window = set(range(start, end))
+    assert set(dst.tolist()) <= window and not (set(dst.tolist()) & set(keep.tolist()))
+    assert not (set(src.tolist()) & window) and len(set(src.tolist()) | set(dst.tolist())) == 2 * len(src)
+    data = rng.standard_normal((2, y * bs))
+    out = O.tail_compact(data, src, dst)
+    # every kept entry now lives inside the region, each exactly once
+    placed = [out[:, j] for j in sorted((set(keep.tolist()) & window) | set(dst.tolist()))]
+    assert len(placed) == n_keep
+    got = sorted(tuple(c) for c in placed)
+    want = sorted(tuple(c) for c in data[:, keep].T)
+    assert got == want
+
+
+# ---------------------------------------------------------------------------------------
 # O6 re-rotation (PACE Sec. 3.2, Proposition 1)
 # ---------------------------------------------------------------------------------------
 
