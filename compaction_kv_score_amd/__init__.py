@@ -120,6 +120,11 @@ def lib() -> ctypes.CDLL:
             "kv_compact_segment_inplace": (i32, [P(KvCacheDesc), i64, i64, vp, i32, ctypes.c_double,
                                                  i32, P(KvMetaDesc), i32, vp]),
             "kv_rope_inv_freq": (i32, [P(KvRope), P(ctypes.c_double)]),
+            "kv_lrfu_workspace_size": (i32, [i64, P(sz)]),
+            "kv_lrfu_update": (i32, [vp, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float, vp, vp, vp, sz,
+                                     vp]),
+            "kv_compact_tail_inplace": (i32, [P(KvCacheDesc), vp, vp, i64, i64, P(KvMetaDesc), i32, P(i64),
+                                              vp, vp]),
             "kv_ref_invalidate": (i32, [P(KvRefStore), i64, i64, vp]),
             "kv_compact_rerope_ex": (i32, [P(KvCacheDesc), P(KvCacheDesc), vp, vp, i64, vp, vp, i32,
                                            P(KvRope), i32, P(KvMetaDesc), i32, P(KvRefStore),
@@ -270,6 +275,35 @@ def kv_select(item_score, item_pinned, item_tokens, n_tokens, budget_items, keep
                            _ptr(n_keep), _ptr(status), _ptr(workspace), workspace.numel(),
                            _stream(item_score.device)), "kv_select")
     return workspace
+
+
+def kv_lrfu_workspace_size(n: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().kv_lrfu_workspace_size(int(n), ctypes.byref(b)), "kv_lrfu_workspace_size")
+    return b.value
+
+
+def kv_lrfu_update(attn_score, keep_score, scale=1.0, top_p=0.9, decay=0.5, hit=None, workspace=None):
+    """ActKV LRFU keep-score step (see kv_lrfu_update in include/kvscore.h)."""
+    n = int(attn_score.numel())
+    if workspace is None:
+        workspace = torch.empty(kv_lrfu_workspace_size(n), dtype=torch.uint8, device=attn_score.device)
+    _check(lib().kv_lrfu_update(_ptr(attn_score), n, float(scale), float(top_p), float(decay),
+                                _ptr(keep_score), _ptr(hit), _ptr(workspace), workspace.numel(),
+                                _stream(attn_score.device)), "kv_lrfu_update")
+    return workspace
+
+
+def kv_compact_tail_inplace(cache: PagedCache, keep_tokens, n_keep, max_keep, budget, meta=None,
+                            status=None) -> int:
+    """ActKV in-place tail compaction (see kv_compact_tail_inplace); meta is a list of
+    tensors moved in place.  Returns the first slot of the target region."""
+    arr, n_meta = _meta_array([(m, m) for m in (meta or [])])
+    start = ctypes.c_int64(0)
+    _check(lib().kv_compact_tail_inplace(ctypes.byref(cache.desc()), _ptr(keep_tokens), _ptr(n_keep),
+                                         int(max_keep), int(budget), arr, n_meta, ctypes.byref(start),
+                                         _ptr(status), _stream(cache.k.device)), "kv_compact_tail_inplace")
+    return start.value
 
 
 def kv_select_segment(n_tokens, prefix_len, evict_tokens, block, keep_tokens=None, n_keep_dev=None):

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvscore.so")
 
-SOURCES = ["kv_api.hip", "kv_score.hip", "kv_epilogue.hip", "kv_select.hip", "kv_compact.hip"]
+SOURCES = ["kv_api.hip", "kv_score.hip", "kv_epilogue.hip", "kv_select.hip", "kv_compact.hip",
+           "kv_lrfu.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -38,11 +39,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libkvscore.so next to this file; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,6 +49,23 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source (in parallel, one object each) and link libkvscore.so next
+    to this file; returns its path."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="kvscore_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, s.replace(".hip", ".o")) for s in SOURCES]
+        cmds = [[hipcc(), *compile_flags, "-c", "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+        with ThreadPoolExecutor(workers) as pool:
+            list(pool.map(lambda c: _run(c, verbose), cmds))
+        tmp = LIB + ".tmp"
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -324,6 +324,39 @@ int32_t kv_select(const float* item_score, const uint8_t* item_pinned, int64_t n
   return e == hipSuccess ? KV_OK : hip_fail(e);
 }
 
+int32_t kv_lrfu_workspace_size(int64_t n, size_t* bytes) {
+  if (!bytes || n <= 0) return KV_EINVAL;
+  *bytes = lrfu_workspace_bytes(n);
+  return KV_OK;
+}
+
+int32_t kv_lrfu_update(const float* attn_score, int64_t n, float scale, float top_p, float decay,
+                       float* keep_score, uint8_t* hit, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!attn_score || !keep_score || n <= 0 || n > 0x7FFFFFFFLL) return KV_EINVAL;
+  if (!(top_p >= 0.f && top_p <= 1.f) || !(decay >= 0.f && decay <= 1.f) || !isfinite(scale))
+    return KV_EINVAL;
+  if (!ws || ws_bytes < lrfu_workspace_bytes(n)) return KV_EWORKSPACE;
+  int32_t rc = check_device();
+  if (rc) return rc;
+  LrfuArgs a;
+  memset(&a, 0, sizeof(a));
+  a.score = attn_score;
+  a.scale = scale;
+  a.n = n;
+  a.top_p = top_p;
+  a.decay = decay;
+  a.keep_score = keep_score;
+  a.hit = hit;
+  a.n_blocks = lrfu_blocks(n);
+  a.per_block = (n + a.n_blocks - 1) / a.n_blocks;
+  char* w = (char*)ws;
+  a.st = (ToppState*)w;
+  a.hist = (unsigned long long*)(w + 256);
+  a.counts = (int64_t*)(w + 256 + (size_t)a.n_blocks * 2048 * sizeof(unsigned long long));
+  const hipError_t e = launch_lrfu(a, stream);
+  return e == hipSuccess ? KV_OK : hip_fail(e);
+}
+
 int32_t kv_select_segment(int64_t n_tokens, int64_t prefix_len, int64_t evict_tokens, int32_t block,
                           int32_t* keep_tokens, int64_t keep_capacity, int64_t* n_keep_dev,
                           int64_t* n_keep_host, int64_t* evict_len_host, hipStream_t stream) {
@@ -549,6 +582,44 @@ int32_t kv_compact_segment_inplace_ex(const kv_cache_desc* cache, int64_t prefix
     if ((e = launch_gather_meta(a, stream)) != hipSuccess) return hip_fail(e);
   }
   return KV_OK;
+}
+
+int32_t kv_compact_tail_inplace(const kv_cache_desc* cache, const int32_t* keep_tokens,
+                                const int64_t* n_keep, int64_t max_keep, int64_t budget,
+                                const kv_meta_desc* meta, int32_t n_meta, int64_t* start_host,
+                                uint32_t* status, hipStream_t stream) {
+  int32_t rc = check_cache(cache);
+  if (rc) return rc;
+  if (!keep_tokens || max_keep < 0 || max_keep > cache->n_tokens || budget <= 0) return KV_EINVAL;
+  MetaSet ms;
+  if ((rc = check_meta(meta, n_meta, &ms))) return rc;
+  for (int i = 0; i < ms.n; ++i)
+    if (ms.src[i] != ms.dst[i]) return KV_EINVAL;
+  const int64_t N = cache->n_tokens, blk = cache->page_size;
+  const int64_t y = (N + blk - 1) / blk, x = (budget + blk - 1) / blk;
+  const int64_t start = budget >= N ? 0 : (y - x) * blk;
+  if (start_host) *start_host = start;
+  if ((rc = check_device())) return rc;
+  TailArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = (uint16_t*)cache->k;
+  a.v = (uint16_t*)cache->v;
+  a.layer_stride = cache->layer_stride;
+  a.page_stride = cache->page_stride;
+  a.bt = cache->block_table;
+  a.n_layers = cache->n_layers;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.page_shift = log2_exact(cache->page_size);
+  a.keep = keep_tokens;
+  a.n_keep = n_keep;
+  a.max_keep = max_keep;
+  a.start = start;
+  a.budget = budget >= N ? N : budget;
+  a.status = status;
+  a.meta = ms;
+  const int64_t grid = max_keep < a.budget ? max_keep : a.budget;
+  const hipError_t e = launch_tail_compact(a, grid, stream);
+  return e == hipSuccess ? KV_OK : hip_fail(e);
 }
 
 int32_t kv_compact_segment_inplace(const kv_cache_desc* cache, int64_t prefix_len, int64_t evict_len,

@@ -231,7 +231,81 @@ __global__ __launch_bounds__(256) void gather_meta_kernel(CompactArgs a) {
   }
 }
 
+// Number of leading entries of a monotone predicate over [0, n) (true, then false),
+// found by the whole workgroup with 256-way splits: a handful of rounds for any n.
+template <class Pred>
+__device__ int64_t block_count_true(int64_t n, Pred pred) {
+  int64_t lo = 0, hi = n;                 // the count lies in [lo, hi]
+  while (hi > lo) {
+    const int64_t step = (hi - lo + kCompactThreads - 1) / kCompactThreads;
+    const int64_t p = lo + (int64_t)(threadIdx.x + 1) * step - 1;
+    const int m = __syncthreads_count(p < hi && pred(p));
+    const int64_t nlo = lo + (int64_t)m * step;
+    const int64_t nhi = lo + (int64_t)(m + 1) * step - 1;
+    lo = nlo;
+    hi = nhi < hi ? nhi : hi;
+  }
+  return lo;
+}
+
+// ActKV Sec. 7.2 / Algorithm 4: the kept entries outside the target region move into
+// the region's free slots, source d to destination d in ascending order.  Workgroup d
+// finds its pair by block-wide searches over the ascending keep list: the d-th source
+// is keep[d] or keep[d + k_in] (k_in kept entries lie inside the region), the d-th free
+// slot is start + d + c with c the kept entries inside whose own free-slot count
+// keep[r] - start - (r - r_in) does not exceed d.  Sources and destinations are
+// disjoint, so every copy runs at once and nothing is staged.
+__global__ __launch_bounds__(kCompactThreads) void tail_compact_kernel(TailArgs a) {
+  const int tid = threadIdx.x;
+  int64_t n_keep = a.n_keep ? *a.n_keep : a.max_keep;
+  n_keep = n_keep < a.max_keep ? n_keep : a.max_keep;
+  n_keep = n_keep < 0 ? 0 : n_keep;
+  const int64_t start = a.start, end = a.start + a.budget;
+  const int32_t* keep = a.keep;
+  const int64_t r_in = block_count_true(n_keep, [&](int64_t i) { return keep[i] < start; });
+  const int64_t r_out = block_count_true(n_keep, [&](int64_t i) { return keep[i] < end; });
+  const int64_t k_in = r_out - r_in;
+  const int64_t n_src = n_keep - k_in, holes = a.budget - k_in;
+  const int64_t n_pairs = n_src < holes ? n_src : holes;
+  if (blockIdx.x == 0 && tid == 0 && a.status) *a.status = n_src > holes ? KV_STATUS_KEEP_OVERFLOW : 0u;
+  const int64_t d = blockIdx.x;
+  if (d >= n_pairs) return;
+  const int64_t src = keep[d < r_in ? d : d + k_in];
+  const int64_t c = block_count_true(k_in, [&](int64_t i) { return keep[r_in + i] - start - i <= d; });
+  const int64_t dst = start + d + c;
+
+  const int slot_stride = a.n_kv_heads * kHeadDim;
+  const int64_t so = token_offset(src, a.page_shift, a.page_stride, a.bt, slot_stride);
+  const int64_t dof = token_offset(dst, a.page_shift, a.page_stride, a.bt, slot_stride);
+  const int per_layer = slot_stride / 8;            // 16-byte chunks per layer
+  const int items = a.n_layers * per_layer;
+  for (int e = tid; e < items; e += kCompactThreads) {
+    const int layer = e / per_layer;
+    const int64_t col = (int64_t)(e - layer * per_layer) * 8;
+    const int64_t lo = (int64_t)layer * a.layer_stride;
+    const uint4 kk = *(const uint4*)(a.k + lo + so + col);
+    const uint4 vv = *(const uint4*)(a.v + lo + so + col);
+    *(uint4*)(a.k + lo + dof + col) = kk;
+    *(uint4*)(a.v + lo + dof + col) = vv;
+  }
+  if (tid == 0) {
+    for (int m = 0; m < a.meta.n; ++m) {
+      switch (a.meta.elem_bytes[m]) {
+        case 1: ((uint8_t*)a.meta.dst[m])[dst] = ((const uint8_t*)a.meta.src[m])[src]; break;
+        case 2: ((uint16_t*)a.meta.dst[m])[dst] = ((const uint16_t*)a.meta.src[m])[src]; break;
+        case 4: ((uint32_t*)a.meta.dst[m])[dst] = ((const uint32_t*)a.meta.src[m])[src]; break;
+        default: ((uint64_t*)a.meta.dst[m])[dst] = ((const uint64_t*)a.meta.src[m])[src]; break;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tail_compact(const TailArgs& a, int64_t grid, hipStream_t s) {
+  hipLaunchKernelGGL(tail_compact_kernel, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(kCompactThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const int64_t n = a.rank1 - a.rank0;

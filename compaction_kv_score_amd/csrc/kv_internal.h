@@ -124,6 +124,35 @@ hipError_t launch_segment_keep(int64_t n_tokens, int64_t prefix, int64_t evict, 
                                int64_t capacity, int64_t* n_keep_dev, int64_t n_keep,
                                hipStream_t s);
 
+// ---------------------------------------------------------------- LRFU keep scores
+struct ToppState {                 // lives in the LRFU workspace
+  uint32_t prefix;               // bits of the boundary score fixed so far
+  uint32_t mask;
+  uint32_t mode;                 // 0 radix, 2 no hits
+  uint32_t ticket;
+  uint32_t max_bits;             // bits of the largest weighted score (0: none)
+  uint32_t pad;
+  uint64_t rem;                  // weight still missing from the target
+  uint64_t total;                // total weight W
+  int64_t c_eq;                  // entries equal to the boundary that are hits
+};
+struct LrfuArgs {
+  const float* score;            // AttnScore before scaling
+  float scale;
+  int64_t n;
+  float top_p, decay;
+  float* keep_score;             // in/out
+  uint8_t* hit;                  // nullable
+  ToppState* st;
+  unsigned long long* hist;      // [n_blocks][2048]
+  int64_t* counts;               // [n_blocks]
+  int n_blocks;
+  int64_t per_block;
+};
+int lrfu_blocks(int64_t n);
+size_t lrfu_workspace_bytes(int64_t n);
+hipError_t launch_lrfu(const LrfuArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- compaction kernels
 struct MetaSet {
   const void* src[KV_MAX_META];
@@ -161,6 +190,21 @@ struct CompactArgs {
 };
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 hipError_t launch_ref_invalidate(int32_t* pos, int64_t count, hipStream_t s);
+
+struct TailArgs {
+  uint16_t* k;
+  uint16_t* v;
+  int64_t layer_stride, page_stride;
+  const int32_t* bt;
+  int n_layers, n_kv_heads, page_shift;
+  const int32_t* keep;           // ascending kept slots
+  const int64_t* n_keep;         // device count (nullable: max_keep)
+  int64_t max_keep;
+  int64_t start, budget;         // target region [start, start + budget)
+  uint32_t* status;              // nullable
+  MetaSet meta;                  // arrays moved in place (src == dst)
+};
+hipError_t launch_tail_compact(const TailArgs& a, int64_t grid, hipStream_t s);
 hipError_t launch_gather_meta(const CompactArgs& a, hipStream_t s);
 
 }  // namespace kvs

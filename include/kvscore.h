@@ -200,6 +200,49 @@ int32_t kv_select(const float *item_score, const uint8_t *item_pinned, int64_t n
                   uint32_t *status, void *workspace, size_t workspace_bytes,
                   hipStream_t stream);
 
+/* Host-only.  Workspace bytes kv_lrfu_update needs for n entries. */
+int32_t kv_lrfu_workspace_size(int64_t n, size_t *bytes /* host */);
+
+/*
+ * ActKV's attention-aware LRFU keep scores ("ActKV: Efficient LLM Agents through
+ * Action-Guided KV Cache Management", Sec. 5.1, Algorithm 1, steps 4-7):
+ *   s_j = attn_score[j] * scale (float32; e.g. kv_score's group-maximum mass times
+ *         1/(L*Hkv*W) gives the mean over layers, KV heads and action queries);
+ *   hit_j: j is in the top-p set, the smallest prefix of the entries in the order
+ *         (s descending, index ascending) whose weight reaches ceil(top_p * W), with
+ *         fixed-point weights w = floor(s * 2^shift) for finite s > 0 (else 0),
+ *         shift = 52 - ceil(log2 n) - e and max s < 2^e, W the total weight; no hits
+ *         when that target is 0;
+ *   keep_score[j] <- decay * keep_score[j] + (hit_j ? s_j : 0).
+ * New entries enter with keep_score 0 (the caller appends them).  The retained set is
+ * then kv_select(keep_score, NULL, ...) (Algorithm 1, step 8).  hit (n bytes, 0/1) may be
+ * NULL.  top_p in [0, 1], decay in [0, 1].  Deterministic.
+ */
+int32_t kv_lrfu_update(const float *attn_score, int64_t n, float scale, float top_p, float decay,
+                       float *keep_score, uint8_t *hit, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * In-place tail compaction (ActKV Sec. 7.2, Algorithm 4).  With N = cache.n_tokens,
+ * block = cache.page_size, Y = ceil(N/block) and X = ceil(budget/block), the target
+ * region is logical slots [start, start + budget) with start = (Y - X)*block.  The kept
+ * slots outside it (keep_tokens, ascending) move into its slots that hold no kept
+ * entry, d-th source to d-th free slot, both ascending; kept slots inside stay.  K, V
+ * (every layer and head) and each meta array (src == dst, indexed by slot, covering
+ * Y*block slots) move together; keys are not re-rotated, their positions travel as
+ * metadata.  Afterwards every kept entry lies in the last X blocks, and blocks
+ * [0, start/block) hold nothing kept.  Sources and destinations are disjoint, so all
+ * copies run at once without staging.  n_keep (device, may be NULL = max_keep) is clamped
+ * to max_keep.  *start_host receives start.  When more kept entries lie outside the
+ * region than it has free slots, only the first ones move and *status (device,
+ * nullable) gets KV_STATUS_KEEP_OVERFLOW (0 otherwise).  budget >= N moves nothing.
+ */
+int32_t kv_compact_tail_inplace(const kv_cache_desc *cache, const int32_t *keep_tokens,
+                                const int64_t *n_keep, int64_t max_keep, int64_t budget,
+                                const kv_meta_desc *meta /* host array */, int32_t n_meta,
+                                int64_t *start_host /* host */, uint32_t *status,
+                                hipStream_t stream);
+
 /*
  * Segment eviction from the front of the private history ("Rethinking KV Cache
  * Eviction for Agentic LLM Serving", Part one): keep [0, P) and [P + E', N) where

@@ -204,3 +204,26 @@ def test_compact_ex_store_validation():
     r = kv.KvRefStore(FAKE, FAKE, 100, 100 * 2 * 128)
     assert L.kv_ref_invalidate(ctypes.byref(r), 90, 20, None) == kv.KV_EINVAL
     assert L.kv_ref_invalidate(ctypes.byref(r), 0, 0, None) == kv.KV_OK
+
+
+def test_lrfu_and_tail_validation():
+    L = kv.lib()
+    n = ctypes.c_size_t()
+    assert L.kv_lrfu_workspace_size(1000, ctypes.byref(n)) == kv.KV_OK and n.value > 256
+    assert L.kv_lrfu_workspace_size(0, ctypes.byref(n)) == kv.KV_EINVAL
+    ok = dict(scale=1.0, top_p=0.9, decay=0.5)
+    call = lambda ws, wb, **kw: L.kv_lrfu_update(FAKE, 1000, kw.get("scale", 1.0), kw.get("top_p", 0.9),  # noqa: E731
+                                                kw.get("decay", 0.5), FAKE, None, ws, wb, None)
+    assert call(FAKE, 16, **ok) == kv.KV_EWORKSPACE
+    assert call(FAKE, 1 << 30, top_p=1.5) == kv.KV_EINVAL
+    assert call(FAKE, 1 << 30, decay=-0.1) == kv.KV_EINVAL
+    assert call(FAKE, 1 << 30, scale=float("inf")) == kv.KV_EINVAL
+    c = _cache()
+    start = ctypes.c_int64()
+    assert L.kv_compact_tail_inplace(ctypes.byref(c), FAKE, None, 10, 0, None, 0, ctypes.byref(start), None,
+                                     None) == kv.KV_EINVAL
+    assert L.kv_compact_tail_inplace(ctypes.byref(c), None, None, 10, 50, None, 0, ctypes.byref(start), None,
+                                     None) == kv.KV_EINVAL
+    meta = (kv.KvMetaDesc * 1)(kv.KvMetaDesc(FAKE, FAKE * 2, 4, 0))
+    assert L.kv_compact_tail_inplace(ctypes.byref(c), FAKE, None, 10, 50, meta, 1, ctypes.byref(start), None,
+                                     None) == kv.KV_EINVAL

@@ -1,0 +1,162 @@
+"""GPU parity of ActKV's LRFU keep scores (top-p hit mask) and in-place tail compaction
+(kv_lrfu_update, kv_compact_tail_inplace) against the oracle.
+
+Bars: hit masks, moved slots, metadata and status bit-exact (integer decisions, taken in
+the same fixed-point arithmetic on both sides); keep scores within 1e-6 relative
+(float32 update against float64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import compaction_kv_score_amd as kv
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _scores(rng, n, dist):
+    if dist == "power":
+        return (rng.random(n) ** 8).astype(np.float32)
+    if dist == "ties":
+        return (rng.integers(0, 6, n) / 8.0).astype(np.float32)
+    if dist == "mixed":
+        s = (rng.random(n) ** 3).astype(np.float32)
+        s[rng.random(n) < 0.1] = 0.0
+        s[rng.random(n) < 0.05] = -0.0
+        s[rng.random(n) < 0.05] = -1.0
+        s[rng.random(n) < 0.01] = np.nan
+        return s
+    if dist == "equal":
+        return np.full(n, 0.125, np.float32)
+    if dist == "tiny":
+        return (rng.random(n) * 1e-30).astype(np.float32)
+    raise ValueError(dist)
+
+
+@pytest.mark.parametrize("n,dist,p,scale", [
+    (1, "power", 0.9, 1.0),
+    (100, "ties", 0.9, 1.0),
+    (5000, "mixed", 0.9, 1.0),
+    (5000, "equal", 0.5, 1.0),
+    (9000, "tiny", 0.9, 1.0),
+    (100_000, "power", 0.9, 1.0 / (36 * 8 * 64)),
+    (100_000, "ties", 1.0, 1.0),
+    (100_000, "mixed", 0.0, 1.0),
+    (262_147, "power", 0.999, 3.0),
+])
+def test_lrfu_update_parity(n, dist, p, scale):
+    rng = np.random.default_rng(n + len(dist))
+    a = _scores(rng, n, dist)
+    ks0 = (rng.random(n) * 2).astype(np.float32)
+    s = (a * np.float32(scale)).astype(np.float32)                # the float32 product the kernel forms
+    ks_ref, hit_ref = O.lrfu_update(ks0.astype(np.float64), s, p=p, decay=0.5)
+    ks = torch.from_numpy(ks0).to(DEV)
+    hit = torch.full((n,), 7, dtype=torch.uint8, device=DEV)
+    kv.kv_lrfu_update(torch.from_numpy(a).to(DEV), ks, scale=scale, top_p=p, decay=0.5, hit=hit)
+    torch.cuda.synchronize()
+    got_hit = hit.cpu().numpy().astype(bool)
+    assert (got_hit == hit_ref).all(), (int((got_hit != hit_ref).sum()), int(hit_ref.sum()))
+    np.testing.assert_allclose(ks.cpu().numpy().astype(np.float64), ks_ref, rtol=1e-6, atol=1e-37)
+
+
+def test_lrfu_steps_then_select():
+    """Five LRFU steps with new entries appended at KS = 0, then TopK by kv_select."""
+    rng = np.random.default_rng(7)
+    n, budget = 3000, 400
+    ks_ref = np.zeros(n)
+    ks = torch.zeros(n, device=DEV)
+    for step in range(5):
+        a = _scores(rng, n, "power")
+        ks_ref, _ = O.lrfu_update(ks_ref, a, p=0.9, decay=0.5)
+        kv.kv_lrfu_update(torch.from_numpy(a).to(DEV), ks, top_p=0.9, decay=0.5)
+        add = 200
+        ks_ref = np.concatenate([ks_ref, np.zeros(add)])
+        ks = torch.cat([ks, torch.zeros(add, device=DEV)])
+        n += add
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(ks.cpu().numpy().astype(np.float64), ks_ref, rtol=1e-5, atol=1e-30)
+    keep = torch.zeros(budget, dtype=torch.int32, device=DEV)
+    nk = torch.zeros(1, dtype=torch.int64, device=DEV)
+    kv.kv_select(ks, None, 1, n, budget, keep, nk)
+    torch.cuda.synchronize()
+    want, _ = O.select_items(ks.cpu().numpy(), None, budget)  # same float32 keys on both sides
+    assert int(nk) == budget and (keep.cpu().numpy() == want).all()
+
+
+def _paged(rng, logical, shuffle):
+    nl, slots, hkv, d = logical.shape
+    pages = slots // 16
+    phys = rng.permutation(pages + 3)[:pages] if shuffle else np.arange(pages)
+    buf = torch.zeros((nl, pages + 3, 16, hkv, d), dtype=torch.bfloat16)
+    lt = torch.from_numpy(logical).to(torch.bfloat16)
+    for p in range(pages):
+        buf[:, phys[p]] = lt[:, p * 16:(p + 1) * 16]
+    bt = torch.from_numpy(phys.astype(np.int32)).to(DEV) if shuffle else None
+    return buf.to(DEV), bt
+
+
+def _logical(t, bt, slots):
+    return O.gather_logical(t.float().cpu().double().numpy(), None if bt is None else bt.cpu().numpy(), 16, slots)
+
+
+@pytest.mark.parametrize("n,budget,n_keep,shuffle,dev_count", [
+    (1000, 300, 300, True, False),     # region reaches past N into the last block
+    (1024, 256, 200, False, True),     # fewer kept than the budget, device count
+    (777, 100, 100, True, False),
+    (5000, 2048, 2048, True, True),
+    (64, 16, 16, False, False),
+    (500, 600, 300, True, False),      # budget above N: nothing moves
+])
+def test_tail_compact_parity(n, budget, n_keep, shuffle, dev_count):
+    rng = np.random.default_rng(n + budget)
+    nl, hkv = 2, 2
+    slots = -(-n // 16) * 16
+    k = O.bf16_round(rng.standard_normal((nl, slots, hkv, 128)))
+    v = O.bf16_round(rng.standard_normal((nl, slots, hkv, 128)))
+    pos = rng.integers(0, 2 ** 31 - 1, slots).astype(np.int32)
+    sc = rng.random(slots).astype(np.float32)
+    keep = np.sort(rng.choice(n, min(n_keep, n), replace=False))
+    kt, bt = _paged(rng, k, shuffle)
+    vt = torch.zeros_like(kt)
+    vt_l, _ = _paged(np.random.default_rng(0), v, False)
+    # V shares K's block table
+    for p in range(slots // 16):
+        phys = int(bt[p]) if bt is not None else p
+        vt[:, phys] = vt_l[:, p]
+    pos_d, sc_d = torch.from_numpy(pos).to(DEV), torch.from_numpy(sc).to(DEV)
+    keep_d = torch.from_numpy(np.concatenate([keep, [0] * 5]).astype(np.int32)).to(DEV)
+    cnt = torch.tensor([len(keep)], dtype=torch.int64, device=DEV) if dev_count else None
+    max_keep = len(keep) + (5 if dev_count else 0)
+    status = torch.full((1,), 99, dtype=torch.int32, device=DEV)
+    start = kv.kv_compact_tail_inplace(kv.PagedCache(kt, vt, n, bt), keep_d, cnt, max_keep if dev_count else len(keep),
+                                       budget, meta=[pos_d, sc_d], status=status)
+    torch.cuda.synchronize()
+    if budget >= n:
+        assert start == 0
+        src = dst = np.zeros(0, dtype=np.int64)
+    else:
+        s0, e0, src, dst, over = O.tail_compaction_pairs(n, keep, budget, 16)
+        assert start == s0 and not over
+    assert int(status.item()) == 0
+    assert (_logical(kt, bt, slots) == O.tail_compact(k, src, dst)).all()
+    assert (_logical(vt, bt, slots) == O.tail_compact(v, src, dst)).all()
+    assert (pos_d.cpu().numpy() == O.tail_compact(pos[None], src, dst)[0]).all()
+    assert (sc_d.cpu().numpy() == O.tail_compact(sc[None], src, dst)[0]).all()
+
+
+def test_tail_compact_overflow_status():
+    rng = np.random.default_rng(5)
+    n, budget = 640, 100
+    keep = np.sort(rng.choice(n, 130, replace=False))          # more kept than the budget
+    k = O.bf16_round(rng.standard_normal((1, n, 1, 128)))
+    kt, _ = _paged(rng, k, False)
+    vt = kt.clone()
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kv.kv_compact_tail_inplace(kv.PagedCache(kt, vt, n), torch.from_numpy(keep.astype(np.int32)).to(DEV), None,
+                               len(keep), budget, status=status)
+    torch.cuda.synchronize()
+    s0, e0, src, dst, over = O.tail_compaction_pairs(n, keep, budget, 16)
+    assert over and int(status.item()) == kv.KV_STATUS_KEEP_OVERFLOW
+    assert (_logical(kt, None, n) == O.tail_compact(k, src, dst)).all()
