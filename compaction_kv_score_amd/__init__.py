@@ -121,6 +121,10 @@ def lib() -> ctypes.CDLL:
                                                  i32, P(KvMetaDesc), i32, vp]),
             "kv_rope_inv_freq": (i32, [P(KvRope), P(ctypes.c_double)]),
             "kv_lrfu_workspace_size": (i32, [i64, P(sz)]),
+            "kv_gather_evicted": (i32, [P(KvCacheDesc), vp, i64, i64, i64, P(KvCacheDesc), vp, P(KvMetaDesc),
+                                        i32, vp]),
+            "kv_offload_workspace_size": (i32, [P(KvCacheDesc), i64, P(sz)]),
+            "kv_offload_evicted": (i32, [P(KvCacheDesc), vp, i64, i64, vp, vp, vp, vp, sz, vp]),
             "kv_lrfu_update": (i32, [vp, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float, vp, vp, vp, sz,
                                      vp]),
             "kv_compact_tail_inplace": (i32, [P(KvCacheDesc), vp, vp, i64, i64, P(KvMetaDesc), i32, P(i64),
@@ -291,6 +295,40 @@ def kv_lrfu_update(attn_score, keep_score, scale=1.0, top_p=0.9, decay=0.5, hit=
     _check(lib().kv_lrfu_update(_ptr(attn_score), n, float(scale), float(top_p), float(decay),
                                 _ptr(keep_score), _ptr(hit), _ptr(workspace), workspace.numel(),
                                 _stream(attn_score.device)), "kv_lrfu_update")
+    return workspace
+
+
+def kv_gather_evicted(src: PagedCache, keep_tokens, n_keep, first, count, dst: PagedCache,
+                      evicted_tokens=None, meta=None):
+    """Gather evicted rows (see kv_gather_evicted); n_keep is a host count; meta is a list
+    of (src, dst) tensor pairs."""
+    arr, n_meta = _meta_array(meta)
+    _check(lib().kv_gather_evicted(ctypes.byref(src.desc()), _ptr(keep_tokens), int(n_keep), int(first),
+                                   int(count), ctypes.byref(dst.desc()), _ptr(evicted_tokens), arr, n_meta,
+                                   _stream(src.k.device)), "kv_gather_evicted")
+
+
+def _host_ptr(t):
+    if t is None:
+        return None
+    if t.is_cuda or not t.is_pinned() or not t.is_contiguous():
+        raise ValueError("host buffers must be contiguous pinned CPU tensors")
+    return t.data_ptr()
+
+
+def kv_offload_evicted(src: PagedCache, keep_tokens, n_keep, host_k, host_v, host_tokens=None, chunk=1024,
+                       workspace=None):
+    """Offload every evicted row to pinned host tensors (see kv_offload_evicted)."""
+    d = src.desc()
+    if workspace is None:
+        b = ctypes.c_size_t(0)
+        _check(lib().kv_offload_workspace_size(ctypes.byref(d), int(chunk), ctypes.byref(b)),
+               "kv_offload_workspace_size")
+        workspace = torch.empty(b.value, dtype=torch.uint8, device=src.k.device)
+    _check(lib().kv_offload_evicted(ctypes.byref(d), _ptr(keep_tokens), int(n_keep), int(chunk),
+                                    _host_ptr(host_k), _host_ptr(host_v), _host_ptr(host_tokens),
+                                    _ptr(workspace), workspace.numel(), _stream(src.k.device)),
+           "kv_offload_evicted")
     return workspace
 
 

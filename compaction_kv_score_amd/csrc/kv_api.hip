@@ -584,6 +584,104 @@ int32_t kv_compact_segment_inplace_ex(const kv_cache_desc* cache, int64_t prefix
   return KV_OK;
 }
 
+int32_t kv_gather_evicted(const kv_cache_desc* src, const int32_t* keep_tokens, int64_t n_keep,
+                          int64_t first, int64_t count, const kv_cache_desc* dst, int32_t* evicted_tokens,
+                          const kv_meta_desc* meta, int32_t n_meta, hipStream_t stream) {
+  int32_t rc = check_cache(src);
+  if (rc) return rc;
+  if ((rc = check_cache(dst))) return rc;
+  if ((n_keep > 0 && !keep_tokens) || n_keep < 0 || n_keep > src->n_tokens) return KV_EINVAL;
+  if (first < 0 || count < 0 || first + count > src->n_tokens - n_keep || dst->n_tokens < count) return KV_EINVAL;
+  if (dst->n_layers != src->n_layers || dst->n_kv_heads != src->n_kv_heads) return KV_EINVAL;
+  if (src->k == dst->k || src->v == dst->v) return KV_EINVAL;
+  MetaSet ms;
+  if ((rc = check_meta(meta, n_meta, &ms))) return rc;
+  if (count == 0) return KV_OK;
+  if ((rc = check_device())) return rc;
+  EvictArgs a;
+  memset(&a, 0, sizeof(a));
+  a.src_k = (const uint16_t*)src->k;
+  a.src_v = (const uint16_t*)src->v;
+  a.src_layer_stride = src->layer_stride;
+  a.src_page_stride = src->page_stride;
+  a.src_bt = src->block_table;
+  a.src_page_shift = log2_exact(src->page_size);
+  a.dst_k = (uint16_t*)dst->k;
+  a.dst_v = (uint16_t*)dst->v;
+  a.dst_layer_stride = dst->layer_stride;
+  a.dst_page_stride = dst->page_stride;
+  a.dst_bt = dst->block_table;
+  a.dst_page_shift = log2_exact(dst->page_size);
+  a.n_layers = src->n_layers;
+  a.n_kv_heads = src->n_kv_heads;
+  a.keep = keep_tokens;
+  a.n_keep = n_keep;
+  a.first = first;
+  a.count = count;
+  a.evicted_tokens = evicted_tokens;
+  a.meta = ms;
+  const hipError_t e = launch_gather_evicted(a, stream);
+  return e == hipSuccess ? KV_OK : hip_fail(e);
+}
+
+static size_t offload_row_bytes(const kv_cache_desc* src, int64_t chunk) {
+  return align256((size_t)chunk * src->n_layers * src->n_kv_heads * kHeadDim * sizeof(uint16_t));
+}
+
+int32_t kv_offload_workspace_size(const kv_cache_desc* src, int64_t chunk, size_t* bytes) {
+  int32_t rc = check_cache(src);
+  if (rc) return rc;
+  if (!bytes || chunk <= 0) return KV_EINVAL;
+  *bytes = 2 * offload_row_bytes(src, chunk) + align256((size_t)chunk * sizeof(int32_t));
+  return KV_OK;
+}
+
+int32_t kv_offload_evicted(const kv_cache_desc* src, const int32_t* keep_tokens, int64_t n_keep, int64_t chunk,
+                           void* host_k, void* host_v, int32_t* host_tokens, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  size_t need = 0;
+  int32_t rc = kv_offload_workspace_size(src, chunk, &need);
+  if (rc) return rc;
+  if (!host_k || !host_v || n_keep < 0 || n_keep > src->n_tokens || (n_keep > 0 && !keep_tokens)) return KV_EINVAL;
+  if (!ws || ws_bytes < need) return KV_EWORKSPACE;
+  const int64_t n_ev = src->n_tokens - n_keep;
+  if (n_ev == 0) return KV_OK;
+  if ((rc = check_device())) return rc;
+  const int64_t slot = (int64_t)src->n_kv_heads * kHeadDim;
+  char* w = (char*)ws;
+  kv_cache_desc stage;
+  memset(&stage, 0, sizeof(stage));
+  stage.k = w;
+  stage.v = w + offload_row_bytes(src, chunk);
+  stage.n_layers = src->n_layers;
+  stage.n_kv_heads = src->n_kv_heads;
+  stage.head_dim = kHeadDim;
+  stage.page_size = 1;
+  stage.n_tokens = chunk;
+  stage.page_stride = slot;
+  stage.layer_stride = chunk * slot;
+  stage.block_table = nullptr;
+  int32_t* ids = (int32_t*)(w + 2 * offload_row_bytes(src, chunk));
+  const size_t row_bytes = (size_t)slot * sizeof(uint16_t);
+  for (int64_t e0 = 0; e0 < n_ev; e0 += chunk) {
+    const int64_t cnt = n_ev - e0 < chunk ? n_ev - e0 : chunk;
+    if ((rc = kv_gather_evicted(src, keep_tokens, n_keep, e0, cnt, &stage, ids, nullptr, 0, stream))) return rc;
+    hipError_t e;
+    for (int which = 0; which < 2; ++which) {
+      char* host = (char*)(which ? host_v : host_k) + (size_t)e0 * row_bytes;
+      const char* dev = (const char*)(which ? stage.v : stage.k);
+      e = hipMemcpy2DAsync(host, (size_t)n_ev * row_bytes, dev, (size_t)chunk * row_bytes,
+                           (size_t)cnt * row_bytes, (size_t)src->n_layers, hipMemcpyDeviceToHost, stream);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    if (host_tokens) {
+      e = hipMemcpyAsync(host_tokens + e0, ids, (size_t)cnt * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+  }
+  return KV_OK;
+}
+
 int32_t kv_compact_tail_inplace(const kv_cache_desc* cache, const int32_t* keep_tokens,
                                 const int64_t* n_keep, int64_t max_keep, int64_t budget,
                                 const kv_meta_desc* meta, int32_t n_meta, int64_t* start_host,

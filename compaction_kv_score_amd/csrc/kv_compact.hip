@@ -300,7 +300,49 @@ __global__ __launch_bounds__(kCompactThreads) void tail_compact_kernel(TailArgs 
   }
 }
 
+// Rows a compaction drops (PACE Sec. 3.4 offloads them at every compaction): workgroup
+// e - first copies the e-th token not in the keep list, t = e + c with c the kept tokens
+// whose own count of dropped tokens before them (keep[i] - i) does not exceed e.
+__global__ __launch_bounds__(kCompactThreads) void gather_evicted_kernel(EvictArgs a) {
+  const int tid = threadIdx.x;
+  const int64_t e = a.first + blockIdx.x;
+  const int32_t* keep = a.keep;
+  const int64_t c = block_count_true(a.n_keep, [&](int64_t i) { return keep[i] - i <= e; });
+  const int64_t t = e + c;
+  const int64_t r = blockIdx.x;
+  const int slot_stride = a.n_kv_heads * kHeadDim;
+  const int64_t so = token_offset(t, a.src_page_shift, a.src_page_stride, a.src_bt, slot_stride);
+  const int64_t dof = token_offset(r, a.dst_page_shift, a.dst_page_stride, a.dst_bt, slot_stride);
+  const int per_layer = slot_stride / 8;
+  const int items = a.n_layers * per_layer;
+  for (int it = tid; it < items; it += kCompactThreads) {
+    const int layer = it / per_layer;
+    const int64_t col = (int64_t)(it - layer * per_layer) * 8;
+    const int64_t s0 = (int64_t)layer * a.src_layer_stride + so + col;
+    const int64_t d0 = (int64_t)layer * a.dst_layer_stride + dof + col;
+    *(uint4*)(a.dst_k + d0) = *(const uint4*)(a.src_k + s0);
+    *(uint4*)(a.dst_v + d0) = *(const uint4*)(a.src_v + s0);
+  }
+  if (tid == 0) {
+    if (a.evicted_tokens) a.evicted_tokens[r] = (int32_t)t;
+    for (int m = 0; m < a.meta.n; ++m) {
+      switch (a.meta.elem_bytes[m]) {
+        case 1: ((uint8_t*)a.meta.dst[m])[r] = ((const uint8_t*)a.meta.src[m])[t]; break;
+        case 2: ((uint16_t*)a.meta.dst[m])[r] = ((const uint16_t*)a.meta.src[m])[t]; break;
+        case 4: ((uint32_t*)a.meta.dst[m])[r] = ((const uint32_t*)a.meta.src[m])[t]; break;
+        default: ((uint64_t*)a.meta.dst[m])[r] = ((const uint64_t*)a.meta.src[m])[t]; break;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gather_evicted(const EvictArgs& a, hipStream_t s) {
+  if (a.count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_evicted_kernel, dim3((unsigned)a.count), dim3(kCompactThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_tail_compact(const TailArgs& a, int64_t grid, hipStream_t s) {
   hipLaunchKernelGGL(tail_compact_kernel, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(kCompactThreads), 0, s, a);

@@ -205,6 +205,26 @@ struct TailArgs {
   MetaSet meta;                  // arrays moved in place (src == dst)
 };
 hipError_t launch_tail_compact(const TailArgs& a, int64_t grid, hipStream_t s);
+
+struct EvictArgs {
+  const uint16_t* src_k;
+  const uint16_t* src_v;
+  int64_t src_layer_stride, src_page_stride;
+  const int32_t* src_bt;
+  int src_page_shift;
+  uint16_t* dst_k;
+  uint16_t* dst_v;
+  int64_t dst_layer_stride, dst_page_stride;
+  const int32_t* dst_bt;
+  int dst_page_shift;
+  int n_layers, n_kv_heads;
+  const int32_t* keep;           // ascending kept tokens
+  int64_t n_keep;
+  int64_t first, count;          // evicted ranks [first, first + count)
+  int32_t* evicted_tokens;       // [count] (nullable)
+  MetaSet meta;                  // dst[e - first] = src[token]
+};
+hipError_t launch_gather_evicted(const EvictArgs& a, hipStream_t s);
 hipError_t launch_gather_meta(const CompactArgs& a, hipStream_t s);
 
 }  // namespace kvs

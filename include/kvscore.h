@@ -244,6 +244,37 @@ int32_t kv_compact_tail_inplace(const kv_cache_desc *cache, const int32_t *keep_
                                 hipStream_t stream);
 
 /*
+ * Rows a compaction drops, gathered for offload (PACE Sec. 3.4: at every compaction the
+ * evicted rows go to pinned host memory).  The evicted tokens are the complement of
+ * keep_tokens[0:n_keep) (ascending, n_keep a host count) in [0, src.n_tokens), in
+ * ascending order; ranks [first, first + count) of them are copied, K and V of every
+ * layer and head, to slots 0..count-1 of dst (a device row of the same layer and head
+ * shape, dst.n_tokens >= count, not overlapping src).  evicted_tokens[r] (device,
+ * nullable) receives the token index of slot r, and every meta array is gathered the
+ * same way (dst[r] = src[token]).  KV_EINVAL when first + count exceeds N - n_keep.
+ */
+int32_t kv_gather_evicted(const kv_cache_desc *src, const int32_t *keep_tokens, int64_t n_keep,
+                          int64_t first, int64_t count, const kv_cache_desc *dst,
+                          int32_t *evicted_tokens, const kv_meta_desc *meta /* host array */,
+                          int32_t n_meta, hipStream_t stream);
+
+/* Host-only.  Device staging bytes kv_offload_evicted needs for chunks of `chunk` tokens. */
+int32_t kv_offload_workspace_size(const kv_cache_desc *src, int64_t chunk, size_t *bytes /* host */);
+
+/*
+ * Offload every evicted row to host memory: chunks of `chunk` tokens (Penelope swaps
+ * through a 1,024-token buffer) are gathered into the device staging workspace with
+ * kv_gather_evicted and copied with asynchronous device-to-host copies on `stream`.
+ * host_k and host_v (pinned host memory, bf16) receive layout [L][N - n_keep][Hkv][128];
+ * host_tokens (pinned host, nullable) the token indices.  Returns after enqueueing; the
+ * host buffers are complete once the stream reaches that point.  Chunks run in stream
+ * order; the caller overlaps them with work on other streams.
+ */
+int32_t kv_offload_evicted(const kv_cache_desc *src, const int32_t *keep_tokens, int64_t n_keep,
+                           int64_t chunk, void *host_k, void *host_v, int32_t *host_tokens,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Segment eviction from the front of the private history ("Rethinking KV Cache
  * Eviction for Agentic LLM Serving", Part one): keep [0, P) and [P + E', N) where
  * E' = min(ceil(E / block) * block, N - P) frees only whole blocks.  Writes the keep

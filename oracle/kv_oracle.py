@@ -642,6 +642,14 @@ def compact_rerope_store(k, v, keep, old_pos, renumber_base, inv_freq, ref_k, re
     return out_k, vv, new_pos, out_ref, out_ref_pos, used
 
 
+def evicted_tokens(n_tokens, keep):
+    """Tokens a compaction drops: the complement of the keep list in [0, N), ascending
+    (PACE Sec. 3.4 offloads them to host memory at every compaction)."""
+    mask = np.ones(n_tokens, dtype=bool)
+    mask[np.asarray(keep, dtype=np.int64)] = False
+    return np.nonzero(mask)[0]
+
+
 def gather_meta(arr, keep):
     """Per-token metadata follows its token through compaction."""
     return np.asarray(arr)[np.asarray(keep, dtype=np.int64)]

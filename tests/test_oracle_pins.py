@@ -781,6 +781,19 @@ def test_reference_store_first_use_and_foreign_entry():
     assert (k3[:, 6] == want).all()
 
 
+def test_evicted_tokens_partition():
+    assert O.evicted_tokens(10, [0, 3, 4, 9]).tolist() == [1, 2, 5, 6, 7, 8]
+    rng = np.random.default_rng(21)
+    for n in (1, 17, 1000):
+        keep = np.sort(rng.choice(n, int(rng.integers(0, n + 1)), replace=False))
+        ev = O.evicted_tokens(n, keep)
+        assert len(ev) + len(keep) == n and not set(ev.tolist()) & set(keep.tolist())
+        assert (np.diff(ev) > 0).all()
+        # the e-th evicted token is e plus the kept tokens before it
+        for e in range(0, len(ev), max(1, len(ev) // 7)):
+            assert ev[e] == e + int((keep < ev[e]).sum())
+
+
 def test_renumbered_rotary_distance_bounded():
     gd = read_golden("pace_numbers.txt")
     keep = np.sort(np.random.default_rng(16).choice(100_000, gd["budget"], replace=False))
