@@ -181,6 +181,224 @@ def clock_summary(pmc_dir):
     return "\n".join(rows)
 
 
+def extras(steps=5, warmup=2):
+    """Timings of the rows beyond the headline step, each on one GPU with inputs resident
+    in HBM, HIP events on the launch stream, mean over `steps` runs after `warmup`:
+      f1: single-pass scoring with a supplied LSE (sum and group maximum), Qwen3-8B 100K;
+      f2: compaction + re-rotation of 2,048 kept tokens through the reference store;
+      f3: LRFU keep-score update over 100K entries, in-place tail compaction of 2,048;
+      f4: gather of 16,384 evicted rows on the device, and offload of 16,384 rows to
+          pinned host memory (PCIe-bound, chunks of 1,024);
+      cfg4: Mistral-7B 131,072-token in-place segment eviction + re-rotation;
+      cfg5: the full step (MemDecay page scoring, select, compaction) at 1,000,000 tokens.
+    Prints one JSON line."""
+    import numpy as np
+    import compaction_kv_score_amd as kv
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    hip = HipEvents()
+    out = {}
+
+    def timed(fn, n=steps, w=warmup):
+        for _ in range(w):
+            fn()
+        evs = [hip.create(2) for _ in range(n)]
+        for e in evs:
+            hip.record(e[0], sh)
+            fn()
+            hip.record(e[1], sh)
+        torch.cuda.synchronize()
+        return sum(hip.ms(e[0], e[1]) for e in evs) / n
+
+    def log(msg):
+        print(f"[extras] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- Qwen3-8B 100K
+    w = synth.workload(3)
+    N, NL, HKV, D, W, B = w.n_tokens, w.n_layers, w.n_kv_heads, w.head_dim, w.window, w.budget_tokens
+    kvb = w.kv_bytes_per_token
+    log("qwen3-8b-n100k inputs")
+    k, v, _ = synth.kv_cache(w, seed=0, device=dev)
+    q = synth.window_queries(w, seed=0, device=dev)
+    src = kv.PagedCache(k, v, N)
+    acc = torch.zeros(N, device=dev)
+    item_score = torch.zeros(N, device=dev)
+    item_pinned = torch.zeros(N, dtype=torch.uint8, device=dev)
+    mass = torch.zeros(N, device=dev)
+    lse = torch.zeros((NL, w.n_q_heads, W), device=dev)
+    kw = dict(policy="h2o", window=W, item_tokens=1, accum=acc, item_score=item_score,
+              item_pinned=item_pinned, mass=mass)
+    ws = torch.empty(kv.kv_score_workspace_size(src, q, **kw), dtype=torch.uint8, device=dev)
+    kv.kv_score(src, q, workspace=ws, lse=lse, **kw)
+    k_bytes = NL * N * HKV * D * 2
+    for agg in ("sum", "max_group"):
+        ev = hip.create(5)
+        evp = ctypes.cast(ev, ctypes.c_void_p)
+        runs = []
+        for i in range(warmup + steps):
+            kv.kv_score(src, q, workspace=ws, lse_in=lse, aggregate=agg, stage_events=evp, **kw)
+            torch.cuda.synchronize()
+            if i >= warmup:
+                runs.append((hip.ms(ev[0], ev[4]), hip.ms(ev[2], ev[3])))
+        tot = sum(r[0] for r in runs) / len(runs)
+        mp = sum(r[1] for r in runs) / len(runs)
+        out[f"f1_single_pass_{agg}"] = {"score_ms": round(tot, 4), "mass_pass_ms": round(mp, 4),
+                                        "mass_pass_GBps": round(k_bytes / (mp * 1e-3) / 1e9, 1)}
+        log(f"f1 {agg}: {out[f'f1_single_pass_{agg}']}")
+    del ws
+
+    g = torch.Generator().manual_seed(5)
+    keep = torch.sort(torch.randperm(N, generator=g)[:B])[0].to(torch.int32).to(dev)
+    old_pos = (torch.arange(N, dtype=torch.int32) + 10_000).to(dev)
+    dk = torch.zeros((NL, B // 16, 16, HKV, D), dtype=torch.bfloat16, device=dev)
+    dv = torch.zeros_like(dk)
+    dst = kv.PagedCache(dk, dv, B)
+    # every kept token holds a valid entry (the stored key equals the cached key at its position)
+    ref_src = kv.RefStore(k.reshape(NL, -1, HKV, D)[:, :N].contiguous(), old_pos.clone())
+    ref_dst = kv.RefStore.empty(NL, B, HKV, dev)
+    newp = torch.zeros(B, dtype=torch.int32, device=dev)
+    rope = kv.kv_rope("default", base=w.rope_theta)
+    t_plain = timed(lambda: kv.kv_compact_rerope(src, dst, keep, None, B, old_pos, newp, renumber_base=0,
+                                                 rope_theta=w.rope_theta))
+    t_store = timed(lambda: kv.kv_compact_rerope(src, dst, keep, None, B, old_pos, newp, renumber_base=0,
+                                                 rope=rope, ref_src=ref_src, ref_dst=ref_dst))
+    assert int((ref_dst.pos != kv.KV_REF_NONE).sum()) == B
+    kb = kvb // 2
+    out["f2_store_compaction"] = {
+        "ms": round(t_store, 4), "plain_ms": round(t_plain, 4), "kept": B,
+        "bytes": 6 * B * kb, "GBps": round(6 * B * kb / (t_store * 1e-3) / 1e9, 1),
+        "note": "reads cached K, stored K, V; writes K, V, stored K (72 KiB each per token)"}
+    log(f"f2: {out['f2_store_compaction']}")
+    del ref_src, ref_dst
+
+    scores = torch.rand(N, generator=g).pow(8).to(dev)
+    ks = torch.zeros(N, device=dev)
+    ws_l = torch.empty(kv.kv_lrfu_workspace_size(N), dtype=torch.uint8, device=dev)
+    t_lrfu = timed(lambda: kv.kv_lrfu_update(scores, ks, top_p=0.9, decay=0.5, workspace=ws_l))
+    out["f3_lrfu_update"] = {"ms": round(t_lrfu, 4), "entries": N}
+    keeps = [torch.sort(torch.randperm(N, generator=g)[:B])[0].to(torch.int32).to(dev)
+             for _ in range(warmup + steps)]
+    it = iter(keeps)
+    moved = [int(((kk < (16 * -(-N // 16) - 16 * -(-B // 16))) | (kk >= 16 * -(-N // 16) - 16 * -(-B // 16) + B))
+                 .sum()) for kk in keeps]
+    t_tail = timed(lambda: kv.kv_compact_tail_inplace(src, next(it), None, B, B))
+    mv = sum(moved[warmup:]) / steps
+    out["f3_tail_compaction"] = {"ms": round(t_tail, 4), "moved_tokens": round(mv, 1),
+                                 "GBps": round(2 * mv * kvb / (t_tail * 1e-3) / 1e9, 1)}
+    log(f"f3: {out['f3_lrfu_update']} {out['f3_tail_compaction']}")
+
+    n_ev = 16384
+    stage_k = torch.zeros((NL, n_ev // 16, 16, HKV, D), dtype=torch.bfloat16, device=dev)
+    stage_v = torch.zeros_like(stage_k)
+    t_gather = timed(lambda: kv.kv_gather_evicted(src, keep, B, 0, n_ev, kv.PagedCache(stage_k, stage_v, n_ev)))
+    keep_off = torch.sort(torch.randperm(N, generator=g)[:N - n_ev])[0].to(torch.int32).to(dev)
+    hk = torch.empty((NL, n_ev, HKV, D), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk).pin_memory()
+    ws_o = None
+
+    def off():
+        nonlocal ws_o
+        ws_o = kv.kv_offload_evicted(src, keep_off, N - n_ev, hk, hv, chunk=1024, workspace=ws_o)
+
+    t_off = timed(off, n=3, w=1)
+    out["f4_gather_evicted"] = {"ms": round(t_gather, 4), "tokens": n_ev,
+                                "GBps": round(2 * n_ev * kvb / (t_gather * 1e-3) / 1e9, 1)}
+    out["f4_offload_to_host"] = {"ms": round(t_off, 3), "tokens": n_ev, "bytes": n_ev * kvb,
+                                 "GBps": round(n_ev * kvb / (t_off * 1e-3) / 1e9, 2),
+                                 "note": "device gather then device-to-host copies into pinned memory"}
+    log(f"f4: {out['f4_gather_evicted']} {out['f4_offload_to_host']}")
+    del k, v, src, dk, dv, stage_k, stage_v, hk, hv, ws_o
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- Mistral-7B segment
+    w4 = synth.workload(4)
+    log("mistral-7b-n131072 inputs")
+    k4, v4, _ = synth.kv_cache(w4, seed=0, device=dev)
+    c4 = kv.PagedCache(k4, v4, w4.n_tokens)
+    n_keep4, e4 = kv.kv_select_segment(w4.n_tokens, w4.segment_prefix, int(w4.segment_frac * w4.n_tokens), 16)
+    pos4 = torch.arange(w4.n_tokens, dtype=torch.int32, device=dev)
+    t4 = timed(lambda: kv.kv_compact_segment_inplace(c4, w4.segment_prefix, e4, pos4, renumber_base=0,
+                                                     rope_theta=w4.rope_theta), n=3, w=1)
+    moved4 = n_keep4 - w4.segment_prefix
+    b4 = 2 * moved4 * w4.kv_bytes_per_token
+    out["cfg4_segment_inplace"] = {"workload": w4.name, "ms": round(t4, 3), "evicted": e4, "moved_tokens": moved4,
+                                   "bytes": b4, "GBps": round(b4 / (t4 * 1e-3) / 1e9, 1),
+                                   "hbm_frac": round(b4 / (t4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"cfg4: {out['cfg4_segment_inplace']}")
+    del k4, v4, c4
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- Qwen3-8B 1M tokens
+    w5 = synth.workload(5)
+    N5, B5 = w5.n_tokens, w5.budget_tokens
+    log("qwen3-8b-n1m inputs (147 GB)")
+    k5, v5, _ = synth.kv_cache(w5, seed=0, device=dev,
+                               progress=lambda l: torch.cuda.synchronize() or log(f"layer {l} generated"))
+    q5 = synth.window_queries(w5, seed=0, device=dev)
+    c5 = kv.PagedCache(k5, v5, N5)
+    ewma, clock = synth.memdecay_state(w5, seed=0)
+    b_r, lam = synth.region_params(0)
+    region = synth.regions(w5, seed=0)
+    sid, nxt = synth.spans(w5, seed=0)
+    n_items = -(-N5 // 16)
+    st5 = dict(region=region.to(dev), base_prio=b_r.to(dev), decay_rate=lam.to(dev), ewma=ewma.to(dev),
+               clock=clock.to(dev), span_id=sid.to(dev), span_next_use=nxt.to(dev), bonus_floor=50000.0,
+               n_sink=w5.n_sink, n_recent=w5.n_recent, pinned_regions=1,
+               item_score=torch.zeros(n_items, device=dev),
+               item_pinned=torch.zeros(n_items, dtype=torch.uint8, device=dev))
+    kw5 = dict(policy="memdecay", window=w5.window, item_tokens=16, rho=w5.rho, alpha=w5.alpha, tau=w5.tau,
+               dt_steps=1, **st5)
+    ws5 = torch.empty(kv.kv_score_workspace_size(c5, q5, **kw5), dtype=torch.uint8, device=dev)
+    keep5 = torch.zeros(N5, dtype=torch.int32, device=dev)
+    nk5 = torch.zeros(1, dtype=torch.int64, device=dev)
+    status5 = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws_s5 = torch.empty(kv.kv_select_workspace_size(n_items), dtype=torch.uint8, device=dev)
+    cap5 = 2 * B5 + 4096
+    dk5 = torch.zeros((w5.n_layers, cap5 // 16, 16, w5.n_kv_heads, w5.head_dim), dtype=torch.bfloat16, device=dev)
+    dv5 = torch.zeros_like(dk5)
+    old5 = torch.arange(N5, dtype=torch.int32, device=dev)
+    new5 = torch.zeros(cap5, dtype=torch.int32, device=dev)
+    ev5 = hip.create(5)
+    ev5p = ctypes.cast(ev5, ctypes.c_void_p)
+    stage = {"score": 0.0, "lse_pass": 0.0, "mass_pass": 0.0, "select": 0.0, "compact": 0.0}
+    tsteps = []
+    for i in range(1 + 3):
+        e_sel, e_cmp = hip.create(2), hip.create(2)
+        t0 = time.perf_counter()
+        kv.kv_score(c5, q5, workspace=ws5, stage_events=ev5p, **kw5)
+        hip.record(e_sel[0], sh)
+        kv.kv_select(st5["item_score"], st5["item_pinned"], 16, N5, B5 // 16, keep5, nk5, status5, workspace=ws_s5)
+        hip.record(e_sel[1], sh)
+        hip.record(e_cmp[0], sh)
+        kv.kv_compact_rerope(c5, kv.PagedCache(dk5, dv5, cap5), keep5, nk5, cap5, old5, new5, renumber_base=0,
+                             rope_theta=w5.rope_theta, limit=w5.limit)
+        hip.record(e_cmp[1], sh)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if i >= 1:
+            tsteps.append((t1 - t0) * 1e3)
+            stage["score"] += hip.ms(ev5[0], ev5[4]) / 3
+            stage["lse_pass"] += hip.ms(ev5[0], ev5[1]) / 3
+            stage["mass_pass"] += hip.ms(ev5[2], ev5[3]) / 3
+            stage["select"] += hip.ms(e_sel[0], e_sel[1]) / 3
+            stage["compact"] += hip.ms(e_cmp[0], e_cmp[1]) / 3
+    ms5 = sum(tsteps) / len(tsteps)
+    kb5 = w5.n_layers * N5 * w5.n_kv_heads * w5.head_dim * 2
+    out["cfg5_full_step"] = {"workload": w5.name, "ms_per_step": round(ms5, 3),
+                             "KV_tokens_per_s": round(N5 / (ms5 * 1e-3), 1), "n_keep": int(nk5.item()),
+                             "status": int(status5.item()),
+                             "stages_ms": {a: round(b, 3) for a, b in stage.items()},
+                             "scoring_pass_GBps": {
+                                 "lse_pass": round(kb5 / (stage["lse_pass"] * 1e-3) / 1e9, 1),
+                                 "mass_pass": round(kb5 / (stage["mass_pass"] * 1e-3) / 1e9, 1)}}
+    log(f"cfg5: {out['cfg5_full_step']}")
+    print(json.dumps({"extras": out, "n_gpus": 1, "data": "synthetic"}), flush=True)
+
+
 def cpu_baseline(w, layers):
     """The CPU oracle, untuned, on a bounded sample of the workload: attention mass and
     epilogue for `layers` of the 36 layers at full N, selection at full N, compaction of
@@ -235,6 +453,10 @@ def main():
     ap.add_argument("--clock-summary", metavar="PMC_DIR",
                     help="print effective clock and MFMA busy share per kernel from a "
                          "rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES run and exit")
+    ap.add_argument("--extras", action="store_true",
+                    help="time the rows beyond the headline step (single-pass and group-maximum "
+                         "scoring, reference store, LRFU, tail compaction, offload, the Mistral "
+                         "segment case and the 1M-token step) and print one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) three "
                          "times, to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -245,6 +467,9 @@ def main():
         return
     if args.clock_summary:
         print(clock_summary(args.clock_summary))
+        return
+    if args.extras:
+        extras()
         return
     if args.copy_calibration:
         a = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")

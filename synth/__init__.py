@@ -107,7 +107,7 @@ def _randn_bf16(shape, gen, device):
     return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
 
 
-def kv_cache(w: Workload, seed=0, device="cpu", paged_shuffle=False, extra_pages=0):
+def kv_cache(w: Workload, seed=0, device="cpu", paged_shuffle=False, extra_pages=0, progress=None):
     """Paged K and V, [layers][physical pages][page][kv heads][head_dim] bf16 ~ N(0,1).
 
     With ``paged_shuffle`` the logical pages map to a random permutation of
@@ -123,6 +123,8 @@ def kv_cache(w: Workload, seed=0, device="cpu", paged_shuffle=False, extra_pages
     for layer in range(w.n_layers):
         k[layer] = _randn_bf16(shape[1:], gk, device)
         v[layer] = _randn_bf16(shape[1:], gv, device)
+        if progress is not None:
+            progress(layer)
     bt = None
     if paged_shuffle:
         gb = _gen(seed, _S_BT, "cpu")
