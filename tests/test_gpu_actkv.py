@@ -11,6 +11,7 @@ import torch
 
 import compaction_kv_score_amd as kv
 import oracle as O
+from layout import unpage
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -81,8 +82,14 @@ def test_lrfu_steps_then_select():
     nk = torch.zeros(1, dtype=torch.int64, device=DEV)
     kv.kv_select(ks, None, 1, n, budget, keep, nk)
     torch.cuda.synchronize()
-    want, _ = O.select_items(ks.cpu().numpy(), None, budget)  # same float32 keys on both sides
-    assert int(nk) == budget and (keep.cpu().numpy() == want).all()
+    # the oracle selects on its own keep scores; the sets may differ only in entries whose
+    # oracle score lies within 1e-5 relative of the oracle's selection threshold
+    want, _ = O.select_items(ks_ref.astype(np.float32), None, budget)
+    got = keep.cpu().numpy()
+    assert int(nk) == budget
+    thr = np.sort(ks_ref)[::-1][budget - 1]
+    diff = np.setxor1d(got, want)
+    assert (np.abs(ks_ref[diff] - thr) <= 1e-5 * abs(thr)).all(), diff
 
 
 def _paged(rng, logical, shuffle):
@@ -98,7 +105,7 @@ def _paged(rng, logical, shuffle):
 
 
 def _logical(t, bt, slots):
-    return O.gather_logical(t.float().cpu().double().numpy(), None if bt is None else bt.cpu().numpy(), 16, slots)
+    return unpage(t.float().cpu().double().numpy(), None if bt is None else bt.cpu().numpy(), 16, slots)
 
 
 @pytest.mark.parametrize("n,budget,n_keep,shuffle,dev_count", [

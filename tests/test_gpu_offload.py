@@ -7,6 +7,7 @@ import torch
 
 import compaction_kv_score_amd as kv
 import oracle as O
+from layout import unpage
 import synth
 
 pytestmark = pytest.mark.gpu
@@ -14,7 +15,7 @@ DEV = "cuda:0"
 
 
 def _logical(t, bt, n):
-    return O.gather_logical(t.float().cpu().double().numpy(), None if bt is None else bt.cpu().numpy(), 16, n)
+    return unpage(t.float().cpu().double().numpy(), None if bt is None else bt.cpu().numpy(), 16, n)
 
 
 @pytest.mark.parametrize("nl,hkv,n,n_keep,first,count,shuffle", [

@@ -18,6 +18,7 @@ import torch
 
 import compaction_kv_score_amd as kv
 import oracle as O
+from layout import unpage
 import synth
 
 pytestmark = pytest.mark.gpu
@@ -56,7 +57,7 @@ def assert_bf16_within_1ulp(got, ref, what=""):
 # ------------------------------------------------------------------------------ compaction
 
 def _paged_to_logical(t, bt, pg, n):
-    return O.gather_logical(np64(t), None if bt is None else bt.cpu().numpy(), pg, n)
+    return unpage(np64(t), None if bt is None else bt.cpu().numpy(), pg, n)
 
 
 @pytest.mark.parametrize("nl,hkv,n,n_keep,shuffle,base,theta", [
@@ -528,3 +529,108 @@ def test_full_size_qwen3_100k_compaction_sampled(qwen3_100k):
     assert (gv == vs).all()
     assert_bf16_within_1ulp(gk, rk, "K at N=100K")
     assert (newp.cpu().numpy() == np.arange(w.budget_tokens)).all()
+
+
+def test_full_size_mistral_131k_segment_sampled():
+    """Mistral-7B shape at full size (131,072 tokens, 16,384-token prefix, 30% evicted):
+    in-place segment eviction + re-rotation as bench.py --extras runs it, checked on
+    sampled ranks against the oracle's rotation of the original rows."""
+    w = synth.workload(4)
+    k, v, _ = synth.kv_cache(w, seed=0, device=DEV)
+    n_keep, e = kv.kv_select_segment(w.n_tokens, w.segment_prefix, int(w.segment_frac * w.n_tokens), 16)
+    assert (n_keep, e) == (w.n_tokens - 39_328, 39_328)
+    g = torch.Generator().manual_seed(3)
+    ranks = sorted(set([0, w.segment_prefix - 1, w.segment_prefix, w.segment_prefix + e - 1, n_keep - 1]
+                       + torch.randint(0, n_keep, (40,), generator=g).tolist()))
+    src = [r if r < w.segment_prefix else r + e for r in ranks]
+    kf, vf = k.reshape(w.n_layers, -1, 8, 128), v.reshape(w.n_layers, -1, 8, 128)
+    ks, vs = np64(kf[:, src]), np64(vf[:, src])
+    pos = torch.arange(w.n_tokens, dtype=torch.int32, device=DEV)
+    kv.kv_compact_segment_inplace(kv.PagedCache(k, v, w.n_tokens), w.segment_prefix, e, pos, renumber_base=0,
+                                  rope_theta=w.rope_theta)
+    torch.cuda.synchronize()
+    delta = np.array(ranks) - np.array(src)
+    rk = O.bf16_round(O.rope_rotate(ks, delta[None, :, None], w.rope_theta))
+    rk[:, delta == 0] = ks[:, delta == 0]
+    gk, gv = np64(kf[:, ranks]), np64(vf[:, ranks])
+    assert (gv == vs).all()
+    assert (gk[:, delta == 0] == ks[:, delta == 0]).all()
+    assert_bf16_within_1ulp(gk, rk, "K at N=131K")
+    assert (pos[:n_keep].cpu().numpy() == np.arange(n_keep)).all()
+    del k, v
+    torch.cuda.empty_cache()
+
+
+def test_full_size_qwen3_1m_step_properties():
+    """Qwen3-8B shape at 1,000,000 tokens (147 GB), the step bench.py --extras times:
+    MemDecay page scoring, page selection, compaction.  The oracle cannot score 1M keys
+    for every row, so: softmax rows sum to one, sampled LSE rows over all keys, the
+    selection against the oracle on the same page scores, and sampled compacted keys."""
+    w = synth.workload(5)
+    N = w.n_tokens
+    k, v, _ = synth.kv_cache(w, seed=0, device=DEV)
+    q = synth.window_queries(w, seed=0, device=DEV)
+    ewma, clock = synth.memdecay_state(w, seed=0)
+    b_r, lam = synth.region_params(0)
+    sid, nxt = synth.spans(w, seed=0)
+    n_items = -(-N // 16)
+    item_score = torch.zeros(n_items, device=DEV)
+    item_pinned = torch.zeros(n_items, dtype=torch.uint8, device=DEV)
+    mass = torch.zeros(N, device=DEV)
+    lse = torch.zeros((w.n_layers, w.n_q_heads, w.window), device=DEV)
+    src = kv.PagedCache(k, v, N)
+    kv.kv_score(src, q, policy="memdecay", window=w.window, item_tokens=16, rho=w.rho, alpha=w.alpha,
+                tau=w.tau, dt_steps=1, region=synth.regions(w, seed=0).to(DEV), base_prio=b_r.to(DEV),
+                decay_rate=lam.to(DEV), ewma=ewma.to(DEV), clock=clock.to(DEV), span_id=sid.to(DEV),
+                span_next_use=nxt.to(DEV), bonus_floor=50000.0, n_sink=w.n_sink, n_recent=w.n_recent,
+                pinned_regions=1, mass=mass, lse=lse, item_score=item_score, item_pinned=item_pinned)
+    B = w.budget_tokens
+    keep = torch.zeros(B, dtype=torch.int32, device=DEV)
+    nk = torch.zeros(1, dtype=torch.int64, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kv.kv_select(item_score, item_pinned, 16, N, B // 16, keep, nk, status)
+    dk = torch.zeros((w.n_layers, B // 16, 16, 8, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    pos = torch.arange(N, dtype=torch.int32, device=DEV)
+    newp = torch.zeros(B, dtype=torch.int32, device=DEV)
+    kv.kv_compact_rerope(src, kv.PagedCache(dk, dv, B), keep, nk, B, pos, newp, renumber_base=0,
+                         rope_theta=w.rope_theta, limit=w.limit)
+    torch.cuda.synchronize()
+    m = np64(mass)
+    assert abs(m.sum() / (w.n_layers * w.n_q_heads * w.window) - 1) < 1e-5 and (m > 0).all()
+    g = torch.Generator().manual_seed(5)
+    for _ in range(3):
+        layer = int(torch.randint(0, w.n_layers, (1,), generator=g))
+        h = int(torch.randint(0, w.n_q_heads, (1,), generator=g))
+        wi = int(torch.randint(0, w.window, (1,), generator=g))
+        qpos = N - w.window + wi
+        kk = np64(k[layer, :, :, h // 4, :].reshape(-1, 128)[: qpos + 1])
+        s = (kk @ np64(q[layer, wi, h])) / math.sqrt(128)
+        mx = s.max()
+        assert abs(float(lse[layer, h, wi]) - (mx + math.log(np.exp(s - mx).sum()))) < 1e-5
+    assert int(status.item()) == 0 and int(nk.item()) == B
+    # pinned pages from the inputs (oracle definition), then the selection's order property
+    # on the device's own page scores: every kept unpinned page ranks above every dropped one
+    tok_pin = O.pinned_tokens(N, region=synth.regions(w, seed=0).numpy(), pinned_regions=1,
+                              n_sink=w.n_sink, n_recent=w.n_recent)
+    pin = O.page_any(tok_pin, 16)
+    assert (item_pinned.cpu().numpy().astype(bool) == pin).all()
+    kept_pages = np.unique(keep.cpu().numpy() // 16)
+    assert len(kept_pages) == B // 16 and pin[kept_pages].sum() == pin.sum()
+    sc = item_score.cpu().numpy()
+    kept = np.zeros(n_items, bool)
+    kept[kept_pages] = True
+    free_kept, dropped = sc[kept & ~pin], sc[~kept & ~pin]
+    assert free_kept.min() >= dropped.max()
+    assert (keep.cpu().numpy() == (kept_pages[:, None] * 16 + np.arange(16)).reshape(-1)).all()
+    ranks = sorted(set([0, B - 1] + torch.randint(0, B, (24,), generator=g).tolist()))
+    srcs = keep.cpu().long()[ranks]
+    kf = k.reshape(w.n_layers, -1, 8, 128)
+    ks = np64(kf[:, srcs.to(DEV)])
+    rk = O.bf16_round(O.rope_rotate(ks, (np.array(ranks) - srcs.numpy())[None, :, None], w.rope_theta))
+    gk = np64(dk.reshape(w.n_layers, -1, 8, 128)[:, ranks])
+    moved = np.array(ranks) != srcs.numpy()
+    assert (gk[:, ~moved] == ks[:, ~moved]).all()
+    assert_bf16_within_1ulp(gk[:, moved], rk[:, moved], "K at N=1M")
+    del k, v, dk, dv
+    torch.cuda.empty_cache()

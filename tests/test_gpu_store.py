@@ -11,6 +11,7 @@ import torch
 
 import compaction_kv_score_amd as kv
 import oracle as O
+from layout import unpage
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -42,7 +43,7 @@ def to_paged(logical, rng, shuffle=True, extra_pages=2):
 
 
 def from_paged(t, bt, n):
-    return O.gather_logical(t.float().cpu().double().numpy(), None if bt is None else bt.cpu().numpy(), PG, n)
+    return unpage(t.float().cpu().double().numpy(), None if bt is None else bt.cpu().numpy(), PG, n)
 
 
 def store_to_dev(ref_k, ref_pos):
