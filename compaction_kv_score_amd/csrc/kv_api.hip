@@ -319,7 +319,7 @@ int32_t kv_select(const float* item_score, const uint8_t* item_pinned, int64_t n
   char* w = (char*)ws;
   a.st = (SelectState*)w;
   a.hist = (uint32_t*)(w + 256);
-  a.counts = (int64_t*)(w + 256 + (size_t)a.n_blocks * kSelBins * sizeof(uint32_t));
+  a.counts = (int64_t*)(w + 256 + (size_t)3 * kSelBins * sizeof(uint32_t));
   const hipError_t e = launch_select(a, stream);
   return e == hipSuccess ? KV_OK : hip_fail(e);
 }

@@ -111,7 +111,7 @@ struct SelectArgs {
   int64_t* n_keep;
   uint32_t* status;
   SelectState* st;
-  uint32_t* hist;                // [n_blocks][kSelBins]
+  uint32_t* hist;                // [3 passes][kSelBins], cleared by the init kernel
   int64_t* counts;               // [n_blocks][2]
   int n_blocks;
   int64_t per_block;             // items per block

@@ -9,9 +9,11 @@
 //
 // Steps, all on the device (no host synchronisation; n_keep stays in device memory):
 //   1. three histogram passes over 11-, 11- and 10-bit digits of an order-preserving
-//      uint32 key, most significant first.  Each block builds a private LDS histogram of the candidates
-//      that still match the digits fixed so far; the last block to finish (atomic
-//      ticket) sums the block histograms in block order and fixes the next digit.
+//      uint32 key, most significant first.  Each block builds a private LDS histogram of
+//      the candidates that still match the digits fixed so far and adds it into the
+//      pass's global histogram with integer atomics (exact, so the order of the blocks
+//      does not matter); the last block to finish (atomic ticket) reads the 2,048 bins
+//      and fixes the next digit.
 //      Afterwards T is the key of the K-th best unpinned item and k_rem is how many
 //      items with key == T are still to be taken (the lowest indices win).
 //   2. a count pass: per block, items kept for sure and items equal to T.
@@ -101,7 +103,9 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
     if (nan_seen) atomicOr(&s_nan, 1u);
   }
   __syncthreads();
-  for (int b = tid; b < kBins; b += kSelThreads) a.hist[(int64_t)blockIdx.x * kBins + b] = h[b];
+  uint32_t* gh = a.hist + (int64_t)pass * kBins;
+  for (int b = tid; b < kBins; b += kSelThreads)
+    if (h[b]) atomicAdd(&gh[b], h[b]);
   if (pass == 0 && tid == 0) {
     a.counts[2 * blockIdx.x] = s_npin;
     a.counts[2 * blockIdx.x + 1] = s_nan;
@@ -113,22 +117,9 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
   if (!s_last) return;
   __threadfence();
 
-  // ---- last block: global histogram (blocks summed in order), then the digit
+  // ---- last block: the global histogram of this pass, then the digit
   const int nb = (int)gridDim.x;
-  for (int b = tid; b < kBins; b += kSelThreads) {
-    uint32_t tot = 0;
-    int blk = 0;
-    for (; blk + 8 <= nb; blk += 8) {
-      uint32_t v[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        v[k] = __atomic_load_n(&a.hist[(int64_t)(blk + k) * kBins + b], __ATOMIC_RELAXED);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) tot += v[k];
-    }
-    for (; blk < nb; ++blk) tot += __atomic_load_n(&a.hist[(int64_t)blk * kBins + b], __ATOMIC_RELAXED);
-    h[b] = tot;
-  }
+  for (int b = tid; b < kBins; b += kSelThreads) h[b] = __atomic_load_n(&gh[b], __ATOMIC_RELAXED);
   __shared__ SelectState st;
   if (tid == 0) {
     st = *a.st;
@@ -337,11 +328,23 @@ int select_blocks(int64_t n_items) {
 
 size_t select_workspace_bytes(int64_t n_items) {
   const int nb = select_blocks(n_items);
-  return 256 + (size_t)nb * kBins * sizeof(uint32_t) + (size_t)nb * 2 * sizeof(int64_t);
+  return 256 + (size_t)3 * kBins * sizeof(uint32_t) + (size_t)nb * 2 * sizeof(int64_t);
+}
+
+// Clears the selection state and the three pass histograms (a kernel rather than a
+// memset, so that the sequence can be captured in a graph).
+__global__ __launch_bounds__(kSelThreads) void select_init_kernel(SelectState* st, uint32_t* hist) {
+  for (int i = threadIdx.x; i < 3 * kBins; i += kSelThreads) hist[i] = 0;
+  if (threadIdx.x == 0) {
+    SelectState z;
+    memset(&z, 0, sizeof(z));
+    *st = z;
+  }
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  hipError_t e = hipMemsetAsync(a.st, 0, sizeof(SelectState), s);
+  hipLaunchKernelGGL(select_init_kernel, dim3(1), dim3(kSelThreads), 0, s, a.st, a.hist);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(a.n_blocks), block(kSelThreads);
   for (int pass = 0; pass < 3; ++pass) {
