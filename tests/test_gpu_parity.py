@@ -410,6 +410,48 @@ def test_score_supplied_lse_both_modes(aggregate, shift):
     assert np.abs(np64(got["lse"]) - lse_in).max() < 1e-5
 
 
+@pytest.mark.parametrize("ps", [1, 2, 4, 8, 64, 1024])
+def test_score_page_sizes(ps):
+    """Every supported page size: the scoring kernels take the per-lane address path
+    below 4 tokens per page and wave-uniform pages from 4 on."""
+    w = synth.workload(1, n_tokens=3000, window=40, n_q_heads=8, n_kv_heads=2, n_layers=2, page_size=ps)
+    k, v, bt = synth.kv_cache(w, seed=ps, device="cpu", paged_shuffle=True, extra_pages=2)
+    q = synth.window_queries(w, seed=ps)
+    acc = torch.zeros(w.n_tokens, device=DEV)
+    got = _run_score(w, k.to(DEV), v.to(DEV), bt.to(DEV), q, policy="h2o", item_tokens=1,
+                     state=dict(accum=acc))
+    kl = O.gather_logical(np64(k), bt.numpy(), ps, w.n_tokens)
+    mass, lse = O.attention_mass(np64(q), kl)
+    assert_rel(np64(got["mass"]), mass, what=f"mass, page {ps}")
+    assert np.abs(np64(got["lse"]) - lse).max() < 1e-5
+
+
+@pytest.mark.parametrize("src_ps,dst_ps", [(1, 1024), (1024, 1), (2, 64), (64, 4)])
+def test_compact_page_sizes(src_ps, dst_ps):
+    nl, hkv, n, n_keep = 2, 2, 2500, 700
+    w = synth.workload(2, n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n, page_size=src_ps)
+    k, v, bt = synth.kv_cache(w, seed=src_ps + dst_ps, device=DEV, paged_shuffle=True, extra_pages=2)
+    g = torch.Generator().manual_seed(src_ps * 7 + dst_ps)
+    keep = torch.sort(torch.randperm(n, generator=g)[:n_keep])[0].to(torch.int32)
+    old_pos = torch.arange(n, dtype=torch.int32) + 5000
+    n_dst_pages = -(-n_keep // dst_ps)
+    dk = torch.zeros((nl, n_dst_pages + 1, dst_ps, hkv, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    dbt = torch.randperm(n_dst_pages + 1, generator=g)[:n_dst_pages].to(torch.int32).to(DEV)
+    newp = torch.zeros(n_keep, dtype=torch.int32, device=DEV)
+    kv.kv_compact_rerope(kv.PagedCache(k, v, n, bt), kv.PagedCache(dk, dv, n_keep, dbt), keep.to(DEV), None,
+                         n_keep, old_pos.to(DEV), newp, renumber_base=0, rope_theta=1e6)
+    torch.cuda.synchronize()
+    kl = O.gather_logical(np64(k), bt.cpu().numpy(), src_ps, n)
+    vl = O.gather_logical(np64(v), bt.cpu().numpy(), src_ps, n)
+    rk, rv, rpos = O.compact_rerope(kl, vl, keep.numpy(), old_pos.numpy(), 0, 1e6)
+    gk = unpage(np64(dk), dbt.cpu().numpy(), dst_ps, n_keep)
+    gv = unpage(np64(dv), dbt.cpu().numpy(), dst_ps, n_keep)
+    assert (newp.cpu().numpy() == rpos).all()
+    assert (gv == rv).all()
+    assert_bf16_within_1ulp(gk, rk, f"K, pages {src_ps}->{dst_ps}")
+
+
 def test_pipeline_end_to_end_config2():
     """score -> select -> compact on the GPU against the oracle pipeline (config 2)."""
     w = synth.workload(2)
