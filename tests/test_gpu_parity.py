@@ -676,3 +676,42 @@ def test_full_size_qwen3_1m_step_properties():
     assert_bf16_within_1ulp(gk[:, moved], rk[:, moved], "K at N=1M")
     del k, v, dk, dv
     torch.cuda.empty_cache()
+
+
+def test_degenerate_sizes():
+    """One token, one query, one head: LSE is the single logit and the mass is one per
+    (layer, head, query); a single item is selected; an empty keep count moves nothing."""
+    w = synth.workload(1, n_tokens=1, window=1, n_q_heads=1, n_kv_heads=1, n_layers=2)
+    k, v, _ = synth.kv_cache(w, seed=1, device="cpu")
+    q = synth.window_queries(w, seed=1)
+    acc = torch.zeros(1, device=DEV)
+    got = _run_score(w, k.to(DEV), v.to(DEV), None, q, policy="h2o", item_tokens=1, state=dict(accum=acc))
+    s = np.einsum("ld,ld->l", np64(q)[:, 0, 0], np64(k)[:, 0, 0, 0]) / math.sqrt(128)
+    assert np.abs(np64(got["lse"]).reshape(-1) - s).max() < 1e-5
+    assert abs(float(got["mass"][0]) - 2.0) < 2e-5
+    keep = torch.full((4,), -1, dtype=torch.int32, device=DEV)
+    nk = torch.zeros(1, dtype=torch.int64, device=DEV)
+    kv.kv_select(got["item_score"].to(DEV), None, 1, 1, 1, keep, nk)
+    torch.cuda.synchronize()
+    assert int(nk) == 1 and int(keep[0]) == 0
+    # a device count of zero moves nothing
+    dk = torch.zeros((2, 1, 16, 1, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    newp = torch.full((1,), -5, dtype=torch.int32, device=DEV)
+    zero = torch.zeros(1, dtype=torch.int64, device=DEV)
+    kv.kv_compact_rerope(kv.PagedCache(k.to(DEV), v.to(DEV), 1), kv.PagedCache(dk, dv, 1), keep[:1], zero, 1,
+                         torch.zeros(1, dtype=torch.int32, device=DEV), newp, renumber_base=3)
+    torch.cuda.synchronize()
+    assert (dk == 0).all() and int(newp[0]) == -5
+
+
+def test_score_bit_reproducible():
+    """Every reduction has a fixed order: two runs give identical bits."""
+    w = synth.workload(1, n_tokens=6000, window=64, n_q_heads=32, n_kv_heads=8, n_layers=2)
+    k, v, bt, q = _make_score_inputs(w, seed=77, shuffle=True)
+    outs = []
+    for _ in range(2):
+        acc = torch.zeros(w.n_tokens, device=DEV)
+        outs.append(_run_score(w, k, v, bt, q, policy="h2o", item_tokens=1, state=dict(accum=acc)))
+    for key in ("mass", "lse", "item_score"):
+        assert torch.equal(outs[0][key], outs[1][key]), key
