@@ -1,0 +1,90 @@
+"""The launch sequences contain no memset and allocate nothing, so a caller can capture
+them in a HIP graph.  Each test captures one sequence, replays it several times with
+eager work and synchronisations between the replays, and checks every replay against
+the eager result of the same inputs."""
+import numpy as np
+import pytest
+import torch
+
+import compaction_kv_score_amd as kv
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def test_select_and_compact_in_a_graph():
+    w = synth.workload(3, n_tokens=20_000, n_layers=4)
+    k, v, _ = synth.kv_cache(w, seed=3, device=DEV)
+    N, B = w.n_tokens, w.budget_tokens
+    score = torch.empty(N, device=DEV)
+    pinned = torch.zeros(N, dtype=torch.uint8, device=DEV)
+    pinned[:4] = 1
+    keep = torch.zeros(B, dtype=torch.int32, device=DEV)
+    nk = torch.zeros(1, dtype=torch.int64, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ws = torch.empty(kv.kv_select_workspace_size(N), dtype=torch.uint8, device=DEV)
+    dk = torch.zeros((4, B // 16, 16, 8, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    pos = torch.arange(N, dtype=torch.int32, device=DEV)
+    newp = torch.zeros(B, dtype=torch.int32, device=DEV)
+    src, dst = kv.PagedCache(k, v, N), kv.PagedCache(dk, dv, B)
+
+    def seq():
+        kv.kv_select(score, pinned, 1, N, B, keep, nk, status, workspace=ws)
+        kv.kv_compact_rerope(src, dst, keep, nk, B, pos, newp, renumber_base=0, rope_theta=1e6, limit=8192)
+
+    score.copy_(torch.from_numpy(synth.scores(N, seed=1).numpy()).to(DEV))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        seq()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq()
+    for rep in range(4):
+        score.copy_(torch.from_numpy(synth.scores(N, seed=10 + rep).numpy()).to(DEV))
+        dk.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (keep.clone(), int(nk.item()), dk.clone(), newp.clone())
+        dk.zero_()
+        seq()                                   # eager, same inputs
+        torch.cuda.synchronize()
+        assert int(nk.item()) == got[1] == B and int(status.item()) == 0, rep
+        assert torch.equal(keep, got[0]) and torch.equal(dk, got[2]) and torch.equal(newp, got[3]), rep
+
+
+def test_lrfu_in_a_graph():
+    n = 70_000
+    att = torch.empty(n, device=DEV)
+    ks = torch.zeros(n, device=DEV)
+    hit = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(kv.kv_lrfu_workspace_size(n), dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(2)
+    att.copy_(torch.from_numpy((rng.random(n) ** 6).astype(np.float32)))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kv.kv_lrfu_update(att, ks, top_p=0.9, decay=0.5, hit=hit, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kv.kv_lrfu_update(att, ks, top_p=0.9, decay=0.5, hit=hit, workspace=ws)
+    for rep in range(4):
+        att.copy_(torch.from_numpy((rng.random(n) ** 6).astype(np.float32)))
+        ks0 = torch.from_numpy(rng.random(n).astype(np.float32)).to(DEV)
+        ks.copy_(ks0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_ks, got_hit = ks.clone(), hit.clone()
+        ks.copy_(ks0)
+        kv.kv_lrfu_update(att, ks, top_p=0.9, decay=0.5, hit=hit, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got_ks, ks) and torch.equal(got_hit, hit), rep
