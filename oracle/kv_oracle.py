@@ -10,8 +10,10 @@ Pages and the parts used (cited by title and section):
   * "PACE: Keeping the Right Tokens in the KV Cache Is Not Enough for Long-Horizon
     LLM Agents" -- Sec. 2 (budgeted eviction, H2O / SnapKV / StreamingLLM),
     Sec. 3.1 (blueprint, foresight bonus), Sec. 3.2 (bounded positions, renumbering,
-    Proposition 1, choosing the limit), Sec. 3.5 (split-half RoPE), Table 1 (budget
-    2,048 incl. 4 sinks and 128 recent), Sec. 5.7 / 7 (foresight floor of 50K).
+    Proposition 1, choosing the limit, non-compounding re-rotation through a reference
+    store), Sec. 3.4 (evicted rows offloaded at every compaction), Sec. 3.5 (split-half
+    RoPE, static frequency scaling), Table 1 (budget 2,048 incl. 4 sinks and 128
+    recent), Sec. 5.7 / 7 (foresight floor of 50K).
   * "MemDecay: Region-Aware KV Cache Eviction for Efficient LLM Agent Inference" --
     Method (region labels, EWMA, decay clock, composite score, pinned regions,
     page-mean eviction, half-life).
@@ -20,7 +22,9 @@ Pages and the parts used (cited by title and section):
     only the needed leading blocks of the private history).
   * "ActKV: Efficient LLM Agents through Action-Guided KV Cache Management" --
     Sec. 2.3 (attention score), Sec. 2.5 (paged KV layout and slot-map example),
-    Sec. 3.3 (the three primitives), Sec. 7.1 (score recovery from the LSE).
+    Sec. 3.3 (the three primitives), Sec. 5.1 and Algorithm 1 (LRFU keep scores, top-p
+    hit mask), Sec. 7.1 and Algorithm 3 (score recovery from the LSE, maximum over the
+    GQA group), Sec. 7.2 and Algorithm 4 (in-place tail compaction).
 
 Readings of points the pages leave open are listed next to each function.
 Parity status: every function here is pinned by a ``-m "not gpu"`` test except the
