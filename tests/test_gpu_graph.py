@@ -88,3 +88,37 @@ def test_lrfu_in_a_graph():
         kv.kv_lrfu_update(att, ks, top_p=0.9, decay=0.5, hit=hit, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(got_ks, ks) and torch.equal(got_hit, hit), rep
+
+
+def test_score_in_a_graph():
+    w = synth.workload(1, n_tokens=8000, window=64, n_q_heads=32, n_kv_heads=8, n_layers=2)
+    k, v, bt = synth.kv_cache(w, seed=4, device=DEV, paged_shuffle=True, extra_pages=1)
+    q = synth.window_queries(w, seed=4, device=DEV)
+    N = w.n_tokens
+    acc = torch.zeros(N, device=DEV)
+    out = dict(mass=torch.zeros(N, device=DEV), item_score=torch.zeros(N, device=DEV),
+               item_pinned=torch.zeros(N, dtype=torch.uint8, device=DEV))
+    cache = kv.PagedCache(k, v, N, bt)
+    kw = dict(policy="h2o", window=w.window, item_tokens=1, accum=acc, **out)
+    ws = torch.empty(kv.kv_score_workspace_size(cache, q, **kw), dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kv.kv_score(cache, q, workspace=ws, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kv.kv_score(cache, q, workspace=ws, **kw)
+    for rep in range(3):
+        q.copy_(synth.window_queries(w, seed=20 + rep, device=DEV))
+        acc.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = {key: t.clone() for key, t in out.items()}
+        acc.zero_()
+        kv.kv_score(cache, q, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        for key in out:
+            assert torch.equal(got[key], out[key]), (rep, key)
