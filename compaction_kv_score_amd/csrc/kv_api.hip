@@ -447,6 +447,7 @@ static void fill_compact_common(CompactArgs* a, const kv_cache_desc* src, const 
   a->dst_bt = dst->block_table;
   a->n_layers = src->n_layers;
   a->n_kv_heads = src->n_kv_heads;
+  a->src_tokens = src->n_tokens;
   a->src_page_shift = log2_exact(src->page_size);
   a->dst_page_shift = log2_exact(dst->page_size);
   a->renumber_base = renumber_base;
@@ -711,6 +712,7 @@ int32_t kv_compact_tail_inplace(const kv_cache_desc* cache, const int32_t* keep_
   a.keep = keep_tokens;
   a.n_keep = n_keep;
   a.max_keep = max_keep;
+  a.n_tokens = N;
   a.start = start;
   a.budget = budget >= N ? N : budget;
   a.status = status;

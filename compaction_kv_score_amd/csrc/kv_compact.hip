@@ -117,6 +117,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
   if (r >= a.rank1) return;
   if (a.n_keep && r >= *a.n_keep) return;
   const int64_t j = source_token(a, r);
+  if (j < 0 || j >= a.src_tokens) return;   // malformed keep entry: nothing is read or written
   const int32_t op = a.old_pos[j];
   const int32_t np = a.renumber_base >= 0 ? a.renumber_base + (int32_t)r : op;
   const bool in_place = a.keep == nullptr && j == r && a.src_k == a.dst_k;
@@ -212,6 +213,7 @@ __global__ __launch_bounds__(256) void gather_meta_kernel(CompactArgs a) {
   if (r >= a.rank1) return;
   if (a.n_keep && r >= *a.n_keep) return;
   const int64_t j = source_token(a, r);
+  if (j < 0 || j >= a.src_tokens) return;
   if (a.new_pos) a.new_pos[r] = a.renumber_base >= 0 ? a.renumber_base + (int32_t)r : a.old_pos[j];
   for (int m = 0; m < a.meta.n; ++m) {
     switch (a.meta.elem_bytes[m]) {
@@ -271,6 +273,7 @@ __global__ __launch_bounds__(kCompactThreads) void tail_compact_kernel(TailArgs 
   const int64_t d = blockIdx.x;
   if (d >= n_pairs) return;
   const int64_t src = keep[d < r_in ? d : d + k_in];
+  if (src < 0 || src >= a.n_tokens) return;  // malformed keep entry: nothing is moved
   const int64_t c = block_count_true(k_in, [&](int64_t i) { return keep[r_in + i] - start - i <= d; });
   const int64_t dst = start + d + c;
 

@@ -170,6 +170,7 @@ struct CompactArgs {
   int64_t dst_layer_stride, dst_page_stride;
   const int32_t* dst_bt;
   int n_layers, n_kv_heads, src_page_shift, dst_page_shift;
+  int64_t src_tokens;            // tokens of the source row: keep entries outside are skipped
   // rank -> source token: keep[r] when keep != nullptr, else r (+ shift when r >= split)
   const int32_t* keep;
   int64_t split, shift;
@@ -200,6 +201,7 @@ struct TailArgs {
   const int32_t* keep;           // ascending kept slots
   const int64_t* n_keep;         // device count (nullable: max_keep)
   int64_t max_keep;
+  int64_t n_tokens;              // used slots: keep entries outside [0, n_tokens) are skipped
   int64_t start, budget;         // target region [start, start + budget)
   uint32_t* status;              // nullable
   MetaSet meta;                  // arrays moved in place (src == dst)

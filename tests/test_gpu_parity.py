@@ -715,3 +715,28 @@ def test_score_bit_reproducible():
         outs.append(_run_score(w, k, v, bt, q, policy="h2o", item_tokens=1, state=dict(accum=acc)))
     for key in ("mass", "lse", "item_score"):
         assert torch.equal(outs[0][key], outs[1][key]), key
+
+
+def test_compact_skips_out_of_range_keep_entries():
+    """Keep entries outside the source row are skipped by the kernels' own bounds checks:
+    their ranks are left untouched and every other rank is compacted normally."""
+    w = synth.workload(2, n_layers=2, n_kv_heads=2, n_q_heads=2, n_tokens=300)
+    k, v, _ = synth.kv_cache(w, seed=9, device=DEV)
+    keep = torch.arange(0, 300, 10, dtype=torch.int32)          # 30 ranks
+    keep[[3, 17]] = torch.tensor([1 << 30, -5], dtype=torch.int32)
+    dk = torch.zeros((2, 2, 16, 2, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    newp = torch.full((30,), -9, dtype=torch.int32, device=DEV)
+    reg = torch.arange(300, dtype=torch.int32, device=DEV)
+    reg_out = torch.full((30,), -1, dtype=torch.int32, device=DEV)
+    pos = torch.arange(300, dtype=torch.int32, device=DEV)
+    kv.kv_compact_rerope(kv.PagedCache(k, v, 300), kv.PagedCache(dk, dv, 30), keep.to(DEV), None, 30, pos, newp,
+                         renumber_base=-1, rope_theta=1e6, meta=[(reg, reg_out)])
+    torch.cuda.synchronize()
+    got_v = unpage(np64(dv), None, 16, 30)
+    src_v = unpage(np64(v), None, 16, 300)
+    ok = [r for r in range(30) if r not in (3, 17)]
+    assert (got_v[:, ok] == src_v[:, keep.numpy()[ok]]).all()
+    assert (got_v[:, [3, 17]] == 0).all()
+    assert (newp.cpu().numpy()[[3, 17]] == -9).all() and (reg_out.cpu().numpy()[[3, 17]] == -1).all()
+    assert (newp.cpu().numpy()[ok] == keep.numpy()[ok]).all()
