@@ -451,11 +451,18 @@ static void fill_compact_common(CompactArgs* a, const kv_cache_desc* src, const 
   a->src_page_shift = log2_exact(src->page_size);
   a->dst_page_shift = log2_exact(dst->page_size);
   a->renumber_base = renumber_base;
+  a->parts = 1;
   for (int i = 0; i < kHeadDim / 2; ++i) a->inv_freq[i] = inv_freq[i];
 }
 
+// Without a reference store a rank's copy is split over several workgroups (its
+// positions and metadata are read and written by the first one only).  The store's check
+// covers the whole key, so that path keeps one workgroup per rank.
 static void fill_ref(CompactArgs* a, const kv_ref_store* src, const kv_ref_store* dst) {
-  if (!src) return;
+  if (!src) {
+    a->parts = compact_parts(a->n_layers, a->n_kv_heads);
+    return;
+  }
   a->ref_src_k = (const uint16_t*)src->k;
   a->ref_src_pos = src->pos;
   a->ref_src_layer_stride = src->layer_stride;
@@ -519,9 +526,6 @@ int32_t kv_compact_rerope_ex(const kv_cache_desc* src, const kv_cache_desc* dst,
   a.meta = ms;
   hipError_t e = launch_compact(a, stream);
   if (e != hipSuccess) return hip_fail(e);
-  if (new_pos || ms.n) {
-    if ((e = launch_gather_meta(a, stream)) != hipSuccess) return hip_fail(e);
-  }
   return KV_OK;
 }
 
@@ -568,11 +572,14 @@ int32_t kv_compact_segment_inplace_ex(const kv_cache_desc* cache, int64_t prefix
   a.new_pos = pos;
   a.meta = ms;
   hipError_t e;
-  // prefix: stays in place (re-rotated only if its positions change)
+  // prefix: stays in place (re-rotated only if its positions change); a rank reads and
+  // writes its own position here, so each rank is one workgroup
+  const int parts = a.parts;
   a.rank0 = 0;
   a.rank1 = prefix_len;
+  a.parts = 1;
   if ((e = launch_compact(a, stream)) != hipSuccess) return hip_fail(e);
-  if ((e = launch_gather_meta(a, stream)) != hipSuccess) return hip_fail(e);
+  a.parts = parts;
   if (evict_len == 0) return KV_OK;
   // suffix: rounds of at most evict_len ranks; round k reads [r0+E, r1+E) and writes
   // [r0, r1), disjoint because r1 - r0 <= E; later rounds read only beyond r1 + E.
@@ -580,7 +587,6 @@ int32_t kv_compact_segment_inplace_ex(const kv_cache_desc* cache, int64_t prefix
     a.rank0 = r0;
     a.rank1 = r0 + evict_len < n_keep ? r0 + evict_len : n_keep;
     if ((e = launch_compact(a, stream)) != hipSuccess) return hip_fail(e);
-    if ((e = launch_gather_meta(a, stream)) != hipSuccess) return hip_fail(e);
   }
   return KV_OK;
 }

@@ -29,6 +29,15 @@ namespace {
 
 constexpr int kCompactThreads = 256;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal: the kept rows are read once, and the hint keeps
+// them from displacing other cached data.
+__device__ __forceinline__ uint4 load_once(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
   return (double)__uint_as_float(bits16 << 16);
 }
@@ -107,13 +116,34 @@ __device__ __forceinline__ void fill_rotation(double2* cs, const CompactArgs& a,
   }
 }
 
+// Per-token metadata of rank r taken from source token j (element sizes 1, 2, 4 or 8).
+__device__ __forceinline__ void gather_meta_row(const MetaSet& m, int64_t j, int64_t r) {
+  for (int i = 0; i < m.n; ++i) {
+    switch (m.elem_bytes[i]) {
+      case 1:
+        ((uint8_t*)m.dst[i])[r] = ((const uint8_t*)m.src[i])[j];
+        break;
+      case 2:
+        ((uint16_t*)m.dst[i])[r] = ((const uint16_t*)m.src[i])[j];
+        break;
+      case 4:
+        ((uint32_t*)m.dst[i])[r] = ((const uint32_t*)m.src[i])[j];
+        break;
+      default:
+        ((uint64_t*)m.dst[i])[r] = ((const uint64_t*)m.src[i])[j];
+        break;
+    }
+  }
+}
+
 template <bool kStore>
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a) {
   __shared__ double2 cs[64];
   __shared__ double2 cs_chk[kStore ? 64 : 1];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
-  const int64_t r = a.rank0 + blockIdx.x;
+  const int64_t r = a.rank0 + blockIdx.x / a.parts;
+  const int part = (int)(blockIdx.x % a.parts);
   if (r >= a.rank1) return;
   if (a.n_keep && r >= *a.n_keep) return;
   const int64_t j = source_token(a, r);
@@ -165,8 +195,11 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
     __syncthreads();
   }
 
+  // this workgroup's share of the (layer, head, chunk pair) items
+  const int e0 = (int)((int64_t)part * items / a.parts);
+  const int e1 = (int)((int64_t)(part + 1) * items / a.parts);
 #pragma unroll 2
-  for (int e = tid; e < items; e += kCompactThreads) {
+  for (int e = e0 + tid; e < e1; e += kCompactThreads) {
     const int layer = e / per_layer;
     const int rem = e - layer * per_layer;
     const int64_t col = (rem >> 3) * kHeadDim + (rem & 7) * 8;
@@ -178,8 +211,8 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
       klo = *(const uint4*)(a.ref_src_k + ro);
       khi = *(const uint4*)(a.ref_src_k + ro + 64);
     } else {
-      klo = *(const uint4*)(a.src_k + so);
-      khi = *(const uint4*)(a.src_k + so + 64);
+      klo = load_once(a.src_k + so);
+      khi = load_once(a.src_k + so + 64);
     }
     if (kStore && (seed || move_entry)) {
       const int64_t rd = (int64_t)layer * a.ref_dst_layer_stride + r * slot_stride + col;
@@ -188,8 +221,8 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
     }
     uint4 vlo, vhi;
     if (!in_place) {
-      vlo = *(const uint4*)(a.src_v + so);
-      vhi = *(const uint4*)(a.src_v + so + 64);
+      vlo = load_once(a.src_v + so);
+      vhi = load_once(a.src_v + so + 64);
     }
     if (delta != 0) rotate_chunk(klo, khi, &cs[(rem & 7) * 8]);
     *(uint4*)(a.dst_k + d_o) = klo;
@@ -199,38 +232,21 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
       *(uint4*)(a.dst_v + d_o + 64) = vhi;
     }
   }
-  if (kStore && tid == 0) a.ref_dst_pos[r] = use_ref ? rp : (seed ? op : KV_REF_NONE);
+  // The rank's new position, metadata and store position, written by its first
+  // workgroup once every wave has read the old ones (the in-place forms pass the same
+  // arrays as source and destination; a launch whose ranks read positions that it also
+  // writes runs one workgroup per rank).
+  __syncthreads();
+  if (tid == 0 && part == 0) {
+    if (a.new_pos) a.new_pos[r] = np;
+    gather_meta_row(a.meta, j, r);
+    if (kStore) a.ref_dst_pos[r] = use_ref ? rp : (seed ? op : KV_REF_NONE);
+  }
 }
 
 __global__ __launch_bounds__(256) void ref_invalidate_kernel(int32_t* pos, int64_t count) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < count) pos[i] = KV_REF_NONE;
-}
-
-// New positions and per-token metadata, one thread per rank (coalesced over ranks).
-__global__ __launch_bounds__(256) void gather_meta_kernel(CompactArgs a) {
-  const int64_t r = a.rank0 + (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= a.rank1) return;
-  if (a.n_keep && r >= *a.n_keep) return;
-  const int64_t j = source_token(a, r);
-  if (j < 0 || j >= a.src_tokens) return;
-  if (a.new_pos) a.new_pos[r] = a.renumber_base >= 0 ? a.renumber_base + (int32_t)r : a.old_pos[j];
-  for (int m = 0; m < a.meta.n; ++m) {
-    switch (a.meta.elem_bytes[m]) {
-      case 1:
-        ((uint8_t*)a.meta.dst[m])[r] = ((const uint8_t*)a.meta.src[m])[j];
-        break;
-      case 2:
-        ((uint16_t*)a.meta.dst[m])[r] = ((const uint16_t*)a.meta.src[m])[j];
-        break;
-      case 4:
-        ((uint32_t*)a.meta.dst[m])[r] = ((const uint32_t*)a.meta.src[m])[j];
-        break;
-      default:
-        ((uint64_t*)a.meta.dst[m])[r] = ((const uint64_t*)a.meta.src[m])[j];
-        break;
-    }
-  }
 }
 
 // Number of leading entries of a monotone predicate over [0, n) (true, then false),
@@ -352,26 +368,26 @@ hipError_t launch_tail_compact(const TailArgs& a, int64_t grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+int compact_parts(int n_layers, int n_kv_heads) {
+  const int items = n_layers * n_kv_heads * 8;
+  return (items + kCompactThreads - 1) / kCompactThreads;
+}
+
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const int64_t n = a.rank1 - a.rank0;
   if (n <= 0) return hipSuccess;
+  const int64_t grid = n * a.parts;
+  if (a.parts < 1 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (a.ref_src_k)
-    hipLaunchKernelGGL(compact_kernel<true>, dim3((unsigned)n), dim3(kCompactThreads), 0, s, a);
+    hipLaunchKernelGGL(compact_kernel<true>, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(compact_kernel<false>, dim3((unsigned)n), dim3(kCompactThreads), 0, s, a);
+    hipLaunchKernelGGL(compact_kernel<false>, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_ref_invalidate(int32_t* pos, int64_t count, hipStream_t s) {
   if (count <= 0) return hipSuccess;
   hipLaunchKernelGGL(ref_invalidate_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, pos, count);
-  return hipGetLastError();
-}
-
-hipError_t launch_gather_meta(const CompactArgs& a, hipStream_t s) {
-  const int64_t n = a.rank1 - a.rank0;
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_meta_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

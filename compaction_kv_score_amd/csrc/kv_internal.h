@@ -175,6 +175,7 @@ struct CompactArgs {
   const int32_t* keep;
   int64_t split, shift;
   int64_t rank0, rank1;          // ranks handled by this launch
+  int parts;                     // workgroups per rank, each moving a contiguous share of its items
   const int64_t* n_keep;         // device count (nullable); ranks >= it are skipped
   const int32_t* old_pos;        // [N] indexed by source token
   int32_t* new_pos;              // [ranks] (nullable)
@@ -189,6 +190,8 @@ struct CompactArgs {
   int64_t ref_dst_layer_stride;
   MetaSet meta;
 };
+// Workgroups per rank that give every thread of the copy at most one item.
+int compact_parts(int n_layers, int n_kv_heads);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 hipError_t launch_ref_invalidate(int32_t* pos, int64_t count, hipStream_t s);
 
@@ -227,6 +230,5 @@ struct EvictArgs {
   MetaSet meta;                  // dst[e - first] = src[token]
 };
 hipError_t launch_gather_evicted(const EvictArgs& a, hipStream_t s);
-hipError_t launch_gather_meta(const CompactArgs& a, hipStream_t s);
 
 }  // namespace kvs

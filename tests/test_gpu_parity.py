@@ -66,6 +66,7 @@ def _paged_to_logical(t, bt, pg, n):
     (2, 8, 777, 100, True, -1, 1e4),
     (2, 8, 4096, 1, False, 5, 1e4),
     (28, 2, 2048, 512, True, 0, 1e6),
+    (5, 8, 600, 150, True, 3, 1e6),     # 320 items per token: two workgroups of 160
 ])
 def test_compact_rerope_parity(nl, hkv, n, n_keep, shuffle, base, theta):
     w = synth.workload(2, n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n)
@@ -131,6 +132,7 @@ def test_compact_respects_device_count():
     (3, 4096, 512, 0.3, 0, 1e4, True),
     (2, 600, 0, 0.9, -1, 1e4, False),
     (2, 300, 200, 0.05, 7, 1e6, False),
+    (9, 2000, 64, 0.3, 5, 1e6, True),  # 576 items per token: three workgroups; prefix shifted
 ])
 def test_segment_inplace_parity(nl, n, prefix, frac, base, theta, shuffle):
     w = synth.workload(4, n_layers=nl, n_tokens=n)
