@@ -302,8 +302,8 @@ __global__ __launch_bounds__(kCompactThreads) void tail_compact_kernel(TailArgs 
     const int layer = e / per_layer;
     const int64_t col = (int64_t)(e - layer * per_layer) * 8;
     const int64_t lo = (int64_t)layer * a.layer_stride;
-    const uint4 kk = *(const uint4*)(a.k + lo + so + col);
-    const uint4 vv = *(const uint4*)(a.v + lo + so + col);
+    const uint4 kk = load_once(a.k + lo + so + col);
+    const uint4 vv = load_once(a.v + lo + so + col);
     *(uint4*)(a.k + lo + dof + col) = kk;
     *(uint4*)(a.v + lo + dof + col) = vv;
   }
@@ -324,25 +324,28 @@ __global__ __launch_bounds__(kCompactThreads) void tail_compact_kernel(TailArgs 
 // whose own count of dropped tokens before them (keep[i] - i) does not exceed e.
 __global__ __launch_bounds__(kCompactThreads) void gather_evicted_kernel(EvictArgs a) {
   const int tid = threadIdx.x;
-  const int64_t e = a.first + blockIdx.x;
+  const int64_t r = blockIdx.x / a.parts;
+  const int part = (int)(blockIdx.x % a.parts);
+  const int64_t e = a.first + r;
   const int32_t* keep = a.keep;
   const int64_t c = block_count_true(a.n_keep, [&](int64_t i) { return keep[i] - i <= e; });
   const int64_t t = e + c;
-  const int64_t r = blockIdx.x;
   const int slot_stride = a.n_kv_heads * kHeadDim;
   const int64_t so = token_offset(t, a.src_page_shift, a.src_page_stride, a.src_bt, slot_stride);
   const int64_t dof = token_offset(r, a.dst_page_shift, a.dst_page_stride, a.dst_bt, slot_stride);
   const int per_layer = slot_stride / 8;
   const int items = a.n_layers * per_layer;
-  for (int it = tid; it < items; it += kCompactThreads) {
+  const int i0 = (int)((int64_t)part * items / a.parts);
+  const int i1 = (int)((int64_t)(part + 1) * items / a.parts);
+  for (int it = i0 + tid; it < i1; it += kCompactThreads) {
     const int layer = it / per_layer;
     const int64_t col = (int64_t)(it - layer * per_layer) * 8;
     const int64_t s0 = (int64_t)layer * a.src_layer_stride + so + col;
     const int64_t d0 = (int64_t)layer * a.dst_layer_stride + dof + col;
-    *(uint4*)(a.dst_k + d0) = *(const uint4*)(a.src_k + s0);
-    *(uint4*)(a.dst_v + d0) = *(const uint4*)(a.src_v + s0);
+    *(uint4*)(a.dst_k + d0) = load_once(a.src_k + s0);
+    *(uint4*)(a.dst_v + d0) = load_once(a.src_v + s0);
   }
-  if (tid == 0) {
+  if (tid == 0 && part == 0) {
     if (a.evicted_tokens) a.evicted_tokens[r] = (int32_t)t;
     for (int m = 0; m < a.meta.n; ++m) {
       switch (a.meta.elem_bytes[m]) {
@@ -357,14 +360,26 @@ __global__ __launch_bounds__(kCompactThreads) void gather_evicted_kernel(EvictAr
 
 }  // namespace
 
-hipError_t launch_gather_evicted(const EvictArgs& a, hipStream_t s) {
-  if (a.count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_evicted_kernel, dim3((unsigned)a.count), dim3(kCompactThreads), 0, s, a);
+// Workgroups per token for a plain K/V copy of `items` 16-byte chunk pairs: every thread
+// moves at most one item, and many short workgroups keep HBM streaming.
+static int copy_parts(int items) { return (items + kCompactThreads - 1) / kCompactThreads; }
+
+hipError_t launch_gather_evicted(const EvictArgs& a0, hipStream_t s) {
+  if (a0.count <= 0) return hipSuccess;
+  EvictArgs a = a0;
+  a.parts = copy_parts(a.n_layers * a.n_kv_heads * (kHeadDim / 8));
+  const int64_t grid = a.count * a.parts;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_evicted_kernel, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_tail_compact(const TailArgs& a, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL(tail_compact_kernel, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(kCompactThreads), 0, s, a);
+// One workgroup per pair: each first locates its pair with three block-wide searches over
+// the keep list (a chain of barriers and cached loads), so splitting a token over several
+// workgroups, as the other copies do, would repeat that latency (measured slower).
+hipError_t launch_tail_compact(const TailArgs& a, int64_t pairs, hipStream_t s) {
+  if (pairs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tail_compact_kernel, dim3((unsigned)(pairs > 0 ? pairs : 1)), dim3(kCompactThreads), 0, s, a);
   return hipGetLastError();
 }
 

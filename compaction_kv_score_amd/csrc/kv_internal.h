@@ -209,7 +209,7 @@ struct TailArgs {
   uint32_t* status;              // nullable
   MetaSet meta;                  // arrays moved in place (src == dst)
 };
-hipError_t launch_tail_compact(const TailArgs& a, int64_t grid, hipStream_t s);
+hipError_t launch_tail_compact(const TailArgs& a, int64_t pairs, hipStream_t s);
 
 struct EvictArgs {
   const uint16_t* src_k;
@@ -228,6 +228,7 @@ struct EvictArgs {
   int64_t first, count;          // evicted ranks [first, first + count)
   int32_t* evicted_tokens;       // [count] (nullable)
   MetaSet meta;                  // dst[e - first] = src[token]
+  int parts;                     // workgroups per evicted token (set by the launcher)
 };
 hipError_t launch_gather_evicted(const EvictArgs& a, hipStream_t s);
 

@@ -108,17 +108,17 @@ def _logical(t, bt, slots):
     return unpage(t.float().cpu().double().numpy(), None if bt is None else bt.cpu().numpy(), 16, slots)
 
 
-@pytest.mark.parametrize("n,budget,n_keep,shuffle,dev_count", [
-    (1000, 300, 300, True, False),     # region reaches past N into the last block
-    (1024, 256, 200, False, True),     # fewer kept than the budget, device count
-    (777, 100, 100, True, False),
-    (5000, 2048, 2048, True, True),
-    (64, 16, 16, False, False),
-    (500, 600, 300, True, False),      # budget above N: nothing moves
+@pytest.mark.parametrize("n,budget,n_keep,shuffle,dev_count,nl,hkv", [
+    (1000, 300, 300, True, False, 2, 2),     # region reaches past N into the last block
+    (1024, 256, 200, False, True, 2, 2),     # fewer kept than the budget, device count
+    (777, 100, 100, True, False, 2, 2),
+    (5000, 2048, 2048, True, True, 2, 2),
+    (64, 16, 16, False, False, 2, 2),
+    (500, 600, 300, True, False, 2, 2),      # budget above N: nothing moves
+    (3000, 1024, 1000, True, True, 9, 4),    # 576 chunk pairs per token, many layers and heads
 ])
-def test_tail_compact_parity(n, budget, n_keep, shuffle, dev_count):
+def test_tail_compact_parity(n, budget, n_keep, shuffle, dev_count, nl, hkv):
     rng = np.random.default_rng(n + budget)
-    nl, hkv = 2, 2
     slots = -(-n // 16) * 16
     k = O.bf16_round(rng.standard_normal((nl, slots, hkv, 128)))
     v = O.bf16_round(rng.standard_normal((nl, slots, hkv, 128)))

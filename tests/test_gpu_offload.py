@@ -23,6 +23,7 @@ def _logical(t, bt, n):
     (3, 8, 777, 0, 10, 500, False),
     (2, 2, 4096, 4000, 0, 96, True),
     (1, 4, 513, 512, 0, 1, True),
+    (9, 4, 2000, 1500, 100, 400, True),     # 576 chunk pairs per token: three workgroups each
 ])
 def test_gather_evicted_parity(nl, hkv, n, n_keep, first, count, shuffle):
     w = synth.workload(2, n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n)
