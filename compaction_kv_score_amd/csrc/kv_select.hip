@@ -43,6 +43,22 @@ __device__ __forceinline__ bool item_pinned(const SelectArgs& a, int64_t i) {
   return a.pinned != nullptr && a.pinned[i] != 0;
 }
 
+// Items a thread loads before it processes any of them: the loads of a batch are all in
+// flight together instead of one memory round trip per item.
+constexpr int kSelBatch = 4;
+
+// Score and pinned flag of items b0 + u*kSelThreads + tid (u < kSelBatch) before `end`.
+__device__ __forceinline__ void load_batch(const SelectArgs& a, int64_t b0, int64_t end,
+                                           float (&sc)[kSelBatch], bool (&pin)[kSelBatch]) {
+#pragma unroll
+  for (int u = 0; u < kSelBatch; ++u) {
+    const int64_t i = b0 + (int64_t)u * kSelThreads + threadIdx.x;
+    const bool in = i < end;
+    pin[u] = in && item_pinned(a, i);
+    sc[u] = in ? a.score[i] : 0.f;
+  }
+}
+
 // Add 1 to bin[d] for every lane with `want`.  Scores of a long row are concentrated in
 // a few bins, so the lanes sharing the most common digits are merged into one atomic
 // each first and only the rest are added one by one.
@@ -71,32 +87,36 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
   __shared__ uint32_t s_npin, s_nan;
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
+  const int64_t end = begin + a.per_block < a.n_items ? begin + a.per_block : a.n_items;
+  // the first batch is requested before the state, so the two latencies overlap
+  float sc[kSelBatch];
+  bool pin[kSelBatch];
+  load_batch(a, begin, end, sc, pin);
+  const uint32_t mode = pass == 0 ? 0u : a.st->mode;
+  const uint32_t prefix = pass == 0 ? 0u : a.st->prefix;
+  const uint32_t mask = pass == 0 ? 0u : a.st->mask;
   for (int b = tid; b < kBins; b += kSelThreads) h[b] = 0;
   if (tid == 0) {
     s_npin = 0;
     s_nan = 0;
   }
   __syncthreads();
-
-  const uint32_t mode = pass == 0 ? 0u : a.st->mode;
   if (mode != 0) return;  // decided without a radix pass (uniform across the grid)
-  const uint32_t prefix = pass == 0 ? 0u : a.st->prefix;
-  const uint32_t mask = pass == 0 ? 0u : a.st->mask;
   const int shift = pass_shift(pass);
   const uint32_t dmask = pass_dmask(pass);
 
-  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
-  const int64_t end = begin + a.per_block < a.n_items ? begin + a.per_block : a.n_items;
   uint32_t npin = 0, nan_seen = 0;
-  for (int64_t i0 = begin; i0 < end; i0 += kSelThreads) {
-    const int64_t i = i0 + tid;
-    const bool in = i < end;
-    const bool pin = in && item_pinned(a, i);
-    const float sc = in ? a.score[i] : 0.f;
-    const uint32_t key = order_key(sc);
-    npin += pin ? 1u : 0u;
-    nan_seen |= (in && !pin && sc != sc) ? 1u : 0u;
-    hist_add(h, in && !pin && (key & mask) == prefix, (key >> shift) & dmask);
+  for (int64_t b0 = begin; b0 < end; b0 += (int64_t)kSelThreads * kSelBatch) {
+    if (b0 != begin) load_batch(a, b0, end, sc, pin);
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {
+      const bool in = b0 + (int64_t)u * kSelThreads + tid < end;
+      const uint32_t key = order_key(sc[u]);
+      npin += pin[u] ? 1u : 0u;
+      nan_seen |= (in && !pin[u] && sc[u] != sc[u]) ? 1u : 0u;
+      hist_add(h, in && !pin[u] && (key & mask) == prefix, (key >> shift) & dmask);
+    }
   }
   if (pass == 0) {
     if (npin) atomicAdd(&s_npin, npin);
@@ -121,15 +141,23 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
   const int nb = (int)gridDim.x;
   for (int b = tid; b < kBins; b += kSelThreads) h[b] = __atomic_load_n(&gh[b], __ATOMIC_RELAXED);
   __shared__ SelectState st;
-  if (tid == 0) {
-    st = *a.st;
+  if (wv == 0) {
+    // pass 0: lane b reads block b's counts (at most 64 blocks), then a wave-wide sum
+    int64_t n_pin = 0;
+    uint32_t nan_any = 0;
     if (pass == 0) {
-      int64_t n_pin = 0;
-      uint32_t nan_any = 0;
-      for (int blk = 0; blk < nb; ++blk) {
-        n_pin += __atomic_load_n(&a.counts[2 * blk], __ATOMIC_RELAXED);
-        nan_any |= (uint32_t)__atomic_load_n(&a.counts[2 * blk + 1], __ATOMIC_RELAXED);
+      if (lane < nb) {
+        n_pin = __atomic_load_n(&a.counts[2 * lane], __ATOMIC_RELAXED);
+        nan_any = (uint32_t)__atomic_load_n(&a.counts[2 * lane + 1], __ATOMIC_RELAXED);
       }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        n_pin += __shfl_xor(n_pin, off);
+        nan_any |= __shfl_xor(nan_any, off);
+      }
+    }
+    if (lane == 0) st = *a.st;
+    if (lane == 0 && pass == 0) {
       st.n_pinned = n_pin;
       st.n_cand = a.n_items - n_pin;
       st.nan_seen = nan_any;
@@ -189,21 +217,29 @@ __global__ __launch_bounds__(kSelThreads) void select_count_kernel(SelectArgs a)
     s_def = 0;
     s_eq = 0;
   }
-  __syncthreads();
-  const uint32_t mode = a.st->mode;
-  const uint32_t T = a.st->prefix;
   const int64_t begin = (int64_t)blockIdx.x * a.per_block;
   const int64_t end = begin + a.per_block < a.n_items ? begin + a.per_block : a.n_items;
+  float sc[kSelBatch];
+  bool pin[kSelBatch];
+  load_batch(a, begin, end, sc, pin);
+  const uint32_t mode = a.st->mode;
+  const uint32_t T = a.st->prefix;
+  __syncthreads();
   uint32_t def = 0, eq = 0;
-  for (int64_t i = begin + tid; i < end; i += kSelThreads) {
-    if (item_pinned(a, i) || mode == 1u) {
-      ++def;
-      continue;
+  for (int64_t b0 = begin; b0 < end; b0 += (int64_t)kSelThreads * kSelBatch) {
+    if (b0 != begin) load_batch(a, b0, end, sc, pin);
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {
+      if (b0 + (int64_t)u * kSelThreads + tid >= end) continue;
+      if (pin[u] || mode == 1u) {
+        ++def;
+        continue;
+      }
+      if (mode == 2u) continue;
+      const uint32_t key = order_key(sc[u]);
+      def += key > T;
+      eq += key == T;
     }
-    if (mode == 2u) continue;
-    const uint32_t key = order_key(a.score[i]);
-    def += key > T;
-    eq += key == T;
   }
   if (def) atomicAdd(&s_def, def);
   if (eq) atomicAdd(&s_eq, eq);
@@ -240,39 +276,62 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
   __shared__ uint32_t s_wave[kWaves];
   __shared__ int64_t s_kept_before, s_eq_before;
   __shared__ int s_last_kept;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
+  const int64_t end = begin + a.per_block < a.n_items ? begin + a.per_block : a.n_items;
+  float sc[kSelBatch];
+  bool pin[kSelBatch];
+  load_batch(a, begin, end, sc, pin);
   const uint32_t mode = a.st->mode;
   const uint32_t T = a.st->prefix;
   const int64_t k_rem = mode == 0u ? a.st->k_rem : 0;
-  if (tid == 0) {
-    int64_t kept = 0, eqb = 0;
-    for (int b = 0; b < (int)blockIdx.x; ++b) {
-      const int64_t def = a.counts[2 * b];
-      const int64_t eq = a.counts[2 * b + 1];
-      int64_t take = k_rem - eqb;
-      take = take < 0 ? 0 : (take > eq ? eq : take);
-      kept += def + take;
-      eqb += eq;
+  if (tid < 64) {
+    // lane b holds block b's counts (b < blockIdx.x <= 63); ties are taken in block order,
+    // so block b takes clamp(k_rem - ties of blocks before b, 0, its ties)
+    const bool mine = lane < (int)blockIdx.x;
+    const int64_t def = mine ? a.counts[2 * lane] : 0;
+    const int64_t eq = mine ? a.counts[2 * lane + 1] : 0;
+    int64_t eq_incl = eq;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t v = __shfl_up(eq_incl, off);
+      if (lane >= off) eq_incl += v;
     }
-    s_kept_before = kept;
-    s_eq_before = eqb;
-    s_last_kept = 0;
+    int64_t take = k_rem - (eq_incl - eq);
+    take = take < 0 ? 0 : (take > eq ? eq : take);
+    int64_t kept = def + take;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) kept += __shfl_xor(kept, off);
+    const int64_t eqb = __shfl(eq_incl, 63);
+    if (lane == 0) {
+      s_kept_before = kept;
+      s_eq_before = eqb;
+      s_last_kept = 0;
+    }
   }
   __syncthreads();
   int64_t kept_before = s_kept_before;
   int64_t eq_before = s_eq_before;
-  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
-  const int64_t end = begin + a.per_block < a.n_items ? begin + a.per_block : a.n_items;
   const int it = a.item_tokens;
   for (int64_t base = begin; base < end; base += kSelThreads) {
+    const int u = (int)(((base - begin) / kSelThreads) % kSelBatch);
+    if (base != begin && u == 0) load_batch(a, base, end, sc, pin);
     const int64_t i = base + tid;
     const bool valid = i < end;
     bool def = false, eq = false;
+    float sc_u = sc[0];
+    bool pin_u = pin[0];
+#pragma unroll
+    for (int v = 1; v < kSelBatch; ++v)
+      if (u == v) {
+        sc_u = sc[v];
+        pin_u = pin[v];
+      }
     if (valid) {
-      if (item_pinned(a, i) || mode == 1u) {
+      if (pin_u || mode == 1u) {
         def = true;
       } else if (mode == 0u) {
-        const uint32_t key = order_key(a.score[i]);
+        const uint32_t key = order_key(sc_u);
         def = key > T;
         eq = key == T;
       }
