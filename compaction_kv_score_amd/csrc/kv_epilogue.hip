@@ -16,33 +16,50 @@ namespace kvs {
 
 namespace {
 
-constexpr int kEpiThreads = 256;
+constexpr int kEpiThreads = 256;   // tokens per block
+constexpr int kEpiSplit = 4;       // threads sharing one token's partials
 
-__global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
+__global__ __launch_bounds__(kEpiThreads * kEpiSplit) void epilogue_kernel(EpilogueArgs a) {
   __shared__ float s_sum[kEpiThreads];
   __shared__ int s_cnt[kEpiThreads];
   __shared__ int s_pin[kEpiThreads];
-  const int tid = threadIdx.x;
+  __shared__ double s_part[kEpiSplit][kEpiThreads];
+  const int tid = threadIdx.x % kEpiThreads;
+  const int quarter = threadIdx.x / kEpiThreads;
   const int64_t N = a.n_tokens;
   const int64_t i = (int64_t)blockIdx.x * kEpiThreads + tid;
   const bool valid = i < N;
 
+  // Fixed-order float64 sum of the partials: thread `quarter` adds a contiguous quarter
+  // of them in order (loads issued 8 at a time so that enough are in flight), and the
+  // four quarter sums are added in quarter order.
+  {
+    const int per = (a.n_parts + kEpiSplit - 1) / kEpiSplit;
+    const int p0 = quarter * per;
+    const int p1 = p0 + per < a.n_parts ? p0 + per : a.n_parts;
+    double qsum = 0.0;
+    if (valid) {
+      const float* mp = a.mass_part + i;
+      int p = p0;
+      for (; p + 8 <= p1; p += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = mp[(int64_t)(p + k) * N];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) qsum += (double)v[k];
+      }
+      for (; p < p1; ++p) qsum += (double)mp[(int64_t)p * N];
+    }
+    s_part[quarter][tid] = qsum;
+  }
+  __syncthreads();
+
   float score = 0.f;
   int pinned = 0;
-  if (valid) {
-    // fixed-order float64 sum of the partials; loads are issued 8 at a time so that
-    // enough of them are in flight
-    double msum = 0.0;
-    const float* mp = a.mass_part + i;
-    int p = 0;
-    for (; p + 8 <= a.n_parts; p += 8) {
-      float v[8];
+  if (valid && quarter == 0) {
+    double msum = s_part[0][tid];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = mp[(int64_t)(p + k) * N];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) msum += (double)v[k];
-    }
-    for (; p < a.n_parts; ++p) msum += (double)mp[(int64_t)p * N];
+    for (int q = 1; q < kEpiSplit; ++q) msum += s_part[q][tid];
     const float mass = (float)msum;
     if (a.mass) a.mass[i] = mass;
 
@@ -80,27 +97,30 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
   }
 
   if (a.item_shift == 0) {
-    if (valid) {
+    if (valid && quarter == 0) {
       a.item_score[i] = score;
       a.item_pinned[i] = (uint8_t)pinned;
     }
     return;
   }
   // page mode: pairwise reduction inside each aligned segment of item_tokens threads
-  s_sum[tid] = valid ? score : 0.f;
-  s_cnt[tid] = valid ? 1 : 0;
-  s_pin[tid] = pinned;
+  // (the first kEpiThreads threads; every thread reaches every barrier)
+  if (quarter == 0) {
+    s_sum[tid] = valid ? score : 0.f;
+    s_cnt[tid] = valid ? 1 : 0;
+    s_pin[tid] = pinned;
+  }
   __syncthreads();
   const int it = 1 << a.item_shift;
   for (int stride = 1; stride < it; stride <<= 1) {
-    if ((tid & (2 * stride - 1)) == 0) {
+    if (quarter == 0 && (tid & (2 * stride - 1)) == 0) {
       s_sum[tid] += s_sum[tid + stride];
       s_cnt[tid] += s_cnt[tid + stride];
       s_pin[tid] |= s_pin[tid + stride];
     }
     __syncthreads();
   }
-  if ((tid & (it - 1)) == 0 && s_cnt[tid] > 0) {
+  if (quarter == 0 && (tid & (it - 1)) == 0 && s_cnt[tid] > 0) {
     const int64_t page = i >> a.item_shift;
     a.item_score[page] = s_sum[tid] / (float)s_cnt[tid];
     a.item_pinned[page] = (uint8_t)(s_pin[tid] != 0);
@@ -111,7 +131,7 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
 
 hipError_t launch_epilogue(const EpilogueArgs& a, hipStream_t s) {
   const int64_t blocks = (a.n_tokens + kEpiThreads - 1) / kEpiThreads;
-  hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)blocks), dim3(kEpiThreads), 0, s, a);
+  hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)blocks), dim3(kEpiThreads * kEpiSplit), 0, s, a);
   return hipGetLastError();
 }
 

@@ -731,13 +731,27 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
   if (a.lse_in) {
     lse2 = (float)((double)a.lse_in[nat] * 1.4426950408889634);
   } else {
+    // partials are read 8 chunks at a time so that their loads are in flight together;
+    // the maximum and the chunk-ordered float64 sum are unchanged by the batching
     const float2* p = a.lse_part + (int64_t)lg * a.n_chunks * a.rows + row;
+    constexpr int kB = 8;
     float mx = -1e30f;
-    for (int ch = 0; ch < a.n_chunks; ++ch) mx = fmaxf(mx, p[(int64_t)ch * a.rows].x);
+    for (int ch0 = 0; ch0 < a.n_chunks; ch0 += kB) {
+      float x[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) x[u] = ch0 + u < a.n_chunks ? p[(int64_t)(ch0 + u) * a.rows].x : -1e30f;
+#pragma unroll
+      for (int u = 0; u < kB; ++u) mx = fmaxf(mx, x[u]);
+    }
     double sum = 0.0;
-    for (int ch = 0; ch < a.n_chunks; ++ch) {
-      const float2 v = p[(int64_t)ch * a.rows];
-      sum += (double)v.y * exp2((double)v.x - (double)mx);
+    for (int ch0 = 0; ch0 < a.n_chunks; ch0 += kB) {
+      float2 v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        v[u] = ch0 + u < a.n_chunks ? p[(int64_t)(ch0 + u) * a.rows] : make_float2(-1e30f, 0.f);
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (ch0 + u < a.n_chunks) sum += (double)v[u].y * exp2((double)v[u].x - (double)mx);
     }
     lse2 = (float)((double)mx + log2(sum));
   }
