@@ -187,6 +187,9 @@ def _select_case(n_items, item_tokens, n_tokens, budget, score, pinned, cap=None
     (100_000, [1.0, 2.0, 3.0], 0.05, 0.5, 0, False),
     (300_000, None, 0.3, 0.2, 0.001, True),        # pinned exceed the budget
     (62_500, None, 0.0, 0.002048, 0, False),
+    # more than 4,096 items per block: several load batches per block, a ragged last one
+    (1_000_000, None, 0.000132, 0.002048, 0.0001, True),
+    (600_001, [1.0, 2.0, 3.0], 0.01, 0.3, 0, False),   # ties at T spread over many blocks
 ])
 def test_select_token_mode(n, alphabet, pin_frac, budget_frac, nan, negz):
     s = synth.scores(n, seed=n, alphabet=alphabet, nan_frac=nan, neg_zero=negz)
