@@ -151,11 +151,29 @@ def pmc_summary(fetch_dir, write_dir, out_json):
                               f"WRITE_SIZE x{calib['WRITE_SIZE']:.4f}")
 
 
-def clock_summary(pmc_dir):
+def measured_mfma_busy():
+    """Executed MFMA busy share of the two scoring passes (SQ_VALU_MFMA_BUSY_CYCLES over the
+    cycles of all SIMDs) from the committed rocprofv3 counter run, per pass, or None for a
+    pass whose source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "mfma_busy.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        recs = json.load(f)
+    out = {}
+    for name in ("lse_pass", "mass_pass"):
+        rec = recs.get(name)
+        ok = rec and rec.get("source_hash") == source_hash(*rec.get("sources", []))
+        out[name] = round(rec["mfma_busy"], 4) if ok else None
+    return out
+
+
+def clock_summary(pmc_dir, out_json=None):
     """Effective core clock and MFMA busy share per kernel from a rocprofv3 --pmc run with
     GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES.  rocprofv3 sums GRBM_GUI_ACTIVE over the
     8 XCDs of the MI355X (a memory-only kernel reads 2.4 GHz with this factor); the MFMA
-    busy share divides by the cycles of all 1,024 SIMDs.  Returns a markdown table."""
+    busy share divides by the cycles of all 1,024 SIMDs.  Writes the scoring passes' shares
+    to out_json (with the source hash they were measured on) and returns a markdown table."""
     import csv
     import glob
     hits = glob.glob(os.path.join(pmc_dir, "**", "*_counter_collection.csv"), recursive=True)
@@ -168,6 +186,7 @@ def clock_summary(pmc_dir):
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     rows = ["| Kernel | Dispatches | Average (us) | Effective clock (GHz) | MFMA busy |",
             "|---|---|---|---|---|"]
+    busy = {}
     for needle in ("lse_pass_kernel", "mass_pass_kernel", "compact_kernel", "select_hist_kernel",
                    "epilogue_kernel", "lse_combine_kernel"):
         ds = [d for (k, _), d in per.items() if needle in k and "GRBM_GUI_ACTIVE" in d]
@@ -178,6 +197,14 @@ def clock_summary(pmc_dir):
         mfma = sum(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds) / len(ds)
         rows.append(f"| {needle} | {len(ds)} | {dur / 1e3:.1f} | {cyc / dur:.2f} | "
                     f"{mfma / (1024.0 * cyc):.1%} |")
+        name = {"lse_pass_kernel": "lse_pass", "mass_pass_kernel": "mass_pass"}.get(needle)
+        if name:
+            srcs = TRAFFIC_KERNELS[name][1]
+            busy[name] = {"mfma_busy": mfma / (1024.0 * cyc), "clock_ghz": cyc / dur, "avg_us": dur / 1e3,
+                          "dispatches": len(ds), "sources": srcs, "source_hash": source_hash(*srcs)}
+    if out_json and busy:
+        with open(out_json, "w") as fh:
+            json.dump(busy, fh, indent=1)
     return "\n".join(rows)
 
 
@@ -452,7 +479,8 @@ def main():
                          "in each directory) into profiles/traffic.json and print a table")
     ap.add_argument("--clock-summary", metavar="PMC_DIR",
                     help="print effective clock and MFMA busy share per kernel from a "
-                         "rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES run and exit")
+                         "rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES run, write the "
+                         "scoring passes' shares to profiles/mfma_busy.json and exit")
     ap.add_argument("--extras", action="store_true",
                     help="time the rows beyond the headline step (single-pass and group-maximum "
                          "scoring, reference store, LRFU, tail compaction, offload, the Mistral "
@@ -466,7 +494,7 @@ def main():
                           os.path.join(ROOT, "profiles", "traffic.json")))
         return
     if args.clock_summary:
-        print(clock_summary(args.clock_summary))
+        print(clock_summary(args.clock_summary, os.path.join(ROOT, "profiles", "mfma_busy.json")))
         return
     if args.extras:
         extras()
@@ -587,7 +615,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern[dom]["hbm_frac"], 4),
                      "traffic": traffic,
                      "mfma_tflops": round(kern[dom]["flops"] / (kern[dom]["ms"] * 1e-3) / 1e12, 1),
-                     "mfma_frac": round(kern[dom]["mfma_frac"], 4)},
+                     "mfma_frac": round(kern[dom]["mfma_frac"], 4),
+                     "mfma_busy_counter": measured_mfma_busy()},
         "stages_ms": {"lse_pass": round(t_lse, 4), "lse_combine": round(t_comb, 4),
                       "mass_pass": round(t_mass, 4), "epilogue": round(t_epi, 4),
                       "select": round(t_sel, 4), "compact_rerope": round(t_cmp, 4)},
