@@ -247,6 +247,11 @@ struct Ctx {
   }
 };
 
+template <int V>
+struct StageC {
+  static constexpr int value = V;
+};
+
 // --------------------------------------------------------------------------- pipeline
 // The tile loop shared by both passes.  Pass P provides mma(tile, half, acc) (the
 // logits of one 32-key half), consume<kMask>(acc, half_j0, half, cb) (the VALU work on
@@ -324,20 +329,31 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
     p.between(nt - 1, cb == 0 ? 2 : cb - 1);
   } else {
     f32x16 acc;
-    for (; t + kAhead < nf && t < nc; ++t) {
+    // Steady state, one step per ring stage (tile t uses stage t % kStages): every LDS
+    // fragment address is then a constant offset from a per-lane base, which saves the
+    // address arithmetic of each read (the two-set schedule above keeps a plain loop:
+    // unrolled, its register allocation spills).
+    auto step = [&](auto stage) -> bool {
+      constexpr int ST = decltype(stage)::value;
+      constexpr int STA = (ST + kStages - 1) % kStages;
+      if (!(t + kAhead < nf && t < nc)) return false;
       const int64_t tj = x.j0 + (int64_t)t * kTile;
-      const int sta = st == 0 ? kStages - 1 : st - 1;
-      x.issue_fast(t + kAhead, kt[sta], junk, ph);
+      x.issue_fast(t + kAhead, kt[STA], junk, ph);
       if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
-      p.mma(kt[st], 0, acc);
+      p.mma(kt[ST], 0, acc);
       p.template consume<false>(acc, tj, 0, cb);
-      p.mma(kt[st], 1, acc);
+      p.mma(kt[ST], 1, acc);
       p.template consume<false>(acc, tj + 32, 1, cb);
       x.wait_and_barrier(kAhead - 1);
       p.between(t, cb);
-      st = st == kStages - 1 ? 0 : st + 1;
+      ++t;
       cb = cb == 2 ? 0 : cb + 1;
+      return true;
+    };
+    static_assert(kStages == 4, "the unrolled steady loop has one step per stage");
+    while (step(StageC<0>{}) && step(StageC<1>{}) && step(StageC<2>{}) && step(StageC<3>{})) {
     }
+    st = t % kStages;
     for (; t < nt; ++t) {
       const int64_t tj = x.j0 + (int64_t)t * kTile;
       const int sta = st == 0 ? kStages - 1 : st - 1;
