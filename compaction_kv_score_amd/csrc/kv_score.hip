@@ -67,8 +67,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 // would conservatively wait for these loads before every LDS read, which would undo the
 // prefetch.  Completion is awaited explicitly with vmcnt before the barrier that
 // publishes a tile (all waits in this file are hand-placed for that reason).
-__device__ __forceinline__ void dma16(const void* src, const uint8_t* lds) {
-  const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)lds);
+// LDS byte address of a location in a __shared__ array (computed once per kernel: the
+// conversion from a generic pointer costs vector instructions).
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
+}
+
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
   // M0 carries the LDS destination; the previous M0 is restored so that the compiler's
   // own view of M0 stays valid.  The wait state separates the M0 write from its use.
@@ -92,7 +98,7 @@ struct Ctx {
   static constexpr bool kJunk = (kLoadsPerTile % NW) != 0;
 
   const ScoreArgs& a;
-  int lane, wv, chunk_id, rs, row0, g, layer, lg, n_tiles, slot_stride;
+  int lane, wv, chunk_id, rs, row0, g, layer, lg, n_tiles, n_full, slot_stride;
   int64_t j0, j1;
   const uint16_t* kbase;
   int fo0;                        // per-lane LDS byte offset of K fragment ks = 0; the
@@ -114,6 +120,7 @@ struct Ctx {
     j0 = (int64_t)chunk_id * a.chunk;
     j1 = j0 + a.chunk < a.n_tokens ? j0 + a.chunk : a.n_tokens;
     n_tiles = (int)((j1 - j0 + kTile - 1) / kTile);
+    n_full = a.page_shift >= 2 ? (int)((j1 - j0) / kTile) : 0;
     slot_stride = a.n_kv_heads * kHeadDim;
     kbase = a.k + (int64_t)layer * a.layer_stride + g * kHeadDim;
     // key row kk = 32*kb + lane%32 holds dims 16*ks + 8*(lane/32) in piece
@@ -155,9 +162,8 @@ struct Ctx {
     return kJunk && i >= kLoadsPerTile ? kLoadsPerTile - 1 : i;
   }
 
-  __device__ __forceinline__ bool uniform_tile(int t) const {
-    return a.page_shift >= 2 && j0 + (int64_t)(t + 1) * kTile <= j1;
-  }
+  // Tile t is full (all 64 keys before the chunk end) and its pages are wave-uniform.
+  __device__ __forceinline__ bool uniform_tile(int t) const { return t < n_full; }
 
   // Physical pages of this wave's loads of tile t (scalar loads, issued one iteration
   // before they are needed so that their latency hides behind a tile of work).
@@ -166,22 +172,23 @@ struct Ctx {
     if (!uniform_tile(t)) return;
     const int64_t tile_j0 = j0 + (int64_t)t * kTile;
 #pragma unroll
-    for (int m = 0; m < LPW; ++m) {
-      const int64_t page = (tile_j0 + 4 * load_slot(m)) >> a.page_shift;
-      ph[m] = bt ? bt[page] : (int32_t)page;
+    for (int m = 0; m < LPW; ++m) ph[m] = (int32_t)((tile_j0 + 4 * load_slot(m)) >> a.page_shift);
+    if (bt) {
+#pragma unroll
+      for (int m = 0; m < LPW; ++m) ph[m] = bt[ph[m]];
     }
   }
 
   // Loads of a full tile whose pages are wave-uniform (page size >= 4): the per-lane part
   // of every address is precomputed.
-  __device__ __forceinline__ void issue_fast(int t, uint8_t* stage, uint8_t* junk,
+  __device__ __forceinline__ void issue_fast(int t, uint32_t stage, uint32_t junk,
                                              const int32_t (&ph)[LPW]) const {
     const int64_t tile_j0 = j0 + (int64_t)t * kTile;
     const int64_t pmask = (1LL << a.page_shift) - 1;
 #pragma unroll
     for (int m = 0; m < LPW; ++m) {
       const int i = load_slot(m);
-      uint8_t* dst = kJunk && wv * LPW + m >= kLoadsPerTile ? junk : stage + i * 1024;
+      const uint32_t dst = kJunk && wv * LPW + m >= kLoadsPerTile ? junk : stage + i * 1024;
       const uint16_t* base =
           kbase + (int64_t)ph[m] * a.page_stride + ((tile_j0 + 4 * i) & pmask) * slot_stride;
       dma16(base + voff[m], dst);
@@ -192,7 +199,7 @@ struct Ctx {
   // rows 4i..4i+3; lane L carries piece (L%16) ^ (row%16) of row 4i + L/16, so it lands
   // in swizzled position.  Keys past the chunk end are clamped to the last valid key
   // (their logits are masked later).
-  __device__ void issue_tile(int t, uint8_t* stage, uint8_t* junk, const int32_t* __restrict__ bt,
+  __device__ void issue_tile(int t, uint32_t stage, uint32_t junk, const int32_t* __restrict__ bt,
                              const int32_t (&ph)[LPW]) const {
     const int64_t tile_j0 = j0 + (int64_t)t * kTile;
     if (uniform_tile(t)) {
@@ -201,7 +208,7 @@ struct Ctx {
 #pragma unroll
       for (int m = 0; m < LPW; ++m) {
         const int i = load_slot(m);
-        uint8_t* dst = kJunk && wv * LPW + m >= kLoadsPerTile ? junk : stage + i * 1024;
+        const uint32_t dst = kJunk && wv * LPW + m >= kLoadsPerTile ? junk : stage + i * 1024;
         const int row = 4 * i + (lane >> 4);
         const int c16 = (lane & 15) ^ (row & 15);
         const uint16_t* base =
@@ -213,7 +220,7 @@ struct Ctx {
 #pragma unroll
       for (int m = 0; m < LPW; ++m) {
         const int i = load_slot(m);
-        uint8_t* dst = kJunk && wv * LPW + m >= kLoadsPerTile ? junk : stage + i * 1024;
+        const uint32_t dst = kJunk && wv * LPW + m >= kLoadsPerTile ? junk : stage + i * 1024;
         const int row = 4 * i + (lane >> 4);
         const int c16 = (lane & 15) ^ (row & 15);
         int64_t j = tile_j0 + row;
@@ -268,6 +275,10 @@ template <bool kOverlap, int NW, class P>
 __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[kTileBytes],
                                           uint8_t* junk, const int32_t* __restrict__ bt) {
   const int nt = x.n_tiles;
+  // LDS addresses of the ring stages and the junk buffer, for the direct-to-LDS loads
+  const uint32_t kt0 = lds_addr(kt[0]);
+  const uint32_t jk = lds_addr(junk);
+  auto stage_addr = [&](int s) { return kt0 + (uint32_t)s * (uint32_t)kTileBytes; };
   // full tiles (all 64 keys before the chunk end) with wave-uniform pages
   const int nf = x.a.page_shift >= 2 ? (int)((x.j1 - x.j0) / kTile) : 0;
   // clean tiles: full and every key visible to every window row
@@ -278,7 +289,7 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
   int32_t ph[Ctx<NW>::LPW] = {};
   for (int t = 0; t < kAhead && t < nt; ++t) {
     x.fetch_pages(t, bt, ph);
-    x.issue_tile(t, kt[t], junk, bt, ph);
+    x.issue_tile(t, stage_addr(t), jk, bt, ph);
   }
   if (kAhead < nt) x.fetch_pages(kAhead, bt, ph);
   x.wait_and_barrier((nt < kAhead ? nt : kAhead) - 1);
@@ -294,7 +305,7 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
       const int st1 = st == kStages - 1 ? 0 : st + 1;
       const int sta = st == 0 ? kStages - 1 : st - 1;   // stage of tile t + kAhead
       const int cbp = cb == 0 ? 2 : cb - 1;
-      x.issue_fast(t + kAhead, kt[sta], junk, ph);
+      x.issue_fast(t + kAhead, stage_addr(sta), jk, ph);
       if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
       p.mma(kt[st], 1, acc1);
       p.template consume<false>(acc0, tj, 0, cb);
@@ -310,7 +321,7 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
       const int st1 = st == kStages - 1 ? 0 : st + 1;
       const int sta = st == 0 ? kStages - 1 : st - 1;
       const int cbp = cb == 0 ? 2 : cb - 1;
-      if (t + kAhead < nt) x.issue_tile(t + kAhead, kt[sta], junk, bt, ph);
+      if (t + kAhead < nt) x.issue_tile(t + kAhead, stage_addr(sta), jk, bt, ph);
       if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
       p.mma(kt[st], 1, acc1);
       if (masked(tj)) p.template consume<true>(acc0, tj, 0, cb);
@@ -338,7 +349,7 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
       constexpr int STA = (ST + kStages - 1) % kStages;
       if (!(t + kAhead < nf && t < nc)) return false;
       const int64_t tj = x.j0 + (int64_t)t * kTile;
-      x.issue_fast(t + kAhead, kt[STA], junk, ph);
+      x.issue_fast(t + kAhead, kt0 + STA * kTileBytes, jk, ph);
       if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
       p.mma(kt[ST], 0, acc);
       p.template consume<false>(acc, tj, 0, cb);
@@ -357,7 +368,7 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
     for (; t < nt; ++t) {
       const int64_t tj = x.j0 + (int64_t)t * kTile;
       const int sta = st == 0 ? kStages - 1 : st - 1;
-      if (t + kAhead < nt) x.issue_tile(t + kAhead, kt[sta], junk, bt, ph);
+      if (t + kAhead < nt) x.issue_tile(t + kAhead, stage_addr(sta), jk, bt, ph);
       if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
