@@ -398,12 +398,14 @@ struct LsePass {
   float c;
   int64_t last_key;               // last key this lane's row may see
   float m, l;
+  float nm;                       // -m, kept so that the exponent argument is one fma
 
   __device__ LsePass(const C& ctx, const bf16x8 (&q)[8]) : x(ctx), qf(q) {
     c = x.a.c;
     const int w = (x.row0 + x.wv * 32 + (x.lane & 31)) / x.a.row_stride;
     last_key = x.a.n_tokens - x.a.window + w;
     m = -1e30f;
+    nm = 1e30f;
     l = 0.f;
   }
 
@@ -432,14 +434,14 @@ struct LsePass {
     return h;
   }
 
-  // Sum of 2^(c*s - ref) over the half; hidden keys are excluded through their exponent
-  // argument (the accumulators are only read, never rewritten).
+  // Sum of 2^(c*s + nref) over the half, nref = -reference; hidden keys are excluded
+  // through their exponent argument (the accumulators are only read, never rewritten).
   template <bool kMask>
-  __device__ __forceinline__ float sums(const f32x16& acc, uint32_t h, float ref) const {
+  __device__ __forceinline__ float sums(const f32x16& acc, uint32_t h, float nref) const {
     float r[4];                                      // four running partial sums
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float arg = __builtin_fmaf(acc[i], c, -ref);
+      float arg = __builtin_fmaf(acc[i], c, nref);
       if (kMask && ((h >> i) & 1u)) arg = -INFINITY;
       const float e = exp2f_fast(arg);
       r[i & 3] = i < 4 ? e : r[i & 3] + e;
@@ -451,7 +453,7 @@ struct LsePass {
   template <bool kMask>
   __device__ __forceinline__ void consume(const f32x16& acc, int64_t half_j0, int, int) {
     const uint32_t h = kMask ? hidden(half_j0) : 0u;
-    float ts = sums<kMask>(acc, h, m);
+    float ts = sums<kMask>(acc, h, nm);
     if (__builtin_amdgcn_ballot_w64(!(ts <= 0x1p64f)) != 0) {
       float tmax = -INFINITY;
 #pragma unroll
@@ -460,7 +462,8 @@ struct LsePass {
       const float mn = fmaxf(m, tmax);
       l *= exp2f_fast(m - mn);
       m = mn;
-      ts = sums<kMask>(acc, h, m);
+      nm = -mn;
+      ts = sums<kMask>(acc, h, nm);
     }
     l += ts;
   }
