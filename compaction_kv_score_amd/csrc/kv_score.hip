@@ -181,6 +181,9 @@ struct Ctx {
 
   // Loads of a full tile whose pages are wave-uniform (page size >= 4): the per-lane part
   // of every address is precomputed.
+  // kScalar: page ids are re-read as scalars first (the stage-unrolled loops need this
+  // to keep the page arithmetic off the vector ALU).
+  template <bool kScalar = false>
   __device__ __forceinline__ void issue_fast(int t, uint32_t stage, uint32_t junk,
                                              const int32_t (&ph)[LPW]) const {
     const int64_t tile_j0 = j0 + (int64_t)t * kTile;
@@ -189,8 +192,9 @@ struct Ctx {
     for (int m = 0; m < LPW; ++m) {
       const int i = load_slot(m);
       const uint32_t dst = kJunk && wv * LPW + m >= kLoadsPerTile ? junk : stage + i * 1024;
+      const int32_t page = kScalar ? __builtin_amdgcn_readfirstlane(ph[m]) : ph[m];
       const uint16_t* base =
-          kbase + (int64_t)ph[m] * a.page_stride + ((tile_j0 + 4 * i) & pmask) * slot_stride;
+          kbase + (int64_t)page * a.page_stride + ((tile_j0 + 4 * i) & pmask) * slot_stride;
       dma16(base + voff[m], dst);
     }
   }
@@ -267,11 +271,15 @@ struct StageC {
 // through the fast page path; the remaining tiles take a general loop with every check
 // in place.  Column buffer cb of tile t is t % 3.
 //
-// kOverlap: each wave computes the logits of the next half while the previous half
+// P::kOverlap: each wave computes the logits of the next half while the previous half
 // goes through exp (two accumulator sets), so one wave keeps both the matrix core and
 // the vector ALU busy.  Otherwise each half runs MFMA then exp with one accumulator
 // set and the overlap comes from the other waves resident on the SIMD.
-template <bool kOverlap, int NW, class P>
+// P::kUnrollStages: the steady-state loop takes one step per ring stage (tile t uses
+// stage t % kStages), so every LDS fragment address is a constant offset from a
+// per-lane base and needs no address arithmetic (the LSE pass does without: unrolled,
+// its register allocation spills).
+template <int NW, class P>
 __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[kTileBytes],
                                           uint8_t* junk, const int32_t* __restrict__ bt) {
   const int nt = x.n_tiles;
@@ -297,9 +305,36 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
   // hidden keys exist only in halves that reach past the last clean key or the chunk end
   auto masked = [&](int64_t hj) { return hj + 31 > last_clean_key || hj + 32 > x.j1; };
   int t = 0, st = 0, cb = 0;  // tile, its LDS stage, its column buffer
-  if (kOverlap) {
+  if constexpr (P::kOverlap) {
     f32x16 acc0, acc1;
     p.mma(kt[0], 0, acc0);
+    if constexpr (P::kUnrollStages) {
+      // one step per ring stage (tile t uses stage t % kStages): every LDS fragment
+      // address is a constant offset from a per-lane base
+      auto step = [&](auto stage) -> bool {
+        constexpr int ST = decltype(stage)::value;
+        constexpr int ST1 = (ST + 1) % kStages, STA = (ST + kStages - 1) % kStages;
+        t = __builtin_amdgcn_readfirstlane(t);   // uniform: keeps the tile arithmetic scalar
+        if (!(t + kAhead < nf && t < nc)) return false;
+        const int64_t tj = x.j0 + (int64_t)t * kTile;
+        const int cbp = cb == 0 ? 2 : cb - 1;
+        x.template issue_fast<true>(t + kAhead, kt0 + STA * kTileBytes, jk, ph);
+        if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
+        p.mma(kt[ST], 1, acc1);
+        p.template consume<false>(acc0, tj, 0, cb);
+        x.wait_and_barrier(kAhead - 1);
+        if (t >= 1) p.between(t - 1, cbp);
+        p.mma(kt[ST1], 0, acc0);
+        p.template consume<false>(acc1, tj + 32, 1, cb);
+        ++t;
+        cb = cb == 2 ? 0 : cb + 1;
+        return true;
+      };
+      static_assert(kStages == 4, "the unrolled steady loop has one step per stage");
+      while (step(StageC<0>{}) && step(StageC<1>{}) && step(StageC<2>{}) && step(StageC<3>{})) {
+      }
+      st = t % kStages;
+    }
     for (; t + kAhead < nf && t < nc; ++t) {
       const int64_t tj = x.j0 + (int64_t)t * kTile;
       const int st1 = st == kStages - 1 ? 0 : st + 1;
@@ -393,6 +428,8 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
 template <int NW>
 struct LsePass {
   using C = Ctx<NW>;
+  static constexpr bool kOverlap = true;
+  static constexpr bool kUnrollStages = false;
   const C& x;
   const bf16x8 (&qf)[8];
   float c;
@@ -486,12 +523,6 @@ struct LsePass {
 // Two workgroups per CU need ceil(2*NW/4) waves per SIMD: 3 for five or six waves (at
 // most 168 VGPRs per lane), 4 for eight (at most 128).  amdgpu_waves_per_eu makes the
 // register allocator honour that; smaller workgroups are bound by LDS instead.
-#ifndef KVS_LSE_OVERLAP
-#define KVS_LSE_OVERLAP true
-#endif
-#ifndef KVS_MASS_OVERLAP
-#define KVS_MASS_OVERLAP false
-#endif
 
 template <int NW>
 __device__ __forceinline__ void lse_pass_body(const ScoreArgs& a, const int32_t* __restrict__ bt) {
@@ -502,7 +533,7 @@ __device__ __forceinline__ void lse_pass_body(const ScoreArgs& a, const int32_t*
   bf16x8 qf[8];
   x.load_queries(qf);
   LsePass<NW> p(x, qf);
-  run_tiles<KVS_LSE_OVERLAP>(x, p, kt, junk, bt);
+  run_tiles(x, p, kt, junk, bt);
 }
 
 template <int NW>
@@ -531,6 +562,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 template <int NW, int kMaxLog>
 struct MassPass {
   using C = Ctx<NW>;
+  // the sum keeps two accumulator sets (the group maximum's extra registers would spill)
+  static constexpr bool kOverlap = kMaxLog == 0;
+  static constexpr bool kUnrollStages = true;
   static constexpr int kColStride = 2 * NW + 1;     // floats per key (partials + pad)
   const C& x;
   const bf16x8 (&qf)[8];
@@ -596,20 +630,28 @@ struct MassPass {
   template <bool kMask>
   __device__ __forceinline__ void consume(const f32x16& acc, int64_t half_j0, int half, int cb) const {
     const uint32_t h = kMask ? hidden(half_j0) : 0u;
-    float nl[16];
-    load_nl(nl);
     float part;
     if constexpr (kMaxLog == 0) {
+      // -LSE2 read four rows at a time, to keep few registers live beside the second
+      // accumulator set
       float r[4];                                    // four running partial sums
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float arg = __builtin_fmaf(acc[i], c, nl[i]);
-        if (kMask && ((h >> i) & 1u)) arg = -INFINITY;
-        const float e = exp2f_fast(arg);
-        r[i & 3] = i < 4 ? e : r[i & 3] + e;
+      for (int g = 0; g < 4; ++g) {
+        const float4 v = *(const float4*)(nlw + 8 * g + 4 * (x.lane >> 5));
+        const float nv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * g + u;
+          float arg = __builtin_fmaf(acc[i], c, nv[u]);
+          if (kMask && ((h >> i) & 1u)) arg = -INFINITY;
+          const float e = exp2f_fast(arg);
+          r[u] = g == 0 ? e : r[u] + e;
+        }
       }
       part = (r[0] + r[1]) + (r[2] + r[3]);
     } else {
+      float nl[16];
+      load_nl(nl);
       float arg[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -695,7 +737,7 @@ __device__ __forceinline__ void mass_pass_body(const ScoreArgs& a, const int32_t
   bf16x8 qf[8];
   x.load_queries(qf);
   P p(x, qf, colp, nls);
-  run_tiles<KVS_MASS_OVERLAP>(x, p, kt, junk, bt);
+  run_tiles(x, p, kt, junk, bt);
 }
 
 template <int NW, int kMaxLog>
