@@ -461,13 +461,17 @@ struct LsePass {
 
   // Bit i set when element i is a key this lane's row must not see (past the chunk
   // end, or after the row's own position).
+  // Element i holds key base + off_i (base = half_j0 + 4*(lane/32), off_i = 8*(i/4) +
+  // i%4), and the row sees keys below min(chunk end, last_key + 1): one 32-bit limit.
   __device__ uint32_t hidden(int64_t half_j0) const {
+    const int64_t base = half_j0 + 4 * (x.lane >> 5);
+    int64_t lim = (x.j1 < last_key + 1 ? x.j1 : last_key + 1) - base;
+    lim = lim < 0 ? 0 : (lim > 32 ? 32 : lim);
+    const int l = (int)lim;
     uint32_t h = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t j = half_j0 + 8 * (i >> 2) + 4 * (x.lane >> 5) + (i & 3);
-      if (j >= x.j1 || j > last_key) h |= 1u << i;
-    }
+    for (int i = 0; i < 16; ++i)
+      if (8 * (i >> 2) + (i & 3) >= l) h |= 1u << i;
     return h;
   }
 
@@ -613,15 +617,21 @@ struct MassPass {
 
   // Bit i set when row i of this lane must not see its key (past the chunk end, or
   // after the row's own position).
+  // Row r (window query w = r / row_stride) sees key j when j <= N - W + w, i.e. when
+  // w >= d = j - (N - W), i.e. when r >= d * row_stride.  Element i holds row
+  // rbase + off_i (rbase = row0 + 32*wv + 4*(lane/32), off_i = 8*(i/4) + i%4), so one
+  // 32-bit limit decides all 16 elements (d is clamped to [0, W]: all rows see the key
+  // below 0, none of the real rows above W).
   __device__ uint32_t hidden(int64_t half_j0) const {
     const int64_t j = half_j0 + (x.lane & 31);
-    const int64_t first_partial_key = x.a.n_tokens - x.a.window;
+    if (j >= x.j1) return 0xFFFFu;
+    const int64_t d64 = j - (x.a.n_tokens - x.a.window);
+    const int d = d64 < 0 ? 0 : (d64 > x.a.window ? x.a.window : (int)d64);
+    const int lim = d * x.a.row_stride - (x.row0 + x.wv * 32 + 4 * (x.lane >> 5));
     uint32_t h = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int w = (x.row0 + x.wv * 32 + 8 * (i >> 2) + 4 * (x.lane >> 5) + (i & 3)) / x.a.row_stride;
-      if (j >= x.j1 || j > first_partial_key + w) h |= 1u << i;
-    }
+    for (int i = 0; i < 16; ++i)
+      if (8 * (i >> 2) + (i & 3) < lim) h |= 1u << i;
     return h;
   }
 
