@@ -17,9 +17,9 @@
 // one lane pair, so the max costs a few v_max and at most one cross-half shuffle, and
 // only one exponential per group is taken.
 //
-// Work decomposition: one workgroup per (layer, KV head, chunk of keys).  Its waves
-// each own 64 of the G*W rows and keep those rows' queries in registers as MFMA
-// operands for the whole chunk.  64-key tiles of K (16 KiB) stream into a ring of LDS
+// Work decomposition: one workgroup per (layer, KV head, chunk of keys, group of at
+// most 256 rows).  Its waves each own 32 of the rows and keep those rows' queries in
+// registers as MFMA operands for the whole chunk.  64-key tiles of K (16 KiB) stream into a ring of LDS
 // buffers by direct global->LDS 16-byte loads issued several tiles ahead, so HBM
 // latency hides behind tiles of work and no VGPRs stage the data.  Rows are stored
 // with an XOR swizzle of their 16-byte pieces, which keeps the loads coalesced (every
@@ -28,8 +28,9 @@
 //
 // Inside a tile each wave works on 32-key halves with two accumulator sets: it computes
 // the logits of one half (v_mfma_f32_32x32x16_bf16) while turning the previous half into
-// exponentials, and the two waves sharing a SIMD order these parts oppositely, so that
-// the matrix core and the vector ALU overlap instead of taking turns.  Logits stay in fp32 accumulators and are consumed in registers: nothing
+// exponentials, so that the matrix core and the vector ALU overlap instead of taking
+// turns (pass 2's group-maximum variant keeps one set and relies on the other waves of
+// the SIMD).  Logits stay in fp32 accumulators and are consumed in registers: nothing
 // of size rows x N is stored.
 //
 // Exponentials use exp2 with the scale folded into c = scale * log2(e).  Pass 1 keeps
