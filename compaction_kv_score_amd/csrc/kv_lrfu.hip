@@ -28,6 +28,8 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBlocks = 64;
 constexpr int kBins = 2048;
+// s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt not waited for
+constexpr int kVmcntZero = (7 << 4) | (15 << 8);
 
 __device__ __forceinline__ bool has_weight(float s) { return s > 0.f && s <= 3.402823466e38f; }
 
@@ -139,9 +141,16 @@ __global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pas
   }
   __syncthreads();
   for (int b = tid; b < kBins; b += kThreads) a.hist[(int64_t)blockIdx.x * kBins + b] = h[b];
-  __threadfence();
+  // Every wave waits for its own stores; then one thread makes the block's histogram
+  // visible device-wide (the release writes back the whole L2, so one per block
+  // suffices) and takes the ticket.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.st->ticket, 1u) == (uint32_t)gridDim.x - 1u;
+  if (tid == 0) {
+    __threadfence();
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);   // the write-back has completed
+    s_last = atomicAdd(&a.st->ticket, 1u) == (uint32_t)gridDim.x - 1u;
+  }
   __syncthreads();
   if (!s_last) return;
   __threadfence();

@@ -31,6 +31,8 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelMaxBlocks = 64;
 constexpr int kWaves = kSelThreads / 64;
 constexpr int kBins = kSelBins;
+// s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt not waited for
+constexpr int kVmcntZero = (7 << 4) | (15 << 8);
 
 __device__ __forceinline__ uint32_t order_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -130,9 +132,16 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
     a.counts[2 * blockIdx.x] = s_npin;
     a.counts[2 * blockIdx.x + 1] = s_nan;
   }
-  __threadfence();
+  // Every wave waits for its own histogram atomics to complete; then one thread makes
+  // the block's results visible device-wide (the release writes back the whole L2, so
+  // one per block suffices: one per wave cost ~7 us per pass) and takes the ticket.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.st->ticket, 1u) == (uint32_t)gridDim.x - 1u;
+  if (tid == 0) {
+    __threadfence();
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);   // the write-back has completed
+    s_last = atomicAdd(&a.st->ticket, 1u) == (uint32_t)gridDim.x - 1u;
+  }
   __syncthreads();
   if (!s_last) return;
   __threadfence();
