@@ -153,7 +153,9 @@ __global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pas
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  // acquire for wave 0, the only wave that reads shared data through the caches (the
+  // histograms below are read with cache-bypassing atomic loads)
+  if (threadIdx.x < 64) __threadfence();
 
   // ---- last block: global weighted histogram (blocks in order), then the digit
   const int nb = (int)gridDim.x;

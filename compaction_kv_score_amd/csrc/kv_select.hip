@@ -144,7 +144,9 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  // acquire for wave 0, the only wave that reads shared data through the caches (the
+  // histograms below are read with cache-bypassing atomic loads)
+  if (threadIdx.x < 64) __threadfence();
 
   // ---- last block: the global histogram of this pass, then the digit
   const int nb = (int)gridDim.x;
