@@ -261,16 +261,17 @@ __global__ __launch_bounds__(kSelThreads) void select_count_kernel(SelectArgs a)
   }
 }
 
-// Exclusive prefix of a per-thread flag over the block, in thread order; returns the
-// prefix and writes the block total.  Wavefront ballots inside waves, LDS across them.
-__device__ __forceinline__ uint32_t block_scan(bool flag, uint32_t* s_wave, uint32_t& total) {
+// Exclusive prefixes of two per-thread flags over the block in one pass (per-wave
+// counts packed as a | b << 16, at most 64 each).
+__device__ __forceinline__ void block_scan2(bool fa, bool fb, uint32_t* s_wave, uint32_t& ra, uint32_t& rb,
+                                            uint32_t& ta, uint32_t& tb) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const uint64_t bal = __builtin_amdgcn_ballot_w64(flag);
-  const uint64_t below = lane == 0 ? 0ull : (bal & (~0ull >> (64 - lane)));
-  const uint32_t in_wave = (uint32_t)__popcll(below);
-  if (lane == 0) s_wave[wv] = (uint32_t)__popcll(bal);
+  const uint64_t ba = __builtin_amdgcn_ballot_w64(fa);
+  const uint64_t bb = __builtin_amdgcn_ballot_w64(fb);
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  if (lane == 0) s_wave[wv] = (uint32_t)__popcll(ba) | ((uint32_t)__popcll(bb) << 16);
   __syncthreads();
   uint32_t before = 0, tot = 0;
   for (int w = 0; w < kWaves; ++w) {
@@ -279,8 +280,10 @@ __device__ __forceinline__ uint32_t block_scan(bool flag, uint32_t* s_wave, uint
     tot += c;
   }
   __syncthreads();
-  total = tot;
-  return before + in_wave;
+  ra = (before & 0xFFFFu) + (uint32_t)__popcll(ba & below);
+  rb = (before >> 16) + (uint32_t)__popcll(bb & below);
+  ta = tot & 0xFFFFu;
+  tb = tot >> 16;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) {
@@ -347,11 +350,15 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
         eq = key == T;
       }
     }
-    uint32_t eq_total;
-    const uint32_t eq_rank = block_scan(eq, s_wave, eq_total);
-    const bool kept = def || (eq && eq_before + (int64_t)eq_rank < k_rem);
-    uint32_t kept_total;
-    const uint32_t out_rank = block_scan(kept, s_wave, kept_total);
+    // def and eq are exclusive; the first max(0, k_rem - eq_before) ties of this round
+    // (in index order) are taken, so one scan of both flags gives every output rank
+    uint32_t def_rank, eq_rank, def_total, eq_total;
+    block_scan2(def, eq, s_wave, def_rank, eq_rank, def_total, eq_total);
+    const int64_t ties_left = k_rem - eq_before > 0 ? k_rem - eq_before : 0;
+    const bool kept = def || (eq && (int64_t)eq_rank < ties_left);
+    const uint32_t out_rank = def_rank + (uint32_t)((int64_t)eq_rank < ties_left ? eq_rank : ties_left);
+    const uint32_t kept_total =
+        def_total + (uint32_t)((int64_t)eq_total < ties_left ? eq_total : ties_left);
     if (kept) {
       const int64_t out = (kept_before + out_rank) * it;
       const int64_t t0 = i * it;
