@@ -39,6 +39,9 @@ int32_t check_device() {
   return v == 1 ? KV_OK : KV_EUNSUPPORTED;
 }
 
+// Scoring workgroups resident at once on an MI355X: two per CU (LDS-bound) x 256 CUs.
+constexpr int64_t kResidentGroups = 512;
+
 int log2_exact(int64_t v) {
   if (v <= 0 || (v & (v - 1)) != 0) return -1;
   int s = 0;
@@ -90,8 +93,27 @@ int32_t score_layout(const kv_cache_desc* c, const kv_score_params* p, ScoreLayo
   // small enough that the grid has thousands of workgroups
   const int n_rsplit = (int)((rows + kRowsPerGroup - 1) / kRowsPerGroup);
   const int64_t units = (int64_t)c->n_layers * c->n_kv_heads;
+  const int64_t n = c->n_tokens;
   int64_t chunk = 4096;
-  while (chunk > 256 && units * n_rsplit * ((c->n_tokens + chunk - 1) / chunk) < 2048) chunk >>= 1;
+  while (chunk > 256 && units * n_rsplit * ((n + chunk - 1) / chunk) < 2048) chunk >>= 1;
+  if (chunk == 4096) {
+    // Enough work to choose a chunk of 2,048-8,192 keys whose grid fills whole rounds of
+    // the chip's resident workgroups, so that the last round does not run mostly empty:
+    // the largest chunk that keeps 99% of the slots busy on average, else the best fill.
+    double best = 0.0;
+    for (int64_t nch = (n + 8191) / 8192; nch <= (n + 2047) / 2048; ++nch) {
+      const int64_t ch = ((n + nch - 1) / nch + kTile - 1) / kTile * kTile;
+      const int64_t wgs = units * n_rsplit * ((n + ch - 1) / ch);
+      if (wgs < 2048) continue;
+      const int64_t rounds = (wgs + kResidentGroups - 1) / kResidentGroups;
+      const double fill = (double)units * n_rsplit * n / ((double)kResidentGroups * rounds * ch);
+      if (fill > best) {
+        best = fill;
+        chunk = ch;
+      }
+      if (fill >= 0.99) break;
+    }
+  }
   L->rows = (int)rows;
   L->n_rsplit = n_rsplit;
   L->group = group;
