@@ -259,7 +259,6 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   ca.window = p->window;
   ca.row_stride = L.row_stride;
   ca.n_lg = n_lg;
-  ca.c = c2;
   ca.lse_in = p->lse_in;
   ca.lse2 = (float*)(w + L.off_lse2);
   ca.lse_out = p->lse;

@@ -51,7 +51,6 @@ hipError_t launch_score_pass(const ScoreArgs& a, bool pass2, hipStream_t s);
 struct CombineArgs {
   const float2* lse_part;
   int n_chunks, rows, n_kv_heads, n_q_heads, group, window, n_lg, row_stride;
-  float c;
   const float* lse_in;          // optional natural-log LSE input [L][Hq][W]
   float* lse2;                  // [L*Hkv][rows]
   float* lse_out;               // optional [L][Hq][W]

@@ -63,17 +63,17 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16-byte global -> LDS load of every lane: lane L's 16 bytes land at lds + 16*L.  It is
-// issued from inline assembly so that the compiler does not track it: otherwise it
-// would conservatively wait for these loads before every LDS read, which would undo the
-// prefetch.  Completion is awaited explicitly with vmcnt before the barrier that
-// publishes a tile (all waits in this file are hand-placed for that reason).
 // LDS byte address of a location in a __shared__ array (computed once per kernel: the
 // conversion from a generic pointer costs vector instructions).
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
 }
 
+// 16-byte global -> LDS load of every lane: lane L's 16 bytes land at lds + 16*L.  It is
+// issued from inline assembly so that the compiler does not track it: otherwise it
+// would conservatively wait for these loads before every LDS read, which would undo the
+// prefetch.  Completion is awaited explicitly with vmcnt before the barrier that
+// publishes a tile (all waits in this file are hand-placed for that reason).
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   const uint32_t dst = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
@@ -288,8 +288,7 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
   const uint32_t kt0 = lds_addr(kt[0]);
   const uint32_t jk = lds_addr(junk);
   auto stage_addr = [&](int s) { return kt0 + (uint32_t)s * (uint32_t)kTileBytes; };
-  // full tiles (all 64 keys before the chunk end) with wave-uniform pages
-  const int nf = x.a.page_shift >= 2 ? (int)((x.j1 - x.j0) / kTile) : 0;
+  const int nf = x.n_full;  // full tiles (all 64 keys before the chunk end), wave-uniform pages
   // clean tiles: full and every key visible to every window row
   const int64_t last_clean_key = x.a.n_tokens - x.a.window;
   const int64_t clean_end = x.j1 < last_clean_key + 1 ? x.j1 : last_clean_key + 1;
@@ -378,8 +377,7 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
     f32x16 acc;
     // Steady state, one step per ring stage (tile t uses stage t % kStages): every LDS
     // fragment address is then a constant offset from a per-lane base, which saves the
-    // address arithmetic of each read (the two-set schedule above keeps a plain loop:
-    // unrolled, its register allocation spills).
+    // address arithmetic of each read.
     auto step = [&](auto stage) -> bool {
       constexpr int ST = decltype(stage)::value;
       constexpr int STA = (ST + kStages - 1) % kStages;
