@@ -508,8 +508,8 @@ def main():
         print(json.dumps({"copy_bytes": a.numel() * 2, "launches": 3}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the per-token mass would be all-reduced across ranks; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(across GPUs the per-token mass would be all-reduced over ranks)", file=sys.stderr)
         sys.exit(2)
     if args.config != 3:
         print("only workload 3 (Qwen3-8B, N=100K) is a bench line", file=sys.stderr)
