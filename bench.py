@@ -129,7 +129,7 @@ def pmc_summary(fetch_dir, write_dir, out_json):
             vals = [v for k, vs in bench.items() if needle in k for v in vs]
             if vals:
                 res.setdefault(name, {})[counter] = sum(vals) / len(vals) * scale
-    w = __import__("synth").workload(3)
+    w = __import__("synth").workload("qwen3-8b-n100k")
     alg = {"lse_pass": w.n_layers * w.n_tokens * w.n_kv_heads * w.head_dim * 2
                        + w.n_layers * w.window * w.n_q_heads * w.head_dim * 2}
     alg["mass_pass"] = alg["lse_pass"]
@@ -216,8 +216,8 @@ def extras(steps=5, warmup=2):
       f3: LRFU keep-score update over 100K entries, in-place tail compaction of 2,048;
       f4: gather of 16,384 evicted rows on the device, and offload of 16,384 rows to
           pinned host memory (PCIe-bound, chunks of 1,024);
-      cfg4: Mistral-7B 131,072-token in-place segment eviction + re-rotation;
-      cfg5: the full step (MemDecay page scoring, select, compaction) at 1,000,000 tokens.
+      Mistral-7B 131,072-token in-place segment eviction + re-rotation;
+      Qwen3-8B at 1,000,000 tokens: the full step (MemDecay page scoring, select, compaction).
     Prints one JSON line."""
     import numpy as np
     import compaction_kv_score_amd as kv
@@ -245,7 +245,7 @@ def extras(steps=5, warmup=2):
         print(f"[extras] {msg}", file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- Qwen3-8B 100K
-    w = synth.workload(3)
+    w = synth.workload("qwen3-8b-n100k")
     N, NL, HKV, D, W, B = w.n_tokens, w.n_layers, w.n_kv_heads, w.head_dim, w.window, w.budget_tokens
     kvb = w.kv_bytes_per_token
     log("qwen3-8b-n100k inputs")
@@ -342,7 +342,7 @@ def extras(steps=5, warmup=2):
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- Mistral-7B segment
-    w4 = synth.workload(4)
+    w4 = synth.workload("mistral-7b-n131072-segment")
     log("mistral-7b-n131072 inputs")
     k4, v4, _ = synth.kv_cache(w4, seed=0, device=dev)
     c4 = kv.PagedCache(k4, v4, w4.n_tokens)
@@ -352,15 +352,15 @@ def extras(steps=5, warmup=2):
                                                      rope_theta=w4.rope_theta), n=3, w=1)
     moved4 = n_keep4 - w4.segment_prefix
     b4 = 2 * moved4 * w4.kv_bytes_per_token
-    out["cfg4_segment_inplace"] = {"workload": w4.name, "ms": round(t4, 3), "evicted": e4, "moved_tokens": moved4,
+    out["mistral7b_n131072_segment_inplace"] = {"workload": w4.name, "ms": round(t4, 3), "evicted": e4, "moved_tokens": moved4,
                                    "bytes": b4, "GBps": round(b4 / (t4 * 1e-3) / 1e9, 1),
                                    "hbm_frac": round(b4 / (t4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    log(f"cfg4: {out['cfg4_segment_inplace']}")
+    log(f"segment: {out['mistral7b_n131072_segment_inplace']}")
     del k4, v4, c4
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- Qwen3-8B 1M tokens
-    w5 = synth.workload(5)
+    w5 = synth.workload("qwen3-8b-n1m")
     N5, B5 = w5.n_tokens, w5.budget_tokens
     log("qwen3-8b-n1m inputs (147 GB)")
     k5, v5, _ = synth.kv_cache(w5, seed=0, device=dev,
@@ -415,14 +415,14 @@ def extras(steps=5, warmup=2):
             stage["compact"] += hip.ms(e_cmp[0], e_cmp[1]) / 3
     ms5 = sum(tsteps) / len(tsteps)
     kb5 = w5.n_layers * N5 * w5.n_kv_heads * w5.head_dim * 2
-    out["cfg5_full_step"] = {"workload": w5.name, "ms_per_step": round(ms5, 3),
+    out["qwen3_8b_n1m_full_step"] = {"workload": w5.name, "ms_per_step": round(ms5, 3),
                              "KV_tokens_per_s": round(N5 / (ms5 * 1e-3), 1), "n_keep": int(nk5.item()),
                              "status": int(status5.item()),
                              "stages_ms": {a: round(b, 3) for a, b in stage.items()},
                              "scoring_pass_GBps": {
                                  "lse_pass": round(kb5 / (stage["lse_pass"] * 1e-3) / 1e9, 1),
                                  "mass_pass": round(kb5 / (stage["mass_pass"] * 1e-3) / 1e9, 1)}}
-    log(f"cfg5: {out['cfg5_full_step']}")
+    log(f"1M step: {out['qwen3_8b_n1m_full_step']}")
     print(json.dumps({"extras": out, "n_gpus": 1, "data": "synthetic"}), flush=True)
 
 
@@ -438,7 +438,7 @@ def cpu_baseline(w, layers):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count() or 1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    ws = synth.workload(3, n_layers=layers)
+    ws = synth.workload("qwen3-8b-n100k", n_layers=layers)
     k, v, _ = synth.kv_cache(ws, seed=0)
     q = synth.window_queries(ws, seed=0)
     span_id, next_use = synth.spans(ws, seed=0)
@@ -471,7 +471,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, help="workload number (3: Qwen3-8B, N=100K)")
+    ap.add_argument("--workload", default="qwen3-8b-n100k", help="workload name (the bench line: qwen3-8b-n100k)")
     ap.add_argument("--cpu-layers", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -511,8 +511,8 @@ def main():
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(across GPUs the per-token mass would be all-reduced over ranks)", file=sys.stderr)
         sys.exit(2)
-    if args.config != 3:
-        print("only workload 3 (Qwen3-8B, N=100K) is a bench line", file=sys.stderr)
+    if args.workload != "qwen3-8b-n100k":
+        print("only the qwen3-8b-n100k workload (Qwen3-8B, N=100K) is a bench line", file=sys.stderr)
         sys.exit(2)
 
     import compaction_kv_score_amd as kv
@@ -520,7 +520,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = synth.workload(args.config)
+    w = synth.workload(args.workload)
     N, NL, HKV, HQ, D, W = w.n_tokens, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.window
     B = w.budget_tokens
     print(f"[bench] generating {w.name}: {N} tokens x {w.kv_bytes_per_token} B", file=sys.stderr, flush=True)

@@ -71,30 +71,29 @@ class Workload:
         return self.n_layers * self.n_kv_heads * self.head_dim * 2 * 2
 
 
-def workload(cfg: int, **override) -> Workload:
-    """The five workloads by number; keyword overrides shrink them for tests."""
-    if cfg == 1:
-        w = Workload("qwen2.5-1.5b-1layer-n512", 1, 12, 2, 128, 512, 32, 16, 1e6,
-                     "memdecay", 16, 128, system_prefix=32)
-    elif cfg == 2:
-        w = Workload("qwen2.5-1.5b-n2048", 28, 12, 2, 128, 2048, 64, 16, 1e6,
-                     "memdecay", 16, 512, system_prefix=128)
-    elif cfg == 3:
-        w = Workload("qwen3-8b-n100k", 36, 32, 8, 128, 100_000, 64, 16, 1e6,
-                     "h2o", 1, 2048, n_sink=4, n_recent=128, n_spans=200,
-                     renumber=True, limit=8192)
-    elif cfg == 4:
-        w = Workload("mistral-7b-n131072-segment", 32, 32, 8, 128, 131_072, 0, 16, 1e4,
-                     "segment", 1, 0, segment_prefix=16_384, segment_frac=0.3,
-                     renumber=True)
-    elif cfg == 5:
-        w = Workload("qwen3-8b-n1m", 36, 32, 8, 128, 1_000_000, 64, 16, 1e6,
-                     "memdecay", 16, 2048, system_prefix=128, n_sink=4, n_recent=128,
-                     n_spans=200, renumber=True, limit=8192,
-                     region_span_log_uniform=True, span_len_min=64, span_len_max=4096)
-    else:
-        raise ValueError(cfg)
-    return dataclasses.replace(w, **override)
+WORKLOADS = {w.name: w for w in (
+    Workload("qwen2.5-1.5b-1layer-n512", 1, 12, 2, 128, 512, 32, 16, 1e6,
+             "memdecay", 16, 128, system_prefix=32),
+    Workload("qwen2.5-1.5b-n2048", 28, 12, 2, 128, 2048, 64, 16, 1e6,
+             "memdecay", 16, 512, system_prefix=128),
+    Workload("qwen3-8b-n100k", 36, 32, 8, 128, 100_000, 64, 16, 1e6,
+             "h2o", 1, 2048, n_sink=4, n_recent=128, n_spans=200,
+             renumber=True, limit=8192),
+    Workload("mistral-7b-n131072-segment", 32, 32, 8, 128, 131_072, 0, 16, 1e4,
+             "segment", 1, 0, segment_prefix=16_384, segment_frac=0.3,
+             renumber=True),
+    Workload("qwen3-8b-n1m", 36, 32, 8, 128, 1_000_000, 64, 16, 1e6,
+             "memdecay", 16, 2048, system_prefix=128, n_sink=4, n_recent=128,
+             n_spans=200, renumber=True, limit=8192,
+             region_span_log_uniform=True, span_len_min=64, span_len_max=4096),
+)}
+
+
+def workload(name: str, **override) -> Workload:
+    """A workload by its name (model shape, token count); keyword overrides shrink it for tests."""
+    if name not in WORKLOADS:
+        raise ValueError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)}")
+    return dataclasses.replace(WORKLOADS[name], **override)
 
 
 def _gen(seed: int, stream: int, device) -> torch.Generator:

@@ -14,7 +14,7 @@ DEV = "cuda:0"
 
 
 def test_select_and_compact_in_a_graph():
-    w = synth.workload(3, n_tokens=20_000, n_layers=4)
+    w = synth.workload("qwen3-8b-n100k", n_tokens=20_000, n_layers=4)
     k, v, _ = synth.kv_cache(w, seed=3, device=DEV)
     N, B = w.n_tokens, w.budget_tokens
     score = torch.empty(N, device=DEV)
@@ -91,7 +91,7 @@ def test_lrfu_in_a_graph():
 
 
 def test_score_in_a_graph():
-    w = synth.workload(1, n_tokens=8000, window=64, n_q_heads=32, n_kv_heads=8, n_layers=2)
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=8000, window=64, n_q_heads=32, n_kv_heads=8, n_layers=2)
     k, v, bt = synth.kv_cache(w, seed=4, device=DEV, paged_shuffle=True, extra_pages=1)
     q = synth.window_queries(w, seed=4, device=DEV)
     N = w.n_tokens

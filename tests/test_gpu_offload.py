@@ -26,7 +26,7 @@ def _logical(t, bt, n):
     (9, 4, 2000, 1500, 100, 400, True),     # 576 chunk pairs per token: three workgroups each
 ])
 def test_gather_evicted_parity(nl, hkv, n, n_keep, first, count, shuffle):
-    w = synth.workload(2, n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n)
+    w = synth.workload("qwen2.5-1.5b-n2048", n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n)
     k, v, bt = synth.kv_cache(w, seed=n + n_keep, device=DEV, paged_shuffle=shuffle, extra_pages=2)
     rng = np.random.default_rng(n)
     keep = np.sort(rng.choice(n, n_keep, replace=False))
@@ -49,7 +49,7 @@ def test_gather_evicted_parity(nl, hkv, n, n_keep, first, count, shuffle):
 @pytest.mark.parametrize("n,n_keep,chunk", [(3000, 2048, 1024), (5000, 100, 1024), (700, 0, 256), (2048, 2048, 64)])
 def test_offload_evicted_to_pinned_host(n, n_keep, chunk):
     nl, hkv = 3, 2
-    w = synth.workload(2, n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n)
+    w = synth.workload("qwen2.5-1.5b-n2048", n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n)
     k, v, bt = synth.kv_cache(w, seed=n, device=DEV, paged_shuffle=True, extra_pages=1)
     rng = np.random.default_rng(n + 1)
     keep = np.sort(rng.choice(n, n_keep, replace=False))

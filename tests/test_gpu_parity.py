@@ -69,7 +69,7 @@ def _paged_to_logical(t, bt, pg, n):
     (5, 8, 600, 150, True, 3, 1e6),     # 320 items per token: two workgroups of 160
 ])
 def test_compact_rerope_parity(nl, hkv, n, n_keep, shuffle, base, theta):
-    w = synth.workload(2, n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n)
+    w = synth.workload("qwen2.5-1.5b-n2048", n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n)
     k, v, bt = synth.kv_cache(w, seed=n, device=DEV, paged_shuffle=shuffle, extra_pages=3)
     g = torch.Generator().manual_seed(n + 1)
     keep = torch.sort(torch.randperm(n, generator=g)[:n_keep])[0].to(torch.int32)
@@ -111,7 +111,7 @@ def test_compact_rerope_parity(nl, hkv, n, n_keep, shuffle, base, theta):
 
 
 def test_compact_respects_device_count():
-    w = synth.workload(1)
+    w = synth.workload("qwen2.5-1.5b-1layer-n512")
     k, v, _ = synth.kv_cache(w, seed=1, device=DEV)
     keep = torch.arange(0, 512, 4, dtype=torch.int32, device=DEV)
     n_keep = torch.tensor([50], dtype=torch.int64, device=DEV)
@@ -135,7 +135,7 @@ def test_compact_respects_device_count():
     (9, 2000, 64, 0.3, 5, 1e6, True),  # 576 items per token: three workgroups; prefix shifted
 ])
 def test_segment_inplace_parity(nl, n, prefix, frac, base, theta, shuffle):
-    w = synth.workload(4, n_layers=nl, n_tokens=n)
+    w = synth.workload("mistral-7b-n131072-segment", n_layers=nl, n_tokens=n)
     k, v, bt = synth.kv_cache(w, seed=n, device=DEV, paged_shuffle=shuffle, extra_pages=2)
     n_keep, e = kv.kv_select_segment(n, prefix, int(frac * n), 16)
     keep = O.select_segment(n, prefix, int(frac * n), 16)
@@ -275,17 +275,17 @@ def _compare_memdecay(w, q, k_logical, st0, dev_state, got, rho, alpha, tau, dt_
     return ref, boundary
 
 
-@pytest.mark.parametrize("cfg,over,shuffle", [
-    (1, {}, False),
-    (1, {}, True),
-    (2, {}, True),
-    (1, dict(n_tokens=1000, window=37, n_q_heads=6, n_kv_heads=2, n_layers=2), True),
-    (1, dict(n_tokens=77, window=77, n_q_heads=4, n_kv_heads=4, n_layers=1, system_prefix=5), False),
-    (1, dict(n_tokens=5000, window=64, n_q_heads=32, n_kv_heads=8, n_layers=2, system_prefix=64), True),
-    (1, dict(n_tokens=9000, window=16, n_q_heads=64, n_kv_heads=2, n_layers=1), False),
+@pytest.mark.parametrize("name,over,shuffle", [
+    ("qwen2.5-1.5b-1layer-n512", {}, False),
+    ("qwen2.5-1.5b-1layer-n512", {}, True),
+    ("qwen2.5-1.5b-n2048", {}, True),
+    ("qwen2.5-1.5b-1layer-n512", dict(n_tokens=1000, window=37, n_q_heads=6, n_kv_heads=2, n_layers=2), True),
+    ("qwen2.5-1.5b-1layer-n512", dict(n_tokens=77, window=77, n_q_heads=4, n_kv_heads=4, n_layers=1, system_prefix=5), False),
+    ("qwen2.5-1.5b-1layer-n512", dict(n_tokens=5000, window=64, n_q_heads=32, n_kv_heads=8, n_layers=2, system_prefix=64), True),
+    ("qwen2.5-1.5b-1layer-n512", dict(n_tokens=9000, window=16, n_q_heads=64, n_kv_heads=2, n_layers=1), False),
 ])
-def test_score_memdecay_parity(cfg, over, shuffle):
-    w = synth.workload(cfg, **over)
+def test_score_memdecay_parity(name, over, shuffle):
+    w = synth.workload(name, **over)
     k, v, bt, q = _make_score_inputs(w, seed=11 + w.n_tokens, shuffle=shuffle)
     st0 = _memdecay_state(w, seed=w.n_tokens)
     dev_state = {key: t.clone() for key, t in st0.items()}
@@ -298,8 +298,8 @@ def test_score_memdecay_parity(cfg, over, shuffle):
 
 
 def test_score_memdecay_sixteen_steps():
-    """State carried across 16 scoring steps with fresh window queries (config 1)."""
-    w = synth.workload(1)
+    """State carried across 16 scoring steps with fresh window queries (Qwen2.5-1.5B shape, 512 tokens)."""
+    w = synth.workload("qwen2.5-1.5b-1layer-n512")
     k, v, bt, _ = _make_score_inputs(w, seed=5, shuffle=True)
     st = _memdecay_state(w, seed=5)
     dev = {key: t.to(DEV) for key, t in st.items()}
@@ -328,7 +328,7 @@ def test_score_memdecay_sixteen_steps():
     (dict(n_tokens=10_000, n_layers=1, n_spans=200), False),
 ])
 def test_score_h2o_foresight_parity(over, shuffle):
-    w = synth.workload(3, **over)
+    w = synth.workload("qwen3-8b-n100k", **over)
     k, v, bt, q = _make_score_inputs(w, seed=w.n_tokens, shuffle=shuffle)
     span_id, next_use = synth.spans(w, seed=3, p_needed=0.2)
     accum = synth.h2o_state(w, seed=3)
@@ -349,7 +349,7 @@ def test_score_h2o_foresight_parity(over, shuffle):
 
 def test_score_with_supplied_lse():
     """Single-pass mode: LSE given by the attention backend (ActKV Sec. 7.1)."""
-    w = synth.workload(1, n_tokens=3000, n_layers=2, window=48)
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=3000, n_layers=2, window=48)
     k, v, bt, q = _make_score_inputs(w, seed=9, shuffle=True)
     kl = _paged_to_logical(k, bt, 16, w.n_tokens)
     mass, lse = O.attention_mass(np64(q), kl)
@@ -372,7 +372,7 @@ def test_score_with_supplied_lse():
 def test_score_max_group_parity(hq, hkv, window, n_tokens, n_layers):
     """ActKV's aggregation (Sec. 7.1, Algorithm 3): per KV head the maximum over its
     query heads of exp(s - LSE), against the oracle; MemDecay divides by L*Hkv*W."""
-    w = synth.workload(1, n_tokens=n_tokens, window=window, n_q_heads=hq, n_kv_heads=hkv,
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=n_tokens, window=window, n_q_heads=hq, n_kv_heads=hkv,
                        n_layers=n_layers)
     k, v, bt, q = _make_score_inputs(w, seed=31 + n_tokens, shuffle=True)
     st0 = _memdecay_state(w, seed=n_tokens)
@@ -401,7 +401,7 @@ def test_score_max_group_parity(hq, hkv, window, n_tokens, n_layers):
 @pytest.mark.parametrize("aggregate,shift", [("sum", 0.0), ("max_group", 0.0), ("max_group", 0.3)])
 def test_score_supplied_lse_both_modes(aggregate, shift):
     """A supplied LSE is used as given (ActKV Sec. 7.1): also when it is not the keys' own."""
-    w = synth.workload(1, n_tokens=2600, n_layers=2, window=40, n_q_heads=12, n_kv_heads=4)
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=2600, n_layers=2, window=40, n_q_heads=12, n_kv_heads=4)
     k, v, bt, q = _make_score_inputs(w, seed=17, shuffle=True)
     kl = _paged_to_logical(k, bt, 16, w.n_tokens)
     _, lse = O.attention_mass(np64(q), kl)
@@ -419,7 +419,7 @@ def test_score_supplied_lse_both_modes(aggregate, shift):
 def test_score_page_sizes(ps):
     """Every supported page size: the scoring kernels take the per-lane address path
     below 4 tokens per page and wave-uniform pages from 4 on."""
-    w = synth.workload(1, n_tokens=3000, window=40, n_q_heads=8, n_kv_heads=2, n_layers=2, page_size=ps)
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=3000, window=40, n_q_heads=8, n_kv_heads=2, n_layers=2, page_size=ps)
     k, v, bt = synth.kv_cache(w, seed=ps, device="cpu", paged_shuffle=True, extra_pages=2)
     q = synth.window_queries(w, seed=ps)
     acc = torch.zeros(w.n_tokens, device=DEV)
@@ -434,7 +434,7 @@ def test_score_page_sizes(ps):
 @pytest.mark.parametrize("src_ps,dst_ps", [(1, 1024), (1024, 1), (2, 64), (64, 4)])
 def test_compact_page_sizes(src_ps, dst_ps):
     nl, hkv, n, n_keep = 2, 2, 2500, 700
-    w = synth.workload(2, n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n, page_size=src_ps)
+    w = synth.workload("qwen2.5-1.5b-n2048", n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n, page_size=src_ps)
     k, v, bt = synth.kv_cache(w, seed=src_ps + dst_ps, device=DEV, paged_shuffle=True, extra_pages=2)
     g = torch.Generator().manual_seed(src_ps * 7 + dst_ps)
     keep = torch.sort(torch.randperm(n, generator=g)[:n_keep])[0].to(torch.int32)
@@ -458,8 +458,8 @@ def test_compact_page_sizes(src_ps, dst_ps):
 
 
 def test_pipeline_end_to_end_config2():
-    """score -> select -> compact on the GPU against the oracle pipeline (config 2)."""
-    w = synth.workload(2)
+    """score -> select -> compact on the GPU against the oracle pipeline (Qwen2.5-1.5B, 28 layers, 2,048 tokens)."""
+    w = synth.workload("qwen2.5-1.5b-n2048")
     k, v, bt, q = _make_score_inputs(w, seed=21, shuffle=True)
     st0 = _memdecay_state(w, seed=21)
     dev = {key: t.to(DEV) for key, t in st0.items()}
@@ -506,7 +506,7 @@ def test_pipeline_end_to_end_config2():
 
 @pytest.fixture(scope="module")
 def qwen3_100k():
-    w = synth.workload(3)
+    w = synth.workload("qwen3-8b-n100k")
     k, v, _ = synth.kv_cache(w, seed=0, device=DEV)
     q = synth.window_queries(w, seed=0, device=DEV)
     yield w, k, v, q
@@ -543,7 +543,7 @@ def test_full_size_qwen3_100k_score_properties(qwen3_100k):
 def test_full_size_qwen3_100k_two_layer_mass(qwen3_100k):
     """Full N with a 2-layer slice of the cache: every token's mass against the oracle."""
     w, k, v, q = qwen3_100k
-    w2 = synth.workload(3, n_layers=2)
+    w2 = synth.workload("qwen3-8b-n100k", n_layers=2)
     k2, v2, q2 = k[:2].contiguous(), v[:2].contiguous(), q[:2].contiguous()
     acc = torch.zeros(w.n_tokens, device=DEV)
     got = _run_score(w2, k2, v2, None, q2, policy="h2o", item_tokens=1, state=dict(accum=acc))
@@ -562,7 +562,7 @@ def test_full_size_qwen3_100k_mass_is_additive_over_layers(qwen3_100k):
     w, k, v, q = qwen3_100k
     acc = torch.zeros(w.n_tokens, device=DEV)
     full = _run_score(w, k, v, None, q, policy="h2o", item_tokens=1, state=dict(accum=acc))
-    w2 = synth.workload(3, n_layers=2)
+    w2 = synth.workload("qwen3-8b-n100k", n_layers=2)
     total = np.zeros(w.n_tokens)
     for l0 in range(0, w.n_layers, 2):
         acc.zero_()
@@ -602,7 +602,7 @@ def test_full_size_mistral_131k_segment_sampled():
     """Mistral-7B shape at full size (131,072 tokens, 16,384-token prefix, 30% evicted):
     in-place segment eviction + re-rotation as bench.py --extras runs it, checked on
     sampled ranks against the oracle's rotation of the original rows."""
-    w = synth.workload(4)
+    w = synth.workload("mistral-7b-n131072-segment")
     k, v, _ = synth.kv_cache(w, seed=0, device=DEV)
     n_keep, e = kv.kv_select_segment(w.n_tokens, w.segment_prefix, int(w.segment_frac * w.n_tokens), 16)
     assert (n_keep, e) == (w.n_tokens - 39_328, 39_328)
@@ -633,7 +633,7 @@ def test_full_size_qwen3_1m_step_properties():
     MemDecay page scoring, page selection, compaction.  The oracle cannot score 1M keys
     for every row, so: softmax rows sum to one, sampled LSE rows over all keys, the
     selection against the oracle on the same page scores, and sampled compacted keys."""
-    w = synth.workload(5)
+    w = synth.workload("qwen3-8b-n1m")
     N = w.n_tokens
     k, v, _ = synth.kv_cache(w, seed=0, device=DEV)
     q = synth.window_queries(w, seed=0, device=DEV)
@@ -706,7 +706,7 @@ def test_full_size_qwen3_1m_step_properties():
 def test_degenerate_sizes():
     """One token, one query, one head: LSE is the single logit and the mass is one per
     (layer, head, query); a single item is selected; an empty keep count moves nothing."""
-    w = synth.workload(1, n_tokens=1, window=1, n_q_heads=1, n_kv_heads=1, n_layers=2)
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=1, window=1, n_q_heads=1, n_kv_heads=1, n_layers=2)
     k, v, _ = synth.kv_cache(w, seed=1, device="cpu")
     q = synth.window_queries(w, seed=1)
     acc = torch.zeros(1, device=DEV)
@@ -732,7 +732,7 @@ def test_degenerate_sizes():
 
 def test_score_bit_reproducible():
     """Every reduction has a fixed order: two runs give identical bits."""
-    w = synth.workload(1, n_tokens=6000, window=64, n_q_heads=32, n_kv_heads=8, n_layers=2)
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=6000, window=64, n_q_heads=32, n_kv_heads=8, n_layers=2)
     k, v, bt, q = _make_score_inputs(w, seed=77, shuffle=True)
     outs = []
     for _ in range(2):
@@ -745,7 +745,7 @@ def test_score_bit_reproducible():
 def test_compact_skips_out_of_range_keep_entries():
     """Keep entries outside the source row are skipped by the kernels' own bounds checks:
     their ranks are left untouched and every other rank is compacted normally."""
-    w = synth.workload(2, n_layers=2, n_kv_heads=2, n_q_heads=2, n_tokens=300)
+    w = synth.workload("qwen2.5-1.5b-n2048", n_layers=2, n_kv_heads=2, n_q_heads=2, n_tokens=300)
     k, v, _ = synth.kv_cache(w, seed=9, device=DEV)
     keep = torch.arange(0, 300, 10, dtype=torch.int32)          # 30 ranks
     keep[[3, 17]] = torch.tensor([1 << 30, -5], dtype=torch.int32)

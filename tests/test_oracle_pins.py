@@ -825,7 +825,7 @@ def test_renumber_counts_match_pages():
 
 def test_kv_footprint_arithmetic():
     gd = read_golden("pace_numbers.txt")
-    w = synth.workload(3)
+    w = synth.workload("qwen3-8b-n100k")
     assert w.kv_bytes_per_token == gd["kv_bytes_per_token"] == 144 * 1024
     assert abs(w.kv_bytes_per_token * 100_000 / 1e9 - gd["kv_gb_100k"]) < 0.05
     assert abs(w.kv_bytes_per_token * 1_000_000 / 1e9 - gd["kv_gb_1m"]) < 0.6
@@ -836,7 +836,7 @@ def test_kv_footprint_arithmetic():
 # ---------------------------------------------------------------------------------------
 
 def test_inactive_equivalence_is_plain_h2o():
-    w = synth.workload(3, n_layers=2, n_tokens=200, n_q_heads=4, n_kv_heads=2, window=8,
+    w = synth.workload("qwen3-8b-n100k", n_layers=2, n_tokens=200, n_q_heads=4, n_kv_heads=2, window=8,
                        n_spans=0, budget_tokens=40)
     k, v, _ = synth.kv_cache(w, seed=2)
     q = synth.window_queries(w, seed=2)
