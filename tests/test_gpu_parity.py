@@ -632,7 +632,8 @@ def test_full_size_qwen3_1m_step_properties():
     """Qwen3-8B shape at 1,000,000 tokens (147 GB), the step bench.py --extras times:
     MemDecay page scoring, page selection, compaction.  The oracle cannot score 1M keys
     for every row, so: softmax rows sum to one, sampled LSE rows over all keys, the
-    selection against the oracle on the same page scores, and sampled compacted keys."""
+    selection against the oracle on the same page scores, sampled compacted keys, and
+    every token's mass against the sum of two-layer runs."""
     w = synth.workload("qwen3-8b-n1m")
     N = w.n_tokens
     k, v, _ = synth.kv_cache(w, seed=0, device=DEV)
@@ -699,7 +700,21 @@ def test_full_size_qwen3_1m_step_properties():
     moved = np.array(ranks) != srcs.numpy()
     assert (gk[:, ~moved] == ks[:, ~moved]).all()
     assert_bf16_within_1ulp(gk[:, moved], rk[:, moved], "K at N=1M")
-    del k, v, dk, dv
+    del dk, dv
+    # every token's mass (and every row's LSE) at this launch configuration equals the sum
+    # over 18 two-layer runs, which split the keys into other chunks: mass is additive over
+    # layers, each side is within RTOL of the exact value, hence 2*RTOL
+    w2 = synth.workload("qwen3-8b-n1m", n_layers=2)
+    acc = torch.zeros(N, device=DEV)
+    total = np.zeros(N)
+    for l0 in range(0, w.n_layers, 2):
+        acc.zero_()
+        part = _run_score(w2, k[l0:l0 + 2].contiguous(), v[l0:l0 + 2].contiguous(), None,
+                          q[l0:l0 + 2].contiguous(), policy="h2o", item_tokens=1, state=dict(accum=acc))
+        total += np64(part["mass"])
+        assert np.abs(np64(lse[l0:l0 + 2]) - np64(part["lse"])).max() < 2e-5, l0
+    assert_rel(m, total, rtol=2 * RTOL, what="1M-token mass vs sum of 2-layer runs")
+    del k, v
     torch.cuda.empty_cache()
 
 
