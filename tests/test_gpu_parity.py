@@ -553,24 +553,28 @@ def test_full_size_qwen3_100k_two_layer_mass(qwen3_100k):
     assert np.abs(np64(got["lse"]) - lse).max() < 1e-5
 
 
-def test_full_size_qwen3_100k_mass_is_additive_over_layers(qwen3_100k):
+@pytest.mark.parametrize("aggregate", ["sum", "max_group"])
+def test_full_size_qwen3_100k_mass_is_additive_over_layers(qwen3_100k, aggregate):
     """Every token's mass at the benchmark's launch configuration (36 layers: a few large key
     chunks per (layer, KV head)) equals the sum of 18 two-layer runs (many small chunks, the
-    configuration the oracle checks token by token above).  The mass is a sum over layers,
-    so this holds exactly in real arithmetic; each side is within RTOL of it, hence 2*RTOL.
-    The LSE of every row must agree the same way."""
+    configuration the oracle checks token by token above and, for the group maximum, at
+    smaller sizes).  Either aggregate is a sum over layers, so this holds exactly in real
+    arithmetic; each side is within RTOL of it, hence 2*RTOL.  Every row's LSE must agree
+    the same way."""
     w, k, v, q = qwen3_100k
     acc = torch.zeros(w.n_tokens, device=DEV)
-    full = _run_score(w, k, v, None, q, policy="h2o", item_tokens=1, state=dict(accum=acc))
+    full = _run_score(w, k, v, None, q, policy="h2o", item_tokens=1, state=dict(accum=acc),
+                      aggregate=aggregate)
     w2 = synth.workload("qwen3-8b-n100k", n_layers=2)
     total = np.zeros(w.n_tokens)
     for l0 in range(0, w.n_layers, 2):
         acc.zero_()
         part = _run_score(w2, k[l0:l0 + 2].contiguous(), v[l0:l0 + 2].contiguous(), None,
-                          q[l0:l0 + 2].contiguous(), policy="h2o", item_tokens=1, state=dict(accum=acc))
+                          q[l0:l0 + 2].contiguous(), policy="h2o", item_tokens=1, state=dict(accum=acc),
+                          aggregate=aggregate)
         total += np64(part["mass"])
         assert np.abs(np64(full["lse"][l0:l0 + 2]) - np64(part["lse"])).max() < 2e-5, l0
-    assert_rel(np64(full["mass"]), total, rtol=2 * RTOL, what="36-layer mass vs sum of 2-layer runs")
+    assert_rel(np64(full["mass"]), total, rtol=2 * RTOL, what=f"36-layer {aggregate} mass vs 2-layer runs")
 
 
 def test_full_size_qwen3_100k_compaction_sampled(qwen3_100k):
