@@ -89,6 +89,32 @@ def test_score_workspace_size_and_validation():
     assert L.kv_score_workspace_size(ctypes.byref(c), ctypes.byref(pp), ctypes.byref(n)) == kv.KV_EUNSUPPORTED
 
 
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("n_layers,hkv,hq,window,n_tokens,want_chunks", [
+    (36, 8, 32, 64, 100_000, 16),      # 16 chunks of 6,272 keys: 4,608 workgroups, 9 full rounds of 512
+    (36, 8, 32, 64, 1_000_000, 125),   # 125 chunks of 8,000 keys: 36,000 workgroups
+    (2, 8, 32, 64, 100_000, 196),      # small grid: chunks of 512 keys so that >= 2,048 workgroups run
+    (2, 2, 4, 8, 100, 1),              # tiny: one chunk
+])
+def test_score_grid_choice(n_layers, hkv, hq, window, n_tokens, want_chunks):
+    """The key chunking behind the scoring grid, read back from the workspace layout
+    (LSE partials [L*Hkv][chunks][rows] float2, final LSE [L*Hkv][rows], mass partials
+    [L*Hkv][N], each 256-byte aligned)."""
+    L = kv.lib()
+    n = ctypes.c_size_t()
+    pages = -(-n_tokens // 16)
+    c = _cache(n_layers=n_layers, n_kv_heads=hkv, n_tokens=n_tokens, page_stride=16 * hkv * 128,
+               layer_stride=pages * 16 * hkv * 128)
+    p = _score_params(n_q_heads=hq, window=window)
+    assert L.kv_score_workspace_size(ctypes.byref(c), ctypes.byref(p), ctypes.byref(n)) == kv.KV_OK
+    units, rows = n_layers * hkv, (hq // hkv) * window
+    rest = _a256(units * rows * 4) + _a256(units * n_tokens * 4)
+    assert n.value == _a256(units * want_chunks * rows * 8) + rest
+
+
 def test_score_group_maximum_validation():
     """The group maximum pads each group to a power of two: G = 3 with W = 150 fits as
     a sum (450 rows) but not as a maximum (4 * 150 = 600 rows); groups above 32 heads
