@@ -34,6 +34,7 @@ only its ordering properties are pinned).
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -168,7 +169,7 @@ def attention_score_max_group(q, k, scale=None, lse=None):
     recovers scores from it); computed from the keys when None.
     Returns (score[N], lse[L][Hq][W]).
     Reading: ActKV does not say how the per-(layer, KV head) scores combine into one keep
-    mask; summing them follows MemDecay's averaging over heads and layers.
+    mask; summing them follows MemDecay's mean over layers and heads.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -222,12 +223,15 @@ def foresight_bonus(next_use, floor=50000.0):
 
 
 def token_bonus(span_id, span_bonus):
-    """Bonus of each token: the bonus of the span it belongs to (span id -1: none)."""
+    """Bonus of each token: the bonus of the span it belongs to.  A token outside every
+    span (id -1) gets none.  Reading: an id that names no span of the table (negative, or
+    not below the number of spans) is treated the same way, as no span."""
     sid = np.asarray(span_id, dtype=np.int64)
     sb = np.asarray(span_bonus, dtype=np.float64)
     out = np.zeros(sid.shape, dtype=np.float64)
-    has = sid >= 0
-    out[has] = sb[sid[has]]
+    for i, s in enumerate(sid.tolist()):
+        if 0 <= s < len(sb):
+            out[i] = sb[s]
     return out
 
 
@@ -244,12 +248,17 @@ def memdecay_update(abar, region, base_prio, decay_rate, rho, alpha, tau, dt_ste
         s_i   = b_r(i) * exp(-lambda_r(i) * dt_i) + alpha * a_i  (+ foresight bonus)
     Readings: updates in the order EWMA, clock, score; "attention above tau" is a
     strict comparison of the windowed Abar_i; dt counts decode steps, dt_steps per
-    observation (k > 1 for sampled intervals).  Returns (ewma', clock', score).
+    observation (k > 1 for sampled intervals).  A label outside the region table names
+    no region: its b and lambda are taken as 0 (the library also reports it in a status
+    bit).  Returns (ewma', clock', score).
     """
     abar = np.asarray(abar, dtype=np.float64)
     r = np.asarray(region, dtype=np.int64)
-    b = np.asarray(base_prio, dtype=np.float64)[r]
-    lam = np.asarray(decay_rate, dtype=np.float64)[r]
+    bp = np.asarray(base_prio, dtype=np.float64)
+    dr = np.asarray(decay_rate, dtype=np.float64)
+    known = (r >= 0) & (r < len(bp))
+    b = np.where(known, bp[np.where(known, r, 0)], 0.0)
+    lam = np.where(known, dr[np.where(known, r, 0)], 0.0)
     a_new = rho * np.asarray(ewma, dtype=np.float64) + (1.0 - rho) * abar
     clock = np.asarray(clock, dtype=np.int64)
     c_new = np.where(abar > tau, 0, clock + dt_steps)
@@ -269,17 +278,19 @@ def h2o_update(mass, accum, bonus=None):
 
 
 def pinned_tokens(n_tokens, region=None, pinned_regions=0, n_sink=0, n_recent=0,
-                  token_pinned=None):
+                  token_pinned=None, n_regions=32):
     """Tokens kept unconditionally.
 
     MemDecay pins whole regions (system by default); PACE's budget always includes 4
     sink and 128 recent tokens (Table 1).  A token is pinned if any rule pins it.
-    ``pinned_regions`` is a bit mask over region labels.
+    ``pinned_regions`` is a bit mask over region labels; a label at or above n_regions
+    names no region and pins nothing.
     """
     p = np.zeros(n_tokens, dtype=bool)
     if region is not None and pinned_regions:
-        r = np.asarray(region, dtype=np.int64)
-        p |= ((pinned_regions >> r) & 1).astype(bool)
+        for i, r in enumerate(np.asarray(region, dtype=np.int64).tolist()):
+            if 0 <= r < n_regions and (pinned_regions >> r) & 1:
+                p[i] = True
     p[: min(n_sink, n_tokens)] = True
     if n_recent > 0:
         p[max(0, n_tokens - n_recent):] = True
@@ -360,34 +371,37 @@ def expand_items(items, item_tokens, n_tokens):
 # O4b: ActKV LRFU keep scores with the top-p hit mask (ActKV Sec. 5.1, Algorithm 1)
 # --------------------------------------------------------------------------------------
 
-def topp_weights(score):
-    """Fixed-point weights of the top-p rule: w_j = floor(s_j * 2**shift) for finite
-    s_j > 0, else 0, with shift = 52 - ceil(log2 n) - e where max s < 2**e, so that the
-    total stays below 2**52 and every sum below is exact in integers and in float64.
-    Reading: ActKV gives the rule (an entry is a hit when its score is in the top-p set,
-    p = 90%) but not the arithmetic; fixing it in integers makes the set reproducible.
-    Returns (w as Python ints, shift)."""
-    sc = np.asarray(score, dtype=np.float32).astype(np.float64)
-    good = np.isfinite(sc) & (sc > 0)
-    n = len(sc)
-    if not good.any():
-        return [0] * n, 0
-    e = int(np.frexp(sc[good].max())[1])            # max < 2**e
-    bits = 52 - (int(math.ceil(math.log2(n))) if n > 1 else 0)
-    shift = bits - e
-    w = [int(math.floor(math.ldexp(float(x), shift))) if g else 0 for x, g in zip(sc, good)]
-    return w, shift
+def exact_score_units(score):
+    """Every float32 score as an exact integer multiple of 2**-149 (the spacing of the
+    smallest float32 subnormal): a finite positive score s becomes the Python int s * 2**149,
+    any other value (zero, negative, NaN, infinity) 0.  Sums of these integers are the exact
+    sums of the scores, with no rounding anywhere."""
+    sc = np.asarray(score, dtype=np.float32)
+    out = []
+    for x in sc.tolist():                        # float32 values as exact Python floats
+        if math.isfinite(x) and x > 0.0:
+            num, den = x.as_integer_ratio()      # den is a power of two <= 2**149
+            out.append(num * ((1 << 149) // den))
+        else:
+            out.append(0)
+    return out
 
 
 def topp_hit_mask(score, p):
-    """Hit mask of ActKV's LRFU (Sec. 5.1): the smallest prefix of the entries in the
-    total order (score descending, index ascending; -0 == +0; NaN and non-positive
-    scores carry no weight) whose weight reaches ceil(p * W), W the total weight (see
-    topp_weights), p as float32.  No entry is a hit when that target is 0."""
+    """Hit mask of ActKV's LRFU (Sec. 5.1, Algorithm 1): an entry is a hit when its
+    action-region score lies in the top-p set.
+
+    Reading (a nucleus set): order the entries by score descending, exact ties by index
+    ascending (-0 == +0); only finite positive scores carry weight, and their weight is
+    the score itself, summed exactly (rational arithmetic, no rounding); the top-p set is
+    the shortest prefix of that order whose weight reaches p times the total weight, p
+    taken as the float32 the device receives.  Entries without weight are never hits, so
+    p = 1 makes every positive score a hit, and p = 0 (or no positive score) none.
+    """
     sc = np.asarray(score, dtype=np.float32)
-    w, _ = topp_weights(sc)
+    w = exact_score_units(sc)
     total = sum(w)
-    target = math.ceil(float(np.float32(p)) * float(total))
+    target = Fraction(float(np.float32(p))) * total       # exact: p * (sum of the scores)
     hit = np.zeros(len(sc), dtype=bool)
     if target <= 0:
         return hit
@@ -396,12 +410,10 @@ def topp_hit_mask(score, p):
     order = sorted(range(len(sc)), key=lambda j: (-key[j], j))
     acc = 0
     for j in order:
-        if w[j] == 0:
+        if acc >= target or w[j] == 0:
             break
         hit[j] = True
         acc += w[j]
-        if acc >= target:
-            break
     return hit
 
 
@@ -514,7 +526,8 @@ def rope_rotate(k, delta, theta=None, inv_freq=None):
 
 
 def scaled_inv_freq(kind, base, head_dim=128, factor=1.0, original_max_position=8192,
-                    low_freq_factor=1.0, high_freq_factor=4.0, beta_fast=32.0, beta_slow=1.0):
+                    low_freq_factor=1.0, high_freq_factor=4.0, beta_fast=32.0, beta_slow=1.0,
+                    truncate=True):
     """RoPE frequencies under static scaling (PACE Sec. 3.5 names default, linear, YaRN
     and Llama-3 style scaling; the definitions are the published methods):
       default: theta_i = base ** (-2i/D);
@@ -523,9 +536,19 @@ def scaled_inv_freq(kind, base, head_dim=128, factor=1.0, original_max_position=
                theta_i, dims with w_i > L / low_freq_factor get theta_i / factor, the rest
                blend (1 - t) theta_i / factor + t theta_i with
                t = (L / w_i - low_freq_factor) / (high_freq_factor - low_freq_factor);
-      yarn:    "NTK-by-parts": r_i = L / w_i rotations over the original context L,
+      yarn:    "NTK-by-parts" as the YaRN authors' code and the inference engines build
+               it: pair i turns r_i = L / w_i times over the original context L, and the
+               pair index at which r_i equals beta turns is
+                   i(beta) = D * ln(L / (2 pi beta)) / (2 ln base);
+               with lo = i(beta_fast) and hi = i(beta_slow) (lo rounded down and hi up when
+               truncate, then clamped to [0, D - 1]; hi = lo + 0.001 when they meet) the ramp
+               g_i = clip((i - lo) / (hi - lo), 0, 1) runs over the pair index and
+               theta'_i = g_i theta_i / factor + (1 - g_i) theta_i;
+      yarn_ratio: the ramp written over r_i instead, as the YaRN paper states it:
                g = clip((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1),
                theta'_i = (1 - g) theta_i / factor + g theta_i.
+    The two YaRN forms agree outside the blended band and differ inside it (r_i falls
+    exponentially with i); keys cached by an engine carry the first.
     L = original_max_position.  Only the rotation is defined here: YaRN's attention
     temperature scales q and k when they are cached, and re-rotating a cached key by a
     position difference leaves that factor in place.
@@ -549,6 +572,20 @@ def scaled_inv_freq(kind, base, head_dim=128, factor=1.0, original_max_position=
                 out[i] = (1.0 - t) * theta[i] / factor + t * theta[i]
         return out
     if kind == "yarn":
+        def pair_at(turns):
+            return head_dim * math.log(L / (turns * 2.0 * math.pi)) / (2.0 * math.log(base))
+        lo, hi = pair_at(beta_fast), pair_at(beta_slow)
+        if truncate:
+            lo, hi = math.floor(lo), math.ceil(hi)
+        lo, hi = max(lo, 0), min(hi, head_dim - 1)
+        if hi == lo:
+            hi = hi + 0.001
+        out = np.empty_like(theta)
+        for i in range(theta.size):
+            g = min(max((i - lo) / (hi - lo), 0.0), 1.0)
+            out[i] = g * theta[i] / factor + (1.0 - g) * theta[i]
+        return out
+    if kind == "yarn_ratio":
         r = L / wavelen
         g = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
         return (1.0 - g) * theta / factor + g * theta
@@ -711,7 +748,7 @@ def score_step(q, k, *, policy, scale=None, region=None, base_prio=None, decay_r
     aggregate 'sum' sums the attention over every query head (attention_mass);
     'max_group' takes the maximum over each GQA group first (attention_score_max_group,
     ActKV).  policy 'memdecay' divides by the number of summed terms, L*Hq*W or L*Hkv*W
-    ("averaged over heads and layers"); policy 'h2o' accumulates the sum.  lse_in is an
+    (the mean over layers, heads and window queries); policy 'h2o' accumulates the sum.  lse_in is an
     optional supplied LSE.  Returns a dict of float64 arrays.
     """
     nl, w_len, hq, _ = np.asarray(q).shape
@@ -739,7 +776,8 @@ def score_step(q, k, *, policy, scale=None, region=None, base_prio=None, decay_r
         out.update(accum=acc, token_score=s)
     else:
         raise ValueError(policy)
-    pin = pinned_tokens(n, region, pinned_regions, n_sink, n_recent, token_pinned)
+    n_regions = len(base_prio) if base_prio is not None else 32
+    pin = pinned_tokens(n, region, pinned_regions, n_sink, n_recent, token_pinned, n_regions)
     out["token_pinned"] = pin
     if item_tokens == 1:
         out["item_score"] = out["token_score"]

@@ -7,6 +7,7 @@ Hugging-Face-style rotate-half RoPE, complex multiplication), or brute force.
 """
 import itertools
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -315,6 +316,35 @@ def test_foresight_dominance_and_soonest_first():
     assert (bon[1:].min() + 0.0) > unprot.max()
 
 
+def test_token_bonus_by_hand():
+    """A token takes its span's bonus; id -1 (no span) and ids that name no span of the
+    table get none."""
+    bonus = np.array([10.0, 20.0, 30.0])
+    sid = np.array([-1, 0, 2, 3, 1, -7, 2 ** 31 - 1, 0])
+    assert O.token_bonus(sid, bonus).tolist() == [0.0, 10.0, 30.0, 0.0, 20.0, 0.0, 0.0, 10.0]
+    # through the score step: H2O adds exactly that bonus to the accumulated mass
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 2, 2, 8))
+    k = rng.standard_normal((1, 8, 1, 8))
+    nxt = np.array([1, 0, 4])                       # spans 0 and 2 are read again
+    out = O.score_step(q, k, policy="h2o", span_id=sid, span_next_use=nxt, bonus_floor=100.0)
+    want = O.token_bonus(sid, [200.0, 0.0, 125.0])
+    np.testing.assert_allclose(out["token_score"] - out["accum"], want, rtol=0, atol=1e-9)
+
+
+def test_region_labels_outside_the_table():
+    """A label at or above the number of regions names no region: no base priority, no
+    decay, no region pinning."""
+    a, c, s = O.memdecay_update(np.array([0.0, 0.0]), np.array([1, 9]), [1.0, 2.0], [0.1, 0.1],
+                                rho=0.5, alpha=1.0, tau=0.01, dt_steps=1, ewma=[0.5, 0.5],
+                                clock=[0, 0])
+    assert c.tolist() == [1, 1]
+    np.testing.assert_allclose(s, [2.0 * math.exp(-0.1) + 0.25, 0.25], rtol=1e-15)
+    pin = O.pinned_tokens(4, np.array([0, 3, 7, 40]), pinned_regions=(1 << 3) | (1 << 7) | 1,
+                          n_regions=5)
+    assert pin.tolist() == [True, True, False, False]
+
+
 # ---------------------------------------------------------------------------------------
 # pins / page aggregation
 # ---------------------------------------------------------------------------------------
@@ -457,28 +487,47 @@ def _rank_order(sc):
     return sorted(range(len(sc)), key=lambda j: (-key[j], j))
 
 
+def _exact_weights(sc):
+    """Each finite positive float32 score as an exact rational, else 0 (independent of the
+    oracle's integer scaling)."""
+    return [Fraction(float(x)) if math.isfinite(float(x)) and float(x) > 0 else Fraction(0)
+            for x in np.asarray(sc, np.float32)]
+
+
+def _hits_by_definition(sc, p):
+    """Per-entry form of the top-p set: an entry with weight is a hit exactly when the
+    weight of the entries ranked before it has not yet reached p times the total."""
+    w = _exact_weights(sc)
+    target = Fraction(float(np.float32(p))) * sum(w)
+    order = _rank_order(np.asarray(sc, np.float32))
+    before = {}
+    acc = Fraction(0)
+    for j in order:
+        before[j] = acc
+        acc += w[j]
+    return np.array([w[j] > 0 and before[j] < target for j in range(len(w))])
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_topp_hit_mask_is_the_minimal_prefix(seed):
-    """The hits reach the target weight, dropping the lowest-ranked hit falls short of
-    it, and every hit ranks above every positive-weight miss (total order: score
+    """The hits reach p times the total exactly, dropping the lowest-ranked hit falls short
+    of it, and every hit ranks above every positive-weight miss (total order: score
     descending, index ascending)."""
     rng = np.random.default_rng(300 + seed)
     n = int(rng.integers(1, 40))
-    sc = rng.choice([0.0, -0.0, 0.25, 0.5, 1e-3, 3.0, float(rng.random())], n).astype(np.float32)
+    sc = rng.choice([0.0, -0.0, 0.25, 0.5, 1e-3, 3.0, 1e-40, float(rng.random())], n).astype(np.float32)
     if seed % 3 == 0:
         sc[rng.integers(0, n)] = np.nan
     p = float(rng.choice([0.5, 0.9, 0.999, 1.0]))
     hit = O.topp_hit_mask(sc, p)
-    w, _ = O.topp_weights(sc)
-    total = sum(w)
-    target = math.ceil(float(np.float32(p)) * total)
+    w = _exact_weights(sc)
+    target = Fraction(float(np.float32(p))) * sum(w)
     hw = [w[j] for j in range(n) if hit[j]]
     if target == 0:
         assert not hit.any()
         return
     assert sum(hw) >= target
-    order = [j for j in _rank_order(sc)]
-    ranks = {j: r for r, j in enumerate(order)}
+    ranks = {j: r for r, j in enumerate(_rank_order(sc))}
     last = max((j for j in range(n) if hit[j]), key=lambda j: ranks[j])
     assert sum(hw) - w[last] < target
     for j in range(n):
@@ -487,21 +536,44 @@ def test_topp_hit_mask_is_the_minimal_prefix(seed):
     assert all(w[j] > 0 for j in range(n) if hit[j])
 
 
-def test_topp_weights_exact_and_bounded():
-    rng = np.random.default_rng(310)
-    sc = (rng.random(100_000) ** 4).astype(np.float32)
-    w, shift = O.topp_weights(sc)
-    assert sum(w) < 2 ** 52
-    order = np.argsort(sc, kind="stable")
-    ws = np.array(w, dtype=np.float64)[order]
-    assert (np.diff(ws) >= 0).all()                   # monotone in the score
-    j = int(np.argmax(sc))
-    assert w[j] == math.floor(float(sc[j]) * 2.0 ** shift)
+def test_topp_exhaustive_against_the_per_entry_definition():
+    """Every score vector of length <= 5 over an alphabet with ties, zeros, a negative, a
+    subnormal and NaN, at several p: the oracle's prefix walk equals the per-entry form."""
+    alphabet = [0.5, 0.25, 0.0, -1.0, 1e-40, float("nan")]
+    ps = [0.0, 0.25, 0.5, 0.75, float(np.nextafter(np.float32(0.5), np.float32(1))), 1.0]
+    count = 0
+    for n in range(1, 6):
+        for combo in itertools.product(alphabet, repeat=n):
+            sc = np.array(combo, dtype=np.float32)
+            for p in ps:
+                assert (O.topp_hit_mask(sc, p) == _hits_by_definition(sc, p)).all(), (combo, p)
+                count += 1
+    assert count > 50_000
+
+
+def test_topp_random_against_the_per_entry_definition():
+    rng = np.random.default_rng(77)
+    for _ in range(40):
+        n = int(rng.integers(1, 300))
+        sc = (rng.random(n) ** rng.integers(1, 30)).astype(np.float32)
+        sc[rng.random(n) < 0.1] = 0.0
+        p = float(rng.choice([0.1, 0.5, 0.9, 0.99, 1.0, float(rng.random())]))
+        assert (O.topp_hit_mask(sc, p) == _hits_by_definition(sc, p)).all()
+
+
+def test_exact_score_units():
+    vals = np.array([1.0, 0.1, 3.4028235e38, 1.1754944e-38, 1e-45, 1e-40, 0.0, -0.0, -2.0,
+                     np.inf, np.nan], dtype=np.float32)
+    u = O.exact_score_units(vals)
+    for x, got in zip(vals, u):
+        want = Fraction(float(x)) * 2 ** 149 if np.isfinite(x) and x > 0 else 0
+        assert got == want and int(want) == want
+    assert u[4] == 1                                   # the smallest subnormal is one unit
 
 
 def test_topp_special_cases():
     # one entry holding 95% of the weight is the only hit at p = 90%
-    sc = np.array([0.01] * 5 + [0.95] + [0.01] * 0, dtype=np.float32)
+    sc = np.array([0.01] * 5 + [0.95], dtype=np.float32)
     assert O.topp_hit_mask(sc, 0.9).tolist() == [False] * 5 + [True]
     # p = 1 takes every entry with weight; equal scores are taken by index
     sc = np.array([0.2, 0.2, 0.2, 0.0, 0.2, 0.2], dtype=np.float32)
@@ -509,6 +581,34 @@ def test_topp_special_cases():
     assert O.topp_hit_mask(sc, 0.5).tolist() == [True, True, True, False, False, False]
     assert not O.topp_hit_mask(np.zeros(7, np.float32), 0.9).any()
     assert not O.topp_hit_mask(sc, 0.0).any()
+    # an exact boundary: 0.5 of a total of 1 is reached by the first entry alone; the next
+    # float32 above 0.5 needs the second one too
+    sc = np.array([0.25, 0.5, 0.25], dtype=np.float32)
+    assert O.topp_hit_mask(sc, 0.5).tolist() == [False, True, False]
+    up = float(np.nextafter(np.float32(0.5), np.float32(1)))
+    assert O.topp_hit_mask(sc, up).tolist() == [True, True, False]
+    # p is the float32 the device receives: float32(0.9) * (0.9f + 0.1f) is below 0.9f, so
+    # the first entry alone reaches it, while the decimal 0.9 would need both
+    sc = np.array([0.9, 0.1], dtype=np.float32)
+    t = Fraction(float(sc[0])) + Fraction(float(sc[1]))
+    assert Fraction(float(np.float32(0.9))) * t <= Fraction(float(sc[0])) < Fraction(0.9) * t
+    assert O.topp_hit_mask(sc, 0.9).tolist() == [True, False]
+
+
+def test_topp_every_positive_score_is_a_hit_at_p_one():
+    """At p = 1 the set must cover the whole weight, so every positive score is a hit,
+    however small next to the others (scores from 1e-45 to 1)."""
+    rng = np.random.default_rng(12)
+    sc = np.float32(10.0) ** rng.uniform(-45, 0, 5000).astype(np.float32)
+    sc = sc.astype(np.float32)
+    sc[:50] = 0.0
+    assert (sc[50:] > 0).all() and sc.min() == 0 and (sc[50:] < 1e-38).any()
+    hit = O.topp_hit_mask(sc, 1.0)
+    assert (hit == (sc > 0)).all()
+    # just below p = 1 the smallest scores stay out: together they weigh less than the
+    # missing 2**-24 of the total
+    below = O.topp_hit_mask(sc, float(np.nextafter(np.float32(1), np.float32(0))))
+    assert below.sum() < hit.sum() and below[np.argmax(sc)]
 
 
 def test_lrfu_update_rule():
@@ -677,17 +777,52 @@ def test_scaled_inv_freq_special_cases():
     mid = ~hi & ~lo
     assert ((ll[mid] > d[mid] / 8.0) & (ll[mid] < d[mid])).all()
     assert (np.diff(ll) < 0).all()
-    ya = O.scaled_inv_freq("yarn", base, factor=16.0, original_max_position=4096)
     r = 4096 / wl
     fast, slow = r > 32.0, r < 1.0
     assert fast.any() and slow.any()
-    np.testing.assert_allclose(ya[fast], d[fast], rtol=1e-15)
-    np.testing.assert_allclose(ya[slow], d[slow] / 16.0, rtol=1e-15)
-    m = ~fast & ~slow
-    assert ((ya[m] > d[m] / 16.0) & (ya[m] < d[m])).all()
+    for kind in ("yarn", "yarn_ratio"):
+        np.testing.assert_allclose(O.scaled_inv_freq(kind, base, factor=1.0), d, rtol=1e-15)
+        ya = O.scaled_inv_freq(kind, base, factor=16.0, original_max_position=4096)
+        np.testing.assert_allclose(ya[fast], d[fast], rtol=1e-15)
+        np.testing.assert_allclose(ya[slow], d[slow] / 16.0, rtol=1e-15)
+        m = ~fast & ~slow
+        assert ((ya[m] >= d[m] / 16.0) & (ya[m] <= d[m])).all()
+        assert (np.diff(ya) < 0).all()
+    # the pair turning exactly beta times over L sits at D ln(L / (2 pi beta)) / (2 ln base)
+    i32 = 128 * math.log(4096 / (2 * math.pi * 32.0)) / (2 * math.log(base))
+    assert abs(4096 / (2 * math.pi / base ** (-2 * i32 / 128)) - 32.0) < 1e-9
 
 
-@pytest.mark.parametrize("kind", ["linear", "llama3", "yarn"])
+def _hf_table(kind, base, factor, L, **params):
+    """The frequencies transformers' model code rotates with (it builds them in float32)."""
+    from transformers import PretrainedConfig
+    from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    rp = dict(rope_type=kind, rope_theta=base, factor=factor, original_max_position_embeddings=L, **params)
+    cfg = PretrainedConfig(hidden_size=4096, num_attention_heads=32, head_dim=128,
+                           max_position_embeddings=int(L * factor), rope_parameters=rp)
+    inv, _ = ROPE_INIT_FUNCTIONS[kind](cfg, "cpu")
+    return inv.double().numpy()
+
+
+@pytest.mark.parametrize("base,factor,L", [(1e6, 4.0, 32768), (5e5, 8.0, 8192), (1e4, 16.0, 4096),
+                                           (150000.0, 32.0, 4096), (1e6, 2.0, 131072)])
+def test_scaled_tables_match_transformers(base, factor, L):
+    """Llama-3 and YaRN tables against the ones transformers' model code caches keys with
+    (an independent implementation).  Its tables are float32, so the bar is a few float32
+    roundings (4e-6 relative).  The YaRN paper's ratio form differs inside the band."""
+    pytest.importorskip("transformers")
+    ll = _hf_table("llama3", base, factor, L, low_freq_factor=1.0, high_freq_factor=4.0)
+    np.testing.assert_allclose(O.scaled_inv_freq("llama3", base, factor=factor, original_max_position=L),
+                               ll, rtol=4e-6, atol=0)
+    for params in (dict(beta_fast=32.0, beta_slow=1.0), dict(beta_fast=16.0, beta_slow=2.0, truncate=False)):
+        hf = _hf_table("yarn", base, factor, L, **params)
+        ours = O.scaled_inv_freq("yarn", base, factor=factor, original_max_position=L, **params)
+        np.testing.assert_allclose(ours, hf, rtol=4e-6, atol=0)
+    ratio = O.scaled_inv_freq("yarn_ratio", base, factor=factor, original_max_position=L)
+    assert np.abs(ratio / _hf_table("yarn", base, factor, L) - 1).max() > 1e-2
+
+
+@pytest.mark.parametrize("kind", ["linear", "llama3", "yarn", "yarn_ratio"])
 def test_proposition1_holds_for_scaled_tables(kind):
     """Re-rotating a key cached at p by q - p gives the key cached at q for any fixed
     frequency table (the model-side rotation written the rotate_half way)."""
