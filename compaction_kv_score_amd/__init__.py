@@ -28,6 +28,7 @@ KV_ELIMIT = -5
 KV_STATUS_PINNED_OVER_BUDGET = 1
 KV_STATUS_NAN_SCORE = 2
 KV_STATUS_KEEP_OVERFLOW = 4
+KV_STATUS_BAD_REGION = 8
 KV_POLICY_MEMDECAY = 0
 KV_POLICY_H2O = 1
 KV_AGG_SUM = 0
@@ -37,9 +38,11 @@ KV_ROPE_LINEAR = 1
 KV_ROPE_LLAMA3 = 2
 KV_ROPE_YARN = 3
 KV_ROPE_TABLE = 4
+KV_ROPE_YARN_RATIO = 5
+KV_ROPE_YARN_NO_TRUNCATE = 1
 KV_REF_NONE = -(2 ** 31)
 KV_MAX_META = 8
-KV_ABI_VERSION = 2  # layout of the structs below
+KV_ABI_VERSION = 3  # layout of the structs below
 
 
 class KvError(RuntimeError):
@@ -77,7 +80,8 @@ class KvScoreParams(ctypes.Structure):
                 ("token_pinned", ctypes.c_void_p), ("mass", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p), ("token_score", ctypes.c_void_p),
                 ("item_score", ctypes.c_void_p), ("item_pinned", ctypes.c_void_p),
-                ("stage_events", ctypes.c_void_p), ("aggregate", ctypes.c_int32)]
+                ("stage_events", ctypes.c_void_p), ("aggregate", ctypes.c_int32),
+                ("status", ctypes.c_void_p)]
 
 
 class KvRope(ctypes.Structure):
@@ -85,7 +89,8 @@ class KvRope(ctypes.Structure):
                 ("base", ctypes.c_double), ("factor", ctypes.c_double),
                 ("low_freq_factor", ctypes.c_double), ("high_freq_factor", ctypes.c_double),
                 ("beta_fast", ctypes.c_double), ("beta_slow", ctypes.c_double),
-                ("inv_freq", ctypes.POINTER(ctypes.c_double))]
+                ("inv_freq", ctypes.POINTER(ctypes.c_double)), ("flags", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class KvRefStore(ctypes.Structure):
@@ -226,7 +231,7 @@ def _score_params(q, *, policy, window, item_tokens, scale=0.0, dt_steps=1, lse_
                   ewma=None, clock=None, accum=None, span_id=None, span_next_use=None,
                   bonus_floor=50000.0, pinned_regions=0, n_sink=0, n_recent=0,
                   token_pinned=None, mass=None, lse=None, token_score=None, item_score=None,
-                  item_pinned=None, stage_events=None, aggregate="sum"):
+                  item_pinned=None, stage_events=None, aggregate="sum", status=None):
     pol = {"memdecay": KV_POLICY_MEMDECAY, "h2o": KV_POLICY_H2O}.get(policy, policy)
     agg = {"sum": KV_AGG_SUM, "max_group": KV_AGG_MAX_GROUP}.get(aggregate, aggregate)
     n_regions = int(base_prio.numel()) if base_prio is not None else 0
@@ -237,7 +242,8 @@ def _score_params(q, *, policy, window, item_tokens, scale=0.0, dt_steps=1, lse_
         float(rho), float(alpha), float(tau), _ptr(ewma), _ptr(clock), _ptr(accum),
         _ptr(span_id), _ptr(span_next_use), n_spans, float(bonus_floor), int(pinned_regions),
         int(n_sink), int(n_recent), _ptr(token_pinned), _ptr(mass), _ptr(lse),
-        _ptr(token_score), _ptr(item_score), _ptr(item_pinned), stage_events, int(agg))
+        _ptr(token_score), _ptr(item_score), _ptr(item_pinned), stage_events, int(agg),
+        _ptr(status))
 
 
 def kv_score_workspace_size(cache: PagedCache, q, **kw) -> int:
@@ -359,12 +365,14 @@ def kv_select_segment(n_tokens, prefix_len, evict_tokens, block, keep_tokens=Non
 
 
 def kv_rope(kind="default", base=1e6, factor=1.0, original_max_position=8192, low_freq_factor=1.0,
-            high_freq_factor=4.0, beta_fast=32.0, beta_slow=1.0, table=None) -> KvRope:
-    """A kv_rope descriptor (see include/kvscore.h); kind is a name or a KV_ROPE_* code."""
+            high_freq_factor=4.0, beta_fast=32.0, beta_slow=1.0, table=None, truncate=True) -> KvRope:
+    """A kv_rope descriptor (see include/kvscore.h); kind is a name or a KV_ROPE_* code;
+    truncate=False sets KV_ROPE_YARN_NO_TRUNCATE."""
     code = {"default": KV_ROPE_DEFAULT, "linear": KV_ROPE_LINEAR, "llama3": KV_ROPE_LLAMA3,
-            "yarn": KV_ROPE_YARN, "table": KV_ROPE_TABLE}.get(kind, kind)
+            "yarn": KV_ROPE_YARN, "yarn_ratio": KV_ROPE_YARN_RATIO, "table": KV_ROPE_TABLE}.get(kind, kind)
     r = KvRope(int(code), int(original_max_position), float(base), float(factor), float(low_freq_factor),
-               float(high_freq_factor), float(beta_fast), float(beta_slow), None)
+               float(high_freq_factor), float(beta_fast), float(beta_slow), None,
+               0 if truncate else KV_ROPE_YARN_NO_TRUNCATE, 0)
     if table is not None:
         arr = (ctypes.c_double * 64)(*[float(x) for x in table])
         r._table = arr                      # keep the host array alive with the struct

@@ -262,6 +262,7 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   ca.lse_in = p->lse_in;
   ca.lse2 = (float*)(w + L.off_lse2);
   ca.lse_out = p->lse;
+  ca.status = p->status;
   if ((e = launch_lse_combine(ca, stream)) != hipSuccess) return hip_fail(e);
   if ((e = mark(2)) != hipSuccess) return hip_fail(e);
   if ((e = launch_score_pass(sa, true, stream)) != hipSuccess) return hip_fail(e);
@@ -272,7 +273,7 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   ea.mass_part = sa.mass_part;
   ea.n_parts = n_lg * L.n_rsplit;
   ea.n_tokens = c->n_tokens;
-  // MemDecay's average over heads and layers: Hq terms per (layer, window query) when
+  // MemDecay's mean over layers and heads: Hq terms per (layer, window query) when
   // summing, one per KV head when each group contributes its maximum
   const int terms_per_query = p->aggregate == KV_AGG_MAX_GROUP ? c->n_kv_heads : p->n_q_heads;
   ea.mass_norm = 1.0 / ((double)c->n_layers * terms_per_query * p->window);
@@ -301,6 +302,7 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   ea.token_score = p->token_score;
   ea.item_score = p->item_score;
   ea.item_pinned = p->item_pinned;
+  ea.status = p->status;
   if ((e = launch_epilogue(ea, stream)) != hipSuccess) return hip_fail(e);
   if ((e = mark(4)) != hipSuccess) return hip_fail(e);
   return KV_OK;
@@ -413,13 +415,32 @@ int32_t kv_rope_inv_freq(const kv_rope* rope, double* inv_freq) {
   const bool scaled = rope->kind != KV_ROPE_DEFAULT;
   if (scaled && !(rope->factor > 0.0 && isfinite(rope->factor))) return KV_EINVAL;
   const double L = (double)rope->original_max_position;
-  if ((rope->kind == KV_ROPE_LLAMA3 || rope->kind == KV_ROPE_YARN) && !(L > 0.0)) return KV_EINVAL;
+  if ((rope->kind == KV_ROPE_LLAMA3 || rope->kind == KV_ROPE_YARN || rope->kind == KV_ROPE_YARN_RATIO) &&
+      !(L > 0.0))
+    return KV_EINVAL;
   if (rope->kind == KV_ROPE_LLAMA3 &&
       !(rope->low_freq_factor > 0.0 && rope->high_freq_factor > rope->low_freq_factor))
     return KV_EINVAL;
-  if (rope->kind == KV_ROPE_YARN && !(rope->beta_fast > rope->beta_slow)) return KV_EINVAL;
-  if (rope->kind < KV_ROPE_DEFAULT || rope->kind > KV_ROPE_YARN) return KV_EINVAL;
+  const bool yarn = rope->kind == KV_ROPE_YARN || rope->kind == KV_ROPE_YARN_RATIO;
+  if (yarn && !(rope->beta_fast > rope->beta_slow && rope->beta_slow > 0.0)) return KV_EINVAL;
+  if (rope->kind < KV_ROPE_DEFAULT || rope->kind > KV_ROPE_YARN_RATIO || rope->kind == KV_ROPE_TABLE)
+    return KV_EINVAL;
+  if (rope->flags & ~(int32_t)KV_ROPE_YARN_NO_TRUNCATE) return KV_EINVAL;
   const double two_pi = 6.283185307179586476925286766559;
+  // YaRN's blend band in pair indices: pair i turns L * f_i / (2 pi) times over the
+  // original context, so it turns beta times at i(beta) = D ln(L / (2 pi beta)) / (2 ln base)
+  double lo = 0.0, hi = 1.0;
+  if (rope->kind == KV_ROPE_YARN) {
+    lo = kHeadDim * log(L / (two_pi * rope->beta_fast)) / (2.0 * log(rope->base));
+    hi = kHeadDim * log(L / (two_pi * rope->beta_slow)) / (2.0 * log(rope->base));
+    if (!(rope->flags & KV_ROPE_YARN_NO_TRUNCATE)) {
+      lo = floor(lo);
+      hi = ceil(hi);
+    }
+    if (lo < 0.0) lo = 0.0;
+    if (hi > kHeadDim - 1) hi = kHeadDim - 1;
+    if (hi == lo) hi += 0.001;
+  }
   for (int i = 0; i < half; ++i) {
     const double f = pow(rope->base, -(2.0 * i) / kHeadDim);
     double out = f;
@@ -436,6 +457,10 @@ int32_t kv_rope_inv_freq(const kv_rope* rope, double* inv_freq) {
         out = (1.0 - t) * f / rope->factor + t * f;
       }
     } else if (rope->kind == KV_ROPE_YARN) {
+      double g = (i - lo) / (hi - lo);
+      g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+      out = g * f / rope->factor + (1.0 - g) * f;
+    } else if (rope->kind == KV_ROPE_YARN_RATIO) {
       const double rot = L / (two_pi / f);
       double g = (rot - rope->beta_slow) / (rope->beta_fast - rope->beta_slow);
       g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
@@ -644,6 +669,7 @@ int32_t kv_gather_evicted(const kv_cache_desc* src, const int32_t* keep_tokens, 
   a.n_kv_heads = src->n_kv_heads;
   a.keep = keep_tokens;
   a.n_keep = n_keep;
+  a.src_tokens = src->n_tokens;
   a.first = first;
   a.count = count;
   a.evicted_tokens = evicted_tokens;

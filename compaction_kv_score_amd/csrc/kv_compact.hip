@@ -330,6 +330,9 @@ __global__ __launch_bounds__(kCompactThreads) void gather_evicted_kernel(EvictAr
   const int32_t* keep = a.keep;
   const int64_t c = block_count_true(a.n_keep, [&](int64_t i) { return keep[i] - i <= e; });
   const int64_t t = e + c;
+  // a keep list that is not strictly ascending inside [0, N) can point past the row:
+  // such a rank is skipped (nothing read or written), as the other copies skip theirs
+  if (t < 0 || t >= a.src_tokens) return;
   const int slot_stride = a.n_kv_heads * kHeadDim;
   const int64_t so = token_offset(t, a.src_page_shift, a.src_page_stride, a.src_bt, slot_stride);
   const int64_t dof = token_offset(r, a.dst_page_shift, a.dst_page_stride, a.dst_bt, slot_stride);

@@ -2,9 +2,10 @@
 //
 // Reduces the per-(layer, KV head) attention-mass partials of one token in a fixed
 // order (float64 accumulation), then applies the retention policy:
-//   MemDecay (MemDecay, Method): Abar = mass / (L*Hq*W) ("averaged over heads and
-//     layers"); a <- rho*a + (1-rho)*Abar; the decay clock resets when Abar > tau and
-//     otherwise advances by dt_steps; s = b_r * exp(-lambda_r * clock) + alpha * a.
+//   MemDecay (MemDecay, Method): Abar = mass / (L*Hq*W), the mean of the weights over
+//     layers, query heads and window queries; a <- rho*a + (1-rho)*Abar; the decay clock
+//     resets when Abar > tau and otherwise advances by dt_steps;
+//     s = b_r * exp(-lambda_r * clock) + alpha * a.
 //   H2O (PACE Sec. 2, heavy hitters): acc <- acc + mass; s = acc.
 // plus PACE's foresight bonus (Sec. 3.1; floor as in Sec. 5.7 and 7) for tokens whose
 // span a future step reads, and the pinning rules (MemDecay pinned regions, PACE
@@ -56,6 +57,7 @@ __global__ __launch_bounds__(kEpiThreads * kEpiSplit) void epilogue_kernel(Epilo
 
   float score = 0.f;
   int pinned = 0;
+  bool bad_region = false;
   if (valid && quarter == 0) {
     double msum = s_part[0][tid];
 #pragma unroll
@@ -71,10 +73,14 @@ __global__ __launch_bounds__(kEpiThreads * kEpiSplit) void epilogue_kernel(Epilo
         if (d >= 1) bonus = a.bonus_floor * (1.0f + 1.0f / (float)d);
       }
     }
+    // a label outside the region table names no region (reported through the status)
     int r = 0;
     if (a.region) {
       r = a.region[i];
-      if (r >= a.n_regions) r = a.n_regions - 1;
+      if (r >= a.n_regions) {
+        bad_region = true;
+        r = 0;
+      }
     }
     if (a.policy == KV_POLICY_MEMDECAY) {
       const float abar = (float)(msum * a.mass_norm);
@@ -82,8 +88,8 @@ __global__ __launch_bounds__(kEpiThreads * kEpiSplit) void epilogue_kernel(Epilo
       const int32_t clk = abar > a.tau ? 0 : a.clock[i] + a.dt_steps;
       a.ewma[i] = ew;
       a.clock[i] = clk;
-      const float b = a.base_prio ? a.base_prio[r] : 0.f;
-      const float lam = a.decay_rate ? a.decay_rate[r] : 0.f;
+      const float b = a.base_prio && !bad_region ? a.base_prio[r] : 0.f;
+      const float lam = a.decay_rate && !bad_region ? a.decay_rate[r] : 0.f;
       score = b * expf(-lam * (float)clk) + a.alpha * ew + bonus;
     } else {
       const float acc = a.accum[i] + mass;
@@ -92,9 +98,11 @@ __global__ __launch_bounds__(kEpiThreads * kEpiSplit) void epilogue_kernel(Epilo
     }
     if (a.token_score) a.token_score[i] = score;
     pinned = (i < a.n_sink) || (i >= N - a.n_recent) ||
-             (a.region && ((a.pinned_regions >> r) & 1u)) ||
+             (a.region && !bad_region && ((a.pinned_regions >> r) & 1u)) ||
              (a.token_pinned && a.token_pinned[i] != 0);
   }
+  if (a.status && __builtin_amdgcn_ballot_w64(bad_region) != 0 && (tid & 63) == 0)
+    atomicOr(a.status, KV_STATUS_BAD_REGION);
 
   if (a.item_shift == 0) {
     if (valid && quarter == 0) {

@@ -54,6 +54,7 @@ struct CombineArgs {
   const float* lse_in;          // optional natural-log LSE input [L][Hq][W]
   float* lse2;                  // [L*Hkv][rows]
   float* lse_out;               // optional [L][Hq][W]
+  uint32_t* status;             // optional kv_score status word, cleared here
 };
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t s);
 
@@ -83,6 +84,7 @@ struct EpilogueArgs {
   float* token_score;
   float* item_score;
   uint8_t* item_pinned;
+  uint32_t* status;             // optional: KV_STATUS_BAD_REGION
 };
 hipError_t launch_epilogue(const EpilogueArgs& a, hipStream_t s);
 
@@ -129,10 +131,9 @@ struct ToppState {                 // lives in the LRFU workspace
   uint32_t mask;
   uint32_t mode;                 // 0 radix, 2 no hits
   uint32_t ticket;
-  uint32_t max_bits;             // bits of the largest weighted score (0: none)
-  uint32_t pad;
-  uint64_t rem;                  // weight still missing from the target
-  uint64_t total;                // total weight W
+  uint32_t pad0, pad1;
+  uint64_t rem;                  // weight still missing from the target, in units of the
+                                 // boundary exponent's 2^(E-150)
   int64_t c_eq;                  // entries equal to the boundary that are hits
 };
 struct LrfuArgs {
@@ -224,6 +225,7 @@ struct EvictArgs {
   int n_layers, n_kv_heads;
   const int32_t* keep;           // ascending kept tokens
   int64_t n_keep;
+  int64_t src_tokens;            // rows whose token falls outside [0, src_tokens) are skipped
   int64_t first, count;          // evicted ranks [first, first + count)
   int32_t* evicted_tokens;       // [count] (nullable)
   MetaSet meta;                  // dst[e - first] = src[token]

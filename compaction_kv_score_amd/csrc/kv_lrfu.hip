@@ -1,22 +1,28 @@
 // ActKV's attention-aware LRFU keep scores (ActKV Sec. 5.1, Algorithm 1) on gfx950.
 //
 //   KS <- decay * KS + AttnScore   for hits,   KS <- decay * KS   for misses,
-// where an entry is a hit when its score lies in the top-p set: the smallest prefix of
+// where an entry is a hit when its score lies in the top-p set: the shortest prefix of
 // the entries in the total order (score descending, index ascending) whose weight
-// reaches ceil(p * W).  Weights are fixed-point, w = floor(s * 2^shift) for finite s > 0
-// (0 otherwise), with shift chosen from the largest score and the entry count so that
-// the total W stays below 2^52; every sum is then exact integer arithmetic and the hit
-// set does not depend on the order of the additions.
+// reaches p times the total weight.  A finite positive score weighs exactly its value;
+// other entries weigh nothing and are never hits.  Every sum is exact:
+//   - a finite positive float32 is M * 2^(E-150) with the integer M = 1.mantissa * 2^23
+//     (subnormals: M = mantissa, E = 1);
+//   - the first radix digit of a score (its top 11 bits) fixes E, so one histogram bin
+//     holds scores of a single exponent and its weight is the integer sum of their M;
+//   - the last block of the first pass adds the bins as multi-word integers in units of
+//     2^-149 (the spacing of the smallest subnormal) and compares them with the target
+//     p * W, both exact, to find the boundary bin and what is missing of the target in
+//     that bin's units;
+//   - from there every candidate shares E, so the later passes are uint64 sums of M.
+// The hit set therefore does not depend on the order of any addition.
 //
 // Steps (no host synchronisation):
-//   1. the largest score (integer atomic max of its bits);
-//   2. three weighted radix passes over the 11-, 11- and 10-bit digits of the score bits:
+//   1. three weighted radix passes over the 11-, 11- and 10-bit digits of the score bits:
 //      per-block LDS histograms of weight sums (64-bit integer atomics), merged by the
-//      last block in block order, which fixes the digit where the weight counted from
-//      the top reaches what is still missing of the target.  Afterwards T is the
-//      boundary score and c the number of entries equal to T (lowest indices first)
-//      that complete the target;
-//   3. a count pass (entries equal to T per block) and an update pass that walks the
+//      last block, which fixes the digit where the weight counted from the top reaches
+//      what is still missing of the target.  Afterwards T is the boundary score and c the
+//      number of entries equal to T (lowest indices first) that complete the target;
+//   2. a count pass (entries equal to T per block) and an update pass that walks the
 //      entries in index order, decides hits and writes KS (and the hit mask).
 #include "kv_internal.h"
 
@@ -28,20 +34,17 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBlocks = 64;
 constexpr int kBins = 2048;
+constexpr int kLimbs = 12;          // 384-bit integers: the total weight stays below 2^336
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt not waited for
 constexpr int kVmcntZero = (7 << 4) | (15 << 8);
 
 __device__ __forceinline__ bool has_weight(float s) { return s > 0.f && s <= 3.402823466e38f; }
 
-__device__ __forceinline__ int weight_shift(uint32_t max_bits, int64_t n) {
-  int e;
-  frexpf(__uint_as_float(max_bits), &e);          // max < 2^e
-  const int lg = n > 1 ? 64 - __clzll((unsigned long long)(n - 1)) : 0;  // ceil(log2 n)
-  return 52 - lg - e;
-}
-
-__device__ __forceinline__ uint64_t weight(float s, int shift) {
-  return has_weight(s) ? (uint64_t)floor(ldexp((double)s, shift)) : 0ull;
+// M of a finite positive score: the significand as an integer (24 bits at most)
+__device__ __forceinline__ uint64_t weight(float s) {
+  if (!has_weight(s)) return 0ull;
+  const uint32_t b = __float_as_uint(s);
+  return (uint64_t)((b & 0x7FFFFFu) | ((b >> 23) != 0 ? 0x800000u : 0u));
 }
 
 __device__ __forceinline__ int pass_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
@@ -83,10 +86,9 @@ __global__ __launch_bounds__(64) void lrfu_init_kernel(ToppState* st) {
     z.mask = 0;
     z.mode = 0;
     z.ticket = 0;
-    z.max_bits = 0;
-    z.pad = 0;
+    z.pad0 = 0;
+    z.pad1 = 0;
     z.rem = 0;
-    z.total = 0;
     z.c_eq = 0;
     *st = z;
   }
@@ -94,48 +96,202 @@ __global__ __launch_bounds__(64) void lrfu_init_kernel(ToppState* st) {
 
 __device__ __forceinline__ float item_score(const LrfuArgs& a, int64_t i) { return a.score[i] * a.scale; }
 
-__global__ __launch_bounds__(kThreads) void lrfu_max_kernel(LrfuArgs a) {
-  __shared__ uint32_t s_max;
-  if (threadIdx.x == 0) s_max = 0;
-  __syncthreads();
-  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
-  const int64_t end = begin + a.per_block < a.n ? begin + a.per_block : a.n;
-  uint32_t m = 0;
-  for (int64_t i = begin + threadIdx.x; i < end; i += kThreads) {
-    const float s = item_score(a, i);
-    if (has_weight(s)) m = max(m, __float_as_uint(s));   // positive floats order as integers
-  }
+// ---- multi-word unsigned integers: kLimbs little-endian 32-bit limbs
+struct Big {
+  uint32_t l[kLimbs];
+};
+
+// Carry-propagate per-limb sums (each below 2^63) into limbs.
+__device__ __forceinline__ Big normalize(const uint64_t (&v)[kLimbs]) {
+  Big r;
+  uint64_t carry = 0;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0 && m) atomicMax(&s_max, m);
+  for (int j = 0; j < kLimbs; ++j) {
+    const uint64_t x = v[j] + carry;
+    r.l[j] = (uint32_t)x;
+    carry = x >> 32;
+  }
+  return r;
+}
+
+__device__ __forceinline__ bool big_less(const Big& a, const Big& b) {   // a < b
+#pragma unroll
+  for (int j = kLimbs - 1; j >= 0; --j)
+    if (a.l[j] != b.l[j]) return a.l[j] < b.l[j];
+  return false;
+}
+
+__device__ __forceinline__ bool big_zero(const Big& a) {
+  uint32_t o = 0;
+#pragma unroll
+  for (int j = 0; j < kLimbs; ++j) o |= a.l[j];
+  return o == 0;
+}
+
+// a - b for a >= b
+__device__ __forceinline__ Big big_sub(const Big& a, const Big& b) {
+  Big r;
+  int64_t borrow = 0;
+#pragma unroll
+  for (int j = 0; j < kLimbs; ++j) {
+    const int64_t x = (int64_t)a.l[j] - (int64_t)b.l[j] - borrow;
+    r.l[j] = (uint32_t)x;
+    borrow = x < 0 ? 1 : 0;
+  }
+  return r;
+}
+
+// ceil(a / 2^sh) for 0 <= sh < 32 * kLimbs, when the quotient fits in 64 bits
+__device__ __forceinline__ uint64_t big_shr_ceil64(const Big& a, int sh) {
+  const int q = sh >> 5, r = sh & 31;
+  uint64_t out = 0;
+  bool sticky = false;
+#pragma unroll
+  for (int j = 0; j < kLimbs; ++j) {
+    const uint64_t limb = a.l[j];
+    if (j < q) {
+      sticky |= limb != 0;
+    } else if (j == q) {
+      sticky |= r != 0 && (limb & ((1ull << r) - 1ull)) != 0;
+      out |= limb >> r;
+    } else if (j - q < 3) {
+      // limb j lands at bit 32*(j-q) - r of the quotient; bits beyond 63 are zero
+      // when the quotient fits in 64 bits
+      const int pos = 32 * (j - q) - r;
+      if (pos < 64) out |= limb << pos;
+    }
+  }
+  return out + (sticky ? 1ull : 0ull);
+}
+
+// ceil(mp * T / 2^k) for a 24-bit mp and 23 <= k < 32 * kLimbs (p = mp * 2^-k <= 1)
+__device__ Big topp_target(const Big& T, uint32_t mp, int k) {
+  uint32_t x[kLimbs + 1];
+  uint64_t carry = 0;
+  for (int j = 0; j < kLimbs; ++j) {
+    const uint64_t v = (uint64_t)T.l[j] * mp + carry;
+    x[j] = (uint32_t)v;
+    carry = v >> 32;
+  }
+  x[kLimbs] = (uint32_t)carry;
+  const int q = k >> 5, r = k & 31;
+  bool sticky = false;
+  for (int j = 0; j < q; ++j) sticky |= x[j] != 0;
+  if (r) sticky |= (x[q] & ((1u << r) - 1u)) != 0;
+  Big t;
+  for (int j = 0; j < kLimbs; ++j) {
+    const int src = j + q;
+    const uint64_t lo = src <= kLimbs ? x[src] : 0u;
+    const uint64_t hi = src + 1 <= kLimbs ? x[src + 1] : 0u;
+    t.l[j] = (uint32_t)(((hi << 32) | lo) >> r);
+  }
+  if (sticky) {
+    for (int j = 0; j < kLimbs; ++j) {
+      if (++t.l[j] != 0) break;
+    }
+  }
+  return t;
+}
+
+// Pass 0, last block: finds the boundary bin of the exact top-p set.  Thread t < 256
+// owns exponent E = 255 - t (descending), i.e. bins 4E..4E+3 (bins >= 1024 hold no
+// positive score), whose weight is Y = sum of M times 2^(max(E,1) - 1) units of 2^-149.
+// A scan over the threads gives every exponent's cumulative weight from the top as an
+// exact multi-word integer; the target is ceil(p * W) in the same units (the prefix
+// weight is an integer, so reaching p * W is reaching its ceiling).
+__device__ void topp_first_digit(const unsigned long long* h, float top_p, ToppState& st,
+                                 uint64_t (*s_wtot)[kLimbs], Big& s_total, Big& s_target) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int e = 255 - tid;
+  uint64_t y = 0;
+  if (e >= 0) y = h[4 * e + 3] + h[4 * e + 2] + h[4 * e + 1] + h[4 * e];
+  const int sh = (e > 0 ? e : 1) - 1;
+  // y * 2^sh spread over limbs j0, j0+1, j0+2
+  const int j0 = sh >> 5, o = sh & 31;
+  const uint64_t lo64 = y << o;
+  const uint64_t top = o ? (y >> (64 - o)) : 0ull;
+  uint64_t own[kLimbs], inc[kLimbs];
+#pragma unroll
+  for (int j = 0; j < kLimbs; ++j) {
+    own[j] = j == j0 ? (lo64 & 0xFFFFFFFFull) : (j == j0 + 1 ? (lo64 >> 32) : (j == j0 + 2 ? top : 0ull));
+    if (e < 0) own[j] = 0;
+    inc[j] = own[j];
+  }
+  // inclusive per-limb scan in thread order (each partial sum stays below 2^43)
+#pragma unroll
+  for (int j = 0; j < kLimbs; ++j) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t v = shfl_up64(inc[j], off);
+      if (lane >= off) inc[j] += v;
+    }
+    if (lane == 63) s_wtot[wv][j] = inc[j];
+  }
   __syncthreads();
-  if (threadIdx.x == 0 && s_max) atomicMax(&a.st->max_bits, s_max);
+  for (int w = 0; w < wv; ++w) {
+#pragma unroll
+    for (int j = 0; j < kLimbs; ++j) inc[j] += s_wtot[w][j];
+  }
+  uint64_t exc[kLimbs];
+#pragma unroll
+  for (int j = 0; j < kLimbs; ++j) exc[j] = inc[j] - own[j];
+  const Big C = normalize(inc), E = normalize(exc);
+  if (tid == 255) s_total = C;
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t pb = __float_as_uint(top_p);
+    const uint32_t pe = (pb >> 23) & 0xFFu, pm = pb & 0x7FFFFFu;
+    const uint32_t mp = pe ? (pm | 0x800000u) : pm;
+    const int k = 150 - (pe ? (int)pe : 1);        // p = mp * 2^-k, k >= 23 for p <= 1
+    if (mp == 0 || big_zero(s_total)) {
+      st.mode = 2u;                                // target 0: no hits
+    } else {
+      s_target = topp_target(s_total, mp, k);
+      st.mode = 0u;
+    }
+    st.prefix = 0;
+    st.mask = 0;
+  }
+  __syncthreads();
+  if (st.mode == 0u && e >= 0 && y != 0 && big_less(E, s_target) && !big_less(C, s_target)) {
+    // the boundary lies in exponent E: what the prefix still needs, in units of 2^sh
+    const uint64_t need = big_shr_ceil64(big_sub(s_target, E), sh);
+    uint64_t cum = 0;
+    for (int b = 4 * e + 3; b >= 4 * e; --b) {
+      if (cum + h[b] >= need) {
+        st.rem = need - cum;
+        st.prefix = (uint32_t)b << 21;
+        st.mask = 2047u << 21;
+        break;
+      }
+      cum += h[b];
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pass) {
   __shared__ unsigned long long h[kBins];
   __shared__ uint64_t s_wsum[kWaves];
+  __shared__ uint64_t s_wtot[kWaves][kLimbs];
+  __shared__ Big s_total, s_target;
   __shared__ int s_last;
   __shared__ ToppState st;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int b = tid; b < kBins; b += kThreads) h[b] = 0;
   __syncthreads();
-  const uint32_t max_bits = a.st->max_bits;
-  if (max_bits == 0) return;                  // no entry carries weight: no hits
   const uint32_t mode = pass == 0 ? 0u : a.st->mode;
-  if (mode != 0) return;
+  if (mode != 0) return;                      // no hits (every block reads the same word)
   const uint32_t prefix = pass == 0 ? 0u : a.st->prefix;
   const uint32_t mask = pass == 0 ? 0u : a.st->mask;
   const int shift = pass_shift(pass);
   const uint32_t dmask = pass_dmask(pass);
-  const int wsh = weight_shift(max_bits, a.n);
 
   const int64_t begin = (int64_t)blockIdx.x * a.per_block;
   const int64_t end = begin + a.per_block < a.n ? begin + a.per_block : a.n;
   for (int64_t i0 = begin; i0 < end; i0 += kThreads) {
     const int64_t i = i0 + tid;
     const float s = i < end ? item_score(a, i) : 0.f;
-    const uint64_t w = weight(s, wsh);
+    const uint64_t w = weight(s);
     const uint32_t key = __float_as_uint(s);
     hist_add(h, w != 0 && (key & mask) == prefix, (key >> shift) & dmask, w);
   }
@@ -157,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pas
   // histograms below are read with cache-bypassing atomic loads)
   if (threadIdx.x < 64) __threadfence();
 
-  // ---- last block: global weighted histogram (blocks in order), then the digit
+  // ---- last block: global weighted histogram (integer sums), then the digit
   const int nb = (int)gridDim.x;
   for (int b = tid; b < kBins; b += kThreads) {
     unsigned long long tot = 0;
@@ -167,28 +323,22 @@ __global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pas
   }
   __syncthreads();
   if (tid == 0) st = *a.st;
-  // thread t owns bins 2047-2t and 2046-2t (descending)
-  const uint64_t c0 = h[kBins - 1 - 2 * tid], c1 = h[kBins - 2 - 2 * tid];
-  uint64_t incl = c0 + c1;
+  __syncthreads();
+  if (pass == 0) {
+    topp_first_digit(h, a.top_p, st, s_wtot, s_total, s_target);
+    __syncthreads();
+  } else {
+    // every candidate shares the exponent: weights are uint64 sums of M.
+    // thread t owns bins 2047-2t and 2046-2t (descending)
+    const uint64_t c0 = h[kBins - 1 - 2 * tid], c1 = h[kBins - 2 - 2 * tid];
+    uint64_t incl = c0 + c1;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t v = shfl_up64(incl, off);
-    if (lane >= off) incl += v;
-  }
-  if (lane == 63) s_wsum[wv] = incl;
-  __syncthreads();
-  if (pass == 0 && tid == 0) {
-    uint64_t total = 0;
-    for (int w = 0; w < kWaves; ++w) total += s_wsum[w];
-    const double target = ceil((double)a.top_p * (double)total);
-    st.total = total;
-    st.rem = target > 0.0 ? (uint64_t)target : 0ull;
-    st.mode = st.rem == 0 ? 2u : 0u;
-    st.prefix = 0;
-    st.mask = 0;
-  }
-  __syncthreads();
-  if (st.mode == 0) {
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t v = shfl_up64(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) s_wsum[wv] = incl;
+    __syncthreads();
     const uint64_t rem = st.rem;
     uint64_t before = 0;
     for (int w = 0; w < wv; ++w) before += s_wsum[w];
@@ -202,6 +352,7 @@ __global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pas
       digit = kBins - 2 - 2 * tid;
       above = excl + c0;
     }
+    __syncthreads();
     if (digit >= 0) {
       st.rem = rem - above;
       st.prefix |= (uint32_t)digit << shift;
@@ -209,8 +360,8 @@ __global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pas
     }
     __syncthreads();
     if (pass == 2 && tid == 0) {
-      // entries equal to the boundary score all weigh w*; c of them complete the target
-      const uint64_t ws = weight(__uint_as_float(st.prefix), wsh);
+      // entries equal to the boundary score all weigh M*; c of them complete the target
+      const uint64_t ws = weight(__uint_as_float(st.prefix));
       st.c_eq = ws ? (int64_t)((st.rem + ws - 1) / ws) : 0;
     }
   }
@@ -233,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void lrfu_count_kernel(LrfuArgs a) {
   const int64_t begin = (int64_t)blockIdx.x * a.per_block;
   const int64_t end = begin + a.per_block < a.n ? begin + a.per_block : a.n;
   uint32_t eq = 0;
-  if (st.max_bits != 0)
+  if (st.mode == 0)
     for (int64_t i = begin + threadIdx.x; i < end; i += kThreads) eq += boundary_equal(a, st, item_score(a, i));
   if (eq) atomicAdd(&s_eq, eq);
   __syncthreads();
@@ -261,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void lrfu_update_kernel(LrfuArgs a) {
   __shared__ uint32_t s_wave[kWaves];
   __shared__ int64_t s_eq_before;
   const ToppState st = *a.st;
-  const bool any = st.max_bits != 0 && st.mode == 0;
+  const bool any = st.mode == 0;
   if (threadIdx.x == 0) {
     int64_t eqb = 0;
     for (int b = 0; b < (int)blockIdx.x; ++b) eqb += a.counts[b];
@@ -307,8 +458,6 @@ hipError_t launch_lrfu(const LrfuArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(a.n_blocks), block(kThreads);
-  hipLaunchKernelGGL(lrfu_max_kernel, grid, block, 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int pass = 0; pass < 3; ++pass) {
     hipLaunchKernelGGL(lrfu_hist_kernel, grid, block, 0, s, a, pass);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -1,7 +1,7 @@
 // Windowed attention mass on gfx950: the one dense contraction of the path.
 //
-// What is computed (MemDecay, Method: windowed attention mass averaged over heads and
-// layers; ActKV Sec. 2.3 and 7.1: A = exp(q.k - LSE) recovered from the log-sum-exp;
+// What is computed (MemDecay, Method: the attention a token receives from the window
+// queries, a mean over layers and heads; ActKV Sec. 2.3 and 7.1: A = exp(q.k - LSE) recovered from the log-sum-exp;
 // PACE Sec. 2: SnapKV's observation window):
 //   for every layer l, KV head g and window row r = (window query w, query head h of
 //   g's GQA group), s_rj = scale * <q_r, k_j> over keys j <= N - W + w;
@@ -795,6 +795,7 @@ hipError_t launch_nw(const ScoreArgs& a, int nw, hipStream_t s) {
 // LSE of each row from its per-chunk (max, sum) partials, or from the caller's LSE.
 __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx == 0 && a.status) *a.status = 0u;   // the epilogue, later on the stream, sets bits
   if (idx >= (int64_t)a.n_lg * a.rows) return;
   const int lg = (int)(idx / a.rows);
   const int row = (int)(idx - (int64_t)lg * a.rows);

@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define KV_ABI_VERSION 2
+#define KV_ABI_VERSION 3
 
 /* return codes */
 #define KV_OK 0
@@ -53,6 +53,8 @@ extern "C" {
 #define KV_STATUS_NAN_SCORE 2u          /* some score was NaN; NaN orders after numbers */
 #define KV_STATUS_KEEP_OVERFLOW 4u      /* keep list larger than keep_capacity; only the
                                            first keep_capacity entries were written */
+/* bit of the device status word written by kv_score */
+#define KV_STATUS_BAD_REGION 8u         /* some region label was >= n_regions */
 
 /*
  * One sequence row of a paged KV cache, all layers (ActKV Sec. 2.5: PagedKVCache
@@ -96,8 +98,8 @@ typedef struct kv_meta_desc {
 /*
  * kv_score parameters.
  *
- * Attention mass (MemDecay, Method: windowed mean attention mass averaged over heads
- * and layers; ActKV Sec. 2.3 / 7.1: A = exp(q.k - LSE); PACE Sec. 2: SnapKV window):
+ * Attention mass (MemDecay, Method: the attention weight a token receives from the
+ * window queries, taken as a mean over layers and heads; ActKV Sec. 2.3 / 7.1: A = exp(q.k - LSE); PACE Sec. 2: SnapKV window):
  * the W window queries are the last W tokens of the row.  For layer l, query head h
  * (KV head h / (Hq/Hkv)) and window query w at position N-W+w,
  *     s_j = scale * <q[l][w][h], k[l][j][h/G]>  for j <= N-W+w,
@@ -117,9 +119,12 @@ typedef struct kv_meta_desc {
  * Foresight bonus (PACE Sec. 3.1 and 7): bonus = bonus_floor*(1 + 1/d) for the token's
  * span when d = span_next_use[span_id[i]] >= 1, else 0 (d = steps until the soonest
  * future step that reads the span).
+ * A span id outside [0, n_spans) names no span (no bonus).
  * Pinned tokens (MemDecay pinned regions; PACE Table 1 sinks and recent window): a token
  * is pinned if its region bit is set in pinned_regions, or i < n_sink, or
  * i >= N - n_recent, or token_pinned[i] != 0.
+ * A region label >= n_regions names no region: the token gets b = lambda = 0, no region
+ * pinning, and KV_STATUS_BAD_REGION is set in *status.
  * Items: item_tokens == 1 scores tokens; item_tokens == page_size scores pages by the
  * mean of their tokens' scores (MemDecay S_p, over the tokens present) and pins a page
  * when any of its tokens is pinned.
@@ -138,7 +143,7 @@ typedef struct kv_score_params {
   const uint8_t *region;      /* [N] region label per token (NULL: no regions) */
   const float *base_prio;     /* [n_regions] b_r >= 0 */
   const float *decay_rate;    /* [n_regions] lambda_r >= 0 */
-  int32_t n_regions;          /* 1..32; labels must be < n_regions */
+  int32_t n_regions;          /* 1..32; labels are expected below n_regions */
   float rho, alpha, tau;
   float *ewma;                /* [N] in/out (MEMDECAY) */
   int32_t *clock;             /* [N] in/out (MEMDECAY) */
@@ -164,6 +169,8 @@ typedef struct kv_score_params {
      pass, after it, after the LSE combine, after the mass pass and after the epilogue */
   hipEvent_t *stage_events;
   int32_t aggregate;          /* KV_AGG_*; memset-zeroed params select KV_AGG_SUM */
+  uint32_t *status;           /* device word or NULL: set to 0, then KV_STATUS_BAD_REGION
+                                 when some label is >= n_regions */
 } kv_score_params;
 
 int32_t kv_abi_version(void);
@@ -208,11 +215,12 @@ int32_t kv_lrfu_workspace_size(int64_t n, size_t *bytes /* host */);
  * Action-Guided KV Cache Management", Sec. 5.1, Algorithm 1, steps 4-7):
  *   s_j = attn_score[j] * scale (float32; e.g. kv_score's group-maximum mass times
  *         1/(L*Hkv*W) gives the mean over layers, KV heads and action queries);
- *   hit_j: j is in the top-p set, the smallest prefix of the entries in the order
- *         (s descending, index ascending) whose weight reaches ceil(top_p * W), with
- *         fixed-point weights w = floor(s * 2^shift) for finite s > 0 (else 0),
- *         shift = 52 - ceil(log2 n) - e and max s < 2^e, W the total weight; no hits
- *         when that target is 0;
+ *   hit_j: j is in the top-p set, the shortest prefix of the entries in the order
+ *         (s descending, index ascending, -0 == +0) whose weight reaches top_p * W, where
+ *         a finite s > 0 weighs exactly s (other entries weigh 0 and are never hits), W
+ *         is the total weight, and every sum and the comparison are exact (no rounding
+ *         of any sum); no hits when top_p * W is 0.  top_p = 1 makes every positive
+ *         score a hit;
  *   keep_score[j] <- decay * keep_score[j] + (hit_j ? s_j : 0).
  * New entries enter with keep_score 0 (the caller appends them).  The retained set is
  * then kv_select(keep_score, NULL, ...) (Algorithm 1, step 8).  hit (n bytes, 0/1) may be
@@ -252,6 +260,8 @@ int32_t kv_compact_tail_inplace(const kv_cache_desc *cache, const int32_t *keep_
  * shape, dst.n_tokens >= count, not overlapping src).  evicted_tokens[r] (device,
  * nullable) receives the token index of slot r, and every meta array is gathered the
  * same way (dst[r] = src[token]).  KV_EINVAL when first + count exceeds N - n_keep.
+ * keep_tokens must be strictly ascending in [0, N); a rank whose token would fall outside
+ * the row because of a malformed list is skipped (its slot and id are not written).
  */
 int32_t kv_gather_evicted(const kv_cache_desc *src, const int32_t *keep_tokens, int64_t n_keep,
                           int64_t first, int64_t count, const kv_cache_desc *dst,
@@ -314,36 +324,52 @@ int32_t kv_compact_rerope(const kv_cache_desc *src, const kv_cache_desc *dst,
 
 /*
  * RoPE frequency tables (PACE Sec. 3.5: split-half RoPE with static frequency scaling,
- * default, linear, YaRN and Llama-3 style).  theta_i (i < 64) rotates pair (i, i + 64).
- *   KV_ROPE_DEFAULT: theta_i = base^(-2i/128)
- *   KV_ROPE_LINEAR:  theta_i = base^(-2i/128) / factor
- *   KV_ROPE_LLAMA3:  with w_i = 2 pi / base^(-2i/128) and L = original_max_position:
- *                    w_i < L/high_freq_factor keeps the frequency, w_i > L/low_freq_factor
- *                    divides it by factor, in between (1-t)/factor + t times it with
- *                    t = (L/w_i - low_freq_factor) / (high_freq_factor - low_freq_factor)
- *   KV_ROPE_YARN:    r_i = L / w_i, g = clamp((r_i - beta_slow)/(beta_fast - beta_slow), 0, 1),
- *                    (1-g)/factor + g times the frequency (only the rotation: a magnitude
- *                    factor applied when the key was cached stays in it)
+ * default, linear, YaRN and Llama-3 style).  theta_i (i < 64) rotates pair (i, i + 64);
+ * f_i = base^(-2i/128) is the unscaled frequency and L = original_max_position.
+ *   KV_ROPE_DEFAULT: theta_i = f_i
+ *   KV_ROPE_LINEAR:  theta_i = f_i / factor
+ *   KV_ROPE_LLAMA3:  with w_i = 2 pi / f_i: w_i < L/high_freq_factor keeps the frequency,
+ *                    w_i > L/low_freq_factor divides it by factor, in between
+ *                    (1-t)/factor + t times it, t = (L/w_i - low_freq_factor) /
+ *                    (high_freq_factor - low_freq_factor)
+ *   KV_ROPE_YARN:    YaRN's "NTK-by-parts" in the form engines cache keys with: the pair
+ *                    turning beta times over L is i(beta) = 128 ln(L/(2 pi beta)) / (2 ln base);
+ *                    lo = floor(i(beta_fast)), hi = ceil(i(beta_slow)) (no rounding with
+ *                    KV_ROPE_YARN_NO_TRUNCATE), clamped to [0, 127], hi = lo + 0.001 if
+ *                    equal; g_i = clamp((i - lo)/(hi - lo), 0, 1) and
+ *                    theta_i = g_i f_i / factor + (1 - g_i) f_i
+ *   KV_ROPE_YARN_RATIO: the same blend written over r_i = L / w_i as the YaRN paper states
+ *                    it: g = clamp((r_i - beta_slow)/(beta_fast - beta_slow), 0, 1),
+ *                    theta_i = (1-g) f_i / factor + g f_i (differs from KV_ROPE_YARN inside
+ *                    the band; use the form the model's keys were rotated with)
  *   KV_ROPE_TABLE:   the caller's 64 frequencies (host array)
+ * Only the rotation is applied: a magnitude factor applied when a key was cached (YaRN's
+ * attention temperature) stays in it through any re-rotation.
  */
 #define KV_ROPE_DEFAULT 0
 #define KV_ROPE_LINEAR 1
 #define KV_ROPE_LLAMA3 2
 #define KV_ROPE_YARN 3
 #define KV_ROPE_TABLE 4
+#define KV_ROPE_YARN_RATIO 5
+
+#define KV_ROPE_YARN_NO_TRUNCATE 1   /* kv_rope.flags: keep YaRN's band ends unrounded */
 
 typedef struct kv_rope {
   int32_t kind;                 /* KV_ROPE_* */
-  int32_t original_max_position;/* L for LLAMA3 and YARN */
+  int32_t original_max_position;/* L for LLAMA3 and the YARN kinds */
   double base;                  /* rope_theta, > 1 */
-  double factor;                /* LINEAR, LLAMA3, YARN: > 0 */
+  double factor;                /* LINEAR, LLAMA3, YARN kinds: > 0 */
   double low_freq_factor;       /* LLAMA3 */
   double high_freq_factor;      /* LLAMA3, > low_freq_factor */
-  double beta_fast, beta_slow;  /* YARN ramp ends in rotations over L (32 and 1 typical) */
+  double beta_fast, beta_slow;  /* YARN kinds: band ends in turns over L (32 and 1 typical),
+                                   beta_fast > beta_slow > 0 */
   const double *inv_freq;       /* host [64], KV_ROPE_TABLE */
+  int32_t flags;                /* KV_ROPE_YARN_NO_TRUNCATE or 0 */
+  int32_t reserved;
 } kv_rope;
 
-/* Host-only.  The 64 frequencies of *rope; KV_EINVAL for an unknown kind or a bad
+/* Host-only.  The 64 frequencies of *rope; KV_EINVAL for an unknown kind or flag or a bad
  * parameter (non-positive factor, base <= 1, non-finite table entry). */
 int32_t kv_rope_inv_freq(const kv_rope *rope, double inv_freq[64] /* host */);
 

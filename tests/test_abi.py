@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     lib = kv.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert kv.kv_abi_version() == kv.KV_ABI_VERSION == 2
+    assert kv.kv_abi_version() == kv.KV_ABI_VERSION == 3
 
 
 def test_strerror_texts():
@@ -192,7 +192,9 @@ def test_binding_refuses_host_tensors():
 @pytest.mark.parametrize("kind,kw", [
     ("default", {}), ("linear", dict(factor=4.0)),
     ("llama3", dict(factor=8.0, original_max_position=8192, low_freq_factor=1.0, high_freq_factor=4.0)),
-    ("yarn", dict(factor=16.0, original_max_position=4096, beta_fast=32.0, beta_slow=1.0))])
+    ("yarn", dict(factor=16.0, original_max_position=4096, beta_fast=32.0, beta_slow=1.0)),
+    ("yarn", dict(factor=4.0, original_max_position=32768, beta_fast=16.0, beta_slow=2.0, truncate=False)),
+    ("yarn_ratio", dict(factor=16.0, original_max_position=4096, beta_fast=32.0, beta_slow=1.0))])
 @pytest.mark.parametrize("base", [1e4, 5e5, 1e6])
 def test_rope_tables_match_oracle(kind, kw, base):
     """kv_rope_inv_freq (host-only) against the oracle's scaled tables."""
@@ -206,9 +208,14 @@ def test_rope_table_validation_and_explicit_table():
     for bad in (kv.kv_rope("default", base=1.0), kv.kv_rope("linear", factor=0.0),
                 kv.kv_rope("llama3", factor=8.0, low_freq_factor=4.0, high_freq_factor=1.0),
                 kv.kv_rope("yarn", factor=2.0, beta_fast=1.0, beta_slow=32.0),
-                kv.kv_rope(7), kv.kv_rope("table"),
+                kv.kv_rope("yarn_ratio", factor=2.0, beta_fast=32.0, beta_slow=0.0),
+                kv.kv_rope("yarn", factor=2.0, original_max_position=0),
+                kv.kv_rope(7), kv.kv_rope(6), kv.kv_rope("table"),
                 kv.kv_rope("table", table=[1.0] * 63 + [float("nan")])):
         assert L.kv_rope_inv_freq(ctypes.byref(bad), out) == kv.KV_EINVAL
+    flags = kv.kv_rope("yarn", factor=2.0)
+    flags.flags = 2                                           # no such flag
+    assert L.kv_rope_inv_freq(ctypes.byref(flags), out) == kv.KV_EINVAL
     tab = [0.5 ** i for i in range(64)]
     assert kv.kv_rope_inv_freq(kv.kv_rope("table", table=tab)) == tab
 

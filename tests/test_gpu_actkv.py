@@ -1,9 +1,10 @@
 """GPU parity of ActKV's LRFU keep scores (top-p hit mask) and in-place tail compaction
 (kv_lrfu_update, kv_compact_tail_inplace) against the oracle.
 
-Bars: hit masks, moved slots, metadata and status bit-exact (integer decisions, taken in
-the same fixed-point arithmetic on both sides); keep scores within 1e-6 relative
-(float32 update against float64).
+Bars: hit masks, moved slots, metadata and status bit-exact (the top-p set is decided
+from exact sums of the float32 scores on both sides: rationals in the oracle, multi-word
+integers on the device); keep scores within 1e-6 relative (float32 update against
+float64).
 """
 import numpy as np
 import pytest
@@ -33,6 +34,17 @@ def _scores(rng, n, dist):
         return np.full(n, 0.125, np.float32)
     if dist == "tiny":
         return (rng.random(n) * 1e-30).astype(np.float32)
+    if dist == "wide":
+        # 10^U(-45, 0): normal and subnormal float32 scores over the whole range
+        s = np.power(10.0, rng.uniform(-45.0, 0.0, n)).astype(np.float32)
+        s[rng.random(n) < 0.05] = 0.0
+        return s
+    if dist == "twobinade":
+        # one dominant score and many others from a single small exponent: the boundary
+        # falls among equal-exponent scores far below the largest
+        s = (1.0 + rng.random(n)).astype(np.float32) * np.float32(2.0 ** -100)
+        s[0] = 1.0
+        return s
     raise ValueError(dist)
 
 
@@ -46,6 +58,14 @@ def _scores(rng, n, dist):
     (100_000, "ties", 1.0, 1.0),
     (100_000, "mixed", 0.0, 1.0),
     (262_147, "power", 0.999, 3.0),
+    (5000, "wide", 1.0, 1.0),                     # every positive score is a hit
+    (5000, "wide", 0.999, 1.0),
+    (100_000, "wide", 0.9, 1.0),
+    (70_000, "wide", 1.0, 1e-20),                 # products underflow to subnormals and 0
+    (4097, "twobinade", 1.0, 1.0),
+    (4097, "twobinade", float(np.nextafter(np.float32(1.0), np.float32(0.0))), 1.0),
+    (1_048_583, "power", 0.9, 1.0),               # the largest block count, ragged tail
+    (1_048_583, "ties", 0.75, 1.0),
 ])
 def test_lrfu_update_parity(n, dist, p, scale):
     rng = np.random.default_rng(n + len(dist))

@@ -43,9 +43,11 @@ def assert_rel(got, ref, rtol=RTOL, what=""):
 
 
 def ulp_bf16(x):
+    """Spacing of bf16 values at |x|: 2**(e-8) for |x| in [2**(e-1), 2**e), never below the
+    subnormal spacing 2**-133 (which is also the spacing at 0)."""
     x = np.abs(np.asarray(x, np.float64))
     _, e = np.frexp(x)
-    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+    return np.where(x == 0, 2.0 ** -133, np.ldexp(1.0, np.maximum(e, -125) - 8))
 
 
 def assert_bf16_within_1ulp(got, ref, what=""):
@@ -316,9 +318,9 @@ def test_score_memdecay_sixteen_steps():
                            ewma=ref_ewma, clock=ref_clock, pinned_regions=1, item_tokens=16)
         excluded |= np.abs(ref["abar"] - f32(w.tau)) <= 1e-5 * f32(w.tau)
         ok = ~excluded
-        assert_rel(np64(dev["ewma"].cpu())[ok], ref["ewma"][ok], rtol=2e-5, what=f"ewma step {step}")
+        assert_rel(np64(dev["ewma"].cpu())[ok], ref["ewma"][ok], what=f"ewma step {step}")
         assert (dev["clock"].cpu().numpy()[ok] == ref["clock"][ok]).all(), step
-        assert_rel(np64(got["token_score"])[ok], ref["token_score"][ok], rtol=2e-5, what=f"score step {step}")
+        assert_rel(np64(got["token_score"])[ok], ref["token_score"][ok], what=f"score step {step}")
         ref_ewma, ref_clock = ref["ewma"], ref["clock"]
     assert excluded.mean() < 0.01
 
@@ -331,6 +333,12 @@ def test_score_h2o_foresight_parity(over, shuffle):
     w = synth.workload("qwen3-8b-n100k", **over)
     k, v, bt, q = _make_score_inputs(w, seed=w.n_tokens, shuffle=shuffle)
     span_id, next_use = synth.spans(w, seed=3, p_needed=0.2)
+    # tokens outside every span (-1) and ids that name no span of the table get no bonus
+    g = torch.Generator().manual_seed(w.n_tokens)
+    r = torch.rand(w.n_tokens, generator=g)
+    span_id = torch.where(r < 0.05, torch.full_like(span_id, -1), span_id)
+    span_id = torch.where((r >= 0.05) & (r < 0.08), span_id + w.n_spans, span_id)
+    span_id[:3] = torch.tensor([-2 ** 31, 2 ** 31 - 1, w.n_spans], dtype=torch.int32)
     accum = synth.h2o_state(w, seed=3)
     dev_acc = accum.to(DEV)
     got = _run_score(w, k, v, bt, q, policy="h2o", item_tokens=1, state=dict(accum=dev_acc),
@@ -344,7 +352,32 @@ def test_score_h2o_foresight_parity(over, shuffle):
     assert_rel(np64(dev_acc.cpu()), ref["accum"], what="accum")
     assert_rel(np64(got["item_score"]), ref["item_score"], what="score")
     assert (got["item_pinned"].numpy().astype(bool) == ref["item_pinned"]).all()
-    assert (next_use > 0).any()
+    assert (next_use > 0).any() and (span_id < 0).any() and (span_id >= w.n_spans).any()
+
+
+def test_score_bad_region_labels_are_reported():
+    """Labels at or above n_regions name no region (b = lambda = 0, no region pin) and set
+    KV_STATUS_BAD_REGION; a clean row leaves the status word at 0."""
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=1000, n_layers=2, window=32)
+    k, v, bt, q = _make_score_inputs(w, seed=44, shuffle=True)
+    st0 = _memdecay_state(w, seed=44)
+    n_regions = int(st0["base_prio"].numel())
+    bad = torch.zeros(w.n_tokens, dtype=torch.bool)
+    bad[::37] = True
+    region = st0["region"].clone()
+    region[bad] = torch.randint(n_regions, 256, (int(bad.sum()),), generator=torch.Generator().manual_seed(1),
+                                dtype=torch.int32).to(torch.uint8)
+    region[5] = 255
+    st_bad = dict(st0, region=region)
+    for state, want in ((st0, 0), (st_bad, kv.KV_STATUS_BAD_REGION)):
+        dev = {key: t.clone().to(DEV) for key, t in state.items()}
+        status = torch.full((1,), 0x55, dtype=torch.int32, device=DEV)
+        got = _run_score(w, k, v, bt, q, policy="memdecay", item_tokens=1, state=dev, rho=w.rho,
+                         alpha=w.alpha, tau=w.tau, dt_steps=2, pinned_regions=0b11, status=status)
+        assert int(status.item()) == want
+        dev_state = {key: t.cpu() for key, t in dev.items()}
+        kl = _paged_to_logical(k, bt, 16, w.n_tokens)
+        _compare_memdecay(w, q, kl, state, dev_state, got, w.rho, w.alpha, w.tau, 2, 1, 0b11)
 
 
 def test_score_with_supplied_lse():
@@ -356,7 +389,7 @@ def test_score_with_supplied_lse():
     acc = torch.zeros(w.n_tokens, device=DEV)
     got = _run_score(w, k, v, bt, q, policy="h2o", item_tokens=1, state=dict(accum=acc),
                      lse_in=torch.from_numpy(lse).float().to(DEV))
-    assert_rel(np64(got["mass"]), mass, rtol=2e-5, what="mass with supplied LSE")
+    assert_rel(np64(got["mass"]), mass, what="mass with supplied LSE")
 
 
 @pytest.mark.parametrize("hq,hkv,window,n_tokens,n_layers", [
@@ -411,7 +444,7 @@ def test_score_supplied_lse_both_modes(aggregate, shift):
     got = _run_score(w, k, v, bt, q, policy="h2o", item_tokens=1,
                      state=dict(accum=torch.zeros(w.n_tokens, device=DEV)),
                      lse_in=torch.from_numpy(lse_in).to(DEV), aggregate=aggregate)
-    assert_rel(np64(got["mass"]), mass, rtol=2e-5, what=f"{aggregate} with supplied LSE")
+    assert_rel(np64(got["mass"]), mass, what=f"{aggregate} with supplied LSE")
     assert np.abs(np64(got["lse"]) - lse_in).max() < 1e-5
 
 
@@ -573,6 +606,7 @@ def test_full_size_qwen3_100k_mass_is_additive_over_layers(qwen3_100k, aggregate
                           q[l0:l0 + 2].contiguous(), policy="h2o", item_tokens=1, state=dict(accum=acc),
                           aggregate=aggregate)
         total += np64(part["mass"])
+        # two device runs, each within 1e-5 of the exact LSE
         assert np.abs(np64(full["lse"][l0:l0 + 2]) - np64(part["lse"])).max() < 2e-5, l0
     assert_rel(np64(full["mass"]), total, rtol=2 * RTOL, what=f"36-layer {aggregate} mass vs 2-layer runs")
 
@@ -716,6 +750,7 @@ def test_full_size_qwen3_1m_step_properties():
         part = _run_score(w2, k[l0:l0 + 2].contiguous(), v[l0:l0 + 2].contiguous(), None,
                           q[l0:l0 + 2].contiguous(), policy="h2o", item_tokens=1, state=dict(accum=acc))
         total += np64(part["mass"])
+        # two device runs, each within 1e-5 of the exact LSE
         assert np.abs(np64(lse[l0:l0 + 2]) - np64(part["lse"])).max() < 2e-5, l0
     assert_rel(m, total, rtol=2 * RTOL, what="1M-token mass vs sum of 2-layer runs")
     del k, v
@@ -732,7 +767,7 @@ def test_degenerate_sizes():
     got = _run_score(w, k.to(DEV), v.to(DEV), None, q, policy="h2o", item_tokens=1, state=dict(accum=acc))
     s = np.einsum("ld,ld->l", np64(q)[:, 0, 0], np64(k)[:, 0, 0, 0]) / math.sqrt(128)
     assert np.abs(np64(got["lse"]).reshape(-1) - s).max() < 1e-5
-    assert abs(float(got["mass"][0]) - 2.0) < 2e-5
+    assert abs(float(got["mass"][0]) - 2.0) <= RTOL * 2.0
     keep = torch.full((4,), -1, dtype=torch.int32, device=DEV)
     nk = torch.zeros(1, dtype=torch.int64, device=DEV)
     kv.kv_select(got["item_score"].to(DEV), None, 1, 1, 1, keep, nk)

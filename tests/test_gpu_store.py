@@ -19,8 +19,10 @@ PG = 16
 
 
 def ulp_bf16(x):
-    _, e = np.frexp(np.abs(np.asarray(x, np.float64)))
-    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+    """bf16 spacing at |x|, with the subnormal spacing 2**-133 at and near 0."""
+    x = np.abs(np.asarray(x, np.float64))
+    _, e = np.frexp(x)
+    return np.where(x == 0, 2.0 ** -133, np.ldexp(1.0, np.maximum(e, -125) - 8))
 
 
 def within_1ulp(got, ref):
@@ -56,6 +58,8 @@ def store_to_dev(ref_k, ref_pos):
     ("linear", dict(factor=4.0)),
     ("llama3", dict(factor=8.0, original_max_position=8192, low_freq_factor=1.0, high_freq_factor=4.0)),
     ("yarn", dict(factor=16.0, original_max_position=4096, beta_fast=32.0, beta_slow=1.0)),
+    ("yarn", dict(factor=4.0, original_max_position=32768, beta_fast=32.0, beta_slow=1.0, truncate=False)),
+    ("yarn_ratio", dict(factor=16.0, original_max_position=4096, beta_fast=32.0, beta_slow=1.0)),
 ])
 def test_compact_scaled_rope_parity(kind, kw):
     rng = np.random.default_rng(40)
