@@ -119,6 +119,7 @@ def lib() -> ctypes.CDLL:
             "kv_score": (i32, [P(KvCacheDesc), P(KvScoreParams), vp, sz, vp]),
             "kv_select_workspace_size": (i32, [i64, P(sz)]),
             "kv_select": (i32, [vp, vp, i64, i32, i64, i64, vp, i64, vp, vp, vp, sz, vp]),
+            "kv_select_noalloc": (i32, [vp, vp, i64, i32, i64, i64, vp, i64, vp, vp, vp]),
             "kv_select_segment": (i32, [i64, i64, i64, i32, vp, i64, vp, P(i64), P(i64), vp]),
             "kv_compact_rerope": (i32, [P(KvCacheDesc), P(KvCacheDesc), vp, vp, i64, vp, vp, i32,
                                         ctypes.c_double, i32, P(KvMetaDesc), i32, vp]),
@@ -285,6 +286,15 @@ def kv_select(item_score, item_pinned, item_tokens, n_tokens, budget_items, keep
                            _ptr(n_keep), _ptr(status), _ptr(workspace), workspace.numel(),
                            _stream(item_score.device)), "kv_select")
     return workspace
+
+
+def kv_select_noalloc(item_score, item_pinned, item_tokens, n_tokens, budget_items, keep_tokens, n_keep,
+                      status=None):
+    """Budget selection in the library's fixed device scratch (see kv_select_noalloc)."""
+    _check(lib().kv_select_noalloc(_ptr(item_score), _ptr(item_pinned), int(item_score.numel()),
+                                   int(item_tokens), int(n_tokens), int(budget_items), _ptr(keep_tokens),
+                                   keep_tokens.numel(), _ptr(n_keep), _ptr(status),
+                                   _stream(item_score.device)), "kv_select_noalloc")
 
 
 def kv_lrfu_workspace_size(n: int) -> int:

@@ -347,6 +347,20 @@ int32_t kv_select(const float* item_score, const uint8_t* item_pinned, int64_t n
   return e == hipSuccess ? KV_OK : hip_fail(e);
 }
 
+int32_t kv_select_noalloc(const float* item_score, const uint8_t* item_pinned, int64_t n_items,
+                          int32_t item_tokens, int64_t n_tokens, int64_t budget_items,
+                          int32_t* keep_tokens, int64_t keep_capacity, int64_t* n_keep,
+                          uint32_t* status, hipStream_t stream) {
+  if (n_items > 0 && select_workspace_bytes(n_items) > kSelectScratchBytes) return KV_EWORKSPACE;
+  int32_t rc = check_device();
+  if (rc) return rc;
+  void* ws = nullptr;
+  const hipError_t e = select_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e);
+  return kv_select(item_score, item_pinned, n_items, item_tokens, n_tokens, budget_items, keep_tokens,
+                   keep_capacity, n_keep, status, ws, kSelectScratchBytes, stream);
+}
+
 int32_t kv_lrfu_workspace_size(int64_t n, size_t* bytes) {
   if (!bytes || n <= 0) return KV_EINVAL;
   *bytes = lrfu_workspace_bytes(n);

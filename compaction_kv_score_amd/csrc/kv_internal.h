@@ -120,6 +120,9 @@ struct SelectArgs {
 constexpr int kSelBins = 2048;     // radix-select histogram bins (11-bit digits)
 int select_blocks(int64_t n_items);
 size_t select_workspace_bytes(int64_t n_items);
+// Fixed per-device scratch that replaces the workspace in kv_select_noalloc.
+constexpr size_t kSelectScratchBytes = 32768;
+hipError_t select_scratch(void** out);   // this device's address of the scratch array
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_segment_keep(int64_t n_tokens, int64_t prefix, int64_t evict, int32_t* keep,
                                int64_t capacity, int64_t* n_keep_dev, int64_t n_keep,

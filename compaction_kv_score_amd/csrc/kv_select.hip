@@ -21,6 +21,8 @@
 //      blocks before it, then walks its items in index order with wavefront ballots and
 //      an LDS scan across waves, and writes the kept token indices.
 
+#include <atomic>
+
 #include "kv_internal.h"
 
 namespace kvs {
@@ -432,6 +434,35 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(select_emit_kernel, grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+// ---- fixed scratch of kv_select_noalloc
+// The selection state, the three pass histograms and the per-block counts of at most
+// kSelMaxBlocks blocks (select_workspace_bytes never exceeds 25,856 bytes) in one file-scope
+// array per device, for callers that cannot allocate.  Each device holds its own copy at
+// its own address; host code only ever uses that address, taken once per device.
+static __device__ __align__(256) unsigned char scratch[kSelectScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch[kScratchDevices];
+}  // namespace
+
+hipError_t select_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // with this device current: the address of its copy of the array
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch_segment_keep(int64_t n_tokens, int64_t prefix, int64_t evict, int32_t* keep,

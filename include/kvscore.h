@@ -207,6 +207,21 @@ int32_t kv_select(const float *item_score, const uint8_t *item_pinned, int64_t n
                   uint32_t *status, void *workspace, size_t workspace_bytes,
                   hipStream_t stream);
 
+/*
+ * kv_select without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and errors as kv_select; the selection state, histograms and
+ * per-block counts live in a fixed 32 KiB device array of the library (one per GPU, held
+ * until the process ends), which covers every n_items (KV_EWORKSPACE if it ever did not).
+ * Every call on a GPU uses that GPU's one array: calls that overlap on the same GPU (two
+ * streams, or two threads) race and must be serialised by the caller.  Each call clears
+ * what it needs before using it.  Allocates nothing.
+ */
+int32_t kv_select_noalloc(const float *item_score, const uint8_t *item_pinned, int64_t n_items,
+                          int32_t item_tokens, int64_t n_tokens, int64_t budget_items,
+                          int32_t *keep_tokens, int64_t keep_capacity, int64_t *n_keep,
+                          uint32_t *status, hipStream_t stream);
+
 /* Host-only.  Workspace bytes kv_lrfu_update needs for n entries. */
 int32_t kv_lrfu_workspace_size(int64_t n, size_t *bytes /* host */);
 
