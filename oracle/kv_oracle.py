@@ -691,6 +691,51 @@ def evicted_tokens(n_tokens, keep):
     return np.nonzero(mask)[0]
 
 
+def load_rows(dst, slots, rows):
+    """Rows coming back from host memory: row r of ``rows`` ([L][count][Hkv][D]) lands in
+    slot slots[r] of ``dst`` ([L][N][Hkv][D], logical order), every layer; other slots are
+    unchanged.  Loading the rows a compaction dropped back into the slots they came from
+    restores the row (the inverse of evicted-row offload, PACE Sec. 3.4; Penelope Part
+    three moves segments back from the CPU tier)."""
+    out = np.array(dst, copy=True)
+    rows = np.asarray(rows)
+    for r, j in enumerate(np.asarray(slots, dtype=np.int64).tolist()):
+        out[:, j] = rows[:, r]
+    return out
+
+
+def chunked_swap(gpu, pool, slots, in_first, buf_first, chunk):
+    """Penelope's swap when both tiers are full ("Rethinking KV Cache Eviction for Agentic
+    LLM Serving", Part three): the segment held in GPU slots ``slots`` moves to the CPU,
+    and the segment in CPU rows [in_first, in_first + count) moves into those GPU slots.
+    Neither tier has free space, so a small CPU swap buffer (``chunk`` rows from buf_first,
+    1,024 tokens in the paper) is used chunk by chunk:
+      - the chunk leaving the GPU is written into the current buffer;
+      - the GPU slots it freed receive the matching chunk coming from the CPU;
+      - the CPU rows that chunk emptied become the buffer for the next chunk.
+    gpu: [L][N][Hkv][D] logical rows; pool: [L][P][Hkv][D] CPU rows.
+    Returns (gpu', pool', out_rows, next_buffer): out_rows[r] is the CPU row where the r-th
+    outgoing row now lives, and next_buffer the first row of the CPU rows left free (the
+    incoming segment's last chunk).
+    Reading: chunks are taken in segment order and a chunk has the buffer's size except
+    the last one."""
+    gpu = np.array(gpu, copy=True)
+    pool = np.array(pool, copy=True)
+    slots = np.asarray(slots, dtype=np.int64)
+    count = len(slots)
+    assert buf_first + min(chunk, count) <= in_first or in_first + count <= buf_first
+    buf = buf_first
+    out_rows = []
+    for c0 in range(0, count, chunk):
+        n = min(chunk, count - c0)
+        leaving = slots[c0:c0 + n]
+        pool[:, buf:buf + n] = gpu[:, leaving]
+        out_rows.extend(range(buf, buf + n))
+        gpu[:, leaving] = pool[:, in_first + c0:in_first + c0 + n]
+        buf = in_first + c0
+    return gpu, pool, np.array(out_rows, dtype=np.int64), buf
+
+
 def gather_meta(arr, keep):
     """Per-token metadata follows its token through compaction."""
     return np.asarray(arr)[np.asarray(keep, dtype=np.int64)]

@@ -929,6 +929,55 @@ def test_evicted_tokens_partition():
             assert ev[e] == e + int((keep < ev[e]).sum())
 
 
+def test_load_rows_is_the_inverse_of_evicted_gather():
+    """Dropping rows (the keep list's complement, gathered in order) and loading them back
+    into the slots they came from restores the row exactly; other slots stay untouched."""
+    rng = np.random.default_rng(61)
+    k = rng.standard_normal((3, 50, 2, 8))
+    keep = np.sort(rng.choice(50, 17, replace=False))
+    ev = O.evicted_tokens(50, keep)
+    rows = k[:, ev]
+    blank = np.where(np.isin(np.arange(50), keep)[None, :, None, None], k, 0.0)
+    assert (O.load_rows(blank, ev, rows) == k).all()
+    other = O.load_rows(k, [3, 9], rows[:, :2])
+    assert (other[:, 3] == rows[:, 0]).all() and (other[:, 9] == rows[:, 1]).all()
+    untouched = np.setdiff1d(np.arange(50), [3, 9])
+    assert (other[:, untouched] == k[:, untouched]).all()
+
+
+@pytest.mark.parametrize("count,chunk", [(1, 4), (4, 4), (10, 4), (9, 3), (7, 16)])
+def test_chunked_swap_moves_both_segments(count, chunk):
+    """The swap through the small buffer ends exactly where an unbounded exchange would:
+    the GPU slots hold the incoming CPU rows, every outgoing row sits in the CPU row
+    reported for it, no other CPU row holding data is overwritten, and swapping the other
+    way with the reported buffer undoes it."""
+    rng = np.random.default_rng(count * 31 + chunk)
+    n, p = 40, count + chunk + 12
+    gpu = rng.standard_normal((2, n, 1, 4))
+    pool = rng.standard_normal((2, p, 1, 4))
+    slots = rng.choice(n, count, replace=False)
+    in_first, buf_first = 5, 5 + count + 3            # buffer after the incoming segment
+    g2, p2, out_rows, nxt = O.chunked_swap(gpu, pool, slots, in_first, buf_first, chunk)
+    assert (g2[:, slots] == pool[:, in_first:in_first + count]).all()
+    assert (p2[:, out_rows] == gpu[:, slots]).all()
+    others = np.setdiff1d(np.arange(n), slots)
+    assert (g2[:, others] == gpu[:, others]).all()
+    # CPU rows outside the incoming segment and the buffer keep their data
+    used = set(range(in_first, in_first + count)) | set(range(buf_first, buf_first + min(chunk, count)))
+    keep_rows = [r for r in range(p) if r not in used]
+    assert (p2[:, keep_rows] == pool[:, keep_rows]).all()
+    # the outgoing rows land in the old buffer, then in the rows the incoming chunks
+    # freed; the last incoming chunk's rows are the next buffer and hold none of them
+    last = (count - 1) // chunk * chunk
+    assert nxt == in_first + last
+    assert set(out_rows.tolist()) <= used and len(set(out_rows.tolist())) == count
+    assert not set(out_rows.tolist()) & set(range(nxt, in_first + count))
+    # swap back: the GPU slots receive the outgoing rows again, from where they landed
+    if (np.diff(out_rows) == 1).all():                    # one contiguous CPU range
+        g3, _, _, _ = O.chunked_swap(g2, p2, slots, int(out_rows[0]), nxt, chunk)
+        assert (g3 == gpu).all()
+
+
 def test_renumbered_rotary_distance_bounded():
     gd = read_golden("pace_numbers.txt")
     keep = np.sort(np.random.default_rng(16).choice(100_000, gd["budget"], replace=False))
