@@ -131,6 +131,10 @@ def lib() -> ctypes.CDLL:
                                         i32, vp]),
             "kv_offload_workspace_size": (i32, [P(KvCacheDesc), i64, P(sz)]),
             "kv_offload_evicted": (i32, [P(KvCacheDesc), vp, i64, i64, vp, vp, vp, vp, sz, vp]),
+            "kv_load_rows": (i32, [P(KvCacheDesc), vp, i64, vp, vp, i64, i64, i64, P(KvMetaDesc), i32, vp,
+                                   sz, vp]),
+            "kv_swap_chunked": (i32, [P(KvCacheDesc), vp, i64, vp, vp, i64, i64, i64, i64, P(i64), P(i64), vp,
+                                      sz, vp]),
             "kv_lrfu_update": (i32, [vp, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float, vp, vp, vp, sz,
                                      vp]),
             "kv_compact_tail_inplace": (i32, [P(KvCacheDesc), vp, vp, i64, i64, P(KvMetaDesc), i32, P(i64),
@@ -346,6 +350,42 @@ def kv_offload_evicted(src: PagedCache, keep_tokens, n_keep, host_k, host_v, hos
                                     _ptr(workspace), workspace.numel(), _stream(src.k.device)),
            "kv_offload_evicted")
     return workspace
+
+
+def kv_offload_workspace_size(cache: PagedCache, chunk) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().kv_offload_workspace_size(ctypes.byref(cache.desc()), int(chunk), ctypes.byref(b)),
+           "kv_offload_workspace_size")
+    return b.value
+
+
+def kv_load_rows(dst: PagedCache, slots, host_k, host_v, host_first=0, count=None, chunk=1024, meta=None,
+                 workspace=None):
+    """Host rows [host_first, host_first + count) of pinned pools [L][rows][Hkv][128] into
+    slots `slots` of dst (see kv_load_rows); meta is a list of (src[count], dst[N]) pairs."""
+    count = int(slots.numel()) if count is None else int(count)
+    if workspace is None:
+        workspace = torch.empty(kv_offload_workspace_size(dst, chunk), dtype=torch.uint8, device=dst.k.device)
+    arr, n_meta = _meta_array(meta)
+    _check(lib().kv_load_rows(ctypes.byref(dst.desc()), _ptr(slots), count, _host_ptr(host_k), _host_ptr(host_v),
+                              int(host_k.shape[1]), int(host_first), int(chunk), arr, n_meta, _ptr(workspace),
+                              workspace.numel(), _stream(dst.k.device)), "kv_load_rows")
+    return workspace
+
+
+def kv_swap_chunked(cache: PagedCache, slots, host_k, host_v, in_first, buf_first, chunk=1024, workspace=None):
+    """Penelope's both-tiers-full swap (see kv_swap_chunked).  Returns (out_rows list,
+    next_buf_first, workspace)."""
+    count = int(slots.numel())
+    if workspace is None:
+        workspace = torch.empty(kv_offload_workspace_size(cache, chunk), dtype=torch.uint8, device=cache.k.device)
+    out = (ctypes.c_int64 * max(1, count))()
+    nxt = ctypes.c_int64(-1)
+    _check(lib().kv_swap_chunked(ctypes.byref(cache.desc()), _ptr(slots), count, _host_ptr(host_k),
+                                 _host_ptr(host_v), int(host_k.shape[1]), int(in_first), int(buf_first),
+                                 int(chunk), out, ctypes.byref(nxt), _ptr(workspace), workspace.numel(),
+                                 _stream(cache.k.device)), "kv_swap_chunked")
+    return list(out)[:count], nxt.value, workspace
 
 
 def kv_compact_tail_inplace(cache: PagedCache, keep_tokens, n_keep, max_keep, budget, meta=None,

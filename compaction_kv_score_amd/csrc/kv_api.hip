@@ -750,6 +750,151 @@ int32_t kv_offload_evicted(const kv_cache_desc* src, const int32_t* keep_tokens,
   return KV_OK;
 }
 
+// Staging rows of the offload / load / swap workspace: chunk tokens of K, then of V,
+// layer-major, then chunk int32 ids.
+static kv_cache_desc staging_desc(const kv_cache_desc* like, void* ws, int64_t chunk) {
+  kv_cache_desc st;
+  memset(&st, 0, sizeof(st));
+  const int64_t slot = (int64_t)like->n_kv_heads * kHeadDim;
+  st.k = ws;
+  st.v = (char*)ws + offload_row_bytes(like, chunk);
+  st.n_layers = like->n_layers;
+  st.n_kv_heads = like->n_kv_heads;
+  st.head_dim = kHeadDim;
+  st.page_size = 1;
+  st.n_tokens = chunk;
+  st.page_stride = slot;
+  st.layer_stride = chunk * slot;
+  st.block_table = nullptr;
+  return st;
+}
+
+static MoveArgs move_args(const kv_cache_desc* src, const kv_cache_desc* dst) {
+  MoveArgs a;
+  memset(&a, 0, sizeof(a));
+  a.src_k = (const uint16_t*)src->k;
+  a.src_v = (const uint16_t*)src->v;
+  a.src_layer_stride = src->layer_stride;
+  a.src_page_stride = src->page_stride;
+  a.src_bt = src->block_table;
+  a.src_page_shift = log2_exact(src->page_size);
+  a.src_tokens = src->n_tokens;
+  a.dst_k = (uint16_t*)dst->k;
+  a.dst_v = (uint16_t*)dst->v;
+  a.dst_layer_stride = dst->layer_stride;
+  a.dst_page_stride = dst->page_stride;
+  a.dst_bt = dst->block_table;
+  a.dst_page_shift = log2_exact(dst->page_size);
+  a.dst_tokens = dst->n_tokens;
+  a.n_layers = src->n_layers;
+  a.n_kv_heads = src->n_kv_heads;
+  return a;
+}
+
+// One chunk's K and V between host rows [host_row, host_row + cnt) of a [L][host_rows]
+// pool and the staging rows, every layer (one 2D copy per array).
+static hipError_t host_chunk_copy(const kv_cache_desc* c, const kv_cache_desc* stage, void* host_k,
+                                  void* host_v, int64_t host_rows, int64_t host_row, int64_t cnt,
+                                  int64_t chunk, bool to_host, hipStream_t stream) {
+  const size_t row_bytes = (size_t)c->n_kv_heads * kHeadDim * sizeof(uint16_t);
+  for (int which = 0; which < 2; ++which) {
+    char* host = (char*)(which ? host_v : host_k) + (size_t)host_row * row_bytes;
+    char* dev = (char*)(which ? stage->v : stage->k);
+    const hipError_t e =
+        to_host ? hipMemcpy2DAsync(host, (size_t)host_rows * row_bytes, dev, (size_t)chunk * row_bytes,
+                                   (size_t)cnt * row_bytes, (size_t)c->n_layers, hipMemcpyDeviceToHost, stream)
+                : hipMemcpy2DAsync(dev, (size_t)chunk * row_bytes, host, (size_t)host_rows * row_bytes,
+                                   (size_t)cnt * row_bytes, (size_t)c->n_layers, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+int32_t kv_load_rows(const kv_cache_desc* dst, const int32_t* slots, int64_t count, const void* host_k,
+                     const void* host_v, int64_t host_rows, int64_t host_first, int64_t chunk,
+                     const kv_meta_desc* meta, int32_t n_meta, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  size_t need = 0;
+  int32_t rc = kv_offload_workspace_size(dst, chunk, &need);
+  if (rc) return rc;
+  if (count < 0 || (count > 0 && (!slots || !host_k || !host_v))) return KV_EINVAL;
+  if (host_first < 0 || host_rows < 0 || host_first + count > host_rows) return KV_EINVAL;
+  MetaSet ms;
+  if ((rc = check_meta(meta, n_meta, &ms))) return rc;
+  if (!ws || ws_bytes < need) return KV_EWORKSPACE;
+  if (count == 0) return KV_OK;
+  if ((rc = check_device())) return rc;
+  const kv_cache_desc stage = staging_desc(dst, ws, chunk);
+  MoveArgs a = move_args(&stage, dst);
+  a.meta = ms;
+  for (int64_t c0 = 0; c0 < count; c0 += chunk) {
+    const int64_t cnt = count - c0 < chunk ? count - c0 : chunk;
+    hipError_t e = host_chunk_copy(dst, &stage, (void*)host_k, (void*)host_v, host_rows, host_first + c0, cnt,
+                                   chunk, false, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    a.src_rows = nullptr;
+    a.src_first = 0;
+    a.dst_rows = slots + c0;
+    a.meta_first = c0;
+    a.count = cnt;
+    if ((e = launch_move_rows(a, stream)) != hipSuccess) return hip_fail(e);
+  }
+  return KV_OK;
+}
+
+int32_t kv_swap_chunked(const kv_cache_desc* cache, const int32_t* slots, int64_t count, void* host_k,
+                        void* host_v, int64_t host_rows, int64_t in_first, int64_t buf_first, int64_t chunk,
+                        int64_t* out_rows, int64_t* next_buf_first, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  size_t need = 0;
+  int32_t rc = kv_offload_workspace_size(cache, chunk, &need);
+  if (rc) return rc;
+  if (count < 0 || (count > 0 && (!slots || !host_k || !host_v))) return KV_EINVAL;
+  if (in_first < 0 || buf_first < 0 || in_first + count > host_rows) return KV_EINVAL;
+  const int64_t first_n = count < chunk ? count : chunk;
+  if (buf_first + first_n > host_rows) return KV_EINVAL;
+  if (count > 0 && buf_first < in_first + count && in_first < buf_first + first_n) return KV_EINVAL;
+  if (!ws || ws_bytes < need) return KV_EWORKSPACE;
+  // where every outgoing row lands: the buffer, then the rows each incoming chunk frees
+  int64_t buf = buf_first;
+  for (int64_t c0 = 0; c0 < count; c0 += chunk) {
+    const int64_t cnt = count - c0 < chunk ? count - c0 : chunk;
+    if (out_rows)
+      for (int64_t r = 0; r < cnt; ++r) out_rows[c0 + r] = buf + r;
+    buf = in_first + c0;
+  }
+  if (next_buf_first) *next_buf_first = buf;
+  if (count == 0) return KV_OK;
+  if ((rc = check_device())) return rc;
+  const kv_cache_desc stage = staging_desc(cache, ws, chunk);
+  MoveArgs out = move_args(cache, &stage);
+  MoveArgs in = move_args(&stage, cache);
+  buf = buf_first;
+  for (int64_t c0 = 0; c0 < count; c0 += chunk) {
+    const int64_t cnt = count - c0 < chunk ? count - c0 : chunk;
+    // the chunk leaving the GPU: gathered, then written into the current CPU buffer
+    out.src_rows = slots + c0;
+    out.dst_rows = nullptr;
+    out.dst_first = 0;
+    out.count = cnt;
+    hipError_t e = launch_move_rows(out, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if ((e = host_chunk_copy(cache, &stage, host_k, host_v, host_rows, buf, cnt, chunk, true, stream)) != hipSuccess)
+      return hip_fail(e);
+    // the chunk coming from the CPU: into the GPU slots just freed
+    if ((e = host_chunk_copy(cache, &stage, host_k, host_v, host_rows, in_first + c0, cnt, chunk, false, stream)) !=
+        hipSuccess)
+      return hip_fail(e);
+    in.src_rows = nullptr;
+    in.src_first = 0;
+    in.dst_rows = slots + c0;
+    in.count = cnt;
+    if ((e = launch_move_rows(in, stream)) != hipSuccess) return hip_fail(e);
+    buf = in_first + c0;   // the CPU rows this chunk emptied are the next buffer
+  }
+  return KV_OK;
+}
+
 int32_t kv_compact_tail_inplace(const kv_cache_desc* cache, const int32_t* keep_tokens,
                                 const int64_t* n_keep, int64_t max_keep, int64_t budget,
                                 const kv_meta_desc* meta, int32_t n_meta, int64_t* start_host,

@@ -361,6 +361,43 @@ __global__ __launch_bounds__(kCompactThreads) void gather_evicted_kernel(EvictAr
   }
 }
 
+// One row per ceil(items/256) workgroups, one 16-byte K and V chunk per thread, as the
+// evicted-row gather: the copies of swaps and loads (device staging <-> cache slots).
+__global__ __launch_bounds__(kCompactThreads) void move_rows_kernel(MoveArgs a) {
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x / a.parts;
+  const int part = (int)(blockIdx.x % a.parts);
+  const int64_t st = a.src_rows ? (int64_t)a.src_rows[r] : a.src_first + r;
+  const int64_t dt = a.dst_rows ? (int64_t)a.dst_rows[r] : a.dst_first + r;
+  if (st < 0 || st >= a.src_tokens || dt < 0 || dt >= a.dst_tokens) return;
+  const int slot_stride = a.n_kv_heads * kHeadDim;
+  const int64_t so = token_offset(st, a.src_page_shift, a.src_page_stride, a.src_bt, slot_stride);
+  const int64_t dof = token_offset(dt, a.dst_page_shift, a.dst_page_stride, a.dst_bt, slot_stride);
+  const int per_layer = slot_stride / 8;
+  const int items = a.n_layers * per_layer;
+  const int i0 = (int)((int64_t)part * items / a.parts);
+  const int i1 = (int)((int64_t)(part + 1) * items / a.parts);
+  for (int it = i0 + tid; it < i1; it += kCompactThreads) {
+    const int layer = it / per_layer;
+    const int64_t col = (int64_t)(it - layer * per_layer) * 8;
+    const int64_t s0 = (int64_t)layer * a.src_layer_stride + so + col;
+    const int64_t d0 = (int64_t)layer * a.dst_layer_stride + dof + col;
+    *(uint4*)(a.dst_k + d0) = load_once(a.src_k + s0);
+    *(uint4*)(a.dst_v + d0) = load_once(a.src_v + s0);
+  }
+  if (tid == 0 && part == 0) {
+    const int64_t m0 = a.meta_first + r;
+    for (int m = 0; m < a.meta.n; ++m) {
+      switch (a.meta.elem_bytes[m]) {
+        case 1: ((uint8_t*)a.meta.dst[m])[dt] = ((const uint8_t*)a.meta.src[m])[m0]; break;
+        case 2: ((uint16_t*)a.meta.dst[m])[dt] = ((const uint16_t*)a.meta.src[m])[m0]; break;
+        case 4: ((uint32_t*)a.meta.dst[m])[dt] = ((const uint32_t*)a.meta.src[m])[m0]; break;
+        default: ((uint64_t*)a.meta.dst[m])[dt] = ((const uint64_t*)a.meta.src[m])[m0]; break;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // Workgroups per token for a plain K/V copy of `items` 16-byte chunk pairs: every thread
@@ -374,6 +411,16 @@ hipError_t launch_gather_evicted(const EvictArgs& a0, hipStream_t s) {
   const int64_t grid = a.count * a.parts;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gather_evicted_kernel, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_move_rows(const MoveArgs& a0, hipStream_t s) {
+  if (a0.count <= 0) return hipSuccess;
+  MoveArgs a = a0;
+  a.parts = copy_parts(a.n_layers * a.n_kv_heads * (kHeadDim / 8));
+  const int64_t grid = a.count * a.parts;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(move_rows_kernel, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a);
   return hipGetLastError();
 }
 

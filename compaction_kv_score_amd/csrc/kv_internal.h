@@ -236,4 +236,31 @@ struct EvictArgs {
 };
 hipError_t launch_gather_evicted(const EvictArgs& a, hipStream_t s);
 
+// Whole token rows (K and V of every layer and head) between two caches:
+// row r copies source token (src_rows ? src_rows[r] : src_first + r) to destination token
+// (dst_rows ? dst_rows[r] : dst_first + r); a row whose token lies outside either cache is
+// skipped.  meta: dst[dst token] = src[meta_first + r].
+struct MoveArgs {
+  const uint16_t* src_k;
+  const uint16_t* src_v;
+  int64_t src_layer_stride, src_page_stride;
+  const int32_t* src_bt;
+  int src_page_shift;
+  int64_t src_tokens;
+  uint16_t* dst_k;
+  uint16_t* dst_v;
+  int64_t dst_layer_stride, dst_page_stride;
+  const int32_t* dst_bt;
+  int dst_page_shift;
+  int64_t dst_tokens;
+  int n_layers, n_kv_heads;
+  const int32_t* src_rows;
+  const int32_t* dst_rows;
+  int64_t src_first, dst_first, meta_first;
+  int64_t count;
+  MetaSet meta;
+  int parts;                     // workgroups per row (set by the launcher)
+};
+hipError_t launch_move_rows(const MoveArgs& a, hipStream_t s);
+
 }  // namespace kvs

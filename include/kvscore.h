@@ -300,6 +300,45 @@ int32_t kv_offload_evicted(const kv_cache_desc *src, const int32_t *keep_tokens,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Rows coming back from host memory (the inverse of kv_offload_evicted; PACE Sec. 3.4
+ * offloads evicted rows, and "Rethinking KV Cache Eviction for Agentic LLM Serving", Part
+ * three, moves segments back from the CPU tier): host rows [host_first, host_first +
+ * count) of pinned pools host_k / host_v, layout [L][host_rows][Hkv][128] bf16 (the
+ * offload layout with host_rows = N - n_keep), are copied to logical slots slots[r]
+ * (device int32, distinct; addressed through dst's block table) of every layer and head of
+ * dst.  Chunks of `chunk` rows go host-to-device into the staging workspace
+ * (kv_offload_workspace_size(dst, chunk)) and are scattered by a kernel, in stream order
+ * on `stream`.  Each meta[m] moves with its row: meta[m].dst[slots[r]] = meta[m].src[r]
+ * (src a device array of count elements).  A slot outside [0, dst.n_tokens) is skipped.
+ * The host pools must stay valid until the stream reaches this point.
+ */
+int32_t kv_load_rows(const kv_cache_desc *dst, const int32_t *slots, int64_t count,
+                     const void *host_k, const void *host_v, int64_t host_rows, int64_t host_first,
+                     int64_t chunk, const kv_meta_desc *meta /* host array */, int32_t n_meta,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Penelope's swap when both tiers are full ("Rethinking KV Cache Eviction for Agentic LLM
+ * Serving", Part three): the segment in GPU slots slots[0:count) (device int32, distinct)
+ * of `cache` moves to the CPU pool host_k / host_v ([L][host_rows][Hkv][128] bf16, pinned),
+ * and the CPU segment in pool rows [in_first, in_first + count) moves into those GPU slots.
+ * With no free space on either side, a swap buffer of `chunk` CPU rows from buf_first
+ * (1,024 tokens in the paper; disjoint from the incoming rows) is used chunk by chunk, in
+ * segment order: the chunk leaving the GPU is written into the buffer, the GPU slots it
+ * freed receive the matching chunk from the CPU, and the CPU rows that chunk emptied are
+ * the buffer for the next chunk.  out_rows (host, nullable, count entries) receives the
+ * pool row of every outgoing row, and *next_buf_first (host, nullable) the first row of
+ * the incoming segment's last chunk, which is free afterwards.  Only K and V move;
+ * workspace as kv_offload_workspace_size(cache, chunk).  All copies and kernels run in
+ * stream order on `stream`.
+ */
+int32_t kv_swap_chunked(const kv_cache_desc *cache, const int32_t *slots, int64_t count,
+                        void *host_k, void *host_v, int64_t host_rows, int64_t in_first,
+                        int64_t buf_first, int64_t chunk, int64_t *out_rows /* host */,
+                        int64_t *next_buf_first /* host */, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Segment eviction from the front of the private history ("Rethinking KV Cache
  * Eviction for Agentic LLM Serving", Part one): keep [0, P) and [P + E', N) where
  * E' = min(ceil(E / block) * block, N - P) frees only whole blocks.  Writes the keep

@@ -260,3 +260,50 @@ def test_lrfu_and_tail_validation():
     meta = (kv.KvMetaDesc * 1)(kv.KvMetaDesc(FAKE, FAKE * 2, 4, 0))
     assert L.kv_compact_tail_inplace(ctypes.byref(c), FAKE, None, 10, 50, meta, 1, ctypes.byref(start), None,
                                      None) == kv.KV_EINVAL
+
+
+def test_load_and_swap_validation():
+    L = kv.lib()
+    c = _cache()
+    ws_need = ctypes.c_size_t()
+    assert L.kv_offload_workspace_size(ctypes.byref(c), 64, ctypes.byref(ws_need)) == kv.KV_OK
+    big = ws_need.value
+    load = lambda **kw: L.kv_load_rows(  # noqa: E731
+        ctypes.byref(c), kw.get("slots", FAKE), kw.get("count", 10), FAKE * 3, FAKE * 4, kw.get("rows", 50),
+        kw.get("first", 0), kw.get("chunk", 64), None, 0, FAKE * 5, kw.get("wb", big), None)
+    assert load(first=45) == kv.KV_EINVAL              # rows past the pool
+    assert load(slots=None) == kv.KV_EINVAL
+    assert load(count=-1) == kv.KV_EINVAL
+    assert load(chunk=0) == kv.KV_EINVAL
+    assert load(wb=big - 1) == kv.KV_EWORKSPACE
+    assert load(count=0) == kv.KV_OK                   # nothing to move: no device call
+    out = (ctypes.c_int64 * 10)()
+    nxt = ctypes.c_int64()
+    swap = lambda **kw: L.kv_swap_chunked(  # noqa: E731
+        ctypes.byref(c), FAKE, kw.get("count", 10), FAKE * 3, FAKE * 4, kw.get("rows", 100),
+        kw.get("in_first", 0), kw.get("buf", 50), kw.get("chunk", 64), out, ctypes.byref(nxt), FAKE * 5,
+        kw.get("wb", big), None)
+    assert swap(buf=5) == kv.KV_EINVAL                 # buffer overlaps the incoming rows
+    assert swap(in_first=95) == kv.KV_EINVAL
+    assert swap(buf=95) == kv.KV_EINVAL                # buffer past the pool
+    assert swap(wb=16) == kv.KV_EWORKSPACE
+
+
+@pytest.mark.parametrize("count,chunk,in_first,buf", [(10, 4, 0, 20), (9, 3, 30, 0), (5, 64, 7, 100),
+                                                      (2048, 1024, 0, 4096), (1, 1, 3, 0)])
+def test_swap_row_bookkeeping_matches_oracle(count, chunk, in_first, buf):
+    """Where kv_swap_chunked reports each outgoing row lands (host logic, computed before
+    any device call), against the oracle's chunk-by-chunk swap."""
+    L = kv.lib()
+    c = _cache(n_tokens=max(count, 100))
+    rows = max(in_first + count, buf + min(chunk, count)) + 5
+    ws = ctypes.c_size_t()
+    assert L.kv_offload_workspace_size(ctypes.byref(c), chunk, ctypes.byref(ws)) == kv.KV_OK
+    out = (ctypes.c_int64 * count)()
+    nxt = ctypes.c_int64(-1)
+    L.kv_swap_chunked(ctypes.byref(c), FAKE, count, FAKE * 3, FAKE * 4, rows, in_first, buf, chunk, out,
+                      ctypes.byref(nxt), FAKE * 5, ws.value, None)
+    gpu = np.zeros((1, count, 1, 1))
+    pool = np.zeros((1, rows, 1, 1))
+    _, _, want, want_next = O.chunked_swap(gpu, pool, np.arange(count), in_first, buf, chunk)
+    assert list(out) == want.tolist() and nxt.value == want_next
