@@ -611,57 +611,127 @@ def test_full_size_qwen3_100k_mass_is_additive_over_layers(qwen3_100k, aggregate
     assert_rel(np64(full["mass"]), total, rtol=2 * RTOL, what=f"36-layer {aggregate} mass vs 2-layer runs")
 
 
-def test_full_size_qwen3_100k_compaction_sampled(qwen3_100k):
+def _rerope_chunks(k_rows, v_rows, old_kept, theta, step=512):
+    """The oracle's compaction of already gathered rows (rank r holds source keep[r] with
+    old position old_kept[r]), renumbered to 0..n-1, in rank chunks to bound memory."""
+    n = k_rows.shape[1]
+    ks, vs, ps = [], [], []
+    for r0 in range(0, n, step):
+        r1 = min(n, r0 + step)
+        rk, rv, rp = O.compact_rerope(k_rows[:, r0:r1], v_rows[:, r0:r1], np.arange(r1 - r0),
+                                      old_kept[r0:r1], r0, theta)      # ranks r0.. renumber to r0..
+        ks.append(rk)
+        vs.append(rv)
+        ps.append(rp)
+    return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1), np.concatenate(ps)
+
+
+def test_full_size_qwen3_100k_bench_step(qwen3_100k):
+    """The benchmark's own step at full size (Qwen3-8B shape, 36 layers, N = 100,000):
+    H2O + foresight scoring, selection of 2,048 tokens with 4 sinks and 128 recent pinned,
+    compaction with renumbering under L = 8,192 and the metadata it carries.  Checked:
+    every token's score is its mass plus the oracle's bonus, the pins follow the rules, the
+    keep list equals the oracle's selection on the device's own scores bit for bit, and all
+    2,048 compacted ranks (V, unrotated and rotated K, positions, metadata) match the
+    oracle's compaction of the kept rows."""
     w, k, v, q = qwen3_100k
-    g = torch.Generator().manual_seed(1)
-    keep = torch.sort(torch.randperm(w.n_tokens, generator=g)[: w.budget_tokens])[0].to(torch.int32)
-    dk = torch.zeros((w.n_layers, w.budget_tokens // 16, 16, 8, 128), dtype=torch.bfloat16, device=DEV)
+    N, B = w.n_tokens, w.budget_tokens
+    span_id, next_use = synth.spans(w, seed=0)
+    accum = torch.zeros(N, device=DEV)
+    mass = torch.zeros(N, device=DEV)
+    tok = torch.zeros(N, device=DEV)
+    item_score = torch.zeros(N, device=DEV)
+    item_pinned = torch.zeros(N, dtype=torch.uint8, device=DEV)
+    src = kv.PagedCache(k, v, N)
+    kv.kv_score(src, q, policy="h2o", window=w.window, item_tokens=1, accum=accum, span_id=span_id.to(DEV),
+                span_next_use=next_use.to(DEV), bonus_floor=50000.0, n_sink=w.n_sink, n_recent=w.n_recent,
+                mass=mass, token_score=tok, item_score=item_score, item_pinned=item_pinned)
+    keep = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+    n_keep = torch.zeros(1, dtype=torch.int64, device=DEV)
+    status = torch.full((1,), 9, dtype=torch.int32, device=DEV)
+    kv.kv_select(item_score, item_pinned, 1, N, B, keep, n_keep, status)
+    dk = torch.zeros((w.n_layers, B // 16, 16, 8, 128), dtype=torch.bfloat16, device=DEV)
     dv = torch.zeros_like(dk)
-    pos = torch.arange(w.n_tokens, dtype=torch.int32, device=DEV)
-    newp = torch.zeros(w.budget_tokens, dtype=torch.int32, device=DEV)
-    kv.kv_compact_rerope(kv.PagedCache(k, v, w.n_tokens), kv.PagedCache(dk, dv, w.budget_tokens),
-                         keep.to(DEV), None, w.budget_tokens, pos, newp, renumber_base=0,
-                         rope_theta=w.rope_theta, limit=w.limit)
+    old_pos = torch.arange(N, dtype=torch.int32, device=DEV)
+    new_pos = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+    dst_accum = torch.zeros(B, device=DEV)
+    dst_span = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    kv.kv_compact_rerope(src, kv.PagedCache(dk, dv, B), keep, n_keep, B, old_pos, new_pos, renumber_base=0,
+                         rope_theta=w.rope_theta, limit=w.limit,
+                         meta=[(accum, dst_accum), (span_id.to(DEV), dst_span)])
     torch.cuda.synchronize()
-    ranks = sorted(set([0, 1, w.budget_tokens - 1] + torch.randint(0, w.budget_tokens, (40,), generator=g).tolist()))
-    src = keep[ranks].long()
-    kf = k.reshape(w.n_layers, -1, 8, 128)
-    vf = v.reshape(w.n_layers, -1, 8, 128)
-    ks, vs = np64(kf[:, src.to(DEV)]), np64(vf[:, src.to(DEV)])
-    rk = O.bf16_round(O.rope_rotate(ks, (np.array(ranks) - src.numpy())[None, :, None], w.rope_theta))
-    gk = np64(dk.reshape(w.n_layers, -1, 8, 128)[:, ranks])
-    gv = np64(dv.reshape(w.n_layers, -1, 8, 128)[:, ranks])
-    assert (gv == vs).all()
-    assert_bf16_within_1ulp(gk, rk, "K at N=100K")
-    assert (newp.cpu().numpy() == np.arange(w.budget_tokens)).all()
+    assert int(status.item()) == 0 and int(n_keep.item()) == B
+    # scores: H2O from a zero accumulator is the mass, plus the span bonus
+    bonus = O.token_bonus(span_id.numpy(), O.foresight_bonus(next_use.numpy(), 50000.0))
+    assert_rel(np64(tok), np64(mass) + bonus, what="score = mass + bonus")
+    assert torch.equal(tok, item_score) and torch.equal(accum, mass)
+    pin = O.pinned_tokens(N, n_sink=w.n_sink, n_recent=w.n_recent)
+    assert (item_pinned.cpu().numpy().astype(bool) == pin).all()
+    want, st = O.select_items(np64(item_score), pin, B)
+    kept = keep.cpu().numpy().astype(np.int64)
+    assert st == 0 and (kept == want).all(), "keep list differs from the oracle's selection"
+    # every compacted rank against the oracle
+    kl = k.reshape(w.n_layers, -1, 8, 128)[:, keep.long()]
+    vl = v.reshape(w.n_layers, -1, 8, 128)[:, keep.long()]
+    rk, rv, rpos = _rerope_chunks(np64(kl), np64(vl), kept, w.rope_theta)
+    gk = np64(dk).reshape(w.n_layers, B, 8, 128)
+    gv = np64(dv).reshape(w.n_layers, B, 8, 128)
+    assert (new_pos.cpu().numpy() == rpos).all() and (rpos == np.arange(B)).all()
+    assert (gv == rv).all(), "V must be bit-exact"
+    still = kept == np.arange(B)
+    assert (gk[:, still] == rk[:, still]).all()
+    assert_bf16_within_1ulp(gk, rk, "K, all 2,048 ranks")
+    assert (dst_accum.cpu() == accum.cpu()[kept]).all() and (dst_span.cpu() == span_id[kept]).all()
 
 
-def test_full_size_mistral_131k_segment_sampled():
-    """Mistral-7B shape at full size (131,072 tokens, 16,384-token prefix, 30% evicted):
-    in-place segment eviction + re-rotation as bench.py --extras runs it, checked on
-    sampled ranks against the oracle's rotation of the original rows."""
+def test_full_size_mistral_131k_segment():
+    """Mistral-7B shape at full size (32 layers, 131,072 tokens, 16,384-token prefix, 30%
+    evicted): in-place segment eviction + re-rotation as bench.py --extras runs it.  Every
+    one of the 91,744 ranks of the first and the last layer against the oracle's
+    compaction of the original rows, and sampled ranks of every layer."""
     w = synth.workload("mistral-7b-n131072-segment")
+    N, NL = w.n_tokens, w.n_layers
     k, v, _ = synth.kv_cache(w, seed=0, device=DEV)
-    n_keep, e = kv.kv_select_segment(w.n_tokens, w.segment_prefix, int(w.segment_frac * w.n_tokens), 16)
-    assert (n_keep, e) == (w.n_tokens - 39_328, 39_328)
+    n_keep, e = kv.kv_select_segment(N, w.segment_prefix, int(w.segment_frac * N), 16)
+    assert (n_keep, e) == (N - 39_328, 39_328)
+    keep = O.select_segment(N, w.segment_prefix, int(w.segment_frac * N), 16)
+    assert len(keep) == n_keep
+    kf, vf = k.reshape(NL, -1, 8, 128), v.reshape(NL, -1, 8, 128)
+    layers = [0, NL - 1]
+    k_edge = kf[layers][:, :N].cpu()
+    v_edge = vf[layers][:, :N].cpu()
     g = torch.Generator().manual_seed(3)
     ranks = sorted(set([0, w.segment_prefix - 1, w.segment_prefix, w.segment_prefix + e - 1, n_keep - 1]
                        + torch.randint(0, n_keep, (40,), generator=g).tolist()))
-    src = [r if r < w.segment_prefix else r + e for r in ranks]
-    kf, vf = k.reshape(w.n_layers, -1, 8, 128), v.reshape(w.n_layers, -1, 8, 128)
-    ks, vs = np64(kf[:, src]), np64(vf[:, src])
-    pos = torch.arange(w.n_tokens, dtype=torch.int32, device=DEV)
-    kv.kv_compact_segment_inplace(kv.PagedCache(k, v, w.n_tokens), w.segment_prefix, e, pos, renumber_base=0,
+    srcs = keep[ranks]
+    srcs_d = torch.from_numpy(srcs).to(DEV)
+    ks_all, vs_all = np64(kf[:, srcs_d]), np64(vf[:, srcs_d])
+    pos = torch.arange(N, dtype=torch.int32, device=DEV)
+    kv.kv_compact_segment_inplace(kv.PagedCache(k, v, N), w.segment_prefix, e, pos, renumber_base=0,
                                   rope_theta=w.rope_theta)
     torch.cuda.synchronize()
-    delta = np.array(ranks) - np.array(src)
-    rk = O.bf16_round(O.rope_rotate(ks, delta[None, :, None], w.rope_theta))
-    rk[:, delta == 0] = ks[:, delta == 0]
-    gk, gv = np64(kf[:, ranks]), np64(vf[:, ranks])
-    assert (gv == vs).all()
-    assert (gk[:, delta == 0] == ks[:, delta == 0]).all()
-    assert_bf16_within_1ulp(gk, rk, "K at N=131K")
     assert (pos[:n_keep].cpu().numpy() == np.arange(n_keep)).all()
+    # first and last layer, every rank
+    gk = kf[layers][:, :n_keep].cpu()
+    gv = vf[layers][:, :n_keep].cpu()
+    step = 8192
+    for r0 in range(0, n_keep, step):
+        r1 = min(n_keep, r0 + step)
+        idx = torch.from_numpy(keep[r0:r1])
+        rk, rv, rp = O.compact_rerope(np64(k_edge[:, idx]), np64(v_edge[:, idx]), np.arange(r1 - r0),
+                                      keep[r0:r1], r0, w.rope_theta)
+        assert (rp == np.arange(r0, r1)).all()
+        assert (np64(gv[:, r0:r1]) == rv).all(), r0
+        got = np64(gk[:, r0:r1])
+        moved = keep[r0:r1] != np.arange(r0, r1)
+        assert (got[:, ~moved] == rk[:, ~moved]).all(), r0
+        assert_bf16_within_1ulp(got, rk, f"K ranks {r0}..{r1}")
+    # sampled ranks of every layer
+    delta = np.array(ranks) - srcs
+    rk = O.bf16_round(O.rope_rotate(ks_all, delta[None, :, None], w.rope_theta))
+    rk[:, delta == 0] = ks_all[:, delta == 0]
+    assert (np64(vf[:, ranks]) == vs_all).all()
+    assert_bf16_within_1ulp(np64(kf[:, ranks]), rk, "K at N=131K, all layers")
     del k, v
     torch.cuda.empty_cache()
 
@@ -715,20 +785,15 @@ def test_full_size_qwen3_1m_step_properties():
         mx = s.max()
         assert abs(float(lse[layer, h, wi]) - (mx + math.log(np.exp(s - mx).sum()))) < 1e-5
     assert int(status.item()) == 0 and int(nk.item()) == B
-    # pinned pages from the inputs (oracle definition), then the selection's order property
-    # on the device's own page scores: every kept unpinned page ranks above every dropped one
+    # pinned pages from the inputs (oracle definition), then the keep list against the
+    # oracle's selection on the device's own 62,500 page scores, bit for bit
     tok_pin = O.pinned_tokens(N, region=synth.regions(w, seed=0).numpy(), pinned_regions=1,
                               n_sink=w.n_sink, n_recent=w.n_recent)
     pin = O.page_any(tok_pin, 16)
     assert (item_pinned.cpu().numpy().astype(bool) == pin).all()
-    kept_pages = np.unique(keep.cpu().numpy() // 16)
-    assert len(kept_pages) == B // 16 and pin[kept_pages].sum() == pin.sum()
-    sc = item_score.cpu().numpy()
-    kept = np.zeros(n_items, bool)
-    kept[kept_pages] = True
-    free_kept, dropped = sc[kept & ~pin], sc[~kept & ~pin]
-    assert free_kept.min() >= dropped.max()
-    assert (keep.cpu().numpy() == (kept_pages[:, None] * 16 + np.arange(16)).reshape(-1)).all()
+    want_pages, st = O.select_items(np64(item_score), pin, B // 16)
+    assert st == 0
+    assert (keep.cpu().numpy() == O.expand_items(want_pages, 16, N)).all(), "1M-token keep list"
     ranks = sorted(set([0, B - 1] + torch.randint(0, B, (24,), generator=g).tolist()))
     srcs = keep.cpu().long()[ranks]
     kf = k.reshape(w.n_layers, -1, 8, 128)
