@@ -208,7 +208,7 @@ def clock_summary(pmc_dir, out_json=None):
     return "\n".join(rows)
 
 
-def extras(steps=5, warmup=2):
+def extras(steps=5, warmup=2, oracle=True):
     """Timings of the rows beyond the headline step, each on one GPU with inputs resident
     in HBM, HIP events on the launch stream, mean over `steps` runs after `warmup`:
       f1: single-pass scoring with a supplied LSE (sum and group maximum), Qwen3-8B 100K;
@@ -217,8 +217,13 @@ def extras(steps=5, warmup=2):
       f4: gather of 16,384 evicted rows on the device, and offload of 16,384 rows to
           pinned host memory (PCIe-bound, chunks of 1,024);
       Mistral-7B 131,072-token in-place segment eviction + re-rotation;
-      Qwen3-8B at 1,000,000 tokens: the full step (MemDecay page scoring, select, compaction).
-    Prints one JSON line."""
+      Qwen3-8B at 1,000,000 tokens: the full step (MemDecay page scoring, select, compaction);
+      the two Qwen2.5-1.5B-shaped workloads (512 and 2,048 tokens): the full step in us;
+      f4 swap-in: 16,384 rows loaded back from pinned host memory, and Penelope's chunked
+          swap of 16,384 rows through a 1,024-row buffer.
+    Prints one JSON line, then (unless oracle=False) a second one with the CPU oracle timed
+    on the 512- and 2,048-token workloads, the Mistral segment case and the 1M-token step
+    (layer samples scaled to all layers)."""
     import numpy as np
     import compaction_kv_score_amd as kv
     import synth
@@ -338,7 +343,37 @@ def extras(steps=5, warmup=2):
                                  "GBps": round(n_ev * kvb / (t_off * 1e-3) / 1e9, 2),
                                  "note": "device gather then device-to-host copies into pinned memory"}
     log(f"f4: {out['f4_gather_evicted']} {out['f4_offload_to_host']}")
-    del k, v, src, dk, dv, stage_k, stage_v, hk, hv, ws_o
+    # swap-in: the same 16,384 rows loaded back from pinned host memory into their slots,
+    # then Penelope's both-tiers-full swap of 16,384 rows through a 1,024-row buffer
+    ht_slots = torch.from_numpy(
+        __import__("oracle").evicted_tokens(N, keep_off.cpu().numpy()).astype("int32")).to(dev)
+    ws_l = None
+
+    def load():
+        nonlocal ws_l
+        ws_l = kv.kv_load_rows(src, ht_slots, hk, hv, chunk=1024, workspace=ws_l)
+
+    t_load = timed(load, n=3, w=1)
+    pool_rows = n_ev + 1024
+    pk = torch.empty((NL, pool_rows, HKV, D), dtype=torch.bfloat16, pin_memory=True)
+    pv = torch.empty_like(pk).pin_memory()
+    swap_slots = torch.sort(torch.randperm(N, generator=g)[:n_ev])[0].to(torch.int32).to(dev)
+    ws_s = None
+
+    def swap():
+        nonlocal ws_s
+        _, _, ws_s = kv.kv_swap_chunked(src, swap_slots, pk, pv, 0, n_ev, chunk=1024, workspace=ws_s)
+
+    t_swap = timed(swap, n=3, w=1)
+    out["f4_load_from_host"] = {"ms": round(t_load, 3), "tokens": n_ev, "bytes": n_ev * kvb,
+                                "GBps": round(n_ev * kvb / (t_load * 1e-3) / 1e9, 2),
+                                "note": "host-to-device copies into staging, then a scatter into the slots"}
+    out["f4_swap_chunked"] = {"ms": round(t_swap, 3), "tokens": n_ev, "chunk": 1024, "bytes": 2 * n_ev * kvb,
+                              "GBps_both_directions": round(2 * n_ev * kvb / (t_swap * 1e-3) / 1e9, 2),
+                              "note": "per chunk: gather, device-to-host into the buffer, host-to-device, "
+                                      "scatter; one stream"}
+    log(f"f4: {out['f4_load_from_host']} {out['f4_swap_chunked']}")
+    del k, v, src, dk, dv, stage_k, stage_v, hk, hv, ws_o, ws_l, ws_s, pk, pv
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- Mistral-7B segment
@@ -423,7 +458,136 @@ def extras(steps=5, warmup=2):
                                  "lse_pass": round(kb5 / (stage["lse_pass"] * 1e-3) / 1e9, 1),
                                  "mass_pass": round(kb5 / (stage["mass_pass"] * 1e-3) / 1e9, 1)}}
     log(f"1M step: {out['qwen3_8b_n1m_full_step']}")
+    del k5, v5, c5, dk5, dv5, ws5
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- small configs
+    for name in ("qwen2.5-1.5b-1layer-n512", "qwen2.5-1.5b-n2048"):
+        out[f"step_{name}"] = small_config_step(name)
+        log(f"{name}: {out[f'step_{name}']}")
     print(json.dumps({"extras": out, "n_gpus": 1, "data": "synthetic"}), flush=True)
+
+    # ---------------------------------------------------------------- oracle baselines
+    if oracle:
+        base = {}
+        for name, layers, rep in (("qwen2.5-1.5b-1layer-n512", None, 3), ("qwen2.5-1.5b-n2048", None, 3),
+                                  ("mistral-7b-n131072-segment", 2, 1), ("qwen3-8b-n1m", 2, 1)):
+            log(f"oracle baseline {name} ({layers or 'all'} layers)")
+            base[name] = oracle_baseline(name, layers, rep)
+            log(f"oracle {name}: {base[name]}")
+        print(json.dumps({"oracle_baselines": base, "data": "synthetic"}), flush=True)
+
+
+def small_config_step(name, steps=20, warmup=3):
+    """One full step of a small workload (Qwen2.5-1.5B head shape): MemDecay page scoring,
+    page selection, compaction of the kept pages with renumbering.  Median over `steps`
+    HIP-event-timed steps after `warmup`, with the MemDecay state restored from a copy
+    before every step, outside its events."""
+    import compaction_kv_score_amd as kv
+    import synth
+    dev = torch.device("cuda:0")
+    sh = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    hip = HipEvents()
+    w = synth.workload(name)
+    N, pg = w.n_tokens, w.page_size
+    k, v, bt = synth.kv_cache(w, seed=0, device=dev, paged_shuffle=True, extra_pages=2)
+    q = synth.window_queries(w, seed=0, device=dev)
+    ewma0, clock0 = synth.memdecay_state(w, seed=0)
+    b_r, lam = synth.region_params(0)
+    ewma, clock = ewma0.to(dev), clock0.to(dev)
+    ewma0, clock0 = ewma.clone(), clock.clone()
+    n_items = w.n_pages
+    item_score = torch.zeros(n_items, device=dev)
+    item_pinned = torch.zeros(n_items, dtype=torch.uint8, device=dev)
+    src = kv.PagedCache(k, v, N, bt)
+    kw = dict(policy="memdecay", window=w.window, item_tokens=pg, region=synth.regions(w, seed=0).to(dev),
+              base_prio=b_r.to(dev), decay_rate=lam.to(dev), rho=w.rho, alpha=w.alpha, tau=w.tau, dt_steps=1,
+              ewma=ewma, clock=clock, pinned_regions=1, item_score=item_score, item_pinned=item_pinned)
+    ws = torch.empty(kv.kv_score_workspace_size(src, q, **kw), dtype=torch.uint8, device=dev)
+    ws_sel = torch.empty(kv.kv_select_workspace_size(n_items), dtype=torch.uint8, device=dev)
+    B = w.budget_tokens
+    keep = torch.zeros(B, dtype=torch.int32, device=dev)
+    nk = torch.zeros(1, dtype=torch.int64, device=dev)
+    dk = torch.zeros((w.n_layers, B // pg, pg, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    dv = torch.zeros_like(dk)
+    dst = kv.PagedCache(dk, dv, B)
+    pos = torch.arange(N, dtype=torch.int32, device=dev)
+    newp = torch.zeros(B, dtype=torch.int32, device=dev)
+    times = []
+    for i in range(warmup + steps):
+        ewma.copy_(ewma0)
+        clock.copy_(clock0)
+        e = hip.create(2)
+        hip.record(e[0], sh)
+        kv.kv_score(src, q, workspace=ws, **kw)
+        kv.kv_select(item_score, item_pinned, pg, N, w.budget_items, keep, nk, workspace=ws_sel)
+        kv.kv_compact_rerope(src, dst, keep, nk, B, pos, newp, renumber_base=0, rope_theta=w.rope_theta)
+        hip.record(e[1], sh)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            times.append(hip.ms(e[0], e[1]))
+    times.sort()
+    return {"workload": name, "step_us_median": round(1e3 * times[len(times) // 2], 1),
+            "step_us_min": round(1e3 * times[0], 1), "steps": steps,
+            "KV_tokens_per_s": round(N / (times[len(times) // 2] * 1e-3), 1)}
+
+
+def oracle_baseline(name, layers=None, repeats=1):
+    """The CPU oracle, untuned, on one workload: score (when the workload scores), select
+    and compact, timed with perf_counter (best of `repeats`).  With `layers` only that many
+    layers are scored and compacted and those parts are scaled to all layers."""
+    import numpy as np
+    import oracle as O
+    import synth
+    full = synth.workload(name)
+    nl = layers or full.n_layers
+    w = synth.workload(name, n_layers=nl)
+    N = w.n_tokens
+    k, v, bt = synth.kv_cache(w, seed=0)
+    kl = k.float().double().numpy().reshape(nl, -1, w.n_kv_heads, w.head_dim)[:, :N]
+    vl = v.float().double().numpy().reshape(nl, -1, w.n_kv_heads, w.head_dim)[:, :N]
+    scale = full.n_layers / nl
+    best = None
+    for _ in range(repeats):
+        t = {}
+        t0 = time.perf_counter()
+        if w.policy == "segment":
+            keep = O.select_segment(N, w.segment_prefix, int(w.segment_frac * N), w.page_size)
+            t1 = t0
+        else:
+            q = synth.window_queries(w, seed=0).float().double().numpy()
+            kw = {}
+            if w.policy == "memdecay":
+                ewma, clock = synth.memdecay_state(w, seed=0)
+                b_r, lam = synth.region_params(0)
+                kw = dict(region=synth.regions(w, seed=0).numpy(), base_prio=b_r.double().numpy(),
+                          decay_rate=lam.double().numpy(), rho=w.rho, alpha=w.alpha, tau=w.tau,
+                          dt_steps=w.dt_steps, ewma=ewma.double().numpy(), clock=clock.numpy(),
+                          pinned_regions=1)
+            else:
+                kw = dict(accum=np.zeros(N))
+            if w.n_spans:
+                sid, nxt = synth.spans(w, seed=0)
+                kw.update(span_id=sid.numpy(), span_next_use=nxt.numpy())
+            t0 = time.perf_counter()
+            out = O.score_step(q, kl, policy=w.policy, n_sink=w.n_sink, n_recent=w.n_recent,
+                               item_tokens=w.item_tokens, **kw)
+            t1 = time.perf_counter()
+            items, _ = O.select_items(out["item_score"], out["item_pinned"], w.budget_items)
+            keep = O.expand_items(items, w.item_tokens, N)
+        t2 = time.perf_counter()
+        O.compact_rerope(kl, vl, keep, np.arange(N), 0, w.rope_theta)
+        t3 = time.perf_counter()
+        t = {"score_s": (t1 - t0) * scale, "select_s": t2 - t1, "compact_s": (t3 - t2) * scale}
+        if best is None or sum(t.values()) < sum(best.values()):
+            best = t
+    total = sum(best.values())
+    return {"workload": name, "kind": "oracle", "total_s": round(total, 4),
+            "KV_tokens_per_s": round(N / total, 1),
+            "parts_s": {a: round(b, 4) for a, b in best.items()},
+            "sample": (f"{nl} of {full.n_layers} layers, score and compaction scaled x{scale:g}"
+                       if nl != full.n_layers else "all layers") + f", best of {repeats}",
+            "host_cpus": os.cpu_count()}
 
 
 def cpu_baseline(w, layers):
@@ -497,7 +661,7 @@ def main():
         print(clock_summary(args.clock_summary, os.path.join(ROOT, "profiles", "mfma_busy.json")))
         return
     if args.extras:
-        extras()
+        extras(oracle=not args.no_cpu)
         return
     if args.copy_calibration:
         a = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")
@@ -561,18 +725,26 @@ def main():
                              meta=[(accum, dst_accum), (span_id, dst_span)])
         hip.record(ev[6], sh)
 
+    # every step scores the same state: the H2O accumulator is restored from a copy before
+    # each step, outside the step's events
+    accum0 = accum.clone()
     warm = hip.create(n_ev)
     for _ in range(args.warmup):
+        accum.copy_(accum0)
         step(warm)
     torch.cuda.synchronize()
     events = [hip.create(n_ev) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        accum.copy_(accum0)
         step(events[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_wall = (t1 - t0) * 1e3 / args.steps
+    step_ms = sorted(hip.ms(e[0], e[6]) for e in events)
+    ms_step = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
     assert int(status.item()) == 0 and int(n_keep.item()) == B
 
     def avg(a, b):
@@ -603,6 +775,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_note": "median over the timed steps of each step's HIP-event time (first kernel "
+                            "to last, one stream); state restored before every step, outside it",
+        "ms_per_step_wall_mean": ms_wall,
+        "ms_per_step_min_max": [step_ms[0], step_ms[-1]],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
