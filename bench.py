@@ -377,21 +377,9 @@ def extras(steps=5, warmup=2, oracle=True):
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- Mistral-7B segment
-    w4 = synth.workload("mistral-7b-n131072-segment")
     log("mistral-7b-n131072 inputs")
-    k4, v4, _ = synth.kv_cache(w4, seed=0, device=dev)
-    c4 = kv.PagedCache(k4, v4, w4.n_tokens)
-    n_keep4, e4 = kv.kv_select_segment(w4.n_tokens, w4.segment_prefix, int(w4.segment_frac * w4.n_tokens), 16)
-    pos4 = torch.arange(w4.n_tokens, dtype=torch.int32, device=dev)
-    t4 = timed(lambda: kv.kv_compact_segment_inplace(c4, w4.segment_prefix, e4, pos4, renumber_base=0,
-                                                     rope_theta=w4.rope_theta), n=3, w=1)
-    moved4 = n_keep4 - w4.segment_prefix
-    b4 = 2 * moved4 * w4.kv_bytes_per_token
-    out["mistral7b_n131072_segment_inplace"] = {"workload": w4.name, "ms": round(t4, 3), "evicted": e4, "moved_tokens": moved4,
-                                   "bytes": b4, "GBps": round(b4 / (t4 * 1e-3) / 1e9, 1),
-                                   "hbm_frac": round(b4 / (t4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    out["mistral7b_n131072_segment_inplace"] = segment_case(steps=3, warmup=1)
     log(f"segment: {out['mistral7b_n131072_segment_inplace']}")
-    del k4, v4, c4
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- Qwen3-8B 1M tokens
@@ -476,6 +464,37 @@ def extras(steps=5, warmup=2, oracle=True):
             base[name] = oracle_baseline(name, layers, rep)
             log(f"oracle {name}: {base[name]}")
         print(json.dumps({"oracle_baselines": base, "data": "synthetic"}), flush=True)
+
+
+def segment_case(steps=3, warmup=1):
+    """Mistral-7B shape, 131,072 tokens: in-place front-of-history segment eviction of 30%
+    (16,384-token prefix kept) with re-rotation of the moved suffix, all 32 layers.  Runs
+    are enqueued back to back on one stream; mean HIP-event time per run."""
+    import compaction_kv_score_amd as kv
+    import synth
+    dev = torch.device("cuda:0")
+    sh = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    hip = HipEvents()
+    w4 = synth.workload("mistral-7b-n131072-segment")
+    k4, v4, _ = synth.kv_cache(w4, seed=0, device=dev)
+    c4 = kv.PagedCache(k4, v4, w4.n_tokens)
+    n_keep4, e4 = kv.kv_select_segment(w4.n_tokens, w4.segment_prefix, int(w4.segment_frac * w4.n_tokens), 16)
+    pos4 = torch.arange(w4.n_tokens, dtype=torch.int32, device=dev)
+    run = lambda: kv.kv_compact_segment_inplace(c4, w4.segment_prefix, e4, pos4, renumber_base=0,  # noqa: E731
+                                                rope_theta=w4.rope_theta)
+    for _ in range(warmup):
+        run()
+    evs = [hip.create(2) for _ in range(steps)]
+    for e in evs:
+        hip.record(e[0], sh)
+        run()
+        hip.record(e[1], sh)
+    torch.cuda.synchronize()
+    t4 = sum(hip.ms(e[0], e[1]) for e in evs) / steps
+    moved4 = n_keep4 - w4.segment_prefix
+    b4 = 2 * moved4 * w4.kv_bytes_per_token
+    return {"workload": w4.name, "ms": round(t4, 3), "evicted": e4, "moved_tokens": moved4, "bytes": b4,
+            "GBps": round(b4 / (t4 * 1e-3) / 1e9, 1), "hbm_frac": round(b4 / (t4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def small_config_step(name, steps=20, warmup=3):
@@ -649,6 +668,9 @@ def main():
                     help="time the rows beyond the headline step (single-pass and group-maximum "
                          "scoring, reference store, LRFU, tail compaction, offload, the Mistral "
                          "segment case and the 1M-token step) and print one JSON line")
+    ap.add_argument("--segment", action="store_true",
+                    help="only the Mistral-7B 131,072-token in-place segment case (5 runs after 1 "
+                         "warm-up), one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) three "
                          "times, to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -662,6 +684,9 @@ def main():
         return
     if args.extras:
         extras(oracle=not args.no_cpu)
+        return
+    if args.segment:
+        print(json.dumps({"segment": segment_case(steps=5, warmup=1)}), flush=True)
         return
     if args.copy_calibration:
         a = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")

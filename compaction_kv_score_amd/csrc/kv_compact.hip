@@ -38,6 +38,17 @@ __device__ __forceinline__ uint4 load_once(const uint16_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16-byte store marked non-temporal: streams to memory without allocating in the caches.
+__device__ __forceinline__ void store_once(uint16_t* p, const uint4& v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)p);
+}
+
+template <bool kNt>
+__device__ __forceinline__ void store16(uint16_t* p, const uint4& v) {
+  if constexpr (kNt) store_once(p, v);
+  else *(uint4*)p = v;
+}
+
 __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) {
   return (double)__uint_as_float(bits16 << 16);
 }
@@ -136,7 +147,7 @@ __device__ __forceinline__ void gather_meta_row(const MetaSet& m, int64_t j, int
   }
 }
 
-template <bool kStore>
+template <bool kStore, bool kNt>
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a) {
   __shared__ double2 cs[64];
   __shared__ double2 cs_chk[kStore ? 64 : 1];
@@ -225,11 +236,11 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
       vhi = load_once(a.src_v + so + 64);
     }
     if (delta != 0) rotate_chunk(klo, khi, &cs[(rem & 7) * 8]);
-    *(uint4*)(a.dst_k + d_o) = klo;
-    *(uint4*)(a.dst_k + d_o + 64) = khi;
+    store16<kNt>(a.dst_k + d_o, klo);
+    store16<kNt>(a.dst_k + d_o + 64, khi);
     if (!in_place) {
-      *(uint4*)(a.dst_v + d_o) = vlo;
-      *(uint4*)(a.dst_v + d_o + 64) = vhi;
+      store16<kNt>(a.dst_v + d_o, vlo);
+      store16<kNt>(a.dst_v + d_o + 64, vhi);
     }
   }
   // The rank's new position, metadata and store position, written by its first
@@ -438,15 +449,27 @@ int compact_parts(int n_layers, int n_kv_heads) {
   return (items + kCompactThreads - 1) / kCompactThreads;
 }
 
+// A launch that writes well beyond what the 256 MB memory-side cache holds streams its
+// stores past the caches (measured: 19.8 GB in-place segment move 3.65 -> 3.39 ms); a
+// smaller one keeps plain stores, whose dirty lines the cache absorbs and writes back
+// after the kernel (2,048 Qwen3-8B tokens, 302 MB written: 0.101 against 0.117 ms).
+constexpr int64_t kStreamStoreBytes = 1LL << 30;
+
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const int64_t n = a.rank1 - a.rank0;
   if (n <= 0) return hipSuccess;
   const int64_t grid = n * a.parts;
   if (a.parts < 1 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (a.ref_src_k)
-    hipLaunchKernelGGL(compact_kernel<true>, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(compact_kernel<false>, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a);
+  const int64_t written = n * a.n_layers * a.n_kv_heads * (int64_t)kHeadDim * 2 * 2;
+  const bool nt = written > kStreamStoreBytes;
+  const dim3 g((unsigned)grid), b(kCompactThreads);
+  if (a.ref_src_k) {
+    if (nt) hipLaunchKernelGGL((compact_kernel<true, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((compact_kernel<true, false>), g, b, 0, s, a);
+  } else {
+    if (nt) hipLaunchKernelGGL((compact_kernel<false, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((compact_kernel<false, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 
