@@ -16,7 +16,9 @@ import re
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvscore.so")
+# KVSCORE_LIB names another build of the same library (the tests load the host-sanitized
+# build this way); by default the library built in place next to this file is loaded.
+LIB_PATH = os.environ.get("KVSCORE_LIB") or os.path.join(_PKG, "libkvscore.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvscore.h")
 
 KV_OK = 0

@@ -70,5 +70,42 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build (device code is compiled as
+# usual; every sanitizer flag applies to the host pass only).
+SANITIZE_HOST_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def asan_runtime() -> str:
+    """The shared AddressSanitizer runtime of the ROCm compiler (to LD_PRELOAD into a
+    process that loads the sanitized library), or '' when it is not installed."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else ""
+
+
+def build_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """Compile libkvscore with the host code under ASan and UBSan into out_dir (for the
+    host-side checks of the argument validation and bookkeeping); returns its path."""
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-O3")] + ["-O1", "-g"] + SANITIZE_HOST_FLAGS
+    from concurrent.futures import ThreadPoolExecutor
+    objs = [os.path.join(out_dir, s.replace(".hip", ".o")) for s in SOURCES]
+    cmds = [[hipcc(), *flags, "-c", "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max(1, min(len(cmds), os.cpu_count() or 1, 8))) as pool:
+        list(pool.map(lambda c: _run(c, verbose), cmds))
+    lib = os.path.join(out_dir, "libkvscore_san.so")
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *SANITIZE_HOST_FLAGS, "-shared-libasan", *objs,
+          "-o", lib], verbose)
+    for o in objs:
+        os.remove(o)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -73,7 +73,9 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // issued from inline assembly so that the compiler does not track it: otherwise it
 // would conservatively wait for these loads before every LDS read, which would undo the
 // prefetch.  Completion is awaited explicitly with vmcnt before the barrier that
-// publishes a tile (all waits in this file are hand-placed for that reason).
+// publishes a tile (all waits in this file are hand-placed for that reason).  A pass
+// reads every key once, so the load is marked non-temporal ("nt"): it streams through
+// the caches instead of displacing what they hold (measured: both passes ~1.5% faster).
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   const uint32_t dst = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
@@ -83,7 +85,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(src), "s"(dst)
