@@ -73,29 +73,45 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // issued from inline assembly so that the compiler does not track it: otherwise it
 // would conservatively wait for these loads before every LDS read, which would undo the
 // prefetch.  Completion is awaited explicitly with vmcnt before the barrier that
-// publishes a tile (all waits in this file are hand-placed for that reason).  A pass
-// reads every key once, so the load is marked non-temporal ("nt"): it streams through
-// the caches instead of displacing what they hold (measured: both passes ~1.5% faster).
+// publishes a tile (all waits in this file are hand-placed for that reason).
+// kNt marks the load non-temporal ("nt"): it streams through the caches instead of
+// allocating in them.  Each pass reads every key once.  Pass 1 streams (measured: pass 1
+// 1.2% faster, and pass 2 0.3% faster too); pass 2 keeps the keys it reads cached, as the
+// compaction that follows re-reads the kept keys, and streaming there too would make
+// compaction 19% slower for another 1.0% on pass 2.
+template <bool kNt>
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   const uint32_t dst = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
   // M0 carries the LDS destination; the previous M0 is restored so that the compiler's
   // own view of M0 stays valid.  The wait state separates the M0 write from its use.
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(dst)
-      : "memory");
+  if constexpr (kNt)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(dst)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(dst)
+        : "memory");
 }
 
 // Everything a workgroup needs to locate its keys and queries.  The G*W rows of one
 // (layer, KV head) are split into groups of at most 256 rows, one workgroup each; wave
-// wv owns rows row0 + 32*wv .. row0 + 32*wv + 31 of its group.
-template <int NW>
+// wv owns rows row0 + 32*wv .. row0 + 32*wv + 31 of its group.  kNt: the key loads are
+// non-temporal (see dma16).
+template <int NW, bool kNt>
 struct Ctx {
   static constexpr int LPW = (kLoadsPerTile + NW - 1) / NW;  // loads per wave per tile
   static constexpr bool kJunk = (kLoadsPerTile % NW) != 0;
@@ -198,7 +214,7 @@ struct Ctx {
       const int32_t page = kScalar ? __builtin_amdgcn_readfirstlane(ph[m]) : ph[m];
       const uint16_t* base =
           kbase + (int64_t)page * a.page_stride + ((tile_j0 + 4 * i) & pmask) * slot_stride;
-      dma16(base + voff[m], dst);
+      dma16<kNt>(base + voff[m], dst);
     }
   }
 
@@ -220,7 +236,7 @@ struct Ctx {
         const int c16 = (lane & 15) ^ (row & 15);
         const uint16_t* base =
             kbase + (int64_t)ph[m] * a.page_stride + ((tile_j0 + 4 * i) & pmask) * slot_stride;
-        dma16(base + (lane >> 4) * slot_stride + c16 * 8, dst);
+        dma16<kNt>(base + (lane >> 4) * slot_stride + c16 * 8, dst);
       }
     } else {
       // small pages or the chunk's ragged last tile: per-lane addresses
@@ -234,7 +250,7 @@ struct Ctx {
         if (j >= j1) j = j1 - 1;
         const uint16_t* src =
             kbase + token_offset(j, a.page_shift, a.page_stride, bt, slot_stride) + c16 * 8;
-        dma16(src, dst);
+        dma16<kNt>(src, dst);
       }
     }
   }
@@ -282,8 +298,8 @@ struct StageC {
 // stage t % kStages), so every LDS fragment address is a constant offset from a
 // per-lane base and needs no address arithmetic (the LSE pass does without: unrolled,
 // its register allocation spills).
-template <int NW, class P>
-__device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[kTileBytes],
+template <int NW, bool kNt, class P>
+__device__ __forceinline__ void run_tiles(const Ctx<NW, kNt>& x, P& p, uint8_t (*kt)[kTileBytes],
                                           uint8_t* junk, const int32_t* __restrict__ bt) {
   const int nt = x.n_tiles;
   // LDS addresses of the ring stages and the junk buffer, for the direct-to-LDS loads
@@ -296,7 +312,7 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
   const int64_t clean_end = x.j1 < last_clean_key + 1 ? x.j1 : last_clean_key + 1;
   const int nc = clean_end > x.j0 ? (int)((clean_end - x.j0) / kTile) : 0;
 
-  int32_t ph[Ctx<NW>::LPW] = {};
+  int32_t ph[Ctx<NW, kNt>::LPW] = {};
   for (int t = 0; t < kAhead && t < nt; ++t) {
     x.fetch_pages(t, bt, ph);
     x.issue_tile(t, stage_addr(t), jk, bt, ph);
@@ -428,7 +444,7 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW>& x, P& p, uint8_t (*kt)[
 // a half (8*(i/4) + 4*(lane/32) + i%4), so the running softmax state is lane-local.
 template <int NW>
 struct LsePass {
-  using C = Ctx<NW>;
+  using C = Ctx<NW, true>;
   static constexpr bool kOverlap = true;
   static constexpr bool kUnrollStages = false;
   const C& x;
@@ -531,7 +547,7 @@ struct LsePass {
 
 template <int NW>
 __device__ __forceinline__ void lse_pass_body(const ScoreArgs& a, const int32_t* __restrict__ bt) {
-  using C = Ctx<NW>;
+  using C = Ctx<NW, true>;
   __shared__ __attribute__((aligned(1024))) uint8_t kt[kStages][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t junk[C::kJunk ? 1024 : 16];
   const C x(a);
@@ -566,7 +582,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 // first (RS = 2^m), one exponential per group.
 template <int NW, int kMaxLog>
 struct MassPass {
-  using C = Ctx<NW>;
+  using C = Ctx<NW, false>;
   // the sum keeps two accumulator sets (the group maximum's extra registers would spill)
   static constexpr bool kOverlap = kMaxLog == 0;
   static constexpr bool kUnrollStages = true;
@@ -738,7 +754,7 @@ struct MassPass {
 
 template <int NW, int kMaxLog>
 __device__ __forceinline__ void mass_pass_body(const ScoreArgs& a, const int32_t* __restrict__ bt) {
-  using C = Ctx<NW>;
+  using C = Ctx<NW, false>;
   using P = MassPass<NW, kMaxLog>;
   __shared__ __attribute__((aligned(1024))) uint8_t kt[kStages][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t junk[C::kJunk ? 1024 : 16];
