@@ -1,7 +1,9 @@
 // C ABI of libkvscore: argument validation, workspace layout and launch order.
 // The entry points and their contracts are documented in include/kvscore.h.
 #include <math.h>
+#include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -9,6 +11,27 @@
 #include "kv_internal.h"
 
 using namespace kvs;
+
+namespace kvs {
+
+bool trace_on() {
+  static const bool on = [] {
+    const char* v = getenv("KVSCORE_TRACE");
+    return v != nullptr && v[0] != '\0' && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void trace_launch(const char* fmt, ...) {
+  char line[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof(line), fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[kvscore] %s\n", line);
+}
+
+}  // namespace kvs
 
 namespace {
 
@@ -485,6 +508,40 @@ int32_t kv_rope_inv_freq(const kv_rope* rope, double* inv_freq) {
   return KV_OK;
 }
 
+// [a, a + an) and [b, b + bn) share a byte
+static bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
+  const uint64_t x = (uint64_t)(uintptr_t)a, y = (uint64_t)(uintptr_t)b;
+  return an && bn && x < y + bn && y < x + an;
+}
+
+// Bytes a cache without a block table spans from its base pointer (the last layer's
+// pages of its n_tokens); 0 when a block table places pages anywhere.
+static uint64_t cache_extent(const kv_cache_desc* c) {
+  if (c->block_table) return 0;
+  const int64_t pages = (c->n_tokens + c->page_size - 1) / c->page_size;
+  return ((uint64_t)(c->n_layers - 1) * (uint64_t)c->layer_stride + (uint64_t)pages * (uint64_t)c->page_stride) * 2u;
+}
+
+// The gather form reads and writes different memory (ActKV Sec. 7.2 names the hazard of
+// overlapping an in-place copy): its K/V extents (known without block tables), its
+// positions and its metadata arrays must not overlap.
+static int32_t check_disjoint(const kv_cache_desc* src, const kv_cache_desc* dst, const int32_t* old_pos,
+                              const int32_t* new_pos, int64_t max_keep, const MetaSet& ms) {
+  const uint64_t se = cache_extent(src), de = cache_extent(dst);
+  const void* sp[2] = {src->k, src->v};
+  const void* dp[2] = {dst->k, dst->v};
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j)
+      if (overlaps(sp[i], se, dp[j], de)) return KV_EINVAL;
+  if (new_pos && overlaps(old_pos, (uint64_t)src->n_tokens * 4u, new_pos, (uint64_t)max_keep * 4u)) return KV_EINVAL;
+  for (int m = 0; m < ms.n; ++m) {
+    const uint64_t b = (uint64_t)ms.elem_bytes[m];
+    if (overlaps(ms.src[m], (uint64_t)src->n_tokens * b, ms.dst[m], (uint64_t)max_keep * b)) return KV_EINVAL;
+    if (new_pos && overlaps(ms.dst[m], (uint64_t)max_keep * b, new_pos, (uint64_t)max_keep * 4u)) return KV_EINVAL;
+  }
+  return KV_OK;
+}
+
 static int32_t check_ref(const kv_ref_store* r, const kv_cache_desc* c, int64_t min_slots) {
   if (!r->k || !r->pos || r->n_slots < min_slots || r->n_slots <= 0) return KV_EINVAL;
   const int64_t slot = (int64_t)c->n_kv_heads * kHeadDim;
@@ -571,6 +628,7 @@ int32_t kv_compact_rerope_ex(const kv_cache_desc* src, const kv_cache_desc* dst,
   if (renumber_base >= 0 && limit > 0 && (int64_t)renumber_base + max_keep > limit) return KV_ELIMIT;
   MetaSet ms;
   if ((rc = check_meta(meta, n_meta, &ms))) return rc;
+  if ((rc = check_disjoint(src, dst, old_pos, new_pos, max_keep, ms))) return rc;
   if (max_keep == 0) return KV_OK;
   if ((rc = check_device())) return rc;
   CompactArgs a;

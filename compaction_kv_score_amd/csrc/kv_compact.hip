@@ -421,6 +421,9 @@ hipError_t launch_gather_evicted(const EvictArgs& a0, hipStream_t s) {
   a.parts = copy_parts(a.n_layers * a.n_kv_heads * (kHeadDim / 8));
   const int64_t grid = a.count * a.parts;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (trace_on())
+    trace_launch("gather_evicted grid=%lld block=%d  rows=%lld first=%lld parts=%d", (long long)grid, kCompactThreads,
+                 (long long)a.count, (long long)a.first, a.parts);
   hipLaunchKernelGGL(gather_evicted_kernel, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -431,6 +434,9 @@ hipError_t launch_move_rows(const MoveArgs& a0, hipStream_t s) {
   a.parts = copy_parts(a.n_layers * a.n_kv_heads * (kHeadDim / 8));
   const int64_t grid = a.count * a.parts;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (trace_on())
+    trace_launch("move_rows grid=%lld block=%d  rows=%lld parts=%d meta=%d", (long long)grid, kCompactThreads,
+                 (long long)a.count, a.parts, a.meta.n);
   hipLaunchKernelGGL(move_rows_kernel, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -440,6 +446,9 @@ hipError_t launch_move_rows(const MoveArgs& a0, hipStream_t s) {
 // workgroups, as the other copies do, would repeat that latency (measured slower).
 hipError_t launch_tail_compact(const TailArgs& a, int64_t pairs, hipStream_t s) {
   if (pairs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (trace_on())
+    trace_launch("tail_compact grid=%lld block=%d  start=%lld budget=%lld", (long long)(pairs > 0 ? pairs : 1),
+                 kCompactThreads, (long long)a.start, (long long)a.budget);
   hipLaunchKernelGGL(tail_compact_kernel, dim3((unsigned)(pairs > 0 ? pairs : 1)), dim3(kCompactThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -463,6 +472,10 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const int64_t written = n * a.n_layers * a.n_kv_heads * (int64_t)kHeadDim * 2 * 2;
   const bool nt = written > kStreamStoreBytes;
   const dim3 g((unsigned)grid), b(kCompactThreads);
+  if (trace_on())
+    trace_launch("compact grid=%lld block=%d  ranks=[%lld,%lld) parts=%d layers=%d kv_heads=%d store=%d stream_stores=%d",
+                 (long long)grid, kCompactThreads, (long long)a.rank0, (long long)a.rank1, a.parts, a.n_layers,
+                 a.n_kv_heads, a.ref_src_k != nullptr, (int)nt);
   if (a.ref_src_k) {
     if (nt) hipLaunchKernelGGL((compact_kernel<true, true>), g, b, 0, s, a);
     else hipLaunchKernelGGL((compact_kernel<true, false>), g, b, 0, s, a);
@@ -475,6 +488,7 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
 
 hipError_t launch_ref_invalidate(int32_t* pos, int64_t count, hipStream_t s) {
   if (count <= 0) return hipSuccess;
+  if (trace_on()) trace_launch("ref_invalidate grid=%lld block=256  slots=%lld", (long long)((count + 255) / 256), (long long)count);
   hipLaunchKernelGGL(ref_invalidate_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, pos, count);
   return hipGetLastError();
 }

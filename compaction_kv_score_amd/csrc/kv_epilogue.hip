@@ -139,6 +139,10 @@ __global__ __launch_bounds__(kEpiThreads * kEpiSplit) void epilogue_kernel(Epilo
 
 hipError_t launch_epilogue(const EpilogueArgs& a, hipStream_t s) {
   const int64_t blocks = (a.n_tokens + kEpiThreads - 1) / kEpiThreads;
+  if (trace_on())
+    trace_launch("epilogue grid=%lld block=%d  tokens=%lld partials=%d policy=%s items_of=%d", (long long)blocks,
+                 kEpiThreads * kEpiSplit, (long long)a.n_tokens, a.n_parts,
+                 a.policy == KV_POLICY_MEMDECAY ? "memdecay" : "h2o", 1 << a.item_shift);
   hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)blocks), dim3(kEpiThreads * kEpiSplit), 0, s, a);
   return hipGetLastError();
 }

@@ -8,6 +8,11 @@
 
 namespace kvs {
 
+// KVSCORE_TRACE set (and not "0") in the environment: every launch logs its kernel, grid,
+// block and the shape that chose them to stderr, one line each (read once per process).
+bool trace_on();
+void trace_launch(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

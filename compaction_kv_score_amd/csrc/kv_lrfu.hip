@@ -454,6 +454,9 @@ size_t lrfu_workspace_bytes(int64_t n) {
 }
 
 hipError_t launch_lrfu(const LrfuArgs& a, hipStream_t s) {
+  if (trace_on())
+    trace_launch("lrfu init+3 hist+count+update grid=%d block=%d  entries=%lld top_p=%g", a.n_blocks, kThreads,
+                 (long long)a.n, (double)a.top_p);
   hipLaunchKernelGGL(lrfu_init_kernel, dim3(1), dim3(64), 0, s, a.st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

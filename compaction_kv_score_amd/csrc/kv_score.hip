@@ -864,6 +864,12 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
 hipError_t launch_score_pass(const ScoreArgs& a, bool pass2, hipStream_t s) {
   const int group_rows = a.rows < kRowsPerGroup ? a.rows : kRowsPerGroup;
   const int nw = (group_rows + 31) / 32;
+  if (trace_on())
+    trace_launch("%s grid=%lld block=%d  layers=%d kv_heads=%d tokens=%lld rows=%d row_groups=%d chunk=%d chunks=%d%s",
+                 pass2 ? "mass_pass" : "lse_pass",
+                 (long long)a.n_chunks * a.n_rsplit * a.n_kv_heads * a.n_layers, nw * 64, a.n_layers, a.n_kv_heads,
+                 (long long)a.n_tokens, a.rows, a.n_rsplit, a.chunk, a.n_chunks,
+                 pass2 && a.max_log ? " group_max" : "");
   if (!pass2) return launch_nw<-1>(a, nw, s);
   switch (a.max_log) {
     case 0: return launch_nw<0>(a, nw, s);
@@ -878,6 +884,9 @@ hipError_t launch_score_pass(const ScoreArgs& a, bool pass2, hipStream_t s) {
 
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.n_lg * a.rows;
+  if (trace_on())
+    trace_launch("lse_combine grid=%lld block=256  rows=%lld chunks=%d%s", (long long)((n + 255) / 256), (long long)n,
+                 a.n_chunks, a.lse_in ? " lse_in" : "");
   hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

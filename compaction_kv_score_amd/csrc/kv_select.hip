@@ -422,6 +422,9 @@ __global__ __launch_bounds__(kSelThreads) void select_init_kernel(SelectState* s
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+  if (trace_on())
+    trace_launch("select init+3 hist+count+emit grid=%d block=%d  items=%lld item_tokens=%d budget=%lld", a.n_blocks,
+                 kSelThreads, (long long)a.n_items, a.item_tokens, (long long)a.budget);
   hipLaunchKernelGGL(select_init_kernel, dim3(1), dim3(kSelThreads), 0, s, a.st, a.hist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -471,6 +474,9 @@ hipError_t launch_segment_keep(int64_t n_tokens, int64_t prefix, int64_t evict, 
   (void)n_tokens;
   const int64_t n_write = keep ? (n_keep < capacity ? n_keep : capacity) : 0;
   const int64_t n = n_write > 1 ? n_write : 1;
+  if (trace_on())
+    trace_launch("segment_keep grid=%lld block=256  tokens=%lld prefix=%lld evict=%lld", (long long)((n + 255) / 256),
+                 (long long)n_tokens, (long long)prefix, (long long)evict);
   hipLaunchKernelGGL(segment_keep_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      prefix, evict, keep, n_write, n_keep_dev, n_keep);
   return hipGetLastError();

@@ -365,7 +365,8 @@ int32_t kv_select_segment(int64_t n_tokens, int64_t prefix_len, int64_t evict_to
  * sizes the launch).  keep_tokens must be ascending indices of src; a rank whose entry
  * lies outside [0, src.n_tokens) is skipped (nothing read or written for it).  dst must
  * not overlap src, and new_pos and the meta destinations must not overlap old_pos,
- * keep_tokens or the meta sources.  dst.n_tokens >= max_keep; its layer and head
+ * keep_tokens or the meta sources.  KV_EINVAL when they visibly do: K/V extents of
+ * caches without a block table, positions and metadata arrays are checked on the host.  dst.n_tokens >= max_keep; its layer and head
  * shapes must equal src's.  limit > 0 with renumbering requires
  * renumber_base + max_keep <= limit (PACE's L), else KV_ELIMIT.  new_pos may be NULL.
  */

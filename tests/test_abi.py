@@ -307,3 +307,33 @@ def test_swap_row_bookkeeping_matches_oracle(count, chunk, in_first, buf):
     pool = np.zeros((1, rows, 1, 1))
     _, _, want, want_next = O.chunked_swap(gpu, pool, np.arange(count), in_first, buf, chunk)
     assert list(out) == want.tolist() and nxt.value == want_next
+
+
+def test_compact_rejects_overlapping_source_and_destination():
+    """The gather form must read and write different memory: overlapping K/V extents
+    (caches without a block table), positions or metadata are refused on the host."""
+    L = kv.lib()
+    G = 1 << 30                                           # far-apart fake bases, never dereferenced
+    src = _cache(k=G, v=2 * G, n_tokens=1000)
+    ok_dst = _cache(k=3 * G, v=4 * G, n_tokens=100)
+    span = 2 * (7 * 16 * 2 * 128 + 63 * 16 * 2 * 128)     # bytes of src's K extent
+    inside = _cache(k=G + span - 256, v=4 * G, n_tokens=100)
+    after = _cache(k=G + span, v=4 * G, n_tokens=100)
+    meta0 = (kv.KvMetaDesc * 1)()
+
+    def call(dst, old=5 * G, new=6 * G, meta=meta0, n_meta=0):
+        return L.kv_compact_rerope(ctypes.byref(src), ctypes.byref(dst), FAKE, None, 100, old, new, 0, 1e6, 0,
+                                   meta, n_meta, None)
+    # validation passes and the call reaches the device check (no GPU here)
+    assert call(ok_dst) not in (kv.KV_EINVAL, kv.KV_ELIMIT, kv.KV_EWORKSPACE)
+    assert call(after) not in (kv.KV_EINVAL, kv.KV_ELIMIT, kv.KV_EWORKSPACE)
+    assert call(inside) == kv.KV_EINVAL                   # dst K inside src K's extent
+    assert call(_cache(k=3 * G, v=2 * G + 512, n_tokens=100)) == kv.KV_EINVAL   # dst V inside src V
+    assert call(ok_dst, old=5 * G, new=5 * G + 3996) == kv.KV_EINVAL          # new_pos over old_pos
+    assert call(ok_dst, old=5 * G, new=5 * G + 4000) not in (kv.KV_EINVAL,)
+    m = (kv.KvMetaDesc * 1)(kv.KvMetaDesc(7 * G, 7 * G + 3000, 4, 0))         # dst inside src
+    assert call(ok_dst, meta=m, n_meta=1) == kv.KV_EINVAL
+    m = (kv.KvMetaDesc * 1)(kv.KvMetaDesc(7 * G, 6 * G + 200, 4, 0))          # dst over new_pos
+    assert call(ok_dst, meta=m, n_meta=1) == kv.KV_EINVAL
+    m = (kv.KvMetaDesc * 1)(kv.KvMetaDesc(7 * G, 8 * G, 4, 0))
+    assert call(ok_dst, meta=m, n_meta=1) not in (kv.KV_EINVAL,)
