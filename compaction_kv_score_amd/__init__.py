@@ -135,8 +135,9 @@ def lib() -> ctypes.CDLL:
             "kv_offload_evicted": (i32, [P(KvCacheDesc), vp, i64, i64, vp, vp, vp, vp, sz, vp]),
             "kv_load_rows": (i32, [P(KvCacheDesc), vp, i64, vp, vp, i64, i64, i64, P(KvMetaDesc), i32, vp,
                                    sz, vp]),
+            "kv_swap_workspace_size": (i32, [P(KvCacheDesc), i64, P(sz)]),
             "kv_swap_chunked": (i32, [P(KvCacheDesc), vp, i64, vp, vp, i64, i64, i64, i64, P(i64), P(i64), vp,
-                                      sz, vp]),
+                                      sz, vp, vp]),
             "kv_lrfu_update": (i32, [vp, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float, vp, vp, vp, sz,
                                      vp]),
             "kv_compact_tail_inplace": (i32, [P(KvCacheDesc), vp, vp, i64, i64, P(KvMetaDesc), i32, P(i64),
@@ -375,18 +376,29 @@ def kv_load_rows(dst: PagedCache, slots, host_k, host_v, host_first=0, count=Non
     return workspace
 
 
-def kv_swap_chunked(cache: PagedCache, slots, host_k, host_v, in_first, buf_first, chunk=1024, workspace=None):
-    """Penelope's both-tiers-full swap (see kv_swap_chunked).  Returns (out_rows list,
-    next_buf_first, workspace)."""
+def kv_swap_workspace_size(cache: PagedCache, chunk) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().kv_swap_workspace_size(ctypes.byref(cache.desc()), int(chunk), ctypes.byref(b)),
+           "kv_swap_workspace_size")
+    return b.value
+
+
+def kv_swap_chunked(cache: PagedCache, slots, host_k, host_v, in_first, buf_first, chunk=1024, workspace=None,
+                    in_stream=None):
+    """Penelope's both-tiers-full swap (see kv_swap_chunked): the outgoing side runs on the
+    current stream, the incoming side on in_stream (a torch.cuda.Stream; None = the current
+    stream, everything in order).  Returns (out_rows list, next_buf_first, workspace)."""
     count = int(slots.numel())
     if workspace is None:
-        workspace = torch.empty(kv_offload_workspace_size(cache, chunk), dtype=torch.uint8, device=cache.k.device)
+        workspace = torch.empty(kv_swap_workspace_size(cache, chunk), dtype=torch.uint8, device=cache.k.device)
     out = (ctypes.c_int64 * max(1, count))()
     nxt = ctypes.c_int64(-1)
+    s = _stream(cache.k.device)
+    s_in = s if in_stream is None else ctypes.c_void_p(in_stream.cuda_stream)
     _check(lib().kv_swap_chunked(ctypes.byref(cache.desc()), _ptr(slots), count, _host_ptr(host_k),
                                  _host_ptr(host_v), int(host_k.shape[1]), int(in_first), int(buf_first),
                                  int(chunk), out, ctypes.byref(nxt), _ptr(workspace), workspace.numel(),
-                                 _stream(cache.k.device)), "kv_swap_chunked")
+                                 s, s_in), "kv_swap_chunked")
     return list(out)[:count], nxt.value, workspace
 
 

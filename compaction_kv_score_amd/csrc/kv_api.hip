@@ -900,12 +900,20 @@ int32_t kv_load_rows(const kv_cache_desc* dst, const int32_t* slots, int64_t cou
   return KV_OK;
 }
 
+int32_t kv_swap_workspace_size(const kv_cache_desc* cache, int64_t chunk, size_t* bytes) {
+  size_t one = 0;
+  const int32_t rc = kv_offload_workspace_size(cache, chunk, &one);
+  if (rc) return rc;
+  *bytes = 2 * one;   // one staging area per direction
+  return KV_OK;
+}
+
 int32_t kv_swap_chunked(const kv_cache_desc* cache, const int32_t* slots, int64_t count, void* host_k,
                         void* host_v, int64_t host_rows, int64_t in_first, int64_t buf_first, int64_t chunk,
                         int64_t* out_rows, int64_t* next_buf_first, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
+                        hipStream_t stream, hipStream_t in_stream) {
   size_t need = 0;
-  int32_t rc = kv_offload_workspace_size(cache, chunk, &need);
+  int32_t rc = kv_swap_workspace_size(cache, chunk, &need);
   if (rc) return rc;
   if (count < 0 || (count > 0 && (!slots || !host_k || !host_v))) return KV_EINVAL;
   if (in_first < 0 || buf_first < 0 || in_first + count > host_rows) return KV_EINVAL;
@@ -924,33 +932,69 @@ int32_t kv_swap_chunked(const kv_cache_desc* cache, const int32_t* slots, int64_
   if (next_buf_first) *next_buf_first = buf;
   if (count == 0) return KV_OK;
   if ((rc = check_device())) return rc;
-  const kv_cache_desc stage = staging_desc(cache, ws, chunk);
-  MoveArgs out = move_args(cache, &stage);
-  MoveArgs in = move_args(&stage, cache);
+  // Outgoing chunks (gather, device-to-host) run on `stream` through the first staging
+  // area, incoming ones (host-to-device, scatter) on `in_stream` through the second, so
+  // that the two directions of the link overlap.  Two orderings cross the streams: chunk
+  // c's scatter overwrites the slots its gather reads, and chunk c's device-to-host copy
+  // overwrites the CPU rows chunk c-1's host-to-device copy reads (its buffer).
+  const bool two = in_stream != stream;
+  size_t one = 0;
+  kv_offload_workspace_size(cache, chunk, &one);
+  const kv_cache_desc st_out = staging_desc(cache, ws, chunk);
+  const kv_cache_desc st_in = staging_desc(cache, (char*)ws + one, chunk);
+  MoveArgs out = move_args(cache, &st_out);
+  MoveArgs in = move_args(&st_in, cache);
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};   // start, gathered, read from the host
+  hipError_t e = hipSuccess;
+  auto cleanup = [&]() {
+    for (hipEvent_t x : ev)
+      if (x) hipEventDestroy(x);   // released once the work recorded on it has completed
+  };
+  if (two) {
+    for (hipEvent_t& x : ev)
+      if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) {
+        cleanup();
+        return hip_fail(e);
+      }
+    // the incoming side starts after the work enqueued so far on `stream`
+    if ((e = hipEventRecord(ev[0], stream)) != hipSuccess || (e = hipStreamWaitEvent(in_stream, ev[0], 0)) != hipSuccess) {
+      cleanup();
+      return hip_fail(e);
+    }
+  }
+  hipStream_t sin = two ? in_stream : stream;
   buf = buf_first;
-  for (int64_t c0 = 0; c0 < count; c0 += chunk) {
+  for (int64_t c0 = 0; c0 < count && e == hipSuccess; c0 += chunk) {
     const int64_t cnt = count - c0 < chunk ? count - c0 : chunk;
-    // the chunk leaving the GPU: gathered, then written into the current CPU buffer
+    // the chunk leaving the GPU: gathered, then written into the current CPU buffer once
+    // the previous incoming chunk has been read from those rows
     out.src_rows = slots + c0;
     out.dst_rows = nullptr;
     out.dst_first = 0;
     out.count = cnt;
-    hipError_t e = launch_move_rows(out, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    if ((e = host_chunk_copy(cache, &stage, host_k, host_v, host_rows, buf, cnt, chunk, true, stream)) != hipSuccess)
-      return hip_fail(e);
-    // the chunk coming from the CPU: into the GPU slots just freed
-    if ((e = host_chunk_copy(cache, &stage, host_k, host_v, host_rows, in_first + c0, cnt, chunk, false, stream)) !=
+    if ((e = launch_move_rows(out, stream)) != hipSuccess) break;
+    if (two && (e = hipEventRecord(ev[1], stream)) != hipSuccess) break;
+    if (two && c0 > 0 && (e = hipStreamWaitEvent(stream, ev[2], 0)) != hipSuccess) break;
+    if ((e = host_chunk_copy(cache, &st_out, host_k, host_v, host_rows, buf, cnt, chunk, true, stream)) != hipSuccess)
+      break;
+    // the chunk coming from the CPU: into the GPU slots freed once they are gathered
+    if ((e = host_chunk_copy(cache, &st_in, host_k, host_v, host_rows, in_first + c0, cnt, chunk, false, sin)) !=
         hipSuccess)
-      return hip_fail(e);
+      break;
+    if (two && (e = hipEventRecord(ev[2], sin)) != hipSuccess) break;
+    if (two && (e = hipStreamWaitEvent(sin, ev[1], 0)) != hipSuccess) break;
     in.src_rows = nullptr;
     in.src_first = 0;
     in.dst_rows = slots + c0;
     in.count = cnt;
-    if ((e = launch_move_rows(in, stream)) != hipSuccess) return hip_fail(e);
+    if ((e = launch_move_rows(in, sin)) != hipSuccess) break;
     buf = in_first + c0;   // the CPU rows this chunk emptied are the next buffer
   }
-  return KV_OK;
+  // the call completes on `stream`
+  if (e == hipSuccess && two && (e = hipEventRecord(ev[2], sin)) == hipSuccess)
+    e = hipStreamWaitEvent(stream, ev[2], 0);
+  cleanup();
+  return e == hipSuccess ? KV_OK : hip_fail(e);
 }
 
 int32_t kv_compact_tail_inplace(const kv_cache_desc* cache, const int32_t* keep_tokens,

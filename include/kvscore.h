@@ -317,6 +317,9 @@ int32_t kv_load_rows(const kv_cache_desc *dst, const int32_t *slots, int64_t cou
                      int64_t chunk, const kv_meta_desc *meta /* host array */, int32_t n_meta,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Host-only.  Workspace bytes kv_swap_chunked needs: two staging areas of `chunk` rows. */
+int32_t kv_swap_workspace_size(const kv_cache_desc *cache, int64_t chunk, size_t *bytes /* host */);
+
 /*
  * Penelope's swap when both tiers are full ("Rethinking KV Cache Eviction for Agentic LLM
  * Serving", Part three): the segment in GPU slots slots[0:count) (device int32, distinct)
@@ -329,14 +332,19 @@ int32_t kv_load_rows(const kv_cache_desc *dst, const int32_t *slots, int64_t cou
  * the buffer for the next chunk.  out_rows (host, nullable, count entries) receives the
  * pool row of every outgoing row, and *next_buf_first (host, nullable) the first row of
  * the incoming segment's last chunk, which is free afterwards.  Only K and V move;
- * workspace as kv_offload_workspace_size(cache, chunk).  All copies and kernels run in
- * stream order on `stream`.
+ * workspace as kv_swap_workspace_size(cache, chunk).
+ * The outgoing side (gather, device-to-host) runs on `stream` and the incoming side
+ * (host-to-device, scatter) on `in_stream`, so the two directions of the host link can
+ * overlap; the library orders them with events it creates and releases itself, waits on
+ * `stream` before starting, and makes `stream` wait for the whole swap, so the call
+ * behaves as one operation on `stream`.  in_stream == stream runs everything in order on
+ * one stream.  The streams must have default priority.
  */
 int32_t kv_swap_chunked(const kv_cache_desc *cache, const int32_t *slots, int64_t count,
                         void *host_k, void *host_v, int64_t host_rows, int64_t in_first,
                         int64_t buf_first, int64_t chunk, int64_t *out_rows /* host */,
                         int64_t *next_buf_first /* host */, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream);
+                        size_t workspace_bytes, hipStream_t stream, hipStream_t in_stream);
 
 /*
  * Segment eviction from the front of the private history ("Rethinking KV Cache

@@ -279,14 +279,18 @@ def test_load_and_swap_validation():
     assert load(count=0) == kv.KV_OK                   # nothing to move: no device call
     out = (ctypes.c_int64 * 10)()
     nxt = ctypes.c_int64()
+    swap_ws = ctypes.c_size_t()
+    assert L.kv_swap_workspace_size(ctypes.byref(c), 64, ctypes.byref(swap_ws)) == kv.KV_OK
+    assert swap_ws.value == 2 * big                    # one staging area per direction
     swap = lambda **kw: L.kv_swap_chunked(  # noqa: E731
         ctypes.byref(c), FAKE, kw.get("count", 10), FAKE * 3, FAKE * 4, kw.get("rows", 100),
         kw.get("in_first", 0), kw.get("buf", 50), kw.get("chunk", 64), out, ctypes.byref(nxt), FAKE * 5,
-        kw.get("wb", big), None)
+        kw.get("wb", swap_ws.value), None, None)
     assert swap(buf=5) == kv.KV_EINVAL                 # buffer overlaps the incoming rows
     assert swap(in_first=95) == kv.KV_EINVAL
     assert swap(buf=95) == kv.KV_EINVAL                # buffer past the pool
     assert swap(wb=16) == kv.KV_EWORKSPACE
+    assert swap(wb=big) == kv.KV_EWORKSPACE           # a single staging area is too small
 
 
 @pytest.mark.parametrize("count,chunk,in_first,buf", [(10, 4, 0, 20), (9, 3, 30, 0), (5, 64, 7, 100),
@@ -298,11 +302,11 @@ def test_swap_row_bookkeeping_matches_oracle(count, chunk, in_first, buf):
     c = _cache(n_tokens=max(count, 100))
     rows = max(in_first + count, buf + min(chunk, count)) + 5
     ws = ctypes.c_size_t()
-    assert L.kv_offload_workspace_size(ctypes.byref(c), chunk, ctypes.byref(ws)) == kv.KV_OK
+    assert L.kv_swap_workspace_size(ctypes.byref(c), chunk, ctypes.byref(ws)) == kv.KV_OK
     out = (ctypes.c_int64 * count)()
     nxt = ctypes.c_int64(-1)
     L.kv_swap_chunked(ctypes.byref(c), FAKE, count, FAKE * 3, FAKE * 4, rows, in_first, buf, chunk, out,
-                      ctypes.byref(nxt), FAKE * 5, ws.value, None)
+                      ctypes.byref(nxt), FAKE * 5, ws.value, None, None)
     gpu = np.zeros((1, count, 1, 1))
     pool = np.zeros((1, rows, 1, 1))
     _, _, want, want_next = O.chunked_swap(gpu, pool, np.arange(count), in_first, buf, chunk)

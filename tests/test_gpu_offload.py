@@ -130,16 +130,19 @@ def test_load_rows_subrange_and_skipped_slots():
     assert (_logical(v, bt, n)[:, slots[ok]] == -pool[:, 150:270][:, ok]).all()
 
 
+@pytest.mark.parametrize("two_streams", [False, True])
 @pytest.mark.parametrize("count,chunk,in_first,buf_first,shuffle", [
     (700, 256, 0, 900, True),        # ragged last chunk
     (1024, 1024, 50, 1100, True),    # one chunk
     (2000, 1024, 2000, 0, False),    # buffer before the incoming rows
     (33, 8, 40, 0, True),
+    (3000, 128, 100, 3200, True),    # 24 chunks: the two directions overlap many times
 ])
-def test_swap_chunked_parity(count, chunk, in_first, buf_first, shuffle):
+def test_swap_chunked_parity(count, chunk, in_first, buf_first, shuffle, two_streams):
     """Penelope's both-tiers-full swap through the CPU buffer against the oracle: GPU slots,
-    every pool row, where each outgoing row landed and the next buffer."""
-    nl, hkv, n = 3, 2, 2500
+    every pool row, where each outgoing row landed and the next buffer; on one stream, and
+    with the incoming side on a second stream."""
+    nl, hkv, n = 3, 2, 4000
     w = synth.workload("qwen2.5-1.5b-n2048", n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n)
     k, v, bt = synth.kv_cache(w, seed=count, device=DEV, paged_shuffle=shuffle, extra_pages=2)
     k0, v0 = _logical(k, bt, n), _logical(v, bt, n)
@@ -150,9 +153,12 @@ def test_swap_chunked_parity(count, chunk, in_first, buf_first, shuffle):
     hk = torch.from_numpy(pk).to(torch.bfloat16).pin_memory()
     hv = torch.from_numpy(pv).to(torch.bfloat16).pin_memory()
     slots = rng.choice(n, count, replace=False)
-    out_rows, nxt, _ = kv.kv_swap_chunked(kv.PagedCache(k, v, n, bt), torch.from_numpy(slots.astype(np.int32)).to(DEV),
-                                          hk, hv, in_first, buf_first, chunk=chunk)
+    in_stream = torch.cuda.Stream() if two_streams else None
+    slots_d = torch.from_numpy(slots.astype(np.int32)).to(DEV)
     torch.cuda.synchronize()
+    out_rows, nxt, _ = kv.kv_swap_chunked(kv.PagedCache(k, v, n, bt), slots_d, hk, hv, in_first, buf_first,
+                                          chunk=chunk, in_stream=in_stream)
+    torch.cuda.current_stream().synchronize()         # the call completes on the current stream
     gk, pk2, want_rows, want_next = O.chunked_swap(k0, pk, slots, in_first, buf_first, chunk)
     gv, pv2, _, _ = O.chunked_swap(v0, pv, slots, in_first, buf_first, chunk)
     assert out_rows == want_rows.tolist() and nxt == want_next
