@@ -397,10 +397,10 @@ def extras(steps=5, warmup=2, oracle=True):
     ewma, clock = synth.memdecay_state(w5, seed=0)
     b_r, lam = synth.region_params(0)
     region = synth.regions(w5, seed=0)
-    sid, nxt = synth.spans(w5, seed=0)
+    sid, sbonus = synth.spans(w5, seed=0)
     n_items = -(-N5 // 16)
     st5 = dict(region=region.to(dev), base_prio=b_r.to(dev), decay_rate=lam.to(dev), ewma=ewma.to(dev),
-               clock=clock.to(dev), span_id=sid.to(dev), span_next_use=nxt.to(dev), bonus_floor=50000.0,
+               clock=clock.to(dev), span_id=sid.to(dev), span_bonus=sbonus.to(dev),
                n_sink=w5.n_sink, n_recent=w5.n_recent, pinned_regions=1,
                item_score=torch.zeros(n_items, device=dev),
                item_pinned=torch.zeros(n_items, dtype=torch.uint8, device=dev))
@@ -590,8 +590,8 @@ def oracle_baseline(name, layers=None, repeats=1):
             else:
                 kw = dict(accum=np.zeros(N))
             if w.n_spans:
-                sid, nxt = synth.spans(w, seed=0)
-                kw.update(span_id=sid.numpy(), span_next_use=nxt.numpy())
+                sid, sbonus = synth.spans(w, seed=0)
+                kw.update(span_id=sid.numpy(), span_bonus=sbonus.numpy())
             t0 = time.perf_counter()
             out = O.score_step(q, kl, policy=w.policy, n_sink=w.n_sink, n_recent=w.n_recent,
                                item_tokens=w.item_tokens, **kw)
@@ -628,12 +628,12 @@ def cpu_baseline(w, layers):
     ws = synth.workload("qwen3-8b-n100k", n_layers=layers)
     k, v, _ = synth.kv_cache(ws, seed=0)
     q = synth.window_queries(ws, seed=0)
-    span_id, next_use = synth.spans(ws, seed=0)
+    span_id, span_bonus = synth.spans(ws, seed=0)
     kl = k.float().double().numpy().reshape(layers, -1, ws.n_kv_heads, ws.head_dim)[:, : ws.n_tokens]
     vl = v.float().double().numpy().reshape(layers, -1, ws.n_kv_heads, ws.head_dim)[:, : ws.n_tokens]
     t0 = time.perf_counter()
     out = O.score_step(q.float().double().numpy(), kl, policy="h2o", accum=np.zeros(ws.n_tokens),
-                       span_id=span_id.numpy(), span_next_use=next_use.numpy(), n_sink=ws.n_sink,
+                       span_id=span_id.numpy(), span_bonus=span_bonus.numpy(), n_sink=ws.n_sink,
                        n_recent=ws.n_recent)
     t1 = time.perf_counter()
     kept, _ = O.select_items(out["item_score"], out["item_pinned"], ws.budget_items)
@@ -719,8 +719,8 @@ def main():
     print(f"[bench] generating {w.name}: {N} tokens x {w.kv_bytes_per_token} B", file=sys.stderr, flush=True)
     k, v, _ = synth.kv_cache(w, seed=0, device=dev)
     q = synth.window_queries(w, seed=0, device=dev)
-    span_id, next_use = synth.spans(w, seed=0)
-    span_id, next_use = span_id.to(dev), next_use.to(dev)
+    span_id, span_bonus = synth.spans(w, seed=0)
+    span_id, span_bonus = span_id.to(dev), span_bonus.to(dev)
     accum = torch.zeros(N, device=dev)
     item_score = torch.zeros(N, device=dev)
     item_pinned = torch.zeros(N, dtype=torch.uint8, device=dev)
@@ -736,7 +736,7 @@ def main():
     src = kv.PagedCache(k, v, N)
     dst = kv.PagedCache(dst_k, dst_v, B)
     score_kw = dict(policy="h2o", window=W, item_tokens=1, accum=accum, span_id=span_id,
-                    span_next_use=next_use, bonus_floor=50000.0, n_sink=w.n_sink, n_recent=w.n_recent,
+                    span_bonus=span_bonus, n_sink=w.n_sink, n_recent=w.n_recent,
                     item_score=item_score, item_pinned=item_pinned)
     ws_score = torch.empty(kv.kv_score_workspace_size(src, q, **score_kw), dtype=torch.uint8, device=dev)
     ws_sel = torch.empty(kv.kv_select_workspace_size(N), dtype=torch.uint8, device=dev)

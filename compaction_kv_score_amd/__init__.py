@@ -44,7 +44,7 @@ KV_ROPE_YARN_RATIO = 5
 KV_ROPE_YARN_NO_TRUNCATE = 1
 KV_REF_NONE = -(2 ** 31)
 KV_MAX_META = 8
-KV_ABI_VERSION = 3  # layout of the structs below
+KV_ABI_VERSION = 4  # layout of the structs below
 
 
 class KvError(RuntimeError):
@@ -76,8 +76,8 @@ class KvScoreParams(ctypes.Structure):
                 ("rho", ctypes.c_float), ("alpha", ctypes.c_float), ("tau", ctypes.c_float),
                 ("ewma", ctypes.c_void_p), ("clock", ctypes.c_void_p),
                 ("accum", ctypes.c_void_p), ("span_id", ctypes.c_void_p),
-                ("span_next_use", ctypes.c_void_p), ("n_spans", ctypes.c_int32),
-                ("bonus_floor", ctypes.c_float), ("pinned_regions", ctypes.c_uint32),
+                ("span_bonus", ctypes.c_void_p), ("n_spans", ctypes.c_int32),
+                ("pinned_regions", ctypes.c_uint32),
                 ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
                 ("token_pinned", ctypes.c_void_p), ("mass", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p), ("token_score", ctypes.c_void_p),
@@ -236,19 +236,21 @@ def _meta_array(meta):
 
 def _score_params(q, *, policy, window, item_tokens, scale=0.0, dt_steps=1, lse_in=None,
                   region=None, base_prio=None, decay_rate=None, rho=0.9, alpha=1.0, tau=0.01,
-                  ewma=None, clock=None, accum=None, span_id=None, span_next_use=None,
-                  bonus_floor=50000.0, pinned_regions=0, n_sink=0, n_recent=0,
+                  ewma=None, clock=None, accum=None, span_id=None, span_bonus=None,
+                  pinned_regions=0, n_sink=0, n_recent=0,
                   token_pinned=None, mass=None, lse=None, token_score=None, item_score=None,
                   item_pinned=None, stage_events=None, aggregate="sum", status=None):
     pol = {"memdecay": KV_POLICY_MEMDECAY, "h2o": KV_POLICY_H2O}.get(policy, policy)
     agg = {"sum": KV_AGG_SUM, "max_group": KV_AGG_MAX_GROUP}.get(aggregate, aggregate)
     n_regions = int(base_prio.numel()) if base_prio is not None else 0
-    n_spans = int(span_next_use.numel()) if span_next_use is not None else 0
+    if span_bonus is not None and span_bonus.dtype != torch.float32:
+        raise TypeError("span_bonus must be float32")
+    n_spans = int(span_bonus.numel()) if span_bonus is not None else 0
     return KvScoreParams(
         _ptr(q), int(q.shape[2]), int(window), float(scale), int(pol), int(item_tokens),
         int(dt_steps), _ptr(lse_in), _ptr(region), _ptr(base_prio), _ptr(decay_rate), n_regions,
         float(rho), float(alpha), float(tau), _ptr(ewma), _ptr(clock), _ptr(accum),
-        _ptr(span_id), _ptr(span_next_use), n_spans, float(bonus_floor), int(pinned_regions),
+        _ptr(span_id), _ptr(span_bonus), n_spans, int(pinned_regions),
         int(n_sink), int(n_recent), _ptr(token_pinned), _ptr(mass), _ptr(lse),
         _ptr(token_score), _ptr(item_score), _ptr(item_pinned), stage_events, int(agg),
         _ptr(status))

@@ -229,7 +229,7 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
     return KV_EINVAL;
   }
   if (p->region && (p->n_regions <= 0 || p->n_regions > 32)) return KV_EINVAL;
-  if (p->span_id && (!p->span_next_use || p->n_spans <= 0)) return KV_EINVAL;
+  if (p->span_id && (!p->span_bonus || p->n_spans <= 0)) return KV_EINVAL;
   if (p->n_sink < 0 || p->n_recent < 0 || p->dt_steps < 0) return KV_EINVAL;
   if (!ws || ws_bytes < L.total) return KV_EWORKSPACE;
   if ((rc = check_device())) return rc;
@@ -314,9 +314,8 @@ int32_t kv_score(const kv_cache_desc* c, const kv_score_params* p, void* ws, siz
   ea.clock = p->clock;
   ea.accum = p->accum;
   ea.span_id = p->span_id;
-  ea.span_next_use = p->span_next_use;
+  ea.span_bonus = p->span_bonus;
   ea.n_spans = p->n_spans;
-  ea.bonus_floor = p->bonus_floor;
   ea.pinned_regions = p->pinned_regions;
   ea.n_sink = p->n_sink;
   ea.n_recent = p->n_recent;

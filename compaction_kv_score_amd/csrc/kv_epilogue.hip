@@ -68,10 +68,7 @@ __global__ __launch_bounds__(kEpiThreads * kEpiSplit) void epilogue_kernel(Epilo
     float bonus = 0.f;
     if (a.span_id) {
       const int sid = a.span_id[i];
-      if (sid >= 0 && sid < a.n_spans) {
-        const int d = a.span_next_use[sid];
-        if (d >= 1) bonus = a.bonus_floor * (1.0f + 1.0f / (float)d);
-      }
+      if (sid >= 0 && sid < a.n_spans) bonus = a.span_bonus[sid];
     }
     // a label outside the region table names no region (reported through the status)
     int r = 0;

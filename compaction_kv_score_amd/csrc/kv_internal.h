@@ -79,9 +79,8 @@ struct EpilogueArgs {
   int32_t* clock;
   float* accum;
   const int32_t* span_id;
-  const int32_t* span_next_use;
+  const float* span_bonus;
   int n_spans;
-  float bonus_floor;
   uint32_t pinned_regions;
   int64_t n_sink, n_recent;
   const uint8_t* token_pinned;

@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define KV_ABI_VERSION 3
+#define KV_ABI_VERSION 4
 
 /* return codes */
 #define KV_OK 0
@@ -116,10 +116,11 @@ typedef struct kv_meta_desc {
  *       ewma <- rho*ewma + (1-rho)*Abar;  clock <- (Abar > tau) ? 0 : clock + dt_steps;
  *       s = base_prio[r]*exp(-decay_rate[r]*clock) + alpha*ewma + bonus
  *   H2O (PACE Sec. 2):  accum <- accum + mass;  s = accum + bonus
- * Foresight bonus (PACE Sec. 3.1 and 7): bonus = bonus_floor*(1 + 1/d) for the token's
- * span when d = span_next_use[span_id[i]] >= 1, else 0 (d = steps until the soonest
- * future step that reads the span).
- * A span id outside [0, n_spans) names no span (no bonus).
+ * Foresight bonus (PACE Sec. 3.1 and 7): the planner turns its forward-reference table
+ * into one bonus per span, soonest-needed spans highest and every needed span at or above
+ * a constant floor; the library takes those values as input and adds
+ * bonus = span_bonus[span_id[i]] to the token's score.  A span id outside [0, n_spans)
+ * names no span (no bonus).
  * Pinned tokens (MemDecay pinned regions; PACE Table 1 sinks and recent window): a token
  * is pinned if its region bit is set in pinned_regions, or i < n_sink, or
  * i >= N - n_recent, or token_pinned[i] != 0.
@@ -151,9 +152,8 @@ typedef struct kv_score_params {
   float *accum;               /* [N] in/out (H2O) */
   /* foresight */
   const int32_t *span_id;     /* [N] span of each token, -1 = none (NULL: no bonus) */
-  const int32_t *span_next_use; /* [n_spans] */
+  const float *span_bonus;    /* [n_spans] bonus of each span, finite */
   int32_t n_spans;
-  float bonus_floor;
   /* pinning */
   uint32_t pinned_regions;    /* bit r pins region r */
   int32_t n_sink;

@@ -13,7 +13,7 @@ Pages and the parts used (cited by title and section):
     Proposition 1, choosing the limit, non-compounding re-rotation through a reference
     store), Sec. 3.4 (evicted rows offloaded at every compaction), Sec. 3.5 (split-half
     RoPE, static frequency scaling), Table 1 (budget 2,048 incl. 4 sinks and 128
-    recent), Sec. 5.7 / 7 (foresight floor of 50K).
+    recent), Sec. 7 (the bonus is added to the eviction score).
   * "MemDecay: Region-Aware KV Cache Eviction for Efficient LLM Agent Inference" --
     Method (region labels, EWMA, decay clock, composite score, pinned regions,
     page-mean eviction, half-life).
@@ -27,9 +27,9 @@ Pages and the parts used (cited by title and section):
     GQA group), Sec. 7.2 and Algorithm 4 (in-place tail compaction).
 
 Readings of points the pages leave open are listed next to each function.
-Parity status: every function here is pinned by a ``-m "not gpu"`` test except the
-exact numerical values of ``foresight_bonus`` (see its docstring: parity unpinned,
-only its ordering properties are pinned).
+Parity status: every function here is pinned by a ``-m "not gpu"`` test.  The foresight
+bonus values themselves come from PACE's planner, which sits above this path: the
+oracle takes them as an input (one value per span) exactly as the library does.
 """
 from __future__ import annotations
 
@@ -201,31 +201,16 @@ def attention_score_max_group(q, k, scale=None, lse=None):
 
 
 # --------------------------------------------------------------------------------------
-# O3: foresight bonus  (PACE Sec. 3.1, Sec. 5.7 and Sec. 7)
+# O3: foresight bonus of each token  (PACE Sec. 3.1 and Sec. 7)
 # --------------------------------------------------------------------------------------
 
-def foresight_bonus(next_use, floor=50000.0):
-    """Per-span bonus from the forward-reference table.
-
-    PACE turns the planner's dependency graph into a per-span bonus that dominates
-    attention scores, keeps soonest-needed context first, is added to H2O's score, and
-    has a constant floor (50K).  The formula itself is not printed.  Reading: with d >= 1
-    the number of steps until the soonest future step that reads the span,
-        bonus = floor * (1 + 1/d),   and 0 when no future step reads it (d <= 0).
-    PARITY UNPINNED for the exact values; pinned only for dominance over unprotected
-    scores below the floor and for soonest-first ordering.
-    """
-    d = np.asarray(next_use, dtype=np.float64)
-    out = np.zeros_like(d)
-    sel = d >= 1
-    out[sel] = floor * (1.0 + 1.0 / d[sel])
-    return out
-
-
 def token_bonus(span_id, span_bonus):
-    """Bonus of each token: the bonus of the span it belongs to.  A token outside every
-    span (id -1) gets none.  Reading: an id that names no span of the table (negative, or
-    not below the number of spans) is treated the same way, as no span."""
+    """Bonus of each token: the bonus of the span it belongs to.  PACE's planner turns its
+    forward-reference table into one bonus per span (Sec. 3.1) and the bonus is added to
+    the eviction score (Sec. 7); the per-span values are its output and arrive here as
+    ``span_bonus``.  A token outside every span (id -1) gets none.  Reading: an id that
+    names no span of the table (negative, or not below the number of spans) is treated
+    the same way, as no span."""
     sid = np.asarray(span_id, dtype=np.int64)
     sb = np.asarray(span_bonus, dtype=np.float64)
     out = np.zeros(sid.shape, dtype=np.float64)
@@ -785,7 +770,7 @@ def simulate_renumbers(session_tokens, budget, limit, headroom):
 
 def score_step(q, k, *, policy, scale=None, region=None, base_prio=None, decay_rate=None,
                rho=0.9, alpha=1.0, tau=0.01, dt_steps=1, ewma=None, clock=None,
-               accum=None, span_id=None, span_next_use=None, bonus_floor=50000.0,
+               accum=None, span_id=None, span_bonus=None,
                pinned_regions=0, n_sink=0, n_recent=0, token_pinned=None, item_tokens=1,
                aggregate="sum", lse_in=None):
     """Score one eviction step: mass -> policy epilogue -> per-item score and pin flag.
@@ -808,8 +793,8 @@ def score_step(q, k, *, policy, scale=None, region=None, base_prio=None, decay_r
         raise ValueError(aggregate)
     n = mass.shape[0]
     bonus = None
-    if span_id is not None and span_next_use is not None:
-        bonus = token_bonus(span_id, foresight_bonus(span_next_use, bonus_floor))
+    if span_id is not None and span_bonus is not None:
+        bonus = token_bonus(span_id, span_bonus)
     out = {"mass": mass, "lse": lse}
     if policy == "memdecay":
         abar = mass / terms

@@ -2,7 +2,9 @@
 
 This module only draws random numbers and lays them out in the shapes of the pages'
 workloads.  It holds none of the method's arithmetic (no attention, no scores, no
-selection, no rotation), so both the HIP path and the CPU oracle can consume it.
+selection, no rotation), so both the HIP path and the CPU oracle can consume it.  The
+per-span foresight bonus it draws stands in for the output of PACE's planner, which sits
+above the path: both sides take it as input.
 
 Workload shapes (from the pages, see the README of the tests for the recipe):
   * KV footprint of Qwen3-8B: 36 layers x 8 KV heads x 128 dims x (K,V) x bf16 =
@@ -210,11 +212,16 @@ def h2o_state(w: Workload, seed=0):
     return (torch.rand(w.n_tokens, generator=g) * 4.0).float()
 
 
-def spans(w: Workload, seed=0, n_steps=16, p_needed=0.01):
-    """Forward-reference table: ``n_spans`` spans partition the tokens with
-    Dirichlet(1) lengths; each span is read by a future step with probability
-    ``p_needed``, at a distance d ~ U{1..n_steps}.  Returns (span_id[N] int32,
-    next_use[S] int32, 0 = not read)."""
+def spans(w: Workload, seed=0, n_steps=16, p_needed=0.01, floor=50000.0):
+    """Spans and the planner's per-span foresight bonus (PACE Sec. 3.1 and 7).
+
+    ``n_spans`` spans partition the tokens with Dirichlet(1) lengths; each span is read
+    by a future step with probability ``p_needed``, at a distance d ~ U{1..n_steps}.
+    The planner that turns this table into bonuses sits above the scoring path, and the
+    pages fix only the bonus's properties: it outranks attention scores, the soonest
+    needed span ranks first, and it has a constant floor of 50K.  This stand-in for the
+    planner's output gives a span read d steps ahead floor * (1 + 1/d) and a span that
+    no future step reads 0.  Returns (span_id[N] int32, span_bonus[S] float32)."""
     g = _gen(seed, _S_SPAN, "cpu")
     s = w.n_spans
     n = w.n_tokens
@@ -229,8 +236,9 @@ def spans(w: Workload, seed=0, n_steps=16, p_needed=0.01):
         start = max(start, end)
     needed = torch.rand(s, generator=g) < p_needed
     dist = torch.randint(1, n_steps + 1, (s,), generator=g)
-    next_use = torch.where(needed, dist, torch.zeros_like(dist)).to(torch.int32)
-    return span_id, next_use
+    bonus = floor * (1.0 + 1.0 / dist.to(torch.float64))
+    span_bonus = torch.where(needed, bonus, torch.zeros_like(bonus)).to(torch.float32)
+    return span_id, span_bonus
 
 
 def scores(n, seed=0, alphabet=None, nan_frac=0.0, neg_zero=False):

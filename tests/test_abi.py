@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     lib = kv.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert kv.kv_abi_version() == kv.KV_ABI_VERSION == 3
+    assert kv.kv_abi_version() == kv.KV_ABI_VERSION == 4
 
 
 def test_strerror_texts():
@@ -146,6 +146,11 @@ def test_score_rejects_missing_state_and_small_workspace():
     assert L.kv_score(ctypes.byref(c), ctypes.byref(p), FAKE, 16, None) == kv.KV_EWORKSPACE
     p = _score_params(item_tokens=8)
     assert L.kv_score(ctypes.byref(c), ctypes.byref(p), FAKE, 1 << 30, None) == kv.KV_EINVAL
+    # span ids need the per-span bonus table and its length
+    for over in (dict(span_id=FAKE), dict(span_id=FAKE, span_bonus=FAKE),
+                 dict(span_id=FAKE, n_spans=4)):
+        p = _score_params(**over)
+        assert L.kv_score(ctypes.byref(c), ctypes.byref(p), FAKE, 1 << 30, None) == kv.KV_EINVAL
 
 
 def test_select_validation():

@@ -255,13 +255,13 @@ def _memdecay_state(w, seed):
 
 
 def _compare_memdecay(w, q, k_logical, st0, dev_state, got, rho, alpha, tau, dt_steps, item_tokens,
-                      pinned_regions, n_sink=0, n_recent=0, span_id=None, next_use=None, floor=50000.0):
+                      pinned_regions, n_sink=0, n_recent=0, span_id=None, span_bonus=None):
     ref = O.score_step(np64(q), k_logical, policy="memdecay", region=st0["region"].numpy(),
                        base_prio=np64(st0["base_prio"]), decay_rate=np64(st0["decay_rate"]),
                        rho=f32(rho), alpha=f32(alpha), tau=f32(tau), dt_steps=dt_steps,
                        ewma=np64(st0["ewma"]), clock=st0["clock"].numpy(),
                        span_id=None if span_id is None else span_id.numpy(),
-                       span_next_use=None if next_use is None else next_use.numpy(), bonus_floor=floor,
+                       span_bonus=None if span_bonus is None else span_bonus.numpy(),
                        pinned_regions=pinned_regions, n_sink=n_sink, n_recent=n_recent,
                        item_tokens=item_tokens)
     assert_rel(np64(got["mass"]), ref["mass"], what="mass")
@@ -287,16 +287,19 @@ def _compare_memdecay(w, q, k_logical, st0, dev_state, got, rho, alpha, tau, dt_
     ("qwen2.5-1.5b-1layer-n512", dict(n_tokens=9000, window=16, n_q_heads=64, n_kv_heads=2, n_layers=1), False),
 ])
 def test_score_memdecay_parity(name, over, shuffle):
-    w = synth.workload(name, **over)
+    w = synth.workload(name, **{**over, "n_spans": 24})
     k, v, bt, q = _make_score_inputs(w, seed=11 + w.n_tokens, shuffle=shuffle)
     st0 = _memdecay_state(w, seed=w.n_tokens)
+    span_id, span_bonus = synth.spans(w, seed=w.n_tokens, p_needed=0.25)
     dev_state = {key: t.clone() for key, t in st0.items()}
     dev = {key: t.to(DEV) for key, t in dev_state.items()}
     got = _run_score(w, k, v, bt, q, policy="memdecay", item_tokens=w.item_tokens, state=dev,
-                     rho=w.rho, alpha=w.alpha, tau=w.tau, dt_steps=3, pinned_regions=1)
+                     rho=w.rho, alpha=w.alpha, tau=w.tau, dt_steps=3, pinned_regions=1,
+                     span_id=span_id.to(DEV), span_bonus=span_bonus.to(DEV))
     dev_state = {key: t.cpu() for key, t in dev.items()}
     kl = _paged_to_logical(k, bt, 16, w.n_tokens)
-    _compare_memdecay(w, q, kl, st0, dev_state, got, w.rho, w.alpha, w.tau, 3, w.item_tokens, 1)
+    _compare_memdecay(w, q, kl, st0, dev_state, got, w.rho, w.alpha, w.tau, 3, w.item_tokens, 1,
+                      span_id=span_id, span_bonus=span_bonus)
 
 
 def test_score_memdecay_sixteen_steps():
@@ -332,7 +335,7 @@ def test_score_memdecay_sixteen_steps():
 def test_score_h2o_foresight_parity(over, shuffle):
     w = synth.workload("qwen3-8b-n100k", **over)
     k, v, bt, q = _make_score_inputs(w, seed=w.n_tokens, shuffle=shuffle)
-    span_id, next_use = synth.spans(w, seed=3, p_needed=0.2)
+    span_id, span_bonus = synth.spans(w, seed=3, p_needed=0.2)
     # tokens outside every span (-1) and ids that name no span of the table get no bonus
     g = torch.Generator().manual_seed(w.n_tokens)
     r = torch.rand(w.n_tokens, generator=g)
@@ -342,17 +345,17 @@ def test_score_h2o_foresight_parity(over, shuffle):
     accum = synth.h2o_state(w, seed=3)
     dev_acc = accum.to(DEV)
     got = _run_score(w, k, v, bt, q, policy="h2o", item_tokens=1, state=dict(accum=dev_acc),
-                     span_id=span_id.to(DEV), span_next_use=next_use.to(DEV), bonus_floor=50000.0,
-                     n_sink=w.n_sink, n_recent=w.n_recent)
+                     span_id=span_id.to(DEV), span_bonus=span_bonus.to(DEV), n_sink=w.n_sink,
+                     n_recent=w.n_recent)
     kl = _paged_to_logical(k, bt, 16, w.n_tokens)
     ref = O.score_step(np64(q), kl, policy="h2o", accum=np64(accum), span_id=span_id.numpy(),
-                       span_next_use=next_use.numpy(), bonus_floor=50000.0, n_sink=w.n_sink,
+                       span_bonus=span_bonus.numpy(), n_sink=w.n_sink,
                        n_recent=w.n_recent)
     assert_rel(np64(got["mass"]), ref["mass"], what="mass")
     assert_rel(np64(dev_acc.cpu()), ref["accum"], what="accum")
     assert_rel(np64(got["item_score"]), ref["item_score"], what="score")
     assert (got["item_pinned"].numpy().astype(bool) == ref["item_pinned"]).all()
-    assert (next_use > 0).any() and (span_id < 0).any() and (span_id >= w.n_spans).any()
+    assert (span_bonus > 0).any() and (span_id < 0).any() and (span_id >= w.n_spans).any()
 
 
 def test_score_bad_region_labels_are_reported():
@@ -550,10 +553,10 @@ def qwen3_100k():
 def test_full_size_qwen3_100k_score_properties(qwen3_100k):
     """Launch configuration of the benchmark: 36 layers, 32/8 heads, N = 100,000."""
     w, k, v, q = qwen3_100k
-    span_id, next_use = synth.spans(w, seed=0)
+    span_id, span_bonus = synth.spans(w, seed=0)
     acc = torch.zeros(w.n_tokens, device=DEV)
     got = _run_score(w, k, v, None, q, policy="h2o", item_tokens=1, state=dict(accum=acc),
-                     span_id=span_id.to(DEV), span_next_use=next_use.to(DEV), n_sink=4, n_recent=128)
+                     span_id=span_id.to(DEV), span_bonus=span_bonus.to(DEV), n_sink=4, n_recent=128)
     mass = np64(got["mass"])
     total = w.n_layers * w.n_q_heads * w.window
     assert abs(mass.sum() / total - 1) < 1e-5          # each query's softmax row sums to 1
@@ -636,7 +639,7 @@ def test_full_size_qwen3_100k_bench_step(qwen3_100k):
     oracle's compaction of the kept rows."""
     w, k, v, q = qwen3_100k
     N, B = w.n_tokens, w.budget_tokens
-    span_id, next_use = synth.spans(w, seed=0)
+    span_id, span_bonus = synth.spans(w, seed=0)
     accum = torch.zeros(N, device=DEV)
     mass = torch.zeros(N, device=DEV)
     tok = torch.zeros(N, device=DEV)
@@ -644,7 +647,7 @@ def test_full_size_qwen3_100k_bench_step(qwen3_100k):
     item_pinned = torch.zeros(N, dtype=torch.uint8, device=DEV)
     src = kv.PagedCache(k, v, N)
     kv.kv_score(src, q, policy="h2o", window=w.window, item_tokens=1, accum=accum, span_id=span_id.to(DEV),
-                span_next_use=next_use.to(DEV), bonus_floor=50000.0, n_sink=w.n_sink, n_recent=w.n_recent,
+                span_bonus=span_bonus.to(DEV), n_sink=w.n_sink, n_recent=w.n_recent,
                 mass=mass, token_score=tok, item_score=item_score, item_pinned=item_pinned)
     keep = torch.full((B,), -1, dtype=torch.int32, device=DEV)
     n_keep = torch.zeros(1, dtype=torch.int64, device=DEV)
@@ -662,7 +665,7 @@ def test_full_size_qwen3_100k_bench_step(qwen3_100k):
     torch.cuda.synchronize()
     assert int(status.item()) == 0 and int(n_keep.item()) == B
     # scores: H2O from a zero accumulator is the mass, plus the span bonus
-    bonus = O.token_bonus(span_id.numpy(), O.foresight_bonus(next_use.numpy(), 50000.0))
+    bonus = O.token_bonus(span_id.numpy(), span_bonus.numpy())
     assert_rel(np64(tok), np64(mass) + bonus, what="score = mass + bonus")
     assert torch.equal(tok, item_score) and torch.equal(accum, mass)
     pin = O.pinned_tokens(N, n_sink=w.n_sink, n_recent=w.n_recent)
@@ -748,7 +751,7 @@ def test_full_size_qwen3_1m_step_properties():
     q = synth.window_queries(w, seed=0, device=DEV)
     ewma, clock = synth.memdecay_state(w, seed=0)
     b_r, lam = synth.region_params(0)
-    sid, nxt = synth.spans(w, seed=0)
+    sid, sbonus = synth.spans(w, seed=0)
     n_items = -(-N // 16)
     item_score = torch.zeros(n_items, device=DEV)
     item_pinned = torch.zeros(n_items, dtype=torch.uint8, device=DEV)
@@ -758,7 +761,7 @@ def test_full_size_qwen3_1m_step_properties():
     kv.kv_score(src, q, policy="memdecay", window=w.window, item_tokens=16, rho=w.rho, alpha=w.alpha,
                 tau=w.tau, dt_steps=1, region=synth.regions(w, seed=0).to(DEV), base_prio=b_r.to(DEV),
                 decay_rate=lam.to(DEV), ewma=ewma.to(DEV), clock=clock.to(DEV), span_id=sid.to(DEV),
-                span_next_use=nxt.to(DEV), bonus_floor=50000.0, n_sink=w.n_sink, n_recent=w.n_recent,
+                span_bonus=sbonus.to(DEV), n_sink=w.n_sink, n_recent=w.n_recent,
                 pinned_regions=1, mass=mass, lse=lse, item_score=item_score, item_pinned=item_pinned)
     B = w.budget_tokens
     keep = torch.zeros(B, dtype=torch.int32, device=DEV)

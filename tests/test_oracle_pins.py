@@ -301,19 +301,31 @@ def test_h2o_accumulates():
 
 
 # ---------------------------------------------------------------------------------------
-# O3 foresight (ordering properties only; exact values are parity unpinned)
+# O3 foresight: the bonus of each token, and the properties the pages fix for the
+# per-span values (drawn by the input generator, as the planner would supply them)
 # ---------------------------------------------------------------------------------------
 
-def test_foresight_dominance_and_soonest_first():
+def test_generated_span_bonus_has_the_pages_properties():
+    """PACE fixes three properties of the planner's bonus: a constant floor of 50K, the
+    soonest-needed span first, and dominance over the unprotected attention scores it
+    measured.  The generator's stand-in must have all three."""
     gd = read_golden("pace_numbers.txt")
     floor = gd["foresight_floor"]
-    bon = O.foresight_bonus(np.array([0, 1, 2, 16, 1000]), floor)
-    assert bon[0] == 0
-    assert bon[1] > bon[2] > bon[3] > bon[4] >= floor
-    # every protected token outranks every unprotected one while unprotected attention
-    # stays below the floor (the pages' maxima were 14.6K and 25.1K)
-    unprot = np.array([0.0, gd["max_unprotected_1m"], gd["max_unprotected_2m"]])
-    assert (bon[1:].min() + 0.0) > unprot.max()
+    w = synth.workload("qwen3-8b-n100k", n_tokens=50000, n_spans=400)
+    sid, bonus = synth.spans(w, seed=5, n_steps=16, p_needed=0.5, floor=floor)
+    assert bonus.dtype == torch.float32 and bonus.shape == (400,)
+    assert sid.min() == 0 and sid.max() == 399 and bool((sid[1:] >= sid[:-1]).all())
+    b = bonus.double().numpy()
+    needed = b > 0
+    assert 50 < needed.sum() < 350
+    assert b[needed].min() >= floor and b[needed].max() <= 2 * floor
+    unprot = np.array([gd["max_unprotected_1m"], gd["max_unprotected_2m"]])
+    assert b[needed].min() > unprot.max()
+    # soonest first: the distinct values, ordered, are floor*(1+1/d) for d = 1, 2, ...
+    vals = np.unique(b[needed])[::-1]
+    d = floor / (vals - floor)
+    np.testing.assert_allclose(d, np.rint(d), rtol=0, atol=1e-3)
+    assert (np.diff(np.rint(d)) > 0).all() and np.rint(d).max() <= 16
 
 
 def test_token_bonus_by_hand():
@@ -326,10 +338,16 @@ def test_token_bonus_by_hand():
     rng = np.random.default_rng(4)
     q = rng.standard_normal((1, 2, 2, 8))
     k = rng.standard_normal((1, 8, 1, 8))
-    nxt = np.array([1, 0, 4])                       # spans 0 and 2 are read again
-    out = O.score_step(q, k, policy="h2o", span_id=sid, span_next_use=nxt, bonus_floor=100.0)
-    want = O.token_bonus(sid, [200.0, 0.0, 125.0])
+    out = O.score_step(q, k, policy="h2o", span_id=sid, span_bonus=bonus)
+    want = [0.0, 10.0, 30.0, 0.0, 20.0, 0.0, 0.0, 10.0]
     np.testing.assert_allclose(out["token_score"] - out["accum"], want, rtol=0, atol=1e-9)
+    # and MemDecay adds it on top of the decay and EWMA terms
+    md = dict(region=np.zeros(8, np.uint8), base_prio=[1.0], decay_rate=[0.5],
+              ewma=np.full(8, 0.25), clock=np.arange(8))
+    out = O.score_step(q, k, policy="memdecay", span_id=sid, span_bonus=bonus, **md)
+    plain = O.score_step(q, k, policy="memdecay", **md)
+    np.testing.assert_allclose(out["token_score"] - plain["token_score"], want, rtol=0,
+                               atol=1e-9)
 
 
 def test_region_labels_outside_the_table():
