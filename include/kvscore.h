@@ -14,6 +14,8 @@
  *   - Pointers are DEVICE pointers owned by the caller unless marked "host".
  *   - The library never allocates device memory and keeps no mutable global state;
  *     scratch space is a caller-provided workspace sized by the *_workspace_size call.
+ *     The one exception is kv_select_noalloc, which works in a fixed device array of its
+ *     own for callers that cannot allocate (see there).
  *   - Work is enqueued asynchronously on the caller's stream; outputs are valid once the
  *     stream has reached that point.  Calls on different streams are independent as
  *     long as their buffers (workspaces included) do not overlap.
