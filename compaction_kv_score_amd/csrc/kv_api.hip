@@ -81,6 +81,7 @@ int32_t check_cache(const kv_cache_desc* c) {
   if (ps < 0 || ps > 10) return KV_EUNSUPPORTED;
   const int64_t slot = (int64_t)c->n_kv_heads * c->head_dim;
   if (c->page_stride < slot * c->page_size) return KV_EINVAL;
+  if (c->page_stride > 0xFFFFFFFFLL) return KV_EUNSUPPORTED;  // page offsets use 32-bit products
   if (c->n_layers > 1 && c->layer_stride < c->page_stride) return KV_EINVAL;
   if (((uintptr_t)c->k | (uintptr_t)c->v) & 15) return KV_EINVAL;
   if ((c->page_stride | c->layer_stride) & 7) return KV_EINVAL;  // keep 16-byte alignment

@@ -189,9 +189,9 @@ struct Ctx {
   __device__ __forceinline__ void fetch_pages(int t, const int32_t* __restrict__ bt,
                                               int32_t (&ph)[LPW]) const {
     if (!uniform_tile(t)) return;
-    const int64_t tile_j0 = j0 + (int64_t)t * kTile;
+    const uint32_t tile_j0 = (uint32_t)j0 + (uint32_t)t * (uint32_t)kTile;   // N < 2^31
 #pragma unroll
-    for (int m = 0; m < LPW; ++m) ph[m] = (int32_t)((tile_j0 + 4 * load_slot(m)) >> a.page_shift);
+    for (int m = 0; m < LPW; ++m) ph[m] = (int32_t)((tile_j0 + 4u * (uint32_t)load_slot(m)) >> a.page_shift);
     if (bt) {
 #pragma unroll
       for (int m = 0; m < LPW; ++m) ph[m] = bt[ph[m]];
@@ -205,15 +205,18 @@ struct Ctx {
   template <bool kScalar = false>
   __device__ __forceinline__ void issue_fast(int t, uint32_t stage, uint32_t junk,
                                              const int32_t (&ph)[LPW]) const {
-    const int64_t tile_j0 = j0 + (int64_t)t * kTile;
-    const int64_t pmask = (1LL << a.page_shift) - 1;
+    // 32-bit pieces: the page stride is below 2^32 elements and the in-page offset small
+    const uint32_t tj_lo = (uint32_t)j0 + (uint32_t)t * (uint32_t)kTile;
+    const uint32_t pmask = (1u << a.page_shift) - 1u;
+    const uint32_t pstride = (uint32_t)a.page_stride;
 #pragma unroll
     for (int m = 0; m < LPW; ++m) {
       const int i = load_slot(m);
       const uint32_t dst = kJunk && wv * LPW + m >= kLoadsPerTile ? junk : stage + i * 1024;
-      const int32_t page = kScalar ? __builtin_amdgcn_readfirstlane(ph[m]) : ph[m];
-      const uint16_t* base =
-          kbase + (int64_t)page * a.page_stride + ((tile_j0 + 4 * i) & pmask) * slot_stride;
+      const uint32_t page = (uint32_t)(kScalar ? __builtin_amdgcn_readfirstlane(ph[m]) : ph[m]);
+      const uint64_t poff = (uint64_t)page * pstride;
+      const uint32_t inpage = ((tj_lo + 4u * (uint32_t)i) & pmask) * (uint32_t)slot_stride;
+      const uint16_t* base = kbase + poff + inpage;
       dma16<kNt>(base + voff[m], dst);
     }
   }

@@ -76,7 +76,8 @@ typedef struct kv_cache_desc {
   int32_t page_size;          /* power of two, 1..1024 */
   int64_t n_tokens;           /* N: logical tokens in the row */
   int64_t layer_stride;       /* elements between layers */
-  int64_t page_stride;        /* elements between physical pages; >= page_size*Hkv*D */
+  int64_t page_stride;        /* elements between physical pages; >= page_size*Hkv*D,
+                                 below 2^32 (else KV_EUNSUPPORTED) */
   const int32_t *block_table; /* device [ceil(N/page_size)] or NULL (identity) */
 } kv_cache_desc;
 

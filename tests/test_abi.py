@@ -78,6 +78,7 @@ def test_score_workspace_size_and_validation():
         (_cache(page_size=12), p, kv.KV_EUNSUPPORTED),
         (_cache(k=None), p, kv.KV_EINVAL),
         (_cache(page_stride=100), p, kv.KV_EINVAL),
+        (_cache(page_stride=1 << 32, layer_stride=1 << 33), p, kv.KV_EUNSUPPORTED),
         (c, _score_params(n_q_heads=3), kv.KV_EINVAL),
         (c, _score_params(window=101), kv.KV_EINVAL),
         (c, _score_params(window=0), kv.KV_EINVAL),
