@@ -721,11 +721,6 @@ def chunked_swap(gpu, pool, slots, in_first, buf_first, chunk):
     return gpu, pool, np.array(out_rows, dtype=np.int64), buf
 
 
-def gather_meta(arr, keep):
-    """Per-token metadata follows its token through compaction."""
-    return np.asarray(arr)[np.asarray(keep, dtype=np.int64)]
-
-
 # --------------------------------------------------------------------------------------
 # Renumber trigger and limit rule (PACE Sec. 3.2)
 # --------------------------------------------------------------------------------------
