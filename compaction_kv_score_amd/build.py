@@ -107,5 +107,31 @@ def build_sanitized(out_dir: str, verbose: bool = False) -> str:
     return lib
 
 
+C_PIPELINE_SRC = os.path.join(ROOT, "tests", "c_pipeline.c")
+C_PIPELINE = os.path.join(ROOT, "tests", "c_pipeline")
+
+
+def build_c_pipeline(verbose: bool = False) -> str:
+    """Build the C test program that drives the library through include/kvscore.h alone
+    (plain C99 host code, gcc), next to its source; it finds libkvscore.so relative to
+    itself.  Returns its path."""
+    libdir = os.path.dirname(LIB)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = C_PIPELINE + ".tmp"
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-isystem", os.path.join(rocm, "include"), C_PIPELINE_SRC,
+           "-L", libdir, "-lkvscore", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../compaction_kv_score_amd", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(tmp, C_PIPELINE)
+    return C_PIPELINE
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_pipeline(verbose=True))
