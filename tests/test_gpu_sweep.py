@@ -1,0 +1,162 @@
+"""Seeded sweeps over shapes the fixed parity cases do not name.
+
+Every configuration is drawn from a fixed seed, so a failure names its case and replays
+exactly.  Each one is held to the bars of the parity tests: selection bit-exact against
+the oracle (keep list, count and status word), compaction with V and unrotated K
+bit-exact and rotated K within 1 bf16 ulp, attention mass and scores within 1e-5
+relative, LSE within 1e-5 absolute."""
+import numpy as np
+import pytest
+import torch
+
+import compaction_kv_score_amd as kv
+import oracle as O
+import synth
+import test_gpu_parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _select_cases(n_cases=100, seed=2024):
+    rng = np.random.default_rng(seed)
+    sizes = [1, 2, 3, 17, 63, 64, 65, 1000, 4095, 4096, 4097, 8191, 12_288, 50_000, 130_000]
+    for c in range(n_cases):
+        n_items = int(rng.choice(sizes)) + (int(rng.integers(0, 50)) if rng.random() < 0.3 else 0)
+        it = int(rng.choice([1, 1, 16, 64]))
+        n_tokens = n_items * it - (int(rng.integers(0, it)) if it > 1 else 0)
+        alphabet = None if rng.random() < 0.6 else [float(x) for x in rng.choice([-1.0, 0.0, 0.5, 1.0, 2.0], 3)]
+        nan = float(rng.choice([0.0, 0.0, 0.01]))
+        negz = bool(rng.random() < 0.3)
+        pin = float(rng.choice([0.0, 0.01, 0.3]))
+        budget = int(rng.integers(0, n_items + 4))
+        cap = None if rng.random() < 0.7 else int(rng.integers(1, max(2, budget * it + 1)))
+        yield c, n_items, it, n_tokens, alphabet, nan, negz, pin, budget, cap
+
+
+@pytest.mark.parametrize("case", list(_select_cases()), ids=lambda c: f"sel{c[0]}")
+def test_select_sweep(case):
+    c, n_items, it, n_tokens, alphabet, nan, negz, pin, budget, cap = case
+    print(f"select sweep {c}: items={n_items} it={it} tokens={n_tokens} budget={budget} cap={cap}", flush=True)
+    s = synth.scores(n_items, seed=100 + c, alphabet=alphabet, nan_frac=nan, neg_zero=negz)
+    p = synth.pinned_mask(n_items, seed=100 + c, frac=pin) if pin else None
+    P._select_case(n_items, it, n_tokens, budget, s, p, cap=cap)
+
+
+def _compact_cases(n_cases=40, seed=77):
+    rng = np.random.default_rng(seed)
+    for c in range(n_cases):
+        nl = int(rng.integers(1, 5))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        src_ps = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+        dst_ps = int(rng.choice([1, 4, 16, 128]))
+        n = int(rng.integers(1, 3000))
+        n_keep = int(rng.integers(1, n + 1))
+        base = int(rng.choice([-1, 0, int(rng.integers(1, 5000))]))
+        theta = float(rng.choice([1e4, 1e6, 5e5]))
+        yield c, nl, hkv, src_ps, dst_ps, n, n_keep, base, theta, bool(rng.random() < 0.5)
+
+
+@pytest.mark.parametrize("case", list(_compact_cases()), ids=lambda c: f"cmp{c[0]}")
+def test_compact_sweep(case):
+    c, nl, hkv, src_ps, dst_ps, n, n_keep, base, theta, shuffle = case
+    print(f"compact sweep {c}: layers={nl} kv_heads={hkv} pages {src_ps}->{dst_ps} n={n} keep={n_keep} "
+          f"base={base}", flush=True)
+    w = synth.workload("qwen2.5-1.5b-n2048", n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n,
+                       page_size=src_ps)
+    k, v, bt = synth.kv_cache(w, seed=500 + c, device=DEV, paged_shuffle=shuffle, extra_pages=2)
+    g = torch.Generator().manual_seed(600 + c)
+    keep = torch.sort(torch.randperm(n, generator=g)[:n_keep])[0].to(torch.int32)
+    old_pos = torch.arange(n, dtype=torch.int32) + torch.randint(0, 200_000, (n,), generator=g, dtype=torch.int32)
+    n_dst_pages = -(-n_keep // dst_ps) + 1
+    dk = torch.zeros((nl, n_dst_pages, dst_ps, hkv, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    dbt = torch.randperm(n_dst_pages, generator=g)[: -(-n_keep // dst_ps)].to(torch.int32).to(DEV) \
+        if shuffle else None
+    meta_src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), generator=g, dtype=torch.int32)
+    meta_dst = torch.zeros(n_keep, dtype=torch.int32, device=DEV)
+    new_pos = torch.full((n_keep,), -7, dtype=torch.int32, device=DEV)
+    kv.kv_compact_rerope(kv.PagedCache(k, v, n, bt), kv.PagedCache(dk, dv, n_keep, dbt), keep.to(DEV), None,
+                         n_keep, old_pos.to(DEV), new_pos, renumber_base=base, rope_theta=theta, limit=0,
+                         meta=[(meta_src.to(DEV), meta_dst)])
+    torch.cuda.synchronize()
+    kl = P._paged_to_logical(k, bt, src_ps, n)
+    vl = P._paged_to_logical(v, bt, src_ps, n)
+    rk, rv, rpos = O.compact_rerope(kl, vl, keep.numpy(), old_pos.numpy(), base, theta)
+    gk = P._paged_to_logical(dk, dbt, dst_ps, n_keep)
+    gv = P._paged_to_logical(dv, dbt, dst_ps, n_keep)
+    assert (new_pos.cpu().numpy() == rpos).all()
+    assert (gv == rv).all()
+    still = rpos == old_pos.numpy()[keep.numpy()]
+    assert (gk[:, still] == rk[:, still]).all()
+    P.assert_bf16_within_1ulp(gk, rk, f"compact sweep {c}")
+    assert (meta_dst.cpu() == meta_src[keep.long()]).all()
+
+
+def _score_cases(n_cases=40, seed=5):
+    rng = np.random.default_rng(seed)
+    for c in range(n_cases):
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 5, 6, 8]))
+        w_ = int(rng.integers(1, 65))
+        while g * w_ > 512 or (1 << max(0, (g - 1).bit_length())) * w_ > 512:
+            w_ //= 2
+        n = int(rng.integers(max(w_, 2), 5000))
+        yield (c, hkv, g, max(w_, 1), n, int(rng.integers(1, 3)), int(rng.choice([1, 4, 16, 64])),
+               str(rng.choice(["sum", "max_group"])), bool(rng.random() < 0.5))
+
+
+@pytest.mark.parametrize("case", list(_score_cases()), ids=lambda c: f"score{c[0]}")
+def test_score_sweep(case):
+    c, hkv, g, win, n, nl, ps, agg, spans = case
+    print(f"score sweep {c}: kv_heads={hkv} G={g} W={win} N={n} layers={nl} page={ps} {agg} spans={spans}",
+          flush=True)
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=n, window=win, n_q_heads=hkv * g, n_kv_heads=hkv,
+                       n_layers=nl, page_size=ps, n_spans=30)
+    k, v, bt = synth.kv_cache(w, seed=700 + c, device="cpu", paged_shuffle=True, extra_pages=2)
+    q = synth.window_queries(w, seed=700 + c)
+    kw = dict(n_sink=min(4, n), n_recent=min(16, n))
+    ref_kw = dict(kw)
+    if spans:
+        sid, sb = synth.spans(w, seed=700 + c, p_needed=0.3)
+        kw.update(span_id=sid.to(DEV), span_bonus=sb.to(DEV))
+        ref_kw.update(span_id=sid.numpy(), span_bonus=sb.numpy())
+    acc0 = synth.h2o_state(w, seed=700 + c)
+    acc = acc0.to(DEV)
+    got = P._run_score(w, k.to(DEV), v.to(DEV), bt.to(DEV), q, policy="h2o", item_tokens=1,
+                       state=dict(accum=acc), aggregate=agg, **kw)
+    kl = O.gather_logical(P.np64(k), bt.numpy(), ps, n)
+    ref = O.score_step(P.np64(q), kl, policy="h2o", accum=P.np64(acc0), aggregate=agg, **ref_kw)
+    P.assert_rel(P.np64(got["mass"]), ref["mass"], what=f"score sweep {c} mass")
+    assert np.abs(P.np64(got["lse"]) - ref["lse"]).max() < 1e-5
+    P.assert_rel(P.np64(acc.cpu()), ref["accum"], what="accum")
+    P.assert_rel(P.np64(got["item_score"]), ref["item_score"], what="score")
+    assert (got["item_pinned"].numpy().astype(bool) == ref["item_pinned"]).all()
+
+
+@pytest.mark.parametrize("case", list(_score_cases(n_cases=20, seed=6)), ids=lambda c: f"memdecay{c[0]}")
+def test_memdecay_sweep(case):
+    """MemDecay over the same kind of shapes, tokens or pages as items (the sum over query
+    heads, as MemDecay defines the mass), with region pins, sinks, recent tokens and spans."""
+    c, hkv, g, win, n, nl, ps, _, spans = case
+    pages = bool(c % 2)
+    print(f"memdecay sweep {c}: kv_heads={hkv} G={g} W={win} N={n} layers={nl} page={ps} page_items={pages}",
+          flush=True)
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=n, window=win, n_q_heads=hkv * g, n_kv_heads=hkv,
+                       n_layers=nl, page_size=ps, n_spans=30, system_prefix=min(32, n))
+    k, v, bt, q = P._make_score_inputs(w, seed=800 + c, shuffle=True)
+    st0 = P._memdecay_state(w, seed=800 + c)
+    dev = {key: t.clone().to(DEV) for key, t in st0.items()}
+    kw, sid, sb = {}, None, None
+    if spans:
+        sid, sb = synth.spans(w, seed=800 + c, p_needed=0.3)
+        kw = dict(span_id=sid.to(DEV), span_bonus=sb.to(DEV))
+    item_tokens = ps if pages else 1
+    n_sink, n_recent = min(4, n), min(16, n)
+    got = P._run_score(w, k, v, bt, q, policy="memdecay", item_tokens=item_tokens, state=dev, rho=w.rho,
+                       alpha=w.alpha, tau=w.tau, dt_steps=2, pinned_regions=0b101, n_sink=n_sink,
+                       n_recent=n_recent, **kw)
+    dev_state = {key: t.cpu() for key, t in dev.items()}
+    kl = P._paged_to_logical(k, bt, ps, n)
+    P._compare_memdecay(w, q, kl, st0, dev_state, got, w.rho, w.alpha, w.tau, 2, item_tokens, 0b101,
+                        n_sink=n_sink, n_recent=n_recent, span_id=sid, span_bonus=sb)
