@@ -160,3 +160,77 @@ def test_memdecay_sweep(case):
     kl = P._paged_to_logical(k, bt, ps, n)
     P._compare_memdecay(w, q, kl, st0, dev_state, got, w.rho, w.alpha, w.tau, 2, item_tokens, 0b101,
                         n_sink=n_sink, n_recent=n_recent, span_id=sid, span_bonus=sb)
+
+
+def _lrfu_cases(n_cases=30, seed=11):
+    rng = np.random.default_rng(seed)
+    dists = ["power", "ties", "mixed", "equal", "tiny", "wide", "twobinade"]
+    for c in range(n_cases):
+        n = int(rng.choice([1, 2, 5, 63, 64, 65, 1000, 4096, 4097, 30_000, 100_000, 250_000]))
+        dist = str(rng.choice(dists))
+        p = float(np.float32(rng.choice([0.0, 1.0, rng.random(), rng.random(), 0.9, 0.5])))
+        scale = float(rng.choice([1.0, 1.0 / (36 * 8 * 64), 1e-20, 3.0]))
+        decay = float(rng.choice([0.0, 0.5, 1.0, rng.random()]))
+        yield c, n, dist, p, scale, decay
+
+
+@pytest.mark.parametrize("case", list(_lrfu_cases()), ids=lambda c: f"lrfu{c[0]}")
+def test_lrfu_sweep(case):
+    import test_gpu_actkv as A
+    c, n, dist, p, scale, decay = case
+    print(f"lrfu sweep {c}: n={n} {dist} p={p!r} scale={scale} decay={decay}", flush=True)
+    rng = np.random.default_rng(900 + c)
+    a = A._scores(rng, n, dist)
+    ks0 = (rng.random(n) * 2).astype(np.float32)
+    s = (a * np.float32(scale)).astype(np.float32)
+    ks_ref, hit_ref = O.lrfu_update(ks0.astype(np.float64), s, p=p, decay=np.float32(decay))
+    ks = torch.from_numpy(ks0).to(DEV)
+    hit = torch.full((n,), 7, dtype=torch.uint8, device=DEV)
+    kv.kv_lrfu_update(torch.from_numpy(a).to(DEV), ks, scale=scale, top_p=p, decay=decay, hit=hit)
+    torch.cuda.synchronize()
+    got_hit = hit.cpu().numpy().astype(bool)
+    assert (got_hit == hit_ref).all(), (int((got_hit != hit_ref).sum()), int(hit_ref.sum()))
+    np.testing.assert_allclose(ks.cpu().numpy().astype(np.float64), ks_ref, rtol=1e-6, atol=1e-37)
+
+
+def _tail_cases(n_cases=20, seed=12):
+    rng = np.random.default_rng(seed)
+    for c in range(n_cases):
+        n = int(rng.integers(1, 4000))
+        budget = int(rng.integers(1, n + 20))
+        n_keep = int(rng.integers(0, min(n, budget) + 1))
+        yield c, n, budget, n_keep, bool(rng.random() < 0.5), int(rng.integers(1, 4)), int(rng.choice([1, 2, 8]))
+
+
+@pytest.mark.parametrize("case", list(_tail_cases()), ids=lambda c: f"tail{c[0]}")
+def test_tail_compact_sweep(case):
+    import test_gpu_actkv as A
+    c, n, budget, n_keep, shuffle, nl, hkv = case
+    print(f"tail sweep {c}: n={n} budget={budget} keep={n_keep} layers={nl} kv_heads={hkv}", flush=True)
+    rng = np.random.default_rng(1000 + c)
+    slots = -(-n // 16) * 16
+    k = O.bf16_round(rng.standard_normal((nl, slots, hkv, 128)))
+    v = O.bf16_round(rng.standard_normal((nl, slots, hkv, 128)))
+    pos = rng.integers(0, 2 ** 31 - 1, slots).astype(np.int32)
+    keep = np.sort(rng.choice(n, n_keep, replace=False)) if n_keep else np.zeros(0, np.int64)
+    kt, bt = A._paged(rng, k, shuffle)
+    vt = torch.zeros_like(kt)
+    vt_l, _ = A._paged(np.random.default_rng(0), v, False)
+    for pg in range(slots // 16):
+        vt[:, int(bt[pg]) if bt is not None else pg] = vt_l[:, pg]
+    pos_d = torch.from_numpy(pos).to(DEV)
+    keep_d = torch.from_numpy(np.concatenate([keep, [0]]).astype(np.int32)).to(DEV)
+    status = torch.full((1,), 99, dtype=torch.int32, device=DEV)
+    start = kv.kv_compact_tail_inplace(kv.PagedCache(kt, vt, n, bt), keep_d, None, len(keep), budget,
+                                       meta=[pos_d], status=status)
+    torch.cuda.synchronize()
+    if budget >= n:
+        assert start == 0
+        src = dst = np.zeros(0, dtype=np.int64)
+    else:
+        s0, _, src, dst, over = O.tail_compaction_pairs(n, keep, budget, 16)
+        assert start == s0 and not over
+    assert int(status.item()) == 0
+    assert (A._logical(kt, bt, slots) == O.tail_compact(k, src, dst)).all()
+    assert (A._logical(vt, bt, slots) == O.tail_compact(v, src, dst)).all()
+    assert (pos_d.cpu().numpy() == O.tail_compact(pos[None], src, dst)[0]).all()
