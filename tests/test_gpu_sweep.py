@@ -234,3 +234,50 @@ def test_tail_compact_sweep(case):
     assert (A._logical(kt, bt, slots) == O.tail_compact(k, src, dst)).all()
     assert (A._logical(vt, bt, slots) == O.tail_compact(v, src, dst)).all()
     assert (pos_d.cpu().numpy() == O.tail_compact(pos[None], src, dst)[0]).all()
+
+
+def _swap_cases(n_cases=12, seed=13):
+    rng = np.random.default_rng(seed)
+    for c in range(n_cases):
+        count = int(rng.integers(1, 2500))
+        chunk = int(rng.choice([1, 7, 64, 256, 1024, 4096]))
+        buf = min(chunk, count)
+        if rng.random() < 0.5:                 # buffer before the incoming rows
+            buf_first = int(rng.integers(0, 50))
+            in_first = buf_first + buf + int(rng.integers(0, 50))
+        else:
+            in_first = int(rng.integers(0, 50))
+            buf_first = in_first + count + int(rng.integers(0, 50))
+        yield c, count, chunk, in_first, buf_first, bool(rng.random() < 0.5), bool(rng.random() < 0.5)
+
+
+@pytest.mark.parametrize("case", list(_swap_cases()), ids=lambda c: f"swap{c[0]}")
+def test_swap_sweep(case):
+    """Penelope's both-tiers-full swap against the oracle's chunk-by-chunk swap."""
+    import test_gpu_offload as F
+    c, count, chunk, in_first, buf_first, shuffle, two_streams = case
+    print(f"swap sweep {c}: count={count} chunk={chunk} in_first={in_first} buf_first={buf_first} "
+          f"two_streams={two_streams}", flush=True)
+    nl, hkv, n = 2, 2, 3000
+    w = synth.workload("qwen2.5-1.5b-n2048", n_layers=nl, n_kv_heads=hkv, n_q_heads=hkv, n_tokens=n)
+    k, v, bt = synth.kv_cache(w, seed=1100 + c, device=DEV, paged_shuffle=shuffle, extra_pages=2)
+    k0, v0 = F._logical(k, bt, n), F._logical(v, bt, n)
+    rng = np.random.default_rng(1200 + c)
+    rows = max(in_first + count, buf_first + min(chunk, count)) + 5
+    pk = O.bf16_round(rng.standard_normal((nl, rows, hkv, 128)))
+    pv = O.bf16_round(rng.standard_normal((nl, rows, hkv, 128)))
+    hk = torch.from_numpy(pk).to(torch.bfloat16).pin_memory()
+    hv = torch.from_numpy(pv).to(torch.bfloat16).pin_memory()
+    slots = rng.choice(n, min(count, n), replace=False)
+    count = len(slots)
+    in_stream = torch.cuda.Stream() if two_streams else None
+    slots_d = torch.from_numpy(slots.astype(np.int32)).to(DEV)
+    torch.cuda.synchronize()
+    out_rows, nxt, _ = kv.kv_swap_chunked(kv.PagedCache(k, v, n, bt), slots_d, hk, hv, in_first, buf_first,
+                                          chunk=chunk, in_stream=in_stream)
+    torch.cuda.current_stream().synchronize()
+    gk, pk2, want_rows, want_next = O.chunked_swap(k0, pk, slots, in_first, buf_first, chunk)
+    gv, pv2, _, _ = O.chunked_swap(v0, pv, slots, in_first, buf_first, chunk)
+    assert out_rows == want_rows.tolist() and nxt == want_next
+    assert (F._logical(k, bt, n) == gk).all() and (F._logical(v, bt, n) == gv).all()
+    assert (hk.double().numpy() == pk2).all() and (hv.double().numpy() == pv2).all()
