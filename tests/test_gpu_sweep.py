@@ -281,3 +281,67 @@ def test_swap_sweep(case):
     assert out_rows == want_rows.tolist() and nxt == want_next
     assert (F._logical(k, bt, n) == gk).all() and (F._logical(v, bt, n) == gv).all()
     assert (hk.double().numpy() == pk2).all() and (hv.double().numpy() == pv2).all()
+
+
+def _store_cases(n_cases=8, seed=14):
+    rng = np.random.default_rng(seed)
+    kinds = [("default", {}), ("linear", dict(factor=4.0)),
+             ("llama3", dict(factor=8.0, original_max_position=8192)),
+             ("yarn", dict(factor=16.0, original_max_position=4096, beta_fast=32.0, beta_slow=1.0))]
+    for c in range(n_cases):
+        kind, kw = kinds[int(rng.integers(0, len(kinds)))]
+        yield (c, int(rng.integers(1, 4)), int(rng.choice([1, 2, 8])), int(rng.integers(100, 1500)), kind, kw,
+               float(rng.uniform(0.3, 0.95)), bool(rng.random() < 0.5))
+
+
+@pytest.mark.parametrize("case", list(_store_cases()), ids=lambda c: f"store{c[0]}")
+def test_reference_store_sweep(case):
+    """Three compaction steps through PACE's reference store (renumbering, new tokens
+    between steps, sometimes a stale entry), each GPU step from the oracle's state."""
+    import test_gpu_store as S
+    c, nl, hkv, n0, kind, kw, frac, plant = case
+    print(f"store sweep {c}: layers={nl} kv_heads={hkv} n={n0} {kind} keep={frac:.2f} stale={plant}", flush=True)
+    rng = np.random.default_rng(1300 + c)
+    inv = O.scaled_inv_freq(kind, 5e5, **kw)
+    rope = kv.kv_rope(kind, base=5e5, **kw)
+    k, v, pos, ref_k, ref_pos = S._state(rng, nl, n0, hkv)
+    for step in range(3):
+        n = k.shape[1]
+        if plant and step == 2 and (ref_pos != O.REF_NONE).any():
+            j = int(np.nonzero(ref_pos != O.REF_NONE)[0][-1])
+            ref_k[:, j] = O.bf16_round(rng.standard_normal((nl, hkv, 128)))
+        n_keep = max(1, int(n * frac))
+        keep = np.sort(rng.choice(n, n_keep, replace=False))
+        base = int(rng.integers(0, 100))
+        ok, ov, opos, oref, orefp, _ = O.compact_rerope_store(k, v, keep, pos, base, inv, ref_k, ref_pos)
+        kt, bt = S.to_paged(k, rng)
+        vt = torch.zeros_like(kt)
+        vl = torch.from_numpy(v).to(torch.bfloat16).to(DEV)
+        for p in range(-(-n // S.PG)):
+            seg = vl[:, p * S.PG:(p + 1) * S.PG]
+            vt[:, int(bt[p]), : seg.shape[1]] = seg
+        src_store = S.store_to_dev(ref_k, ref_pos)
+        dst_store = kv.RefStore.empty(nl, n_keep, hkv, DEV)
+        dk = torch.zeros((nl, -(-n_keep // S.PG), S.PG, hkv, 128), dtype=torch.bfloat16, device=DEV)
+        dv = torch.zeros_like(dk)
+        newp = torch.zeros(n_keep, dtype=torch.int32, device=DEV)
+        kv.kv_compact_rerope(kv.PagedCache(kt, vt, n, bt), kv.PagedCache(dk, dv, n_keep),
+                             torch.from_numpy(keep.astype(np.int32)).to(DEV), None, n_keep,
+                             torch.from_numpy(pos.astype(np.int32)).to(DEV), newp, renumber_base=base,
+                             rope=rope, ref_src=src_store, ref_dst=dst_store)
+        torch.cuda.synchronize()
+        gp = dst_store.pos.cpu().numpy().astype(np.int64)
+        assert (newp.cpu().numpy() == opos).all(), step
+        assert (S.from_paged(dv, None, n_keep) == ov).all(), step
+        assert (gp == orefp).all(), step
+        valid = orefp != O.REF_NONE
+        gref = dst_store.k.float().cpu().double().numpy()
+        assert (gref[:, valid] == oref[:, valid]).all(), step
+        assert S.within_1ulp(S.from_paged(dk, None, n_keep), ok), step
+        add = int(rng.integers(1, 200))
+        k_new, v_new, _, _, _ = S._state(rng, nl, add, hkv)
+        k = np.concatenate([ok, k_new], axis=1)
+        v = np.concatenate([ov, v_new], axis=1)
+        pos = np.concatenate([opos, opos.max() + 1 + np.arange(add)])
+        ref_k = np.concatenate([oref, np.zeros_like(k_new)], axis=1)
+        ref_pos = np.concatenate([orefp, np.full(add, O.REF_NONE, dtype=np.int64)])
