@@ -342,16 +342,17 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW, kNt>& x, P& p, uint8_t (
         x.template issue_fast<true>(t + kAhead, kt0 + STA * kTileBytes, jk, ph);
         if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
         p.mma(kt[ST], 1, acc1);
-        p.template consume<false>(acc0, tj, 0, cb);
+        p.template consume<false, true>(acc0, tj, 0, cb);
         x.wait_and_barrier(kAhead - 1);
         if (t >= 1) p.between(t - 1, cbp);
         p.mma(kt[ST1], 0, acc0);
-        p.template consume<false>(acc1, tj + 32, 1, cb);
+        p.template consume<false, true>(acc1, tj + 32, 1, cb);
         ++t;
         cb = cb == 2 ? 0 : cb + 1;
         return true;
       };
       static_assert(kStages == 4, "the unrolled steady loop has one step per stage");
+      p.enter_steady();
       while (step(StageC<0>{}) && step(StageC<1>{}) && step(StageC<2>{}) && step(StageC<3>{})) {
       }
       st = t % kStages;
@@ -595,6 +596,8 @@ struct MassPass {
   float (*colp)[kTile * kColStride];
   const float* nlw;                                  // -LSE2 of this wave's 32 rows (LDS)
   float c;
+  float nl_[16];                                     // this lane's 16 rows' -LSE2, held in
+                                                     // registers over the steady loop
 
   // nls: LDS block of NW*32 floats; each wave stores -LSE2 of its rows (-inf past the
   // last row).  Only the owning wave reads them, so no barrier is needed.
@@ -608,6 +611,13 @@ struct MassPass {
       own[x.lane] = row < x.a.rows ? -x.a.lse2[(int64_t)x.lg * x.a.rows + row] : -INFINITY;
     }
     nlw = own;
+  }
+
+  // The steady loop takes every row's -LSE2 from registers: reading them from LDS for
+  // each half tile cost about 4% of the pass.  The other loops read them from LDS, so
+  // that these registers are free there.
+  __device__ __forceinline__ void enter_steady() {
+    if constexpr (kMaxLog == 0) load_nl(nl_);
   }
 
   // -LSE2 of this lane's 16 rows 8*(i/4) + 4*(lane/32) + i%4, as four float4 reads
@@ -657,18 +667,28 @@ struct MassPass {
 
   // This lane's share of the column sum of one half: hidden entries are excluded by
   // their exponent argument (the accumulators are only read, never rewritten).
-  template <bool kMask>
+  // kRegNl: -LSE2 from the registers loaded by enter_steady, else from LDS.
+  template <bool kMask, bool kRegNl = false>
   __device__ __forceinline__ void consume(const f32x16& acc, int64_t half_j0, int half, int cb) const {
     const uint32_t h = kMask ? hidden(half_j0) : 0u;
     float part;
     if constexpr (kMaxLog == 0) {
-      // -LSE2 read four rows at a time, to keep few registers live beside the second
-      // accumulator set
       float r[4];                                    // four running partial sums
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 v = *(const float4*)(nlw + 8 * g + 4 * (x.lane >> 5));
-        const float nv[4] = {v.x, v.y, v.z, v.w};
+        float nv[4];
+        if constexpr (kRegNl) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) nv[u] = nl_[4 * g + u];
+        } else {
+          // four rows at a time, to keep few registers live beside the second
+          // accumulator set
+          const float4 v = *(const float4*)(nlw + 8 * g + 4 * (x.lane >> 5));
+          nv[0] = v.x;
+          nv[1] = v.y;
+          nv[2] = v.z;
+          nv[3] = v.w;
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i = 4 * g + u;
