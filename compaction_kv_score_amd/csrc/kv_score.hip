@@ -408,9 +408,9 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW, kNt>& x, P& p, uint8_t (
       x.issue_fast(t + kAhead, kt0 + STA * kTileBytes, jk, ph);
       if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
       p.mma(kt[ST], 0, acc);
-      p.template consume<false>(acc, tj, 0, cb);
+      p.template consume<false, true>(acc, tj, 0, cb);
       p.mma(kt[ST], 1, acc);
-      p.template consume<false>(acc, tj + 32, 1, cb);
+      p.template consume<false, true>(acc, tj + 32, 1, cb);
       x.wait_and_barrier(kAhead - 1);
       p.between(t, cb);
       ++t;
@@ -418,6 +418,7 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW, kNt>& x, P& p, uint8_t (
       return true;
     };
     static_assert(kStages == 4, "the unrolled steady loop has one step per stage");
+    p.enter_steady();
     while (step(StageC<0>{}) && step(StageC<1>{}) && step(StageC<2>{}) && step(StageC<3>{})) {
     }
     st = t % kStages;
@@ -616,9 +617,7 @@ struct MassPass {
   // The steady loop takes every row's -LSE2 from registers: reading them from LDS for
   // each half tile cost about 4% of the pass.  The other loops read them from LDS, so
   // that these registers are free there.
-  __device__ __forceinline__ void enter_steady() {
-    if constexpr (kMaxLog == 0) load_nl(nl_);
-  }
+  __device__ __forceinline__ void enter_steady() { load_nl(nl_); }
 
   // -LSE2 of this lane's 16 rows 8*(i/4) + 4*(lane/32) + i%4, as four float4 reads
   __device__ __forceinline__ void load_nl(float (&nl)[16]) const {
@@ -701,7 +700,12 @@ struct MassPass {
       part = (r[0] + r[1]) + (r[2] + r[3]);
     } else {
       float nl[16];
-      load_nl(nl);
+      if constexpr (kRegNl) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) nl[i] = nl_[i];
+      } else {
+        load_nl(nl);
+      }
       float arg[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
