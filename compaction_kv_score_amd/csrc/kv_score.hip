@@ -299,8 +299,8 @@ struct StageC {
 // set and the overlap comes from the other waves resident on the SIMD.
 // P::kUnrollStages: the steady-state loop takes one step per ring stage (tile t uses
 // stage t % kStages), so every LDS fragment address is a constant offset from a
-// per-lane base and needs no address arithmetic (the LSE pass does without: unrolled,
-// its register allocation spills).
+// per-lane base and needs no address arithmetic.  P::enter_steady() runs once before
+// that loop, and its consume calls pass kRegNl = true.
 template <int NW, bool kNt, class P>
 __device__ __forceinline__ void run_tiles(const Ctx<NW, kNt>& x, P& p, uint8_t (*kt)[kTileBytes],
                                           uint8_t* junk, const int32_t* __restrict__ bt) {
@@ -374,6 +374,7 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW, kNt>& x, P& p, uint8_t (
       cb = cb == 2 ? 0 : cb + 1;
     }
     for (; t < nt; ++t) {
+      t = __builtin_amdgcn_readfirstlane(t);   // uniform: keeps the tile arithmetic scalar
       const int64_t tj = x.j0 + (int64_t)t * kTile;
       const int st1 = st == kStages - 1 ? 0 : st + 1;
       const int sta = st == 0 ? kStages - 1 : st - 1;
@@ -447,22 +448,29 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW, kNt>& x, P& p, uint8_t (
 // --------------------------------------------------------------------------- pass 1
 // S^T = K Q^T: each lane holds one query row (row0 + 32*wv + lane%32) against 16 keys of
 // a half (8*(i/4) + 4*(lane/32) + i%4), so the running softmax state is lane-local.
+// Element i of a lane's 32x32 MFMA block sits at offset 8*(i/4) + i%4 from the lane's
+// first row or key; the number of these offsets below l, for 0 <= l <= 32.
+__device__ __forceinline__ int offsets_below(int l) {
+  const int r = l & 7;
+  return 4 * (l >> 3) + (r < 4 ? r : 4);
+}
+
 template <int NW>
 struct LsePass {
   using C = Ctx<NW, true>;
   static constexpr bool kOverlap = true;
-  static constexpr bool kUnrollStages = false;
+  static constexpr bool kUnrollStages = true;
   const C& x;
   const bf16x8 (&qf)[8];
   float c;
-  int64_t last_key;               // last key this lane's row may see
+  int last_key;                   // last key this lane's row may see (rows are below 2^31 keys)
   float m, l;
   float nm;                       // -m, kept so that the exponent argument is one fma
 
   __device__ LsePass(const C& ctx, const bf16x8 (&q)[8]) : x(ctx), qf(q) {
     c = x.a.c;
     const int w = (x.row0 + x.wv * 32 + (x.lane & 31)) / x.a.row_stride;
-    last_key = x.a.n_tokens - x.a.window + w;
+    last_key = (int)(x.a.n_tokens - x.a.window) + w;
     m = -1e30f;
     nm = 1e30f;
     l = 0.f;
@@ -486,15 +494,13 @@ struct LsePass {
   // Element i holds key base + off_i (base = half_j0 + 4*(lane/32), off_i = 8*(i/4) +
   // i%4), and the row sees keys below min(chunk end, last_key + 1): one 32-bit limit.
   __device__ uint32_t hidden(int64_t half_j0) const {
-    const int64_t base = half_j0 + 4 * (x.lane >> 5);
-    int64_t lim = (x.j1 < last_key + 1 ? x.j1 : last_key + 1) - base;
-    lim = lim < 0 ? 0 : (lim > 32 ? 32 : lim);
-    const int l = (int)lim;
-    uint32_t h = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (8 * (i >> 2) + (i & 3) >= l) h |= 1u << i;
-    return h;
+    const int base = (int)half_j0 + 4 * (x.lane >> 5);
+    const int end = (int)x.j1 < last_key + 1 ? (int)x.j1 : last_key + 1;
+    int l = end - base;
+    l = l < 0 ? 0 : (l > 32 ? 32 : l);
+    // the offsets increase with i, so the hidden elements are the ones from the count of
+    // offsets below l on
+    return (0xFFFFu << offsets_below(l)) & 0xFFFFu;
   }
 
   // Sum of 2^(c*s + nref) over the half, nref = -reference; hidden keys are excluded
@@ -512,8 +518,10 @@ struct LsePass {
     return (r[0] + r[1]) + (r[2] + r[3]);
   }
 
+  __device__ __forceinline__ void enter_steady() {}
+
   // Fold a half into the running state, rescaling when its sum left [0, 2^64].
-  template <bool kMask>
+  template <bool kMask, bool = false>
   __device__ __forceinline__ void consume(const f32x16& acc, int64_t half_j0, int, int) {
     const uint32_t h = kMask ? hidden(half_j0) : 0u;
     float ts = sums<kMask>(acc, h, nm);
@@ -656,12 +664,9 @@ struct MassPass {
     if (j >= x.j1) return 0xFFFFu;
     const int64_t d64 = j - (x.a.n_tokens - x.a.window);
     const int d = d64 < 0 ? 0 : (d64 > x.a.window ? x.a.window : (int)d64);
-    const int lim = d * x.a.row_stride - (x.row0 + x.wv * 32 + 4 * (x.lane >> 5));
-    uint32_t h = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (8 * (i >> 2) + (i & 3) < lim) h |= 1u << i;
-    return h;
+    int lim = d * x.a.row_stride - (x.row0 + x.wv * 32 + 4 * (x.lane >> 5));
+    lim = lim < 0 ? 0 : (lim > 32 ? 32 : lim);
+    return (1u << offsets_below(lim)) - 1u;   // the offsets increase with i
   }
 
   // This lane's share of the column sum of one half: hidden entries are excluded by
