@@ -7,8 +7,8 @@
 //     resets when Abar > tau and otherwise advances by dt_steps;
 //     s = b_r * exp(-lambda_r * clock) + alpha * a.
 //   H2O (PACE Sec. 2, heavy hitters): acc <- acc + mass; s = acc.
-// plus PACE's foresight bonus (Sec. 3.1; floor as in Sec. 5.7 and 7) for tokens whose
-// span a future step reads, and the pinning rules (MemDecay pinned regions, PACE
+// plus the foresight bonus of the token's span, one value per span from the caller's
+// planner (PACE Sec. 3.1 and 7), and the pinning rules (MemDecay pinned regions, PACE
 // Table 1 sinks and recent window).  In page mode a page's score is the mean over the
 // tokens it holds (MemDecay's S_p) and a page is pinned when any token is.
 #include "kv_internal.h"
