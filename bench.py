@@ -36,11 +36,19 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
 
 class HipEvents:
-    """hipEvent_t handles through the HIP runtime (timing on the library's own stream)."""
+    """hipEvent_t handles through the HIP runtime (timing on the library's own stream).
+
+    The events are created with hipEventDisableSystemFence: they are only read after a full
+    device synchronisation, and without the system-scope fence an event recorded between
+    two launches holds the next launch back less (by kernel trace on this part: 4.9 us
+    instead of 6.6 us)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
@@ -50,7 +58,7 @@ class HipEvents:
         arr = (ctypes.c_void_p * n)()
         for i in range(n):
             h = ctypes.c_void_p()
-            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            assert self.hip.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE) == 0
             arr[i] = h
         return arr
 
@@ -748,8 +756,8 @@ def main():
     def step(ev=None, edge=None):
         """One step.  ev: 7 events recorded between the stages (kv_score records the first
         five), for the per-kernel times.  edge: 2 events recorded before and after the step
-        only; every event recorded between two launches holds the next one back by a few
-        microseconds, so the step time is taken from steps that record none inside."""
+        only; every event recorded between two launches holds the next one back by about
+        5 us, so the step time is taken from steps that record none inside."""
         if edge is not None:
             hip.record(edge[0], sh)
         kv.kv_score(src, q, workspace=ws_score,
