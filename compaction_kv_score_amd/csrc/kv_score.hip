@@ -297,10 +297,10 @@ struct StageC {
 // goes through exp (two accumulator sets), so one wave keeps both the matrix core and
 // the vector ALU busy.  Otherwise each half runs MFMA then exp with one accumulator
 // set and the overlap comes from the other waves resident on the SIMD.
-// P::kUnrollStages: the steady-state loop takes one step per ring stage (tile t uses
-// stage t % kStages), so every LDS fragment address is a constant offset from a
-// per-lane base and needs no address arithmetic.  P::enter_steady() runs once before
-// that loop, and its consume calls pass kRegNl = true.
+// The steady-state loop takes one step per ring stage (tile t uses stage t % kStages),
+// so every LDS fragment address is a constant offset from a per-lane base and needs no
+// address arithmetic.  P::enter_steady() runs once before that loop, and its consume
+// calls pass kRegNl = true.
 template <int NW, bool kNt, class P>
 __device__ __forceinline__ void run_tiles(const Ctx<NW, kNt>& x, P& p, uint8_t (*kt)[kTileBytes],
                                           uint8_t* junk, const int32_t* __restrict__ bt) {
@@ -329,50 +329,32 @@ __device__ __forceinline__ void run_tiles(const Ctx<NW, kNt>& x, P& p, uint8_t (
   if constexpr (P::kOverlap) {
     f32x16 acc0, acc1;
     p.mma(kt[0], 0, acc0);
-    if constexpr (P::kUnrollStages) {
-      // one step per ring stage (tile t uses stage t % kStages): every LDS fragment
-      // address is a constant offset from a per-lane base
-      auto step = [&](auto stage) -> bool {
-        constexpr int ST = decltype(stage)::value;
-        constexpr int ST1 = (ST + 1) % kStages, STA = (ST + kStages - 1) % kStages;
-        t = __builtin_amdgcn_readfirstlane(t);   // uniform: keeps the tile arithmetic scalar
-        if (!(t + kAhead < nf && t < nc)) return false;
-        const int64_t tj = x.j0 + (int64_t)t * kTile;
-        const int cbp = cb == 0 ? 2 : cb - 1;
-        x.template issue_fast<true>(t + kAhead, kt0 + STA * kTileBytes, jk, ph);
-        if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
-        p.mma(kt[ST], 1, acc1);
-        p.template consume<false, true>(acc0, tj, 0, cb);
-        x.wait_and_barrier(kAhead - 1);
-        if (t >= 1) p.between(t - 1, cbp);
-        p.mma(kt[ST1], 0, acc0);
-        p.template consume<false, true>(acc1, tj + 32, 1, cb);
-        ++t;
-        cb = cb == 2 ? 0 : cb + 1;
-        return true;
-      };
-      static_assert(kStages == 4, "the unrolled steady loop has one step per stage");
-      p.enter_steady();
-      while (step(StageC<0>{}) && step(StageC<1>{}) && step(StageC<2>{}) && step(StageC<3>{})) {
-      }
-      st = t % kStages;
-    }
-    for (; t + kAhead < nf && t < nc; ++t) {
+    // one step per ring stage (tile t uses stage t % kStages): every LDS fragment
+    // address is a constant offset from a per-lane base
+    auto step = [&](auto stage) -> bool {
+      constexpr int ST = decltype(stage)::value;
+      constexpr int ST1 = (ST + 1) % kStages, STA = (ST + kStages - 1) % kStages;
+      t = __builtin_amdgcn_readfirstlane(t);   // uniform: keeps the tile arithmetic scalar
+      if (!(t + kAhead < nf && t < nc)) return false;
       const int64_t tj = x.j0 + (int64_t)t * kTile;
-      const int st1 = st == kStages - 1 ? 0 : st + 1;
-      const int sta = st == 0 ? kStages - 1 : st - 1;   // stage of tile t + kAhead
       const int cbp = cb == 0 ? 2 : cb - 1;
-      x.issue_fast(t + kAhead, stage_addr(sta), jk, ph);
+      x.template issue_fast<true>(t + kAhead, kt0 + STA * kTileBytes, jk, ph);
       if (t + kAhead + 1 < nt) x.fetch_pages(t + kAhead + 1, bt, ph);
-      p.mma(kt[st], 1, acc1);
-      p.template consume<false>(acc0, tj, 0, cb);
+      p.mma(kt[ST], 1, acc1);
+      p.template consume<false, true>(acc0, tj, 0, cb);
       x.wait_and_barrier(kAhead - 1);
       if (t >= 1) p.between(t - 1, cbp);
-      p.mma(kt[st1], 0, acc0);
-      p.template consume<false>(acc1, tj + 32, 1, cb);
-      st = st1;
+      p.mma(kt[ST1], 0, acc0);
+      p.template consume<false, true>(acc1, tj + 32, 1, cb);
+      ++t;
       cb = cb == 2 ? 0 : cb + 1;
+      return true;
+    };
+    static_assert(kStages == 4, "the unrolled steady loop has one step per stage");
+    p.enter_steady();
+    while (step(StageC<0>{}) && step(StageC<1>{}) && step(StageC<2>{}) && step(StageC<3>{})) {
     }
+    st = t % kStages;
     for (; t < nt; ++t) {
       t = __builtin_amdgcn_readfirstlane(t);   // uniform: keeps the tile arithmetic scalar
       const int64_t tj = x.j0 + (int64_t)t * kTile;
@@ -459,7 +441,6 @@ template <int NW>
 struct LsePass {
   using C = Ctx<NW, true>;
   static constexpr bool kOverlap = true;
-  static constexpr bool kUnrollStages = true;
   const C& x;
   const bf16x8 (&qf)[8];
   float c;
@@ -598,7 +579,6 @@ struct MassPass {
   using C = Ctx<NW, false>;
   // the sum keeps two accumulator sets (the group maximum's extra registers would spill)
   static constexpr bool kOverlap = kMaxLog == 0;
-  static constexpr bool kUnrollStages = true;
   static constexpr int kColStride = 2 * NW + 1;     // floats per key (partials + pad)
   const C& x;
   const bf16x8 (&qf)[8];
