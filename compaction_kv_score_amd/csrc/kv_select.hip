@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
       const bool in = b0 + (int64_t)u * kSelThreads + tid < end;
       const uint32_t key = order_key(sc[u]);
       npin += pin[u] ? 1u : 0u;
-      nan_seen |= (in && !pin[u] && sc[u] != sc[u]) ? 1u : 0u;
+      nan_seen |= (in && sc[u] != sc[u]) ? 1u : 0u;   // any item, pinned ones included
       hist_add(h, in && !pin[u] && (key & mask) == prefix, (key >> shift) & dmask);
     }
   }

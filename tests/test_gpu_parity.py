@@ -208,6 +208,21 @@ def test_select_page_mode(n_tokens, budget_pages):
     _select_case(n_items, 16, n_tokens, budget_pages, s, pin)
 
 
+def test_select_nan_only_in_pinned_items():
+    """KV_STATUS_NAN_SCORE reports a NaN score of any item, also when only pinned items
+    have one (they are kept whatever their score)."""
+    s = synth.scores(5000, seed=12)
+    pin = torch.zeros(5000, dtype=torch.uint8)
+    pin[[7, 4000]] = 1
+    s[[7, 4000]] = float("nan")
+    _select_case(5000, 1, 5000, 300, s, pin)
+    s2 = synth.scores(50, seed=13)
+    p2 = torch.zeros(50, dtype=torch.uint8)
+    p2[49] = 1
+    s2[49] = float("nan")
+    _select_case(50, 1, 50, 0, s2, p2)                 # pinned over budget as well
+
+
 def test_select_overflow_and_budget_extremes():
     s = synth.scores(1000, seed=3)
     _select_case(1000, 1, 1000, 1000, s, None)

@@ -9,6 +9,8 @@ import itertools
 import math
 from fractions import Fraction
 
+import hypothesis as hyp
+import hypothesis.strategies as st
 import numpy as np
 import pytest
 import torch
@@ -426,6 +428,42 @@ def test_select_exhaustive_brute_force():
                     assert bool(status & O.STATUS_PINNED_OVER_BUDGET) == (sum(pinned) > budget)
                     count += 1
     assert count > 1000
+
+
+def _before(score, i, e):
+    """Item i precedes item e in the selection order: numbers before NaN, higher score
+    first, -0 equal to +0, the lower index first on a tie."""
+    ki = (1, 0.0) if math.isnan(score[i]) else (0, -(score[i] + 0.0))
+    ke = (1, 0.0) if math.isnan(score[e]) else (0, -(score[e] + 0.0))
+    return (ki, i) < (ke, e)
+
+
+@hyp.settings(max_examples=400, deadline=None)
+@hyp.given(st.data())
+def test_select_total_order_brute_force(data):
+    """Every float class (NaN, infinities, signed zeros, ties) against the brute-force
+    characterisation: the kept set holds every pinned item, has min(n, max(B, #pinned))
+    items, and each kept unpinned item precedes each evicted unpinned one."""
+    vals = [math.nan, -math.inf, -1.0, -0.0, 0.0, 0.5, 1.0, math.inf]
+    score = data.draw(st.lists(st.sampled_from(vals), min_size=1, max_size=7))
+    n = len(score)
+    pinned = data.draw(st.lists(st.booleans(), min_size=n, max_size=n))
+    budget = data.draw(st.integers(0, n + 1))
+    kept, status = O.select_items(np.array(score), np.array(pinned), budget)
+    npin = sum(pinned)
+    want = None
+    for size in range(n + 1):
+        for c in itertools.combinations(range(n), size):
+            cs = set(c)
+            if not all(i in cs for i in range(n) if pinned[i]) or size != min(n, max(budget, npin)):
+                continue
+            if all(_before(score, i, e) for i in cs if not pinned[i]
+                   for e in range(n) if e not in cs and not pinned[e]):
+                assert want is None, "the characterisation admits one set only"
+                want = list(c)
+    assert list(kept) == want
+    assert bool(status & O.STATUS_NAN_SCORE) == any(math.isnan(v) for v in score)
+    assert bool(status & O.STATUS_PINNED_OVER_BUDGET) == (npin > budget)
 
 
 def test_select_properties_random():
