@@ -544,23 +544,52 @@ def small_config_step(name, steps=20, warmup=3):
     dst = kv.PagedCache(dk, dv, B)
     pos = torch.arange(N, dtype=torch.int32, device=dev)
     newp = torch.zeros(B, dtype=torch.int32, device=dev)
-    times = []
-    for i in range(warmup + steps):
-        ewma.copy_(ewma0)
-        clock.copy_(clock0)
-        e = hip.create(2)
-        hip.record(e[0], sh)
+    def step():
         kv.kv_score(src, q, workspace=ws, **kw)
         kv.kv_select(item_score, item_pinned, pg, N, w.budget_items, keep, nk, workspace=ws_sel)
         kv.kv_compact_rerope(src, dst, keep, nk, B, pos, newp, renumber_base=0, rope_theta=w.rope_theta)
-        hip.record(e[1], sh)
-        torch.cuda.synchronize()
-        if i >= warmup:
-            times.append(hip.ms(e[0], e[1]))
-    times.sort()
-    return {"workload": name, "step_us_median": round(1e3 * times[len(times) // 2], 1),
-            "step_us_min": round(1e3 * times[0], 1), "steps": steps,
-            "KV_tokens_per_s": round(N / (times[len(times) // 2] * 1e-3), 1)}
+
+    def timed(run):
+        times = []
+        for i in range(warmup + steps):
+            ewma.copy_(ewma0)
+            clock.copy_(clock0)
+            e = hip.create(2)
+            hip.record(e[0], sh)
+            run()
+            hip.record(e[1], sh)
+            torch.cuda.synchronize()
+            if i >= warmup:
+                times.append(hip.ms(e[0], e[1]))
+        return sorted(times)
+
+    # eager: the three calls from Python, so the host's enqueue time is part of the step
+    times = timed(step)
+    ref = [t.clone() for t in (keep, nk, dk, dv, newp, item_score)]
+    # the same step captured once in a HIP graph (the library records no memset and
+    # allocates nothing) and replayed: the device-side time without the Python calls
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(cap):
+        ewma.copy_(ewma0)
+        clock.copy_(clock0)
+        step()
+    torch.cuda.current_stream(dev).wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    gtimes = timed(g.replay)
+    same = all(torch.equal(a, b) for a, b in zip(ref, (keep, nk, dk, dv, newp, item_score)))
+    if not same:
+        raise RuntimeError(f"{name}: the graph replay differs from the eager step")
+    med, gmed = times[len(times) // 2], gtimes[len(gtimes) // 2]
+    return {"workload": name, "step_us_median": round(1e3 * med, 1), "step_us_min": round(1e3 * times[0], 1),
+            "steps": steps, "KV_tokens_per_s": round(N / (med * 1e-3), 1),
+            "graph_step_us_median": round(1e3 * gmed, 1), "graph_step_us_min": round(1e3 * gtimes[0], 1),
+            "graph_KV_tokens_per_s": round(N / (gmed * 1e-3), 1),
+            "note": "step_us: eager calls from Python (host enqueue included); graph_step_us: the same "
+                    "launches replayed from one captured HIP graph, outputs identical"}
 
 
 def oracle_baseline(name, layers=None, repeats=1):
@@ -683,6 +712,8 @@ def main():
     ap.add_argument("--segment", action="store_true",
                     help="only the Mistral-7B 131,072-token in-place segment case (5 runs after 1 "
                          "warm-up), one JSON line")
+    ap.add_argument("--small", action="store_true",
+                    help="only the two Qwen2.5-1.5B-shaped steps (eager and graph-replayed), one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reads 1 GiB, writes 1 GiB) three "
                          "times, to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -699,6 +730,10 @@ def main():
         return
     if args.segment:
         print(json.dumps({"segment": segment_case(steps=5, warmup=1)}), flush=True)
+        return
+    if args.small:
+        print(json.dumps({f"step_{n}": small_config_step(n)
+                          for n in ("qwen2.5-1.5b-1layer-n512", "qwen2.5-1.5b-n2048")}), flush=True)
         return
     if args.copy_calibration:
         a = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")

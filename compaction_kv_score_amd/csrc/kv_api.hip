@@ -948,7 +948,7 @@ int32_t kv_swap_chunked(const kv_cache_desc* cache, const int32_t* slots, int64_
   hipError_t e = hipSuccess;
   auto cleanup = [&]() {
     for (hipEvent_t x : ev)
-      if (x) hipEventDestroy(x);   // released once the work recorded on it has completed
+      if (x) (void)hipEventDestroy(x);   // released once the work recorded on it has completed
   };
   if (two) {
     for (hipEvent_t& x : ev)

@@ -20,6 +20,8 @@
 //   3. an emit pass: every block derives its output offset from the counts of the
 //      blocks before it, then walks its items in index order with wavefront ballots and
 //      an LDS scan across waves, and writes the kept token indices.
+// A row of at most 4,096 items fits one block: then one launch does the same steps with
+// the histograms in LDS and no count pass (there are no other blocks to count).
 
 #include <atomic>
 
@@ -85,6 +87,180 @@ __device__ __forceinline__ void hist_add(uint32_t* bin, bool want, uint32_t d) {
 __device__ __forceinline__ int pass_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __device__ __forceinline__ uint32_t pass_dmask(int pass) { return pass == 2 ? 1023u : 2047u; }
 
+// ---- steps shared by the multi-block sequence and the one-block kernel
+
+// Adds the candidates among this block's items [begin, end) to the LDS histogram h for
+// one pass (unpinned items whose key matches `prefix` under `mask`), and counts pinned
+// items and NaN scores (any item, pinned ones included).  sc/pin hold the first batch.
+__device__ __forceinline__ void hist_items(const SelectArgs& a, int64_t begin, int64_t end,
+                                           float (&sc)[kSelBatch], bool (&pin)[kSelBatch], int pass,
+                                           uint32_t prefix, uint32_t mask, uint32_t* h, uint32_t& npin,
+                                           uint32_t& nan_seen) {
+  const int shift = pass_shift(pass);
+  const uint32_t dmask = pass_dmask(pass);
+  for (int64_t b0 = begin; b0 < end; b0 += (int64_t)kSelThreads * kSelBatch) {
+    if (b0 != begin) load_batch(a, b0, end, sc, pin);
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {
+      const bool in = b0 + (int64_t)u * kSelThreads + threadIdx.x < end;
+      const uint32_t key = order_key(sc[u]);
+      npin += pin[u] ? 1u : 0u;
+      nan_seen |= (in && sc[u] != sc[u]) ? 1u : 0u;
+      hist_add(h, in && !pin[u] && (key & mask) == prefix, (key >> shift) & dmask);
+    }
+  }
+}
+
+// The state after pass 0's counts: how many unpinned items are still to be taken, and
+// whether the radix passes are needed at all (mode 1: every unpinned item fits; mode 2:
+// the pinned items alone fill the budget).
+__device__ __forceinline__ void start_state(SelectState& st, const SelectArgs& a, int64_t n_pin, uint32_t nan_any) {
+  st.n_pinned = n_pin;
+  st.n_cand = a.n_items - n_pin;
+  st.nan_seen = nan_any;
+  st.prefix = 0;
+  st.mask = 0;
+  const int64_t k = a.budget - n_pin;
+  st.k_rem = k;
+  st.mode = k >= st.n_cand ? 1u : (k <= 0 ? 2u : 0u);
+}
+
+// Block-wide (every thread calls it): from the complete histogram h of a pass, the digit
+// at which the count from the top reaches st.k_rem; narrows st (prefix, mask, k_rem).
+// Thread t owns bins 2047-2t and 2046-2t (descending); an exclusive scan of the pair
+// sums locates the bin.
+__device__ __forceinline__ void decide_digit(const uint32_t* h, SelectState& st, int pass, uint32_t* s_wsum) {
+  if (st.mode != 0) return;  // uniform: st is shared
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t k_rem = st.k_rem;
+  const uint32_t c0 = h[kBins - 1 - 2 * tid], c1 = h[kBins - 2 - 2 * tid];
+  uint32_t incl = c0 + c1;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s_wsum[wv] = incl;
+  __syncthreads();
+  int64_t before = 0;
+  for (int w = 0; w < wv; ++w) before += s_wsum[w];
+  const int64_t excl = before + incl - (c0 + c1);
+  int digit = -1;
+  int64_t above = 0;
+  if (excl < k_rem && excl + c0 >= k_rem) {
+    digit = kBins - 1 - 2 * tid;
+    above = excl;
+  } else if (excl + c0 < k_rem && excl + c0 + c1 >= k_rem) {
+    digit = kBins - 2 - 2 * tid;
+    above = excl + c0;
+  }
+  if (digit >= 0) {
+    st.k_rem = k_rem - above;
+    st.prefix |= (uint32_t)digit << pass_shift(pass);
+    st.mask |= pass_dmask(pass) << pass_shift(pass);
+  }
+  __syncthreads();
+}
+
+// Exclusive prefixes of two per-thread flags over the block in one pass (per-wave
+// counts packed as a | b << 16, at most 64 each).
+__device__ __forceinline__ void block_scan2(bool fa, bool fb, uint32_t* s_wave, uint32_t& ra, uint32_t& rb,
+                                            uint32_t& ta, uint32_t& tb) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const uint64_t ba = __builtin_amdgcn_ballot_w64(fa);
+  const uint64_t bb = __builtin_amdgcn_ballot_w64(fb);
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  if (lane == 0) s_wave[wv] = (uint32_t)__popcll(ba) | ((uint32_t)__popcll(bb) << 16);
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t c = s_wave[w];
+    before += w < wv ? c : 0u;
+    tot += c;
+  }
+  __syncthreads();
+  ra = (before & 0xFFFFu) + (uint32_t)__popcll(ba & below);
+  rb = (before >> 16) + (uint32_t)__popcll(bb & below);
+  ta = tot & 0xFFFFu;
+  tb = tot >> 16;
+}
+
+// Writes the kept token indices of items [begin, end) in index order, given the items
+// kept before `begin` and the ties (key == T) before it; returns the items kept up to
+// `end`.  Sets *s_last_kept when the row's last item is kept.  sc/pin hold the first batch.
+__device__ __forceinline__ int64_t emit_items(const SelectArgs& a, int64_t begin, int64_t end,
+                                              float (&sc)[kSelBatch], bool (&pin)[kSelBatch], uint32_t mode,
+                                              uint32_t T, int64_t k_rem, int64_t kept_before, int64_t eq_before,
+                                              uint32_t* s_wave, int* s_last_kept) {
+  const int tid = threadIdx.x;
+  const int it = a.item_tokens;
+  for (int64_t base = begin; base < end; base += kSelThreads) {
+    const int u = (int)(((base - begin) / kSelThreads) % kSelBatch);
+    if (base != begin && u == 0) load_batch(a, base, end, sc, pin);
+    const int64_t i = base + tid;
+    const bool valid = i < end;
+    bool def = false, eq = false;
+    float sc_u = sc[0];
+    bool pin_u = pin[0];
+#pragma unroll
+    for (int v = 1; v < kSelBatch; ++v)
+      if (u == v) {
+        sc_u = sc[v];
+        pin_u = pin[v];
+      }
+    if (valid) {
+      if (pin_u || mode == 1u) {
+        def = true;
+      } else if (mode == 0u) {
+        const uint32_t key = order_key(sc_u);
+        def = key > T;
+        eq = key == T;
+      }
+    }
+    // def and eq are exclusive; the first max(0, k_rem - eq_before) ties of this round
+    // (in index order) are taken, so one scan of both flags gives every output rank
+    uint32_t def_rank, eq_rank, def_total, eq_total;
+    block_scan2(def, eq, s_wave, def_rank, eq_rank, def_total, eq_total);
+    const int64_t ties_left = k_rem - eq_before > 0 ? k_rem - eq_before : 0;
+    const bool kept = def || (eq && (int64_t)eq_rank < ties_left);
+    const uint32_t out_rank = def_rank + (uint32_t)((int64_t)eq_rank < ties_left ? eq_rank : ties_left);
+    const uint32_t kept_total =
+        def_total + (uint32_t)((int64_t)eq_total < ties_left ? eq_total : ties_left);
+    if (kept) {
+      const int64_t out = (kept_before + out_rank) * it;
+      const int64_t t0 = i * it;
+      const int64_t t1 = t0 + it < a.n_tokens ? t0 + it : a.n_tokens;
+      for (int64_t t = t0; t < t1; ++t) {
+        const int64_t o = out + (t - t0);
+        if (o < a.keep_capacity) a.keep[o] = (int32_t)t;
+      }
+      if (i == a.n_items - 1) *s_last_kept = 1;
+    }
+    kept_before += kept_total;
+    eq_before += eq_total;
+  }
+  return kept_before;
+}
+
+// One thread: the kept token count and the status word of the row.
+__device__ __forceinline__ void write_result(const SelectArgs& a, int64_t kept_items, bool last_kept,
+                                             uint32_t nan_seen, int64_t n_pinned) {
+  // the last item may be a partial page holding n_tokens - (n_items-1)*it tokens
+  const int it = a.item_tokens;
+  int64_t n_tok = kept_items * it;
+  if (last_kept) n_tok -= (int64_t)a.n_items * it - a.n_tokens;
+  *a.n_keep = n_tok;
+  uint32_t status = 0;
+  if (nan_seen) status |= KV_STATUS_NAN_SCORE;
+  if (n_pinned > a.budget) status |= KV_STATUS_PINNED_OVER_BUDGET;
+  if (n_tok > a.keep_capacity) status |= KV_STATUS_KEEP_OVERFLOW;
+  if (a.status) *a.status = status;
+}
+
+// ---- the multi-block sequence
+
 __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, int pass) {
   __shared__ uint32_t h[kBins];
   __shared__ uint32_t s_wsum[kWaves];
@@ -107,21 +283,9 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
   }
   __syncthreads();
   if (mode != 0) return;  // decided without a radix pass (uniform across the grid)
-  const int shift = pass_shift(pass);
-  const uint32_t dmask = pass_dmask(pass);
 
   uint32_t npin = 0, nan_seen = 0;
-  for (int64_t b0 = begin; b0 < end; b0 += (int64_t)kSelThreads * kSelBatch) {
-    if (b0 != begin) load_batch(a, b0, end, sc, pin);
-#pragma unroll
-    for (int u = 0; u < kSelBatch; ++u) {
-      const bool in = b0 + (int64_t)u * kSelThreads + tid < end;
-      const uint32_t key = order_key(sc[u]);
-      npin += pin[u] ? 1u : 0u;
-      nan_seen |= (in && sc[u] != sc[u]) ? 1u : 0u;   // any item, pinned ones included
-      hist_add(h, in && !pin[u] && (key & mask) == prefix, (key >> shift) & dmask);
-    }
-  }
+  hist_items(a, begin, end, sc, pin, pass, prefix, mask, h, npin, nan_seen);
   if (pass == 0) {
     if (npin) atomicAdd(&s_npin, npin);
     if (nan_seen) atomicOr(&s_nan, 1u);
@@ -170,50 +334,10 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelectArgs a, 
       }
     }
     if (lane == 0) st = *a.st;
-    if (lane == 0 && pass == 0) {
-      st.n_pinned = n_pin;
-      st.n_cand = a.n_items - n_pin;
-      st.nan_seen = nan_any;
-      st.prefix = 0;
-      st.mask = 0;
-      const int64_t k = a.budget - n_pin;
-      st.k_rem = k;
-      st.mode = k >= st.n_cand ? 1u : (k <= 0 ? 2u : 0u);
-    }
+    if (lane == 0 && pass == 0) start_state(st, a, n_pin, nan_any);
   }
   __syncthreads();
-  if (st.mode == 0) {
-    // thread t owns bins 2047-2t and 2046-2t (descending); an exclusive scan of the
-    // pair sums locates the bin where the count from the top reaches k_rem
-    const int64_t k_rem = st.k_rem;
-    const uint32_t c0 = h[kBins - 1 - 2 * tid], c1 = h[kBins - 2 - 2 * tid];
-    uint32_t incl = c0 + c1;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
-    }
-    if (lane == 63) s_wsum[wv] = incl;
-    __syncthreads();
-    int64_t before = 0;
-    for (int w = 0; w < wv; ++w) before += s_wsum[w];
-    const int64_t excl = before + incl - (c0 + c1);
-    int digit = -1;
-    int64_t above = 0;
-    if (excl < k_rem && excl + c0 >= k_rem) {
-      digit = kBins - 1 - 2 * tid;
-      above = excl;
-    } else if (excl + c0 < k_rem && excl + c0 + c1 >= k_rem) {
-      digit = kBins - 2 - 2 * tid;
-      above = excl + c0;
-    }
-    if (digit >= 0) {
-      st.k_rem = k_rem - above;
-      st.prefix |= (uint32_t)digit << shift;
-      st.mask |= dmask << shift;
-    }
-    __syncthreads();
-  }
+  decide_digit(h, st, pass, s_wsum);
   if (tid == 0) {
     st.ticket = 0;
     *a.st = st;
@@ -263,31 +387,6 @@ __global__ __launch_bounds__(kSelThreads) void select_count_kernel(SelectArgs a)
   }
 }
 
-// Exclusive prefixes of two per-thread flags over the block in one pass (per-wave
-// counts packed as a | b << 16, at most 64 each).
-__device__ __forceinline__ void block_scan2(bool fa, bool fb, uint32_t* s_wave, uint32_t& ra, uint32_t& rb,
-                                            uint32_t& ta, uint32_t& tb) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const uint64_t ba = __builtin_amdgcn_ballot_w64(fa);
-  const uint64_t bb = __builtin_amdgcn_ballot_w64(fb);
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  if (lane == 0) s_wave[wv] = (uint32_t)__popcll(ba) | ((uint32_t)__popcll(bb) << 16);
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t c = s_wave[w];
-    before += w < wv ? c : 0u;
-    tot += c;
-  }
-  __syncthreads();
-  ra = (before & 0xFFFFu) + (uint32_t)__popcll(ba & below);
-  rb = (before >> 16) + (uint32_t)__popcll(bb & below);
-  ta = tot & 0xFFFFu;
-  tb = tot >> 16;
-}
-
 __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) {
   __shared__ uint32_t s_wave[kWaves];
   __shared__ int64_t s_kept_before, s_eq_before;
@@ -326,66 +425,54 @@ __global__ __launch_bounds__(kSelThreads) void select_emit_kernel(SelectArgs a) 
     }
   }
   __syncthreads();
-  int64_t kept_before = s_kept_before;
-  int64_t eq_before = s_eq_before;
-  const int it = a.item_tokens;
-  for (int64_t base = begin; base < end; base += kSelThreads) {
-    const int u = (int)(((base - begin) / kSelThreads) % kSelBatch);
-    if (base != begin && u == 0) load_batch(a, base, end, sc, pin);
-    const int64_t i = base + tid;
-    const bool valid = i < end;
-    bool def = false, eq = false;
-    float sc_u = sc[0];
-    bool pin_u = pin[0];
-#pragma unroll
-    for (int v = 1; v < kSelBatch; ++v)
-      if (u == v) {
-        sc_u = sc[v];
-        pin_u = pin[v];
-      }
-    if (valid) {
-      if (pin_u || mode == 1u) {
-        def = true;
-      } else if (mode == 0u) {
-        const uint32_t key = order_key(sc_u);
-        def = key > T;
-        eq = key == T;
-      }
-    }
-    // def and eq are exclusive; the first max(0, k_rem - eq_before) ties of this round
-    // (in index order) are taken, so one scan of both flags gives every output rank
-    uint32_t def_rank, eq_rank, def_total, eq_total;
-    block_scan2(def, eq, s_wave, def_rank, eq_rank, def_total, eq_total);
-    const int64_t ties_left = k_rem - eq_before > 0 ? k_rem - eq_before : 0;
-    const bool kept = def || (eq && (int64_t)eq_rank < ties_left);
-    const uint32_t out_rank = def_rank + (uint32_t)((int64_t)eq_rank < ties_left ? eq_rank : ties_left);
-    const uint32_t kept_total =
-        def_total + (uint32_t)((int64_t)eq_total < ties_left ? eq_total : ties_left);
-    if (kept) {
-      const int64_t out = (kept_before + out_rank) * it;
-      const int64_t t0 = i * it;
-      const int64_t t1 = t0 + it < a.n_tokens ? t0 + it : a.n_tokens;
-      for (int64_t t = t0; t < t1; ++t) {
-        const int64_t o = out + (t - t0);
-        if (o < a.keep_capacity) a.keep[o] = (int32_t)t;
-      }
-      if (i == a.n_items - 1) s_last_kept = 1;
-    }
-    kept_before += kept_total;
-    eq_before += eq_total;
-  }
+  const int64_t kept = emit_items(a, begin, end, sc, pin, mode, T, k_rem, s_kept_before, s_eq_before, s_wave,
+                                  &s_last_kept);
   __syncthreads();
-  if (blockIdx.x == gridDim.x - 1 && tid == 0) {
-    // the last item may be a partial page holding n_tokens - (n_items-1)*it tokens
-    int64_t n_tok = kept_before * it;
-    if (s_last_kept) n_tok -= (int64_t)a.n_items * it - a.n_tokens;
-    *a.n_keep = n_tok;
-    uint32_t status = 0;
-    if (a.st->nan_seen) status |= KV_STATUS_NAN_SCORE;
-    if (a.st->n_pinned > a.budget) status |= KV_STATUS_PINNED_OVER_BUDGET;
-    if (n_tok > a.keep_capacity) status |= KV_STATUS_KEEP_OVERFLOW;
-    if (a.status) *a.status = status;
+  if (blockIdx.x == gridDim.x - 1 && tid == 0) write_result(a, kept, s_last_kept != 0, a.st->nan_seen, a.st->n_pinned);
+}
+
+// ---- rows that fit one block (at most kSelThreads * kSelBatch items): every step in one
+// launch.  Each thread loads its items once; the three passes build their histograms in
+// LDS, the digits are decided in place, and the emit needs no counts of other blocks.
+// No workspace memory is touched.
+__global__ __launch_bounds__(kSelThreads) void select_one_block_kernel(SelectArgs a) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t s_wave[kWaves];
+  __shared__ uint32_t s_npin, s_nan;
+  __shared__ int s_last_kept;
+  __shared__ SelectState st;
+  const int tid = threadIdx.x;
+  float sc[kSelBatch];
+  bool pin[kSelBatch];
+  load_batch(a, 0, a.n_items, sc, pin);
+  if (tid == 0) {
+    s_npin = 0;
+    s_nan = 0;
+    s_last_kept = 0;
   }
+  for (int pass = 0; pass < 3; ++pass) {
+    for (int b = tid; b < kBins; b += kSelThreads) h[b] = 0;
+    __syncthreads();   // also closes the previous pass's reads of h and its update of st
+    if (pass > 0 && st.mode != 0) break;   // uniform
+    uint32_t npin = 0, nan_seen = 0;
+    hist_items(a, 0, a.n_items, sc, pin, pass, pass == 0 ? 0u : st.prefix, pass == 0 ? 0u : st.mask, h, npin,
+               nan_seen);
+    if (pass == 0) {
+      if (npin) atomicAdd(&s_npin, npin);
+      if (nan_seen) atomicOr(&s_nan, 1u);
+    }
+    __syncthreads();
+    if (pass == 0) {
+      if (tid == 0) start_state(st, a, s_npin, s_nan);
+      __syncthreads();
+    }
+    decide_digit(h, st, pass, s_wave);
+  }
+  const uint32_t mode = st.mode;
+  const int64_t kept = emit_items(a, 0, a.n_items, sc, pin, mode, st.prefix, mode == 0u ? st.k_rem : 0, 0, 0,
+                                  s_wave, &s_last_kept);
+  __syncthreads();
+  if (tid == 0) write_result(a, kept, s_last_kept != 0, st.nan_seen, st.n_pinned);
 }
 
 __global__ __launch_bounds__(256) void segment_keep_kernel(int64_t prefix, int64_t evict,
@@ -423,8 +510,14 @@ __global__ __launch_bounds__(kSelThreads) void select_init_kernel(SelectState* s
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (trace_on())
-    trace_launch("select init+3 hist+count+emit grid=%d block=%d  items=%lld item_tokens=%d budget=%lld", a.n_blocks,
-                 kSelThreads, (long long)a.n_items, a.item_tokens, (long long)a.budget);
+    trace_launch(a.n_blocks == 1 ? "select one block (3 hist passes, emit) grid=%d block=%d  items=%lld item_tokens=%d budget=%lld"
+                                 : "select init+3 hist+count+emit grid=%d block=%d  items=%lld item_tokens=%d budget=%lld",
+                 a.n_blocks, kSelThreads, (long long)a.n_items, a.item_tokens, (long long)a.budget);
+  if (a.n_blocks == 1) {
+    // the whole row fits one block: one launch instead of six
+    hipLaunchKernelGGL(select_one_block_kernel, dim3(1), dim3(kSelThreads), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(select_init_kernel, dim3(1), dim3(kSelThreads), 0, s, a.st, a.hist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

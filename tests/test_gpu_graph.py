@@ -122,3 +122,71 @@ def test_score_in_a_graph():
         torch.cuda.synchronize()
         for key in out:
             assert torch.equal(got[key], out[key]), (rep, key)
+
+
+def test_memdecay_page_step_in_a_graph():
+    """MemDecay page scoring, page selection and compaction with renumbering (the
+    Qwen2.5-1.5B-shaped step: 28 layers, N = 2,048, budget 512 tokens) captured as one
+    graph; each replay matches the eager step on the same state bit for bit."""
+    w = synth.workload("qwen2.5-1.5b-n2048")
+    N, pg, B = w.n_tokens, w.page_size, w.budget_tokens
+    k, v, bt = synth.kv_cache(w, seed=5, device=DEV, paged_shuffle=True, extra_pages=2)
+    q = synth.window_queries(w, seed=5, device=DEV)
+    ewma0, clock0 = (t.to(DEV) for t in synth.memdecay_state(w, seed=5))
+    ewma, clock = ewma0.clone(), clock0.clone()
+    b_r, lam = synth.region_params(5)
+    n_items = w.n_pages
+    item_score = torch.zeros(n_items, device=DEV)
+    item_pinned = torch.zeros(n_items, dtype=torch.uint8, device=DEV)
+    src = kv.PagedCache(k, v, N, bt)
+    kw = dict(policy="memdecay", window=w.window, item_tokens=pg, region=synth.regions(w, seed=5).to(DEV),
+              base_prio=b_r.to(DEV), decay_rate=lam.to(DEV), rho=w.rho, alpha=w.alpha, tau=w.tau, dt_steps=1,
+              ewma=ewma, clock=clock, pinned_regions=1, item_score=item_score, item_pinned=item_pinned)
+    ws = torch.empty(kv.kv_score_workspace_size(src, q, **kw), dtype=torch.uint8, device=DEV)
+    ws_sel = torch.empty(kv.kv_select_workspace_size(n_items), dtype=torch.uint8, device=DEV)
+    keep = torch.zeros(B, dtype=torch.int32, device=DEV)
+    nk = torch.zeros(1, dtype=torch.int64, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dk = torch.zeros((w.n_layers, B // pg, pg, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    dst = kv.PagedCache(dk, dv, B)
+    pos = torch.arange(N, dtype=torch.int32, device=DEV)
+    newp = torch.zeros(B, dtype=torch.int32, device=DEV)
+    outs = (item_score, item_pinned, ewma, clock, keep, nk, status, dk, dv, newp)
+
+    def step():
+        kv.kv_score(src, q, workspace=ws, **kw)
+        kv.kv_select(item_score, item_pinned, pg, N, w.budget_items, keep, nk, status, workspace=ws_sel)
+        kv.kv_compact_rerope(src, dst, keep, nk, B, pos, newp, renumber_base=0, rope_theta=w.rope_theta)
+
+    def clear():
+        for t in (item_score, item_pinned, keep, nk, dk, dv, newp):
+            t.zero_()
+        status.fill_(7)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        q.copy_(synth.window_queries(w, seed=30 + rep, device=DEV))
+        clear()
+        ewma.copy_(ewma0)
+        clock.copy_(clock0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in outs]
+        clear()
+        ewma.copy_(ewma0)
+        clock.copy_(clock0)
+        step()                                  # eager, same inputs and state
+        torch.cuda.synchronize()
+        assert int(nk.item()) == B and int(status.item()) == 0, rep
+        for i, (x, y) in enumerate(zip(got, outs)):
+            assert torch.equal(x, y), (rep, i)

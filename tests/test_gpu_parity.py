@@ -184,6 +184,12 @@ def _select_case(n_items, item_tokens, n_tokens, budget, score, pinned, cap=None
     (1, None, 0.0, 1.0, 0, False),
     (5, [0.0, 0.5, 1.0], 0.2, 0.6, 0, True),
     (100, [0.1, 0.2], 0.1, 0.3, 0, False),
+    # rows of at most 4,096 items take the one-block kernel: the largest such row with
+    # NaN, -0 and pins, ties at T, pinned items over the budget, every item kept
+    (4096, None, 0.02, 0.1, 0.01, True),
+    (4096, [0.0, 1.0], 0.01, 0.5, 0, True),
+    (3000, None, 0.5, 0.1, 0.002, False),
+    (2500, [0.5, 0.25], 0.1, 1.0, 0, False),
     (4097, None, 0.02, 0.1, 0.01, True),
     (100_000, None, 0.0013, 0.02048, 0, False),
     (100_000, [1.0, 2.0, 3.0], 0.05, 0.5, 0, False),
