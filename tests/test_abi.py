@@ -97,13 +97,19 @@ def _a256(x):
 @pytest.mark.parametrize("n_layers,hkv,hq,window,n_tokens,want_chunks", [
     (36, 8, 32, 64, 100_000, 16),      # 16 chunks of 6,272 keys: 4,608 workgroups, 9 full rounds of 512
     (36, 8, 32, 64, 1_000_000, 125),   # 125 chunks of 8,000 keys: 36,000 workgroups
-    (2, 8, 32, 64, 100_000, 196),      # small grid: chunks of 512 keys so that >= 2,048 workgroups run
-    (2, 2, 4, 8, 100, 1),              # tiny: one chunk
+    # less work (under 2,048 workgroups at 4,096 keys): the cheapest of rounds x (tiles +
+    # 4), a grid of at most one workgroup per CU at 0.6 of that
+    (2, 8, 32, 64, 100_000, 32),       # one full round: 32 chunks of 3,136 keys, 512 workgroups
+    (8, 8, 32, 64, 30_000, 8),         # one full round: 8 chunks of 3,776 keys
+    (2, 8, 32, 64, 8_000, 16),         # one workgroup per CU: 16 chunks of 512 keys
+    (2, 2, 4, 8, 100, 2),              # tiny: two 64-key chunks
+    (1, 2, 12, 32, 512, 8),            # Qwen2.5-1.5B head shape, one layer: 8 single-tile chunks
+    (28, 2, 12, 64, 2048, 2),          # 28 layers, 384 rows in two groups: 2 chunks of 1,024 keys
 ])
 def test_score_grid_choice(n_layers, hkv, hq, window, n_tokens, want_chunks):
     """The key chunking behind the scoring grid, read back from the workspace layout
     (LSE partials [L*Hkv][chunks][rows] float2, final LSE [L*Hkv][rows], mass partials
-    [L*Hkv][N], each 256-byte aligned)."""
+    [L*Hkv*row groups][N], each 256-byte aligned)."""
     L = kv.lib()
     n = ctypes.c_size_t()
     pages = -(-n_tokens // 16)
@@ -112,7 +118,8 @@ def test_score_grid_choice(n_layers, hkv, hq, window, n_tokens, want_chunks):
     p = _score_params(n_q_heads=hq, window=window)
     assert L.kv_score_workspace_size(ctypes.byref(c), ctypes.byref(p), ctypes.byref(n)) == kv.KV_OK
     units, rows = n_layers * hkv, (hq // hkv) * window
-    rest = _a256(units * rows * 4) + _a256(units * n_tokens * 4)
+    n_rsplit = -(-rows // 256)             # row groups of at most 256, each with its own mass partial
+    rest = _a256(units * rows * 4) + _a256(units * n_rsplit * n_tokens * 4)
     assert n.value == _a256(units * want_chunks * rows * 8) + rest
 
 
