@@ -33,6 +33,15 @@ __device__ __forceinline__ int64_t token_offset(int64_t j, int page_shift, int64
 }
 
 // ---------------------------------------------------------------- scoring kernels
+struct CombineArgs {
+  const float2* lse_part;
+  int n_chunks, rows, n_kv_heads, n_q_heads, group, window, n_lg, row_stride;
+  const float* lse_in;          // optional natural-log LSE input [L][Hq][W]
+  float* lse2;                  // [L*Hkv][rows]
+  float* lse_out;               // optional [L][Hq][W]
+  uint32_t* status;             // optional kv_score status word, cleared here
+};
+
 struct ScoreArgs {
   const uint16_t* k;            // bf16 bits
   int64_t layer_stride, page_stride;
@@ -49,18 +58,12 @@ struct ScoreArgs {
   float2* lse_part;             // [L*Hkv][n_chunks][rows] (max, sum) in log2 units
   const float* lse2;            // [L*Hkv][rows] log2-unit LSE (pass 2 input)
   float* mass_part;             // [L*Hkv][n_rsplit][N]
+  int fuse_combine;             // pass 2 combines its rows' LSE itself (no combine launch)
+  CombineArgs comb;             // what that combine reads and writes
 };
 
 hipError_t launch_score_pass(const ScoreArgs& a, bool pass2, hipStream_t s);
 
-struct CombineArgs {
-  const float2* lse_part;
-  int n_chunks, rows, n_kv_heads, n_q_heads, group, window, n_lg, row_stride;
-  const float* lse_in;          // optional natural-log LSE input [L][Hq][W]
-  float* lse2;                  // [L*Hkv][rows]
-  float* lse_out;               // optional [L][Hq][W]
-  uint32_t* status;             // optional kv_score status word, cleared here
-};
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t s);
 
 struct EpilogueArgs {

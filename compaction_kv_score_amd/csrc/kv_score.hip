@@ -569,6 +569,47 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 // --------------------------------------------------------------------------- pass 2
 // S = Q K^T: each lane holds one key of a half (32*half + lane%32) against 16 rows
 // (row0 + 32*wv + 8*(i/4) + 4*(lane/32) + i%4), so the per-key row sums are lane-local.
+// LSE (log2 units) of row `row` of (layer, KV head) lg: its per-chunk (max, sum) partials
+// combined in float64 in chunk order, or the caller's natural-log LSE; +inf for a padding
+// row of the group maximum (weight exp(-inf) = 0).  *nat: the row's [L][Hq][W] index, or
+// -1 for a padding row.
+__device__ __forceinline__ float row_lse2(const CombineArgs& a, int lg, int row, int64_t* nat) {
+  const int layer = lg / a.n_kv_heads;
+  const int g = lg - layer * a.n_kv_heads;
+  const int w = row / a.row_stride;
+  const int hl = row - w * a.row_stride;
+  if (hl >= a.group) {
+    *nat = -1;
+    return INFINITY;
+  }
+  const int h = g * a.group + hl;
+  *nat = ((int64_t)layer * a.n_q_heads + h) * a.window + w;
+  if (a.lse_in) return (float)((double)a.lse_in[*nat] * 1.4426950408889634);
+  // partials are read 8 chunks at a time so that their loads are in flight together;
+  // the maximum and the chunk-ordered float64 sum are unchanged by the batching
+  const float2* p = a.lse_part + (int64_t)lg * a.n_chunks * a.rows + row;
+  constexpr int kB = 8;
+  float mx = -1e30f;
+  for (int ch0 = 0; ch0 < a.n_chunks; ch0 += kB) {
+    float x[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) x[u] = ch0 + u < a.n_chunks ? p[(int64_t)(ch0 + u) * a.rows].x : -1e30f;
+#pragma unroll
+    for (int u = 0; u < kB; ++u) mx = fmaxf(mx, x[u]);
+  }
+  double sum = 0.0;
+  for (int ch0 = 0; ch0 < a.n_chunks; ch0 += kB) {
+    float2 v[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      v[u] = ch0 + u < a.n_chunks ? p[(int64_t)(ch0 + u) * a.rows] : make_float2(-1e30f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (ch0 + u < a.n_chunks) sum += (double)v[u].y * exp2((double)v[u].x - (double)mx);
+  }
+  return (float)((double)mx + log2(sum));
+}
+
 // Each lane leaves its partial in LDS; after the barrier that closes the tile 64
 // threads add the 2*NW partials of each key in a fixed order and store the tile's
 // column sums (three column buffers rotate between tiles).
@@ -597,8 +638,24 @@ struct MassPass {
     float* own = nls + x.wv * 32;
     if (x.lane < 32) {
       const int row = x.row0 + x.wv * 32 + x.lane;
-      own[x.lane] = row < x.a.rows ? -x.a.lse2[(int64_t)x.lg * x.a.rows + row] : -INFINITY;
+      float nl = -INFINITY;
+      if (row < x.a.rows) {
+        if (x.a.fuse_combine) {
+          // a small grid combines its rows' chunk partials itself, with the arithmetic of
+          // lse_combine_kernel; the workgroup of chunk 0 also writes the caller's LSE
+          int64_t nat;
+          const float l2 = row_lse2(x.a.comb, x.lg, row, &nat);
+          if (x.chunk_id == 0 && nat >= 0 && x.a.comb.lse_out)
+            x.a.comb.lse_out[nat] = (float)((double)l2 * 0.6931471805599453);
+          nl = -l2;
+        } else {
+          nl = -x.a.lse2[(int64_t)x.lg * x.a.rows + row];
+        }
+      }
+      own[x.lane] = nl;
     }
+    // the status word is cleared before the epilogue, later on the stream, sets bits
+    if (x.a.fuse_combine && blockIdx.x == 0 && threadIdx.x == 0 && x.a.comb.status) *x.a.comb.status = 0u;
     nlw = own;
   }
 
@@ -829,46 +886,10 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
   if (idx >= (int64_t)a.n_lg * a.rows) return;
   const int lg = (int)(idx / a.rows);
   const int row = (int)(idx - (int64_t)lg * a.rows);
-  const int layer = lg / a.n_kv_heads;
-  const int g = lg - layer * a.n_kv_heads;
-  const int w = row / a.row_stride;
-  const int hl = row - w * a.row_stride;
-  if (hl >= a.group) {                 // padding row of max mode: weight exp(-inf) = 0
-    a.lse2[idx] = INFINITY;
-    return;
-  }
-  const int h = g * a.group + hl;
-  const int64_t nat = ((int64_t)layer * a.n_q_heads + h) * a.window + w;
-  float lse2;
-  if (a.lse_in) {
-    lse2 = (float)((double)a.lse_in[nat] * 1.4426950408889634);
-  } else {
-    // partials are read 8 chunks at a time so that their loads are in flight together;
-    // the maximum and the chunk-ordered float64 sum are unchanged by the batching
-    const float2* p = a.lse_part + (int64_t)lg * a.n_chunks * a.rows + row;
-    constexpr int kB = 8;
-    float mx = -1e30f;
-    for (int ch0 = 0; ch0 < a.n_chunks; ch0 += kB) {
-      float x[kB];
-#pragma unroll
-      for (int u = 0; u < kB; ++u) x[u] = ch0 + u < a.n_chunks ? p[(int64_t)(ch0 + u) * a.rows].x : -1e30f;
-#pragma unroll
-      for (int u = 0; u < kB; ++u) mx = fmaxf(mx, x[u]);
-    }
-    double sum = 0.0;
-    for (int ch0 = 0; ch0 < a.n_chunks; ch0 += kB) {
-      float2 v[kB];
-#pragma unroll
-      for (int u = 0; u < kB; ++u)
-        v[u] = ch0 + u < a.n_chunks ? p[(int64_t)(ch0 + u) * a.rows] : make_float2(-1e30f, 0.f);
-#pragma unroll
-      for (int u = 0; u < kB; ++u)
-        if (ch0 + u < a.n_chunks) sum += (double)v[u].y * exp2((double)v[u].x - (double)mx);
-    }
-    lse2 = (float)((double)mx + log2(sum));
-  }
+  int64_t nat;
+  const float lse2 = row_lse2(a, lg, row, &nat);
   a.lse2[idx] = lse2;
-  if (a.lse_out) a.lse_out[nat] = (float)((double)lse2 * 0.6931471805599453);
+  if (nat >= 0 && a.lse_out) a.lse_out[nat] = (float)((double)lse2 * 0.6931471805599453);
 }
 
 }  // namespace
@@ -877,11 +898,11 @@ hipError_t launch_score_pass(const ScoreArgs& a, bool pass2, hipStream_t s) {
   const int group_rows = a.rows < kRowsPerGroup ? a.rows : kRowsPerGroup;
   const int nw = (group_rows + 31) / 32;
   if (trace_on())
-    trace_launch("%s grid=%lld block=%d  layers=%d kv_heads=%d tokens=%lld rows=%d row_groups=%d chunk=%d chunks=%d%s",
+    trace_launch("%s grid=%lld block=%d  layers=%d kv_heads=%d tokens=%lld rows=%d row_groups=%d chunk=%d chunks=%d%s%s",
                  pass2 ? "mass_pass" : "lse_pass",
                  (long long)a.n_chunks * a.n_rsplit * a.n_kv_heads * a.n_layers, nw * 64, a.n_layers, a.n_kv_heads,
                  (long long)a.n_tokens, a.rows, a.n_rsplit, a.chunk, a.n_chunks,
-                 pass2 && a.max_log ? " group_max" : "");
+                 pass2 && a.max_log ? " group_max" : "", pass2 && a.fuse_combine ? " combines_lse" : "");
   if (!pass2) return launch_nw<-1>(a, nw, s);
   switch (a.max_log) {
     case 0: return launch_nw<0>(a, nw, s);

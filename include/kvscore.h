@@ -169,7 +169,10 @@ typedef struct kv_score_params {
   float *item_score;          /* [ceil(N/item_tokens)] */
   uint8_t *item_pinned;       /* [ceil(N/item_tokens)] */
   /* profiling (optional): host array of 5 events, recorded on the stream before the LSE
-     pass, after it, after the LSE combine, after the mass pass and after the epilogue */
+     pass, after it, after the LSE combine, after the mass pass and after the epilogue
+     (the second and third mark the same point when the mass pass combines the LSE
+     itself, which a grid of at most 512 mass-pass workgroups over at most 16 key chunks
+     does) */
   hipEvent_t *stage_events;
   int32_t aggregate;          /* KV_AGG_*; memset-zeroed params select KV_AGG_SUM */
   uint32_t *status;           /* device word or NULL: set to 0, then KV_STATUS_BAD_REGION

@@ -379,10 +379,13 @@ def test_score_h2o_foresight_parity(over, shuffle):
     assert (span_bonus > 0).any() and (span_id < 0).any() and (span_id >= w.n_spans).any()
 
 
-def test_score_bad_region_labels_are_reported():
+# 1,000 tokens: the mass pass combines the LSE itself; 40,000: 64 key chunks, so a
+# separate combine launch does it (and clears the status word)
+@pytest.mark.parametrize("n_tokens", [1000, 40_000])
+def test_score_bad_region_labels_are_reported(n_tokens):
     """Labels at or above n_regions name no region (b = lambda = 0, no region pin) and set
     KV_STATUS_BAD_REGION; a clean row leaves the status word at 0."""
-    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=1000, n_layers=2, window=32)
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=n_tokens, n_layers=2, window=32)
     k, v, bt, q = _make_score_inputs(w, seed=44, shuffle=True)
     st0 = _memdecay_state(w, seed=44)
     n_regions = int(st0["base_prio"].numel())
@@ -455,10 +458,16 @@ def test_score_max_group_parity(hq, hkv, window, n_tokens, n_layers):
         assert torch.equal(s["mass"], got["mass"])
 
 
-@pytest.mark.parametrize("aggregate,shift", [("sum", 0.0), ("max_group", 0.0), ("max_group", 0.3)])
-def test_score_supplied_lse_both_modes(aggregate, shift):
+# 1,000 tokens (16 key chunks): the mass pass reads the supplied LSE itself; 2,600 and
+# 40,000 (21 and 63 chunks): the combine launch converts it first
+@pytest.mark.parametrize("aggregate,shift,n_tokens", [("sum", 0.0, 1000), ("max_group", 0.0, 1000),
+                                                      ("max_group", 0.3, 1000), ("sum", 0.0, 2600),
+                                                      ("max_group", 0.3, 2600), ("sum", 0.0, 40_000),
+                                                      ("max_group", 0.3, 40_000)])
+def test_score_supplied_lse_both_modes(aggregate, shift, n_tokens):
     """A supplied LSE is used as given (ActKV Sec. 7.1): also when it is not the keys' own."""
-    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=2600, n_layers=2, window=40, n_q_heads=12, n_kv_heads=4)
+    w = synth.workload("qwen2.5-1.5b-1layer-n512", n_tokens=n_tokens, n_layers=2, window=40, n_q_heads=12,
+                       n_kv_heads=4)
     k, v, bt, q = _make_score_inputs(w, seed=17, shuffle=True)
     kl = _paged_to_logical(k, bt, 16, w.n_tokens)
     _, lse = O.attention_mass(np64(q), kl)

@@ -41,6 +41,8 @@ def test_trace_logs_every_launch(flag, expect):
         assert lines == []
         return
     names = [l.split()[1] for l in lines]
-    assert names == ["lse_pass", "lse_combine", "mass_pass", "epilogue", "select", "compact"], names
+    # a grid this small combines the LSE inside the mass pass (no combine launch)
+    assert names == ["lse_pass", "mass_pass", "epilogue", "select", "compact"], names
+    assert "combines_lse" in lines[1]
     assert "tokens=512" in lines[0] and "block=" in lines[0] and "grid=" in lines[0]
     assert "stream_stores=0" in lines[-1]
