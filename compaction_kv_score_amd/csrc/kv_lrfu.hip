@@ -24,6 +24,8 @@
 //      number of entries equal to T (lowest indices first) that complete the target;
 //   2. a count pass (entries equal to T per block) and an update pass that walks the
 //      entries in index order, decides hits and writes KS (and the hit mask).
+// A row of at most 4,096 entries fits one block: then one launch does the same steps with
+// the state and the histograms in LDS and no count pass.
 #include "kv_internal.h"
 
 namespace kvs {
@@ -33,6 +35,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBlocks = 64;
+constexpr int kMaxPerBlock = 4096;  // entries per block while the grid has room
 constexpr int kBins = 2048;
 constexpr int kLimbs = 12;          // 384-bit integers: the total weight stays below 2^336
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt not waited for
@@ -269,63 +272,16 @@ __device__ void topp_first_digit(const unsigned long long* h, float top_p, ToppS
   }
 }
 
-__global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pass) {
-  __shared__ unsigned long long h[kBins];
-  __shared__ uint64_t s_wsum[kWaves];
-  __shared__ uint64_t s_wtot[kWaves][kLimbs];
-  __shared__ Big s_total, s_target;
-  __shared__ int s_last;
-  __shared__ ToppState st;
+// Block-wide (every thread calls it), once h holds a pass's complete weighted histogram
+// and st the state before the pass: fixes the pass's digit (pass 0: the boundary
+// exponent's bin, from exact multi-word sums) and narrows st; after pass 2, st.c_eq.
+__device__ __forceinline__ void decide_digit(const unsigned long long* h, float top_p, int pass, ToppState& st,
+                             uint64_t* s_wsum, uint64_t (*s_wtot)[kLimbs], Big& s_total, Big& s_target) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int b = tid; b < kBins; b += kThreads) h[b] = 0;
-  __syncthreads();
-  const uint32_t mode = pass == 0 ? 0u : a.st->mode;
-  if (mode != 0) return;                      // no hits (every block reads the same word)
-  const uint32_t prefix = pass == 0 ? 0u : a.st->prefix;
-  const uint32_t mask = pass == 0 ? 0u : a.st->mask;
   const int shift = pass_shift(pass);
   const uint32_t dmask = pass_dmask(pass);
-
-  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
-  const int64_t end = begin + a.per_block < a.n ? begin + a.per_block : a.n;
-  for (int64_t i0 = begin; i0 < end; i0 += kThreads) {
-    const int64_t i = i0 + tid;
-    const float s = i < end ? item_score(a, i) : 0.f;
-    const uint64_t w = weight(s);
-    const uint32_t key = __float_as_uint(s);
-    hist_add(h, w != 0 && (key & mask) == prefix, (key >> shift) & dmask, w);
-  }
-  __syncthreads();
-  for (int b = tid; b < kBins; b += kThreads) a.hist[(int64_t)blockIdx.x * kBins + b] = h[b];
-  // Every wave waits for its own stores; then one thread makes the block's histogram
-  // visible device-wide (the release writes back the whole L2, so one per block
-  // suffices) and takes the ticket.
-  __builtin_amdgcn_s_waitcnt(kVmcntZero);
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);   // the write-back has completed
-    s_last = atomicAdd(&a.st->ticket, 1u) == (uint32_t)gridDim.x - 1u;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // acquire for wave 0, the only wave that reads shared data through the caches (the
-  // histograms below are read with cache-bypassing atomic loads)
-  if (threadIdx.x < 64) __threadfence();
-
-  // ---- last block: global weighted histogram (integer sums), then the digit
-  const int nb = (int)gridDim.x;
-  for (int b = tid; b < kBins; b += kThreads) {
-    unsigned long long tot = 0;
-    for (int blk = 0; blk < nb; ++blk)
-      tot += __atomic_load_n(&a.hist[(int64_t)blk * kBins + b], __ATOMIC_RELAXED);
-    h[b] = tot;
-  }
-  __syncthreads();
-  if (tid == 0) st = *a.st;
-  __syncthreads();
   if (pass == 0) {
-    topp_first_digit(h, a.top_p, st, s_wtot, s_total, s_target);
+    topp_first_digit(h, top_p, st, s_wtot, s_total, s_target);
     __syncthreads();
   } else {
     // every candidate shares the exponent: weights are uint64 sums of M.
@@ -365,6 +321,71 @@ __global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pas
       st.c_eq = ws ? (int64_t)((st.rem + ws - 1) / ws) : 0;
     }
   }
+}
+
+// Adds the weights of the candidate entries of [begin, end) (positive finite scores
+// whose bits match `prefix` under `mask`) to the LDS histogram h, by this pass's digit.
+__device__ __forceinline__ void hist_entries(const LrfuArgs& a, int64_t begin, int64_t end, int pass,
+                                             uint32_t prefix, uint32_t mask, unsigned long long* h) {
+  const int shift = pass_shift(pass);
+  const uint32_t dmask = pass_dmask(pass);
+  for (int64_t i0 = begin; i0 < end; i0 += kThreads) {
+    const int64_t i = i0 + threadIdx.x;
+    const float s = i < end ? item_score(a, i) : 0.f;
+    const uint64_t w = weight(s);
+    const uint32_t key = __float_as_uint(s);
+    hist_add(h, w != 0 && (key & mask) == prefix, (key >> shift) & dmask, w);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pass) {
+  __shared__ unsigned long long h[kBins];
+  __shared__ uint64_t s_wsum[kWaves];
+  __shared__ uint64_t s_wtot[kWaves][kLimbs];
+  __shared__ Big s_total, s_target;
+  __shared__ int s_last;
+  __shared__ ToppState st;
+  const int tid = threadIdx.x;
+  for (int b = tid; b < kBins; b += kThreads) h[b] = 0;
+  __syncthreads();
+  const uint32_t mode = pass == 0 ? 0u : a.st->mode;
+  if (mode != 0) return;                      // no hits (every block reads the same word)
+  const uint32_t prefix = pass == 0 ? 0u : a.st->prefix;
+  const uint32_t mask = pass == 0 ? 0u : a.st->mask;
+
+  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
+  const int64_t end = begin + a.per_block < a.n ? begin + a.per_block : a.n;
+  hist_entries(a, begin, end, pass, prefix, mask, h);
+  __syncthreads();
+  for (int b = tid; b < kBins; b += kThreads) a.hist[(int64_t)blockIdx.x * kBins + b] = h[b];
+  // Every wave waits for its own stores; then one thread makes the block's histogram
+  // visible device-wide (the release writes back the whole L2, so one per block
+  // suffices) and takes the ticket.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);   // the write-back has completed
+    s_last = atomicAdd(&a.st->ticket, 1u) == (uint32_t)gridDim.x - 1u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // acquire for wave 0, the only wave that reads shared data through the caches (the
+  // histograms below are read with cache-bypassing atomic loads)
+  if (threadIdx.x < 64) __threadfence();
+
+  // ---- last block: global weighted histogram (integer sums), then the digit
+  const int nb = (int)gridDim.x;
+  for (int b = tid; b < kBins; b += kThreads) {
+    unsigned long long tot = 0;
+    for (int blk = 0; blk < nb; ++blk)
+      tot += __atomic_load_n(&a.hist[(int64_t)blk * kBins + b], __ATOMIC_RELAXED);
+    h[b] = tot;
+  }
+  __syncthreads();
+  if (tid == 0) st = *a.st;
+  __syncthreads();
+  decide_digit(h, a.top_p, pass, st, s_wsum, s_wtot, s_total, s_target);
   if (tid == 0) {
     st.ticket = 0;
     *a.st = st;
@@ -408,20 +429,11 @@ __device__ __forceinline__ uint32_t block_scan(bool flag, uint32_t* s_wave, uint
   return before + (uint32_t)__popcll(below);
 }
 
-__global__ __launch_bounds__(kThreads) void lrfu_update_kernel(LrfuArgs a) {
-  __shared__ uint32_t s_wave[kWaves];
-  __shared__ int64_t s_eq_before;
-  const ToppState st = *a.st;
+// Walks entries [begin, end) in index order, given the entries equal to the boundary
+// before `begin`, and writes each keep score (and hit flag).
+__device__ __forceinline__ void update_entries(const LrfuArgs& a, int64_t begin, int64_t end, const ToppState& st,
+                                               int64_t eq_before, uint32_t* s_wave) {
   const bool any = st.mode == 0;
-  if (threadIdx.x == 0) {
-    int64_t eqb = 0;
-    for (int b = 0; b < (int)blockIdx.x; ++b) eqb += a.counts[b];
-    s_eq_before = eqb;
-  }
-  __syncthreads();
-  int64_t eq_before = s_eq_before;
-  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
-  const int64_t end = begin + a.per_block < a.n ? begin + a.per_block : a.n;
   for (int64_t base = begin; base < end; base += kThreads) {
     const int64_t i = base + threadIdx.x;
     const bool valid = i < end;
@@ -439,10 +451,60 @@ __global__ __launch_bounds__(kThreads) void lrfu_update_kernel(LrfuArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kThreads) void lrfu_update_kernel(LrfuArgs a) {
+  __shared__ uint32_t s_wave[kWaves];
+  __shared__ int64_t s_eq_before;
+  const ToppState st = *a.st;
+  if (threadIdx.x == 0) {
+    int64_t eqb = 0;
+    for (int b = 0; b < (int)blockIdx.x; ++b) eqb += a.counts[b];
+    s_eq_before = eqb;
+  }
+  __syncthreads();
+  const int64_t begin = (int64_t)blockIdx.x * a.per_block;
+  const int64_t end = begin + a.per_block < a.n ? begin + a.per_block : a.n;
+  update_entries(a, begin, end, st, s_eq_before, s_wave);
+}
+
+// ---- rows that fit one block (at most kMaxPerBlock entries): every step in one launch,
+// the state and the three weighted histograms in LDS, no count pass (no other blocks)
+// and no workspace memory touched.
+__global__ __launch_bounds__(kThreads) void lrfu_one_block_kernel(LrfuArgs a) {
+  __shared__ unsigned long long h[kBins];
+  __shared__ uint64_t s_wsum[kWaves];
+  __shared__ uint64_t s_wtot[kWaves][kLimbs];
+  __shared__ Big s_total, s_target;
+  __shared__ uint32_t s_wave[kWaves];
+  __shared__ ToppState st;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    ToppState z;
+    z.prefix = 0;
+    z.mask = 0;
+    z.mode = 0;
+    z.ticket = 0;
+    z.pad0 = 0;
+    z.pad1 = 0;
+    z.rem = 0;
+    z.c_eq = 0;
+    st = z;
+  }
+  for (int pass = 0; pass < 3; ++pass) {
+    for (int b = tid; b < kBins; b += kThreads) h[b] = 0;
+    __syncthreads();   // also closes the previous pass's reads of h and its update of st
+    if (st.mode != 0) break;   // no hits (uniform)
+    hist_entries(a, 0, a.n, pass, st.prefix, st.mask, h);
+    __syncthreads();
+    decide_digit(h, a.top_p, pass, st, s_wsum, s_wtot, s_total, s_target);
+  }
+  __syncthreads();
+  update_entries(a, 0, a.n, st, 0, s_wave);
+}
+
 }  // namespace
 
 int lrfu_blocks(int64_t n) {
-  int64_t b = (n + 4095) / 4096;
+  int64_t b = (n + kMaxPerBlock - 1) / kMaxPerBlock;
   if (b < 1) b = 1;
   if (b > kMaxBlocks) b = kMaxBlocks;
   return (int)b;
@@ -455,8 +517,14 @@ size_t lrfu_workspace_bytes(int64_t n) {
 
 hipError_t launch_lrfu(const LrfuArgs& a, hipStream_t s) {
   if (trace_on())
-    trace_launch("lrfu init+3 hist+count+update grid=%d block=%d  entries=%lld top_p=%g", a.n_blocks, kThreads,
-                 (long long)a.n, (double)a.top_p);
+    trace_launch(a.n_blocks == 1 ? "lrfu one block (3 hist passes, update) grid=%d block=%d  entries=%lld top_p=%g"
+                                 : "lrfu init+3 hist+count+update grid=%d block=%d  entries=%lld top_p=%g",
+                 a.n_blocks, kThreads, (long long)a.n, (double)a.top_p);
+  if (a.n_blocks == 1) {
+    // the whole row fits one block: one launch instead of six
+    hipLaunchKernelGGL(lrfu_one_block_kernel, dim3(1), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(lrfu_init_kernel, dim3(1), dim3(64), 0, s, a.st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

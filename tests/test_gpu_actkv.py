@@ -66,6 +66,16 @@ def _scores(rng, n, dist):
     (4097, "twobinade", float(np.nextafter(np.float32(1.0), np.float32(0.0))), 1.0),
     (1_048_583, "power", 0.9, 1.0),               # the largest block count, ragged tail
     (1_048_583, "ties", 0.75, 1.0),
+    # rows of at most 4,096 entries take the one-block kernel
+    (4096, "mixed", 0.9, 1.0),
+    (4096, "mixed", 0.0, 1.0),
+    (4096, "wide", 1.0, 1.0),
+    (4096, "wide", 0.999, 1.0),
+    (4096, "twobinade", 1.0, 1.0),
+    (4096, "twobinade", float(np.nextafter(np.float32(1.0), np.float32(0.0))), 1.0),
+    (3000, "tiny", 0.9, 1.0),
+    (2000, "equal", 0.5, 1.0),
+    (2500, "wide", 1.0, 1e-20),
 ])
 def test_lrfu_update_parity(n, dist, p, scale):
     rng = np.random.default_rng(n + len(dist))
