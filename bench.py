@@ -393,6 +393,9 @@ def extras(steps=5, warmup=2, oracle=True):
     out["mistral7b_n131072_segment_inplace"] = segment_case(steps=3, warmup=1)
     log(f"segment: {out['mistral7b_n131072_segment_inplace']}")
     torch.cuda.empty_cache()
+    out["mistral7b_n131072_segment_remap"] = segment_remap_case(steps=3, warmup=1)
+    log(f"segment remap: {out['mistral7b_n131072_segment_remap']}")
+    torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- Qwen3-8B 1M tokens
     w5 = synth.workload("qwen3-8b-n1m")
@@ -507,6 +510,47 @@ def segment_case(steps=3, warmup=1):
     b4 = 2 * moved4 * w4.kv_bytes_per_token
     return {"workload": w4.name, "ms": round(t4, 3), "evicted": e4, "moved_tokens": moved4, "bytes": b4,
             "GBps": round(b4 / (t4 * 1e-3) / 1e9, 1), "hbm_frac": round(b4 / (t4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def segment_remap_case(steps=3, warmup=1):
+    """The same Mistral-7B segment eviction through the page-table form: a shuffled block
+    table, the suffix relinked instead of moved, its keys re-rotated in place (renumbered
+    from 0), values untouched; and the same without renumbering (only the table changes).
+    Mean HIP-event time per run, runs back to back on one stream."""
+    import compaction_kv_score_amd as kv
+    import synth
+    dev = torch.device("cuda:0")
+    sh = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    hip = HipEvents()
+    w4 = synth.workload("mistral-7b-n131072-segment")
+    N = w4.n_tokens
+    k4, v4, bt4 = synth.kv_cache(w4, seed=0, device=dev, paged_shuffle=True, extra_pages=4)
+    c4 = kv.PagedCache(k4, v4, N, bt4)
+    n_keep4, e4 = kv.kv_select_segment(N, w4.segment_prefix, int(w4.segment_frac * N), 16)
+    old = torch.arange(N, dtype=torch.int32, device=dev)
+    new = torch.zeros(n_keep4, dtype=torch.int32, device=dev)
+    bt_out = torch.zeros(-(-n_keep4 // 16), dtype=torch.int32, device=dev)
+    freed = torch.zeros(e4 // 16, dtype=torch.int32, device=dev)
+    out = {}
+    for base in (0, -1):
+        run = lambda: kv.kv_compact_segment_remap(c4, w4.segment_prefix, e4, bt_out, old, new,  # noqa: E731
+                                                  freed_pages=freed, renumber_base=base, rope_theta=w4.rope_theta)
+        for _ in range(warmup):
+            run()
+        evs = [hip.create(2) for _ in range(steps)]
+        for e in evs:
+            hip.record(e[0], sh)
+            run()
+            hip.record(e[1], sh)
+        torch.cuda.synchronize()
+        out[base] = sum(hip.ms(e[0], e[1]) for e in evs) / steps
+    moved4 = n_keep4 - w4.segment_prefix
+    b4 = moved4 * w4.kv_bytes_per_token            # the suffix's keys read and written
+    return {"workload": w4.name, "ms": round(out[0], 3), "evicted": e4, "rotated_tokens": moved4, "bytes": b4,
+            "GBps": round(b4 / (out[0] * 1e-3) / 1e9, 1),
+            "hbm_frac": round(b4 / (out[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "no_renumber_us": round(out[-1] * 1e3, 1),
+            "note": "block table relinked; keys re-rotated in place, values not touched"}
 
 
 def small_config_step(name, steps=20, warmup=3):
@@ -712,6 +756,9 @@ def main():
     ap.add_argument("--segment", action="store_true",
                     help="only the Mistral-7B 131,072-token in-place segment case (5 runs after 1 "
                          "warm-up), one JSON line")
+    ap.add_argument("--segment-remap", action="store_true",
+                    help="only the same segment eviction through the page table (kv_compact_segment_remap, "
+                         "with and without renumbering; 5 runs after 1 warm-up), one JSON line")
     ap.add_argument("--small", action="store_true",
                     help="only the two Qwen2.5-1.5B-shaped steps (eager and graph-replayed), one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -730,6 +777,9 @@ def main():
         return
     if args.segment:
         print(json.dumps({"segment": segment_case(steps=5, warmup=1)}), flush=True)
+        return
+    if args.segment_remap:
+        print(json.dumps({"segment_remap": segment_remap_case(steps=5, warmup=1)}), flush=True)
         return
     if args.small:
         print(json.dumps({f"step_{n}": small_config_step(n)

@@ -148,6 +148,8 @@ def lib() -> ctypes.CDLL:
                                            P(KvRefStore), vp]),
             "kv_compact_segment_inplace_ex": (i32, [P(KvCacheDesc), i64, i64, vp, i32, P(KvRope), i32,
                                                     P(KvMetaDesc), i32, P(KvRefStore), vp]),
+            "kv_compact_segment_remap": (i32, [P(KvCacheDesc), i64, i64, vp, vp, vp, vp, i32, P(KvRope), i32,
+                                               P(KvMetaDesc), i32, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -496,6 +498,22 @@ def kv_compact_rerope(src: PagedCache, dst: PagedCache, keep_tokens, n_keep, max
                                       _ptr(keep_tokens), _ptr(n_keep), int(max_keep), _ptr(old_pos),
                                       _ptr(new_pos), int(renumber_base), ctypes.byref(rope), int(limit),
                                       arr, n_meta, rs, rd, _stream(src.k.device)), "kv_compact_rerope_ex")
+
+
+def kv_compact_segment_remap(cache: PagedCache, prefix_len, evict_len, block_table_out, old_pos, new_pos,
+                             freed_pages=None, renumber_base=-1, rope_theta=1e6, limit=0, meta=None, rope=None):
+    """Page-table segment eviction (see kv_compact_segment_remap): the suffix is relinked
+    in block_table_out, keys whose position changes are re-rotated in place; meta is a
+    list of (src, dst) tensor pairs indexed by logical token."""
+    if cache.block_table is None:
+        raise ValueError("kv_compact_segment_remap needs a paged cache with a block table")
+    rope = rope if rope is not None else kv_rope("default", base=rope_theta)
+    arr, n_meta = _meta_array(meta or [])
+    _check(lib().kv_compact_segment_remap(ctypes.byref(cache.desc()), int(prefix_len), int(evict_len),
+                                          _ptr(block_table_out), _ptr(freed_pages), _ptr(old_pos), _ptr(new_pos),
+                                          int(renumber_base), ctypes.byref(rope), int(limit), arr, n_meta,
+                                          _stream(cache.k.device)),
+           "kv_compact_segment_remap")
 
 
 def kv_compact_segment_inplace(cache: PagedCache, prefix_len, evict_len, pos, renumber_base=-1,

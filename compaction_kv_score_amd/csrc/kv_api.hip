@@ -716,6 +716,7 @@ int32_t kv_compact_segment_inplace_ex(const kv_cache_desc* cache, int64_t prefix
   a.old_pos = pos;
   a.new_pos = pos;
   a.meta = ms;
+  a.rows_in_place = 1;
   hipError_t e;
   // prefix: stays in place (re-rotated only if its positions change); a rank reads and
   // writes its own position here, so each rank is one workgroup
@@ -1061,6 +1062,71 @@ int32_t kv_compact_tail_inplace(const kv_cache_desc* cache, const int32_t* keep_
   const int64_t grid = max_keep < a.budget ? max_keep : a.budget;
   const hipError_t e = launch_tail_compact(a, grid, stream);
   return e == hipSuccess ? KV_OK : hip_fail(e);
+}
+
+int32_t kv_compact_segment_remap(const kv_cache_desc* cache, int64_t prefix_len, int64_t evict_len,
+                                 int32_t* block_table_out, int32_t* freed_pages, const int32_t* old_pos,
+                                 int32_t* new_pos, int32_t renumber_base, const kv_rope* rope, int32_t limit,
+                                 const kv_meta_desc* meta, int32_t n_meta, hipStream_t stream) {
+  int32_t rc = check_cache(cache);
+  if (rc) return rc;
+  const int64_t N = cache->n_tokens, pg = cache->page_size;
+  if (!cache->block_table || !block_table_out || !old_pos || !new_pos) return KV_EINVAL;
+  if (prefix_len < 0 || evict_len < 0 || prefix_len + evict_len > N) return KV_EINVAL;
+  if (prefix_len % pg || evict_len % pg) return KV_EINVAL;   // whole pages only
+  double inv_freq[kHeadDim / 2];
+  if ((rc = rope_table(rope, inv_freq))) return rc;
+  const int64_t n_keep = N - evict_len;
+  if (renumber_base >= 0 && limit > 0 && (int64_t)renumber_base + n_keep > limit) return KV_ELIMIT;
+  const int64_t n_pages = (N + pg - 1) / pg, keep_pages = (n_keep + pg - 1) / pg, evict_pages = evict_len / pg;
+  // every output lands in memory that no input of the call occupies
+  const uint64_t bt_bytes = (uint64_t)n_pages * 4u, out_bytes = (uint64_t)keep_pages * 4u;
+  if (overlaps(cache->block_table, bt_bytes, block_table_out, out_bytes)) return KV_EINVAL;
+  if (freed_pages && (overlaps(cache->block_table, bt_bytes, freed_pages, (uint64_t)evict_pages * 4u) ||
+                      overlaps(block_table_out, out_bytes, freed_pages, (uint64_t)evict_pages * 4u)))
+    return KV_EINVAL;
+  if (overlaps(old_pos, (uint64_t)N * 4u, new_pos, (uint64_t)n_keep * 4u)) return KV_EINVAL;
+  MetaSet ms;
+  if ((rc = check_meta(meta, n_meta, &ms))) return rc;
+  for (int m = 0; m < ms.n; ++m) {
+    const uint64_t b = (uint64_t)ms.elem_bytes[m];
+    if (overlaps(ms.src[m], (uint64_t)N * b, ms.dst[m], (uint64_t)n_keep * b) ||
+        overlaps(ms.dst[m], (uint64_t)n_keep * b, new_pos, (uint64_t)n_keep * 4u))
+      return KV_EINVAL;
+  }
+  if ((rc = check_device())) return rc;
+  hipError_t e = launch_remap_table(cache->block_table, block_table_out, freed_pages, keep_pages,
+                                    prefix_len / pg, evict_pages, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  // every kept token keeps its physical slot: rank r's slot under the new table is its
+  // source token's slot under the old one, so keys are re-rotated in place and values
+  // stay where they are; no rank writes what another reads, so one launch covers all
+  kv_cache_desc out = *cache;
+  out.block_table = block_table_out;
+  out.n_tokens = n_keep;
+  CompactArgs a;
+  memset(&a, 0, sizeof(a));
+  fill_compact_common(&a, cache, &out, renumber_base, inv_freq);
+  fill_ref(&a, nullptr, nullptr);
+  a.keep = nullptr;
+  a.split = prefix_len;
+  a.shift = evict_len;
+  a.n_keep = nullptr;
+  a.old_pos = old_pos;
+  a.new_pos = new_pos;
+  a.meta = ms;
+  a.rows_in_place = 0;
+  a.rank0 = 0;
+  a.rank1 = n_keep;
+  // One workgroup per rank: with values untouched a rank's key is little work, and
+  // splitting it (as the moving forms do) made the Mistral-7B row slower (measured: 8
+  // workgroups per rank 2.32-2.38 ms, 4 2.11-2.12, 2 2.15, 1 2.04 ms).
+  a.parts = 1;
+  // without renumbering no position changes: positions and metadata only
+  if (renumber_base < 0) e = launch_remap_rows(a, n_keep, stream);
+  else e = launch_compact(a, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return KV_OK;
 }
 
 int32_t kv_compact_segment_inplace(const kv_cache_desc* cache, int64_t prefix_len, int64_t evict_len,

@@ -161,12 +161,14 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
   if (j < 0 || j >= a.src_tokens) return;   // malformed keep entry: nothing is read or written
   const int32_t op = a.old_pos[j];
   const int32_t np = a.renumber_base >= 0 ? a.renumber_base + (int32_t)r : op;
-  const bool in_place = a.keep == nullptr && j == r && a.src_k == a.dst_k;
-  if (in_place && np == op) return;  // already where it belongs, store entry included
 
   const int slot_stride = a.n_kv_heads * kHeadDim;
   const int64_t src_off = token_offset(j, a.src_page_shift, a.src_page_stride, a.src_bt, slot_stride);
   const int64_t dst_off = token_offset(r, a.dst_page_shift, a.dst_page_stride, a.dst_bt, slot_stride);
+  // the token's key and value already sit in its destination slot (the in-place forms):
+  // V is not copied, and K is rewritten only when it is re-rotated
+  const bool in_place = a.src_k == a.dst_k && src_off == dst_off;
+  if (in_place && np == op && a.rows_in_place) return;  // nothing to write, store entry included
   const int per_layer = a.n_kv_heads * 8;
   const int items = a.n_layers * per_layer;
 
@@ -206,9 +208,11 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
     __syncthreads();
   }
 
-  // this workgroup's share of the (layer, head, chunk pair) items
-  const int e0 = (int)((int64_t)part * items / a.parts);
-  const int e1 = (int)((int64_t)(part + 1) * items / a.parts);
+  // this workgroup's share of the (layer, head, chunk pair) items; none when the token
+  // stays in its slot unrotated (only its position and metadata are written below)
+  const bool touch = !(in_place && delta == 0 && !seed && !move_entry);
+  const int e0 = touch ? (int)((int64_t)part * items / a.parts) : 0;
+  const int e1 = touch ? (int)((int64_t)(part + 1) * items / a.parts) : 0;
 #pragma unroll 2
   for (int e = e0 + tid; e < e1; e += kCompactThreads) {
     const int layer = e / per_layer;
@@ -253,6 +257,24 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
     gather_meta_row(a.meta, j, r);
     if (kStore) a.ref_dst_pos[r] = use_ref ? rp : (seed ? op : KV_REF_NONE);
   }
+}
+
+__global__ __launch_bounds__(256) void remap_table_kernel(const int32_t* bt, int32_t* bt_out, int32_t* freed,
+                                                          int64_t keep_pages, int64_t prefix_pages,
+                                                          int64_t evict_pages) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p < keep_pages) bt_out[p] = bt[p < prefix_pages ? p : p + evict_pages];
+  if (freed && p < evict_pages) freed[p] = bt[prefix_pages + p];
+}
+
+// Positions and metadata of ranks [0, n) whose tokens keep their slot and their position
+// (a remap without renumbering): one thread per rank, nothing else is touched.
+__global__ __launch_bounds__(256) void remap_rows_kernel(CompactArgs a, int64_t n) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= n) return;
+  const int64_t j = source_token(a, r);
+  a.new_pos[r] = a.old_pos[j];
+  gather_meta_row(a.meta, j, r);
 }
 
 __global__ __launch_bounds__(256) void ref_invalidate_kernel(int32_t* pos, int64_t count) {
@@ -450,6 +472,25 @@ hipError_t launch_tail_compact(const TailArgs& a, int64_t pairs, hipStream_t s) 
     trace_launch("tail_compact grid=%lld block=%d  start=%lld budget=%lld", (long long)(pairs > 0 ? pairs : 1),
                  kCompactThreads, (long long)a.start, (long long)a.budget);
   hipLaunchKernelGGL(tail_compact_kernel, dim3((unsigned)(pairs > 0 ? pairs : 1)), dim3(kCompactThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_remap_table(const int32_t* bt, int32_t* bt_out, int32_t* freed, int64_t keep_pages,
+                              int64_t prefix_pages, int64_t evict_pages, hipStream_t s) {
+  const int64_t n = keep_pages > evict_pages ? keep_pages : evict_pages;
+  if (n <= 0) return hipSuccess;
+  if (trace_on())
+    trace_launch("remap_table grid=%lld block=256  keep_pages=%lld prefix_pages=%lld evict_pages=%lld",
+                 (long long)((n + 255) / 256), (long long)keep_pages, (long long)prefix_pages, (long long)evict_pages);
+  hipLaunchKernelGGL(remap_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, bt, bt_out, freed,
+                     keep_pages, prefix_pages, evict_pages);
+  return hipGetLastError();
+}
+
+hipError_t launch_remap_rows(const CompactArgs& a, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (trace_on()) trace_launch("remap_rows grid=%lld block=256  ranks=%lld", (long long)((n + 255) / 256), (long long)n);
+  hipLaunchKernelGGL(remap_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, n);
   return hipGetLastError();
 }
 

@@ -199,11 +199,21 @@ struct CompactArgs {
   int32_t* ref_dst_pos;
   int64_t ref_dst_layer_stride;
   MetaSet meta;
+  // new_pos and the metadata destinations are the position and metadata sources
+  // themselves (the in-place segment form): a rank that keeps its slot and its
+  // position then has nothing to write at all
+  int rows_in_place;
 };
 // Workgroups per rank that give every thread of the copy at most one item.
 int compact_parts(int n_layers, int n_kv_heads);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 hipError_t launch_ref_invalidate(int32_t* pos, int64_t count, hipStream_t s);
+// Page-table form of segment eviction: bt_out[p] = bt[p < prefix_pages ? p : p +
+// evict_pages] for p < keep_pages, freed[i] = bt[prefix_pages + i] (nullable).
+hipError_t launch_remap_table(const int32_t* bt, int32_t* bt_out, int32_t* freed, int64_t keep_pages,
+                              int64_t prefix_pages, int64_t evict_pages, hipStream_t s);
+// new_pos[r] = old_pos[source] and the metadata of ranks [0, n), nothing else.
+hipError_t launch_remap_rows(const CompactArgs& a, int64_t n, hipStream_t s);
 
 struct TailArgs {
   uint16_t* k;

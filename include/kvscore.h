@@ -509,6 +509,32 @@ int32_t kv_compact_segment_inplace_ex(const kv_cache_desc *cache, int64_t prefix
                                       const kv_meta_desc *meta /* host array */, int32_t n_meta,
                                       const kv_ref_store *ref /* host */, hipStream_t stream);
 
+/*
+ * Page-table form of segment eviction for a paged cache (cache->block_table != NULL).
+ * Penelope frees the evicted segment's blocks ("Rethinking KV Cache Eviction for Agentic
+ * LLM Serving", Part one; E' is whole blocks, as kv_select_segment gives); here the
+ * surviving suffix is relinked instead of moved.  prefix_len (P) and evict_len (E') must
+ * be multiples of page_size.
+ *   block_table_out[0 .. ceil((N-E')/page_size))  the new logical->physical map: the
+ *       prefix's entries, then the suffix's (logical token r takes the slot of old token
+ *       r < P ? r : r + E');
+ *   freed_pages[0 .. E'/page_size)  the evicted segment's physical pages (or NULL);
+ *   new_pos[r] = renumber_base + r when renumber_base >= 0, else old_pos[source]; a key
+ *       whose position changes is re-rotated in place (PACE Sec. 3.2, Proposition 1);
+ *       values and unchanged keys are not touched at all;
+ *   meta[m].dst[r] = meta[m].src[source] for r < N - E'.
+ * Compared with kv_compact_segment_inplace this reads and writes only the keys that
+ * change position (nothing at all without renumbering).  Outputs must not overlap any
+ * input: block_table_out, freed_pages, new_pos and the metadata destinations are arrays
+ * of their own.  limit as in kv_compact_rerope.  No reference store.
+ */
+int32_t kv_compact_segment_remap(const kv_cache_desc *cache, int64_t prefix_len,
+                                 int64_t evict_len, int32_t *block_table_out,
+                                 int32_t *freed_pages, const int32_t *old_pos, int32_t *new_pos,
+                                 int32_t renumber_base, const kv_rope *rope /* host */,
+                                 int32_t limit, const kv_meta_desc *meta /* host array */,
+                                 int32_t n_meta, hipStream_t stream);
+
 /* Host-only.  PACE's renumber trigger (Sec. 3.2): 1 when the next physical position
  * comes within headroom of the limit (next_pos >= limit - headroom), else 0. */
 int32_t kv_renumber_needed(int64_t next_pos, int32_t headroom, int32_t limit);

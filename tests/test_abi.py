@@ -196,6 +196,33 @@ def test_compact_limit_rule_and_validation():
                                         None) == kv.KV_EINVAL
 
 
+def test_segment_remap_validation():
+    """kv_compact_segment_remap needs a block table, whole pages and outputs of their own
+    (every case is refused before anything touches the device)."""
+    L = kv.lib()
+    rope = kv.kv_rope("default", base=1e4)
+    meta = (kv.KvMetaDesc * 1)()
+    paged = _cache(n_tokens=10000, layer_stride=700 * 16 * 256, page_stride=16 * 256, block_table=FAKE * 64)
+    flat = _cache(n_tokens=10000, layer_stride=700 * 16 * 256, page_stride=16 * 256)
+    out, old, new = FAKE * 128, FAKE * 256, FAKE * 512
+
+    def call(c, p, e, bt_out=out, freed=None, old_pos=old, new_pos=new, base=0, limit=0, m=meta, n_meta=0):
+        return L.kv_compact_segment_remap(ctypes.byref(c), p, e, bt_out, freed, old_pos, new_pos, base,
+                                          ctypes.byref(rope), limit, m, n_meta, None)
+
+    assert call(flat, 160, 320) == kv.KV_EINVAL                   # no block table
+    assert call(paged, 8, 320) == kv.KV_EINVAL                    # prefix not whole pages
+    assert call(paged, 160, 300) == kv.KV_EINVAL                  # evicted segment not whole pages
+    assert call(paged, 9984, 32) == kv.KV_EINVAL                  # past the row
+    assert call(paged, 160, 320, bt_out=None) == kv.KV_EINVAL
+    assert call(paged, 160, 320, bt_out=FAKE * 64 + 64) == kv.KV_EINVAL     # new table inside the old
+    assert call(paged, 160, 320, freed=FAKE * 64) == kv.KV_EINVAL           # freed list over the old
+    assert call(paged, 160, 320, new_pos=old + 400) == kv.KV_EINVAL         # new positions over the old
+    assert call(paged, 160, 320, limit=9000) == kv.KV_ELIMIT                # 9,680 kept from 0
+    bad = (kv.KvMetaDesc * 1)(kv.KvMetaDesc(FAKE * 1024, FAKE * 1024 + 8, 4, 0))
+    assert call(paged, 160, 320, m=bad, n_meta=1) == kv.KV_EINVAL          # metadata in place
+
+
 def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
