@@ -19,16 +19,17 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _case(nl, hkv, n, prefix, evict, base, theta, seed, meta=True):
-    w = synth.workload("mistral-7b-n131072-segment", n_layers=nl, n_kv_heads=hkv, n_q_heads=4 * hkv, n_tokens=n)
+def _case(nl, hkv, n, prefix, evict, base, theta, seed, meta=True, pg=16):
+    w = synth.workload("mistral-7b-n131072-segment", n_layers=nl, n_kv_heads=hkv, n_q_heads=4 * hkv, n_tokens=n,
+                       page_size=pg)
     k, v, bt = synth.kv_cache(w, seed=seed, device=DEV, paged_shuffle=True, extra_pages=3)
     k0, v0 = k.clone(), v.clone()
     g = torch.Generator().manual_seed(seed)
     old_pos = (torch.arange(n, dtype=torch.int32) + torch.randint(0, 50, (1,), generator=g).int()).to(DEV)
     n_keep = n - evict
-    keep_pages = -(-n_keep // 16)
+    keep_pages = -(-n_keep // pg)
     bt_out = torch.full((keep_pages + 2,), -7, dtype=torch.int32, device=DEV)
-    freed = torch.full((evict // 16 + 2,), -7, dtype=torch.int32, device=DEV)
+    freed = torch.full((evict // pg + 2,), -7, dtype=torch.int32, device=DEV)
     new_pos = torch.full((n_keep + 3,), -7, dtype=torch.int32, device=DEV)
     region = torch.randint(0, 7, (n,), generator=g, dtype=torch.int32).to(torch.uint8).to(DEV)
     span = torch.randint(-1, 200, (n,), generator=g, dtype=torch.int32).to(DEV)
@@ -40,19 +41,19 @@ def _case(nl, hkv, n, prefix, evict, base, theta, seed, meta=True):
     torch.cuda.synchronize()
 
     btn, bto = bt.cpu().numpy(), bt_out.cpu().numpy()
-    pp, ep = prefix // 16, evict // 16
+    pp, ep = prefix // pg, evict // pg
     want_bt = np.concatenate([btn[:pp], btn[pp + ep:]])
     assert (bto[:keep_pages] == want_bt).all() and (bto[keep_pages:] == -7).all()
     assert (freed.cpu().numpy()[:ep] == btn[pp:pp + ep]).all() and (freed.cpu().numpy()[ep:] == -7).all()
 
     keep = np.concatenate([np.arange(prefix), np.arange(prefix + evict, n)]).astype(np.int64)
     op = old_pos.cpu().numpy()
-    kl = unpage(np64(k0), btn, 16, n)
-    vl = unpage(np64(v0), btn, 16, n)
+    kl = unpage(np64(k0), btn, pg, n)
+    vl = unpage(np64(v0), btn, pg, n)
     rk, rv, rpos = O.compact_rerope(kl, vl, keep, op, base, theta)
     assert (new_pos.cpu().numpy()[:n_keep] == rpos).all() and (new_pos.cpu().numpy()[n_keep:] == -7).all()
-    gk = unpage(np64(k), bto[:keep_pages], 16, n_keep)
-    gv = unpage(np64(v), bto[:keep_pages], 16, n_keep)
+    gk = unpage(np64(k), bto[:keep_pages], pg, n_keep)
+    gv = unpage(np64(v), bto[:keep_pages], pg, n_keep)
     assert (gv == rv).all()
     same = rpos == op[keep]
     assert (gk[:, same] == rk[:, same]).all()
@@ -63,7 +64,7 @@ def _case(nl, hkv, n, prefix, evict, base, theta, seed, meta=True):
     moved_phys = np.zeros(kphys.shape[1:3], bool)               # [physical page][slot]
     for r in np.nonzero(~same)[0]:
         j = keep[r]
-        moved_phys[btn[j // 16], j % 16] = True
+        moved_phys[btn[j // pg], j % pg] = True
     assert (kphys[:, ~moved_phys] == k0phys[:, ~moved_phys]).all()
     if meta:
         assert (reg_out.cpu().numpy() == region.cpu().numpy()[keep]).all()

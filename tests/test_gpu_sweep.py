@@ -345,3 +345,30 @@ def test_reference_store_sweep(case):
         pos = np.concatenate([opos, opos.max() + 1 + np.arange(add)])
         ref_k = np.concatenate([oref, np.zeros_like(k_new)], axis=1)
         ref_pos = np.concatenate([orefp, np.full(add, O.REF_NONE, dtype=np.int64)])
+
+
+def _remap_cases(n_cases=30, seed=515):
+    rng = np.random.default_rng(seed)
+    for c in range(n_cases):
+        pg = int(rng.choice([1, 2, 4, 8, 16, 64]))
+        nl = int(rng.integers(1, 4))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        n = int(rng.integers(1, 3000))
+        pages = -(-n // pg)
+        pp = int(rng.integers(0, pages + 1))
+        full = n // pg                         # evicted pages must lie inside the row
+        ep = int(rng.integers(0, max(1, full - pp + 1))) if full > pp else 0
+        base = int(rng.choice([-1, 0, int(rng.integers(1, 4000))]))
+        theta = float(rng.choice([1e4, 1e6]))
+        yield c, nl, hkv, n, pg, pp * pg, ep * pg, base, theta
+
+
+@pytest.mark.parametrize("case", list(_remap_cases()), ids=lambda c: f"remap{c[0]}")
+def test_segment_remap_sweep(case):
+    import test_gpu_remap as R
+    c, nl, hkv, n, pg, prefix, evict, base, theta = case
+    if prefix + evict > n:
+        prefix = (n - evict) // pg * pg
+    print(f"remap sweep {c}: layers={nl} kv_heads={hkv} tokens={n} page={pg} prefix={prefix} evict={evict} "
+          f"base={base}", flush=True)
+    R._case(nl, hkv, n, prefix, evict, base, theta, seed=900 + c, pg=pg)
