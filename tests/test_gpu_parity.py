@@ -428,6 +428,9 @@ def test_score_with_supplied_lse():
     (40, 8, 50, 2500, 1),    # G = 5, padded to 8: 400 rows, two row groups
     (32, 2, 20, 1800, 1),    # G = 16: 320 rows
     (32, 1, 16, 1300, 1),    # G = 32: 512 rows
+    # grids small enough that the mass pass combines the LSE itself, with two row groups
+    (32, 2, 20, 600, 1),     # G = 16: 320 rows, 10 key chunks
+    (40, 8, 50, 700, 1),     # G = 5, padded to 8: 400 rows, 11 key chunks
 ])
 def test_score_max_group_parity(hq, hkv, window, n_tokens, n_layers):
     """ActKV's aggregation (Sec. 7.1, Algorithm 3): per KV head the maximum over its
