@@ -31,6 +31,7 @@ KV_STATUS_PINNED_OVER_BUDGET = 1
 KV_STATUS_NAN_SCORE = 2
 KV_STATUS_KEEP_OVERFLOW = 4
 KV_STATUS_BAD_REGION = 8
+KV_STATUS_NOT_WHOLE_PAGES = 16
 KV_POLICY_MEMDECAY = 0
 KV_POLICY_H2O = 1
 KV_AGG_SUM = 0
@@ -150,6 +151,8 @@ def lib() -> ctypes.CDLL:
                                                     P(KvMetaDesc), i32, P(KvRefStore), vp]),
             "kv_compact_segment_remap": (i32, [P(KvCacheDesc), i64, i64, vp, vp, vp, vp, i32, P(KvRope), i32,
                                                P(KvMetaDesc), i32, vp]),
+            "kv_compact_pages_remap": (i32, [P(KvCacheDesc), vp, vp, i64, vp, vp, vp, i32, P(KvRope), i32,
+                                             P(KvMetaDesc), i32, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -514,6 +517,23 @@ def kv_compact_segment_remap(cache: PagedCache, prefix_len, evict_len, block_tab
                                           int(renumber_base), ctypes.byref(rope), int(limit), arr, n_meta,
                                           _stream(cache.k.device)),
            "kv_compact_segment_remap")
+
+
+def kv_compact_pages_remap(cache: PagedCache, keep, n_keep, max_keep, block_table_out, old_pos, new_pos,
+                           renumber_base=-1, rope_theta=1e6, limit=0, meta=None, rope=None, status=None):
+    """Page-table compaction of a page-mode selection (see kv_compact_pages_remap): the kept
+    pages relinked in block_table_out, keys whose position changes re-rotated in place;
+    meta is a list of (src, dst) tensor pairs; status (int32 device word) gets
+    KV_STATUS_NOT_WHOLE_PAGES when the keep list is not whole pages."""
+    if cache.block_table is None:
+        raise ValueError("kv_compact_pages_remap needs a paged cache with a block table")
+    rope = rope if rope is not None else kv_rope("default", base=rope_theta)
+    arr, n_meta = _meta_array(meta or [])
+    _check(lib().kv_compact_pages_remap(ctypes.byref(cache.desc()), _ptr(keep), _ptr(n_keep), int(max_keep),
+                                        _ptr(block_table_out), _ptr(old_pos), _ptr(new_pos), int(renumber_base),
+                                        ctypes.byref(rope), int(limit), arr, n_meta, _ptr(status),
+                                        _stream(cache.k.device)),
+           "kv_compact_pages_remap")
 
 
 def kv_compact_segment_inplace(cache: PagedCache, prefix_len, evict_len, pos, renumber_base=-1,

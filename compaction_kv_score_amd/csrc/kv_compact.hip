@@ -169,6 +169,10 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a)
   // V is not copied, and K is rewritten only when it is re-rotated
   const bool in_place = a.src_k == a.dst_k && src_off == dst_off;
   if (in_place && np == op && a.rows_in_place) return;  // nothing to write, store entry included
+  if (a.remap_only && !in_place) {                      // not a whole-page keep entry: left alone
+    if (tid == 0 && part == 0 && a.status) atomicOr(a.status, KV_STATUS_NOT_WHOLE_PAGES);
+    return;
+  }
   const int per_layer = a.n_kv_heads * 8;
   const int items = a.n_layers * per_layer;
 
@@ -265,6 +269,19 @@ __global__ __launch_bounds__(256) void remap_table_kernel(const int32_t* bt, int
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (p < keep_pages) bt_out[p] = bt[p < prefix_pages ? p : p + evict_pages];
   if (freed && p < evict_pages) freed[p] = bt[prefix_pages + p];
+}
+
+__global__ __launch_bounds__(256) void remap_pages_kernel(const int32_t* bt, int32_t* bt_out, const int32_t* keep,
+                                                          const int64_t* n_keep, int64_t max_keep, int page_shift,
+                                                          int64_t n_pages_src, uint32_t* status) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i == 0 && status) *status = 0u;                  // the compaction, next on the stream, sets bits
+  int64_t n = n_keep ? *n_keep : max_keep;
+  n = n < max_keep ? n : max_keep;
+  const int64_t page = (int64_t)1 << page_shift;
+  if (i * page >= n) return;
+  const int64_t first = keep[i * page];
+  if (first >= 0 && (first >> page_shift) < n_pages_src) bt_out[i] = bt[first >> page_shift];
 }
 
 // Positions and metadata of ranks [0, n) whose tokens keep their slot and their position
@@ -491,6 +508,18 @@ hipError_t launch_remap_rows(const CompactArgs& a, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (trace_on()) trace_launch("remap_rows grid=%lld block=256  ranks=%lld", (long long)((n + 255) / 256), (long long)n);
   hipLaunchKernelGGL(remap_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_remap_pages(const int32_t* bt, int32_t* bt_out, const int32_t* keep, const int64_t* n_keep,
+                              int64_t max_keep, int page_shift, int64_t n_pages_src, uint32_t* status,
+                              hipStream_t s) {
+  const int64_t pages = (max_keep + ((int64_t)1 << page_shift) - 1) >> page_shift;
+  const int64_t n = pages > 1 ? pages : 1;             // at least one thread clears the status
+  if (trace_on())
+    trace_launch("remap_pages grid=%lld block=256  max_pages=%lld", (long long)((n + 255) / 256), (long long)pages);
+  hipLaunchKernelGGL(remap_pages_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, bt, bt_out, keep,
+                     n_keep, max_keep, page_shift, n_pages_src, status);
   return hipGetLastError();
 }
 

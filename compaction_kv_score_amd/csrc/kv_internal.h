@@ -203,6 +203,10 @@ struct CompactArgs {
   // themselves (the in-place segment form): a rank that keeps its slot and its
   // position then has nothing to write at all
   int rows_in_place;
+  // the relinking forms: every rank must already sit in its destination slot; one that
+  // does not is left alone and sets KV_STATUS_NOT_WHOLE_PAGES in *status (nullable)
+  int remap_only;
+  uint32_t* status;
 };
 // Workgroups per rank that give every thread of the copy at most one item.
 int compact_parts(int n_layers, int n_kv_heads);
@@ -214,6 +218,11 @@ hipError_t launch_remap_table(const int32_t* bt, int32_t* bt_out, int32_t* freed
                               int64_t prefix_pages, int64_t evict_pages, hipStream_t s);
 // new_pos[r] = old_pos[source] and the metadata of ranks [0, n), nothing else.
 hipError_t launch_remap_rows(const CompactArgs& a, int64_t n, hipStream_t s);
+// Page-list form: bt_out[i] = bt[keep[i * page] / page] for the kept pages of
+// min(*n_keep, max_keep) kept tokens; *status = 0 (nullable).
+hipError_t launch_remap_pages(const int32_t* bt, int32_t* bt_out, const int32_t* keep, const int64_t* n_keep,
+                              int64_t max_keep, int page_shift, int64_t n_pages_src, uint32_t* status,
+                              hipStream_t s);
 
 struct TailArgs {
   uint16_t* k;

@@ -57,6 +57,9 @@ extern "C" {
                                            first keep_capacity entries were written */
 /* bit of the device status word written by kv_score */
 #define KV_STATUS_BAD_REGION 8u         /* some region label was >= n_regions */
+/* bit of the device status word written by kv_compact_pages_remap */
+#define KV_STATUS_NOT_WHOLE_PAGES 16u   /* some kept token would have to leave its slot (the
+                                           keep list is not whole pages); it was not moved */
 
 /*
  * One sequence row of a paged KV cache, all layers (ActKV Sec. 2.5: PagedKVCache
@@ -534,6 +537,29 @@ int32_t kv_compact_segment_remap(const kv_cache_desc *cache, int64_t prefix_len,
                                  int32_t renumber_base, const kv_rope *rope /* host */,
                                  int32_t limit, const kv_meta_desc *meta /* host array */,
                                  int32_t n_meta, hipStream_t stream);
+
+/*
+ * Page-table compaction of a page-mode selection (MemDecay scores pages, S_p, and keeps the
+ * best ones; kv_select with item_tokens == page_size writes their tokens as ascending runs
+ * of whole pages, the row's partial last page included).  The kept pages are relinked in
+ * logical order instead of gathered:
+ *   block_table_out[i] = cache->block_table[keep_tokens[i * page_size] / page_size]
+ *       for the ceil(n_keep / page_size) kept pages (n_keep: device count, max_keep its
+ *       host bound, as for kv_compact_rerope);
+ *   new_pos and meta as in kv_compact_rerope; a key whose position changes is re-rotated
+ *       in its slot (PACE Sec. 3.2, Proposition 1); values and unchanged keys are not
+ *       touched.
+ * A kept token that would have to leave its slot (a keep list that is not whole pages) is
+ * left alone and sets KV_STATUS_NOT_WHOLE_PAGES in *status (device word or NULL; set to 0
+ * otherwise).  The pages no entry of block_table_out names are free; the caller holds both
+ * tables.  Outputs must not overlap any input.  No reference store.
+ */
+int32_t kv_compact_pages_remap(const kv_cache_desc *cache, const int32_t *keep_tokens,
+                               const int64_t *n_keep, int64_t max_keep, int32_t *block_table_out,
+                               const int32_t *old_pos, int32_t *new_pos, int32_t renumber_base,
+                               const kv_rope *rope /* host */, int32_t limit,
+                               const kv_meta_desc *meta /* host array */, int32_t n_meta,
+                               uint32_t *status, hipStream_t stream);
 
 /* Host-only.  PACE's renumber trigger (Sec. 3.2): 1 when the next physical position
  * comes within headroom of the limit (next_pos >= limit - headroom), else 0. */

@@ -223,6 +223,28 @@ def test_segment_remap_validation():
     assert call(paged, 160, 320, m=bad, n_meta=1) == kv.KV_EINVAL          # metadata in place
 
 
+def test_pages_remap_validation():
+    """kv_compact_pages_remap needs a block table and outputs of its own (every case is
+    refused before anything touches the device)."""
+    L = kv.lib()
+    rope = kv.kv_rope("default", base=1e4)
+    meta = (kv.KvMetaDesc * 1)()
+    paged = _cache(n_tokens=10000, layer_stride=700 * 16 * 256, page_stride=16 * 256, block_table=FAKE * 64)
+    flat = _cache(n_tokens=10000, layer_stride=700 * 16 * 256, page_stride=16 * 256)
+    keep, out, old, new = FAKE * 2048, FAKE * 128, FAKE * 256, FAKE * 512
+
+    def call(c, max_keep=2048, keep_=keep, bt_out=out, old_pos=old, new_pos=new, base=0, limit=0):
+        return L.kv_compact_pages_remap(ctypes.byref(c), keep_, None, max_keep, bt_out, old_pos, new_pos, base,
+                                        ctypes.byref(rope), limit, meta, 0, None, None)
+
+    assert call(flat) == kv.KV_EINVAL                                  # no block table
+    assert call(paged, keep_=None) == kv.KV_EINVAL
+    assert call(paged, max_keep=10001) == kv.KV_EINVAL                 # more kept than the row holds
+    assert call(paged, bt_out=FAKE * 64 + 16) == kv.KV_EINVAL          # new table inside the old one
+    assert call(paged, new_pos=old + 40) == kv.KV_EINVAL               # new positions over the old
+    assert call(paged, limit=2000) == kv.KV_ELIMIT                     # 2,048 kept from 0
+
+
 def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):

@@ -195,3 +195,95 @@ def test_full_size_mistral_131k_segment_remap():
     assert_bf16_within_1ulp(np64(_rows(k, bto, ranks)), rk, "K at N=131K, all layers")
     del k, v
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ page-list form
+
+def _pages_case(nl, hkv, n, pg, budget_pages, base, theta, seed, pin_frac=0.05):
+    """Page-mode selection on a paged row, then kv_compact_pages_remap; checked against the
+    oracle read through the new table, the physical invariants and the gather form."""
+    w = synth.workload("mistral-7b-n131072-segment", n_layers=nl, n_kv_heads=hkv, n_q_heads=4 * hkv, n_tokens=n,
+                       page_size=pg)
+    k, v, bt = synth.kv_cache(w, seed=seed, device=DEV, paged_shuffle=True, extra_pages=3)
+    k0, v0 = k.clone(), v.clone()
+    n_items = -(-n // pg)
+    score = synth.scores(n_items, seed=seed, alphabet=[0.25, 0.5, 0.75] if seed % 2 else None)
+    pinned = synth.pinned_mask(n_items, seed=seed, frac=pin_frac)
+    max_keep = min(n, max(1, budget_pages) * pg + pg)
+    keep = torch.full((max_keep,), -1, dtype=torch.int32, device=DEV)
+    nk = torch.zeros(1, dtype=torch.int64, device=DEV)
+    kv.kv_select(score.to(DEV), pinned.to(DEV), pg, n, budget_pages, keep, nk)
+    g = torch.Generator().manual_seed(seed)
+    old_pos = (torch.arange(n, dtype=torch.int32) + torch.randint(0, 30, (1,), generator=g).int()).to(DEV)
+    out_pages = -(-max_keep // pg)
+    bt_out = torch.full((out_pages,), -7, dtype=torch.int32, device=DEV)
+    new_pos = torch.full((max_keep,), -7, dtype=torch.int32, device=DEV)
+    span = torch.randint(-1, 100, (n,), generator=g, dtype=torch.int32).to(DEV)
+    span_out = torch.full((max_keep,), -9, dtype=torch.int32, device=DEV)
+    status = torch.full((1,), 0x55, dtype=torch.int32, device=DEV)
+    kv.kv_compact_pages_remap(kv.PagedCache(k, v, n, bt), keep, nk, max_keep, bt_out, old_pos, new_pos,
+                              renumber_base=base, rope_theta=theta, meta=[(span, span_out)], status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+
+    items, _ = O.select_items(score.double().numpy(), pinned.numpy(), budget_pages)
+    toks = O.expand_items(items, pg, n)
+    n_keep = int(nk.item())
+    assert n_keep == len(toks) and (keep.cpu().numpy()[:n_keep] == toks).all()
+    btn, bto = bt.cpu().numpy(), bt_out.cpu().numpy()
+    kp = -(-n_keep // pg)
+    assert (bto[:kp] == btn[np.asarray(items, np.int64)]).all()
+    op = old_pos.cpu().numpy()
+    kl = unpage(np64(k0), btn, pg, n)
+    vl = unpage(np64(v0), btn, pg, n)
+    rk, rv, rpos = O.compact_rerope(kl, vl, toks, op, base, theta)
+    assert (new_pos.cpu().numpy()[:n_keep] == rpos).all()
+    assert (span_out.cpu().numpy()[:n_keep] == span.cpu().numpy()[toks]).all()
+    gk = unpage(np64(k), bto[:kp], pg, n_keep)
+    gv = unpage(np64(v), bto[:kp], pg, n_keep)
+    assert (gv == rv).all()
+    same = rpos == op[toks]
+    assert (gk[:, same] == rk[:, same]).all()
+    assert_bf16_within_1ulp(gk, rk, "relinked K")
+    assert torch.equal(v, v0)
+    # the gather form on the original row gives the same keys bit for bit
+    dk = torch.zeros((nl, out_pages, pg, hkv, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    kv.kv_compact_rerope(kv.PagedCache(k0, v0, n, bt), kv.PagedCache(dk, dv, max_keep), keep, nk, max_keep,
+                         old_pos, None, renumber_base=base, rope_theta=theta)
+    torch.cuda.synchronize()
+    assert (np64(dk).reshape(nl, -1, hkv, 128)[:, :n_keep] == gk).all()
+    return n_keep
+
+
+@pytest.mark.parametrize("nl,hkv,n,pg,budget_pages,base,theta", [
+    (2, 8, 3000, 16, 40, 0, 1e4),      # ragged last page (pinned pages include it sometimes)
+    (2, 8, 3000, 16, 40, -1, 1e4),     # positions kept: nothing but the table changes
+    (3, 2, 2048, 64, 8, 5, 1e6),       # large pages, renumbered from 5
+    (1, 4, 777, 4, 50, 0, 1e6),        # small pages
+    (2, 2, 500, 16, 100, 0, 1e4),      # budget above the row: every page kept
+])
+def test_pages_remap_parity(nl, hkv, n, pg, budget_pages, base, theta):
+    _pages_case(nl, hkv, n, pg, budget_pages, base, theta, seed=n + pg + budget_pages)
+
+
+def test_pages_remap_refuses_to_move_partial_pages():
+    """A keep list that is not whole pages: the entries that would leave their slots are
+    left alone and the status reports it; values are never touched."""
+    w = synth.workload("mistral-7b-n131072-segment", n_layers=1, n_kv_heads=2, n_q_heads=8, n_tokens=640)
+    k, v, bt = synth.kv_cache(w, seed=3, device=DEV, paged_shuffle=True, extra_pages=2)
+    k0, v0 = k.clone(), v.clone()
+    toks = np.concatenate([np.arange(32, 48), np.arange(100, 110), np.arange(160, 176)]).astype(np.int32)
+    keep = torch.from_numpy(toks).to(DEV)
+    nk = torch.tensor([len(toks)], dtype=torch.int64, device=DEV)
+    bt_out = torch.zeros(-(-len(toks) // 16), dtype=torch.int32, device=DEV)
+    new_pos = torch.zeros(len(toks), dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kv.kv_compact_pages_remap(kv.PagedCache(k, v, 640, bt), keep, nk, len(toks), bt_out,
+                              torch.arange(640, dtype=torch.int32, device=DEV), new_pos, renumber_base=-1,
+                              status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == kv.KV_STATUS_NOT_WHOLE_PAGES
+    assert torch.equal(v, v0) and torch.equal(k, k0)
+    # the whole first page was relinked and its positions written
+    assert (new_pos.cpu().numpy()[:16] == np.arange(32, 48)).all()

@@ -372,3 +372,26 @@ def test_segment_remap_sweep(case):
     print(f"remap sweep {c}: layers={nl} kv_heads={hkv} tokens={n} page={pg} prefix={prefix} evict={evict} "
           f"base={base}", flush=True)
     R._case(nl, hkv, n, prefix, evict, base, theta, seed=900 + c, pg=pg)
+
+
+def _pages_remap_cases(n_cases=20, seed=616):
+    rng = np.random.default_rng(seed)
+    for c in range(n_cases):
+        pg = int(rng.choice([1, 2, 4, 8, 16, 64]))
+        nl = int(rng.integers(1, 4))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        n = int(rng.integers(1, 2500))
+        pages = -(-n // pg)
+        budget = int(rng.integers(0, pages + 3))
+        base = int(rng.choice([-1, 0, int(rng.integers(1, 4000))]))
+        theta = float(rng.choice([1e4, 1e6]))
+        yield c, nl, hkv, n, pg, budget, base, theta
+
+
+@pytest.mark.parametrize("case", list(_pages_remap_cases()), ids=lambda c: f"pages{c[0]}")
+def test_pages_remap_sweep(case):
+    import test_gpu_remap as R
+    c, nl, hkv, n, pg, budget, base, theta = case
+    print(f"pages remap sweep {c}: layers={nl} kv_heads={hkv} tokens={n} page={pg} budget={budget} base={base}",
+          flush=True)
+    R._pages_case(nl, hkv, n, pg, budget, base, theta, seed=700 + c, pin_frac=0.0)
