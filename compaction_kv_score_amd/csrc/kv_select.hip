@@ -485,9 +485,13 @@ __global__ __launch_bounds__(256) void segment_keep_kernel(int64_t prefix, int64
 
 }  // namespace
 
+// A row that fits one block's batch takes the one-block kernel; larger rows spread over
+// blocks of about 2,048 items (at most 64 blocks): the passes are latency bound, and more
+// blocks overlap more of it (measured at 100,000 items in the step: 4,096 items per block
+// 58.8-59.5 us, 2,048 52.8-53.1 us, 1,563 52.7-53.2 us, 8,192 69.9-70.6 us).
 int select_blocks(int64_t n_items) {
-  int64_t b = (n_items + 4095) / 4096;
-  if (b < 1) b = 1;
+  if (n_items <= (int64_t)kSelThreads * kSelBatch) return 1;
+  int64_t b = (n_items + 2047) / 2048;
   if (b > kSelMaxBlocks) b = kSelMaxBlocks;
   return (int)b;
 }
