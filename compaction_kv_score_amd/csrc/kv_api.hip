@@ -439,7 +439,7 @@ int32_t kv_lrfu_update(const float* attn_score, int64_t n, float scale, float to
   char* w = (char*)ws;
   a.st = (ToppState*)w;
   a.hist = (unsigned long long*)(w + 256);
-  a.counts = (int64_t*)(w + 256 + (size_t)a.n_blocks * 2048 * sizeof(unsigned long long));
+  a.counts = (int64_t*)(w + 256 + (size_t)3 * 2048 * sizeof(unsigned long long));
   const hipError_t e = launch_lrfu(a, stream);
   return e == hipSuccess ? KV_OK : hip_fail(e);
 }

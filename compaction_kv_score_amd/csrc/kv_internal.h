@@ -154,7 +154,7 @@ struct LrfuArgs {
   float* keep_score;             // in/out
   uint8_t* hit;                  // nullable
   ToppState* st;
-  unsigned long long* hist;      // [n_blocks][2048]
+  unsigned long long* hist;      // [3 passes][2048], cleared by the init kernel
   int64_t* counts;               // [n_blocks]
   int n_blocks;
   int64_t per_block;

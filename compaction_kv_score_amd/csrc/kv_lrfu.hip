@@ -18,9 +18,10 @@
 //
 // Steps (no host synchronisation):
 //   1. three weighted radix passes over the 11-, 11- and 10-bit digits of the score bits:
-//      per-block LDS histograms of weight sums (64-bit integer atomics), merged by the
-//      last block, which fixes the digit where the weight counted from the top reaches
-//      what is still missing of the target.  Afterwards T is the boundary score and c the
+//      per-block LDS histograms of weight sums (64-bit integer atomics), added into one
+//      global histogram per pass with 64-bit integer atomics; the last block to finish
+//      reads it and fixes the digit where the weight counted from the top reaches what is
+//      still missing of the target.  Afterwards T is the boundary score and c the
 //      number of entries equal to T (lowest indices first) that complete the target;
 //   2. a count pass (entries equal to T per block) and an update pass that walks the
 //      entries in index order, decides hits and writes KS (and the hit mask).
@@ -35,7 +36,8 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBlocks = 64;
-constexpr int kMaxPerBlock = 4096;  // entries per block while the grid has room
+constexpr int kMaxPerBlock = 4096;  // rows up to this size run in one block
+constexpr int kPerBlock = 2048;     // entries per block for longer rows, while the grid has room
 constexpr int kBins = 2048;
 constexpr int kLimbs = 12;          // 384-bit integers: the total weight stays below 2^336
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt not waited for
@@ -82,7 +84,10 @@ __device__ __forceinline__ void hist_add(unsigned long long* bin, bool want, uin
   if (want && w) atomicAdd(&bin[d], (unsigned long long)w);
 }
 
-__global__ __launch_bounds__(64) void lrfu_init_kernel(ToppState* st) {
+// Clears the state and the three pass histograms (a kernel rather than a memset, so that
+// the sequence can be captured in a graph).
+__global__ __launch_bounds__(kThreads) void lrfu_init_kernel(ToppState* st, unsigned long long* hist) {
+  for (int i = threadIdx.x; i < 3 * kBins; i += kThreads) hist[i] = 0ull;
   if (threadIdx.x == 0) {
     ToppState z;
     z.prefix = 0;
@@ -357,8 +362,12 @@ __global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pas
   const int64_t end = begin + a.per_block < a.n ? begin + a.per_block : a.n;
   hist_entries(a, begin, end, pass, prefix, mask, h);
   __syncthreads();
-  for (int b = tid; b < kBins; b += kThreads) a.hist[(int64_t)blockIdx.x * kBins + b] = h[b];
-  // Every wave waits for its own stores; then one thread makes the block's histogram
+  // the block's non-zero bins go into the pass's global histogram (integer atomics:
+  // exact, so the order of the blocks does not matter)
+  unsigned long long* gh = a.hist + (int64_t)pass * kBins;
+  for (int b = tid; b < kBins; b += kThreads)
+    if (h[b]) atomicAdd(&gh[b], h[b]);
+  // Every wave waits for its own atomics; then one thread makes the block's results
   // visible device-wide (the release writes back the whole L2, so one per block
   // suffices) and takes the ticket.
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
@@ -374,14 +383,8 @@ __global__ __launch_bounds__(kThreads) void lrfu_hist_kernel(LrfuArgs a, int pas
   // histograms below are read with cache-bypassing atomic loads)
   if (threadIdx.x < 64) __threadfence();
 
-  // ---- last block: global weighted histogram (integer sums), then the digit
-  const int nb = (int)gridDim.x;
-  for (int b = tid; b < kBins; b += kThreads) {
-    unsigned long long tot = 0;
-    for (int blk = 0; blk < nb; ++blk)
-      tot += __atomic_load_n(&a.hist[(int64_t)blk * kBins + b], __ATOMIC_RELAXED);
-    h[b] = tot;
-  }
+  // ---- last block: the pass's global weighted histogram (integer sums), then the digit
+  for (int b = tid; b < kBins; b += kThreads) h[b] = __atomic_load_n(&gh[b], __ATOMIC_RELAXED);
   __syncthreads();
   if (tid == 0) st = *a.st;
   __syncthreads();
@@ -504,15 +507,15 @@ __global__ __launch_bounds__(kThreads) void lrfu_one_block_kernel(LrfuArgs a) {
 }  // namespace
 
 int lrfu_blocks(int64_t n) {
-  int64_t b = (n + kMaxPerBlock - 1) / kMaxPerBlock;
-  if (b < 1) b = 1;
+  if (n <= kMaxPerBlock) return 1;
+  int64_t b = (n + kPerBlock - 1) / kPerBlock;
   if (b > kMaxBlocks) b = kMaxBlocks;
   return (int)b;
 }
 
 size_t lrfu_workspace_bytes(int64_t n) {
   const int nb = lrfu_blocks(n);
-  return 256 + (size_t)nb * kBins * sizeof(unsigned long long) + (size_t)nb * sizeof(int64_t);
+  return 256 + (size_t)3 * kBins * sizeof(unsigned long long) + (size_t)nb * sizeof(int64_t);
 }
 
 hipError_t launch_lrfu(const LrfuArgs& a, hipStream_t s) {
@@ -525,7 +528,7 @@ hipError_t launch_lrfu(const LrfuArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(lrfu_one_block_kernel, dim3(1), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(lrfu_init_kernel, dim3(1), dim3(64), 0, s, a.st);
+  hipLaunchKernelGGL(lrfu_init_kernel, dim3(1), dim3(kThreads), 0, s, a.st, a.hist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(a.n_blocks), block(kThreads);
