@@ -64,6 +64,8 @@ def _scores(rng, n, dist):
     (70_000, "wide", 1.0, 1e-20),                 # products underflow to subnormals and 0
     (4097, "twobinade", 1.0, 1.0),
     (4097, "twobinade", float(np.nextafter(np.float32(1.0), np.float32(0.0))), 1.0),
+    (131_072, "mixed", 0.9, 1.0),                 # 64 full blocks of 2,048 entries
+    (131_073, "wide", 0.999, 1.0),                # 64 blocks of 2,049 (the last one short)
     (1_048_583, "power", 0.9, 1.0),               # the largest block count, ragged tail
     (1_048_583, "ties", 0.75, 1.0),
     # rows of at most 4,096 entries take the one-block kernel

@@ -720,6 +720,51 @@ def test_full_size_qwen3_100k_bench_step(qwen3_100k):
     assert (dst_accum.cpu() == accum.cpu()[kept]).all() and (dst_span.cpu() == span_id[kept]).all()
 
 
+def test_long_single_head_row_many_chunks():
+    """One layer, one KV head (two query heads, W = 4) over 2^21 + 37 tokens behind a shuffled
+    block table: every scoring pass splits the row into hundreds of key chunks of the one
+    (layer, KV head), so the LSE combine takes that many partials per row and the selection
+    runs on two million items over its largest block count.  LSE, every token's mass and
+    score against the oracle; the keep list bit-exact against the oracle's selection on the
+    device's own scores; all kept ranks' K within 1 ulp and V, positions exact."""
+    N = (1 << 21) + 37
+    w = synth.workload("qwen3-8b-n100k", n_layers=1, n_q_heads=2, n_kv_heads=1, window=4, n_tokens=N)
+    k, v, bt = synth.kv_cache(w, seed=5, device=DEV, paged_shuffle=True, extra_pages=3)
+    q = synth.window_queries(w, seed=5, device=DEV)
+    acc0 = torch.rand(N, generator=torch.Generator().manual_seed(5)) * 1e-5   # comparable with the mass
+    acc = acc0.to(DEV)
+    got = _run_score(w, k, v, bt, q, policy="h2o", item_tokens=1, state=dict(accum=acc), n_sink=4, n_recent=128)
+    kl = _paged_to_logical(k, bt, 16, N)
+    ref = O.score_step(np64(q), kl, policy="h2o", accum=np64(acc0), n_sink=4, n_recent=128, item_tokens=1)
+    assert np.abs(np64(got["lse"]) - ref["lse"]).max() < 1e-5
+    assert_rel(np64(got["mass"]), ref["mass"], what="mass")
+    assert_rel(np64(acc), ref["accum"], what="accum")
+    assert_rel(np64(got["item_score"]), ref["item_score"], what="item score")
+    assert (got["item_pinned"].numpy().astype(bool) == ref["item_pinned"]).all()
+    # selection on the device's own scores, bit-exact
+    B = 2048
+    keep = torch.zeros(B, dtype=torch.int32, device=DEV)
+    n_keep = torch.zeros(1, dtype=torch.int64, device=DEV)
+    kv.kv_select(got["item_score"].to(DEV), got["item_pinned"].to(DEV), 1, N, B, keep, n_keep)
+    items, _ = O.select_items(np64(got["item_score"]), got["item_pinned"].numpy(), B)
+    torch.cuda.synchronize()
+    nk = int(n_keep.item())
+    keep_np = keep[:nk].cpu().numpy()
+    assert nk == B and (keep_np == items).all()
+    # compaction of every kept rank, renumbered from 0
+    dk = torch.zeros((1, B // 16, 16, 1, 128), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros_like(dk)
+    pos = torch.arange(N, dtype=torch.int32, device=DEV)
+    newp = torch.zeros(B, dtype=torch.int32, device=DEV)
+    kv.kv_compact_rerope(kv.PagedCache(k, v, N, bt), kv.PagedCache(dk, dv, B), keep, n_keep, B, pos, newp,
+                         renumber_base=0, rope_theta=w.rope_theta, limit=0)
+    torch.cuda.synchronize()
+    rk, rv, rpos = O.compact_rerope(kl, _paged_to_logical(v, bt, 16, N), keep_np, np.arange(N), 0, w.rope_theta)
+    assert (newp.cpu().numpy() == rpos).all()
+    assert (np64(dv).reshape(1, B, 1, 128) == rv).all()
+    assert_bf16_within_1ulp(np64(dk).reshape(1, B, 1, 128), rk, "long row K")
+
+
 def test_full_size_mistral_131k_segment():
     """Mistral-7B shape at full size (32 layers, 131,072 tokens, 16,384-token prefix, 30%
     evicted): in-place segment eviction + re-rotation as bench.py --extras runs it.  Every
