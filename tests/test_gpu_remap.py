@@ -256,15 +256,16 @@ def _pages_case(nl, hkv, n, pg, budget_pages, base, theta, seed, pin_frac=0.05):
     return n_keep
 
 
-@pytest.mark.parametrize("nl,hkv,n,pg,budget_pages,base,theta", [
-    (2, 8, 3000, 16, 40, 0, 1e4),      # ragged last page (pinned pages include it sometimes)
-    (2, 8, 3000, 16, 40, -1, 1e4),     # positions kept: nothing but the table changes
-    (3, 2, 2048, 64, 8, 5, 1e6),       # large pages, renumbered from 5
-    (1, 4, 777, 4, 50, 0, 1e6),        # small pages
-    (2, 2, 500, 16, 100, 0, 1e4),      # budget above the row: every page kept
+@pytest.mark.parametrize("nl,hkv,n,pg,budget_pages,base,theta,pin_frac", [
+    (2, 8, 3000, 16, 40, 0, 1e4, 0.05),       # ragged last page (pinned pages include it sometimes)
+    (2, 8, 3000, 16, 40, -1, 1e4, 0.05),      # positions kept: nothing but the table changes
+    (3, 2, 2048, 64, 8, 5, 1e6, 0.05),        # large pages, renumbered from 5
+    (1, 4, 777, 4, 50, 0, 1e6, 0.05),         # small pages
+    (2, 2, 500, 16, 100, 0, 1e4, 0.05),       # budget above the row: every page kept
+    (1, 1, 1_000_003, 16, 128, 0, 1e6, 5e-4),  # 62,501 pages (the last one partial) down to 128
 ])
-def test_pages_remap_parity(nl, hkv, n, pg, budget_pages, base, theta):
-    _pages_case(nl, hkv, n, pg, budget_pages, base, theta, seed=n + pg + budget_pages)
+def test_pages_remap_parity(nl, hkv, n, pg, budget_pages, base, theta, pin_frac):
+    _pages_case(nl, hkv, n, pg, budget_pages, base, theta, seed=n + pg + budget_pages, pin_frac=pin_frac)
 
 
 def test_pages_remap_refuses_to_move_partial_pages():
