@@ -236,7 +236,7 @@ int32_t kv_lrfu_workspace_size(int64_t n, size_t *bytes /* host */);
 
 /*
  * ActKV's attention-aware LRFU keep scores ("ActKV: Efficient LLM Agents through
- * Action-Guided KV Cache Management", Sec. 5.1, Algorithm 1, steps 4-7):
+ * Action-Guided KV Cache Management", Sec. 5.1, Algorithm 1, its keep-score update):
  *   s_j = attn_score[j] * scale (float32; e.g. kv_score's group-maximum mass times
  *         1/(L*Hkv*W) gives the mean over layers, KV heads and action queries);
  *   hit_j: j is in the top-p set, the shortest prefix of the entries in the order
@@ -247,7 +247,7 @@ int32_t kv_lrfu_workspace_size(int64_t n, size_t *bytes /* host */);
  *         score a hit;
  *   keep_score[j] <- decay * keep_score[j] + (hit_j ? s_j : 0).
  * New entries enter with keep_score 0 (the caller appends them).  The retained set is
- * then kv_select(keep_score, NULL, ...) (Algorithm 1, step 8).  hit (n bytes, 0/1) may be
+ * then kv_select(keep_score, NULL, ...) (Algorithm 1, its TopK selection).  hit (n bytes, 0/1) may be
  * NULL.  top_p in [0, 1], decay in [0, 1].  Deterministic.
  */
 int32_t kv_lrfu_update(const float *attn_score, int64_t n, float scale, float top_p, float decay,

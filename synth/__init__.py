@@ -6,7 +6,7 @@ selection, no rotation), so both the HIP path and the CPU oracle can consume it.
 per-span foresight bonus it draws stands in for the output of PACE's planner, which sits
 above the path: both sides take it as input.
 
-Workload shapes (from the pages, see the README of the tests for the recipe):
+Workload shapes (from the pages; the value distributions are those of the generators below):
   * KV footprint of Qwen3-8B: 36 layers x 8 KV heads x 128 dims x (K,V) x bf16 =
     144 KiB per token (PACE, Sec. 1).
   * Qwen2.5-1.5B head shape 12 Q / 2 KV heads (MemDecay's models).

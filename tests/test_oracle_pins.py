@@ -668,7 +668,7 @@ def test_topp_every_positive_score_is_a_hit_at_p_one():
 
 
 def test_lrfu_update_rule():
-    """KS <- lambda KS + AttnScore on hits, lambda KS on misses (Algorithm 1, steps 4-7):
+    """KS <- lambda KS + AttnScore on hits, lambda KS on misses (Algorithm 1, its keep-score update):
     lambda = 0 keeps only the current hits, lambda = 1 accumulates, and a missed entry
     decays geometrically instead of dropping out."""
     a = np.array([0.5, 0.25, 0.125, 0.125], dtype=np.float32)  # 0.75 < 0.85 <= 0.875
