@@ -21,7 +21,9 @@
 //      blocks before it, then walks its items in index order with wavefront ballots and
 //      an LDS scan across waves, and writes the kept token indices.
 // A row of at most 4,096 items fits one block: then one launch does the same steps with
-// the histograms in LDS and no count pass (there are no other blocks to count).
+// the histograms in LDS and no count pass (there are no other blocks to count); a row of
+// at most 256 items finds T and k_rem by counting, for each candidate, the candidates
+// ahead of it in the order.
 
 #include <atomic>
 
@@ -52,6 +54,10 @@ __device__ __forceinline__ bool item_pinned(const SelectArgs& a, int64_t i) {
 // Items a thread loads before it processes any of them: the loads of a batch are all in
 // flight together instead of one memory round trip per item.
 constexpr int kSelBatch = 4;
+
+// Rows of at most this many items rank their candidates by counting in the one-block
+// kernel (a few hundred comparisons per thread) instead of three histogram passes.
+constexpr int kRankItems = 256;
 
 // Score and pinned flag of items b0 + u*kSelThreads + tid (u < kSelBatch) before `end`.
 __device__ __forceinline__ void load_batch(const SelectArgs& a, int64_t b0, int64_t end,
@@ -450,6 +456,64 @@ __global__ __launch_bounds__(kSelThreads) void select_one_block_kernel(SelectArg
     s_nan = 0;
     s_last_kept = 0;
   }
+  if (a.n_items <= kRankItems) {
+    // A short row: each candidate counts the candidates before it in the order (higher
+    // key, or equal key and lower index) instead of three histogram passes; the boundary
+    // key T and the ties still to take come out as the passes would give them.  Four
+    // neighbouring lanes share an item, each counting a quarter of the row, 4 keys per
+    // 16-byte LDS read; two lane swaps add the quarters.
+    __shared__ __attribute__((aligned(16))) uint32_t s_key[kRankItems];
+    __shared__ __attribute__((aligned(16))) uint32_t s_cand[kRankItems];   // 1 = candidate
+    const int n = (int)a.n_items;
+    if (tid < kRankItems) {
+      const bool in = tid < n;
+      s_key[tid] = order_key(sc[0]);
+      s_cand[tid] = (in && !pin[0]) ? 1u : 0u;
+      if (in && pin[0]) atomicAdd(&s_npin, 1u);
+      if (in && sc[0] != sc[0]) atomicOr(&s_nan, 1u);
+    }
+    __syncthreads();
+    if (tid == 0) start_state(st, a, s_npin, s_nan);
+    __syncthreads();
+    const uint32_t mode0 = st.mode;
+    const int64_t k_rem = st.k_rem;
+    __syncthreads();   // every thread holds the state before one of them rewrites it
+    const int item = tid >> 2, quarter = tid & 3;
+    if (mode0 == 0u && item < kRankItems) {                      // uniform per wave
+      const uint32_t key = s_key[item];
+      const bool cand = s_cand[item] != 0u;
+      const int span = ((n + 15) / 16) * 4;                      // keys per quarter, a multiple of 4
+      const int j0 = quarter * span;
+      uint32_t above = 0, equal = 0, equal_before = 0;
+      for (int j = j0; j < j0 + span; j += 4) {
+        const uint4 k4 = *(const uint4*)&s_key[j];
+        const uint4 c4 = *(const uint4*)&s_cand[j];
+        const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+        const uint32_t cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          above += (kk[u] > key) ? cc[u] : 0u;
+          const uint32_t eq = (kk[u] == key) ? cc[u] : 0u;
+          equal += eq;
+          equal_before += (j + u < item) ? eq : 0u;
+        }
+      }
+      above += __shfl_xor(above, 1);
+      above += __shfl_xor(above, 2);
+      equal += __shfl_xor(equal, 1);
+      equal += __shfl_xor(equal, 2);
+      equal_before += __shfl_xor(equal_before, 1);
+      equal_before += __shfl_xor(equal_before, 2);
+      // the first of the candidates with key T writes the state
+      if (quarter == 0 && cand && equal_before == 0 && (int64_t)above < k_rem &&
+          k_rem <= (int64_t)(above + equal)) {
+        st.prefix = key;
+        st.mask = 0xFFFFFFFFu;
+        st.k_rem = k_rem - above;
+      }
+    }
+    __syncthreads();
+  } else {
   for (int pass = 0; pass < 3; ++pass) {
     for (int b = tid; b < kBins; b += kSelThreads) h[b] = 0;
     __syncthreads();   // also closes the previous pass's reads of h and its update of st
@@ -467,6 +531,7 @@ __global__ __launch_bounds__(kSelThreads) void select_one_block_kernel(SelectArg
       __syncthreads();
     }
     decide_digit(h, st, pass, s_wave);
+  }
   }
   const uint32_t mode = st.mode;
   const int64_t kept = emit_items(a, 0, a.n_items, sc, pin, mode, st.prefix, mode == 0u ? st.k_rem : 0, 0, 0,

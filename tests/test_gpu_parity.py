@@ -229,6 +229,29 @@ def test_select_nan_only_in_pinned_items():
     _select_case(50, 1, 50, 0, s2, p2)                 # pinned over budget as well
 
 
+def test_select_short_rows_every_class():
+    """Rows of 1 to 300 items (the one-block kernel ranks rows of at most 256 by counting,
+    longer ones by histogram passes): scores drawn from a small set with ties, NaN, +-0 and
+    +-inf, pins, budgets from 0 to past the row, token and page items (partial last
+    pages), small keep capacities; each against the oracle's selection."""
+    rng = np.random.default_rng(256)
+    palette = np.array([np.nan, -np.inf, -1.5, -0.0, 0.0, 0.25, 0.5, 0.5, 1.0, np.inf], np.float32)
+    for case in range(160):
+        n_items = int(rng.integers(1, 301)) if case % 4 else int(rng.choice([1, 2, 255, 256, 257, 300]))
+        if case % 3 == 0:
+            s = rng.choice(palette, n_items).astype(np.float32)
+        else:
+            s = rng.random(n_items).astype(np.float32)
+            s[rng.random(n_items) < 0.2] = s[0]                      # exact ties
+        pin = (rng.random(n_items) < rng.choice([0.0, 0.05, 0.5])).astype(np.uint8)
+        it = int(rng.choice([1, 1, 16]))
+        n_tokens = n_items * it - (int(rng.integers(0, it)) if it > 1 else 0)
+        budget = int(rng.integers(0, n_items + 6))
+        cap = None if case % 5 else max(1, int(rng.integers(1, n_tokens + 1)))
+        _select_case(n_items, it, n_tokens, budget, torch.from_numpy(s),
+                     torch.from_numpy(pin) if pin.any() or case % 2 else None, cap=cap)
+
+
 def test_select_overflow_and_budget_extremes():
     s = synth.scores(1000, seed=3)
     _select_case(1000, 1, 1000, 1000, s, None)
